@@ -1,0 +1,180 @@
+"""CPU oracle for HiLS attention (test infrastructure only).
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, loads or calls anything here.
+
+The arithmetic lives in ``hils_oracle.c`` (plain C, double precision; see its
+header for the passages of the HiLS pages each step follows).  This module only
+marshals numpy arrays through ctypes.  Inputs are either ``float32`` arrays or
+``uint16`` arrays holding bf16 bit patterns.
+
+Parity status of each function (what pins it is in ``tests/test_oracle_*.py``):
+  landmark_scores  pinned (numpy einsum in fp64)
+  fwd (selection)  pinned (numpy lexsort, subset brute force, exact ties)
+  fwd (attention)  pinned (dense causal attention via the chunk-LSE identity,
+                   single-chunk reduction, equal-score mean, invariances)
+  decode           pinned (single-chunk reduction; prefill-row consistency)
+  bwd              pinned (central finite differences, closed-form sums)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "hils_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+DT_BF16 = 0
+DT_F32 = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (OpenMP over independent rows / heads)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", _SRC, "-o", tmp, "-lm"]
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, dbl, vp, ip = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p, ctypes.c_int
+    lib.oracle_landmark_scores.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, dbl, ip, ip]
+    lib.oracle_landmark_scores.restype = None
+    lib.oracle_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, ip, vp, i64, ip, vp,
+                               vp, vp, vp, vp, vp, ip]
+    lib.oracle_fwd.restype = ip
+    lib.oracle_decode.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, dbl, ip,
+                                  vp, vp, vp, vp, vp, ip]
+    lib.oracle_decode.restype = ip
+    lib.oracle_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, ip, vp, vp, vp,
+                               vp, ip]
+    lib.oracle_bwd.restype = ip
+    _lib = lib
+    return lib
+
+
+def _dt(*arrs):
+    kinds = {a.dtype for a in arrs}
+    if len(kinds) != 1:
+        raise TypeError(f"mixed input dtypes {kinds}")
+    k = kinds.pop()
+    if k == np.uint16:
+        return DT_BF16
+    if k == np.float32:
+        return DT_F32
+    raise TypeError(f"oracle inputs must be float32 or uint16 (bf16 bits), got {k}")
+
+
+def _c(a):
+    return np.ascontiguousarray(a)
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def landmark_scores(Q, Klm, C, scale=None, nthreads=0):
+    """S[b,h,t,j] = fp32(scale*<q_t, Klm_j>) for j <= t//C, -inf above; returned as float64."""
+    Q, Klm = _c(Q), _c(Klm)
+    B, H, L, d = Q.shape
+    N = Klm.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    S = np.empty((B, H, L, N), np.float64)
+    _load().oracle_landmark_scores(_p(Q), _p(Klm), _p(S), B, H, L, d, C, scale, _dt(Q, Klm), nthreads)
+    return S
+
+
+def fwd(Q, K, V, Klm, C, k, scale=None, rows=None, idx=None, override_scores=None, nthreads=0):
+    """Forward of every row (or of the flattened rows listed in ``rows``).
+
+    Returns a dict with idx [.., k+1] int32, sel / w / lse [.., k+1] float64,
+    O [.., d] float64 and ``threads`` (threads used).  With ``rows`` the leading
+    shape is [len(rows)].  ``idx`` (same shape as the output idx) fixes the
+    selection; ``override_scores`` [B,H,L,N] float64 replaces the landmark
+    scores for selection and fusion.
+    """
+    Q, K, V, Klm = _c(Q), _c(K), _c(V), _c(Klm)
+    B, H, L, d = Q.shape
+    N = Klm.shape[2]
+    if N != (L + C - 1) // C:
+        raise ValueError("Klm must hold one row per chunk")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    k1 = k + 1
+    if rows is not None:
+        rows = _c(np.asarray(rows, np.int64))
+        lead = (rows.shape[0],)
+    else:
+        lead = (B, H, L)
+    use_idx = idx is not None
+    idx_out = _c(np.array(idx, np.int32, copy=True)).reshape(lead + (k1,)) if use_idx else np.empty(lead + (k1,), np.int32)
+    sel = np.empty(lead + (k1,), np.float64)
+    w = np.empty(lead + (k1,), np.float64)
+    lse = np.empty(lead + (k1,), np.float64)
+    O = np.empty(lead + (d,), np.float64)
+    ov = _c(np.asarray(override_scores, np.float64)) if override_scores is not None else None
+    used = _load().oracle_fwd(_p(Q), _p(K), _p(V), _p(Klm), B, H, L, d, C, k, scale, _dt(Q, K, V, Klm),
+                              _p(rows), 0 if rows is None else rows.shape[0], int(use_idx), _p(ov),
+                              _p(idx_out), _p(sel), _p(w), _p(lse), _p(O), nthreads)
+    return {"idx": idx_out, "sel": sel, "w": w, "lse": lse, "O": O, "threads": used}
+
+
+def decode(q, k_new, v_new, Kc, Vc, Klm, n, C, k, scale=None, nthreads=0):
+    """One decode step at position n for every (b,h).
+
+    Writes k_new / v_new into row n of ``Kc`` / ``Vc`` in place (these are the
+    caller's host arrays, [B,H,Lmax,d]) and returns idx / sel / w / lse [B,H,k+1]
+    and o [B,H,d].
+    """
+    q, k_new, v_new, Klm = _c(q), _c(k_new), _c(v_new), _c(Klm)
+    if not (Kc.flags.c_contiguous and Vc.flags.c_contiguous):
+        raise ValueError("caches must be C-contiguous (they are updated in place)")
+    B, H, d = q.shape
+    Lmax = Kc.shape[2]
+    Nmax = Klm.shape[2]
+    if not (0 <= n < Lmax) or n // C >= Nmax:
+        raise ValueError("n out of range")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    k1 = k + 1
+    idx = np.empty((B, H, k1), np.int32)
+    sel = np.empty((B, H, k1), np.float64)
+    w = np.empty((B, H, k1), np.float64)
+    lse = np.empty((B, H, k1), np.float64)
+    o = np.empty((B, H, d), np.float64)
+    used = _load().oracle_decode(_p(q), _p(k_new), _p(v_new), _p(Kc), _p(Vc), _p(Klm), n, Lmax, Nmax, B, H,
+                                 d, C, k, scale, _dt(q, k_new, v_new, Kc, Vc, Klm), _p(idx), _p(sel), _p(w),
+                                 _p(lse), _p(o), nthreads)
+    return {"idx": idx, "sel": sel, "w": w, "lse": lse, "o": o, "threads": used}
+
+
+def bwd(Q, K, V, Klm, dO, idx, C, k, scale=None, nthreads=0):
+    """Gradients dQ, dK, dV [B,H,L,d] and dKlm [B,H,N,d] (float64), selection fixed by idx."""
+    Q, K, V, Klm, dO = _c(Q), _c(K), _c(V), _c(Klm), _c(dO)
+    B, H, L, d = Q.shape
+    N = Klm.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    idx = _c(np.asarray(idx, np.int32))
+    if idx.shape != (B, H, L, k + 1):
+        raise ValueError("idx must be [B,H,L,k+1]")
+    dQ = np.empty((B, H, L, d), np.float64)
+    dK = np.empty((B, H, L, d), np.float64)
+    dV = np.empty((B, H, L, d), np.float64)
+    dKlm = np.empty((B, H, N, d), np.float64)
+    used = _load().oracle_bwd(_p(Q), _p(K), _p(V), _p(Klm), _p(dO), _p(idx), B, H, L, d, C, k, scale,
+                              _dt(Q, K, V, Klm, dO), _p(dQ), _p(dK), _p(dV), _p(dKlm), nthreads)
+    return {"dQ": dQ, "dK": dK, "dV": dV, "dKlm": dKlm, "threads": used}

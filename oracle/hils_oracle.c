@@ -1,0 +1,338 @@
+/*
+ * CPU oracle for HiLS (Hierarchical Landmark Sparse) attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header, table or helper
+ * with the HIP library.
+ *
+ * What it computes is the plain definition of the operator, written from:
+ *   [HiLS-p5] "Hierarchical Sparse Attention Done Right" abstract (chatpaper
+ *             page, English and German text): each query attends to every
+ *             retrieved chunk on its own, and the per-chunk outputs are fused
+ *             by the chunk retrieval scores.
+ *   [HiLS-p1] ai-feeds summary of the same paper, section "Method" >
+ *             "Input & chunking" (fixed-size chunks with landmark
+ *             representatives) and "Key modules" items 1-2 (landmark scores,
+ *             chunk-level softmax, top-k chunks, per-chunk attention, fusion).
+ *   [HiLS-p2] paper.oopus.info review, section 2 "Core method" (landmark per
+ *             chunk, score, in-chunk attention, weighted fusion) and section 3
+ *             (head dim 64, chunk size 64).
+ * Points the pages leave open are fixed as follows (one landmark key per
+ * chunk; scale 1/sqrt(d) on both softmax levels; top-k ties go to the lower
+ * chunk index; the query's own chunk is always in the set, is not counted in
+ * k, is scored by its own landmark and is attended causally; when fewer than
+ * k past chunks exist all of them are taken; the fusion softmax runs over the
+ * selected set only; the selection is a hard constant in the backward pass).
+ *
+ * Arithmetic: every input element (bf16 bit pattern or fp32) is widened to
+ * double; all sums, exponentials and logarithms are in double.  Chunk scores
+ * are rounded to fp32 once, so that selection decisions are taken on fp32
+ * scores exactly as the GPU path takes them; everything downstream of the
+ * selection stays in double.  Outputs are double.
+ *
+ * Layouts (row-major, head dim innermost):
+ *   Q,K,V,dO [B,H,L,d]   Klm [B,H,N,d] with N = ceil(L/C)
+ *   idx [B,H,L,k+1] int32: slots 0..m-1 = selected past chunks in order
+ *       (score desc, index asc); slots m..k-1 = -1; slot k = own chunk.
+ *   sel, w, lse [B,H,L,k+1] double (sel = the fp32 score, -inf when unused;
+ *       w = 0 and lse = -inf when unused).
+ *   O [B,H,L,d] double.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define DT_BF16 0
+#define DT_F32 1
+
+/* bf16 is the upper half of an IEEE binary32; widening appends 16 zero bits. */
+static double elem(const void* p, int64_t i, int dt) {
+  if (dt == DT_F32) return (double)((const float*)p)[i];
+  uint32_t bits = ((uint32_t)((const uint16_t*)p)[i]) << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+static double dot_row(const void* A, int64_t ra, const void* Bm, int64_t rb, int64_t d, int dt) {
+  double s = 0.0;
+  for (int64_t e = 0; e < d; ++e) s += elem(A, ra * d + e, dt) * elem(Bm, rb * d + e, dt);
+  return s;
+}
+
+typedef struct {
+  const void *Q, *K, *V, *Klm;
+  int64_t B, H, L, d, C, k, N;
+  int64_t Lkv;  /* rows per (b,h) in K/V (L for prefill, Lmax for a decode cache) */
+  int64_t Nlm;  /* rows per (b,h) in Klm */
+  double scale;
+  int dt;
+} prob_t;
+
+typedef struct { float s; int32_t j; } cand_t;
+
+/* total order of the selection: higher fp32 score first, lower index on ties */
+static int cand_cmp(const void* a, const void* b) {
+  const cand_t* x = (const cand_t*)a;
+  const cand_t* y = (const cand_t*)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  return (x->j < y->j) ? -1 : (x->j > y->j);
+}
+
+/* chunk score of query row t against landmark j (HiLS-p2 section 2, step 1):
+ * scale * <q_t, Klm_j>, computed in double and rounded to fp32 */
+static float chunk_score(const prob_t* P, const void* q, int64_t qrow, int64_t bh, int64_t j) {
+  return (float)(P->scale * dot_row(q, qrow, P->Klm, bh * P->Nlm + j, P->d, P->dt));
+}
+
+/*
+ * Selection (HiLS-p1 "Key modules" item 2, top-k chunks): the m = min(k, c)
+ * past chunks with the largest scores under (score desc, index asc).
+ * Writes idx[0..k] and the fp32 score of each slot into sel[0..k].
+ */
+static void select_chunks(const prob_t* P, const void* q, int64_t qrow, int64_t bh, int64_t t,
+                          const double* override_s, int32_t* idx, double* sel) {
+  int64_t c = t / P->C;
+  int64_t m = c < P->k ? c : P->k;
+  cand_t* cs = (cand_t*)malloc(sizeof(cand_t) * (size_t)(c > 0 ? c : 1));
+  for (int64_t j = 0; j < c; ++j) {
+    cs[j].s = override_s ? (float)override_s[j] : chunk_score(P, q, qrow, bh, j);
+    cs[j].j = (int32_t)j;
+  }
+  qsort(cs, (size_t)c, sizeof(cand_t), cand_cmp);
+  for (int64_t r = 0; r < P->k; ++r) {
+    idx[r] = r < m ? cs[r].j : -1;
+    sel[r] = r < m ? (double)cs[r].s : -INFINITY;
+  }
+  idx[P->k] = (int32_t)c;
+  sel[P->k] = override_s ? (double)(float)override_s[c] : (double)chunk_score(P, q, qrow, bh, c);
+  free(cs);
+}
+
+/*
+ * Attention of query row t inside one chunk j (HiLS-p1 "Key modules" item 2,
+ * HiLS-p5: each query attends to each retrieved chunk independently).
+ * Keys are the whole chunk for a past chunk and jC..t for the own chunk.
+ * Returns lse_j and writes o_j[0..d-1] = sum_i softmax_i(a) v_i.
+ */
+static double chunk_attention(const prob_t* P, const void* q, int64_t qrow, int64_t bh, int64_t t,
+                              int64_t j, double* o_j, double* a_buf) {
+  int64_t lo = j * P->C;
+  int64_t hi = (j == t / P->C) ? t : lo + P->C - 1;
+  int64_t n = hi - lo + 1;
+  double amax = -INFINITY;
+  for (int64_t i = 0; i < n; ++i) {
+    a_buf[i] = P->scale * dot_row(q, qrow, P->K, bh * P->Lkv + lo + i, P->d, P->dt);
+    if (a_buf[i] > amax) amax = a_buf[i];
+  }
+  double z = 0.0;
+  for (int64_t i = 0; i < n; ++i) z += exp(a_buf[i] - amax);
+  double lse = amax + log(z);
+  for (int64_t e = 0; e < P->d; ++e) o_j[e] = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    double p = exp(a_buf[i] - lse);
+    for (int64_t e = 0; e < P->d; ++e) o_j[e] += p * elem(P->V, (bh * P->Lkv + lo + i) * P->d + e, P->dt);
+  }
+  return lse;
+}
+
+/*
+ * One query row: selection (or the given idx), fusion weights, per-chunk
+ * attention, fused output.  Fusion weights are the softmax of the chunk
+ * scores over the selected set (HiLS-p1 "Key modules" item 1, chunk-level
+ * softmax; item 2 and HiLS-p5, score-weighted fusion).
+ */
+static void row_forward(const prob_t* P, const void* q, int64_t qrow, int64_t bh, int64_t t,
+                        int use_idx, const double* override_s, int32_t* idx, double* sel,
+                        double* w, double* lse, double* o) {
+  int64_t k1 = P->k + 1;
+  int64_t c = t / P->C;
+  if (use_idx) {
+    for (int64_t r = 0; r < k1; ++r) {
+      if (idx[r] < 0) { sel[r] = -INFINITY; continue; }
+      sel[r] = override_s ? (double)(float)override_s[idx[r]]
+                          : (double)chunk_score(P, q, qrow, bh, idx[r]);
+    }
+  } else {
+    select_chunks(P, q, qrow, bh, t, override_s, idx, sel);
+  }
+  /* chunk-level softmax over the selected set */
+  double smax = -INFINITY;
+  for (int64_t r = 0; r < k1; ++r) if (idx[r] >= 0 && sel[r] > smax) smax = sel[r];
+  double zs = 0.0;
+  for (int64_t r = 0; r < k1; ++r) if (idx[r] >= 0) zs += exp(sel[r] - smax);
+  double* oj = (double*)malloc(sizeof(double) * (size_t)P->d);
+  double* abuf = (double*)malloc(sizeof(double) * (size_t)P->C);
+  for (int64_t e = 0; e < P->d; ++e) o[e] = 0.0;
+  for (int64_t r = 0; r < k1; ++r) {
+    if (idx[r] < 0) { w[r] = 0.0; lse[r] = -INFINITY; continue; }
+    w[r] = exp(sel[r] - smax) / zs;
+    lse[r] = chunk_attention(P, q, qrow, bh, t, idx[r], oj, abuf);
+    for (int64_t e = 0; e < P->d; ++e) o[e] += w[r] * oj[e];
+  }
+  (void)c;
+  free(oj);
+  free(abuf);
+}
+
+static int set_threads(int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+  return omp_get_max_threads();
+#else
+  (void)nthreads;
+  return 1;
+#endif
+}
+
+/* Landmark scores S[b,h,t,j] = fp32(scale <q_t, Klm_j>) for j <= t/C, -inf otherwise. */
+void oracle_landmark_scores(const void* Q, const void* Klm, double* S, int64_t B, int64_t H,
+                            int64_t L, int64_t d, int64_t C, double scale, int dt, int nthreads) {
+  prob_t P = {Q, NULL, NULL, Klm, B, H, L, d, C, 0, (L + C - 1) / C, L, (L + C - 1) / C, scale, dt};
+  set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t row = 0; row < B * H * L; ++row) {
+    int64_t bh = row / L, t = row % L;
+    for (int64_t j = 0; j < P.N; ++j)
+      S[row * P.N + j] = (j <= t / C) ? (double)chunk_score(&P, Q, row, bh, j) : -INFINITY;
+  }
+}
+
+/*
+ * Forward over all rows, or over a list of rows (rows != NULL: flattened
+ * (b*H+h)*L+t indices; outputs are then packed per listed row).
+ * use_idx: take the selection from idx instead of computing it.
+ * override_s: optional [B,H,L,N] double chunk scores used instead of the
+ * landmark scores for both selection and fusion (a test hook).
+ * Returns the number of threads used.
+ */
+int oracle_fwd(const void* Q, const void* K, const void* V, const void* Klm,
+               int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t k, double scale,
+               int dt, const int64_t* rows, int64_t nrows, int use_idx, const double* override_s,
+               int32_t* idx, double* sel, double* w, double* lse, double* O, int nthreads) {
+  int64_t N = (L + C - 1) / C;
+  prob_t P = {Q, K, V, Klm, B, H, L, d, C, k, N, L, N, scale, dt};
+  int used = set_threads(nthreads);
+  int64_t total = rows ? nrows : B * H * L;
+  int64_t k1 = k + 1;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t r = 0; r < total; ++r) {
+    int64_t row = rows ? rows[r] : r;
+    int64_t bh = row / L, t = row % L;
+    row_forward(&P, Q, row, bh, t, use_idx, override_s ? override_s + row * N : NULL,
+                idx + r * k1, sel + r * k1, w + r * k1, lse + r * k1, O + r * d);
+  }
+  return used;
+}
+
+/*
+ * One decode step for every (b,h): write k_new, v_new into row n of the
+ * caches (this oracle's own host copies), then run the forward of query row
+ * t = n over keys 0..n and landmark rows 0..n/C.  The landmark row of the
+ * open chunk n/C is read as the caller supplied it.
+ * Caches are [B,H,Lmax,d]; Klm is [B,H,Nmax,d].
+ */
+int oracle_decode(const void* q, const void* k_new, const void* v_new, void* Kc, void* Vc,
+                  const void* Klm, int64_t n, int64_t Lmax, int64_t Nmax, int64_t B, int64_t H,
+                  int64_t d, int64_t C, int64_t k, double scale, int dt, int32_t* idx,
+                  double* sel, double* w, double* lse, double* o, int nthreads) {
+  int64_t esz = dt == DT_F32 ? 4 : 2;
+  for (int64_t bh = 0; bh < B * H; ++bh) {
+    memcpy((char*)Kc + ((bh * Lmax + n) * d) * esz, (const char*)k_new + bh * d * esz, (size_t)(d * esz));
+    memcpy((char*)Vc + ((bh * Lmax + n) * d) * esz, (const char*)v_new + bh * d * esz, (size_t)(d * esz));
+  }
+  prob_t P = {q, Kc, Vc, Klm, B, H, n + 1, d, C, k, Nmax, Lmax, Nmax, scale, dt};
+  int used = set_threads(nthreads);
+  int64_t k1 = k + 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t bh = 0; bh < B * H; ++bh)
+    row_forward(&P, q, bh, bh, n, 0, NULL, idx + bh * k1, sel + bh * k1, w + bh * k1,
+                lse + bh * k1, o + bh * d);
+  return used;
+}
+
+/*
+ * Backward with the selection held fixed (idx given), gradients in double.
+ * For row t with g = dO_t, selected set S, weights w_j, per-chunk outputs o_j,
+ * per-chunk probabilities p_i (softmax inside chunk j):
+ *   D_j = g.o_j,  D = sum_j w_j D_j,  ds_j = w_j (D_j - D)
+ *   da_i = w_j p_i (g.v_i - D_j)           for key i of chunk j
+ *   dV_i += w_j p_i g,  dK_i += scale da_i q_t,  dQ_t += scale da_i k_i
+ *   dQ_t += scale ds_j Klm_j,  dKlm_j += scale ds_j q_t
+ * (the chain rule through the fused output, the chunk-level softmax, the
+ * in-chunk softmax and both dot-product scores; the hard selection carries no
+ * gradient).  dQ, dK, dV are [B,H,L,d]; dKlm is [B,H,N,d].  Work is split
+ * across (b,h) only, so every accumulation is sequential in row order.
+ */
+int oracle_bwd(const void* Q, const void* K, const void* V, const void* Klm, const void* dO,
+               const int32_t* idx_in, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
+               int64_t k, double scale, int dt, double* dQ, double* dK, double* dV, double* dKlm,
+               int nthreads) {
+  int64_t N = (L + C - 1) / C;
+  prob_t P = {Q, K, V, Klm, B, H, L, d, C, k, N, L, N, scale, dt};
+  int used = set_threads(nthreads);
+  int64_t k1 = k + 1;
+  memset(dQ, 0, sizeof(double) * (size_t)(B * H * L * d));
+  memset(dK, 0, sizeof(double) * (size_t)(B * H * L * d));
+  memset(dV, 0, sizeof(double) * (size_t)(B * H * L * d));
+  memset(dKlm, 0, sizeof(double) * (size_t)(B * H * N * d));
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bh = 0; bh < B * H; ++bh) {
+    int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)k1);
+    double* sel = (double*)malloc(sizeof(double) * (size_t)k1);
+    double* w = (double*)malloc(sizeof(double) * (size_t)k1);
+    double* lse = (double*)malloc(sizeof(double) * (size_t)k1);
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+    double* oj = (double*)malloc(sizeof(double) * (size_t)(k1 * d));
+    double* Dj = (double*)malloc(sizeof(double) * (size_t)k1);
+    double* abuf = (double*)malloc(sizeof(double) * (size_t)C);
+    double* g = (double*)malloc(sizeof(double) * (size_t)d);
+    double* qv = (double*)malloc(sizeof(double) * (size_t)d);
+    for (int64_t t = 0; t < L; ++t) {
+      int64_t row = bh * L + t;
+      memcpy(idx, idx_in + row * k1, sizeof(int32_t) * (size_t)k1);
+      row_forward(&P, Q, row, bh, t, 1, NULL, idx, sel, w, lse, o);
+      for (int64_t e = 0; e < d; ++e) { g[e] = elem(dO, row * d + e, dt); qv[e] = elem(Q, row * d + e, dt); }
+      /* per-chunk outputs o_j and D_j = g.o_j */
+      double D = 0.0;
+      for (int64_t r = 0; r < k1; ++r) {
+        Dj[r] = 0.0;
+        if (idx[r] < 0) continue;
+        chunk_attention(&P, Q, row, bh, t, idx[r], oj + r * d, abuf);
+        for (int64_t e = 0; e < d; ++e) Dj[r] += g[e] * oj[r * d + e];
+        D += w[r] * Dj[r];
+      }
+      for (int64_t r = 0; r < k1; ++r) {
+        if (idx[r] < 0) continue;
+        int64_t j = idx[r];
+        double ds = w[r] * (Dj[r] - D);
+        for (int64_t e = 0; e < d; ++e) {
+          dQ[row * d + e] += scale * ds * elem(Klm, (bh * N + j) * d + e, dt);
+          dKlm[(bh * N + j) * d + e] += scale * ds * qv[e];
+        }
+        int64_t lo = j * C;
+        int64_t hi = (j == t / C) ? t : lo + C - 1;
+        for (int64_t i = lo; i <= hi; ++i) {
+          double a = scale * dot_row(Q, row, K, bh * L + i, d, dt);
+          double p = exp(a - lse[r]);
+          double gv = 0.0;
+          for (int64_t e = 0; e < d; ++e) gv += g[e] * elem(V, (bh * L + i) * d + e, dt);
+          double da = w[r] * p * (gv - Dj[r]);
+          for (int64_t e = 0; e < d; ++e) {
+            dV[(bh * L + i) * d + e] += w[r] * p * g[e];
+            dK[(bh * L + i) * d + e] += scale * da * qv[e];
+            dQ[row * d + e] += scale * da * elem(K, (bh * L + i) * d + e, dt);
+          }
+        }
+      }
+    }
+    free(idx); free(sel); free(w); free(lse); free(o); free(oj); free(Dj); free(abuf); free(g); free(qv);
+  }
+  return used;
+}

@@ -1,0 +1,383 @@
+"""Pins of the CPU oracle against results fixed by mathematics or library routines.
+
+None of these re-types the oracle's formulas: each compares it with a
+textbook routine (torch's scaled-dot-product attention, numpy einsum /
+lexsort), a brute-force enumeration, a closed form or an invariant.  The
+operator definition followed is the one of the HiLS pages: per-chunk attention
+fused by a softmax over the selected chunks' landmark scores ("Hierarchical
+Sparse Attention Done Right", abstract; ai-feeds summary, "Method" > "Key
+modules"), with the open points fixed as stated in the oracle's header.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_landmark_amd import synth
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def rand_inputs(B, H, L, d, C=64, seed=0, dtype="f32", **kw):
+    return synth.prefill_inputs(B, H, L, d, C=C, seed=seed, dtype=dtype, **kw)
+
+
+def f64(x):
+    return synth.as_f32(x).astype(np.float64)
+
+
+def dense_causal(Q, K, V):
+    """Textbook causal softmax attention (torch SDPA, float64, default scale 1/sqrt(d))."""
+    q, k, v = (torch.from_numpy(f64(a)) for a in (Q, K, V))
+    return torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True).numpy()
+
+
+def attn_one(q, K, V):
+    """Softmax attention of one query row over the given keys (torch SDPA, float64)."""
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, None, None], torch.from_numpy(K)[None, None], torch.from_numpy(V)[None, None])
+    return out[0, 0, 0].numpy()
+
+
+def chunk_lse(Q, K, C):
+    """LSE_tj = log sum_{i in chunk j, i <= t} exp(<q_t,k_i>/sqrt(d)); -inf for future chunks."""
+    q, k = f64(Q), f64(K)
+    B, H, L, d = q.shape
+    N = L // C
+    a = np.einsum("bhtd,bhsd->bhts", q, k) / math.sqrt(d)
+    a = np.where(np.tril(np.ones((L, L), bool)), a, -np.inf)
+    a = a.reshape(B, H, L, N, C)
+    m = a.max(axis=-1, keepdims=True)
+    with np.errstate(invalid="ignore"):
+        lse = (m + np.log(np.exp(a - np.where(np.isfinite(m), m, 0)).sum(-1, keepdims=True)))[..., 0]
+    return np.where(np.isfinite(m[..., 0]), lse, -np.inf)
+
+
+# --------------------------------------------------------------------------- scores
+
+
+def test_scores_match_einsum(oracle_mod):
+    x = rand_inputs(1, 2, 256, 32, C=64, seed=1)
+    S = oracle_mod.landmark_scores(x["Q"], x["Klm"], 64)
+    ref = np.einsum("bhtd,bhjd->bhtj", f64(x["Q"]), f64(x["Klm"])) / math.sqrt(32)
+    t = np.arange(256)[:, None]
+    j = np.arange(4)[None, :]
+    mask = j <= t // 64
+    assert np.all(np.isneginf(S[..., ~mask]))
+    np.testing.assert_allclose(S[..., mask], ref[..., mask], rtol=1e-6, atol=1e-7)
+    # scores are fp32 values
+    assert np.all(S[..., mask] == S[..., mask].astype(np.float32))
+
+
+def test_scores_bf16_inputs_exact(oracle_mod):
+    x = rand_inputs(1, 1, 128, 16, C=64, seed=2, dtype="bf16")
+    S = oracle_mod.landmark_scores(x["Q"], x["Klm"], 64)
+    ref = np.einsum("bhtd,bhjd->bhtj", f64(x["Q"]), f64(x["Klm"])) / 4.0
+    ok = np.isfinite(S)
+    np.testing.assert_array_equal(S[ok], ref[ok].astype(np.float32).astype(np.float64))
+
+
+# --------------------------------------------------------------------------- selection
+
+
+def test_selection_matches_lexsort(oracle_mod):
+    B, H, L, d, C, k = 1, 2, 1024, 16, 64, 4
+    x = rand_inputs(B, H, L, d, C=C, seed=3)
+    r = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], C, k)
+    S = oracle_mod.landmark_scores(x["Q"], x["Klm"], C)
+    for b in range(B):
+        for h in range(H):
+            for t in range(0, L, 7):
+                c = t // C
+                m = min(k, c)
+                s = S[b, h, t, :c].astype(np.float32)
+                order = np.lexsort((np.arange(c), -s))[:m]
+                got = r["idx"][b, h, t]
+                np.testing.assert_array_equal(got[:m], order)
+                assert np.all(got[m:k] == -1)
+                assert got[k] == c
+                np.testing.assert_array_equal(r["sel"][b, h, t, :m], s[order])
+                assert r["sel"][b, h, t, k] == np.float32(S[b, h, t, c])
+
+
+def test_selection_bruteforce_subsets(oracle_mod):
+    """The selected set is the only m-subset whose members all beat all non-members."""
+    B, H, C, d, k = 1, 1, 8, 8, 3
+    L = 10 * C
+    x = rand_inputs(B, H, L, d, C=C, seed=4)
+    r = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], C, k)
+    S = oracle_mod.landmark_scores(x["Q"], x["Klm"], C)
+    for t in range(C, L, 3):
+        c = t // C
+        m = min(k, c)
+        s = S[0, 0, t, :c]
+        beats = lambda a, b: s[a] > s[b] or (s[a] == s[b] and a < b)
+        winners = [set(sub) for sub in itertools.combinations(range(c), m)
+                   if all(beats(a, b) for a in sub for b in range(c) if b not in sub)]
+        assert len(winners) == 1
+        assert set(r["idx"][0, 0, t, :m].tolist()) == winners[0]
+
+
+def test_selection_exact_ties_prefer_lower_index(oracle_mod):
+    B, H, L, d, C, k = 1, 1, 512, 16, 64, 2
+    x = rand_inputs(B, H, L, d, C=C, seed=5)
+    Klm = x["Klm"].copy()
+    Klm[0, 0, 5] = Klm[0, 0, 1]  # chunks 1 and 5 tie exactly
+    Klm[0, 0, 3] = Klm[0, 0, 2]  # chunks 2 and 3 tie exactly
+    r = oracle_mod.fwd(x["Q"], x["K"], x["V"], Klm, C, k)
+    S = oracle_mod.landmark_scores(x["Q"], Klm, C)
+    for t in range(6 * C, L):
+        sel = r["idx"][0, 0, t, :k].tolist()
+        assert not (5 in sel and 1 not in sel)
+        assert not (3 in sel and 2 not in sel)
+        assert S[0, 0, t, 1] == S[0, 0, t, 5]
+    # all-equal landmarks: the m lowest indices win
+    Klm[:] = Klm[0, 0, 0]
+    r = oracle_mod.fwd(x["Q"], x["K"], x["V"], Klm, C, k)
+    for t in range(0, L, 5):
+        c = t // C
+        m = min(k, c)
+        assert r["idx"][0, 0, t, :m].tolist() == list(range(m))
+
+
+def test_few_past_chunks_takes_all(oracle_mod):
+    B, H, L, d, C, k = 1, 1, 384, 16, 64, 8
+    x = rand_inputs(B, H, L, d, C=C, seed=6)
+    r = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], C, k)
+    for t in range(L):
+        c = t // C
+        got = r["idx"][0, 0, t]
+        assert sorted(got[:c].tolist()) == list(range(c))
+        assert np.all(got[c:k] == -1) and got[k] == c
+        assert np.all(r["w"][0, 0, t, c:k] == 0.0)
+
+
+# --------------------------------------------------------------------------- attention and fusion
+
+
+def test_single_chunk_reduces_to_dense(oracle_mod):
+    """L = C: every query sees only its own chunk with weight 1, i.e. dense causal attention."""
+    x = rand_inputs(1, 2, 64, 32, C=64, seed=7)
+    r = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], 64, 4)
+    np.testing.assert_allclose(r["O"], dense_causal(x["Q"], x["K"], x["V"]), rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(r["w"][..., 4], 1.0)
+    # rows of the first chunk of a longer sequence as well
+    x = rand_inputs(1, 1, 256, 16, C=64, seed=8, dtype="bf16")
+    r = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], 64, 2)
+    ref = dense_causal(x["Q"][..., :64, :], x["K"][..., :64, :], x["V"][..., :64, :])
+    np.testing.assert_allclose(r["O"][..., :64, :], ref, rtol=0, atol=1e-12)
+
+
+def test_chunk_lse_scores_reproduce_dense_attention(oracle_mod):
+    """Grouping dense attention by chunks: with every chunk selected and each chunk scored by the
+    log-sum-exp of its (causal) logits, the fused output is dense causal attention exactly.  This is
+    the exact form behind the pages' first-order (Taylor) reading of the retrieval score."""
+    B, H, L, d, C = 1, 2, 512, 16, 64
+    N = L // C
+    x = rand_inputs(B, H, L, d, C=C, seed=9)
+    lse = chunk_lse(x["Q"], x["K"], C)
+    # the oracle rounds override scores to fp32; make them fp32-exact so the identity is exact
+    lse32 = np.where(np.isfinite(lse), lse.astype(np.float32), -np.inf).astype(np.float64)
+    r = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], C, N, override_scores=lse32)
+    dense = dense_causal(x["Q"], x["K"], x["V"])
+    # fp32 rounding of the chunk log-partition functions changes weights by <= 2^-24 relative
+    np.testing.assert_allclose(r["O"], dense, rtol=0, atol=5e-7)
+    # the per-chunk lse the oracle reports is the chunk log-partition function
+    for t in (0, 63, 64, 200, 511):
+        c = t // C
+        got = dict(zip(r["idx"][0, 0, t].tolist(), r["lse"][0, 0, t].tolist()))
+        for j in range(c + 1):
+            assert abs(got[j] - lse[0, 0, t, j]) < 1e-12
+
+
+def test_constant_keys_reproduce_dense_at_chunk_ends(oracle_mod):
+    """Keys constant inside each chunk and landmark = that key: the landmark score equals the chunk
+    LSE minus log C for full chunks, so at t = C-1 (mod C) the fused output is dense attention."""
+    B, H, L, d, C = 1, 1, 384, 16, 64
+    N = L // C
+    rng = np.random.default_rng(10)
+    kap = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    K = np.repeat(kap, C, axis=2)
+    Q = rng.standard_normal((B, H, L, d)).astype(np.float32)
+    V = rng.standard_normal((B, H, L, d)).astype(np.float32)
+    r = oracle_mod.fwd(Q, K, V, kap, C, N)
+    dense = dense_causal(Q, K, V)
+    ends = np.arange(C - 1, L, C)
+    np.testing.assert_allclose(r["O"][..., ends, :], dense[..., ends, :], rtol=0, atol=2e-6)
+    # elsewhere the own chunk is only partly filled and the two differ
+    assert np.abs(r["O"][..., 70, :] - dense[..., 70, :]).max() > 1e-4
+
+
+@pytest.mark.parametrize("k", [3, 8])
+def test_equal_scores_give_mean_of_chunk_attentions(oracle_mod, k):
+    """All landmark rows equal: every selected chunk gets the same weight, so the output is the mean
+    of the per-chunk attentions over the selected set (the m lowest past chunks and the own chunk)."""
+    B, H, L, d, C = 1, 1, 512, 16, 64
+    x = rand_inputs(B, H, L, d, C=C, seed=11)
+    Klm = np.broadcast_to(x["Klm"][:, :, :1], x["Klm"].shape).copy()
+    r = oracle_mod.fwd(x["Q"], x["K"], x["V"], Klm, C, k)
+    q, K, V = f64(x["Q"])[0, 0], f64(x["K"])[0, 0], f64(x["V"])[0, 0]
+    for t in (0, 65, 130, 255, 300, 511):
+        c = t // C
+        m = min(k, c)
+        chunks = list(range(m)) + [c]
+        outs = [attn_one(q[t], K[j * C:min(j * C + C, t + 1)], V[j * C:min(j * C + C, t + 1)]) for j in chunks]
+        np.testing.assert_allclose(r["O"][0, 0, t], np.mean(outs, axis=0), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(r["w"][0, 0, t, :m], 1.0 / (m + 1), rtol=1e-14)
+
+
+def test_weights_form_a_distribution(oracle_mod):
+    x = rand_inputs(1, 2, 1024, 64, C=64, seed=12, dtype="bf16")
+    r = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], 64, 4)
+    np.testing.assert_allclose(r["w"].sum(-1), 1.0, rtol=0, atol=1e-12)
+    assert np.all(r["w"] >= 0)
+    # weights are the softmax of the selected scores: their log-ratios are score differences
+    t = 900
+    w, s = r["w"][0, 0, t], r["sel"][0, 0, t]
+    np.testing.assert_allclose(np.log(w[:4] / w[4]), s[:4] - s[4], rtol=0, atol=1e-12)
+
+
+def test_invariances(oracle_mod):
+    B, H, L, d, C, k = 1, 1, 512, 16, 64, 3
+    x = rand_inputs(B, H, L, d, C=C, seed=13)
+    base = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], C, k)
+    # (i) a common vector added to every landmark shifts all scores of a query equally
+    shift = np.float32(0.5) * np.ones((1, 1, 1, d), np.float32)
+    r = oracle_mod.fwd(x["Q"], x["K"], x["V"], (x["Klm"] + shift).astype(np.float32), C, k)
+    same = np.all(r["idx"] == base["idx"], axis=-1)
+    assert same.mean() > 0.99  # fp32 rounding of shifted scores may flip a near tie
+    np.testing.assert_allclose(r["O"][same], base["O"][same], rtol=0, atol=2e-6)
+    # (ii) adding b to every value row adds b to the output (V rounded to bf16 values and b dyadic,
+    # so that V + b is exact in fp32)
+    Vb = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(x["V"]))
+    b = (np.arange(d, dtype=np.float32) - d / 2) / np.float32(8)
+    r0 = oracle_mod.fwd(x["Q"], x["K"], Vb, x["Klm"], C, k)
+    r = oracle_mod.fwd(x["Q"], x["K"], Vb + b, x["Klm"], C, k)
+    np.testing.assert_allclose(r["O"], r0["O"] + b, rtol=0, atol=1e-12)
+    # (iii) permuting (k, v) pairs inside a past chunk leaves the output unchanged
+    perm = np.random.default_rng(0).permutation(C)
+    K2, V2 = x["K"].copy(), x["V"].copy()
+    K2[..., C:2 * C, :] = x["K"][..., C + perm, :]
+    V2[..., C:2 * C, :] = x["V"][..., C + perm, :]
+    r = oracle_mod.fwd(x["Q"], K2, V2, x["Klm"], C, k)
+    np.testing.assert_allclose(r["O"][..., 2 * C:, :], base["O"][..., 2 * C:, :], rtol=0, atol=1e-12)
+
+
+def test_row_subset_matches_full(oracle_mod):
+    x = rand_inputs(1, 2, 512, 16, C=64, seed=14, dtype="bf16")
+    full = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], 64, 3)
+    rows = np.array([0, 63, 64, 511, 512 + 300, 1023])
+    sub = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], 64, 3, rows=rows)
+    for i, rw in enumerate(rows):
+        bh, t = divmod(int(rw), 512)
+        np.testing.assert_array_equal(sub["O"][i], full["O"][0, bh, t])
+        np.testing.assert_array_equal(sub["idx"][i], full["idx"][0, bh, t])
+
+
+# --------------------------------------------------------------------------- decode
+
+
+def test_decode_matches_prefill_rows(oracle_mod):
+    B, H, d, C, k = 1, 2, 16, 64, 3
+    ctx, steps = 256, 80
+    x = synth.decode_inputs(B, H, d, ctx, steps, C=C, seed=15, dtype="bf16")
+    Kc, Vc = x["K_cache"].copy(), x["V_cache"].copy()
+    outs = []
+    for s in range(steps):
+        outs.append(oracle_mod.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc, Vc, x["Klm"], ctx + s, C, k))
+    L = ctx + steps
+    L_pad = ((L + C - 1) // C) * C
+    Q = np.zeros((B, H, L_pad, d), np.uint16)
+    for s in range(steps):
+        Q[:, :, ctx + s] = x["q"][s]
+    K = np.zeros_like(Q)
+    V = np.zeros_like(Q)
+    K[:, :, :L] = Kc[:, :, :L]
+    V[:, :, :L] = Vc[:, :, :L]
+    Klm = x["Klm"][:, :, :L_pad // C]
+    rows = np.array([bh * L_pad + ctx + s for s in range(steps) for bh in range(B * H)])
+    ref = oracle_mod.fwd(Q, K, V, Klm, C, k, rows=rows)
+    for i, (s, bh) in enumerate((s, bh) for s in range(steps) for bh in range(B * H)):
+        np.testing.assert_array_equal(outs[s]["idx"].reshape(-1, k + 1)[bh], ref["idx"][i])
+        np.testing.assert_array_equal(outs[s]["o"].reshape(-1, d)[bh], ref["O"][i])
+    # the appended rows are the step inputs
+    np.testing.assert_array_equal(Kc[:, :, ctx:L], np.moveaxis(x["k_new"], 0, 2))
+
+
+def test_decode_in_first_chunk_is_dense(oracle_mod):
+    B, H, d, C, k = 1, 1, 16, 64, 4
+    x = synth.decode_inputs(B, H, d, 0, 40, C=C, seed=16, dtype="f32", needle=False)
+    Kc, Vc = x["K_cache"].copy(), x["V_cache"].copy()
+    for s in range(40):
+        o = oracle_mod.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc, Vc, x["Klm"], s, C, k)["o"]
+        ref = attn_one(x["q"][s][0, 0].astype(np.float64), Kc[0, 0, :s + 1].astype(np.float64),
+                       Vc[0, 0, :s + 1].astype(np.float64))
+        np.testing.assert_allclose(o[0, 0], ref, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- backward
+
+
+def _loss(oracle_mod, Q, K, V, Klm, G, idx, C, k):
+    O = oracle_mod.fwd(Q, K, V, Klm, C, k, idx=idx)["O"]
+    return float(np.sum(O * G.astype(np.float64)))
+
+
+def test_bwd_central_differences(oracle_mod):
+    B, H, L, d, C, k = 1, 1, 256, 8, 64, 2
+    x = rand_inputs(B, H, L, d, C=C, seed=17, with_dO=True)
+    G = x["dO"]
+    idx = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], C, k)["idx"]
+    g = oracle_mod.bwd(x["Q"], x["K"], x["V"], x["Klm"], G, idx, C, k)
+    h = 2.0 ** -10
+    rng = np.random.default_rng(0)
+    names = {"Q": "dQ", "K": "dK", "V": "dV", "Klm": "dKlm"}
+    for name, gname in names.items():
+        arr = x[name]
+        for _ in range(12):
+            pos = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            vals = []
+            for sgn in (1, -1):
+                pert = {n: x[n] for n in names}
+                a = arr.copy()
+                a[pos] = np.float32(a[pos] + sgn * h)
+                pert[name] = a
+                vals.append(_loss(oracle_mod, pert["Q"], pert["K"], pert["V"], pert["Klm"], G, idx, C, k))
+            fd = (vals[0] - vals[1]) / (2 * h)
+            an = g[gname][pos]
+            assert abs(fd - an) <= 2e-4 * max(1.0, abs(an)), (name, pos, fd, an)
+
+
+def test_bwd_closed_form_sums(oracle_mod):
+    B, H, L, d, C, k = 1, 2, 512, 16, 64, 3
+    x = rand_inputs(B, H, L, d, C=C, seed=18, dtype="bf16", with_dO=True)
+    idx = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], C, k)["idx"]
+    g = oracle_mod.bwd(x["Q"], x["K"], x["V"], x["Klm"], x["dO"], idx, C, k)
+    # shift of every landmark by a common vector changes nothing: sum_j dKlm_j = 0
+    np.testing.assert_allclose(g["dKlm"].sum(axis=2), 0.0, atol=1e-10)
+    # a common logit shift inside a chunk changes nothing: per-chunk sums of dK vanish
+    np.testing.assert_allclose(g["dK"].reshape(B, H, L // C, C, d).sum(axis=3), 0.0, atol=1e-10)
+    # adding b to every value row adds b to every output: sum_i dV_i = sum_t dO_t
+    np.testing.assert_allclose(g["dV"].sum(axis=2), f64(x["dO"]).sum(axis=2), rtol=1e-10, atol=1e-10)
+    # chunks never selected (and keys never attended) get no gradient
+    used = np.zeros((B, H, L // C), bool)
+    for b in range(B):
+        for h in range(H):
+            used[b, h, np.unique(idx[b, h][idx[b, h] >= 0])] = True
+    assert np.all(g["dKlm"][~used] == 0)
+
+
+def test_bwd_single_chunk_matches_autograd_dense(oracle_mod):
+    """L = C: the operator is dense causal attention, whose gradients torch autograd gives."""
+    x = rand_inputs(1, 1, 64, 16, C=64, seed=19, with_dO=True)
+    idx = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], 64, 2)["idx"]
+    g = oracle_mod.bwd(x["Q"], x["K"], x["V"], x["Klm"], x["dO"], idx, 64, 2)
+    q, k, v = (torch.from_numpy(f64(x[n])).requires_grad_(True) for n in ("Q", "K", "V"))
+    out = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+    out.backward(torch.from_numpy(f64(x["dO"])))
+    np.testing.assert_allclose(g["dQ"], q.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(g["dK"], k.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(g["dV"], v.grad.numpy(), atol=1e-11)
+    np.testing.assert_array_equal(g["dKlm"], 0.0)
