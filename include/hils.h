@@ -1,0 +1,166 @@
+/*
+ * libhils — HiLS (Hierarchical Landmark Sparse) attention on AMD Instinct
+ * MI355X (gfx950).  C ABI.
+ *
+ * The operator (sources: "Hierarchical Sparse Attention Done Right",
+ * abstract on the chatpaper page; ai-feeds summary, section "Method" >
+ * "Input & chunking" and "Key modules" items 1-3; paper.oopus.info review,
+ * sections 2-3):
+ *   the sequence is cut into chunks of C = 64 tokens, each with one landmark
+ *   key; query t scores every completed past chunk j < t/C through its
+ *   landmark, s_tj = scale * <q_t, Klm_j>; it keeps the top-k of them (ties to
+ *   the lower chunk index) plus its own chunk c = t/C (scored by Klm_c, not
+ *   counted in k, attended causally); it runs softmax attention inside each
+ *   kept chunk, o_tj; and returns o_t = sum_j w_tj o_tj with w the softmax of
+ *   the kept chunks' scores.  scale is 1/sqrt(d) unless the caller passes
+ *   another positive value.
+ *
+ * Common conventions
+ *   Layouts are row-major with the head dim innermost:
+ *     Q, K, V, O, dO     [B][H][L][d]
+ *     K_lm               [B][H][N][d]        N = L / C
+ *     idx                [B][H][L][k+1] int32: slots 0..m-1 hold the kept past
+ *                        chunks in selection order (score desc, index asc),
+ *                        m = min(k, t/C); slots m..k-1 hold -1; slot k holds t/C.
+ *     sel_score, w, lse  [B][H][L][k+1] float: the fp32 chunk score, fusion
+ *                        weight and chunk log-partition function of each slot
+ *                        (-inf, 0, unspecified on unused slots).
+ *   Element type (dt): HILS_BF16 (storage of Q,K,V,K_lm,O,dO as bf16) or
+ *   HILS_FP32.  Arithmetic: products on MFMA with fp32 accumulation; fp32
+ *   inputs are rounded to bf16 where they enter an attention MFMA, while
+ *   chunk scores of fp32 inputs use fp32 MFMA.
+ *   Sizes: B, H >= 1; d in {64, 128}; C == 64; L a positive multiple of C;
+ *   N = L/C <= 16384; 1 <= k <= 16; B*H*L*(k+1) < 2^31.
+ *   Pointers are device pointers, 16-byte aligned, non-overlapping between
+ *   inputs and outputs.  The caller allocates and frees every buffer,
+ *   including the workspace (see hils_workspace_size); the library never
+ *   allocates device memory and keeps no device state between calls.
+ *   Every call validates all arguments on the host before touching the
+ *   device, enqueues its kernels on `stream` (a hipStream_t, NULL = default
+ *   stream) and returns without synchronising; outputs are valid once the
+ *   stream has reached that point.  Faults inside a kernel surface at the
+ *   caller's next synchronisation.  NaN/Inf inputs are not checked; the
+ *   selection they produce is unspecified.  Calls on distinct streams with
+ *   distinct buffers may run concurrently.
+ *   Errors: a non-zero hils_status; hils_last_error() then returns a message
+ *   (per calling thread) describing it.
+ */
+#ifndef HILS_H
+#define HILS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HILS_OK = 0,
+  HILS_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer */
+  HILS_ERR_UNSUPPORTED = 2, /* valid but not implemented (d, C, k, dtype limits) */
+  HILS_ERR_WORKSPACE = 3,   /* workspace missing or smaller than hils_workspace_size */
+  HILS_ERR_HIP = 4          /* the HIP runtime reported an error */
+} hils_status;
+
+typedef enum { HILS_BF16 = 0, HILS_FP32 = 1 } hils_dtype;
+
+/* operation codes for hils_workspace_size */
+enum {
+  HILS_OP_SCORES = 0,
+  HILS_OP_TOPK = 1,
+  HILS_OP_FWD = 2,
+  HILS_OP_DECODE = 3,
+  HILS_OP_BWD = 4
+};
+
+/* Message of the last non-OK status returned to the calling thread ("" if none). */
+const char* hils_last_error(void);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int hils_version(void);
+
+/*
+ * Bytes of workspace the operation needs for these sizes (0 if none; a
+ * null workspace pointer is then accepted).  For HILS_OP_DECODE pass the
+ * cache capacity L_max as L.  Returns 0 and sets hils_last_error for
+ * invalid sizes.
+ */
+size_t hils_workspace_size(int op, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk);
+
+/*
+ * Dense causal landmark scores (first step of the method: ai-feeds summary
+ * "Key modules" item 1; oopus review section 2).
+ *   S[b][h][t][j] = scale * <Q[b][h][t], K_lm[b][h][j]>  for j <= t/C,
+ *                   -inf                                 for j >  t/C.
+ * S: [B][H][L][N] float, written in full.  Materialises B*H*L*N floats:
+ * meant for inspection and tests; the forward never forms this matrix.
+ */
+hils_status hils_landmark_scores(const void* Q, const void* K_lm, float* S, int64_t B, int64_t H, int64_t L,
+                                 int64_t d, int64_t C, float scale, hils_dtype dt, void* stream);
+
+/*
+ * Causal top-k chunk selection fused with the scoring (ai-feeds summary
+ * "Key modules" items 1-2: scores, top-k chunks, chunk-level softmax).
+ * Writes idx, sel_score and (if w is non-null) the fusion weights w for every
+ * query row.  Scores are never materialised.  No workspace.
+ */
+hils_status hils_topk_select(const void* Q, const void* K_lm, int32_t* idx, float* sel_score, float* w,
+                             int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk, float scale,
+                             hils_dtype dt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Forward of the operator (whole method: abstract on the chatpaper page;
+ * ai-feeds summary "Key modules" items 1-3).
+ *   select = 1: compute the selection and write idx and sel_score;
+ *   select = 0: read the caller's idx (same layout; slot k must hold t/C,
+ *               past slots must be distinct chunks < t/C or -1, and the
+ *               valid ones must come first) and write sel_score for it.
+ * O (element type dt) is written for every row.  w_out and lse_out
+ * ([B][H][L][k+1] float) are optional (null = not returned); the backward
+ * pass needs both.  Workspace: hils_workspace_size(HILS_OP_FWD, ...).
+ */
+hils_status hils_sparse_attn_fwd(const void* Q, const void* K, const void* V, const void* K_lm, int32_t* idx,
+                                 float* sel_score, int select, void* O, float* w_out, float* lse_out, int64_t B,
+                                 int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk, float scale,
+                                 hils_dtype dt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One decode step (the per-step landmark scan the ai-feeds summary names
+ * under "Limitations"; the same operator for a single new query per head).
+ *   q, k_new, v_new : [B][H][d] (element type dt)
+ *   K_cache, V_cache: [B][H][L_max][d]; row n_ctx receives k_new / v_new
+ *   K_lm_cache      : [B][H][N_max][d], N_max = ceil(L_max / C); the caller
+ *                     must have written row n_ctx / C (the open chunk's
+ *                     landmark) before the call.
+ * The query at position n_ctx attends over keys 0..n_ctx:  past chunks
+ * j < n_ctx/C are candidates, the open chunk n_ctx/C is its own chunk.
+ * Outputs: o [B][H][d] (dt), idx and w [B][H][k+1] (as in the prefill layout).
+ * 0 <= n_ctx < L_max.  Re-issuing a step with the same n_ctx is idempotent.
+ * Workspace: hils_workspace_size(HILS_OP_DECODE, B, H, L_max, d, C, topk).
+ */
+hils_status hils_decode_step(const void* q, const void* k_new, const void* v_new, void* K_cache, void* V_cache,
+                             const void* K_lm_cache, int64_t n_ctx, int64_t L_max, void* o, int32_t* idx, float* w,
+                             int64_t B, int64_t H, int64_t d, int64_t C, int64_t topk, float scale, hils_dtype dt,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward with the selection held fixed (native sparse training: ai-feeds
+ * summary "Key modules" item 3 and "Output & training"; the retrieval
+ * scores receive gradients through the fusion weights, abstract on the
+ * chatpaper page).  Inputs: the forward's Q, K, V, K_lm, O (dt), upstream
+ * gradient dO (dt), and its idx, w, lse.  Outputs (float, written in full):
+ *   dQ, dK, dV [B][H][L][d];  dK_lm [B][H][N][d].
+ * Workspace: hils_workspace_size(HILS_OP_BWD, ...).
+ */
+hils_status hils_sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* K_lm, const void* O,
+                                 const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
+                                 float* dK, float* dV, float* dK_lm, int64_t B, int64_t H, int64_t L, int64_t d,
+                                 int64_t C, int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HILS_H */

@@ -1,0 +1,320 @@
+// C ABI of libhils: argument validation, workspace carving and kernel launches.
+// Every check runs on the host before any HIP call; see include/hils.h for the
+// contract of each entry point.
+#include "../../include/hils.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "hils_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+hils_status fail(hils_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+hils_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return HILS_OK;
+  return fail(HILS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Dims {
+  int64_t B, H, L, d, C, k, N;
+};
+
+// Shape checks shared by the prefill-shaped entry points.
+hils_status check_dims(int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t k, bool need_k, Dims* out) {
+  if (B < 1 || H < 1) return fail(HILS_ERR_INVALID_ARG, "B and H must be >= 1 (got B=%lld H=%lld)", (long long)B, (long long)H);
+  if (L < 1) return fail(HILS_ERR_INVALID_ARG, "L must be >= 1 (got %lld)", (long long)L);
+  if (C != 64) return fail(HILS_ERR_UNSUPPORTED, "chunk size C must be 64 (got %lld)", (long long)C);
+  if (L % C) return fail(HILS_ERR_INVALID_ARG, "L (%lld) must be a multiple of C (%lld)", (long long)L, (long long)C);
+  if (d != 64 && d != 128) return fail(HILS_ERR_UNSUPPORTED, "head dim d must be 64 or 128 (got %lld)", (long long)d);
+  const int64_t N = L / C;
+  if (N > 16384) return fail(HILS_ERR_UNSUPPORTED, "at most 16384 chunks per sequence (got %lld)", (long long)N);
+  if (need_k && (k < 1 || k > 16)) return fail(HILS_ERR_UNSUPPORTED, "top-k must be in [1, 16] (got %lld)", (long long)k);
+  const int64_t kk = need_k ? k : 0;
+  if (B * H * L * (kk + 1) >= (int64_t(1) << 31) || B * H * L * d >= (int64_t(1) << 40))
+    return fail(HILS_ERR_UNSUPPORTED, "problem too large for 32-bit pair indexing");
+  if (B * H > 65535 * 64) return fail(HILS_ERR_UNSUPPORTED, "B*H too large");
+  *out = Dims{B, H, L, d, C, kk, N};
+  return HILS_OK;
+}
+
+hils_status check_dt(int dt) {
+  if (dt != HILS_BF16 && dt != HILS_FP32) return fail(HILS_ERR_INVALID_ARG, "unknown element type %d", dt);
+  return HILS_OK;
+}
+
+#define REQUIRE_PTR(p)                                                                          \
+  do {                                                                                          \
+    if (!(p)) return fail(HILS_ERR_INVALID_ARG, "%s must not be null", #p);                     \
+    if (!aligned16(p)) return fail(HILS_ERR_INVALID_ARG, "%s must be 16-byte aligned", #p);      \
+  } while (0)
+#define OPTIONAL_PTR(p)                                                                         \
+  do {                                                                                          \
+    if ((p) && !aligned16(p)) return fail(HILS_ERR_INVALID_ARG, "%s must be 16-byte aligned", #p); \
+  } while (0)
+
+// Workspace carving: a bump allocator over the caller's buffer.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <typename T> T* take(size_t count) {
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+struct FwdWs {
+  hils::RouteBufs rb;
+  uint16_t* partial;
+  float* w_tmp;
+  float* lse_tmp;
+};
+
+size_t carve_route(Carver& cv, const Dims& D, hils::RouteBufs& rb, int ppi) {
+  const int64_t BH = D.B * D.H;
+  rb.nseg = hils::route_nseg((int)D.L);
+  rb.seg_q = 1024;
+  rb.pairs_per_item = ppi;
+  rb.max_items = hils::route_max_items((int)D.L, (int)D.N, (int)D.k, ppi);
+  rb.counts = cv.take<int>((size_t)BH * rb.nseg * D.N);
+  rb.chunk_off = cv.take<int>((size_t)BH * (D.N + 1));
+  rb.items = cv.take<int2>((size_t)BH * rb.max_items);
+  rb.n_items = cv.take<int>((size_t)BH);
+  rb.pairs = cv.take<int>((size_t)BH * D.L * D.k);
+  return cv.off;
+}
+
+size_t carve_fwd(void* base, const Dims& D, FwdWs* ws) {
+  Carver cv(base);
+  const int64_t BH = D.B * D.H;
+  carve_route(cv, D, ws->rb, hils::FWD_PAIRS_PER_ITEM);
+  ws->partial = cv.take<uint16_t>((size_t)BH * D.L * D.k * D.d);
+  ws->w_tmp = cv.take<float>((size_t)BH * D.L * (D.k + 1));
+  ws->lse_tmp = cv.take<float>((size_t)BH * D.L * (D.k + 1));
+  return cv.off;
+}
+
+size_t carve_bwd(void* base, const Dims& D, hils::BwdBufs* ws) {
+  Carver cv(base);
+  const int64_t BH = D.B * D.H;
+  ws->Dt = cv.take<float>((size_t)BH * D.L);
+  carve_route(cv, D, ws->rb, hils::FWD_PAIRS_PER_ITEM);
+  ws->dq_part = cv.take<float>((size_t)BH * D.L * (D.k + 1) * D.d);
+  return cv.off;
+}
+
+size_t carve_decode(void* base, int64_t BH, int64_t Lmax, int64_t d, int64_t k, hils::DecodeBufs* ws) {
+  Carver cv(base);
+  ws->cand = cv.take<uint64_t>((size_t)BH * hils::decode_slices(Lmax - 1) * 16 + 16);
+  ws->part = cv.take<float>((size_t)BH * (k + 1) * d);
+  ws->ticket = cv.take<int>((size_t)BH);
+  return cv.off;
+}
+
+hils_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return HILS_OK;
+  if (!ws) return fail(HILS_ERR_WORKSPACE, "workspace of %zu bytes required, got null", need);
+  if (!aligned16(ws)) return fail(HILS_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (ws_bytes < need) return fail(HILS_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  return HILS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hils_last_error(void) { return g_err; }
+
+int hils_version(void) { return 10000; }
+
+size_t hils_workspace_size(int op, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk) {
+  Dims D;
+  g_err[0] = 0;
+  switch (op) {
+    case HILS_OP_SCORES:
+    case HILS_OP_TOPK:
+      return 0;
+    case HILS_OP_FWD: {
+      if (check_dims(B, H, L, d, C, topk, true, &D) != HILS_OK) return 0;
+      FwdWs ws;
+      return carve_fwd(nullptr, D, &ws);
+    }
+    case HILS_OP_BWD: {
+      if (check_dims(B, H, L, d, C, topk, true, &D) != HILS_OK) return 0;
+      hils::BwdBufs ws;
+      return carve_bwd(nullptr, D, &ws);
+    }
+    case HILS_OP_DECODE: {
+      if (check_dims(B, H, ((L + C - 1) / (C > 0 ? C : 1)) * (C > 0 ? C : 1), d, C, topk, true, &D) != HILS_OK)
+        return 0;
+      hils::DecodeBufs ws;
+      return carve_decode(nullptr, B * H, L, d, topk, &ws);
+    }
+    default:
+      fail(HILS_ERR_INVALID_ARG, "unknown operation code %d", op);
+      return 0;
+  }
+}
+
+hils_status hils_landmark_scores(const void* Q, const void* K_lm, float* S, int64_t B, int64_t H, int64_t L,
+                                 int64_t d, int64_t C, float scale, hils_dtype dt, void* stream) {
+  Dims D;
+  hils_status st;
+  if ((st = check_dims(B, H, L, d, C, 0, false, &D)) != HILS_OK) return st;
+  if ((st = check_dt(dt)) != HILS_OK) return st;
+  REQUIRE_PTR(Q);
+  REQUIRE_PTR(K_lm);
+  REQUIRE_PTR(S);
+  if (!(scale > 0.f)) return fail(HILS_ERR_INVALID_ARG, "scale must be positive");
+  if (B * H * L * D.N >= (int64_t(1) << 40)) return fail(HILS_ERR_UNSUPPORTED, "score matrix too large");
+  return hip_status(hils::launch_landmark_scores(dt, (int)d, Q, K_lm, S, (int)(B * H), (int)L, (int)D.N, scale,
+                                                 (hipStream_t)stream),
+                    "hils_landmark_scores");
+}
+
+hils_status hils_topk_select(const void* Q, const void* K_lm, int32_t* idx, float* sel_score, float* w, int64_t B,
+                             int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk, float scale, hils_dtype dt,
+                             void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  Dims D;
+  hils_status st;
+  if ((st = check_dims(B, H, L, d, C, topk, true, &D)) != HILS_OK) return st;
+  if ((st = check_dt(dt)) != HILS_OK) return st;
+  REQUIRE_PTR(Q);
+  REQUIRE_PTR(K_lm);
+  REQUIRE_PTR(idx);
+  REQUIRE_PTR(sel_score);
+  OPTIONAL_PTR(w);
+  if (!(scale > 0.f)) return fail(HILS_ERR_INVALID_ARG, "scale must be positive");
+  return hip_status(hils::launch_topk(dt, (int)d, Q, K_lm, idx, sel_score, w, (int)(B * H), (int)L, (int)D.N,
+                                      (int)topk, scale, (hipStream_t)stream),
+                    "hils_topk_select");
+}
+
+hils_status hils_sparse_attn_fwd(const void* Q, const void* K, const void* V, const void* K_lm, int32_t* idx,
+                                 float* sel_score, int select, void* O, float* w_out, float* lse_out, int64_t B,
+                                 int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk, float scale,
+                                 hils_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+  Dims D;
+  hils_status st;
+  if ((st = check_dims(B, H, L, d, C, topk, true, &D)) != HILS_OK) return st;
+  if ((st = check_dt(dt)) != HILS_OK) return st;
+  REQUIRE_PTR(Q);
+  REQUIRE_PTR(K);
+  REQUIRE_PTR(V);
+  REQUIRE_PTR(K_lm);
+  REQUIRE_PTR(idx);
+  REQUIRE_PTR(sel_score);
+  REQUIRE_PTR(O);
+  OPTIONAL_PTR(w_out);
+  OPTIONAL_PTR(lse_out);
+  if (select != 0 && select != 1) return fail(HILS_ERR_INVALID_ARG, "select must be 0 or 1");
+  if (!(scale > 0.f)) return fail(HILS_ERR_INVALID_ARG, "scale must be positive");
+  FwdWs W;
+  const size_t need = carve_fwd(nullptr, D, &W);
+  if ((st = check_ws(ws, ws_bytes, need)) != HILS_OK) return st;
+  carve_fwd(ws, D, &W);
+  const int BH = (int)(B * H), iL = (int)L, iN = (int)D.N, ik = (int)topk, id = (int)d;
+  hipStream_t s = (hipStream_t)stream;
+  float* w = w_out ? w_out : W.w_tmp;
+  hipError_t e;
+  if (select) e = hils::launch_topk(dt, id, Q, K_lm, idx, sel_score, w, BH, iL, iN, ik, scale, s);
+  else e = hils::launch_fixed_selection(dt, id, Q, K_lm, idx, sel_score, w, BH, iL, iN, ik, scale, s);
+  if (e != hipSuccess) return hip_status(e, "hils_sparse_attn_fwd: selection");
+  if ((e = hils::launch_route(idx, W.rb, BH, iL, iN, ik, s)) != hipSuccess)
+    return hip_status(e, "hils_sparse_attn_fwd: routing");
+  if ((e = hils::launch_chunk_attn_fwd(dt, id, Q, K, V, W.rb, w, lse_out, W.partial, BH, iL, iN, ik, scale, s)) !=
+      hipSuccess)
+    return hip_status(e, "hils_sparse_attn_fwd: chunk attention");
+  if ((e = hils::launch_own_combine(dt, id, Q, K, V, idx, w, W.partial, O, lse_out, BH, iL, iN, ik, scale, s)) !=
+      hipSuccess)
+    return hip_status(e, "hils_sparse_attn_fwd: own chunk and fusion");
+  return HILS_OK;
+}
+
+hils_status hils_decode_step(const void* q, const void* k_new, const void* v_new, void* K_cache, void* V_cache,
+                             const void* K_lm_cache, int64_t n_ctx, int64_t L_max, void* o, int32_t* idx, float* w,
+                             int64_t B, int64_t H, int64_t d, int64_t C, int64_t topk, float scale, hils_dtype dt,
+                             void* ws, size_t ws_bytes, void* stream) {
+  Dims D;
+  hils_status st;
+  if (L_max < 1) return fail(HILS_ERR_INVALID_ARG, "L_max must be >= 1 (got %lld)", (long long)L_max);
+  if (C != 64) return fail(HILS_ERR_UNSUPPORTED, "chunk size C must be 64 (got %lld)", (long long)C);
+  const int64_t Nmax = (L_max + C - 1) / C;
+  if ((st = check_dims(B, H, Nmax * C, d, C, topk, true, &D)) != HILS_OK) return st;
+  if ((st = check_dt(dt)) != HILS_OK) return st;
+  if (n_ctx < 0 || n_ctx >= L_max)
+    return fail(HILS_ERR_INVALID_ARG, "n_ctx (%lld) must be in [0, L_max=%lld)", (long long)n_ctx, (long long)L_max);
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k_new);
+  REQUIRE_PTR(v_new);
+  REQUIRE_PTR(K_cache);
+  REQUIRE_PTR(V_cache);
+  REQUIRE_PTR(K_lm_cache);
+  REQUIRE_PTR(o);
+  REQUIRE_PTR(idx);
+  REQUIRE_PTR(w);
+  if (!(scale > 0.f)) return fail(HILS_ERR_INVALID_ARG, "scale must be positive");
+  hils::DecodeBufs W;
+  const size_t need = carve_decode(nullptr, B * H, L_max, d, topk, &W);
+  if ((st = check_ws(ws, ws_bytes, need)) != HILS_OK) return st;
+  carve_decode(ws, B * H, L_max, d, topk, &W);
+  return hip_status(hils::launch_decode(dt, (int)d, q, k_new, v_new, K_cache, V_cache, K_lm_cache, n_ctx, L_max, Nmax,
+                                        o, idx, w, (int)(B * H), (int)topk, scale, W, (hipStream_t)stream),
+                    "hils_decode_step");
+}
+
+hils_status hils_sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* K_lm, const void* O,
+                                 const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
+                                 float* dK, float* dV, float* dK_lm, int64_t B, int64_t H, int64_t L, int64_t d,
+                                 int64_t C, int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  Dims D;
+  hils_status st;
+  if ((st = check_dims(B, H, L, d, C, topk, true, &D)) != HILS_OK) return st;
+  if ((st = check_dt(dt)) != HILS_OK) return st;
+  if (dt == HILS_FP32 && d != 64) return fail(HILS_ERR_UNSUPPORTED, "fp32 backward supports head dim 64 only");
+  REQUIRE_PTR(Q);
+  REQUIRE_PTR(K);
+  REQUIRE_PTR(V);
+  REQUIRE_PTR(K_lm);
+  REQUIRE_PTR(O);
+  REQUIRE_PTR(dO);
+  REQUIRE_PTR(idx);
+  REQUIRE_PTR(w);
+  REQUIRE_PTR(lse);
+  REQUIRE_PTR(dQ);
+  REQUIRE_PTR(dK);
+  REQUIRE_PTR(dV);
+  REQUIRE_PTR(dK_lm);
+  if (!(scale > 0.f)) return fail(HILS_ERR_INVALID_ARG, "scale must be positive");
+  hils::BwdBufs W;
+  const size_t need = carve_bwd(nullptr, D, &W);
+  if ((st = check_ws(ws, ws_bytes, need)) != HILS_OK) return st;
+  carve_bwd(ws, D, &W);
+  return hip_status(hils::launch_bwd(dt, (int)d, Q, K, V, K_lm, O, dO, idx, w, lse, dQ, dK, dV, dK_lm, (int)(B * H),
+                                     (int)L, (int)D.N, (int)topk, scale, W, (hipStream_t)stream),
+                    "hils_sparse_attn_bwd");
+}
+
+}  // extern "C"

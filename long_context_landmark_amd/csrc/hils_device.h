@@ -1,0 +1,194 @@
+// Device-side building blocks shared by the HiLS kernels (gfx950 / CDNA4).
+//
+// Operand fragments follow the 16x16x32 bf16 MFMA lane layout of gfx950:
+// lane l feeds row (A) / column (B) l%16 and the eight consecutive k-elements
+// 8*(l/16) .. 8*(l/16)+7 of a 32-wide k block; the 4 accumulator values of
+// lane l are rows 4*(l/16)+i, column l%16.  An fp32 fragment holds the same
+// eight k-elements and is consumed by eight 16x16x4 fp32 MFMAs, so callers see
+// one layout for both element types.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hils {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
+
+struct bf16_t {  // storage type of a bf16 element
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite in this library)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<bf16_t> {
+  static constexpr int bytes = 2;
+  __device__ static float to_f32(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i].bits); }
+  __device__ static void store(bf16_t* p, int64_t i, float v) { p[i].bits = f32_to_bf16(v); }
+};
+template <> struct Elem<float> {
+  static constexpr int bytes = 4;
+  __device__ static float to_f32(const float* p, int64_t i) { return p[i]; }
+  __device__ static void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+
+// Eight consecutive k-elements of one row, as one MFMA operand fragment.
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> {
+  bf16x8_t v;
+  __device__ __forceinline__ void zero() {
+    u16x8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
+    v = __builtin_bit_cast(bf16x8_t, z);
+  }
+  // 16-byte aligned load of 8 consecutive elements
+  __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const bf16x8_t*>(p); }
+  // elements e=0..3 from p0, e=4..7 from p1 (each 8-byte aligned)
+  __device__ __forceinline__ void load4x2(const bf16_t* p0, const bf16_t* p1) {
+    u16x4_t a = *reinterpret_cast<const u16x4_t*>(p0);
+    u16x4_t b = *reinterpret_cast<const u16x4_t*>(p1);
+    u16x8_t c = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    v = __builtin_bit_cast(bf16x8_t, c);
+  }
+  __device__ __forceinline__ void set(const float (&f)[8]) {
+    u16x8_t c;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = f32_to_bf16(f[e]);
+    v = __builtin_bit_cast(bf16x8_t, c);
+  }
+  __device__ __forceinline__ float get(int e) const {
+    u16x8_t c = __builtin_bit_cast(u16x8_t, v);
+    return bf16_to_f32(c[e]);
+  }
+};
+template <> struct Frag<float> {
+  float v[8];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+  }
+  __device__ __forceinline__ void load(const float* p) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+    float4 a = q[0], b = q[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ __forceinline__ void load4x2(const float* p0, const float* p1) {
+    float4 a = *reinterpret_cast<const float4*>(p0);
+    float4 b = *reinterpret_cast<const float4*>(p1);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ __forceinline__ void set(const float (&f)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = f[e];
+  }
+  __device__ __forceinline__ float get(int e) const { return v[e]; }
+};
+
+// acc += A(16x32) * B(32x16) for one k block
+__device__ __forceinline__ void mma(f32x4_t& acc, const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4_t& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t zero4() {
+  f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+  return z;
+}
+
+// ---------------------------------------------------------------------------
+// Selection keys: a 64-bit integer whose unsigned order is the selection order
+// (higher fp32 score first, lower chunk index on equal scores).
+__device__ __forceinline__ uint32_t ordered_bits(float s) {
+  uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unordered_float(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ uint64_t make_key(float s, int32_t j) {
+  s = s + 0.0f;  // -0 and +0 compare equal as scores; give them one key
+  return ((uint64_t)ordered_bits(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
+}
+__device__ __forceinline__ int32_t key_index(uint64_t key) { return (int32_t)(0xFFFFFFFFu - (uint32_t)key); }
+__device__ __forceinline__ float key_score(uint64_t key) { return unordered_float((uint32_t)(key >> 32)); }
+
+template <typename K> __device__ __forceinline__ void cmpswap_desc(K& a, K& b) {
+  K hi = a > b ? a : b;
+  K lo = a > b ? b : a;
+  a = hi;
+  b = lo;
+}
+
+// Sort 16 values descending in registers (bitonic network, fully unrolled).
+template <typename K> __device__ __forceinline__ void sort16_desc(K (&a)[16]) {
+#pragma unroll
+  for (int size = 2; size <= 16; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        int p = i ^ stride;
+        if (p > i) {
+          bool desc = (i & size) == 0;
+          if (desc) cmpswap_desc(a[i], a[p]);
+          else cmpswap_desc(a[p], a[i]);
+        }
+      }
+    }
+  }
+}
+
+// a is bitonic; sort it descending.
+template <typename K> __device__ __forceinline__ void bitonic_merge16_desc(K (&a)[16]) {
+#pragma unroll
+  for (int stride = 8; stride > 0; stride >>= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      int p = i ^ stride;
+      if (p > i) cmpswap_desc(a[i], a[p]);
+    }
+  }
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = (uint32_t)__shfl_xor((int)lo, mask);
+  hi = (uint32_t)__shfl_xor((int)hi, mask);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask); }
+__device__ __forceinline__ uint64_t shfl_xor_any(uint64_t v, int m) { return shfl_xor_u64(v, m); }
+__device__ __forceinline__ float shfl_xor_any(float v, int m) { return shfl_xor_f(v, m); }
+
+// Lanes l and l^mask each hold a descending list of 16; afterwards both hold the
+// 16 largest of the union, descending.
+template <typename K> __device__ __forceinline__ void merge16_with_lane(K (&a)[16], int mask) {
+  K b[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) b[i] = shfl_xor_any(a[i], mask);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a[i] = a[i] > b[15 - i] ? a[i] : b[15 - i];
+  bitonic_merge16_desc(a);
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int from_mask, int to_mask) {
+  for (int m = from_mask; m <= to_mask; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+}  // namespace hils

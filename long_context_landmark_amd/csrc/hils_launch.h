@@ -1,0 +1,59 @@
+// Host-side launchers of the HiLS kernels (internal to the library).
+// Element type code: 0 = bf16, 1 = fp32.  All launches are asynchronous on
+// the given stream and return the launch status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hils {
+
+hipError_t launch_landmark_scores(int dt, int d, const void* Q, const void* Klm, float* S, int BH, int L, int N,
+                                  float scale, hipStream_t st);
+hipError_t launch_topk(int dt, int d, const void* Q, const void* Klm, int32_t* idx, float* sel, float* w, int BH,
+                       int L, int N, int k, float scale, hipStream_t st);
+// scores and weights of a caller-given selection (slots with idx < 0 are unused)
+hipError_t launch_fixed_selection(int dt, int d, const void* Q, const void* Klm, const int32_t* idx, float* sel,
+                                  float* w, int BH, int L, int N, int k, float scale, hipStream_t st);
+
+// routing inversion: per (b,h) and chunk j, the list of (query, slot) pairs whose selection holds j
+struct RouteBufs {
+  int* counts;     // [BH][nseg][N]: per-segment counts, then per-segment offsets
+  int* chunk_off;  // [BH][N+1]
+  int2* items;     // [BH][max_items]: (chunk, part) work items of the chunk-major kernels
+  int* n_items;    // [BH]
+  int* pairs;      // [BH][L*k]: (t << 5) | slot, grouped by chunk, ascending (t, slot) inside a chunk
+  int nseg, seg_q, max_items, pairs_per_item;
+};
+int route_nseg(int L);
+int route_max_items(int L, int N, int k, int pairs_per_item);
+hipError_t launch_route(const int32_t* idx, const RouteBufs& rb, int BH, int L, int N, int k, hipStream_t st);
+
+hipError_t launch_chunk_attn_fwd(int dt, int d, const void* Q, const void* K, const void* V, const RouteBufs& rb,
+                                 const float* w, float* lse, uint16_t* partial, int BH, int L, int N, int k,
+                                 float scale, hipStream_t st);
+hipError_t launch_own_combine(int dt, int d, const void* Q, const void* K, const void* V, const int32_t* idx,
+                              const float* w, const uint16_t* partial, void* O, float* lse, int BH, int L, int N, int k, float scale,
+                              hipStream_t st);
+constexpr int FWD_PAIRS_PER_ITEM = 256;
+
+struct DecodeBufs {
+  uint64_t* cand;  // [BH][slices][16] sorted slice top-16 keys
+  float* part;     // [BH][k+1][d] weighted per-chunk partial outputs
+  int* ticket;     // [BH] arrival counters (reset by every step)
+};
+int decode_slices(int64_t n_ctx);
+
+struct BwdBufs {
+  float* Dt;       // [BH][L] dO_t . O_t
+  RouteBufs rb;
+  float* dq_part;  // [BH][L][k+1][d] dQ contribution of every (query, slot)
+};
+hipError_t launch_bwd(int dt, int d, const void* Q, const void* K, const void* V, const void* Klm, const void* O,
+                      const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ, float* dK,
+                      float* dV, float* dKlm, int BH, int L, int N, int k, float scale, const BwdBufs& ws,
+                      hipStream_t st);
+hipError_t launch_decode(int dt, int d, const void* q, const void* k_new, const void* v_new, void* Kc, void* Vc,
+                         const void* Klm, int64_t n, int64_t Lmax, int64_t Nmax, void* o, int32_t* idx, float* w,
+                         int BH, int k, float scale, const DecodeBufs& ws, hipStream_t st);
+
+}  // namespace hils

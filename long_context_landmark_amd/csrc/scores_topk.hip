@@ -1,0 +1,319 @@
+// Landmark scoring and causal top-k chunk selection (HiLS attention, step 1-2).
+//
+// Passages defining the operation:
+//   "Hierarchical Sparse Attention Done Right" (ai-feeds summary), section
+//   "Method" > "Key modules" item 1 (each query scores the chunks through
+//   their landmark representation; chunk-level softmax gives the retrieval
+//   weights) and item 2 (the query keeps the top-k chunks);
+//   paper.oopus.info review, section 2 (one landmark token per chunk scored by
+//   the current query; the highest scoring chunks are read in detail).
+// Fixed here: score = scale * <q_t, Klm_j> with scale = 1/sqrt(d) by default;
+// candidates of query t are the completed past chunks j < t/64; ties go to
+// the lower chunk index; the own chunk t/64 is always added, scored by its
+// own landmark, and not counted in k.
+//
+// Scores are a dense contraction Q . Klm^T, so they run on bf16 MFMA with
+// fp32 accumulation.  Selection never materialises the score matrix: a first
+// sweep keeps, per query, the running maximum of each of 64 residue groups
+// (chunk index mod 64).  The m-th largest of those maxima is a lower bound on
+// the m-th largest score (the maxima are m distinct candidates), so a second
+// sweep, which recomputes bit-identical scores, only has to keep candidates at
+// or above it.  The exact top-m is then sorted out of the few survivors.  A
+// query with more survivors than fit in LDS (possible only with many exactly
+// tied scores) falls back to m exact arg-max sweeps.
+#include "hils_device.h"
+#include "hils_launch.h"
+
+namespace hils {
+
+// ----------------------------------------------------------------------------
+// Dense causal scores S[b,h,t,j] (fp32; -inf for j > t/64).  One workgroup per
+// 64 queries x 64 chunks; wave w takes the 16-chunk block w of the tile and all
+// 64 queries (4 column blocks), matching the selection kernel's arithmetic.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void landmark_scores_kernel(const T* __restrict__ Q, const T* __restrict__ Klm,
+                                                              float* __restrict__ S, int L, int N, float scale) {
+  const int bh = blockIdx.z;
+  const int t0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
+  const T* Qb = Q + (int64_t)bh * L * D;
+  const T* Kb = Klm + (int64_t)bh * N * D;
+  const int jrow = j0 + 16 * w + r16;
+  f32x4_t acc[4];
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb) acc[qb] = zero4();
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    Frag<T> a;
+    if (jrow < N) a.load(Kb + (int64_t)jrow * D + ks * 32 + 8 * g);
+    else a.zero();
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const int tq = t0 + 16 * qb + r16;
+      Frag<T> b;
+      if (tq < L) b.load(Qb + (int64_t)tq * D + ks * 32 + 8 * g);
+      else b.zero();
+      mma(acc[qb], a, b);
+    }
+  }
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb) {
+    const int t = t0 + 16 * qb + r16;
+    if (t >= L) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + 16 * w + 4 * g + i;
+      if (j < N) S[((int64_t)bh * L + t) * N + j] = (j <= t / 64) ? scale * acc[qb][i] : -INFINITY;
+    }
+  }
+}
+
+constexpr int TK_CAP = 64;  // survivor slots per query (16 per sorting lane)
+
+// One workgroup per (b,h, query chunk c): the 64 queries t = 64c .. 64c+63
+// share the candidate set {0..c-1}.  Wave w scores the 16-chunk block w of
+// every 64-chunk landmark tile against all 64 queries.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void topk_select_kernel(const T* __restrict__ Q, const T* __restrict__ Klm,
+                                                          int32_t* __restrict__ idx, float* __restrict__ sel,
+                                                          float* __restrict__ wout, int L, int N, int k,
+                                                          float scale) {
+  const int nc = L / 64;
+  const int c = nc - 1 - (int)blockIdx.x;  // longest candidate lists first
+  const int bh = blockIdx.y;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
+  const int m = min(k, c);
+  const int k1 = k + 1;
+  const T* Qb = Q + ((int64_t)bh * L + (int64_t)c * 64) * D;
+  const T* Kb = Klm + (int64_t)bh * N * D;
+
+  __shared__ float gmax_s[64][65];
+  __shared__ uint64_t surv[64][TK_CAP];
+  __shared__ uint64_t top_s[64][16];
+  __shared__ int cnt_s[64];
+  __shared__ float tau_s[64];
+  __shared__ int ovf_s;
+
+  Frag<T> qf[4][D / 32];
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) qf[qb][ks].load(Qb + (int64_t)(16 * qb + r16) * D + ks * 32 + 8 * g);
+
+  const int ntile = (c + 63) / 64;
+  // scores of chunks tile*64 + 16w + 4g + i (i = 0..3) for queries 16qb + r16
+  auto score_tile = [&](int tile, f32x4_t(&acc)[4]) {
+    const int jrow = tile * 64 + 16 * w + r16;
+    Frag<T> a[D / 32];
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      if (jrow < c) a[ks].load(Kb + (int64_t)jrow * D + ks * 32 + 8 * g);
+      else a[ks].zero();
+    }
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      acc[qb] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) mma(acc[qb], a[ks], qf[qb][ks]);
+    }
+  };
+
+  if (tid == 0) ovf_s = 0;
+  if (tid < 64) cnt_s[tid] = 0;
+
+  if (m > 0) {
+    // sweep 1: per-group running maxima
+    float gm[4][4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gm[qb][i] = -INFINITY;
+    for (int tile = 0; tile < ntile; ++tile) {
+      f32x4_t acc[4];
+      score_tile(tile, acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = tile * 64 + 16 * w + 4 * g + i;
+        if (j < c) {
+#pragma unroll
+          for (int qb = 0; qb < 4; ++qb) gm[qb][i] = fmaxf(gm[qb][i], scale * acc[qb][i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gmax_s[16 * qb + r16][16 * w + 4 * g + i] = gm[qb][i];
+    __syncthreads();
+    {
+      const int q = tid >> 2, part = tid & 3;
+      float v[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = gmax_s[q][16 * part + e];
+      sort16_desc(v);
+      merge16_with_lane(v, 1);
+      merge16_with_lane(v, 2);
+      float tau = v[0];
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (e == m - 1) tau = v[e];
+      if (part == 0) tau_s[q] = tau;
+    }
+    __syncthreads();
+    // sweep 2: keep candidates at or above the bound
+    float tau_r[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) tau_r[qb] = tau_s[16 * qb + r16];
+    for (int tile = 0; tile < ntile; ++tile) {
+      f32x4_t acc[4];
+      score_tile(tile, acc);
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = tile * 64 + 16 * w + 4 * g + i;
+          const float s = scale * acc[qb][i];
+          if (j < c && s >= tau_r[qb]) {
+            const int q = 16 * qb + r16;
+            const int p = atomicAdd(&cnt_s[q], 1);
+            if (p < TK_CAP) surv[q][p] = make_key(s, j);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // exact top-m among the survivors: 4 lanes per query, 16 slots each
+    {
+      const int q = tid >> 2, part = tid & 3;
+      const int n = cnt_s[q];
+      uint64_t v[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int p = 16 * part + e;
+        v[e] = (p < n && p < TK_CAP) ? surv[q][p] : 0ull;
+      }
+      sort16_desc(v);
+      merge16_with_lane(v, 1);
+      merge16_with_lane(v, 2);
+      if (part == 0) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) top_s[q][e] = v[e];
+        if (n > TK_CAP) atomicOr(&ovf_s, 1);
+      }
+    }
+    __syncthreads();
+    if (ovf_s) {
+      // exact fallback: for each rank, the largest key below the previous one
+      __shared__ uint64_t best_s[64];
+      __shared__ uint64_t prev_s[64];
+      __shared__ int redo_s[64];
+      if (tid < 64) {
+        redo_s[tid] = cnt_s[tid] > TK_CAP;
+        prev_s[tid] = ~0ull;
+      }
+      __syncthreads();
+      for (int r = 0; r < m; ++r) {
+        if (tid < 64) best_s[tid] = 0ull;
+        __syncthreads();
+        for (int tile = 0; tile < ntile; ++tile) {
+          f32x4_t acc[4];
+          score_tile(tile, acc);
+#pragma unroll
+          for (int qb = 0; qb < 4; ++qb) {
+            const int q = 16 * qb + r16;
+            if (!redo_s[q]) continue;
+            const uint64_t prev = prev_s[q];
+            uint64_t best = 0ull;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int j = tile * 64 + 16 * w + 4 * g + i;
+              if (j < c) {
+                const uint64_t key = make_key(scale * acc[qb][i], j);
+                if (key < prev && key > best) best = key;
+              }
+            }
+            if (best) atomicMax((unsigned long long*)&best_s[q], (unsigned long long)best);
+          }
+        }
+        __syncthreads();
+        if (tid < 64 && redo_s[tid]) {
+          top_s[tid][r] = best_s[tid];
+          prev_s[tid] = best_s[tid];
+        }
+        __syncthreads();
+      }
+    }
+  }
+  __syncthreads();
+
+  // own-chunk score (VALU dot, 4 lanes per query), fusion weights, outputs
+  {
+    const int q = tid >> 2, part = tid & 3;
+    const T* qrow = Qb + (int64_t)q * D;
+    const T* lrow = Kb + (int64_t)c * D;
+    float dot = 0.f;
+    for (int e = part * (D / 4); e < (part + 1) * (D / 4); ++e) dot += Elem<T>::to_f32(qrow, e) * Elem<T>::to_f32(lrow, e);
+    dot += __shfl_xor(dot, 1);
+    dot += __shfl_xor(dot, 2);
+    const float s_own = scale * dot;
+    if (part == 0) {
+      const int64_t row = ((int64_t)bh * L + (int64_t)c * 64 + q) * k1;
+      float mx = s_own;
+      for (int r = 0; r < m; ++r) mx = fmaxf(mx, key_score(top_s[q][r]));
+      float den = __expf(s_own - mx);
+      for (int r = 0; r < m; ++r) den += __expf(key_score(top_s[q][r]) - mx);
+      const float inv = 1.f / den;
+      for (int r = 0; r < k; ++r) {
+        if (r < m) {
+          const float s = key_score(top_s[q][r]);
+          idx[row + r] = key_index(top_s[q][r]);
+          sel[row + r] = s;
+          if (wout) wout[row + r] = __expf(s - mx) * inv;
+        } else {
+          idx[row + r] = -1;
+          sel[row + r] = -INFINITY;
+          if (wout) wout[row + r] = 0.f;
+        }
+      }
+      idx[row + k] = c;
+      sel[row + k] = s_own;
+      if (wout) wout[row + k] = __expf(s_own - mx) * inv;
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_landmark_scores_t(const void* Q, const void* Klm, float* S, int BH, int L, int N, float scale,
+                                    hipStream_t st) {
+  dim3 grid((L + 63) / 64, (N + 63) / 64, BH);
+  hipLaunchKernelGGL((landmark_scores_kernel<T, D>), grid, dim3(256), 0, st, (const T*)Q, (const T*)Klm, S, L, N,
+                     scale);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_topk_t(const void* Q, const void* Klm, int32_t* idx, float* sel, float* w, int BH, int L, int N,
+                         int k, float scale, hipStream_t st) {
+  dim3 grid(L / 64, BH);
+  hipLaunchKernelGGL((topk_select_kernel<T, D>), grid, dim3(256), 0, st, (const T*)Q, (const T*)Klm, idx, sel, w, L,
+                     N, k, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_landmark_scores(int dt, int d, const void* Q, const void* Klm, float* S, int BH, int L, int N,
+                                  float scale, hipStream_t st) {
+  if (dt == 0) return d == 64 ? launch_landmark_scores_t<bf16_t, 64>(Q, Klm, S, BH, L, N, scale, st)
+                              : launch_landmark_scores_t<bf16_t, 128>(Q, Klm, S, BH, L, N, scale, st);
+  return d == 64 ? launch_landmark_scores_t<float, 64>(Q, Klm, S, BH, L, N, scale, st)
+                 : launch_landmark_scores_t<float, 128>(Q, Klm, S, BH, L, N, scale, st);
+}
+
+hipError_t launch_topk(int dt, int d, const void* Q, const void* Klm, int32_t* idx, float* sel, float* w, int BH,
+                       int L, int N, int k, float scale, hipStream_t st) {
+  if (dt == 0) return d == 64 ? launch_topk_t<bf16_t, 64>(Q, Klm, idx, sel, w, BH, L, N, k, scale, st)
+                              : launch_topk_t<bf16_t, 128>(Q, Klm, idx, sel, w, BH, L, N, k, scale, st);
+  return d == 64 ? launch_topk_t<float, 64>(Q, Klm, idx, sel, w, BH, L, N, k, scale, st)
+                 : launch_topk_t<float, 128>(Q, Klm, idx, sel, w, BH, L, N, k, scale, st);
+}
+
+}  // namespace hils

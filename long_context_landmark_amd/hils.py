@@ -1,0 +1,189 @@
+"""Thin Python binding of libhils (ctypes over the C ABI in include/hils.h).
+
+Argument marshalling only: every step of the operator runs in the library's
+HIP kernels.  Tensors are torch tensors on the current HIP device; the
+library call is enqueued on torch's current stream.  If the built library is
+missing this module raises at import: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhils.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libhils.so not found at {LIB_PATH}; build it with "
+                      f"`python -m long_context_landmark_amd.build` (or __graft_entry__.build())")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_i64, _f, _vp, _int, _sz = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+
+_lib.hils_last_error.restype = ctypes.c_char_p
+_lib.hils_version.restype = _int
+_lib.hils_workspace_size.argtypes = [_int, _i64, _i64, _i64, _i64, _i64, _i64]
+_lib.hils_workspace_size.restype = _sz
+_lib.hils_landmark_scores.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f, _int, _vp]
+_lib.hils_topk_select.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _f, _int, _vp, _sz,
+                                  _vp]
+_lib.hils_sparse_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                      _i64, _i64, _f, _int, _vp, _sz, _vp]
+_lib.hils_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                  _i64, _f, _int, _vp, _sz, _vp]
+_lib.hils_sparse_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
+                                      _i64, _i64, _i64, _i64, _f, _int, _vp, _sz, _vp]
+for _fn in ("hils_landmark_scores", "hils_topk_select", "hils_sparse_attn_fwd", "hils_decode_step",
+            "hils_sparse_attn_bwd"):
+    getattr(_lib, _fn).restype = _int
+
+OP_SCORES, OP_TOPK, OP_FWD, OP_DECODE, OP_BWD = range(5)
+BF16, FP32 = 0, 1
+
+EXPORTS = ("hils_last_error", "hils_version", "hils_workspace_size", "hils_landmark_scores", "hils_topk_select",
+           "hils_sparse_attn_fwd", "hils_decode_step", "hils_sparse_attn_bwd")
+
+
+class HilsError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libhils status {status}: {msg}")
+        self.status = status
+
+
+def _check(status: int):
+    if status != 0:
+        raise HilsError(status, _lib.hils_last_error().decode())
+
+
+def version() -> int:
+    return _lib.hils_version()
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _scale(d, scale):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def workspace_size(op: int, B, H, L, d, C, k) -> int:
+    n = _lib.hils_workspace_size(op, B, H, L, d, C, k)
+    err = _lib.hils_last_error().decode()
+    if n == 0 and err:
+        raise HilsError(1, err)
+    return n
+
+
+def _workspace(op, B, H, L, d, C, k, device, ws=None):
+    n = workspace_size(op, B, H, L, d, C, k)
+    if n == 0:
+        return None, 0
+    if ws is not None:
+        if ws.numel() < n:
+            raise ValueError(f"workspace of {ws.numel()} bytes < {n} required")
+        return ws, ws.numel()
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def _dims(Q, K_lm, C):
+    B, H, L, d = Q.shape
+    if K_lm.shape != (B, H, L // C, d):
+        raise ValueError(f"K_lm must be [B,H,L/C,d] = {(B, H, L // C, d)}, got {tuple(K_lm.shape)}")
+    return B, H, L, d
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def landmark_scores(Q, K_lm, C=64, scale=None):
+    _contig(Q, K_lm)
+    B, H, L, d = _dims(Q, K_lm, C)
+    S = torch.empty((B, H, L, L // C), dtype=torch.float32, device=Q.device)
+    _check(_lib.hils_landmark_scores(_p(Q), _p(K_lm), _p(S), B, H, L, d, C, _scale(d, scale), _dt(Q), _stream()))
+    return S
+
+
+def topk_select(Q, K_lm, k, C=64, scale=None, with_weights=True):
+    _contig(Q, K_lm)
+    B, H, L, d = _dims(Q, K_lm, C)
+    idx = torch.empty((B, H, L, k + 1), dtype=torch.int32, device=Q.device)
+    sel = torch.empty((B, H, L, k + 1), dtype=torch.float32, device=Q.device)
+    w = torch.empty_like(sel) if with_weights else None
+    _check(_lib.hils_topk_select(_p(Q), _p(K_lm), _p(idx), _p(sel), _p(w), B, H, L, d, C, k, _scale(d, scale),
+                                 _dt(Q), None, 0, _stream()))
+    return idx, sel, w
+
+
+def sparse_attn_fwd(Q, K, V, K_lm, k, C=64, scale=None, idx=None, save_for_backward=False, ws=None, out=None):
+    """Returns (O, idx, sel_score, w, lse); w and lse are None unless save_for_backward."""
+    _contig(Q, K, V, K_lm, idx)
+    B, H, L, d = _dims(Q, K_lm, C)
+    for t in (K, V):
+        if t.shape != Q.shape or t.dtype != Q.dtype:
+            raise ValueError("Q, K, V must share shape and dtype")
+    select = 1
+    if idx is None:
+        idx = torch.empty((B, H, L, k + 1), dtype=torch.int32, device=Q.device)
+    else:
+        select = 0
+        if idx.shape != (B, H, L, k + 1) or idx.dtype != torch.int32:
+            raise ValueError("idx must be int32 [B,H,L,k+1]")
+    sel = torch.empty((B, H, L, k + 1), dtype=torch.float32, device=Q.device)
+    w = torch.empty_like(sel) if save_for_backward else None
+    lse = torch.empty_like(sel) if save_for_backward else None
+    O = out if out is not None else torch.empty_like(Q)
+    wsb, n = _workspace(OP_FWD, B, H, L, d, C, k, Q.device, ws)
+    _check(_lib.hils_sparse_attn_fwd(_p(Q), _p(K), _p(V), _p(K_lm), _p(idx), _p(sel), select, _p(O), _p(w), _p(lse),
+                                     B, H, L, d, C, k, _scale(d, scale), _dt(Q), _p(wsb), n, _stream()))
+    return O, idx, sel, w, lse
+
+
+def decode_step(q, k_new, v_new, K_cache, V_cache, K_lm_cache, n_ctx, k, C=64, scale=None, ws=None, out=None,
+                idx=None, w=None):
+    """One decode step at position n_ctx; returns (o, idx, w).  The caches are updated in place."""
+    _contig(q, k_new, v_new, K_cache, V_cache, K_lm_cache)
+    B, H, d = q.shape
+    L_max = K_cache.shape[2]
+    o = out if out is not None else torch.empty_like(q)
+    idx = idx if idx is not None else torch.empty((B, H, k + 1), dtype=torch.int32, device=q.device)
+    w = w if w is not None else torch.empty((B, H, k + 1), dtype=torch.float32, device=q.device)
+    wsb, n = _workspace(OP_DECODE, B, H, L_max, d, C, k, q.device, ws)
+    _check(_lib.hils_decode_step(_p(q), _p(k_new), _p(v_new), _p(K_cache), _p(V_cache), _p(K_lm_cache), n_ctx, L_max,
+                                 _p(o), _p(idx), _p(w), B, H, d, C, k, _scale(d, scale), _dt(q), _p(wsb), n,
+                                 _stream()))
+    return o, idx, w
+
+
+def sparse_attn_bwd(Q, K, V, K_lm, O, dO, idx, w, lse, k, C=64, scale=None, ws=None):
+    """Returns (dQ, dK, dV, dK_lm) in float32, selection held fixed."""
+    _contig(Q, K, V, K_lm, O, dO, idx, w, lse)
+    B, H, L, d = _dims(Q, K_lm, C)
+    f32 = dict(dtype=torch.float32, device=Q.device)
+    dQ = torch.empty((B, H, L, d), **f32)
+    dK = torch.empty((B, H, L, d), **f32)
+    dV = torch.empty((B, H, L, d), **f32)
+    dKlm = torch.empty((B, H, L // C, d), **f32)
+    wsb, n = _workspace(OP_BWD, B, H, L, d, C, k, Q.device, ws)
+    _check(_lib.hils_sparse_attn_bwd(_p(Q), _p(K), _p(V), _p(K_lm), _p(O), _p(dO), _p(idx), _p(w), _p(lse), _p(dQ),
+                                     _p(dK), _p(dV), _p(dKlm), B, H, L, d, C, k, _scale(d, scale), _dt(Q), _p(wsb), n,
+                                     _stream()))
+    return dQ, dK, dV, dKlm

@@ -128,6 +128,7 @@ def decode_inputs(B, H, d, ctx, steps, C=64, seed=0, dtype="bf16", needle=True):
     Klm = rng.standard_normal((B, H, Nmax, d), dtype=np.float32).astype(np.float64)
     nch = np.zeros((B, H), np.int64)
     u = None
+    needle = needle and ctx // C > 0
     if needle:
         u = _unit(rng, (B, H), d)
         nch = rng.integers(0, ctx // C, size=(B, H))

@@ -56,6 +56,8 @@ def _load():
     i64, dbl, vp, ip = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p, ctypes.c_int
     lib.oracle_landmark_scores.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, dbl, ip, ip]
     lib.oracle_landmark_scores.restype = None
+    lib.oracle_landmark_scores_rows.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, dbl, ip, vp, i64, ip]
+    lib.oracle_landmark_scores_rows.restype = None
     lib.oracle_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, ip, vp, i64, ip, vp,
                                vp, vp, vp, vp, vp, ip]
     lib.oracle_fwd.restype = ip
@@ -97,6 +99,19 @@ def landmark_scores(Q, Klm, C, scale=None, nthreads=0):
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     S = np.empty((B, H, L, N), np.float64)
     _load().oracle_landmark_scores(_p(Q), _p(Klm), _p(S), B, H, L, d, C, scale, _dt(Q, Klm), nthreads)
+    return S
+
+
+def landmark_scores_rows(Q, Klm, C, rows, scale=None, nthreads=0):
+    """Scores of the listed flattened rows ((b*H+h)*L+t): [len(rows), N] float64."""
+    Q, Klm = _c(Q), _c(Klm)
+    B, H, L, d = Q.shape
+    N = Klm.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    rows = _c(np.asarray(rows, np.int64))
+    S = np.empty((rows.shape[0], N), np.float64)
+    _load().oracle_landmark_scores_rows(_p(Q), _p(Klm), _p(S), B, H, L, d, C, scale, _dt(Q, Klm), _p(rows),
+                                        rows.shape[0], nthreads)
     return S
 
 

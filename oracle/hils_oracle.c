@@ -204,6 +204,20 @@ void oracle_landmark_scores(const void* Q, const void* Klm, double* S, int64_t B
   }
 }
 
+/* Scores of the listed rows only (flattened (b*H+h)*L+t); S is [nrows][N]. */
+void oracle_landmark_scores_rows(const void* Q, const void* Klm, double* S, int64_t B, int64_t H, int64_t L,
+                                 int64_t d, int64_t C, double scale, int dt, const int64_t* rows, int64_t nrows,
+                                 int nthreads) {
+  prob_t P = {Q, NULL, NULL, Klm, B, H, L, d, C, 0, (L + C - 1) / C, L, (L + C - 1) / C, scale, dt};
+  set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t r = 0; r < nrows; ++r) {
+    int64_t row = rows[r], bh = row / L, t = row % L;
+    for (int64_t j = 0; j < P.N; ++j)
+      S[r * P.N + j] = (j <= t / C) ? (double)chunk_score(&P, Q, row, bh, j) : -INFINITY;
+  }
+}
+
 /*
  * Forward over all rows, or over a list of rows (rows != NULL: flattened
  * (b*H+h)*L+t indices; outputs are then packed per listed row).

@@ -19,3 +19,20 @@ def oracle_mod():
 
     oracle.build(force=False)
     return oracle
+
+
+@pytest.fixture(scope="session")
+def hils():
+    """The HIP binding; raises if the library was not built (no fallback exists)."""
+    from long_context_landmark_amd import hils as h
+
+    return h
+
+
+@pytest.fixture(scope="session")
+def gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test collected on a machine without a HIP device")
+    return torch.device("cuda:0")

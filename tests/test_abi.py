@@ -1,0 +1,95 @@
+"""The C ABI library loads, exports what include/hils.h declares, and rejects bad arguments on the host.
+
+Runs without a GPU: every call below fails validation before any HIP call is made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hils.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x10000)  # aligned non-null address; never dereferenced by a failing call
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(hils_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib(hils):
+    return hils._lib
+
+
+def test_header_declares_the_five_entry_points():
+    names = declared_functions()
+    for n in ("hils_landmark_scores", "hils_topk_select", "hils_sparse_attn_fwd", "hils_decode_step",
+              "hils_sparse_attn_bwd", "hils_workspace_size", "hils_last_error", "hils_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in include/hils.h but not exported"
+
+
+def test_version_and_error_string(lib, hils):
+    assert hils.version() >= 10000
+    assert isinstance(lib.hils_last_error(), bytes)
+
+
+def _topk(lib, Q=FAKE, Klm=FAKE, idx=FAKE, sel=FAKE, w=None, B=1, H=1, L=128, d=64, C=64, k=4, scale=0.125, dt=0):
+    return lib.hils_topk_select(Q, Klm, idx, sel, w, B, H, L, d, C, k, scale, dt, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Q=None), INVALID, "Q must not be null"),
+    (dict(idx=None), INVALID, "idx must not be null"),
+    (dict(Klm=MISALIGNED), INVALID, "aligned"),
+    (dict(w=MISALIGNED), INVALID, "aligned"),
+    (dict(d=96), UNSUPPORTED, "head dim"),
+    (dict(C=32), UNSUPPORTED, "chunk size"),
+    (dict(L=100), INVALID, "multiple of C"),
+    (dict(L=0), INVALID, "L must be"),
+    (dict(B=0), INVALID, "B and H"),
+    (dict(k=0), UNSUPPORTED, "top-k"),
+    (dict(k=17), UNSUPPORTED, "top-k"),
+    (dict(dt=7), INVALID, "element type"),
+    (dict(scale=0.0), INVALID, "scale"),
+    (dict(scale=float("nan")), INVALID, "scale"),
+    (dict(L=64 * 20000), UNSUPPORTED, "chunks"),
+])
+def test_topk_validation(lib, kw, status, msg):
+    assert _topk(lib, **kw) == status
+    assert msg in lib.hils_last_error().decode()
+
+
+def test_fwd_workspace_checks(lib, hils):
+    need = hils.workspace_size(hils.OP_FWD, 1, 2, 1024, 64, 64, 4)
+    assert need > 0
+    args = [FAKE] * 6 + [1, FAKE, None, None, 1, 2, 1024, 64, 64, 4, 0.125, 0]
+    assert lib.hils_sparse_attn_fwd(*args, None, need, None) == WORKSPACE
+    assert lib.hils_sparse_attn_fwd(*args, FAKE, need - 1, None) == WORKSPACE
+    assert "too small" in lib.hils_last_error().decode()
+    bad_select = [FAKE] * 6 + [2, FAKE, None, None, 1, 2, 1024, 64, 64, 4, 0.125, 0]
+    assert lib.hils_sparse_attn_fwd(*bad_select, FAKE, need, None) == INVALID
+
+
+def test_workspace_size_grows_with_problem(hils):
+    a = hils.workspace_size(hils.OP_FWD, 1, 1, 1024, 64, 64, 4)
+    b = hils.workspace_size(hils.OP_FWD, 1, 2, 1024, 64, 64, 4)
+    c = hils.workspace_size(hils.OP_FWD, 1, 1, 2048, 128, 64, 8)
+    assert 0 < a < b and a < c
+    assert hils.workspace_size(hils.OP_TOPK, 1, 1, 1024, 64, 64, 4) == 0
+    with pytest.raises(hils.HilsError):
+        hils.workspace_size(hils.OP_FWD, 1, 1, 1000, 64, 64, 4)
+
+
+def test_scores_validation(lib):
+    assert lib.hils_landmark_scores(FAKE, FAKE, None, 1, 1, 128, 64, 64, 0.125, 0, None) == INVALID
+    assert lib.hils_landmark_scores(FAKE, FAKE, FAKE, 1, 1, 128, 80, 64, 0.125, 0, None) == UNSUPPORTED
