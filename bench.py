@@ -1,0 +1,446 @@
+#!/usr/bin/env python
+"""Benchmark of the HiLS attention hot path on one MI355X.
+
+Headline (``value``): prefill tokens/s of the 8K workload (B=1, H=16, d=64,
+L=8192, C=64, k=8, chunk-mean landmarks with four needle chunks).  One step is
+one ``hils_sparse_attn_fwd`` call: scoring + top-k, routing, chunk attention,
+own-chunk attention and fusion, with inputs resident in HBM.  The same JSON
+line carries the 128K prefill, the 512K-context decode (cold-cache protocol:
+R independent caches, one per emulated layer) and the 8K training step
+(forward + backward), each with its per-kernel times.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip decode_512k,...]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s @8K & 128K; decode µs/token + HBM GB/s @512K ctx"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- algorithmic work
+
+
+def prefill_work(B, H, L, d, k, C=64):
+    """Algorithmic FLOPs and bytes of one prefill forward, total and per kernel."""
+    BH, N = B * H, L // C
+    pairs = BH * C * sum(min(k, c) for c in range(N))
+    f_topk = BH * 2 * d * (C * N * (N - 1) // 2 + L)
+    f_chunk = pairs * 4 * C * d
+    f_own = BH * N * 4 * d * (C * (C + 1) // 2)
+    io = BH * (4 * L * d * 2 + N * d * 2)
+    k1 = k + 1
+    return {
+        "pairs": pairs,
+        "flops": f_topk + f_chunk + f_own,
+        "bytes": io,
+        "kernels": {
+            # name: (bound, algorithmic flops, algorithmic bytes)
+            "topk_select": ("mfma", f_topk, BH * (L * d * 2 + N * d * 2 + L * k1 * 12)),
+            "chunk_attn_fwd": ("hbm", f_chunk, pairs * (2 * d + 2 * d + 8) + BH * N * C * d * 4),
+            "own_combine": ("hbm", f_own, BH * L * (3 * d * 2 + d * 2 + k1 * 8) + pairs * 2 * d),
+            "route_count": ("hbm", 0, BH * L * k * 4),
+            "route_scan": ("hbm", 0, BH * 2 * N * 4 * max(1, L // 1024)),
+            "route_scatter": ("hbm", 0, BH * L * k * 8),
+        },
+    }
+
+
+def decode_work(B, H, d, n, k, C=64):
+    BH = B * H
+    c = n // C
+    m = min(k, c)
+    own = n - c * C + 1
+    b_scan = BH * c * d * 2
+    b_attn = BH * (m * C + own) * d * 2 * 2
+    return {
+        "bytes": b_scan + b_attn + BH * d * 2 * 5,
+        "flops": BH * (2 * d * (c + 1) + 4 * d * (m * C + own)),
+        "kernels": {"decode_scan": ("hbm", BH * 2 * d * c, b_scan), "decode_attend": ("hbm", 0, b_attn)},
+    }
+
+
+def train_work(B, H, L, d, k, C=64):
+    fw = prefill_work(B, H, L, d, k, C)
+    BH, N = B * H, L // C
+    pairs_all = fw["pairs"] + BH * L
+    f_bwd = (fw["pairs"] * 10 * C * d) + BH * N * 10 * d * (C * (C + 1) // 2)
+    b_bwd = pairs_all * (2 * d * 2 + 4 * d + 12) + BH * L * (3 * d * 2 + 4 * d * 4) + BH * N * C * d * 2 * 2
+    kern = dict(fw["kernels"])
+    kern["chunk_bwd"] = ("hbm", f_bwd, pairs_all * (2 * d * 2 + 4 * d + 12) + BH * N * C * d * (2 * 2 + 4 * 2))
+    kern["dq_reduce"] = ("hbm", 0, pairs_all * (4 * d + 2 * d + 12) + BH * L * d * 4)
+    kern["klm_bwd"] = ("hbm", 0, pairs_all * (2 * d + 8) + BH * N * d * 4)
+    return {"flops": fw["flops"] + f_bwd, "bytes": fw["bytes"] + b_bwd, "kernels": kern}
+
+
+def roofline(kernels_ms, work, launches_per_step):
+    """Roofline of the kernel with the largest time per step."""
+    if not kernels_ms:
+        return None
+    name = max(kernels_ms, key=lambda n: kernels_ms[n][0])
+    total_ms, calls = kernels_ms[name]
+    per_launch_ms = total_ms / max(1, calls)
+    bound, flops, nbytes = work["kernels"].get(name, ("hbm", 0, 0))
+    per = max(1, launches_per_step.get(name, 1))
+    if bound == "mfma":
+        achieved = flops / per / (per_launch_ms * 1e-3) / 1e12
+        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved = nbytes / per / (per_launch_ms * 1e-3) / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    return {"kernel": name, "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 5), "traffic": None, "avg_launch_us": round(per_launch_ms * 1e3, 3)}
+
+
+# ----------------------------------------------------------------------------- timing
+
+
+def timed(fn, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(steps):
+        fn()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def timed_graph(fn, steps, warmup):
+    """Capture one call of fn in a HIP graph and time ``steps`` replays (no host launch overhead)."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(steps):
+        g.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall, g
+
+
+def kernel_times(hils, fn, steps):
+    import torch
+
+    torch.cuda.synchronize()
+    hils.profile_enable(True)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    res = hils.profile_read()
+    hils.profile_enable(False)
+    return res
+
+
+# ----------------------------------------------------------------------------- workloads
+
+
+def bench_prefill(hils, synth, name, steps, warmup):
+    import torch
+
+    w = synth.WORKLOADS[name]
+    x = synth.torch_prefill_inputs(w)
+    ws = torch.empty(hils.workspace_size(hils.OP_FWD, w.B, w.H, w.L, w.d, w.C, w.k), dtype=torch.uint8,
+                     device="cuda:0")
+    O = torch.empty_like(x["Q"])
+
+    def step():
+        hils.sparse_attn_fwd(x["Q"], x["K"], x["V"], x["Klm"], w.k, ws=ws, out=O)
+
+    ms_eager, _ = timed(step, steps, warmup)
+    ms, wall, graph = timed_graph(step, steps, warmup)
+    del graph
+    kt = kernel_times(hils, step, max(1, min(steps, 10)))
+    work = prefill_work(w.B, w.H, w.L, w.d, w.k, w.C)
+    nsteps = max(1, min(steps, 10))
+    per_kernel = {n: round(t / c * 1e3, 3) for n, (t, c) in kt.items()}
+    rl = roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()})
+    res = {
+        "tokens_per_s": w.B * w.L / (ms * 1e-3),
+        "ms_per_step": ms,
+        "ms_per_step_eager": ms_eager,
+        "timing": "HIP graph of one step, replayed",
+        "wall_s": wall,
+        "tflops": work["flops"] / (ms * 1e-3) / 1e12,
+        "mfma_frac": work["flops"] / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "algorithmic_gflop": work["flops"] / 1e9,
+        "pairs": work["pairs"],
+        "kernel_us": per_kernel,
+        "roofline": rl,
+        "config": {"workload": name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "C": w.C, "k": w.k},
+    }
+    del x, ws, O
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_train(hils, synth, name, steps, warmup):
+    import torch
+
+    w = synth.WORKLOADS[name]
+    x = synth.torch_prefill_inputs(w, with_dO=True)
+    wsf = torch.empty(hils.workspace_size(hils.OP_FWD, w.B, w.H, w.L, w.d, w.C, w.k), dtype=torch.uint8,
+                      device="cuda:0")
+    wsb = torch.empty(hils.workspace_size(hils.OP_BWD, w.B, w.H, w.L, w.d, w.C, w.k), dtype=torch.uint8,
+                      device="cuda:0")
+
+    # outputs of forward and backward are allocated once so the step can be replayed from a graph
+    B, H, L, d, k1 = w.B, w.H, w.L, w.d, w.k + 1
+    f32 = dict(dtype=torch.float32, device="cuda:0")
+    O = torch.empty_like(x["Q"])
+    idx = torch.empty((B, H, L, k1), dtype=torch.int32, device="cuda:0")
+    sel, wt, lse = (torch.empty((B, H, L, k1), **f32) for _ in range(3))
+    grads = [torch.empty((B, H, L, d), **f32) for _ in range(3)] + [torch.empty((B, H, L // w.C, d), **f32)]
+    import ctypes
+
+    lib = hils._lib
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def step():
+        s_ = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        hils._check(lib.hils_sparse_attn_fwd(P(x["Q"]), P(x["K"]), P(x["V"]), P(x["Klm"]), P(idx), P(sel), 1, P(O),
+                                             P(wt), P(lse), B, H, L, d, w.C, w.k, 1.0 / math.sqrt(d), 0, P(wsf),
+                                             wsf.numel(), s_))
+        hils._check(lib.hils_sparse_attn_bwd(P(x["Q"]), P(x["K"]), P(x["V"]), P(x["Klm"]), P(x["dO"]), P(idx),
+                                             P(wt), P(lse), *(P(g_) for g_ in grads), B, H, L, d, w.C, w.k,
+                                             1.0 / math.sqrt(d), 0, P(wsb), wsb.numel(), s_))
+
+    ms_eager, _ = timed(step, steps, warmup)
+    ms, wall, graph = timed_graph(step, steps, warmup)
+    del graph
+    nsteps = max(1, min(steps, 10))
+    kt = kernel_times(hils, step, nsteps)
+    work = train_work(w.B, w.H, w.L, w.d, w.k, w.C)
+    res = {
+        "tokens_per_s": w.B * w.L / (ms * 1e-3),
+        "ms_per_step": ms,
+        "ms_per_step_eager": ms_eager,
+        "timing": "HIP graph of one step, replayed",
+        "wall_s": wall,
+        "tflops": work["flops"] / (ms * 1e-3) / 1e12,
+        "algorithmic_gflop": work["flops"] / 1e9,
+        "kernel_us": {n: round(t / c * 1e3, 3) for n, (t, c) in kt.items()},
+        "roofline": roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()}),
+        "config": {"workload": name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "C": w.C, "k": w.k,
+                   "step": "forward + backward"},
+    }
+    del x, wsf, wsb
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(hils, synth, name, replicas, warmup):
+    import torch
+
+    w = synth.WORKLOADS[name]
+    x = synth.torch_decode_inputs(w, replicas=replicas)
+    reps = x["replicas"]
+    B, H, d = w.B, w.H, w.d
+    Lmax = w.L + w.steps
+    ws = torch.empty(hils.workspace_size(hils.OP_DECODE, B, H, Lmax, d, w.C, w.k), dtype=torch.uint8,
+                     device="cuda:0")
+    o = torch.empty((B, H, d), dtype=torch.bfloat16, device="cuda:0")
+    idx = torch.empty((B, H, w.k + 1), dtype=torch.int32, device="cuda:0")
+    wt = torch.empty((B, H, w.k + 1), dtype=torch.float32, device="cuda:0")
+
+    def token(s):
+        for r in reps:
+            hils.decode_step(x["q"][s], x["k_new"][s], x["v_new"][s], r["K_cache"], r["V_cache"], r["Klm"],
+                             w.L + s, w.k, ws=ws, out=o, idx=idx, w=wt)
+
+    for s in range(warmup):
+        token(s)
+    torch.cuda.synchronize()
+    # eager pass (host launch overhead included), then the whole run captured once and replayed
+    t0 = time.perf_counter()
+    for s in range(w.steps):
+        token(s)
+    torch.cuda.synchronize()
+    eager_us = (time.perf_counter() - t0) * 1e6 / (w.steps * len(reps))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s in range(w.steps):
+            token(s)
+    graph.replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(st)
+    graph.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del graph
+    calls = w.steps * len(reps)
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    # per-kernel times over a further pass of 16 tokens
+    hils.profile_enable(True)
+    for s in range(16):
+        token(s)
+    torch.cuda.synchronize()
+    kt = hils.profile_read()
+    hils.profile_enable(False)
+    mid = w.L + w.steps // 2
+    work = decode_work(B, H, d, mid, w.k, w.C)
+    res = {
+        "us_per_token": us,
+        "us_per_token_eager": eager_us,
+        "timing": "every step of every replica captured in one HIP graph, replayed once",
+        "hbm_gbs": work["bytes"] / (us * 1e-6) / 1e9,
+        "hbm_frac": work["bytes"] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+        "bytes_per_token": work["bytes"],
+        "calls": calls,
+        "wall_s": wall,
+        "kernel_us": {n: round(t / c * 1e3, 3) for n, (t, c) in kt.items()},
+        "roofline": roofline(kt, work, {n: 1 for n in kt}),
+        "config": {"workload": name, "B": B, "H": H, "d": d, "context": w.L, "steps": w.steps, "k": w.k,
+                   "replicas": len(reps), "protocol": "cold" if len(reps) > 1 else "warm"},
+    }
+    del x, reps, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(synth, name):
+    """The oracle (plain C, double precision) on the host cores, on the full 8K workload."""
+    import oracle
+
+    w = synth.WORKLOADS[name]
+    x = synth.workload_inputs(w)
+    nthreads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    r = oracle.fwd(x["Q"], x["K"], x["V"], x["Klm"], w.C, w.k, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    return {"value": w.B * w.L / dt, "unit": "tokens/s", "cores": int(r["threads"]), "kind": "oracle",
+            "sample": f"full {name} forward (B={w.B} H={w.H} L={w.L} d={w.d} k={w.k}), {dt:.2f} s"}
+
+
+# ----------------------------------------------------------------------------- main
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--skip", default="", help="comma list of workloads to skip")
+    ap.add_argument("--only", default="", help="run only this workload (prefill_8k, prefill_128k, decode_512k, "
+                                               "train_8k) and print its result object; for profiling runs")
+    ap.add_argument("--decode-replicas", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the HiLS hot path here is built and timed on a single MI355X; "
+              "--gpus above 1 is not supported.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from long_context_landmark_amd import hils, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    skip = set(s for s in args.skip.split(",") if s)
+    torch.cuda.set_device(0)
+    if args.only:
+        if args.only == "copy_calibration":
+            # a plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
+            nbytes = 1 << 30
+            src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            print(json.dumps({"workload": "copy_calibration", "bytes_per_copy": nbytes, "copies": 3}), flush=True)
+            return
+        if args.only.startswith("prefill"):
+            res = bench_prefill(hils, synth, args.only, args.steps, args.warmup)
+        elif args.only.startswith("decode"):
+            res = bench_decode(hils, synth, args.only, args.decode_replicas, args.warmup)
+        elif args.only.startswith("train"):
+            res = bench_train(hils, synth, args.only, args.steps, args.warmup)
+        else:
+            raise SystemExit(f"unknown workload {args.only}")
+        print(json.dumps({"workload": args.only, **res}), flush=True)
+        return
+    log(f"[bench] prefill_8k: {args.steps} steps, {args.warmup} warmup")
+    head = bench_prefill(hils, synth, "prefill_8k", args.steps, args.warmup)
+    log(f"[bench] prefill_8k {head['tokens_per_s']:.4g} tokens/s, {head['ms_per_step']*1e3:.1f} us/step")
+    extra = {}
+    if "prefill_128k" not in skip:
+        log("[bench] prefill_128k")
+        extra["prefill_128k"] = bench_prefill(hils, synth, "prefill_128k", max(3, min(args.steps, 10)), 2)
+        log(f"[bench] prefill_128k {extra['prefill_128k']['tokens_per_s']:.4g} tokens/s")
+    if "decode_512k" not in skip:
+        log(f"[bench] decode_512k cold ({args.decode_replicas} replicas)")
+        extra["decode_512k"] = bench_decode(hils, synth, "decode_512k", args.decode_replicas, 4)
+        log(f"[bench] decode_512k {extra['decode_512k']['us_per_token']:.2f} us/token")
+        log("[bench] decode_512k warm (1 replica)")
+        extra["decode_512k_warm"] = bench_decode(hils, synth, "decode_512k", 1, 4)
+    if "train_8k" not in skip:
+        log("[bench] train_8k")
+        extra["train_8k"] = bench_train(hils, synth, "train_8k", max(3, min(args.steps, 20)), 2)
+        log(f"[bench] train_8k {extra['train_8k']['ms_per_step']*1e3:.1f} us/step")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(synth, "prefill_8k")
+    line = {
+        "metric": METRIC,
+        "value": round(head["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "detail": {"prefill_8k": {k: v for k, v in head.items() if k not in ("roofline", "config")}},
+        "workloads": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

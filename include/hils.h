@@ -26,9 +26,9 @@
  *                        weight and chunk log-partition function of each slot
  *                        (-inf, 0, unspecified on unused slots).
  *   Element type (dt): HILS_BF16 (storage of Q,K,V,K_lm,O,dO as bf16) or
- *   HILS_FP32.  Arithmetic: products on MFMA with fp32 accumulation; fp32
- *   inputs are rounded to bf16 where they enter an attention MFMA, while
- *   chunk scores of fp32 inputs use fp32 MFMA.
+ *   HILS_FP32.  Arithmetic: products on MFMA with fp32 accumulation (bf16
+ *   MFMA for bf16 inputs, fp32 MFMA for fp32 inputs); the per-pair partial
+ *   outputs of the forward travel through the workspace as bf16 for both.
  *   Sizes: B, H >= 1; d in {64, 128}; C == 64; L a positive multiple of C;
  *   N = L/C <= 16384; 1 <= k <= 16; B*H*L*(k+1) < 2^31.
  *   Pointers are device pointers, 16-byte aligned, non-overlapping between
@@ -148,16 +148,32 @@ hils_status hils_decode_step(const void* q, const void* k_new, const void* v_new
  * Backward with the selection held fixed (native sparse training: ai-feeds
  * summary "Key modules" item 3 and "Output & training"; the retrieval
  * scores receive gradients through the fusion weights, abstract on the
- * chatpaper page).  Inputs: the forward's Q, K, V, K_lm, O (dt), upstream
- * gradient dO (dt), and its idx, w, lse.  Outputs (float, written in full):
- *   dQ, dK, dV [B][H][L][d];  dK_lm [B][H][N][d].
- * Workspace: hils_workspace_size(HILS_OP_BWD, ...).
+ * chatpaper page).  Inputs: the forward's Q, K, V, K_lm (dt), the upstream
+ * gradient dO (dt), and the forward's idx, w and lse.  Outputs (float,
+ * written in full):  dQ, dK, dV [B][H][L][d];  dK_lm [B][H][N][d].
+ * The gradient of the fusion weights uses D = sum_j w_j dO.o_j formed from
+ * the per-chunk outputs, so the forward output O is not an input.
+ * fp32 inputs: d = 64 only.  Workspace: hils_workspace_size(HILS_OP_BWD, ...).
  */
-hils_status hils_sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* K_lm, const void* O,
-                                 const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
-                                 float* dK, float* dV, float* dK_lm, int64_t B, int64_t H, int64_t L, int64_t d,
-                                 int64_t C, int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
-                                 void* stream);
+hils_status hils_sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* K_lm, const void* dO,
+                                 const int32_t* idx, const float* w, const float* lse, float* dQ, float* dK,
+                                 float* dV, float* dK_lm, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
+                                 int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Optional per-kernel timing, for measurement only (off by default; not a
+ * step of the method).  While enabled, every kernel an entry point launches is
+ * bracketed by a pair of HIP events recorded on the caller's stream, which
+ * adds a little launch overhead.  hils_profile_enable(on) clears the totals
+ * and switches recording on or off.  hils_profile_read waits for the recorded
+ * events and returns the number of distinct kernels seen so far; for the first
+ * max_kernels of them it writes the kernel name (NUL-terminated, name_stride
+ * bytes per entry), the summed duration in milliseconds and the launch count.
+ * Any output pointer may be null.  Host-side state only; not thread-safe with
+ * concurrent enable/read calls.
+ */
+void hils_profile_enable(int on);
+int hils_profile_read(char* names, int name_stride, double* total_ms, long* calls, int max_kernels);
 
 #ifdef __cplusplus
 }

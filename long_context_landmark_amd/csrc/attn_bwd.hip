@@ -13,18 +13,22 @@
 //   da_i = w_j p_i (g.v_i - D_j)
 //   dV_i += w_j p_i g     dK_i += scale da_i q_t     dQ_t += scale da_i k_i
 //   dQ_t += scale ds_j Klm_j                          dKlm_j += scale ds_j q_t
-// (D is taken from the forward's O, as flash-attention style backward passes do.)
+// D is formed exactly as sum_j w_j D_j from the per-chunk D_j, so that the
+// fusion gradients ds_j sum to zero for every query as they do in the maths
+// (a D taken from the rounded forward output would not).
 //
 // Kernels:
-//   prep         D_t = dO_t . O_t per row.
 //   chunk_bwd    one workgroup per chunk j: its own-chunk tile (the 64 queries
 //                of chunk j, causal) and then the tiles of the queries that
-//                selected j (routing lists, ascending (t, slot)).  dK_j, dV_j
-//                and dKlm_j accumulate inside the workgroup in a fixed order,
-//                so they are written once, without atomics, and bit-for-bit
-//                reproducible.  Every pair writes its dQ contribution to a
-//                per-(query, slot) buffer.
-//   dq_reduce    dQ_t = sum over the query's slots, in slot order.
+//                selected j (routing lists, ascending (t, slot)).  dK_j and
+//                dV_j accumulate inside the workgroup in a fixed order, so they
+//                are written once, without atomics, and bit-for-bit
+//                reproducible.  Every pair writes its in-chunk dQ contribution
+//                and D_j to per-(query, slot) buffers.
+//   dq_reduce    per query: D, ds_j, and dQ_t = sum over slots (slot order) of
+//                the in-chunk parts plus scale * sum_j ds_j Klm_j; ds is kept.
+//   klm_bwd      one workgroup per chunk j: dKlm_j = scale * sum ds_tj q_t over
+//                the chunk's pairs in routing order.
 #include "hils_device.h"
 #include "hils_launch.h"
 
@@ -40,36 +44,20 @@ template <typename T, int D> struct BwdLds {
   T gt[D * TS];   // dO^T  [d][tile query]
   T pt[64 * TS];  // (w P)^T [key][tile query]
   T dat[64 * TS]; // dA^T  [key][tile query]
-  float klm[D];
-  float ds[64];
-  float red[4][D];
 };
-
-template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ O, const T* __restrict__ dO,
-                                                       float* __restrict__ Dt, int64_t rows) {
-  const int64_t row = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
-  const int part = threadIdx.x & 3;
-  float acc = 0.f;
-  if (row < rows)
-    for (int e = part * (D / 4); e < (part + 1) * (D / 4); ++e)
-      acc += Elem<T>::to_f32(O, row * D + e) * Elem<T>::to_f32(dO, row * D + e);
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  if (row < rows && part == 0) Dt[row] = acc;
-}
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                         const T* __restrict__ V, const T* __restrict__ Klm,
                                                         const T* __restrict__ dO, const float* __restrict__ w,
-                                                        const float* __restrict__ lse, const float* __restrict__ Dt,
+                                                        const float* __restrict__ lse,
                                                         const int* __restrict__ chunk_off,
-                                                        const int* __restrict__ pairs, float* __restrict__ dq_part,
-                                                        float* __restrict__ dK, float* __restrict__ dV,
-                                                        float* __restrict__ dKlm, int L, int N, int k, float scale) {
+                                                        const int* __restrict__ pairs, uint16_t* __restrict__ dq_part,
+                                                        float* __restrict__ Dpart, float* __restrict__ dK,
+                                                        float* __restrict__ dV, int L, int N, int k, float scale) {
   using S = BwdLds<T, D>;
-  const int j = blockIdx.x, bh = blockIdx.y;
+  int j, bh;
+  xcd_map(j, bh);
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
   const int k1 = k + 1;
   __shared__ S s;
@@ -87,7 +75,6 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
 #pragma unroll
       for (int e = 0; e < EPP; ++e) s.kt[(e0 + e) * S::TS + key] = vals[e];
     }
-    for (int e = tid; e < D; e += 256) s.klm[e] = Elem<T>::to_f32(Klm, ((int64_t)bh * N + j) * D + e);
   }
   __syncthreads();
 
@@ -105,10 +92,6 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
     accV[db] = zero4();
     accK[db] = zero4();
   }
-  constexpr int PARTS = 256 / D;
-  const int kd = tid % D, kpart = tid / D;
-  float acc_klm = 0.f;
-
   for (int tile = 0; tile < ntiles; ++tile) {
     int t, slot, causal;
     bool valid;
@@ -139,7 +122,6 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
     }
     const float lse_q = valid ? lse[row * k1 + slot] : 0.f;
     const float w_q = valid ? w[row * k1 + slot] : 0.f;
-    const float D_q = valid ? Dt[row] : 0.f;
     // S^T = K Q^T and dP^T = V dO^T: lane holds query qi, keys 16cb + 4g + i
     f32x4_t sc[4], dp[4];
 #pragma unroll
@@ -167,7 +149,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
       }
     Dj += __shfl_xor(Dj, 16);
     Dj += __shfl_xor(Dj, 32);
-    const float ds_q = w_q * (Dj - D_q);
+    if (valid && g == 0) Dpart[row * k1 + slot] = Dj;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -193,12 +175,10 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
           mma(dq, a, daf[h]);
         }
         if (valid) {
-          float4 out;
-          out.x = scale * (dq[0] + ds_q * s.klm[16 * db + 4 * g + 0]);
-          out.y = scale * (dq[1] + ds_q * s.klm[16 * db + 4 * g + 1]);
-          out.z = scale * (dq[2] + ds_q * s.klm[16 * db + 4 * g + 2]);
-          out.w = scale * (dq[3] + ds_q * s.klm[16 * db + 4 * g + 3]);
-          *reinterpret_cast<float4*>(dq_part + (row * k1 + slot) * D + 16 * db + 4 * g) = out;
+          u16x4_t h4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) h4[i] = __builtin_bit_cast(uint16_t, (_Float16)(scale * dq[i]));
+          *reinterpret_cast<u16x4_t*>(dq_part + (row * k1 + slot) * D + 16 * db + 4 * g) = h4;
         }
       }
     }
@@ -218,7 +198,6 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
         Elem<T>::store(s.pt, key * S::TS + qi, w_q * sc[cb][i]);
         Elem<T>::store(s.dat, key * S::TS + qi, dp[cb][i]);
       }
-    if (g == 0) s.ds[qi] = ds_q;
     __syncthreads();
     // this wave's 16 keys: dV += (wP)^T dO, dK += dA^T Q (contraction over the 64 tile queries)
 #pragma unroll
@@ -235,9 +214,6 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
         mma(accK[db], ad, bq);
       }
     }
-    // dKlm_j += sum_q ds_q q  (thread: one d, a quarter or half of the queries)
-    for (int q = kpart * (64 / PARTS); q < (kpart + 1) * (64 / PARTS); ++q)
-      acc_klm += s.ds[q] * Elem<T>::to_f32(s.qt, kd * S::TS + q);
   }
   // write dK, dV of this chunk: lane holds d = 16db + r16, keys 16wv + 4g + i
   const int64_t krow0 = (int64_t)bh * L + (int64_t)j * 64 + 16 * wv + 4 * g;
@@ -248,65 +224,142 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
       dV[(krow0 + i) * D + 16 * db + r16] = accV[db][i];
       dK[(krow0 + i) * D + 16 * db + r16] = scale * accK[db][i];
     }
-  s.red[kpart][kd] = acc_klm;
+}
+
+// Eight consecutive d of one query row per thread: D = sum_j w_j D_j, ds_j = w_j (D_j - D),
+// dQ = sum_j (in-chunk part_j + scale ds_j Klm_j) in slot order.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* __restrict__ dq_part,
+                                                        const float* __restrict__ Dpart,
+                                                        const int32_t* __restrict__ idx, const float* __restrict__ w,
+                                                        const T* __restrict__ Klm, float* __restrict__ ds_out,
+                                                        float* __restrict__ dQ, int64_t rows, int L, int N, int k,
+                                                        float scale) {
+  constexpr int V8 = D / 8;  // threads per row
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / V8;
+  const int c8 = (int)(gid % V8);
+  if (row >= rows) return;
+  const int k1 = k + 1;
+  const int64_t bh = row / L;
+  int jr[17];
+  float wr[17], dr[17];
+#pragma unroll
+  for (int r = 0; r < 17; ++r) {
+    if (r < k1) {
+      jr[r] = idx[row * k1 + r];
+      wr[r] = w[row * k1 + r];
+      dr[r] = Dpart[row * k1 + r];
+    }
+  }
+  float Dsum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 17; ++r)
+    if (r < k1 && (r == k || (jr[r] >= 0 && jr[r] < N))) Dsum += wr[r] * dr[r];
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int r = 0; r < 17; ++r) {
+    if (r >= k1 || (r < k && (jr[r] < 0 || jr[r] >= N))) continue;
+    const float ds = wr[r] * (dr[r] - Dsum);
+    if (c8 == 0) ds_out[row * k1 + r] = ds;
+    const uint4 raw = *reinterpret_cast<const uint4*>(dq_part + (row * k1 + r) * D + 8 * c8);
+    _Float16 h[8];
+    __builtin_memcpy(h, &raw, 16);
+    const int64_t lrow = (bh * N + jr[r]) * D + 8 * c8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += (float)h[e] + scale * ds * Elem<T>::to_f32(Klm, lrow + e);
+  }
+  float4* out = reinterpret_cast<float4*>(dQ + row * D + 8 * c8);
+  out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  out[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
+// dKlm_j = scale * sum over the chunk's own tile and its routed pairs of ds_tj q_t.
+// Tiles of 64 pairs; thread (pair p, quarter of d) accumulates across tiles; the 64 pair
+// lanes are then summed in a fixed order.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void klm_bwd_kernel(const T* __restrict__ Q, const float* __restrict__ ds,
+                                                      const int* __restrict__ chunk_off, const int* __restrict__ pairs,
+                                                      float* __restrict__ dKlm, int L, int N, int k, float scale) {
+  constexpr int QD = D / 4;                   // elements per thread
+  constexpr int EPP = 16 / Elem<T>::bytes;    // elements per 16-byte load
+  __shared__ float red[64][D + 1];
+  int j, bh;
+  xcd_map(j, bh);
+  const int tid = threadIdx.x;
+  const int p = tid >> 2, qt = tid & 3;
+  const int k1 = k + 1;
+  const int* co = chunk_off + (int64_t)bh * (N + 1);
+  const int p_begin = co[j], p_end = co[j + 1];
+  const int* pl = pairs + (int64_t)bh * L * k;
+  const int ntiles = 1 + (p_end - p_begin + 63) / 64;
+  float acc[QD];
+#pragma unroll
+  for (int e = 0; e < QD; ++e) acc[e] = 0.f;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    int t, slot;
+    bool valid = true;
+    if (tile == 0) {
+      t = j * 64 + p;
+      slot = k;
+    } else {
+      const int pp = p_begin + (tile - 1) * 64 + p;
+      valid = pp < p_end;
+      const int pe = valid ? pl[pp] : 0;
+      t = pe >> 5;
+      slot = pe & 31;
+    }
+    if (!valid) continue;
+    const int64_t row = (int64_t)bh * L + t;
+    const float dsv = ds[row * k1 + slot];
+    const T* qp = Q + row * D + qt * QD;
+#pragma unroll
+    for (int u = 0; u < QD / EPP; ++u) {
+      const int4 raw = *reinterpret_cast<const int4*>(qp + u * EPP);
+      T vals[EPP];
+      __builtin_memcpy(vals, &raw, 16);
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) acc[u * EPP + e] += dsv * Elem<T>::to_f32(vals, e);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < QD; ++e) red[p][qt * QD + e] = acc[e];
   __syncthreads();
   if (tid < D) {
     float a = 0.f;
-    for (int p = 0; p < PARTS; ++p) a += s.red[p][tid];
+    for (int q = 0; q < 64; ++q) a += red[q][tid];
     dKlm[((int64_t)bh * N + j) * D + tid] = scale * a;
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void dq_reduce_kernel(const float* __restrict__ dq_part,
-                                                        const int32_t* __restrict__ idx, float* __restrict__ dQ,
-                                                        int64_t rows, int N, int k) {
-  constexpr int V4 = D / 4;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gid / V4;
-  const int c4 = (int)(gid % V4);
-  if (row >= rows) return;
-  const int k1 = k + 1;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int r = 0; r < k1; ++r) {
-    if (r < k && (idx[row * k1 + r] < 0 || idx[row * k1 + r] >= N)) continue;
-    const float4 v = *reinterpret_cast<const float4*>(dq_part + (row * k1 + r) * D + 4 * c4);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
-  }
-  *reinterpret_cast<float4*>(dQ + row * D + 4 * c4) = acc;
-}
-
 template <typename T, int D>
-static hipError_t bwd_t(const void* Q, const void* K, const void* V, const void* Klm, const void* O, const void* dO,
+static hipError_t bwd_t(const void* Q, const void* K, const void* V, const void* Klm, const void* dO,
                         const int32_t* idx, const float* w, const float* lse, float* dQ, float* dK, float* dV,
                         float* dKlm, int BH, int L, int N, int k, float scale, const BwdBufs& ws, hipStream_t st) {
   const int64_t rows = (int64_t)BH * L;
-  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)((rows + 63) / 64)), dim3(256), 0, st, (const T*)O,
-                     (const T*)dO, ws.Dt, rows);
   hipError_t e = launch_route(idx, ws.rb, BH, L, N, k, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((chunk_bwd_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)Q, (const T*)K, (const T*)V,
-                     (const T*)Klm, (const T*)dO, w, lse, ws.Dt, ws.rb.chunk_off, ws.rb.pairs, ws.dq_part, dK, dV,
-                     dKlm, L, N, k, scale);
-  hipLaunchKernelGGL((dq_reduce_kernel<D>), dim3((unsigned)((rows * (D / 4) + 255) / 256)), dim3(256), 0, st,
-                     ws.dq_part, idx, dQ, rows, N, k);
+  HILS_LAUNCH("chunk_bwd", (chunk_bwd_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)Q, (const T*)K,
+              (const T*)V, (const T*)Klm, (const T*)dO, w, lse, ws.rb.chunk_off, ws.rb.pairs, ws.dq_part, ws.Dpart,
+              dK, dV, L, N, k, scale);
+  HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D>), dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, st,
+              ws.dq_part, ws.Dpart, idx, w, (const T*)Klm, ws.ds, dQ, rows, L, N, k, scale);
+  HILS_LAUNCH("klm_bwd", (klm_bwd_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)Q, ws.ds, ws.rb.chunk_off,
+              ws.rb.pairs, dKlm, L, N, k, scale);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(int dt, int d, const void* Q, const void* K, const void* V, const void* Klm, const void* O,
-                      const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ, float* dK,
-                      float* dV, float* dKlm, int BH, int L, int N, int k, float scale, const BwdBufs& ws,
-                      hipStream_t st) {
+hipError_t launch_bwd(int dt, int d, const void* Q, const void* K, const void* V, const void* Klm, const void* dO,
+                      const int32_t* idx, const float* w, const float* lse, float* dQ, float* dK, float* dV,
+                      float* dKlm, int BH, int L, int N, int k, float scale, const BwdBufs& ws, hipStream_t st) {
   if (dt == 0)
-    return d == 64 ? bwd_t<bf16_t, 64>(Q, K, V, Klm, O, dO, idx, w, lse, dQ, dK, dV, dKlm, BH, L, N, k, scale, ws, st)
-                   : bwd_t<bf16_t, 128>(Q, K, V, Klm, O, dO, idx, w, lse, dQ, dK, dV, dKlm, BH, L, N, k, scale, ws,
-                                        st);
+    return d == 64 ? bwd_t<bf16_t, 64>(Q, K, V, Klm, dO, idx, w, lse, dQ, dK, dV, dKlm, BH, L, N, k, scale, ws, st)
+                   : bwd_t<bf16_t, 128>(Q, K, V, Klm, dO, idx, w, lse, dQ, dK, dV, dKlm, BH, L, N, k, scale, ws, st);
   // fp32 inputs: head dim 64 only (the fp32 LDS tiles of d = 128 exceed a workgroup's LDS)
   if (d != 64) return hipErrorInvalidValue;
-  return bwd_t<float, 64>(Q, K, V, Klm, O, dO, idx, w, lse, dQ, dK, dV, dKlm, BH, L, N, k, scale, ws, st);
+  return bwd_t<float, 64>(Q, K, V, Klm, dO, idx, w, lse, dQ, dK, dV, dKlm, BH, L, N, k, scale, ws, st);
 }
 
 }  // namespace hils

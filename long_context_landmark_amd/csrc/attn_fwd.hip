@@ -126,9 +126,10 @@ __global__ __launch_bounds__(256) void chunk_attn_fwd_kernel(const T* __restrict
                                                              const float* __restrict__ w, float* __restrict__ lse,
                                                              uint16_t* __restrict__ partial, int L, int N, int k,
                                                              int max_items, float scale) {
-  const int bh = blockIdx.y;
-  if ((int)blockIdx.x >= n_items[bh]) return;
-  const int2 it = items[(int64_t)bh * max_items + blockIdx.x];
+  int item, bh;
+  xcd_map(item, bh);
+  if (item >= n_items[bh]) return;
+  const int2 it = items[(int64_t)bh * max_items + item];
   const int j = it.x;
   const int* co = chunk_off + (int64_t)bh * (N + 1);
   const int p0 = co[j] + it.y * FWD_PAIRS_PER_ITEM;
@@ -176,7 +177,8 @@ __global__ __launch_bounds__(256) void own_combine_kernel(const T* __restrict__ 
                                                           const float* __restrict__ w,
                                                           const uint16_t* __restrict__ partial, T* __restrict__ O,
                                                           float* __restrict__ lse, int L, int N, int k, float scale) {
-  const int c = blockIdx.x, bh = blockIdx.y;
+  int c, bh;
+  xcd_map(c, bh);
   __shared__ ChunkLds<T, D> s;
   stage_chunk<T, D>(s, K + (int64_t)bh * L * D, V + (int64_t)bh * L * D, (int64_t)c * 64);
   __syncthreads();
@@ -250,7 +252,7 @@ template <typename T, int D>
 static hipError_t chunk_attn_t(const void* Q, const void* K, const void* V, const RouteBufs& rb, const float* w,
                                float* lse, uint16_t* partial, int BH, int L, int N, int k, float scale,
                                hipStream_t st) {
-  hipLaunchKernelGGL((chunk_attn_fwd_kernel<T, D>), dim3(rb.max_items, BH), dim3(256), 0, st, (const T*)Q,
+  HILS_LAUNCH("chunk_attn_fwd", (chunk_attn_fwd_kernel<T, D>), dim3(rb.max_items, BH), dim3(256), 0, st, (const T*)Q,
                      (const T*)K, (const T*)V, rb.chunk_off, rb.items, rb.n_items, rb.pairs, w, lse, partial, L, N,
                      k, rb.max_items, scale);
   return hipGetLastError();
@@ -260,7 +262,7 @@ template <typename T, int D>
 static hipError_t own_combine_t(const void* Q, const void* K, const void* V, const int32_t* idx, const float* w,
                                 const uint16_t* partial, void* O, float* lse, int BH, int L, int N, int k, float scale,
                                 hipStream_t st) {
-  hipLaunchKernelGGL((own_combine_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)Q, (const T*)K,
+  HILS_LAUNCH("own_combine", (own_combine_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)Q, (const T*)K,
                      (const T*)V, idx, w, partial, (T*)O, lse, L, N, k, scale);
   return hipGetLastError();
 }
@@ -288,10 +290,10 @@ hipError_t launch_fixed_selection(int dt, int d, const void* Q, const void* Klm,
   const int64_t rows = (int64_t)BH * L;
   const dim3 grid((unsigned)((rows + 255) / 256));
   if (dt == 0)
-    hipLaunchKernelGGL(fixed_selection_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)Q, (const bf16_t*)Klm,
+    HILS_LAUNCH("fixed_selection", fixed_selection_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)Q, (const bf16_t*)Klm,
                        idx, sel, w, rows, L, N, d, k, scale);
   else
-    hipLaunchKernelGGL(fixed_selection_kernel<float>, grid, dim3(256), 0, st, (const float*)Q, (const float*)Klm, idx,
+    HILS_LAUNCH("fixed_selection", fixed_selection_kernel<float>, grid, dim3(256), 0, st, (const float*)Q, (const float*)Klm, idx,
                        sel, w, rows, L, N, d, k, scale);
   return hipGetLastError();
 }

@@ -92,7 +92,7 @@ struct FwdWs {
 size_t carve_route(Carver& cv, const Dims& D, hils::RouteBufs& rb, int ppi) {
   const int64_t BH = D.B * D.H;
   rb.nseg = hils::route_nseg((int)D.L);
-  rb.seg_q = 1024;
+  rb.seg_q = hils::route_seg_q((int)D.L);
   rb.pairs_per_item = ppi;
   rb.max_items = hils::route_max_items((int)D.L, (int)D.N, (int)D.k, ppi);
   rb.counts = cv.take<int>((size_t)BH * rb.nseg * D.N);
@@ -116,17 +116,18 @@ size_t carve_fwd(void* base, const Dims& D, FwdWs* ws) {
 size_t carve_bwd(void* base, const Dims& D, hils::BwdBufs* ws) {
   Carver cv(base);
   const int64_t BH = D.B * D.H;
-  ws->Dt = cv.take<float>((size_t)BH * D.L);
   carve_route(cv, D, ws->rb, hils::FWD_PAIRS_PER_ITEM);
-  ws->dq_part = cv.take<float>((size_t)BH * D.L * (D.k + 1) * D.d);
+  ws->dq_part = cv.take<uint16_t>((size_t)BH * D.L * (D.k + 1) * D.d);
+  ws->Dpart = cv.take<float>((size_t)BH * D.L * (D.k + 1));
+  ws->ds = cv.take<float>((size_t)BH * D.L * (D.k + 1));
   return cv.off;
 }
 
 size_t carve_decode(void* base, int64_t BH, int64_t Lmax, int64_t d, int64_t k, hils::DecodeBufs* ws) {
   Carver cv(base);
-  ws->cand = cv.take<uint64_t>((size_t)BH * hils::decode_slices(Lmax - 1) * 16 + 16);
-  ws->part = cv.take<float>((size_t)BH * (k + 1) * d);
-  ws->ticket = cv.take<int>((size_t)BH);
+  ws->scores = cv.take<float>((size_t)BH * ((Lmax + 63) / 64));
+  (void)d;
+  (void)k;
   return cv.off;
 }
 
@@ -284,8 +285,7 @@ hils_status hils_decode_step(const void* q, const void* k_new, const void* v_new
                     "hils_decode_step");
 }
 
-hils_status hils_sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* K_lm, const void* O,
-                                 const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
+hils_status hils_sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* K_lm, const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
                                  float* dK, float* dV, float* dK_lm, int64_t B, int64_t H, int64_t L, int64_t d,
                                  int64_t C, int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
                                  void* stream) {
@@ -298,7 +298,6 @@ hils_status hils_sparse_attn_bwd(const void* Q, const void* K, const void* V, co
   REQUIRE_PTR(K);
   REQUIRE_PTR(V);
   REQUIRE_PTR(K_lm);
-  REQUIRE_PTR(O);
   REQUIRE_PTR(dO);
   REQUIRE_PTR(idx);
   REQUIRE_PTR(w);
@@ -312,7 +311,7 @@ hils_status hils_sparse_attn_bwd(const void* Q, const void* K, const void* V, co
   const size_t need = carve_bwd(nullptr, D, &W);
   if ((st = check_ws(ws, ws_bytes, need)) != HILS_OK) return st;
   carve_bwd(ws, D, &W);
-  return hip_status(hils::launch_bwd(dt, (int)d, Q, K, V, K_lm, O, dO, idx, w, lse, dQ, dK, dV, dK_lm, (int)(B * H),
+  return hip_status(hils::launch_bwd(dt, (int)d, Q, K, V, K_lm, dO, idx, w, lse, dQ, dK, dV, dK_lm, (int)(B * H),
                                      (int)L, (int)D.N, (int)topk, scale, W, (hipStream_t)stream),
                     "hils_sparse_attn_bwd");
 }

@@ -191,4 +191,22 @@ __device__ __forceinline__ float wave_max_xor(float v, int from_mask, int to_mas
   return v;
 }
 
+// XCD-aware grid mapping for a 2D grid (x = work index inside a head, y = head).
+// Workgroups are dispatched to the 8 XCDs in round-robin order of their linear
+// id, each XCD with its own L2.  When the head count is a multiple of 8, remap so
+// that all workgroups of a head run on one XCD, in x order: the head's data then
+// stays in one L2 instead of eight.  Otherwise the plain mapping is kept.
+constexpr int NUM_XCD = 8;
+__device__ __forceinline__ void xcd_map(int& x, int& y) {
+  const int gx = (int)gridDim.x, gy = (int)gridDim.y;
+  x = (int)blockIdx.x;
+  y = (int)blockIdx.y;
+  if (gy % NUM_XCD) return;
+  const int64_t lin = (int64_t)blockIdx.y * gx + blockIdx.x;
+  const int xcd = (int)(lin % NUM_XCD);
+  const int64_t r = lin / NUM_XCD;
+  y = (int)(r / gx) * NUM_XCD + xcd;
+  x = (int)(r % gx);
+}
+
 }  // namespace hils

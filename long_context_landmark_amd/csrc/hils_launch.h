@@ -7,6 +7,17 @@
 
 namespace hils {
 
+namespace prof {  // opt-in per-kernel HIP-event timing (off unless enabled through the C ABI)
+void begin(const char* name, hipStream_t st);
+void end(hipStream_t st);
+}  // namespace prof
+#define HILS_LAUNCH(name, kernel, grid, block, lds, st, ...)       \
+  do {                                                            \
+    ::hils::prof::begin(name, st);                                \
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, __VA_ARGS__); \
+    ::hils::prof::end(st);                                        \
+  } while (0)
+
 hipError_t launch_landmark_scores(int dt, int d, const void* Q, const void* Klm, float* S, int BH, int L, int N,
                                   float scale, hipStream_t st);
 hipError_t launch_topk(int dt, int d, const void* Q, const void* Klm, int32_t* idx, float* sel, float* w, int BH,
@@ -25,6 +36,7 @@ struct RouteBufs {
   int nseg, seg_q, max_items, pairs_per_item;
 };
 int route_nseg(int L);
+int route_seg_q(int L);
 int route_max_items(int L, int N, int k, int pairs_per_item);
 hipError_t launch_route(const int32_t* idx, const RouteBufs& rb, int BH, int L, int N, int k, hipStream_t st);
 
@@ -34,21 +46,20 @@ hipError_t launch_chunk_attn_fwd(int dt, int d, const void* Q, const void* K, co
 hipError_t launch_own_combine(int dt, int d, const void* Q, const void* K, const void* V, const int32_t* idx,
                               const float* w, const uint16_t* partial, void* O, float* lse, int BH, int L, int N, int k, float scale,
                               hipStream_t st);
-constexpr int FWD_PAIRS_PER_ITEM = 256;
+constexpr int FWD_PAIRS_PER_ITEM = 1024;
 
 struct DecodeBufs {
-  uint64_t* cand;  // [BH][slices][16] sorted slice top-16 keys
-  float* part;     // [BH][k+1][d] weighted per-chunk partial outputs
-  int* ticket;     // [BH] arrival counters (reset by every step)
+  float* scores;  // [BH][N_max] landmark scores of the step
 };
 int decode_slices(int64_t n_ctx);
 
 struct BwdBufs {
-  float* Dt;       // [BH][L] dO_t . O_t
   RouteBufs rb;
-  float* dq_part;  // [BH][L][k+1][d] dQ contribution of every (query, slot)
+  uint16_t* dq_part;  // [BH][L][k+1][d] fp16 in-chunk dQ contribution of every (query, slot)
+  float* Dpart;    // [BH][L][k+1]    D_j = dO_t . o_tj of every (query, slot)
+  float* ds;       // [BH][L][k+1]    fusion-score gradient of every (query, slot)
 };
-hipError_t launch_bwd(int dt, int d, const void* Q, const void* K, const void* V, const void* Klm, const void* O,
+hipError_t launch_bwd(int dt, int d, const void* Q, const void* K, const void* V, const void* Klm,
                       const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ, float* dK,
                       float* dV, float* dKlm, int BH, int L, int N, int k, float scale, const BwdBufs& ws,
                       hipStream_t st);

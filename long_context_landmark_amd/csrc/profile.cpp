@@ -1,0 +1,98 @@
+// Opt-in per-kernel timing with HIP events on the launching stream.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/hils.h"
+#include "hils_launch.h"
+
+namespace hils {
+namespace prof {
+namespace {
+struct Pending {
+  const char* name;
+  hipEvent_t a, b;
+};
+struct Acc {
+  std::string name;
+  double ms;
+  long calls;
+};
+std::mutex g_mu;
+bool g_on = false;
+std::vector<Pending> g_pending;
+std::vector<Acc> g_acc;
+thread_local hipEvent_t t_begin = nullptr;
+thread_local const char* t_name = nullptr;
+}  // namespace
+
+void begin(const char* name, hipStream_t st) {
+  if (!g_on) return;
+  hipEvent_t a;
+  if (hipEventCreate(&a) != hipSuccess) return;
+  (void)hipEventRecord(a, st);
+  t_begin = a;
+  t_name = name;
+}
+
+void end(hipStream_t st) {
+  if (!g_on || !t_begin) return;
+  hipEvent_t b;
+  if (hipEventCreate(&b) != hipSuccess) return;
+  (void)hipEventRecord(b, st);
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_pending.push_back({t_name, t_begin, b});
+  t_begin = nullptr;
+}
+
+void collect() {
+  std::lock_guard<std::mutex> lk(g_mu);
+  for (auto& p : g_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.b) != hipSuccess || hipEventElapsedTime(&ms, p.a, p.b) != hipSuccess) ms = 0.f;
+    (void)hipEventDestroy(p.a);
+    (void)hipEventDestroy(p.b);
+    bool found = false;
+    for (auto& a : g_acc)
+      if (a.name == p.name) {
+        a.ms += ms;
+        a.calls += 1;
+        found = true;
+        break;
+      }
+    if (!found) g_acc.push_back({p.name, (double)ms, 1});
+  }
+  g_pending.clear();
+}
+}  // namespace prof
+}  // namespace hils
+
+extern "C" {
+
+void hils_profile_enable(int on) {
+  hils::prof::collect();
+  std::lock_guard<std::mutex> lk(hils::prof::g_mu);
+  hils::prof::g_on = on != 0;
+  hils::prof::g_acc.clear();
+}
+
+int hils_profile_read(char* names, int name_stride, double* total_ms, long* calls, int max_kernels) {
+  hils::prof::collect();
+  std::lock_guard<std::mutex> lk(hils::prof::g_mu);
+  int n = 0;
+  for (auto& a : hils::prof::g_acc) {
+    if (n >= max_kernels) break;
+    if (names && name_stride > 0) {
+      std::strncpy(names + (size_t)n * name_stride, a.name.c_str(), (size_t)name_stride - 1);
+      names[(size_t)n * name_stride + name_stride - 1] = 0;
+    }
+    if (total_ms) total_ms[n] = a.ms;
+    if (calls) calls[n] = a.calls;
+    ++n;
+  }
+  return (int)hils::prof::g_acc.size();
+}
+}

@@ -20,25 +20,32 @@
 
 namespace hils {
 
-constexpr int ROUTE_SEG_Q = 1024;  // queries per counting segment
-
-int route_nseg(int L) { return (L + ROUTE_SEG_Q - 1) / ROUTE_SEG_Q; }
+// queries per counting segment: short sequences use short segments (more parallel
+// scatter wavefronts), long ones longer segments (fewer per-segment counters)
+int route_seg_q(int L) { return L / 64 <= 1024 ? 256 : 1024; }
+int route_nseg(int L) { return (L + route_seg_q(L) - 1) / route_seg_q(L); }
 int route_max_items(int L, int N, int k, int ppi) {
   return N + (int)(((int64_t)L * k + ppi - 1) / ppi);
 }
 
 __global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restrict__ idx, int* __restrict__ counts,
-                                                          int L, int N, int k, int nseg) {
+                                                          int L, int N, int k, int nseg, int seg_q) {
   extern __shared__ int hist[];
   const int seg = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   for (int j = tid; j < N; j += 256) hist[j] = 0;
   __syncthreads();
-  const int t0 = seg * ROUTE_SEG_Q, t1 = min(L, t0 + ROUTE_SEG_Q);
+  const int t0 = seg * seg_q, t1 = min(L, t0 + seg_q);
   const int total = (t1 - t0) * k;
-  for (int f = tid; f < total; f += 256) {
-    const int t = t0 + f / k, r = f % k;
-    const int j = idx[((int64_t)bh * L + t) * (k + 1) + r];
-    if (j >= 0 && j < N) atomicAdd(&hist[j], 1);
+  for (int f0 = 0; f0 < total; f0 += 8 * 256) {
+    int jj[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int f = f0 + u * 256 + tid;
+      jj[u] = f < total ? idx[((int64_t)bh * L + t0 + f / k) * (k + 1) + f % k] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (jj[u] >= 0 && jj[u] < N) atomicAdd(&hist[jj[u]], 1);
   }
   __syncthreads();
   int* out = counts + ((int64_t)bh * nseg + seg) * N;
@@ -72,11 +79,15 @@ __global__ __launch_bounds__(256) void route_scan_kernel(int* __restrict__ count
     const int j = base + tid;
     int tot = 0;
     if (j < N) {
-      for (int s = 0; s < nseg; ++s) {
-        int* p = counts + ((int64_t)bh * nseg + s) * N + j;
-        const int cnum = *p;
-        *p = tot;
-        tot += cnum;
+      for (int s0 = 0; s0 < nseg; s0 += 8) {
+        int cv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) cv[u] = s0 + u < nseg ? counts[((int64_t)bh * nseg + s0 + u) * N + j] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (s0 + u < nseg) counts[((int64_t)bh * nseg + s0 + u) * N + j] = tot;
+          tot += cv[u];
+        }
       }
     }
     const int nit = (tot + ppi - 1) / ppi;
@@ -100,51 +111,61 @@ __global__ __launch_bounds__(256) void route_scan_kernel(int* __restrict__ count
 __global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __restrict__ idx,
                                                            const int* __restrict__ segoff,
                                                            const int* __restrict__ chunk_off, int* __restrict__ pairs,
-                                                           int L, int N, int k, int nseg, int nbits) {
+                                                           int L, int N, int k, int nseg, int nbits, int seg_q) {
   extern __shared__ int cur[];
-  const int seg = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
+  int seg, bh;
+  xcd_map(seg, bh);  // a head's segments run in order on one XCD: its list writes merge in one L2
+  const int lane = threadIdx.x;
   const int* so = segoff + ((int64_t)bh * nseg + seg) * N;
   const int* co = chunk_off + (int64_t)bh * (N + 1);
   for (int j = lane; j < N; j += 64) cur[j] = co[j] + so[j];
   __syncthreads();
   int* out = pairs + (int64_t)bh * L * k;
-  const int t0 = seg * ROUTE_SEG_Q, t1 = min(L, t0 + ROUTE_SEG_Q);
+  const int t0 = seg * seg_q, t1 = min(L, t0 + seg_q);
   const int total = (t1 - t0) * k;
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int base = 0; base < total; base += 64) {
-    const int f = base + lane;
-    int j = -1, t = 0, r = 0;
-    if (f < total) {
-      t = t0 + f / k;
-      r = f % k;
-      j = idx[((int64_t)bh * L + t) * (k + 1) + r];
+  constexpr int U = 8;  // batches whose chunk ids are loaded together
+  for (int b0 = 0; b0 < total; b0 += U * 64) {
+    int jj[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int f = b0 + u * 64 + lane;
+      jj[u] = f < total ? idx[((int64_t)bh * L + t0 + f / k) * (k + 1) + f % k] : -1;
     }
-    const bool act = j >= 0 && j < N;
-    uint64_t peers = __ballot(act);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = act && ((j >> b) & 1);
-      const uint64_t ones = __ballot(bit);
-      peers &= bit ? ones : ~ones;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int f = b0 + u * 64 + lane;
+      const int j = jj[u];
+      const bool act = j >= 0 && j < N;
+      uint64_t peers = __ballot(act);
+      if (peers == 0) continue;
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = act && ((j >> b) & 1);
+        const uint64_t ones = __ballot(bit);
+        peers &= bit ? ones : ~ones;
+      }
+      int pos = 0;
+      if (act) pos = cur[j] + __popcll(peers & below);
+      // LDS instructions of one wavefront execute in order: every lane's read of cur[j]
+      // precedes the leader's update below
+      __builtin_amdgcn_wave_barrier();
+      if (act && (peers & below) == 0) cur[j] = pos + __popcll(peers);
+      __builtin_amdgcn_wave_barrier();
+      if (act) out[pos] = ((t0 + f / k) << 5) | (f % k);
     }
-    int pos = 0;
-    if (act) pos = cur[j] + __popcll(peers & below);
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    if (act && (peers & below) == 0) cur[j] = pos + __popcll(peers);
-    __builtin_amdgcn_wave_barrier();
-    if (act) out[pos] = (t << 5) | r;
   }
 }
 
 hipError_t launch_route(const int32_t* idx, const RouteBufs& rb, int BH, int L, int N, int k, hipStream_t st) {
   const size_t lds = (size_t)N * sizeof(int);
-  hipLaunchKernelGGL(route_count_kernel, dim3(rb.nseg, BH), dim3(256), lds, st, idx, rb.counts, L, N, k, rb.nseg);
-  hipLaunchKernelGGL(route_scan_kernel, dim3(BH), dim3(256), 0, st, rb.counts, rb.chunk_off, rb.items, rb.n_items, N,
+  HILS_LAUNCH("route_count", route_count_kernel, dim3(rb.nseg, BH), dim3(256), lds, st, idx, rb.counts, L, N, k, rb.nseg,
+              rb.seg_q);
+  HILS_LAUNCH("route_scan", route_scan_kernel, dim3(BH), dim3(256), 0, st, rb.counts, rb.chunk_off, rb.items, rb.n_items, N,
                      rb.nseg, rb.pairs_per_item, rb.max_items);
   int nbits = 1;
   while ((1 << nbits) < N) ++nbits;
-  hipLaunchKernelGGL(route_scatter_kernel, dim3(rb.nseg, BH), dim3(64), lds, st, idx, rb.counts, rb.chunk_off,
-                     rb.pairs, L, N, k, rb.nseg, nbits);
+  HILS_LAUNCH("route_scatter", route_scatter_kernel, dim3(rb.nseg, BH), dim3(64), lds, st, idx, rb.counts, rb.chunk_off,
+                     rb.pairs, L, N, k, rb.nseg, nbits, rb.seg_q);
   return hipGetLastError();
 }
 

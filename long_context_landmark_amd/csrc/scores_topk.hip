@@ -79,17 +79,23 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const T* __restrict__ 
                                                           float* __restrict__ wout, int L, int N, int k,
                                                           float scale) {
   const int nc = L / 64;
-  const int c = nc - 1 - (int)blockIdx.x;  // longest candidate lists first
-  const int bh = blockIdx.y;
+  int xi, bh;
+  xcd_map(xi, bh);  // a head's landmark rows are re-read by all its query chunks: keep them in one L2
+  const int c = nc - 1 - xi;  // longest candidate lists first
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
   const int m = min(k, c);
   const int k1 = k + 1;
   const T* Qb = Q + ((int64_t)bh * L + (int64_t)c * 64) * D;
   const T* Kb = Klm + (int64_t)bh * N * D;
 
-  __shared__ float gmax_s[64][65];
-  __shared__ uint64_t surv[64][TK_CAP];
+  // the group maxima (sweep 1) and the survivors (sweep 2) share storage
+  __shared__ union {
+    float gmax[64][65];
+    uint64_t surv[64][TK_CAP];
+  } u_s;
   __shared__ uint64_t top_s[64][16];
+  auto& gmax_s = u_s.gmax;
+  auto& surv = u_s.surv;
   __shared__ int cnt_s[64];
   __shared__ float tau_s[64];
   __shared__ int ovf_s;
@@ -101,20 +107,37 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const T* __restrict__ 
     for (int ks = 0; ks < D / 32; ++ks) qf[qb][ks].load(Qb + (int64_t)(16 * qb + r16) * D + ks * 32 + 8 * g);
 
   const int ntile = (c + 63) / 64;
-  // scores of chunks tile*64 + 16w + 4g + i (i = 0..3) for queries 16qb + r16
-  auto score_tile = [&](int tile, f32x4_t(&acc)[4]) {
+  // scores of chunks tile*64 + 16w + 4g + i (i = 0..3) for queries 16qb + r16; the landmark
+  // fragments of the next tile are loaded while the current one is on the MFMA units
+  auto load_tile = [&](int tile, Frag<T>(&a)[D / 32]) {
     const int jrow = tile * 64 + 16 * w + r16;
-    Frag<T> a[D / 32];
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
       if (jrow < c) a[ks].load(Kb + (int64_t)jrow * D + ks * 32 + 8 * g);
       else a[ks].zero();
     }
+  };
+  auto mma_tile = [&](const Frag<T>(&a)[D / 32], f32x4_t(&acc)[4]) {
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       acc[qb] = zero4();
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) mma(acc[qb], a[ks], qf[qb][ks]);
+    }
+  };
+  auto sweep = [&](auto&& visit) {
+    Frag<T> a0[D / 32], a1[D / 32];
+    load_tile(0, a0);
+    for (int tile = 0; tile < ntile; tile += 2) {
+      f32x4_t acc[4];
+      if (tile + 1 < ntile) load_tile(tile + 1, a1);
+      mma_tile(a0, acc);
+      visit(tile, acc);
+      if (tile + 1 < ntile) {
+        if (tile + 2 < ntile) load_tile(tile + 2, a0);
+        mma_tile(a1, acc);
+        visit(tile + 1, acc);
+      }
     }
   };
 
@@ -128,22 +151,29 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const T* __restrict__ 
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) gm[qb][i] = -INFINITY;
-    for (int tile = 0; tile < ntile; ++tile) {
-      f32x4_t acc[4];
-      score_tile(tile, acc);
+    // raw accumulators: the scale is positive, so the maximum commutes with the
+    // (monotonic) rounded multiplication applied once below
+    sweep([&](int tile, f32x4_t(&acc)[4]) {
+      if ((tile + 1) * 64 <= c) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = tile * 64 + 16 * w + 4 * g + i;
-        if (j < c) {
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int qb = 0; qb < 4; ++qb) gm[qb][i] = fmaxf(gm[qb][i], scale * acc[qb][i]);
+          for (int qb = 0; qb < 4; ++qb) gm[qb][i] = fmaxf(gm[qb][i], acc[qb][i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = tile * 64 + 16 * w + 4 * g + i;
+          if (j < c) {
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb) gm[qb][i] = fmaxf(gm[qb][i], acc[qb][i]);
+          }
         }
       }
-    }
+    });
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) gmax_s[16 * qb + r16][16 * w + 4 * g + i] = gm[qb][i];
+      for (int i = 0; i < 4; ++i) gmax_s[16 * qb + r16][16 * w + 4 * g + i] = scale * gm[qb][i];
     __syncthreads();
     {
       const int q = tid >> 2, part = tid & 3;
@@ -164,23 +194,23 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const T* __restrict__ 
     float tau_r[4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) tau_r[qb] = tau_s[16 * qb + r16];
-    for (int tile = 0; tile < ntile; ++tile) {
-      f32x4_t acc[4];
-      score_tile(tile, acc);
+    __syncthreads();  // every lane has read its bounds: the survivor buffer may overwrite the maxima
+    sweep([&](int tile, f32x4_t(&acc)[4]) {
+      const bool full = (tile + 1) * 64 <= c;
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = tile * 64 + 16 * w + 4 * g + i;
           const float s = scale * acc[qb][i];
-          if (j < c && s >= tau_r[qb]) {
+          if ((full || j < c) && s >= tau_r[qb]) {
             const int q = 16 * qb + r16;
             const int p = atomicAdd(&cnt_s[q], 1);
             if (p < TK_CAP) surv[q][p] = make_key(s, j);
           }
         }
       }
-    }
+    });
     __syncthreads();
     // exact top-m among the survivors: 4 lanes per query, 16 slots each
     {
@@ -215,9 +245,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const T* __restrict__ 
       for (int r = 0; r < m; ++r) {
         if (tid < 64) best_s[tid] = 0ull;
         __syncthreads();
-        for (int tile = 0; tile < ntile; ++tile) {
-          f32x4_t acc[4];
-          score_tile(tile, acc);
+        sweep([&](int tile, f32x4_t(&acc)[4]) {
 #pragma unroll
           for (int qb = 0; qb < 4; ++qb) {
             const int q = 16 * qb + r16;
@@ -234,7 +262,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const T* __restrict__ 
             }
             if (best) atomicMax((unsigned long long*)&best_s[q], (unsigned long long)best);
           }
-        }
+        });
         __syncthreads();
         if (tid < 64 && redo_s[tid]) {
           top_s[tid][r] = best_s[tid];
@@ -286,7 +314,7 @@ template <typename T, int D>
 hipError_t launch_landmark_scores_t(const void* Q, const void* Klm, float* S, int BH, int L, int N, float scale,
                                     hipStream_t st) {
   dim3 grid((L + 63) / 64, (N + 63) / 64, BH);
-  hipLaunchKernelGGL((landmark_scores_kernel<T, D>), grid, dim3(256), 0, st, (const T*)Q, (const T*)Klm, S, L, N,
+  HILS_LAUNCH("landmark_scores", (landmark_scores_kernel<T, D>), grid, dim3(256), 0, st, (const T*)Q, (const T*)Klm, S, L, N,
                      scale);
   return hipGetLastError();
 }
@@ -295,7 +323,7 @@ template <typename T, int D>
 hipError_t launch_topk_t(const void* Q, const void* Klm, int32_t* idx, float* sel, float* w, int BH, int L, int N,
                          int k, float scale, hipStream_t st) {
   dim3 grid(L / 64, BH);
-  hipLaunchKernelGGL((topk_select_kernel<T, D>), grid, dim3(256), 0, st, (const T*)Q, (const T*)Klm, idx, sel, w, L,
+  HILS_LAUNCH("topk_select", (topk_select_kernel<T, D>), grid, dim3(256), 0, st, (const T*)Q, (const T*)Klm, idx, sel, w, L,
                      N, k, scale);
   return hipGetLastError();
 }

@@ -34,8 +34,13 @@ _lib.hils_sparse_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _
                                       _i64, _i64, _f, _int, _vp, _sz, _vp]
 _lib.hils_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                   _i64, _f, _int, _vp, _sz, _vp]
-_lib.hils_sparse_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
+_lib.hils_sparse_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
                                       _i64, _i64, _i64, _i64, _f, _int, _vp, _sz, _vp]
+_lib.hils_profile_enable.argtypes = [_int]
+_lib.hils_profile_enable.restype = None
+_lib.hils_profile_read.argtypes = [ctypes.c_char_p, _int, ctypes.POINTER(ctypes.c_double),
+                                   ctypes.POINTER(ctypes.c_long), _int]
+_lib.hils_profile_read.restype = _int
 for _fn in ("hils_landmark_scores", "hils_topk_select", "hils_sparse_attn_fwd", "hils_decode_step",
             "hils_sparse_attn_bwd"):
     getattr(_lib, _fn).restype = _int
@@ -44,7 +49,27 @@ OP_SCORES, OP_TOPK, OP_FWD, OP_DECODE, OP_BWD = range(5)
 BF16, FP32 = 0, 1
 
 EXPORTS = ("hils_last_error", "hils_version", "hils_workspace_size", "hils_landmark_scores", "hils_topk_select",
-           "hils_sparse_attn_fwd", "hils_decode_step", "hils_sparse_attn_bwd")
+           "hils_sparse_attn_fwd", "hils_decode_step", "hils_sparse_attn_bwd", "hils_profile_enable",
+           "hils_profile_read")
+
+
+def profile_enable(on: bool = True):
+    """Switch per-kernel HIP-event timing on or off (clears the totals)."""
+    _lib.hils_profile_enable(1 if on else 0)
+
+
+def profile_read(max_kernels: int = 64):
+    """{kernel name: (total ms, launches)} recorded since profile_enable(True)."""
+    stride = 64
+    names = ctypes.create_string_buffer(stride * max_kernels)
+    ms = (ctypes.c_double * max_kernels)()
+    calls = (ctypes.c_long * max_kernels)()
+    n = min(_lib.hils_profile_read(names, stride, ms, calls, max_kernels), max_kernels)
+    out = {}
+    for i in range(n):
+        nm = names.raw[i * stride:(i + 1) * stride].split(b"\0", 1)[0].decode()
+        out[nm] = (ms[i], calls[i])
+    return out
 
 
 class HilsError(RuntimeError):
@@ -173,17 +198,20 @@ def decode_step(q, k_new, v_new, K_cache, V_cache, K_lm_cache, n_ctx, k, C=64, s
     return o, idx, w
 
 
-def sparse_attn_bwd(Q, K, V, K_lm, O, dO, idx, w, lse, k, C=64, scale=None, ws=None):
+def sparse_attn_bwd(Q, K, V, K_lm, dO, idx, w, lse, k, C=64, scale=None, ws=None, out=None):
     """Returns (dQ, dK, dV, dK_lm) in float32, selection held fixed."""
-    _contig(Q, K, V, K_lm, O, dO, idx, w, lse)
+    _contig(Q, K, V, K_lm, dO, idx, w, lse)
     B, H, L, d = _dims(Q, K_lm, C)
     f32 = dict(dtype=torch.float32, device=Q.device)
-    dQ = torch.empty((B, H, L, d), **f32)
-    dK = torch.empty((B, H, L, d), **f32)
-    dV = torch.empty((B, H, L, d), **f32)
-    dKlm = torch.empty((B, H, L // C, d), **f32)
+    if out is not None:
+        dQ, dK, dV, dKlm = out
+    else:
+        dQ = torch.empty((B, H, L, d), **f32)
+        dK = torch.empty((B, H, L, d), **f32)
+        dV = torch.empty((B, H, L, d), **f32)
+        dKlm = torch.empty((B, H, L // C, d), **f32)
     wsb, n = _workspace(OP_BWD, B, H, L, d, C, k, Q.device, ws)
-    _check(_lib.hils_sparse_attn_bwd(_p(Q), _p(K), _p(V), _p(K_lm), _p(O), _p(dO), _p(idx), _p(w), _p(lse), _p(dQ),
+    _check(_lib.hils_sparse_attn_bwd(_p(Q), _p(K), _p(V), _p(K_lm), _p(dO), _p(idx), _p(w), _p(lse), _p(dQ),
                                      _p(dK), _p(dV), _p(dKlm), B, H, L, d, C, k, _scale(d, scale), _dt(Q), _p(wsb), n,
                                      _stream()))
     return dQ, dK, dV, dKlm

@@ -194,3 +194,96 @@ def workload_inputs(w: Workload, **override):
             g[key] = override[key]
     return prefill_inputs(p["B"], p["H"], override.get("L", w.L), p["d"], C=p["C"], seed=p["seed"],
                           dtype=p["dtype"], **g)
+
+
+# ----------------------------------------------------------------------------
+# Device-side generation with torch's seeded RNG, for the benchmark's large
+# inputs.  Same recipe as above; the random stream is torch's, not numpy's, so
+# values differ from the host generator for the same seed.
+
+
+def _torch_gen(seed, device):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def torch_prefill_inputs(w: Workload, device="cuda:0", seed=None, with_dO=None):
+    """Inputs of a prefill / training workload generated on the device (torch tensors)."""
+    import torch
+
+    g = _torch_gen(w.seed if seed is None else seed, device)
+    B, H, L, d, C = w.B, w.H, w.L, w.d, w.C
+    N = L // C
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    std = float(w.gen.get("qkv_std", 1.0))
+
+    def normal(shape):
+        return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+
+    Q = normal((B, H, L, d)) * std
+    K = (normal((B, H, L, d)) * std).to(dt)
+    V = (normal((B, H, L, d)) * std).to(dt)
+    noise = normal((B, H, N, d))
+    if w.gen.get("klm", "iid") == "chunkmean":
+        Klm = K.float().view(B, H, N, C, d).mean(dim=3) + float(w.gen.get("klm_noise", 0.1)) * noise
+    else:
+        Klm = noise
+    needles = int(w.gen.get("needles", 0))
+    if needles:
+        first_q = L - int(w.gen.get("needle_window", 256))
+        u = normal((B, H, d))
+        u = u / u.norm(dim=-1, keepdim=True)
+        for b in range(B):
+            for h in range(H):
+                ch = torch.randperm(first_q // C, generator=g, device=device)[:needles]
+                Klm[b, h, ch] = Klm[b, h, ch].norm(dim=-1, keepdim=True) * u[b, h]
+        q = Q[:, :, first_q:].double()
+        uu = u[:, :, None, :].double()
+        par = (q * uu).sum(-1, keepdim=True)
+        perp = q - par * uu
+        perp = perp / perp.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+        Q[:, :, first_q:] = (q.norm(dim=-1, keepdim=True) * (0.9 * uu + math.sqrt(0.19) * perp)).float()
+    out = {"Q": Q.to(dt).contiguous(), "K": K.contiguous(), "V": V.contiguous(), "Klm": Klm.to(dt).contiguous()}
+    if with_dO if with_dO is not None else w.gen.get("with_dO", False):
+        out["dO"] = normal((B, H, L, d)).to(dt)
+    return out
+
+
+def torch_decode_inputs(w: Workload, replicas=1, device="cuda:0", seed=None):
+    """Decode workload on the device: ``replicas`` independent caches (one per emulated layer) and the
+    per-step q, k_new, v_new shared by them.  One needle chunk per head and replica."""
+    import torch
+
+    g = _torch_gen(w.seed if seed is None else seed, device)
+    B, H, d, C, ctx, steps = w.B, w.H, w.d, w.C, w.L, w.steps
+    Lmax = ctx + steps
+    Nmax = (Lmax + C - 1) // C
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    reps = []
+    u = torch.randn((B, H, d), generator=g, device=device)
+    u = u / u.norm(dim=-1, keepdim=True)
+    for _ in range(replicas):
+        Kc = torch.zeros((B, H, Lmax, d), dtype=dt, device=device)
+        Vc = torch.zeros((B, H, Lmax, d), dtype=dt, device=device)
+        Kc[:, :, :ctx] = torch.randn((B, H, ctx, d), generator=g, device=device).to(dt)
+        Vc[:, :, :ctx] = torch.randn((B, H, ctx, d), generator=g, device=device).to(dt)
+        Klm = torch.randn((B, H, Nmax, d), generator=g, device=device)
+        nch = torch.randint(0, ctx // C, (B, H), generator=g, device=device)
+        for b in range(B):
+            for h in range(H):
+                j = int(nch[b, h])
+                Klm[b, h, j] = Klm[b, h, j].norm() * u[b, h]
+        reps.append({"K_cache": Kc, "V_cache": Vc, "Klm": Klm.to(dt).contiguous(), "needle_chunk": nch})
+    q = torch.randn((steps, B, H, d), generator=g, device=device).double()
+    uu = u[None].double()
+    par = (q * uu).sum(-1, keepdim=True)
+    perp = q - par * uu
+    perp = perp / perp.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+    q = q.norm(dim=-1, keepdim=True) * (0.9 * uu + math.sqrt(0.19) * perp)
+    k_new = torch.randn((steps, B, H, d), generator=g, device=device).to(dt)
+    v_new = torch.randn((steps, B, H, d), generator=g, device=device).to(dt)
+    return {"replicas": reps, "q": q.to(dt).contiguous(), "k_new": k_new.contiguous(), "v_new": v_new.contiguous(),
+            "ctx": ctx}
