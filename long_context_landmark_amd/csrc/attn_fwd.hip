@@ -120,42 +120,50 @@ __device__ __forceinline__ void wave_chunk_attention(const ChunkLds<T, D>& s, co
 template <typename T, int D>
 __global__ __launch_bounds__(256) void chunk_attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                              const T* __restrict__ V, const int* __restrict__ chunk_off,
-                                                             const int2* __restrict__ items,
+                                                             const int4* __restrict__ items,
                                                              const int* __restrict__ n_items,
                                                              const int* __restrict__ pairs,
                                                              const float* __restrict__ w, float* __restrict__ lse,
                                                              uint16_t* __restrict__ partial, int L, int N, int k,
-                                                             int max_items, float scale) {
+                                                             int max_items, int ppi, float scale) {
   int item, bh;
   xcd_map(item, bh);
+  // the item (chunk, pair range) and the item count are read together; items past the count
+  // hold stale data and are discarded
+  const int4 it = items[(int64_t)bh * max_items + item];
   if (item >= n_items[bh]) return;
-  const int2 it = items[(int64_t)bh * max_items + item];
   const int j = it.x;
-  const int* co = chunk_off + (int64_t)bh * (N + 1);
-  const int p0 = co[j] + it.y * FWD_PAIRS_PER_ITEM;
-  const int p1 = min(co[j + 1], p0 + FWD_PAIRS_PER_ITEM);
+  const int p0 = it.y, p1 = it.z;
+  (void)chunk_off;
+  (void)ppi;
   __shared__ ChunkLds<T, D> s;
-  stage_chunk<T, D>(s, K + (int64_t)bh * L * D, V + (int64_t)bh * L * D, (int64_t)j * 64);
-  __syncthreads();
   const int tid = threadIdx.x, w_ = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
   const int* pl = pairs + (int64_t)bh * L * k;
   const T* Qb = Q + (int64_t)bh * L * D;
   const int k1 = k + 1;
-  for (int base = p0; base < p1; base += 64) {
-    const int pidx = base + 16 * w_ + r16;
-    const bool valid = pidx < p1;
-    const int pe = valid ? pl[pidx] : 0;
-    const int t = pe >> 5, r = pe & 31;
-    Frag<T> qf[D / 32];
+  // software pipeline over 64-pair tiles: pair entries two tiles ahead, query rows one tile ahead
+  auto pair_at = [&](int base) { const int pidx = base + 16 * w_ + r16; return pidx < p1 ? pl[pidx] : -1; };
+  auto load_q = [&](int pe, Frag<T>(&qf)[D / 32]) {
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
-      if (valid) qf[ks].load(Qb + (int64_t)t * D + ks * 32 + 8 * g);
+      if (pe >= 0) qf[ks].load(Qb + (int64_t)(pe >> 5) * D + ks * 32 + 8 * g);
       else qf[ks].zero();
     }
+  };
+  int pe_cur = pair_at(p0), pe_nxt = pair_at(p0 + 64);
+  Frag<T> q_cur[D / 32], q_nxt[D / 32];
+  load_q(pe_cur, q_cur);
+  stage_chunk<T, D>(s, K + (int64_t)bh * L * D, V + (int64_t)bh * L * D, (int64_t)j * 64);
+  __syncthreads();
+  for (int base = p0; base < p1; base += 64) {
+    const bool more = base + 64 < p1;
+    if (more) load_q(pe_nxt, q_nxt);
+    const int pe_after = (base + 128 < p1) ? pair_at(base + 128) : -1;
     f32x4_t o[D / 16];
     float mx, sum;
-    wave_chunk_attention<T, D>(s, qf, scale, -1, o, mx, sum);
-    if (valid) {
+    wave_chunk_attention<T, D>(s, q_cur, scale, -1, o, mx, sum);
+    if (pe_cur >= 0) {
+      const int t = pe_cur >> 5, r = pe_cur & 31;
       const int64_t prow = (int64_t)bh * L + t;
       const float f = w[prow * k1 + r] / sum;
       uint16_t* dst = partial + (prow * k + r) * D;
@@ -168,6 +176,12 @@ __global__ __launch_bounds__(256) void chunk_attn_fwd_kernel(const T* __restrict
       }
       if (lse && g == 0) lse[prow * k1 + r] = mx + __logf(sum);
     }
+    if (more) {
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) q_cur[ks] = q_nxt[ks];
+    }
+    pe_cur = pe_nxt;
+    pe_nxt = pe_after;
   }
 }
 
@@ -199,15 +213,29 @@ __global__ __launch_bounds__(256) void own_combine_kernel(const T* __restrict__ 
   for (int db = 0; db < D / 16; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[db][i] = 0.f;
-  for (int r = 0; r < m; ++r) {
-    if (idx[prow * k1 + r] < 0) continue;
-    const uint16_t* src = partial + (prow * k + r) * D;
+  // kept-slot flags first, then the partial rows four slots at a time (loads in flight together)
+  bool kept[16];
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-      const u16x4_t v4 = *reinterpret_cast<const u16x4_t*>(src + 16 * db + 4 * g);
+  for (int r = 0; r < 16; ++r) kept[r] = r < m && idx[prow * k1 + r] >= 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[db][i] += bf16_to_f32(v4[i]);
+  for (int r0 = 0; r0 < 16; r0 += 4) {
+    if (r0 >= m) break;
+    u16x4_t v[4][D / 16];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint16_t* src = partial + (prow * k + r0 + u) * D;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        if (kept[r0 + u]) v[u][db] = *reinterpret_cast<const u16x4_t*>(src + 16 * db + 4 * g);
+        else v[u][db] = u16x4_t{0, 0, 0, 0};
+      }
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[db][i] += bf16_to_f32(v[u][db][i]);
   }
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
@@ -254,7 +282,7 @@ static hipError_t chunk_attn_t(const void* Q, const void* K, const void* V, cons
                                hipStream_t st) {
   HILS_LAUNCH("chunk_attn_fwd", (chunk_attn_fwd_kernel<T, D>), dim3(rb.max_items, BH), dim3(256), 0, st, (const T*)Q,
                      (const T*)K, (const T*)V, rb.chunk_off, rb.items, rb.n_items, rb.pairs, w, lse, partial, L, N,
-                     k, rb.max_items, scale);
+                     k, rb.max_items, rb.pairs_per_item, scale);
   return hipGetLastError();
 }
 

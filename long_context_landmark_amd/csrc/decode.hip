@@ -24,17 +24,25 @@
 
 namespace hils {
 
-constexpr int DEC_ROWS = 256;  // landmark rows per scan workgroup
-constexpr int DEC_MAX_CHUNKS = 16384;  // the library's chunk limit
+constexpr int DEC_ROWS = 256;   // landmark rows per scan workgroup
+constexpr int DEC_GROUP = 32;   // chunks per group maximum written by the scan
 
 int decode_slices(int64_t n_ctx) { return (int)((n_ctx / 64 + DEC_ROWS - 1) / DEC_ROWS); }
+// row strides of the per-head score row (a multiple of 32 floats) and group-maximum row
+int64_t decode_score_stride(int64_t Nmax) { return (Nmax + 31) / 32 * 32; }
+int64_t decode_gmax_stride(int64_t Nmax) { return (Nmax + DEC_ROWS - 1) / DEC_ROWS * (DEC_ROWS / DEC_GROUP); }
+
+__device__ __forceinline__ int64_t decode_score_stride_d(int64_t Nmax) { return (Nmax + 31) / 32 * 32; }
+__device__ __forceinline__ int64_t decode_gmax_stride_d(int64_t Nmax) {
+  return (Nmax + DEC_ROWS - 1) / DEC_ROWS * (DEC_ROWS / DEC_GROUP);
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ q, const T* __restrict__ k_new,
                                                           const T* __restrict__ v_new, T* __restrict__ Kc,
                                                           T* __restrict__ Vc, const T* __restrict__ Klm,
-                                                          float* __restrict__ scores, int64_t n, int64_t Lmax,
-                                                          int64_t Nmax, float scale) {
+                                                          float* __restrict__ scores, float* __restrict__ gmax,
+                                                          int64_t n, int64_t Lmax, int64_t Nmax, float scale) {
   constexpr int EPP = 16 / Elem<T>::bytes;  // elements per 16-byte piece
   constexpr int PIECES = D / EPP;           // pieces per row
   constexpr int RPR = 256 / PIECES;         // rows per round
@@ -61,7 +69,8 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ 
     const int j = j0 + round * RPR + rr;
     raw[round] = j < c ? *reinterpret_cast<const int4*>(base + (int64_t)j * D) : make_int4(0, 0, 0, 0);
   }
-  float* out = scores + (int64_t)bh * Nmax;
+  __shared__ float sc[DEC_ROWS];
+  float* out = scores + (int64_t)bh * decode_score_stride_d(Nmax);
 #pragma unroll
   for (int round = 0; round < ROUNDS; ++round) {
     T vals[EPP];
@@ -72,7 +81,19 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ 
 #pragma unroll
     for (int m = 1; m < PIECES; m <<= 1) dot += __shfl_xor(dot, m);
     const int j = j0 + round * RPR + rr;
-    if (piece == 0 && j < c) out[j] = scale * dot;
+    if (piece == 0) {
+      const float v = j < c ? scale * dot : -INFINITY;
+      sc[round * RPR + rr] = v;
+      if (j < c) out[j] = v;
+    }
+  }
+  __syncthreads();
+  // maxima of the slice's groups of DEC_GROUP chunks (-inf past the last chunk)
+  if (tid < DEC_ROWS / DEC_GROUP) {
+    float mx = -INFINITY;
+#pragma unroll 8
+    for (int e = 0; e < DEC_GROUP; ++e) mx = fmaxf(mx, sc[tid * DEC_GROUP + e]);
+    gmax[(int64_t)bh * decode_gmax_stride_d(Nmax) + s * (DEC_ROWS / DEC_GROUP) + tid] = mx;
   }
 }
 
@@ -92,29 +113,71 @@ template <typename K> __device__ __forceinline__ K wave_sort_desc(K v, int lane)
   return v;
 }
 
-// top[0..m-1] = the m best keys of sc[0..c) (score desc, index asc); sc is in LDS.  Run by one full wave.
-__device__ void wave_select_topm(const float* sc, int c, int m, uint64_t* top, uint64_t* surv, int lane) {
+// top[0..m-1] = the m best keys of the score row sc[0..c) (score desc, index asc), given the
+// maxima gm[] of its groups of DEC_GROUP chunks.  Run by one full wave.  Each lane holds
+// the maxima of groups lane, lane+64, ...; the m-th largest lane maximum is a lower bound
+// tau on the m-th best score (lane maxima are distinct candidates), so only groups whose
+// maximum reaches tau are read, and their scores >= tau are sorted exactly.
+__device__ void wave_select_topm(const float* __restrict__ sc, const float* __restrict__ gm, int c, int m,
+                                 uint64_t* top, uint64_t* surv, int lane) {
+  constexpr int PER_LANE = 8;  // survivor slots per lane
+  constexpr int MAXG = (16384 / DEC_GROUP + 63) / 64;  // group maxima per lane at the chunk limit
+  const int ngroups = (c + DEC_GROUP - 1) / DEC_GROUP;
+  // every load of the row issued before any is used: one memory round trip
+  float gv[MAXG];
+#pragma unroll
+  for (int u = 0; u < MAXG; ++u) {
+    const int gi = lane + 64 * u;
+    gv[u] = gi < ngroups ? gm[gi] : -INFINITY;
+  }
   float mx = -INFINITY;
-#pragma unroll 8
-  for (int j = lane; j < c; j += 64) mx = fmaxf(mx, sc[j]);
+#pragma unroll
+  for (int u = 0; u < MAXG; ++u) mx = fmaxf(mx, gv[u]);
   const float sorted = wave_sort_desc(mx, lane);
-  const float tau = __shfl(sorted, m - 1);  // lane maxima are distinct candidates: tau <= m-th best
-  const uint64_t below = (1ull << lane) - 1ull;
+  const float tau = __shfl(sorted, m - 1);
+  uint64_t mine[PER_LANE];
   int cnt = 0;
-  for (int j0 = 0; j0 < c; j0 += 64) {
-    const int j = j0 + lane;
-    const float s = j < c ? sc[j] : -INFINITY;
-    const bool keep = j < c && s >= tau;
-    const uint64_t mask = __ballot(keep);
-    if (mask) {
-      const int pos = cnt + __popcll(mask & below);
-      if (keep && pos < 64) surv[pos] = make_key(s, j);
-      cnt += __popcll(mask);
+  bool ovf = false;
+#pragma unroll
+  for (int u = 0; u < MAXG; ++u) {
+    const int gi = lane + 64 * u;
+    if (gi >= ngroups || gv[u] < tau) continue;
+    const float4* gp = reinterpret_cast<const float4*>(sc + gi * DEC_GROUP);
+    float4 v4[DEC_GROUP / 4];
+#pragma unroll
+    for (int u = 0; u < DEC_GROUP / 4; ++u) v4[u] = gp[u];
+#pragma unroll
+    for (int u = 0; u < DEC_GROUP / 4; ++u) {
+      const float vv[4] = {v4[u].x, v4[u].y, v4[u].z, v4[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = gi * DEC_GROUP + 4 * u + e;
+        if (j < c && vv[e] >= tau) {
+#pragma unroll
+          for (int q = 0; q < PER_LANE; ++q)
+            if (q == cnt) mine[q] = make_key(vv[e], j);
+          ovf |= cnt >= PER_LANE;
+          ++cnt;
+        }
+      }
     }
   }
-  __builtin_amdgcn_wave_barrier();
-  if (cnt <= 64) {
-    const uint64_t key = wave_sort_desc<uint64_t>(lane < cnt ? surv[lane] : (uint64_t)0, lane);
+  // exclusive prefix of the per-lane counts
+  int pre = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(pre, off);
+    if (lane >= off) pre += o;
+  }
+  const int total = __shfl(pre, 63);
+  pre -= cnt;
+  const bool any_ovf = __ballot(ovf) != 0;
+  if (!any_ovf && total <= 64) {
+#pragma unroll
+    for (int q = 0; q < PER_LANE; ++q)
+      if (q < cnt) surv[pre + q] = mine[q];
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t key = wave_sort_desc<uint64_t>(lane < total ? surv[lane] : (uint64_t)0, lane);
     if (lane < m) top[lane] = key;
   } else {
     // many exact ties at the bound: m passes of "largest key below the previous one"
@@ -143,7 +206,8 @@ __device__ void wave_select_topm(const float* sc, int c, int m, uint64_t* top, u
 template <typename T, int D>
 __global__ __launch_bounds__(1024) void decode_attend_kernel(const T* __restrict__ q, const T* __restrict__ Kc,
                                                              const T* __restrict__ Vc, const T* __restrict__ Klm,
-                                                             const float* __restrict__ scores, T* __restrict__ o,
+                                                             const float* __restrict__ scores,
+                                                             const float* __restrict__ gmax, T* __restrict__ o,
                                                              int32_t* __restrict__ idx, float* __restrict__ wout,
                                                              int64_t n, int64_t Lmax, int64_t Nmax, int k,
                                                              float scale) {
@@ -153,21 +217,18 @@ __global__ __launch_bounds__(1024) void decode_attend_kernel(const T* __restrict
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c = (int)(n / 64);
   const int m = min(k, c);
-  __shared__ float all_s[DEC_MAX_CHUNKS];
   __shared__ uint64_t top[16];
   __shared__ uint64_t surv[64];
   __shared__ float qs[D];
   __shared__ float sc_w[16][64];
   __shared__ float po[17][D];
   __shared__ float s_own_s;
+  __shared__ float wsl[17];
   for (int e = tid; e < D; e += 1024) qs[e] = Elem<T>::to_f32(q, (int64_t)bh * D + e);
-  if (m > 0) {
-    const float* srow = scores + (int64_t)bh * Nmax;
-#pragma unroll 8
-    for (int jj = tid; jj < c; jj += 1024) all_s[jj] = srow[jj];
-  }
+  if (wv == 0 && m > 0)
+    wave_select_topm(scores + (int64_t)bh * decode_score_stride_d(Nmax), gmax + (int64_t)bh * decode_gmax_stride_d(Nmax),
+                     c, m, top, surv, lane);
   __syncthreads();
-  if (wv == 0 && m > 0) wave_select_topm(all_s, c, m, top, surv, lane);
   if (wv == 1) {
     float dot = 0.f;
     for (int e = lane; e < D; e += 64) dot += qs[e] * Elem<T>::to_f32(Klm, ((int64_t)bh * Nmax + c) * D + e);
@@ -176,31 +237,47 @@ __global__ __launch_bounds__(1024) void decode_attend_kernel(const T* __restrict
     if (lane == 0) s_own_s = scale * dot;
   }
   __syncthreads();
-  float smax = s_own_s;
-  for (int i = 0; i < m; ++i) smax = fmaxf(smax, key_score(top[i]));
-  float den = __expf(s_own_s - smax);
-  for (int i = 0; i < m; ++i) den += __expf(key_score(top[i]) - smax);
+  if (wv == 0) {
+    // fusion weights of the kept slots (lane i < m: past slot i; lane 16: own chunk)
+    const bool used = lane < m || lane == 16;
+    const float sv = lane < m ? key_score(top[lane]) : (lane == 16 ? s_own_s : -INFINITY);
+    float smax = sv;
+#pragma unroll
+    for (int msk = 1; msk < 64; msk <<= 1) smax = fmaxf(smax, __shfl_xor(smax, msk));
+    const float ev = used ? __expf(sv - smax) : 0.f;
+    float den = ev;
+#pragma unroll
+    for (int msk = 1; msk < 64; msk <<= 1) den += __shfl_xor(den, msk);
+    if (lane < 17) wsl[lane] = ev / den;
+  }
+  __syncthreads();
   const int piece = lane % PIECES, kl = lane / PIECES;
   for (int item = wv; item <= m; item += 16) {
     const int r = item < m ? item : k;
     const int j = item < m ? key_index(top[item]) : c;
     const int nkeys = item < m ? 64 : (int)(n - (int64_t)c * 64) + 1;
     const int64_t row0 = (int64_t)bh * Lmax + (int64_t)j * 64;
-    // logits: a row spread over PIECES lanes, KPR rows per round, loads issued 8 rounds at a time
+    // keys and values of the chunk are requested together (one memory round trip) when a row
+    // spans at most 8 lanes; wider rows load keys, then values, 8 rounds at a time.  A row is
+    // spread over PIECES lanes, KPR rows per round.
     constexpr int UB = PIECES < 8 ? PIECES : 8;
+    constexpr bool JOINT = PIECES <= 8;
+    int4 vraw[JOINT ? PIECES : 1];
 #pragma unroll
     for (int u0 = 0; u0 < PIECES; u0 += UB) {
-      int4 raw[UB];
+      int4 kraw[UB];
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         const int key = (u0 + u) * KPR + kl;
-        raw[u] = key < nkeys ? *reinterpret_cast<const int4*>(Kc + (row0 + key) * D + piece * EPP)
-                             : make_int4(0, 0, 0, 0);
+        const bool ok = key < nkeys;
+        kraw[u] = ok ? *reinterpret_cast<const int4*>(Kc + (row0 + key) * D + piece * EPP) : make_int4(0, 0, 0, 0);
+        if constexpr (JOINT)
+          vraw[u] = ok ? *reinterpret_cast<const int4*>(Vc + (row0 + key) * D + piece * EPP) : make_int4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         T vals[EPP];
-        __builtin_memcpy(vals, &raw[u], 16);
+        __builtin_memcpy(vals, &kraw[u], 16);
         float dot = 0.f;
 #pragma unroll
         for (int e = 0; e < EPP; ++e) dot += qs[piece * EPP + e] * Elem<T>::to_f32(vals, e);
@@ -222,7 +299,6 @@ __global__ __launch_bounds__(1024) void decode_attend_kernel(const T* __restrict
     __builtin_amdgcn_wave_barrier();
     sc_w[wv][lane] = p;
     __builtin_amdgcn_wave_barrier();
-    // P V with the same lane layout: rows u*KPR + kl, elements piece*EPP ..
     float acc[EPP];
 #pragma unroll
     for (int e = 0; e < EPP; ++e) acc[e] = 0.f;
@@ -231,9 +307,13 @@ __global__ __launch_bounds__(1024) void decode_attend_kernel(const T* __restrict
       int4 raw[UB];
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
-        const int key = (u0 + u) * KPR + kl;
-        raw[u] = key < nkeys ? *reinterpret_cast<const int4*>(Vc + (row0 + key) * D + piece * EPP)
-                             : make_int4(0, 0, 0, 0);
+        if constexpr (JOINT) {
+          raw[u] = vraw[u0 + u];
+        } else {
+          const int key = (u0 + u) * KPR + kl;
+          raw[u] = key < nkeys ? *reinterpret_cast<const int4*>(Vc + (row0 + key) * D + piece * EPP)
+                               : make_int4(0, 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
@@ -248,9 +328,8 @@ __global__ __launch_bounds__(1024) void decode_attend_kernel(const T* __restrict
     for (int msk = PIECES; msk < 64; msk <<= 1)
 #pragma unroll
       for (int e = 0; e < EPP; ++e) acc[e] += __shfl_xor(acc[e], msk);
-    const float s_r = item < m ? key_score(top[item]) : s_own_s;
-    const float f = __expf(s_r - smax) / den / sum;
     const int slot = item < m ? item : 16;
+    const float f = wsl[slot] / sum;
     if (kl == 0) {
 #pragma unroll
       for (int e = 0; e < EPP; ++e) po[slot][piece * EPP + e] = f * acc[e];
@@ -266,9 +345,8 @@ __global__ __launch_bounds__(1024) void decode_attend_kernel(const T* __restrict
   }
   if (tid <= k) {
     const bool used = tid < m || tid == k;
-    const float s_t = tid == k ? s_own_s : (used ? key_score(top[tid]) : 0.f);
     idx[(int64_t)bh * (k + 1) + tid] = tid == k ? c : (used ? key_index(top[tid]) : -1);
-    wout[(int64_t)bh * (k + 1) + tid] = used ? __expf(s_t - smax) / den : 0.f;
+    wout[(int64_t)bh * (k + 1) + tid] = tid == k ? wsl[16] : (used ? wsl[tid] : 0.f);
   }
 }
 
@@ -278,9 +356,9 @@ static hipError_t decode_t(const void* q, const void* k_new, const void* v_new, 
                            float scale, const DecodeBufs& ws, hipStream_t st) {
   const int S = decode_slices(n);
   HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D>), dim3(S > 0 ? S : 1, BH), dim3(256), 0, st, (const T*)q,
-              (const T*)k_new, (const T*)v_new, (T*)Kc, (T*)Vc, (const T*)Klm, ws.scores, n, Lmax, Nmax, scale);
+              (const T*)k_new, (const T*)v_new, (T*)Kc, (T*)Vc, (const T*)Klm, ws.scores, ws.gmax, n, Lmax, Nmax, scale);
   HILS_LAUNCH("decode_attend", (decode_attend_kernel<T, D>), dim3(BH), dim3(1024), 0, st, (const T*)q, (const T*)Kc,
-              (const T*)Vc, (const T*)Klm, ws.scores, (T*)o, idx, w, n, Lmax, Nmax, k, scale);
+              (const T*)Vc, (const T*)Klm, ws.scores, ws.gmax, (T*)o, idx, w, n, Lmax, Nmax, k, scale);
   return hipGetLastError();
 }
 

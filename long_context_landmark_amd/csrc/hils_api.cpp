@@ -97,7 +97,7 @@ size_t carve_route(Carver& cv, const Dims& D, hils::RouteBufs& rb, int ppi) {
   rb.max_items = hils::route_max_items((int)D.L, (int)D.N, (int)D.k, ppi);
   rb.counts = cv.take<int>((size_t)BH * rb.nseg * D.N);
   rb.chunk_off = cv.take<int>((size_t)BH * (D.N + 1));
-  rb.items = cv.take<int2>((size_t)BH * rb.max_items);
+  rb.items = cv.take<int4>((size_t)BH * rb.max_items);
   rb.n_items = cv.take<int>((size_t)BH);
   rb.pairs = cv.take<int>((size_t)BH * D.L * D.k);
   return cv.off;
@@ -106,7 +106,7 @@ size_t carve_route(Carver& cv, const Dims& D, hils::RouteBufs& rb, int ppi) {
 size_t carve_fwd(void* base, const Dims& D, FwdWs* ws) {
   Carver cv(base);
   const int64_t BH = D.B * D.H;
-  carve_route(cv, D, ws->rb, hils::FWD_PAIRS_PER_ITEM);
+  carve_route(cv, D, ws->rb, hils::fwd_pairs_per_item((int)D.N));
   ws->partial = cv.take<uint16_t>((size_t)BH * D.L * D.k * D.d);
   ws->w_tmp = cv.take<float>((size_t)BH * D.L * (D.k + 1));
   ws->lse_tmp = cv.take<float>((size_t)BH * D.L * (D.k + 1));
@@ -116,7 +116,7 @@ size_t carve_fwd(void* base, const Dims& D, FwdWs* ws) {
 size_t carve_bwd(void* base, const Dims& D, hils::BwdBufs* ws) {
   Carver cv(base);
   const int64_t BH = D.B * D.H;
-  carve_route(cv, D, ws->rb, hils::FWD_PAIRS_PER_ITEM);
+  carve_route(cv, D, ws->rb, hils::fwd_pairs_per_item((int)D.N));
   ws->dq_part = cv.take<uint16_t>((size_t)BH * D.L * (D.k + 1) * D.d);
   ws->Dpart = cv.take<float>((size_t)BH * D.L * (D.k + 1));
   ws->ds = cv.take<float>((size_t)BH * D.L * (D.k + 1));
@@ -125,7 +125,9 @@ size_t carve_bwd(void* base, const Dims& D, hils::BwdBufs* ws) {
 
 size_t carve_decode(void* base, int64_t BH, int64_t Lmax, int64_t d, int64_t k, hils::DecodeBufs* ws) {
   Carver cv(base);
-  ws->scores = cv.take<float>((size_t)BH * ((Lmax + 63) / 64));
+  const int64_t Nmax = (Lmax + 63) / 64;
+  ws->scores = cv.take<float>((size_t)(BH * hils::decode_score_stride(Nmax)));
+  ws->gmax = cv.take<float>((size_t)(BH * hils::decode_gmax_stride(Nmax)));
   (void)d;
   (void)k;
   return cv.off;

@@ -30,7 +30,7 @@ hipError_t launch_fixed_selection(int dt, int d, const void* Q, const void* Klm,
 struct RouteBufs {
   int* counts;     // [BH][nseg][N]: per-segment counts, then per-segment offsets
   int* chunk_off;  // [BH][N+1]
-  int2* items;     // [BH][max_items]: (chunk, part) work items of the chunk-major kernels
+  int4* items;     // [BH][max_items]: (chunk, first pair, end pair, -) work items of the chunk-major kernels
   int* n_items;    // [BH]
   int* pairs;      // [BH][L*k]: (t << 5) | slot, grouped by chunk, ascending (t, slot) inside a chunk
   int nseg, seg_q, max_items, pairs_per_item;
@@ -46,12 +46,16 @@ hipError_t launch_chunk_attn_fwd(int dt, int d, const void* Q, const void* K, co
 hipError_t launch_own_combine(int dt, int d, const void* Q, const void* K, const void* V, const int32_t* idx,
                               const float* w, const uint16_t* partial, void* O, float* lse, int BH, int L, int N, int k, float scale,
                               hipStream_t st);
-constexpr int FWD_PAIRS_PER_ITEM = 1024;
+// pairs per chunk-major work item: short sequences favour balance, long ones fewer K/V re-reads
+inline int fwd_pairs_per_item(int N) { return N <= 1024 ? 256 : 1024; }
 
 struct DecodeBufs {
-  float* scores;  // [BH][N_max] landmark scores of the step
+  float* scores;  // [BH][decode_score_stride(N_max)] landmark scores of the step
+  float* gmax;    // [BH][decode_gmax_stride(N_max)] maxima of groups of 32 consecutive scores
 };
 int decode_slices(int64_t n_ctx);
+int64_t decode_score_stride(int64_t Nmax);
+int64_t decode_gmax_stride(int64_t Nmax);
 
 struct BwdBufs {
   RouteBufs rb;

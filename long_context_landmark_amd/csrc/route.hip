@@ -70,7 +70,7 @@ __device__ int block_excl_scan(int v, int* buf, int* total) {
 }
 
 __global__ __launch_bounds__(256) void route_scan_kernel(int* __restrict__ counts, int* __restrict__ chunk_off,
-                                                         int2* __restrict__ items, int* __restrict__ n_items, int N,
+                                                         int4* __restrict__ items, int* __restrict__ n_items, int N,
                                                          int nseg, int ppi, int max_items) {
   __shared__ int buf[256];
   const int bh = blockIdx.x, tid = threadIdx.x;
@@ -95,9 +95,10 @@ __global__ __launch_bounds__(256) void route_scan_kernel(int* __restrict__ count
     const int ex_p = block_excl_scan(tot, buf, &sum_p);
     const int ex_i = block_excl_scan(nit, buf, &sum_i);
     if (j < N) {
-      chunk_off[(int64_t)bh * (N + 1) + j] = carry_p + ex_p;
-      int2* it = items + (int64_t)bh * max_items + carry_i + ex_i;
-      for (int u = 0; u < nit; ++u) it[u] = make_int2(j, u);
+      const int off = carry_p + ex_p;
+      chunk_off[(int64_t)bh * (N + 1) + j] = off;
+      int4* it = items + (int64_t)bh * max_items + carry_i + ex_i;
+      for (int u = 0; u < nit; ++u) it[u] = make_int4(j, off + u * ppi, min(off + tot, off + (u + 1) * ppi), 0);
     }
     carry_p += sum_p;
     carry_i += sum_i;

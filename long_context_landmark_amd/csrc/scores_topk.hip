@@ -74,7 +74,7 @@ constexpr int TK_CAP = 64;  // survivor slots per query (16 per sorting lane)
 // share the candidate set {0..c-1}.  Wave w scores the 16-chunk block w of
 // every 64-chunk landmark tile against all 64 queries.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void topk_select_kernel(const T* __restrict__ Q, const T* __restrict__ Klm,
+__global__ __launch_bounds__(256, 3) void topk_select_kernel(const T* __restrict__ Q, const T* __restrict__ Klm,
                                                           int32_t* __restrict__ idx, float* __restrict__ sel,
                                                           float* __restrict__ wout, int L, int N, int k,
                                                           float scale) {
@@ -125,9 +125,8 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const T* __restrict__ 
       for (int ks = 0; ks < D / 32; ++ks) mma(acc[qb], a[ks], qf[qb][ks]);
     }
   };
-  auto sweep = [&](auto&& visit) {
-    Frag<T> a0[D / 32], a1[D / 32];
-    load_tile(0, a0);
+  auto sweep_from = [&](Frag<T>(&a0)[D / 32], auto&& visit) {
+    Frag<T> a1[D / 32];
     for (int tile = 0; tile < ntile; tile += 2) {
       f32x4_t acc[4];
       if (tile + 1 < ntile) load_tile(tile + 1, a1);
@@ -140,6 +139,33 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const T* __restrict__ 
       }
     }
   };
+  auto sweep = [&](auto&& visit) {
+    Frag<T> a0[D / 32];
+    load_tile(0, a0);
+    sweep_from(a0, visit);
+  };
+
+  // the first landmark tile and the own-chunk operands are requested before anything waits
+  Frag<T> first_tile[D / 32];
+  if (m > 0) load_tile(0, first_tile);
+  __shared__ float own_s[64];
+  {
+    const int q = tid >> 2, part = tid & 3;
+    Frag<T> oq[D / 32], ol[D / 32];
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u) {
+      oq[u].load(Qb + (int64_t)q * D + part * (D / 4) + 8 * u);
+      ol[u].load(Kb + (int64_t)c * D + part * (D / 4) + 8 * u);
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot += oq[u].get(e) * ol[u].get(e);
+    dot += __shfl_xor(dot, 1);
+    dot += __shfl_xor(dot, 2);
+    if (part == 0) own_s[q] = scale * dot;
+  }
 
   if (tid == 0) ovf_s = 0;
   if (tid < 64) cnt_s[tid] = 0;
@@ -153,7 +179,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const T* __restrict__ 
       for (int i = 0; i < 4; ++i) gm[qb][i] = -INFINITY;
     // raw accumulators: the scale is positive, so the maximum commutes with the
     // (monotonic) rounded multiplication applied once below
-    sweep([&](int tile, f32x4_t(&acc)[4]) {
+    sweep_from(first_tile, [&](int tile, f32x4_t(&acc)[4]) {
       if ((tile + 1) * 64 <= c) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -274,16 +300,10 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const T* __restrict__ 
   }
   __syncthreads();
 
-  // own-chunk score (VALU dot, 4 lanes per query), fusion weights, outputs
+  // fusion weights and outputs
   {
     const int q = tid >> 2, part = tid & 3;
-    const T* qrow = Qb + (int64_t)q * D;
-    const T* lrow = Kb + (int64_t)c * D;
-    float dot = 0.f;
-    for (int e = part * (D / 4); e < (part + 1) * (D / 4); ++e) dot += Elem<T>::to_f32(qrow, e) * Elem<T>::to_f32(lrow, e);
-    dot += __shfl_xor(dot, 1);
-    dot += __shfl_xor(dot, 2);
-    const float s_own = scale * dot;
+    const float s_own = own_s[q];
     if (part == 0) {
       const int64_t row = ((int64_t)bh * L + (int64_t)c * 64 + q) * k1;
       float mx = s_own;
