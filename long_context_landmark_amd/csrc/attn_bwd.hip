@@ -147,8 +147,8 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
         sc[cb][i] = p;
         Dj += p * dp[cb][i];
       }
-    Dj += __shfl_xor(Dj, 16);
-    Dj += __shfl_xor(Dj, 32);
+    Dj += lane_xor(Dj, 16);
+    Dj += lane_xor(Dj, 32);
     if (valid && g == 0) Dpart[row * k1 + slot] = Dj;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)

@@ -82,8 +82,8 @@ __device__ __forceinline__ void wave_chunk_attention(const ChunkLds<T, D>& s, co
       sc[cb][i] = v;
       mx = fmaxf(mx, v);
     }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = fmaxf(mx, lane_xor(mx, 16));
+  mx = fmaxf(mx, lane_xor(mx, 32));
   sum = 0.f;
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
@@ -93,8 +93,8 @@ __device__ __forceinline__ void wave_chunk_attention(const ChunkLds<T, D>& s, co
       sc[cb][i] = p;
       sum += p;
     }
-  sum += __shfl_xor(sum, 16);
-  sum += __shfl_xor(sum, 32);
+  sum += lane_xor(sum, 16);
+  sum += lane_xor(sum, 32);
   // O^T[d][q] = sum_key V^T[d][key] P^T[key][q]; element e of lane group g is key 32h + 16(e/4) + 4g + e%4
   Frag<T> pf[2];
 #pragma unroll

@@ -26,6 +26,7 @@ namespace hils {
 
 constexpr int DEC_ROWS = 256;   // landmark rows per scan workgroup
 constexpr int DEC_GROUP = 32;   // chunks per group maximum written by the scan
+constexpr int DEC_MAX_GROUPS = 16384 / DEC_GROUP;  // groups at the library's chunk limit
 
 int decode_slices(int64_t n_ctx) { return (int)((n_ctx / 64 + DEC_ROWS - 1) / DEC_ROWS); }
 // row strides of the per-head score row (a multiple of 32 floats) and group-maximum row
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ 
 #pragma unroll
     for (int e = 0; e < EPP; ++e) dot += qv[e] * Elem<T>::to_f32(vals, e);
 #pragma unroll
-    for (int m = 1; m < PIECES; m <<= 1) dot += __shfl_xor(dot, m);
+    for (int m = 1; m < PIECES; m <<= 1) dot += lane_xor(dot, m);
     const int j = j0 + round * RPR + rr;
     if (piece == 0) {
       const float v = j < c ? scale * dot : -INFINITY;
@@ -119,7 +120,7 @@ template <typename K> __device__ __forceinline__ K wave_sort_desc(K v, int lane)
 // tau on the m-th best score (lane maxima are distinct candidates), so only groups whose
 // maximum reaches tau are read, and their scores >= tau are sorted exactly.
 __device__ void wave_select_topm(const float* __restrict__ sc, const float* __restrict__ gm, int c, int m,
-                                 uint64_t* top, uint64_t* surv, int lane) {
+                                 uint64_t* top, uint64_t* surv, int* cg, int lane) {
   constexpr int PER_LANE = 8;  // survivor slots per lane
   constexpr int MAXG = (16384 / DEC_GROUP + 63) / 64;  // group maxima per lane at the chunk limit
   const int ngroups = (c + DEC_GROUP - 1) / DEC_GROUP;
@@ -134,14 +135,25 @@ __device__ void wave_select_topm(const float* __restrict__ sc, const float* __re
 #pragma unroll
   for (int u = 0; u < MAXG; ++u) mx = fmaxf(mx, gv[u]);
   const float sorted = wave_sort_desc(mx, lane);
-  const float tau = __shfl(sorted, m - 1);
-  uint64_t mine[PER_LANE];
-  int cnt = 0;
-  bool ovf = false;
+  const float tau = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sorted), m - 1));
+  // groups whose maximum reaches tau, compacted in LDS; then one pass of loads per 64 of them
+  const uint64_t below = (1ull << lane) - 1ull;
+  int ncand = 0;
 #pragma unroll
   for (int u = 0; u < MAXG; ++u) {
     const int gi = lane + 64 * u;
-    if (gi >= ngroups || gv[u] < tau) continue;
+    const bool is = gi < ngroups && gv[u] >= tau;
+    const uint64_t mask = __ballot(is);
+    if (is) cg[ncand + __popcll(mask & below)] = gi;
+    ncand += __popcll(mask);
+  }
+  __builtin_amdgcn_wave_barrier();
+  uint64_t mine[PER_LANE];
+  int cnt = 0;
+  bool ovf = false;
+  for (int p0 = 0; p0 < ncand; p0 += 64) {
+    const int gi = p0 + lane < ncand ? cg[p0 + lane] : -1;
+    if (gi < 0) continue;
     const float4* gp = reinterpret_cast<const float4*>(sc + gi * DEC_GROUP);
     float4 v4[DEC_GROUP / 4];
 #pragma unroll
@@ -169,7 +181,7 @@ __device__ void wave_select_topm(const float* __restrict__ sc, const float* __re
     const int o = __shfl_up(pre, off);
     if (lane >= off) pre += o;
   }
-  const int total = __shfl(pre, 63);
+  const int total = __builtin_amdgcn_readlane(pre, 63);
   pre -= cnt;
   const bool any_ovf = __ballot(ovf) != 0;
   if (!any_ovf && total <= 64) {
@@ -219,6 +231,7 @@ __global__ __launch_bounds__(1024) void decode_attend_kernel(const T* __restrict
   const int m = min(k, c);
   __shared__ uint64_t top[16];
   __shared__ uint64_t surv[64];
+  __shared__ int cgl[DEC_MAX_GROUPS];
   __shared__ float qs[D];
   __shared__ float sc_w[16][64];
   __shared__ float po[17][D];
@@ -227,13 +240,13 @@ __global__ __launch_bounds__(1024) void decode_attend_kernel(const T* __restrict
   for (int e = tid; e < D; e += 1024) qs[e] = Elem<T>::to_f32(q, (int64_t)bh * D + e);
   if (wv == 0 && m > 0)
     wave_select_topm(scores + (int64_t)bh * decode_score_stride_d(Nmax), gmax + (int64_t)bh * decode_gmax_stride_d(Nmax),
-                     c, m, top, surv, lane);
+                     c, m, top, surv, cgl, lane);
   __syncthreads();
   if (wv == 1) {
     float dot = 0.f;
     for (int e = lane; e < D; e += 64) dot += qs[e] * Elem<T>::to_f32(Klm, ((int64_t)bh * Nmax + c) * D + e);
 #pragma unroll
-    for (int msk = 1; msk < 64; msk <<= 1) dot += __shfl_xor(dot, msk);
+    for (int msk = 1; msk < 64; msk <<= 1) dot += lane_xor(dot, msk);
     if (lane == 0) s_own_s = scale * dot;
   }
   __syncthreads();
@@ -243,11 +256,11 @@ __global__ __launch_bounds__(1024) void decode_attend_kernel(const T* __restrict
     const float sv = lane < m ? key_score(top[lane]) : (lane == 16 ? s_own_s : -INFINITY);
     float smax = sv;
 #pragma unroll
-    for (int msk = 1; msk < 64; msk <<= 1) smax = fmaxf(smax, __shfl_xor(smax, msk));
+    for (int msk = 1; msk < 64; msk <<= 1) smax = fmaxf(smax, lane_xor(smax, msk));
     const float ev = used ? __expf(sv - smax) : 0.f;
     float den = ev;
 #pragma unroll
-    for (int msk = 1; msk < 64; msk <<= 1) den += __shfl_xor(den, msk);
+    for (int msk = 1; msk < 64; msk <<= 1) den += lane_xor(den, msk);
     if (lane < 17) wsl[lane] = ev / den;
   }
   __syncthreads();
@@ -282,7 +295,7 @@ __global__ __launch_bounds__(1024) void decode_attend_kernel(const T* __restrict
 #pragma unroll
         for (int e = 0; e < EPP; ++e) dot += qs[piece * EPP + e] * Elem<T>::to_f32(vals, e);
 #pragma unroll
-        for (int msk = 1; msk < PIECES; msk <<= 1) dot += __shfl_xor(dot, msk);
+        for (int msk = 1; msk < PIECES; msk <<= 1) dot += lane_xor(dot, msk);
         const int key = (u0 + u) * KPR + kl;
         if (piece == 0) sc_w[wv][key] = key < nkeys ? scale * dot : -INFINITY;
       }
@@ -291,11 +304,11 @@ __global__ __launch_bounds__(1024) void decode_attend_kernel(const T* __restrict
     const float v = sc_w[wv][lane];
     float mx = v;
 #pragma unroll
-    for (int msk = 1; msk < 64; msk <<= 1) mx = fmaxf(mx, __shfl_xor(mx, msk));
+    for (int msk = 1; msk < 64; msk <<= 1) mx = fmaxf(mx, lane_xor(mx, msk));
     const float p = __expf(v - mx);
     float sum = p;
 #pragma unroll
-    for (int msk = 1; msk < 64; msk <<= 1) sum += __shfl_xor(sum, msk);
+    for (int msk = 1; msk < 64; msk <<= 1) sum += lane_xor(sum, msk);
     __builtin_amdgcn_wave_barrier();
     sc_w[wv][lane] = p;
     __builtin_amdgcn_wave_barrier();
@@ -327,7 +340,7 @@ __global__ __launch_bounds__(1024) void decode_attend_kernel(const T* __restrict
 #pragma unroll
     for (int msk = PIECES; msk < 64; msk <<= 1)
 #pragma unroll
-      for (int e = 0; e < EPP; ++e) acc[e] += __shfl_xor(acc[e], msk);
+      for (int e = 0; e < EPP; ++e) acc[e] += lane_xor(acc[e], msk);
     const int slot = item < m ? item : 16;
     const float f = wsl[slot] / sum;
     if (kl == 0) {

@@ -165,15 +165,60 @@ template <typename K> __device__ __forceinline__ void bitonic_merge16_desc(K (&a
   }
 }
 
+// Value of lane (l ^ mask) for the lane-xor patterns of butterfly reductions and
+// bitonic networks, without the LDS crossbar (ds_bpermute) that __shfl_xor uses:
+//   mask 1, 2: DPP quad permutations [1,0,3,2] and [2,3,0,1];
+//   mask 4:    row_half_mirror (l -> 7-l in each 8) then quad permutation [3,2,1,0];
+//   mask 8:    DPP row rotate by 8 inside each row of 16;
+//   mask 16:   v_permlane16_swap (exchanges the odd rows of one copy with the even
+//              rows of the other: element 0 holds row r^1 on odd rows, element 1 on even);
+//   mask 32:   v_permlane32_swap (the same between the two halves of the wave).
+// Other masks fall back to __shfl_xor.  After loop unrolling the mask is a constant
+// and the switch folds away.
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v, int mask) {
+  const int iv = (int)v;
+  switch (mask) {
+    case 1: return (uint32_t)__builtin_amdgcn_update_dpp(iv, iv, 0xB1, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_update_dpp(iv, iv, 0x4E, 0xF, 0xF, false);
+    case 4: {
+      const int h = __builtin_amdgcn_update_dpp(iv, iv, 0x141, 0xF, 0xF, false);
+      return (uint32_t)__builtin_amdgcn_update_dpp(h, h, 0x1B, 0xF, 0xF, false);
+    }
+    case 8: return (uint32_t)__builtin_amdgcn_update_dpp(iv, iv, 0x128, 0xF, 0xF, false);
+    case 16: {
+      const auto sw = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+      return (__lane_id() & 16) ? sw[0] : sw[1];
+    }
+    case 32: {
+      const auto sw = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+      return (__lane_id() & 32) ? sw[0] : sw[1];
+    }
+    default: return (uint32_t)__shfl_xor(iv, mask);
+  }
+}
+__device__ __forceinline__ float lane_xor(float v, int mask) {
+  return __uint_as_float(lane_xor_u32(__float_as_uint(v), mask));
+}
+__device__ __forceinline__ int lane_xor(int v, int mask) { return (int)lane_xor_u32((uint32_t)v, mask); }
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
-  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  lo = (uint32_t)__shfl_xor((int)lo, mask);
-  hi = (uint32_t)__shfl_xor((int)hi, mask);
+  const uint32_t lo = lane_xor_u32((uint32_t)v, mask), hi = lane_xor_u32((uint32_t)(v >> 32), mask);
   return ((uint64_t)hi << 32) | lo;
 }
-__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask); }
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return lane_xor(v, mask); }
 __device__ __forceinline__ uint64_t shfl_xor_any(uint64_t v, int m) { return shfl_xor_u64(v, m); }
 __device__ __forceinline__ float shfl_xor_any(float v, int m) { return shfl_xor_f(v, m); }
+
+// Butterfly reductions over all 64 lanes (every lane receives the result).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += lane_xor(v, m);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, lane_xor(v, m));
+  return v;
+}
 
 // Lanes l and l^mask each hold a descending list of 16; afterwards both hold the
 // 16 largest of the union, descending.
@@ -187,7 +232,8 @@ template <typename K> __device__ __forceinline__ void merge16_with_lane(K (&a)[1
 }
 
 __device__ __forceinline__ float wave_max_xor(float v, int from_mask, int to_mask) {
-  for (int m = from_mask; m <= to_mask; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+#pragma unroll
+  for (int m = from_mask; m <= to_mask; m <<= 1) v = fmaxf(v, lane_xor(v, m));
   return v;
 }
 

@@ -162,8 +162,8 @@ __global__ __launch_bounds__(256, 3) void topk_select_kernel(const T* __restrict
     for (int u = 0; u < D / 32; ++u)
 #pragma unroll
       for (int e = 0; e < 8; ++e) dot += oq[u].get(e) * ol[u].get(e);
-    dot += __shfl_xor(dot, 1);
-    dot += __shfl_xor(dot, 2);
+    dot += lane_xor(dot, 1);
+    dot += lane_xor(dot, 2);
     if (part == 0) own_s[q] = scale * dot;
   }
 
