@@ -34,6 +34,43 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# ----------------------------------------------------------------------------- measured HBM traffic
+# FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the dominant kernel of each workload, from
+# rocprofv3 --pmc runs of this script (the commands and tables are in profiles/).  FETCH_SIZE
+# reads half the bytes a plain 1 GiB copy moves and WRITE_SIZE all of them, so the traffic is
+# 2*FETCH + WRITE.  Each entry records a digest of the kernel's sources when the counters were
+# taken; once the sources differ the entry no longer describes the kernel and traffic is null.
+COUNTER_SCALE = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
+KERNEL_SOURCES = {
+    "chunk_attn_fwd": "attn_fwd.hip", "own_combine": "attn_fwd.hip", "topk_select": "scores_topk.hip",
+    "decode_scan": "decode.hip", "decode_attend": "decode.hip", "chunk_bwd": "attn_bwd.hip",
+    "dq_reduce": "attn_bwd.hip", "klm_bwd": "attn_bwd.hip", "route_scatter": "route.hip",
+}
+MEASURED_TRAFFIC = {
+    # workload: (kernel, FETCH_SIZE KiB, WRITE_SIZE KiB, source digest)
+    "prefill_8k": ("chunk_attn_fwd", 30612.9, 126464.0, "bf0777efc24d5c2b"),
+}
+
+
+def kernel_source_digest(kernel):
+    import hashlib
+
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "long_context_landmark_amd", "csrc")
+    for f in (KERNEL_SOURCES[kernel], "hils_device.h", "hils_launch.h"):
+        with open(os.path.join(src, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of the kernel from the recorded counters, or None."""
+    rec = MEASURED_TRAFFIC.get(workload)
+    if rec is None or rec[0] != kernel or kernel_source_digest(kernel) != rec[3]:
+        return None
+    return round((rec[1] * COUNTER_SCALE["FETCH_SIZE"] + rec[2] * COUNTER_SCALE["WRITE_SIZE"]) * 1024)
+
+
 # ----------------------------------------------------------------------------- algorithmic work
 
 
@@ -89,7 +126,7 @@ def train_work(B, H, L, d, k, C=64):
     return {"flops": fw["flops"] + f_bwd, "bytes": fw["bytes"] + b_bwd, "kernels": kern}
 
 
-def roofline(kernels_ms, work, launches_per_step):
+def roofline(kernels_ms, work, launches_per_step, workload=None):
     """Roofline of the kernel with the largest time per step."""
     if not kernels_ms:
         return None
@@ -105,7 +142,8 @@ def roofline(kernels_ms, work, launches_per_step):
         achieved = nbytes / per / (per_launch_ms * 1e-3) / 1e9
         peak, unit = PEAK_HBM_GBS, "GB/s"
     return {"kernel": name, "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 5), "traffic": None, "avg_launch_us": round(per_launch_ms * 1e3, 3)}
+            "frac": round(achieved / peak, 5), "traffic": measured_traffic(workload, name),
+            "avg_launch_us": round(per_launch_ms * 1e3, 3)}
 
 
 # ----------------------------------------------------------------------------- timing
@@ -188,7 +226,7 @@ def bench_prefill(hils, synth, name, steps, warmup):
     work = prefill_work(w.B, w.H, w.L, w.d, w.k, w.C)
     nsteps = max(1, min(steps, 10))
     per_kernel = {n: round(t / c * 1e3, 3) for n, (t, c) in kt.items()}
-    rl = roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()})
+    rl = roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()}, name)
     res = {
         "tokens_per_s": w.B * w.L / (ms * 1e-3),
         "ms_per_step": ms,
@@ -254,7 +292,7 @@ def bench_train(hils, synth, name, steps, warmup):
         "tflops": work["flops"] / (ms * 1e-3) / 1e12,
         "algorithmic_gflop": work["flops"] / 1e9,
         "kernel_us": {n: round(t / c * 1e3, 3) for n, (t, c) in kt.items()},
-        "roofline": roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()}),
+        "roofline": roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()}, name),
         "config": {"workload": name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "C": w.C, "k": w.k,
                    "step": "forward + backward"},
     }
@@ -327,7 +365,7 @@ def bench_decode(hils, synth, name, replicas, warmup):
         "calls": calls,
         "wall_s": wall,
         "kernel_us": {n: round(t / c * 1e3, 3) for n, (t, c) in kt.items()},
-        "roofline": roofline(kt, work, {n: 1 for n in kt}),
+        "roofline": roofline(kt, work, {n: 1 for n in kt}, name),
         "config": {"workload": name, "B": B, "H": H, "d": d, "context": w.L, "steps": w.steps, "k": w.k,
                    "replicas": len(reps), "protocol": "cold" if len(reps) > 1 else "warm"},
     }

@@ -11,39 +11,53 @@
 //
 // The step is bound by HBM reads of the landmark rows (every step reads all of
 // them).  decode_scan streams them with 16-byte coalesced loads over many
-// workgroups and writes one fp32 score per chunk (4 bytes per 128-256 bytes
-// read).  decode_attend runs one 1024-thread workgroup per head.  One wavefront
-// selects the top-m from the score row: the m-th largest of the 64 lane maxima
-// (a wave-wide bitonic sort) bounds the m-th largest score from below, and the
-// few scores at or above it are compacted with ballots and sorted exactly.  The
-// k+1 kept chunks are then split over the 16 wavefronts (split-K), each reading
-// its chunk's keys and values with 16-byte loads, and the weighted per-chunk
-// outputs are fused in LDS in slot order.
+// workgroups; each workgroup scores 256 chunks and writes only its 16 best
+// (score, chunk) keys, sorted.  The top-m of the context is the top-m of the
+// union of these lists, since m <= 16.  decode_attend runs one 1024-thread
+// workgroup per head: wave 0 merges the lists (the m-th largest of a few list
+// heads bounds the answer from below; the keys above the bound are compacted
+// with ballots and sorted exactly) while wave 15 already attends to the open
+// chunk, which needs no selection.  The kept chunks are then split over the 16
+// wavefronts (split-K), each reading its chunk's keys and values with 16-byte
+// loads, and the per-chunk outputs are fused with the retrieval weights in LDS.
 #include "hils_device.h"
 #include "hils_launch.h"
 
 namespace hils {
 
-constexpr int DEC_ROWS = 256;   // landmark rows per scan workgroup
-constexpr int DEC_GROUP = 32;   // chunks per group maximum written by the scan
-constexpr int DEC_MAX_GROUPS = 16384 / DEC_GROUP;  // groups at the library's chunk limit
+constexpr int DEC_ROWS = 256;                          // landmark rows per scan workgroup
+constexpr int DEC_LIST = 16;                           // keys kept per slice: the largest k accepted
+constexpr int DEC_MAX_SLICES = 16384 / DEC_ROWS;       // slices at the library's chunk limit
 
 int decode_slices(int64_t n_ctx) { return (int)((n_ctx / 64 + DEC_ROWS - 1) / DEC_ROWS); }
-// row strides of the per-head score row (a multiple of 32 floats) and group-maximum row
-int64_t decode_score_stride(int64_t Nmax) { return (Nmax + 31) / 32 * 32; }
-int64_t decode_gmax_stride(int64_t Nmax) { return (Nmax + DEC_ROWS - 1) / DEC_ROWS * (DEC_ROWS / DEC_GROUP); }
+int decode_max_slices() { return DEC_MAX_SLICES; }
+int decode_list_len() { return DEC_LIST; }
 
-__device__ __forceinline__ int64_t decode_score_stride_d(int64_t Nmax) { return (Nmax + 31) / 32 * 32; }
-__device__ __forceinline__ int64_t decode_gmax_stride_d(int64_t Nmax) {
-  return (Nmax + DEC_ROWS - 1) / DEC_ROWS * (DEC_ROWS / DEC_GROUP);
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Exclusive prefix sum over the lanes of counts in [0, 32), and their total, from five ballots.
+__device__ __forceinline__ int wave_excl_prefix_small(int v, int& total) {
+  int pre = 0;
+  total = 0;
+#pragma unroll
+  for (int b = 0; b < 5; ++b) {
+    const uint64_t bits = __ballot((v >> b) & 1);
+    pre += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bits >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0u)) << b;
+    total += __popcll(bits) << b;
+  }
+  return pre;
 }
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ q, const T* __restrict__ k_new,
                                                           const T* __restrict__ v_new, T* __restrict__ Kc,
                                                           T* __restrict__ Vc, const T* __restrict__ Klm,
-                                                          float* __restrict__ scores, float* __restrict__ gmax,
-                                                          int64_t n, int64_t Lmax, int64_t Nmax, float scale) {
+                                                          uint64_t* __restrict__ lists, int64_t n, int64_t Lmax,
+                                                          int64_t Nmax, float scale) {
   constexpr int EPP = 16 / Elem<T>::bytes;  // elements per 16-byte piece
   constexpr int PIECES = D / EPP;           // pieces per row
   constexpr int RPR = 256 / PIECES;         // rows per round
@@ -70,8 +84,7 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ 
     const int j = j0 + round * RPR + rr;
     raw[round] = j < c ? *reinterpret_cast<const int4*>(base + (int64_t)j * D) : make_int4(0, 0, 0, 0);
   }
-  __shared__ float sc[DEC_ROWS];
-  float* out = scores + (int64_t)bh * decode_score_stride_d(Nmax);
+  __shared__ __align__(16) float sc[DEC_ROWS];
 #pragma unroll
   for (int round = 0; round < ROUNDS; ++round) {
     T vals[EPP];
@@ -81,279 +94,260 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ 
     for (int e = 0; e < EPP; ++e) dot += qv[e] * Elem<T>::to_f32(vals, e);
 #pragma unroll
     for (int m = 1; m < PIECES; m <<= 1) dot += lane_xor(dot, m);
-    const int j = j0 + round * RPR + rr;
-    if (piece == 0) {
-      const float v = j < c ? scale * dot : -INFINITY;
-      sc[round * RPR + rr] = v;
-      if (j < c) out[j] = v;
-    }
+    if (piece == 0) sc[round * RPR + rr] = scale * dot;
   }
   __syncthreads();
-  // maxima of the slice's groups of DEC_GROUP chunks (-inf past the last chunk)
-  if (tid < DEC_ROWS / DEC_GROUP) {
-    float mx = -INFINITY;
-#pragma unroll 8
-    for (int e = 0; e < DEC_GROUP; ++e) mx = fmaxf(mx, sc[tid * DEC_GROUP + e]);
-    gmax[(int64_t)bh * decode_gmax_stride_d(Nmax) + s * (DEC_ROWS / DEC_GROUP) + tid] = mx;
+  if (tid >= 64) return;
+  // The slice's DEC_LIST best keys, by one wave.  Lane l holds scores 4l..4l+3.  The
+  // DEC_LIST-th largest of the 64 group maxima bounds the DEC_LIST-th largest score from
+  // below (those groups hold that many distinct scores at or above it), so only scores
+  // at or above it are sorted as keys.  Order bits of the scores (0 = no chunk) are
+  // compared as integers, which is the order of the keys' upper halves.
+  const int lane = tid;
+  const int nval = min(DEC_ROWS, c - j0);
+  const float4 v4 = reinterpret_cast<const float4*>(sc)[lane];
+  const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+  uint32_t ob[4];
+  uint32_t gmx = 0u;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    ob[u] = 4 * lane + u < nval ? ordered_bits(vv[u] + 0.0f) : 0u;
+    gmx = max(gmx, ob[u]);
   }
-}
-
-// Wave-wide bitonic sort, descending: afterwards lane i holds the i-th largest value.
-template <typename K> __device__ __forceinline__ K wave_sort_desc(K v, int lane) {
-#pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const K o = shfl_xor_any(v, stride);
-      const bool desc = (lane & size) == 0;
-      const bool lower = (lane & stride) == 0;
-      const K hi = v > o ? v : o, lo = v > o ? o : v;
-      v = (desc == lower) ? hi : lo;
-    }
-  }
-  return v;
-}
-
-// top[0..m-1] = the m best keys of the score row sc[0..c) (score desc, index asc), given the
-// maxima gm[] of its groups of DEC_GROUP chunks.  Run by one full wave.  Each lane holds
-// the maxima of groups lane, lane+64, ...; the m-th largest lane maximum is a lower bound
-// tau on the m-th best score (lane maxima are distinct candidates), so only groups whose
-// maximum reaches tau are read, and their scores >= tau are sorted exactly.
-__device__ void wave_select_topm(const float* __restrict__ sc, const float* __restrict__ gm, int c, int m,
-                                 uint64_t* top, uint64_t* surv, int* cg, int lane) {
-  constexpr int PER_LANE = 8;  // survivor slots per lane
-  constexpr int MAXG = (16384 / DEC_GROUP + 63) / 64;  // group maxima per lane at the chunk limit
-  const int ngroups = (c + DEC_GROUP - 1) / DEC_GROUP;
-  // every load of the row issued before any is used: one memory round trip
-  float gv[MAXG];
-#pragma unroll
-  for (int u = 0; u < MAXG; ++u) {
-    const int gi = lane + 64 * u;
-    gv[u] = gi < ngroups ? gm[gi] : -INFINITY;
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int u = 0; u < MAXG; ++u) mx = fmaxf(mx, gv[u]);
-  const float sorted = wave_sort_desc(mx, lane);
-  const float tau = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sorted), m - 1));
-  // groups whose maximum reaches tau, compacted in LDS; then one pass of loads per 64 of them
-  const uint64_t below = (1ull << lane) - 1ull;
-  int ncand = 0;
-#pragma unroll
-  for (int u = 0; u < MAXG; ++u) {
-    const int gi = lane + 64 * u;
-    const bool is = gi < ngroups && gv[u] >= tau;
-    const uint64_t mask = __ballot(is);
-    if (is) cg[ncand + __popcll(mask & below)] = gi;
-    ncand += __popcll(mask);
-  }
-  __builtin_amdgcn_wave_barrier();
-  uint64_t mine[PER_LANE];
+  const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)wave_sort_desc<uint32_t>(gmx, lane), DEC_LIST - 1);
   int cnt = 0;
-  bool ovf = false;
-  for (int p0 = 0; p0 < ncand; p0 += 64) {
-    const int gi = p0 + lane < ncand ? cg[p0 + lane] : -1;
-    if (gi < 0) continue;
-    const float4* gp = reinterpret_cast<const float4*>(sc + gi * DEC_GROUP);
-    float4 v4[DEC_GROUP / 4];
 #pragma unroll
-    for (int u = 0; u < DEC_GROUP / 4; ++u) v4[u] = gp[u];
+  for (int u = 0; u < 4; ++u) cnt += (ob[u] != 0u && ob[u] >= tau) ? 1 : 0;
+  int total;
+  const int pre = wave_excl_prefix_small(cnt, total);
+  __shared__ uint64_t surv[64];
+  uint64_t* out = lists + ((int64_t)bh * DEC_MAX_SLICES + s) * DEC_LIST;
+  if (total <= 64) {
+    int p = pre;
 #pragma unroll
-    for (int u = 0; u < DEC_GROUP / 4; ++u) {
-      const float vv[4] = {v4[u].x, v4[u].y, v4[u].z, v4[u].w};
+    for (int u = 0; u < 4; ++u)
+      if (ob[u] != 0u && ob[u] >= tau) surv[p++] = make_key(vv[u], j0 + 4 * lane + u);
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t key = wave_sort_desc<uint64_t>(lane < total ? surv[lane] : 0ull, lane);
+    if (lane < DEC_LIST) out[lane] = key;
+  } else {
+    // many scores tied at the bound: a tournament between the lanes' sorted quadruples
+    uint64_t kq[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = gi * DEC_GROUP + 4 * u + e;
-        if (j < c && vv[e] >= tau) {
+    for (int u = 0; u < 4; ++u) kq[u] = ob[u] != 0u ? make_key(vv[u], j0 + 4 * lane + u) : 0ull;
+    cmpswap_desc(kq[0], kq[1]);
+    cmpswap_desc(kq[2], kq[3]);
+    cmpswap_desc(kq[0], kq[2]);
+    cmpswap_desc(kq[1], kq[3]);
+    cmpswap_desc(kq[1], kq[2]);
+    int ptr = 0;
+    for (int r = 0; r < DEC_LIST; ++r) {
+      const uint64_t head = ptr == 0 ? kq[0] : ptr == 1 ? kq[1] : ptr == 2 ? kq[2] : ptr == 3 ? kq[3] : 0ull;
+      uint64_t best = head;
 #pragma unroll
-          for (int q = 0; q < PER_LANE; ++q)
-            if (q == cnt) mine[q] = make_key(vv[e], j);
-          ovf |= cnt >= PER_LANE;
-          ++cnt;
-        }
+      for (int msk = 1; msk < 64; msk <<= 1) {
+        const uint64_t o = shfl_xor_u64(best, msk);
+        best = o > best ? o : best;
       }
+      if (lane == 0) out[r] = best;
+      if (head == best && best != 0ull) ++ptr;
     }
   }
-  // exclusive prefix of the per-lane counts
-  int pre = cnt;
+}
+
+// top[0..m-1] = the m best keys of the union of S sorted lists of DEC_LIST keys
+// (0 = no chunk).  Run by one full wave; lane l holds list l.  The m-th largest
+// of the first R = ceil(m/S) keys of every list bounds the m-th best key from below
+// (S*R >= m distinct keys), so only keys at or above it take part in the exact sort;
+// the bound is taken on the keys' upper halves (the score order bits), which can only
+// let in more keys.  When more than 64 keys reach it, m rounds of a tournament between
+// the list heads give the same answer.
+__device__ void wave_merge_lists(const uint64_t* __restrict__ lists, int S, int m, uint64_t* top, uint64_t* surv,
+                                 int lane) {
+  const int R = (m + S - 1) / S;
+  const int nb = S * R;  // <= 64: S if S >= m, else below m + S
+  const uint32_t* hi_words = reinterpret_cast<const uint32_t*>(lists);
+  const uint32_t bhi = lane < nb ? hi_words[2 * ((lane % S) * DEC_LIST + lane / S) + 1] : 0u;
+  uint64_t mine[DEC_LIST];
+  {
+    const ulonglong2* lp = reinterpret_cast<const ulonglong2*>(lists + lane * DEC_LIST);
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(pre, off);
-    if (lane >= off) pre += o;
+    for (int u = 0; u < DEC_LIST / 2; ++u) {
+      const ulonglong2 v2 = lane < S ? lp[u] : make_ulonglong2(0ull, 0ull);
+      mine[2 * u] = v2.x;
+      mine[2 * u + 1] = v2.y;
+    }
   }
-  const int total = __builtin_amdgcn_readlane(pre, 63);
-  pre -= cnt;
-  const bool any_ovf = __ballot(ovf) != 0;
-  if (!any_ovf && total <= 64) {
+  const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)wave_sort_desc<uint32_t>(bhi, lane), m - 1);
+  int cnt = 0;
 #pragma unroll
-    for (int q = 0; q < PER_LANE; ++q)
-      if (q < cnt) surv[pre + q] = mine[q];
+  for (int r = 0; r < DEC_LIST; ++r) cnt += (mine[r] != 0ull && (uint32_t)(mine[r] >> 32) >= tau) ? 1 : 0;
+  int total;
+  const int pre = wave_excl_prefix_small(cnt, total);
+  if (total <= 64) {
+#pragma unroll
+    for (int r = 0; r < DEC_LIST; ++r)
+      if (r < cnt) surv[pre + r] = mine[r];
     __builtin_amdgcn_wave_barrier();
-    const uint64_t key = wave_sort_desc<uint64_t>(lane < total ? surv[lane] : (uint64_t)0, lane);
+    const uint64_t key = wave_sort_desc<uint64_t>(lane < total ? surv[lane] : 0ull, lane);
     if (lane < m) top[lane] = key;
   } else {
-    // many exact ties at the bound: m passes of "largest key below the previous one"
-    uint64_t prev = ~0ull;
+    int ptr = 0;
     for (int r = 0; r < m; ++r) {
-      uint64_t best = 0ull;
-      for (int j = lane; j < c; j += 64) {
-        const uint64_t key = make_key(sc[j], j);
-        if (key < prev && key > best) best = key;
-      }
+      uint64_t head = 0ull;
+#pragma unroll
+      for (int u = 0; u < DEC_LIST; ++u)
+        if (u == ptr) head = mine[u];
+      uint64_t best = head;
 #pragma unroll
       for (int msk = 1; msk < 64; msk <<= 1) {
         const uint64_t o = shfl_xor_u64(best, msk);
         best = o > best ? o : best;
       }
       if (lane == 0) top[r] = best;
-      prev = best;
+      if (head == best) ++ptr;  // keys are distinct: one lane advances
     }
   }
   __builtin_amdgcn_wave_barrier();
 }
 
-// One 1024-thread workgroup per head: wave 0 selects, then each of the 16 wavefronts
-// attends to one kept chunk (wave 0 also to a 17th), and the weighted per-chunk
-// outputs are fused in LDS in slot order.  No cross-workgroup communication.
+// One wave: softmax attention of the query (this lane's piece qv) over the nkeys keys of the
+// chunk starting at row0; writes the normalised output row to out[0..D).  A key row is
+// spread over PIECES lanes, KPR rows per round.
+template <typename T, int D>
+__device__ __forceinline__ void wave_attend_chunk(const T* __restrict__ Kc, const T* __restrict__ Vc, int64_t row0,
+                                                  int nkeys, const float (&qv)[16 / Elem<T>::bytes], float scale,
+                                                  float* scw, float* out, int lane) {
+  constexpr int EPP = 16 / Elem<T>::bytes;
+  constexpr int PIECES = D / EPP;
+  constexpr int KPR = 64 / PIECES;
+  // keys and values are requested together (one memory round trip) when a row spans at most 8
+  // lanes; wider rows load keys, then values, 8 rounds at a time
+  constexpr int UB = PIECES < 8 ? PIECES : 8;
+  constexpr bool JOINT = PIECES <= 8;
+  const int piece = lane % PIECES, kl = lane / PIECES;
+  int4 vraw[JOINT ? PIECES : 1];
+#pragma unroll
+  for (int u0 = 0; u0 < PIECES; u0 += UB) {
+    int4 kraw[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int key = (u0 + u) * KPR + kl;
+      const bool ok = key < nkeys;
+      kraw[u] = ok ? *reinterpret_cast<const int4*>(Kc + (row0 + key) * D + piece * EPP) : make_int4(0, 0, 0, 0);
+      if constexpr (JOINT)
+        vraw[u] = ok ? *reinterpret_cast<const int4*>(Vc + (row0 + key) * D + piece * EPP) : make_int4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      T vals[EPP];
+      __builtin_memcpy(vals, &kraw[u], 16);
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) dot += qv[e] * Elem<T>::to_f32(vals, e);
+#pragma unroll
+      for (int msk = 1; msk < PIECES; msk <<= 1) dot += lane_xor(dot, msk);
+      const int key = (u0 + u) * KPR + kl;
+      if (piece == 0) scw[key] = key < nkeys ? scale * dot : -INFINITY;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  const float v = scw[lane];
+  const float mx = wave_max(v);
+  const float p = __expf(v - mx);
+  const float sum = wave_sum(p);
+  __builtin_amdgcn_wave_barrier();
+  scw[lane] = p;
+  __builtin_amdgcn_wave_barrier();
+  float acc[EPP];
+#pragma unroll
+  for (int e = 0; e < EPP; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int u0 = 0; u0 < PIECES; u0 += UB) {
+    int4 raw[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      if constexpr (JOINT) {
+        raw[u] = vraw[u0 + u];
+      } else {
+        const int key = (u0 + u) * KPR + kl;
+        raw[u] = key < nkeys ? *reinterpret_cast<const int4*>(Vc + (row0 + key) * D + piece * EPP)
+                             : make_int4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      T vals[EPP];
+      __builtin_memcpy(vals, &raw[u], 16);
+      const float pk = scw[(u0 + u) * KPR + kl];
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) acc[e] += pk * Elem<T>::to_f32(vals, e);
+    }
+  }
+#pragma unroll
+  for (int msk = PIECES; msk < 64; msk <<= 1)
+#pragma unroll
+    for (int e = 0; e < EPP; ++e) acc[e] += lane_xor(acc[e], msk);
+  const float inv = 1.f / sum;
+  if (kl == 0) {
+#pragma unroll
+    for (int e = 0; e < EPP; ++e) out[piece * EPP + e] = acc[e] * inv;
+  }
+}
+
+// One 1024-thread workgroup per head.  Wave 0 merges the slice lists and computes the
+// fusion weights while wave 15 attends to the open chunk, which needs no selection; then
+// wavefront i attends to kept chunk i (split-K over the wavefronts), and the outputs are
+// fused in LDS in slot order.  No cross-workgroup communication.
 template <typename T, int D>
 __global__ __launch_bounds__(1024) void decode_attend_kernel(const T* __restrict__ q, const T* __restrict__ Kc,
                                                              const T* __restrict__ Vc, const T* __restrict__ Klm,
-                                                             const float* __restrict__ scores,
-                                                             const float* __restrict__ gmax, T* __restrict__ o,
+                                                             const uint64_t* __restrict__ lists, T* __restrict__ o,
                                                              int32_t* __restrict__ idx, float* __restrict__ wout,
                                                              int64_t n, int64_t Lmax, int64_t Nmax, int k,
                                                              float scale) {
   constexpr int EPP = 16 / Elem<T>::bytes;
-  constexpr int PIECES = D / EPP;   // 16-byte pieces per row (8 or 16 for bf16)
-  constexpr int KPR = 64 / PIECES;  // keys per round when a row is spread over PIECES lanes
+  constexpr int PIECES = D / EPP;
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c = (int)(n / 64);
   const int m = min(k, c);
+  const int S = (c + DEC_ROWS - 1) / DEC_ROWS;
   __shared__ uint64_t top[16];
   __shared__ uint64_t surv[64];
-  __shared__ int cgl[DEC_MAX_GROUPS];
-  __shared__ float qs[D];
   __shared__ float sc_w[16][64];
   __shared__ float po[17][D];
-  __shared__ float s_own_s;
   __shared__ float wsl[17];
-  for (int e = tid; e < D; e += 1024) qs[e] = Elem<T>::to_f32(q, (int64_t)bh * D + e);
-  if (wv == 0 && m > 0)
-    wave_select_topm(scores + (int64_t)bh * decode_score_stride_d(Nmax), gmax + (int64_t)bh * decode_gmax_stride_d(Nmax),
-                     c, m, top, surv, cgl, lane);
-  __syncthreads();
-  if (wv == 1) {
-    float dot = 0.f;
-    for (int e = lane; e < D; e += 64) dot += qs[e] * Elem<T>::to_f32(Klm, ((int64_t)bh * Nmax + c) * D + e);
+  const int piece = lane % PIECES;
+  float qv[EPP];
 #pragma unroll
-    for (int msk = 1; msk < 64; msk <<= 1) dot += lane_xor(dot, msk);
-    if (lane == 0) s_own_s = scale * dot;
-  }
-  __syncthreads();
+  for (int e = 0; e < EPP; ++e) qv[e] = Elem<T>::to_f32(q, (int64_t)bh * D + piece * EPP + e);
+  const T* Kh = Kc + (int64_t)bh * Lmax * D;
+  const T* Vh = Vc + (int64_t)bh * Lmax * D;
   if (wv == 0) {
-    // fusion weights of the kept slots (lane i < m: past slot i; lane 16: own chunk)
+    // score of the open chunk (its landmark row is given), then the selection and the weights
+    float dot = 0.f;
+    for (int e = lane; e < D; e += 64)
+      dot += Elem<T>::to_f32(q, (int64_t)bh * D + e) * Elem<T>::to_f32(Klm, ((int64_t)bh * Nmax + c) * D + e);
+    const float s_own = scale * wave_sum(dot);
+    if (m > 0) wave_merge_lists(lists + (int64_t)bh * DEC_MAX_SLICES * DEC_LIST, S, m, top, surv, lane);
     const bool used = lane < m || lane == 16;
-    const float sv = lane < m ? key_score(top[lane]) : (lane == 16 ? s_own_s : -INFINITY);
-    float smax = sv;
-#pragma unroll
-    for (int msk = 1; msk < 64; msk <<= 1) smax = fmaxf(smax, lane_xor(smax, msk));
+    const float sv = lane < m ? key_score(top[lane]) : (lane == 16 ? s_own : -INFINITY);
+    const float smax = wave_max(sv);
     const float ev = used ? __expf(sv - smax) : 0.f;
-    float den = ev;
-#pragma unroll
-    for (int msk = 1; msk < 64; msk <<= 1) den += lane_xor(den, msk);
+    const float den = wave_sum(ev);
     if (lane < 17) wsl[lane] = ev / den;
+  } else if (wv == 15) {
+    wave_attend_chunk<T, D>(Kh, Vh, (int64_t)c * 64, (int)(n - (int64_t)c * 64) + 1, qv, scale, sc_w[wv], po[16],
+                            lane);
   }
   __syncthreads();
-  const int piece = lane % PIECES, kl = lane / PIECES;
-  for (int item = wv; item <= m; item += 16) {
-    const int r = item < m ? item : k;
-    const int j = item < m ? key_index(top[item]) : c;
-    const int nkeys = item < m ? 64 : (int)(n - (int64_t)c * 64) + 1;
-    const int64_t row0 = (int64_t)bh * Lmax + (int64_t)j * 64;
-    // keys and values of the chunk are requested together (one memory round trip) when a row
-    // spans at most 8 lanes; wider rows load keys, then values, 8 rounds at a time.  A row is
-    // spread over PIECES lanes, KPR rows per round.
-    constexpr int UB = PIECES < 8 ? PIECES : 8;
-    constexpr bool JOINT = PIECES <= 8;
-    int4 vraw[JOINT ? PIECES : 1];
-#pragma unroll
-    for (int u0 = 0; u0 < PIECES; u0 += UB) {
-      int4 kraw[UB];
-#pragma unroll
-      for (int u = 0; u < UB; ++u) {
-        const int key = (u0 + u) * KPR + kl;
-        const bool ok = key < nkeys;
-        kraw[u] = ok ? *reinterpret_cast<const int4*>(Kc + (row0 + key) * D + piece * EPP) : make_int4(0, 0, 0, 0);
-        if constexpr (JOINT)
-          vraw[u] = ok ? *reinterpret_cast<const int4*>(Vc + (row0 + key) * D + piece * EPP) : make_int4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < UB; ++u) {
-        T vals[EPP];
-        __builtin_memcpy(vals, &kraw[u], 16);
-        float dot = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPP; ++e) dot += qs[piece * EPP + e] * Elem<T>::to_f32(vals, e);
-#pragma unroll
-        for (int msk = 1; msk < PIECES; msk <<= 1) dot += lane_xor(dot, msk);
-        const int key = (u0 + u) * KPR + kl;
-        if (piece == 0) sc_w[wv][key] = key < nkeys ? scale * dot : -INFINITY;
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    const float v = sc_w[wv][lane];
-    float mx = v;
-#pragma unroll
-    for (int msk = 1; msk < 64; msk <<= 1) mx = fmaxf(mx, lane_xor(mx, msk));
-    const float p = __expf(v - mx);
-    float sum = p;
-#pragma unroll
-    for (int msk = 1; msk < 64; msk <<= 1) sum += lane_xor(sum, msk);
-    __builtin_amdgcn_wave_barrier();
-    sc_w[wv][lane] = p;
-    __builtin_amdgcn_wave_barrier();
-    float acc[EPP];
-#pragma unroll
-    for (int e = 0; e < EPP; ++e) acc[e] = 0.f;
-#pragma unroll
-    for (int u0 = 0; u0 < PIECES; u0 += UB) {
-      int4 raw[UB];
-#pragma unroll
-      for (int u = 0; u < UB; ++u) {
-        if constexpr (JOINT) {
-          raw[u] = vraw[u0 + u];
-        } else {
-          const int key = (u0 + u) * KPR + kl;
-          raw[u] = key < nkeys ? *reinterpret_cast<const int4*>(Vc + (row0 + key) * D + piece * EPP)
-                               : make_int4(0, 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < UB; ++u) {
-        T vals[EPP];
-        __builtin_memcpy(vals, &raw[u], 16);
-        const float pk = sc_w[wv][(u0 + u) * KPR + kl];
-#pragma unroll
-        for (int e = 0; e < EPP; ++e) acc[e] += pk * Elem<T>::to_f32(vals, e);
-      }
-    }
-#pragma unroll
-    for (int msk = PIECES; msk < 64; msk <<= 1)
-#pragma unroll
-      for (int e = 0; e < EPP; ++e) acc[e] += lane_xor(acc[e], msk);
-    const int slot = item < m ? item : 16;
-    const float f = wsl[slot] / sum;
-    if (kl == 0) {
-#pragma unroll
-      for (int e = 0; e < EPP; ++e) po[slot][piece * EPP + e] = f * acc[e];
-    }
-    (void)r;
-  }
+  if (wv < m)
+    wave_attend_chunk<T, D>(Kh, Vh, (int64_t)key_index(top[wv]) * 64, 64, qv, scale, sc_w[wv], po[wv], lane);
   __syncthreads();
   for (int e = tid; e < D; e += 1024) {
     float acc = 0.f;
-    for (int i = 0; i < m; ++i) acc += po[i][e];
-    acc += po[16][e];
+    for (int i = 0; i < m; ++i) acc += wsl[i] * po[i][e];
+    acc += wsl[16] * po[16][e];
     Elem<T>::store(o, (int64_t)bh * D + e, acc);
   }
   if (tid <= k) {
@@ -369,9 +363,9 @@ static hipError_t decode_t(const void* q, const void* k_new, const void* v_new, 
                            float scale, const DecodeBufs& ws, hipStream_t st) {
   const int S = decode_slices(n);
   HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D>), dim3(S > 0 ? S : 1, BH), dim3(256), 0, st, (const T*)q,
-              (const T*)k_new, (const T*)v_new, (T*)Kc, (T*)Vc, (const T*)Klm, ws.scores, ws.gmax, n, Lmax, Nmax, scale);
-  HILS_LAUNCH("decode_attend", (decode_attend_kernel<T, D>), dim3(BH), dim3(1024), 0, st, (const T*)q, (const T*)Kc,
-              (const T*)Vc, (const T*)Klm, ws.scores, ws.gmax, (T*)o, idx, w, n, Lmax, Nmax, k, scale);
+              (const T*)k_new, (const T*)v_new, (T*)Kc, (T*)Vc, (const T*)Klm, ws.lists, n, Lmax, Nmax, scale);
+  HILS_LAUNCH("decode_attend", (decode_attend_kernel<T, D>), dim3(BH), dim3(1024), 0, st, (const T*)q,
+              (const T*)Kc, (const T*)Vc, (const T*)Klm, ws.lists, (T*)o, idx, w, n, Lmax, Nmax, k, scale);
   return hipGetLastError();
 }
 

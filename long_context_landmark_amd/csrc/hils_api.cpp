@@ -125,9 +125,8 @@ size_t carve_bwd(void* base, const Dims& D, hils::BwdBufs* ws) {
 
 size_t carve_decode(void* base, int64_t BH, int64_t Lmax, int64_t d, int64_t k, hils::DecodeBufs* ws) {
   Carver cv(base);
-  const int64_t Nmax = (Lmax + 63) / 64;
-  ws->scores = cv.take<float>((size_t)(BH * hils::decode_score_stride(Nmax)));
-  ws->gmax = cv.take<float>((size_t)(BH * hils::decode_gmax_stride(Nmax)));
+  ws->lists = cv.take<uint64_t>((size_t)(BH * hils::decode_max_slices() * hils::decode_list_len()));
+  (void)Lmax;
   (void)d;
   (void)k;
   return cv.off;

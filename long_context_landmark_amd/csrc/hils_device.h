@@ -178,13 +178,13 @@ template <typename K> __device__ __forceinline__ void bitonic_merge16_desc(K (&a
 __device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v, int mask) {
   const int iv = (int)v;
   switch (mask) {
-    case 1: return (uint32_t)__builtin_amdgcn_update_dpp(iv, iv, 0xB1, 0xF, 0xF, false);
-    case 2: return (uint32_t)__builtin_amdgcn_update_dpp(iv, iv, 0x4E, 0xF, 0xF, false);
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true);
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true);
     case 4: {
-      const int h = __builtin_amdgcn_update_dpp(iv, iv, 0x141, 0xF, 0xF, false);
-      return (uint32_t)__builtin_amdgcn_update_dpp(h, h, 0x1B, 0xF, 0xF, false);
+      const int h = __builtin_amdgcn_mov_dpp(iv, 0x141, 0xF, 0xF, true);
+      return (uint32_t)__builtin_amdgcn_mov_dpp(h, 0x1B, 0xF, 0xF, true);
     }
-    case 8: return (uint32_t)__builtin_amdgcn_update_dpp(iv, iv, 0x128, 0xF, 0xF, false);
+    case 8: return (uint32_t)__builtin_amdgcn_mov_dpp(iv, 0x128, 0xF, 0xF, true);
     case 16: {
       const auto sw = __builtin_amdgcn_permlane16_swap(v, v, false, false);
       return (__lane_id() & 16) ? sw[0] : sw[1];
@@ -207,6 +207,23 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return lane_xor(v, mask); }
 __device__ __forceinline__ uint64_t shfl_xor_any(uint64_t v, int m) { return shfl_xor_u64(v, m); }
 __device__ __forceinline__ float shfl_xor_any(float v, int m) { return shfl_xor_f(v, m); }
+__device__ __forceinline__ uint32_t shfl_xor_any(uint32_t v, int m) { return lane_xor_u32(v, m); }
+
+// Wave-wide bitonic sort, descending: afterwards lane i holds the i-th largest value.
+// Each stage keeps, per lane, the partner's value when it is larger and this lane
+// keeps the maximum of the pair, or smaller and it keeps the minimum.
+template <typename K> __device__ __forceinline__ K wave_sort_desc(K v, int lane) {
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const K o = shfl_xor_any(v, stride);
+      const bool keep_max = ((lane & size) == 0) == ((lane & stride) == 0);
+      v = ((o > v) == keep_max) ? o : v;
+    }
+  }
+  return v;
+}
 
 // Butterfly reductions over all 64 lanes (every lane receives the result).
 __device__ __forceinline__ float wave_sum(float v) {

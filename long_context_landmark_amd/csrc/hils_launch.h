@@ -50,12 +50,11 @@ hipError_t launch_own_combine(int dt, int d, const void* Q, const void* K, const
 inline int fwd_pairs_per_item(int N) { return N <= 1024 ? 256 : 1024; }
 
 struct DecodeBufs {
-  float* scores;  // [BH][decode_score_stride(N_max)] landmark scores of the step
-  float* gmax;    // [BH][decode_gmax_stride(N_max)] maxima of groups of 32 consecutive scores
+  uint64_t* lists;  // [BH][decode_max_slices()][decode_list_len()] best (score, chunk) keys of every slice
 };
 int decode_slices(int64_t n_ctx);
-int64_t decode_score_stride(int64_t Nmax);
-int64_t decode_gmax_stride(int64_t Nmax);
+int decode_max_slices();
+int decode_list_len();
 
 struct BwdBufs {
   RouteBufs rb;
