@@ -34,86 +34,136 @@ template <typename T, int D> struct ChunkLds {
 };
 
 // Stage chunk rows [row0, row0+64) of K (as [key][d]) and V (as V^T [d][key]) into LDS.
+// Every load is issued before the first LDS write (one memory round trip).
 template <typename T, int D>
 __device__ __forceinline__ void stage_chunk(ChunkLds<T, D>& s, const T* __restrict__ K, const T* __restrict__ V,
                                             int64_t row0) {
   constexpr int PER_ROW = D * Elem<T>::bytes / 16;  // 16-byte pieces per row
   constexpr int EPP = 16 / Elem<T>::bytes;           // elements per piece
+  constexpr int NP = 64 * PER_ROW / 256;             // pieces per thread
   const int tid = threadIdx.x;
-  for (int p = tid; p < 64 * PER_ROW; p += 256) {
+  int4 kv[NP], vv[NP];
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const int p = tid + 256 * u;
     const int key = p / PER_ROW, e0 = (p % PER_ROW) * EPP;
-    const int4 kv = *reinterpret_cast<const int4*>(K + (row0 + key) * D + e0);
-    *reinterpret_cast<int4*>(&s.k[key * ChunkLds<T, D>::KS + e0]) = kv;
-    const int4 vv = *reinterpret_cast<const int4*>(V + (row0 + key) * D + e0);
+    kv[u] = *reinterpret_cast<const int4*>(K + (row0 + key) * D + e0);
+    vv[u] = *reinterpret_cast<const int4*>(V + (row0 + key) * D + e0);
+  }
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const int p = tid + 256 * u;
+    const int key = p / PER_ROW, e0 = (p % PER_ROW) * EPP;
+    *reinterpret_cast<int4*>(&s.k[key * ChunkLds<T, D>::KS + e0]) = kv[u];
     T vals[EPP];
-    __builtin_memcpy(vals, &vv, 16);
+    __builtin_memcpy(vals, &vv[u], 16);
 #pragma unroll
     for (int e = 0; e < EPP; ++e) s.vt[(e0 + e) * ChunkLds<T, D>::VS + key] = vals[e];
   }
 }
 
-// One wave: attention of 16 query rows (given as B fragments) over the 64 keys in LDS.
-// mask_q >= 0 applies the causal mask key <= mask_q + (query index inside the block);
-// returns o (unnormalised, 4 rows of d per 16-d block), the row max and the row sum.
-template <typename T, int D>
-__device__ __forceinline__ void wave_chunk_attention(const ChunkLds<T, D>& s, const Frag<T> (&qf)[D / 32],
-                                                     float scale, int causal_q, f32x4_t (&o)[D / 16], float& mx,
-                                                     float& sum) {
-  const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+// The MFMA operand fragments of one staged chunk as a wave uses them: K rows (A operand of
+// S^T = K Q^T) and V^T rows (A operand of O^T = V^T P^T).  With REG they are read from LDS
+// once and stay in registers for every query tile the wave runs against the chunk (64 + 64
+// registers at d = 128 in bf16); otherwise each use reads LDS.
+template <typename T, int D, bool REG> struct ChunkFrags;
+template <typename T, int D> struct ChunkFrags<T, D, true> {
+  Frag<T> kf[4][D / 32];
+  Frag<T> vf[D / 16][2];
+  __device__ __forceinline__ void init(const ChunkLds<T, D>& s) {
+    const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) kf[cb][ks].load(&s.k[(16 * cb + r16) * ChunkLds<T, D>::KS + ks * 32 + 8 * g]);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const T* row = &s.vt[(16 * db + r16) * ChunkLds<T, D>::VS + 32 * h + 4 * g];
+        vf[db][h].load4x2(row, row + 16);
+      }
+  }
+  __device__ __forceinline__ const Frag<T>& k(const ChunkLds<T, D>&, int cb, int ks) const { return kf[cb][ks]; }
+  __device__ __forceinline__ const Frag<T>& v(const ChunkLds<T, D>&, int db, int h) const { return vf[db][h]; }
+};
+template <typename T, int D> struct ChunkFrags<T, D, false> {
+  __device__ __forceinline__ void init(const ChunkLds<T, D>&) {}
+  __device__ __forceinline__ Frag<T> k(const ChunkLds<T, D>& s, int cb, int ks) const {
+    const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+    Frag<T> a;
+    a.load(&s.k[(16 * cb + r16) * ChunkLds<T, D>::KS + ks * 32 + 8 * g]);
+    return a;
+  }
+  __device__ __forceinline__ Frag<T> v(const ChunkLds<T, D>& s, int db, int h) const {
+    const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+    Frag<T> a;
+    const T* row = &s.vt[(16 * db + r16) * ChunkLds<T, D>::VS + 32 * h + 4 * g];
+    a.load4x2(row, row + 16);
+    return a;
+  }
+};
+// fragments in registers except for fp32 at d = 128, which would need 256 registers for them
+template <typename T, int D> constexpr bool frags_in_regs() { return Elem<T>::bytes == 2 || D == 64; }
+
+// One wave: attention of 16 query rows (given as B fragments) over the 64 keys of a chunk.
+// causal_q >= 0 applies the causal mask key <= causal_q (the lane's query index inside the
+// chunk).  Returns o = wt * softmax(scale * q K^T) V (4 rows of d per 16-d block; wt is the
+// lane's query weight), the row's scaled maximum and its sum of exponentials relative to it.
+// The exponentials are exp2 of one fused multiply-add: scale * log2(e) is folded into the
+// raw scores, and wt / sum into the probabilities before they are rounded for the PV product.
+template <typename T, int D, bool REG>
+__device__ __forceinline__ void wave_chunk_attention(const ChunkLds<T, D>& s, const ChunkFrags<T, D, REG>& cf,
+                                                     const Frag<T> (&qf)[D / 32], float scale, int causal_q, float wt,
+                                                     f32x4_t (&o)[D / 16], float& mx, float& sum) {
+  const int lane = threadIdx.x & 63, g = lane >> 4;
   f32x4_t sc[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     sc[cb] = zero4();
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      Frag<T> a;
-      a.load(&s.k[(16 * cb + r16) * ChunkLds<T, D>::KS + ks * 32 + 8 * g]);
-      mma(sc[cb], a, qf[ks]);
-    }
+    for (int ks = 0; ks < D / 32; ++ks) mma(sc[cb], cf.k(s, cb, ks), qf[ks]);
   }
   // lane holds query r16, keys 16cb + 4g + i
-  mx = -INFINITY;
+  float mraw = -INFINITY;
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float v = scale * sc[cb][i];
-      if (causal_q >= 0 && 16 * cb + 4 * g + i > causal_q) v = -INFINITY;
-      sc[cb][i] = v;
-      mx = fmaxf(mx, v);
+      if (causal_q >= 0 && 16 * cb + 4 * g + i > causal_q) sc[cb][i] = -INFINITY;
+      mraw = fmaxf(mraw, sc[cb][i]);
     }
-  mx = fmaxf(mx, lane_xor(mx, 16));
-  mx = fmaxf(mx, lane_xor(mx, 32));
+  mraw = fmaxf(mraw, lane_xor(mraw, 16));
+  mraw = fmaxf(mraw, lane_xor(mraw, 32));
+  const float c2 = scale * 1.44269504088896341f;  // scale * log2(e)
+  const float off = -mraw * c2;
   sum = 0.f;
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float p = __expf(sc[cb][i] - mx);
+      const float p = __builtin_amdgcn_exp2f(fmaf(sc[cb][i], c2, off));
       sc[cb][i] = p;
       sum += p;
     }
   sum += lane_xor(sum, 16);
   sum += lane_xor(sum, 32);
+  mx = scale * mraw;
+  const float f = wt * __builtin_amdgcn_rcpf(sum);
   // O^T[d][q] = sum_key V^T[d][key] P^T[key][q]; element e of lane group g is key 32h + 16(e/4) + 4g + e%4
   Frag<T> pf[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     float pv[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pv[e] = sc[2 * h + e / 4][e % 4];
+    for (int e = 0; e < 8; ++e) pv[e] = f * sc[2 * h + e / 4][e % 4];
     pf[h].set(pv);
   }
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) {
     o[db] = zero4();
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      Frag<T> vf;
-      const T* row = &s.vt[(16 * db + r16) * ChunkLds<T, D>::VS + 32 * h + 4 * g];
-      vf.load4x2(row, row + 16);
-      mma(o[db], vf, pf[h]);
-    }
+    for (int h = 0; h < 2; ++h) mma(o[db], cf.v(s, db, h), pf[h]);
   }
 }
 
@@ -123,8 +173,9 @@ __global__ __launch_bounds__(256) void chunk_attn_fwd_kernel(const T* __restrict
                                                              const int4* __restrict__ items,
                                                              const int* __restrict__ n_items,
                                                              const int* __restrict__ pairs,
-                                                             const float* __restrict__ w, float* __restrict__ lse,
-                                                             uint16_t* __restrict__ partial, int L, int N, int k,
+                                                             const float* __restrict__ w, float* __restrict__ lse_pair,
+                                                             uint16_t* __restrict__ partial, uint16_t* __restrict__ trash,
+                                                             float* __restrict__ trash_lse, int L, int N, int k,
                                                              int max_items, int ppi, float scale) {
   int item, bh;
   xcd_map(item, bh);
@@ -141,110 +192,206 @@ __global__ __launch_bounds__(256) void chunk_attn_fwd_kernel(const T* __restrict
   const int* pl = pairs + (int64_t)bh * L * k;
   const T* Qb = Q + (int64_t)bh * L * D;
   const int k1 = k + 1;
-  // software pipeline over 64-pair tiles: pair entries two tiles ahead, query rows one tile ahead
-  auto pair_at = [&](int base) { const int pidx = base + 16 * w_ + r16; return pidx < p1 ? pl[pidx] : -1; };
+  // Software pipeline over 64-pair tiles with three register sets used in turn, so no loaded
+  // value is ever copied: while tile i runs on one set, the query rows and fusion weights of
+  // tiles i+1 and i+2 are in flight in the other two and the pair entries of tile i+3 are
+  // read.  Loads are unconditional (clamped to valid rows; rows of absent pairs are computed
+  // and dropped) so that every wait covers exactly the data about to be used.
+  auto pair_raw = [&](int base) { return pl[min(base + 16 * w_ + r16, p1 - 1)]; };
+  auto pair_ok = [&](int base) { return base + 16 * w_ + r16 < p1; };
   auto load_q = [&](int pe, Frag<T>(&qf)[D / 32]) {
+    const int64_t t = pe >= 0 ? (pe >> 5) : 0;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      if (pe >= 0) qf[ks].load(Qb + (int64_t)(pe >> 5) * D + ks * 32 + 8 * g);
-      else qf[ks].zero();
-    }
+    for (int ks = 0; ks < D / 32; ++ks) qf[ks].load(Qb + t * D + ks * 32 + 8 * g);
   };
-  int pe_cur = pair_at(p0), pe_nxt = pair_at(p0 + 64);
-  Frag<T> q_cur[D / 32], q_nxt[D / 32];
-  load_q(pe_cur, q_cur);
-  stage_chunk<T, D>(s, K + (int64_t)bh * L * D, V + (int64_t)bh * L * D, (int64_t)j * 64);
-  __syncthreads();
-  for (int base = p0; base < p1; base += 64) {
-    const bool more = base + 64 < p1;
-    if (more) load_q(pe_nxt, q_nxt);
-    const int pe_after = (base + 128 < p1) ? pair_at(base + 128) : -1;
+  auto load_w = [&](int pe) {
+    const int64_t t = pe >= 0 ? (pe >> 5) : 0;
+    return w[((int64_t)bh * L + t) * k1 + (pe >= 0 ? (pe & 31) : 0)];
+  };
+  ChunkFrags<T, D, frags_in_regs<T, D>()> cf;
+  // Results go to the pairs' own positions in the list, so a tile's 64 rows are consecutive.
+  // With the chunk's fragments in registers the staging LDS is free after they are read: each
+  // wave then turns its 16 output rows around there and stores them as whole rows (16 bytes a
+  // lane, 1 KiB a store).  Rows of absent pairs go to a scratch row: every lane stores, so
+  // the waits on the loads of the next tiles can count the stores.
+  constexpr bool ROWS = frags_in_regs<T, D>();
+  constexpr int RSB = D + 8;  // row stride of the turnaround buffer (bf16 elements)
+  uint16_t* rowbuf = reinterpret_cast<uint16_t*>(&s) + w_ * 16 * RSB;
+  static_assert(!ROWS || 4 * 16 * RSB * 2 <= (int)sizeof(ChunkLds<T, D>), "turnaround buffer fits the staging LDS");
+  auto tile = [&](const Frag<T>(&qf)[D / 32], float wf, int pe, int base) {
     f32x4_t o[D / 16];
     float mx, sum;
-    wave_chunk_attention<T, D>(s, q_cur, scale, -1, o, mx, sum);
-    if (pe_cur >= 0) {
-      const int t = pe_cur >> 5, r = pe_cur & 31;
-      const int64_t prow = (int64_t)bh * L + t;
-      const float f = w[prow * k1 + r] / sum;
-      uint16_t* dst = partial + (prow * k + r) * D;
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        u16x4_t v4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v4[i] = f32_to_bf16(f * o[db][i]);
-        *reinterpret_cast<u16x4_t*>(dst + 16 * db + 4 * g) = v4;
-      }
-      if (lse && g == 0) lse[prow * k1 + r] = mx + __logf(sum);
-    }
-    if (more) {
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) q_cur[ks] = q_nxt[ks];
-    }
-    pe_cur = pe_nxt;
-    pe_nxt = pe_after;
-  }
-}
-
-template <typename T, int D>
-__global__ __launch_bounds__(256) void own_combine_kernel(const T* __restrict__ Q, const T* __restrict__ K,
-                                                          const T* __restrict__ V, const int32_t* __restrict__ idx,
-                                                          const float* __restrict__ w,
-                                                          const uint16_t* __restrict__ partial, T* __restrict__ O,
-                                                          float* __restrict__ lse, int L, int N, int k, float scale) {
-  int c, bh;
-  xcd_map(c, bh);
-  __shared__ ChunkLds<T, D> s;
-  stage_chunk<T, D>(s, K + (int64_t)bh * L * D, V + (int64_t)bh * L * D, (int64_t)c * 64);
-  __syncthreads();
-  const int tid = threadIdx.x, w_ = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
-  const int qi = 16 * w_ + r16;  // query inside the chunk
-  const int64_t prow = (int64_t)bh * L + (int64_t)c * 64 + qi;
-  Frag<T> qf[D / 32];
-#pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) qf[ks].load(Q + prow * D + ks * 32 + 8 * g);
-  f32x4_t o[D / 16];
-  float mx, sum;
-  wave_chunk_attention<T, D>(s, qf, scale, qi, o, mx, sum);
-  const int k1 = k + 1;
-  const int m = min(k, c);
-  const float f = w[prow * k1 + k] / sum;
-  float acc[D / 16][4];
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[db][i] = 0.f;
-  // kept-slot flags first, then the partial rows four slots at a time (loads in flight together)
-  bool kept[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) kept[r] = r < m && idx[prow * k1 + r] >= 0;
-#pragma unroll
-  for (int r0 = 0; r0 < 16; r0 += 4) {
-    if (r0 >= m) break;
-    u16x4_t v[4][D / 16];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint16_t* src = partial + (prow * k + r0 + u) * D;
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        if (kept[r0 + u]) v[u][db] = *reinterpret_cast<const u16x4_t*>(src + 16 * db + 4 * g);
-        else v[u][db] = u16x4_t{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
+    wave_chunk_attention(s, cf, qf, scale, -1, wf, o, mx, sum);
+    const bool ok = pe >= 0;
+    const int64_t prow = (int64_t)bh * L * k + base + 16 * w_ + r16;
+    if constexpr (ROWS) {
+      constexpr int PPR = D / 8, RPI = 64 / PPR;  // 16-byte pieces per row, rows per store
 #pragma unroll
       for (int db = 0; db < D / 16; ++db)
+        *reinterpret_cast<uint2*>(rowbuf + r16 * RSB + 16 * db + 4 * g) =
+            make_uint2(pack_bf16x2(o[db][0], o[db][1]), pack_bf16x2(o[db][2], o[db][3]));
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[db][i] += bf16_to_f32(v[u][db][i]);
+      for (int it = 0; it < 16 / RPI; ++it) {
+        const int row = it * RPI + lane / PPR, pc = lane % PPR;
+        const uint4 v = *reinterpret_cast<const uint4*>(rowbuf + row * RSB + 8 * pc);
+        const int pidx = base + 16 * w_ + row;
+        uint16_t* dst = pidx < p1 ? partial + ((int64_t)bh * L * k + pidx) * D : trash;
+        *reinterpret_cast<uint4*>(dst + 8 * pc) = v;
+      }
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      uint16_t* dst = ok ? partial + prow * D : trash;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const uint2 v2 = make_uint2(pack_bf16x2(o[db][0], o[db][1]), pack_bf16x2(o[db][2], o[db][3]));
+        *reinterpret_cast<uint2*>(dst + 16 * db + 4 * g) = v2;
+      }
+    }
+    // the four lane groups hold the same row statistics
+    *(ok ? lse_pair + prow : trash_lse) = mx + __logf(sum);
+  };
+  Frag<T> q0[D / 32], q1[D / 32], q2[D / 32];
+  float w0, w1, w2;
+  int pe0 = pair_ok(p0) ? pair_raw(p0) : -1;
+  int pe1 = pair_ok(p0 + 64) ? pair_raw(p0 + 64) : -1;
+  int pe2;
+  load_q(pe0, q0);
+  w0 = load_w(pe0);
+  load_q(pe1, q1);
+  w1 = load_w(pe1);
+  int raw = pair_raw(p0 + 128);
+  stage_chunk<T, D>(s, K + (int64_t)bh * L * D, V + (int64_t)bh * L * D, (int64_t)j * 64);
+  __syncthreads();
+  cf.init(s);
+  if constexpr (ROWS) __syncthreads();  // every wave holds its fragments: the staging LDS is reused
+  // one step: resolve the entry of tile base+128, start its loads into the free set, read the
+  // entry of tile base+192, run tile base
+#define HILS_FWD_STEP(QU, WU, PU, QF, WF, PF)                  \
+  PF = pair_ok(base + 128) ? raw : -1;                         \
+  load_q(PF, QF);                                              \
+  WF = load_w(PF);                                             \
+  raw = pair_raw(base + 192);                                  \
+  tile(QU, WU, PU, base);                                      \
+  base += 64;                                                  \
+  if (base >= p1) break;
+  for (int base = p0;;) {
+    HILS_FWD_STEP(q0, w0, pe0, q2, w2, pe2)
+    HILS_FWD_STEP(q1, w1, pe1, q0, w0, pe0)
+    HILS_FWD_STEP(q2, w2, pe2, q1, w1, pe1)
   }
+#undef HILS_FWD_STEP
+}
+
+// Per query chunk: the causal own-chunk tile on MFMA, then the fusion sum in row layout.
+// The weighted own output goes through LDS into rows; each thread then owns 16-byte pieces
+// of output rows and adds the same piece of the query's partial rows, which chunk_attn_fwd
+// stored at the pairs' list positions (pos_of): every partial row is read as whole
+// 128-byte lines, and O and lse are written row by row.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void own_combine_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                          const T* __restrict__ V, const int* __restrict__ pos_of,
+                                                          const float* __restrict__ w,
+                                                          const uint16_t* __restrict__ partial,
+                                                          const float* __restrict__ lse_pair, T* __restrict__ O,
+                                                          float* __restrict__ lse, int L, int N, int k, float scale) {
+  constexpr int RS = D + 4;         // row stride of the output rows in LDS (floats)
+  constexpr int PPR = D / 8;        // 8-element pieces per row
+  constexpr int NI = 64 * PPR / 256;  // pieces per thread
+  int c, bh;
+  xcd_map(c, bh);
+  __shared__ union {
+    ChunkLds<T, D> s;
+    float orow[64 * RS];
+  } u;
+  __shared__ int pos_s[64][16];
+  __shared__ float own_lse[64];
+  const int tid = threadIdx.x, w_ = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
+  const int qi = 16 * w_ + r16;  // query inside the chunk (MFMA layout)
+  const int64_t row0 = (int64_t)bh * L + (int64_t)c * 64;
+  const int k1 = k + 1;
+  // requested before the first wait: query rows, own weight, the list positions of the
+  // query chunk's pairs, the chunk's keys and values
+  Frag<T> qf[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) qf[ks].load(Q + (row0 + qi) * D + ks * 32 + 8 * g);
+  const float w_own = w[(row0 + qi) * k1 + k];
+  int pv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid + 256 * i;  // (query, slot) = (e / 16, e % 16); slots >= k are unused
+    pv[i] = (e % 16) < k ? pos_of[(row0 + e / 16) * k + (e % 16)] : -1;
+  }
+  stage_chunk<T, D>(u.s, K + (int64_t)bh * L * D, V + (int64_t)bh * L * D, (int64_t)c * 64);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pos_s[(tid + 256 * i) / 16][(tid + 256 * i) % 16] = pv[i];
+  __syncthreads();
+  f32x4_t o[D / 16];
+  float mx, sum;
+  ChunkFrags<T, D, false> cf;  // one tile: the fragments are read once either way
+  wave_chunk_attention(u.s, cf, qf, scale, qi, w_own, o, mx, sum);
+  __syncthreads();  // every wave is done with the keys and values: the rows reuse their space
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Elem<T>::store(O, prow * D + 16 * db + 4 * g + i, acc[db][i] + f * o[db][i]);
-  if (lse && g == 0) {
-    lse[prow * k1 + k] = mx + __logf(sum);
-    for (int r = 0; r < k; ++r)
-      if (r >= m || idx[prow * k1 + r] < 0) lse[prow * k1 + r] = -INFINITY;
+    for (int i = 0; i < 4; ++i) u.orow[qi * RS + 16 * db + 4 * g + i] = o[db][i];
+  if (g == 0) own_lse[qi] = mx + __logf(sum);
+  __syncthreads();
+  const int64_t pbase = (int64_t)bh * L * k;
+  float acc[NI][8];
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int e = tid + 256 * it, q = e / PPR, pc = e % PPR;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc[it][x] = u.orow[q * RS + 8 * pc + x];
+  }
+  // partial pieces of SB slots for every owned piece are in flight together; a slot whose
+  // position is -1 reads row 0 of the head's list and is dropped
+  constexpr int SB = NI == 2 ? 8 : 4;
+  const int m = min(k, 16);
+#pragma unroll
+  for (int r0 = 0; r0 < 16; r0 += SB) {
+    if (r0 >= m) break;
+    uint4 v[NI][SB];
+    bool kept[NI][SB];
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      const int e = tid + 256 * it, q = e / PPR, pc = e % PPR;
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        const int p = pos_s[q][r0 + sb];
+        kept[it][sb] = p >= 0;
+        v[it][sb] = *reinterpret_cast<const uint4*>(partial + (pbase + max(p, 0)) * D + 8 * pc);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < NI; ++it)
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        const uint32_t wds[4] = {v[it][sb].x, v[it][sb].y, v[it][sb].z, v[it][sb].w};
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          acc[it][2 * x] += kept[it][sb] ? __uint_as_float(wds[x] << 16) : 0.f;
+          acc[it][2 * x + 1] += kept[it][sb] ? __uint_as_float(wds[x] & 0xFFFF0000u) : 0.f;
+        }
+      }
+  }
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int e = tid + 256 * it, q = e / PPR, pc = e % PPR;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) Elem<T>::store(O, (row0 + q) * D + 8 * pc + x, acc[it][x]);
+  }
+  if (lse) {
+    for (int e = tid; e < 64 * k1; e += 256) {
+      const int q = e / k1, r = e % k1;
+      float v = own_lse[q];
+      if (r < k) {
+        const int p = pos_s[q][r];
+        v = p >= 0 ? lse_pair[pbase + p] : -INFINITY;
+      }
+      lse[row0 * k1 + e] = v;
+    }
   }
 }
 
@@ -278,39 +425,41 @@ __global__ __launch_bounds__(256) void fixed_selection_kernel(const T* __restric
 
 template <typename T, int D>
 static hipError_t chunk_attn_t(const void* Q, const void* K, const void* V, const RouteBufs& rb, const float* w,
-                               float* lse, uint16_t* partial, int BH, int L, int N, int k, float scale,
-                               hipStream_t st) {
+                               float* lse, uint16_t* partial, uint16_t* trash, float* trash_lse, int BH, int L, int N,
+                               int k, float scale, hipStream_t st) {
   HILS_LAUNCH("chunk_attn_fwd", (chunk_attn_fwd_kernel<T, D>), dim3(rb.max_items, BH), dim3(256), 0, st, (const T*)Q,
-                     (const T*)K, (const T*)V, rb.chunk_off, rb.items, rb.n_items, rb.pairs, w, lse, partial, L, N,
-                     k, rb.max_items, rb.pairs_per_item, scale);
+                     (const T*)K, (const T*)V, rb.chunk_off, rb.items, rb.n_items, rb.pairs, w, lse, partial, trash,
+                     trash_lse, L, N, k, rb.max_items, rb.pairs_per_item, scale);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t own_combine_t(const void* Q, const void* K, const void* V, const int32_t* idx, const float* w,
-                                const uint16_t* partial, void* O, float* lse, int BH, int L, int N, int k, float scale,
-                                hipStream_t st) {
+static hipError_t own_combine_t(const void* Q, const void* K, const void* V, const int* pos_of, const float* w,
+                                const uint16_t* partial, const float* lse_pair, void* O, float* lse, int BH, int L,
+                                int N, int k, float scale, hipStream_t st) {
   HILS_LAUNCH("own_combine", (own_combine_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)Q, (const T*)K,
-                     (const T*)V, idx, w, partial, (T*)O, lse, L, N, k, scale);
+              (const T*)V, pos_of, w, partial, lse_pair, (T*)O, lse, L, N, k, scale);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_attn_fwd(int dt, int d, const void* Q, const void* K, const void* V, const RouteBufs& rb,
-                                 const float* w, float* lse, uint16_t* partial, int BH, int L, int N, int k,
-                                 float scale, hipStream_t st) {
-  if (dt == 0) return d == 64 ? chunk_attn_t<bf16_t, 64>(Q, K, V, rb, w, lse, partial, BH, L, N, k, scale, st)
-                              : chunk_attn_t<bf16_t, 128>(Q, K, V, rb, w, lse, partial, BH, L, N, k, scale, st);
-  return d == 64 ? chunk_attn_t<float, 64>(Q, K, V, rb, w, lse, partial, BH, L, N, k, scale, st)
-                 : chunk_attn_t<float, 128>(Q, K, V, rb, w, lse, partial, BH, L, N, k, scale, st);
+                                 const float* w, float* lse, uint16_t* partial, uint16_t* trash, float* trash_lse,
+                                 int BH, int L, int N, int k, float scale, hipStream_t st) {
+  if (dt == 0)
+    return d == 64 ? chunk_attn_t<bf16_t, 64>(Q, K, V, rb, w, lse, partial, trash, trash_lse, BH, L, N, k, scale, st)
+                   : chunk_attn_t<bf16_t, 128>(Q, K, V, rb, w, lse, partial, trash, trash_lse, BH, L, N, k, scale, st);
+  return d == 64 ? chunk_attn_t<float, 64>(Q, K, V, rb, w, lse, partial, trash, trash_lse, BH, L, N, k, scale, st)
+                 : chunk_attn_t<float, 128>(Q, K, V, rb, w, lse, partial, trash, trash_lse, BH, L, N, k, scale, st);
 }
 
-hipError_t launch_own_combine(int dt, int d, const void* Q, const void* K, const void* V, const int32_t* idx,
-                              const float* w, const uint16_t* partial, void* O, float* lse, int BH, int L, int N, int k,
-                              float scale, hipStream_t st) {
-  if (dt == 0) return d == 64 ? own_combine_t<bf16_t, 64>(Q, K, V, idx, w, partial, O, lse, BH, L, N, k, scale, st)
-                              : own_combine_t<bf16_t, 128>(Q, K, V, idx, w, partial, O, lse, BH, L, N, k, scale, st);
-  return d == 64 ? own_combine_t<float, 64>(Q, K, V, idx, w, partial, O, lse, BH, L, N, k, scale, st)
-                 : own_combine_t<float, 128>(Q, K, V, idx, w, partial, O, lse, BH, L, N, k, scale, st);
+hipError_t launch_own_combine(int dt, int d, const void* Q, const void* K, const void* V, const int* pos_of,
+                              const float* w, const uint16_t* partial, const float* lse_pair, void* O, float* lse,
+                              int BH, int L, int N, int k, float scale, hipStream_t st) {
+  if (dt == 0)
+    return d == 64 ? own_combine_t<bf16_t, 64>(Q, K, V, pos_of, w, partial, lse_pair, O, lse, BH, L, N, k, scale, st)
+                   : own_combine_t<bf16_t, 128>(Q, K, V, pos_of, w, partial, lse_pair, O, lse, BH, L, N, k, scale, st);
+  return d == 64 ? own_combine_t<float, 64>(Q, K, V, pos_of, w, partial, lse_pair, O, lse, BH, L, N, k, scale, st)
+                 : own_combine_t<float, 128>(Q, K, V, pos_of, w, partial, lse_pair, O, lse, BH, L, N, k, scale, st);
 }
 
 hipError_t launch_fixed_selection(int dt, int d, const void* Q, const void* Klm, const int32_t* idx, float* sel,

@@ -1,7 +1,7 @@
 // C ABI of libhils: argument validation, workspace carving and kernel launches.
 // Every check runs on the host before any HIP call; see include/hils.h for the
 // contract of each entry point.
-#include "../../include/hils.h"
+#include "hils.h"
 
 #include <hip/hip_runtime.h>
 
@@ -85,8 +85,10 @@ struct Carver {
 struct FwdWs {
   hils::RouteBufs rb;
   uint16_t* partial;
+  uint16_t* trash;   // d elements: stores of absent pairs in the chunk-major kernel
+  float* trash_lse;
+  float* lse_pair;  // [BH][L*k] chunk log-partition of every pair, in list order
   float* w_tmp;
-  float* lse_tmp;
 };
 
 size_t carve_route(Carver& cv, const Dims& D, hils::RouteBufs& rb, int ppi) {
@@ -100,6 +102,7 @@ size_t carve_route(Carver& cv, const Dims& D, hils::RouteBufs& rb, int ppi) {
   rb.items = cv.take<int4>((size_t)BH * rb.max_items);
   rb.n_items = cv.take<int>((size_t)BH);
   rb.pairs = cv.take<int>((size_t)BH * D.L * D.k);
+  rb.pos_of = nullptr;
   return cv.off;
 }
 
@@ -107,9 +110,12 @@ size_t carve_fwd(void* base, const Dims& D, FwdWs* ws) {
   Carver cv(base);
   const int64_t BH = D.B * D.H;
   carve_route(cv, D, ws->rb, hils::fwd_pairs_per_item((int)D.N));
+  ws->rb.pos_of = cv.take<int>((size_t)BH * D.L * D.k);
   ws->partial = cv.take<uint16_t>((size_t)BH * D.L * D.k * D.d);
+  ws->lse_pair = cv.take<float>((size_t)BH * D.L * D.k);
   ws->w_tmp = cv.take<float>((size_t)BH * D.L * (D.k + 1));
-  ws->lse_tmp = cv.take<float>((size_t)BH * D.L * (D.k + 1));
+  ws->trash = cv.take<uint16_t>((size_t)D.d);
+  ws->trash_lse = cv.take<float>(64);
   return cv.off;
 }
 
@@ -245,11 +251,11 @@ hils_status hils_sparse_attn_fwd(const void* Q, const void* K, const void* V, co
   if (e != hipSuccess) return hip_status(e, "hils_sparse_attn_fwd: selection");
   if ((e = hils::launch_route(idx, W.rb, BH, iL, iN, ik, s)) != hipSuccess)
     return hip_status(e, "hils_sparse_attn_fwd: routing");
-  if ((e = hils::launch_chunk_attn_fwd(dt, id, Q, K, V, W.rb, w, lse_out, W.partial, BH, iL, iN, ik, scale, s)) !=
-      hipSuccess)
+  if ((e = hils::launch_chunk_attn_fwd(dt, id, Q, K, V, W.rb, w, W.lse_pair, W.partial, W.trash, W.trash_lse, BH, iL,
+                                       iN, ik, scale, s)) != hipSuccess)
     return hip_status(e, "hils_sparse_attn_fwd: chunk attention");
-  if ((e = hils::launch_own_combine(dt, id, Q, K, V, idx, w, W.partial, O, lse_out, BH, iL, iN, ik, scale, s)) !=
-      hipSuccess)
+  if ((e = hils::launch_own_combine(dt, id, Q, K, V, W.rb.pos_of, w, W.partial, W.lse_pair, O, lse_out, BH, iL, iN,
+                                    ik, scale, s)) != hipSuccess)
     return hip_status(e, "hils_sparse_attn_fwd: own chunk and fusion");
   return HILS_OK;
 }

@@ -23,11 +23,13 @@ struct bf16_t {  // storage type of a bf16 element
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// fp32 -> bf16, round to nearest even (inputs are finite in this library)
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even: gfx950 converts in hardware (v_cvt_pk_bf16_f32,
+// two values per instruction)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <typename T> struct Elem;
@@ -60,10 +62,8 @@ template <> struct Frag<bf16_t> {
     v = __builtin_bit_cast(bf16x8_t, c);
   }
   __device__ __forceinline__ void set(const float (&f)[8]) {
-    u16x8_t c;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) c[e] = f32_to_bf16(f[e]);
-    v = __builtin_bit_cast(bf16x8_t, c);
+    for (int e = 0; e < 8; ++e) v[e] = (__bf16)f[e];
   }
   __device__ __forceinline__ float get(int e) const {
     u16x8_t c = __builtin_bit_cast(u16x8_t, v);

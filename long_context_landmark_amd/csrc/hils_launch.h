@@ -33,6 +33,7 @@ struct RouteBufs {
   int4* items;     // [BH][max_items]: (chunk, first pair, end pair, -) work items of the chunk-major kernels
   int* n_items;    // [BH]
   int* pairs;      // [BH][L*k]: (t << 5) | slot, grouped by chunk, ascending (t, slot) inside a chunk
+  int* pos_of;     // [BH][L][k]: position of pair (t, slot) in pairs, -1 for unused slots (null: not kept)
   int nseg, seg_q, max_items, pairs_per_item;
 };
 int route_nseg(int L);
@@ -40,12 +41,18 @@ int route_seg_q(int L);
 int route_max_items(int L, int N, int k, int pairs_per_item);
 hipError_t launch_route(const int32_t* idx, const RouteBufs& rb, int BH, int L, int N, int k, hipStream_t st);
 
+// Writes, for every pair at position p of the routing lists, the weighted partial output
+// partial[bh][p][d] (bf16) and the chunk log-partition lse_pair[bh][p]: consecutive pairs of a
+// work item land in consecutive rows.  trash (d elements) and trash_lse (one float) receive
+// the stores of absent pairs.
 hipError_t launch_chunk_attn_fwd(int dt, int d, const void* Q, const void* K, const void* V, const RouteBufs& rb,
-                                 const float* w, float* lse, uint16_t* partial, int BH, int L, int N, int k,
-                                 float scale, hipStream_t st);
-hipError_t launch_own_combine(int dt, int d, const void* Q, const void* K, const void* V, const int32_t* idx,
-                              const float* w, const uint16_t* partial, void* O, float* lse, int BH, int L, int N, int k, float scale,
-                              hipStream_t st);
+                                 const float* w, float* lse_pair, uint16_t* partial, uint16_t* trash, float* trash_lse,
+                                 int BH, int L, int N, int k, float scale, hipStream_t st);
+// partial and lse_pair are indexed by pair position (chunk-major, as chunk_attn_fwd writes
+// them); pos_of maps (query, slot) to that position
+hipError_t launch_own_combine(int dt, int d, const void* Q, const void* K, const void* V, const int* pos_of,
+                              const float* w, const uint16_t* partial, const float* lse_pair, void* O, float* lse,
+                              int BH, int L, int N, int k, float scale, hipStream_t st);
 // pairs per chunk-major work item: short sequences favour balance, long ones fewer K/V re-reads
 inline int fwd_pairs_per_item(int N) { return N <= 1024 ? 256 : 1024; }
 

@@ -6,7 +6,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/hils.h"
+#include "hils.h"
 #include "hils_launch.h"
 
 namespace hils {

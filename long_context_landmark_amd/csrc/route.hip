@@ -14,7 +14,10 @@
 //            exclusive scan over chunks; also the chunk-major work items;
 //   scatter  one wavefront per segment walks its pairs in (t, slot) order and
 //            ranks equal chunks inside each 64-pair batch with ballots, so the
-//            list of every chunk is sorted by (t, slot) on every run.
+//            list of every chunk is sorted by (t, slot) on every run; it also
+//            records where each pair went (the inverse map, written in query
+//            order), so per-pair results stored in list order can be gathered
+//            back per query.
 #include "hils_device.h"
 #include "hils_launch.h"
 
@@ -112,7 +115,8 @@ __global__ __launch_bounds__(256) void route_scan_kernel(int* __restrict__ count
 __global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __restrict__ idx,
                                                            const int* __restrict__ segoff,
                                                            const int* __restrict__ chunk_off, int* __restrict__ pairs,
-                                                           int L, int N, int k, int nseg, int nbits, int seg_q) {
+                                                           int* __restrict__ pos_of, int L, int N, int k, int nseg,
+                                                           int nbits, int seg_q) {
   extern __shared__ int cur[];
   int seg, bh;
   xcd_map(seg, bh);  // a head's segments run in order on one XCD: its list writes merge in one L2
@@ -139,7 +143,10 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __rest
       const int j = jj[u];
       const bool act = j >= 0 && j < N;
       uint64_t peers = __ballot(act);
-      if (peers == 0) continue;
+      if (peers == 0) {
+        if (pos_of && f < total) pos_of[((int64_t)bh * L + t0) * k + f] = -1;
+        continue;
+      }
       for (int b = 0; b < nbits; ++b) {
         const bool bit = act && ((j >> b) & 1);
         const uint64_t ones = __ballot(bit);
@@ -153,6 +160,7 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __rest
       if (act && (peers & below) == 0) cur[j] = pos + __popcll(peers);
       __builtin_amdgcn_wave_barrier();
       if (act) out[pos] = ((t0 + f / k) << 5) | (f % k);
+      if (pos_of && f < total) pos_of[((int64_t)bh * L + t0) * k + f] = act ? pos : -1;
     }
   }
 }
@@ -166,7 +174,7 @@ hipError_t launch_route(const int32_t* idx, const RouteBufs& rb, int BH, int L, 
   int nbits = 1;
   while ((1 << nbits) < N) ++nbits;
   HILS_LAUNCH("route_scatter", route_scatter_kernel, dim3(rb.nseg, BH), dim3(64), lds, st, idx, rb.counts, rb.chunk_off,
-                     rb.pairs, L, N, k, rb.nseg, nbits, rb.seg_q);
+                     rb.pairs, rb.pos_of, L, N, k, rb.nseg, nbits, rb.seg_q);
   return hipGetLastError();
 }
 

@@ -73,7 +73,9 @@ constexpr int TK_CAP = 64;  // survivor slots per query (16 per sorting lane)
 // One workgroup per (b,h, query chunk c): the 64 queries t = 64c .. 64c+63
 // share the candidate set {0..c-1}.  Wave w scores the 16-chunk block w of
 // every 64-chunk landmark tile against all 64 queries.
-template <typename T, int D>
+// SMALL: every query chunk has at most two landmark tiles of candidates (N <= 129 chunks);
+// the score tiles of sweep 1 are then kept in registers for sweep 2.
+template <typename T, int D, bool SMALL>
 __global__ __launch_bounds__(256, 3) void topk_select_kernel(const T* __restrict__ Q, const T* __restrict__ Klm,
                                                           int32_t* __restrict__ idx, float* __restrict__ sel,
                                                           float* __restrict__ wout, int L, int N, int k,
@@ -109,13 +111,12 @@ __global__ __launch_bounds__(256, 3) void topk_select_kernel(const T* __restrict
   const int ntile = (c + 63) / 64;
   // scores of chunks tile*64 + 16w + 4g + i (i = 0..3) for queries 16qb + r16; the landmark
   // fragments of the next tile are loaded while the current one is on the MFMA units
+  // rows past the candidates (j >= c) load row c-1 instead: their scores are never used, and
+  // unconditional loads let the compiler wait for exactly the tile it needs
   auto load_tile = [&](int tile, Frag<T>(&a)[D / 32]) {
-    const int jrow = tile * 64 + 16 * w + r16;
+    const int jrow = min(tile * 64 + 16 * w + r16, c - 1);
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      if (jrow < c) a[ks].load(Kb + (int64_t)jrow * D + ks * 32 + 8 * g);
-      else a[ks].zero();
-    }
+    for (int ks = 0; ks < D / 32; ++ks) a[ks].load(Kb + (int64_t)jrow * D + ks * 32 + 8 * g);
   };
   auto mma_tile = [&](const Frag<T>(&a)[D / 32], f32x4_t(&acc)[4]) {
 #pragma unroll
@@ -125,15 +126,17 @@ __global__ __launch_bounds__(256, 3) void topk_select_kernel(const T* __restrict
       for (int ks = 0; ks < D / 32; ++ks) mma(acc[qb], a[ks], qf[qb][ks]);
     }
   };
+  // the next tile is always requested (the last one again at the end) so that every wait
+  // covers exactly the tile about to be used
   auto sweep_from = [&](Frag<T>(&a0)[D / 32], auto&& visit) {
     Frag<T> a1[D / 32];
     for (int tile = 0; tile < ntile; tile += 2) {
       f32x4_t acc[4];
-      if (tile + 1 < ntile) load_tile(tile + 1, a1);
+      load_tile(min(tile + 1, ntile - 1), a1);
       mma_tile(a0, acc);
       visit(tile, acc);
+      load_tile(min(tile + 2, ntile - 1), a0);
       if (tile + 1 < ntile) {
-        if (tile + 2 < ntile) load_tile(tile + 2, a0);
         mma_tile(a1, acc);
         visit(tile + 1, acc);
       }
@@ -171,15 +174,17 @@ __global__ __launch_bounds__(256, 3) void topk_select_kernel(const T* __restrict
   if (tid < 64) cnt_s[tid] = 0;
 
   if (m > 0) {
-    // sweep 1: per-group running maxima
+    // With at most two landmark tiles (c <= 128) both score tiles stay in registers and the
+    // second sweep reads them there; longer candidate lists recompute them.
+    f32x4_t keep0[SMALL ? 4 : 1], keep1[SMALL ? 4 : 1];
+    // sweep 1: per-group running maxima of the raw accumulators (the scale is positive, so
+    // the maximum commutes with the monotonic rounded multiplication applied once below)
     float gm[4][4];
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) gm[qb][i] = -INFINITY;
-    // raw accumulators: the scale is positive, so the maximum commutes with the
-    // (monotonic) rounded multiplication applied once below
-    sweep_from(first_tile, [&](int tile, f32x4_t(&acc)[4]) {
+    auto group_max = [&](int tile, const f32x4_t(&acc)[4]) {
       if ((tile + 1) * 64 <= c) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -195,7 +200,17 @@ __global__ __launch_bounds__(256, 3) void topk_select_kernel(const T* __restrict
           }
         }
       }
-    });
+    };
+    if constexpr (SMALL) {
+      Frag<T> a1[D / 32];
+      load_tile(min(1, ntile - 1), a1);
+      mma_tile(first_tile, keep0);
+      mma_tile(a1, keep1);
+      group_max(0, keep0);
+      if (ntile > 1) group_max(1, keep1);
+    } else {
+      sweep_from(first_tile, [&](int tile, f32x4_t(&acc)[4]) { group_max(tile, acc); });
+    }
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
@@ -216,27 +231,42 @@ __global__ __launch_bounds__(256, 3) void topk_select_kernel(const T* __restrict
       if (part == 0) tau_s[q] = tau;
     }
     __syncthreads();
-    // sweep 2: keep candidates at or above the bound
-    float tau_r[4];
+    // sweep 2: keep candidates at or above the bound.  A raw-accumulator bound a little below
+    // tau / scale first rejects whole rows of four (every score that reaches tau after the
+    // rounded scaling passes it: the margin exceeds the rounding of both quotients); the few
+    // that pass are then tested exactly on the scaled score.
+    float tau_r[4], raw_lo[4];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) tau_r[qb] = tau_s[16 * qb + r16];
+    for (int qb = 0; qb < 4; ++qb) {
+      tau_r[qb] = tau_s[16 * qb + r16];
+      const float t = tau_r[qb] / scale;
+      raw_lo[qb] = t - fabsf(t) * 1e-6f - 1e-30f;
+    }
     __syncthreads();  // every lane has read its bounds: the survivor buffer may overwrite the maxima
-    sweep([&](int tile, f32x4_t(&acc)[4]) {
-      const bool full = (tile + 1) * 64 <= c;
+    auto survive = [&](int tile, const f32x4_t(&acc)[4]) {
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) {
+        const float m4 = fmaxf(fmaxf(acc[qb][0], acc[qb][1]), fmaxf(acc[qb][2], acc[qb][3]));
+        if (m4 >= raw_lo[qb]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = tile * 64 + 16 * w + 4 * g + i;
-          const float s = scale * acc[qb][i];
-          if ((full || j < c) && s >= tau_r[qb]) {
-            const int q = 16 * qb + r16;
-            const int p = atomicAdd(&cnt_s[q], 1);
-            if (p < TK_CAP) surv[q][p] = make_key(s, j);
+          for (int i = 0; i < 4; ++i) {
+            const int j = tile * 64 + 16 * w + 4 * g + i;
+            const float sv = scale * acc[qb][i];
+            if (j < c && sv >= tau_r[qb]) {
+              const int q = 16 * qb + r16;
+              const int p = atomicAdd(&cnt_s[q], 1);
+              if (p < TK_CAP) surv[q][p] = make_key(sv, j);
+            }
           }
         }
       }
-    });
+    };
+    if constexpr (SMALL) {
+      survive(0, keep0);
+      if (ntile > 1) survive(1, keep1);
+    } else {
+      sweep([&](int tile, f32x4_t(&acc)[4]) { survive(tile, acc); });
+    }
     __syncthreads();
     // exact top-m among the survivors: 4 lanes per query, 16 slots each
     {
@@ -343,8 +373,12 @@ template <typename T, int D>
 hipError_t launch_topk_t(const void* Q, const void* Klm, int32_t* idx, float* sel, float* w, int BH, int L, int N,
                          int k, float scale, hipStream_t st) {
   dim3 grid(L / 64, BH);
-  HILS_LAUNCH("topk_select", (topk_select_kernel<T, D>), grid, dim3(256), 0, st, (const T*)Q, (const T*)Klm, idx, sel, w, L,
-                     N, k, scale);
+  if (N <= 129)
+    HILS_LAUNCH("topk_select", (topk_select_kernel<T, D, true>), grid, dim3(256), 0, st, (const T*)Q, (const T*)Klm, idx,
+                sel, w, L, N, k, scale);
+  else
+    HILS_LAUNCH("topk_select", (topk_select_kernel<T, D, false>), grid, dim3(256), 0, st, (const T*)Q, (const T*)Klm, idx,
+                sel, w, L, N, k, scale);
   return hipGetLastError();
 }
 

@@ -38,6 +38,8 @@ CASES = [
     ("bf16", 1, 1, 1024, 64, 16, "iid"),  # k = N
     ("f32", 1, 2, 1024, 64, 4, "iid"),  # the tiny fp32 workload
     ("f32", 1, 1, 2048, 128, 8, "iid"),
+    ("bf16", 1, 2, 19200, 64, 16, "iid"),  # 300 chunks: the multi-tile two-sweep selection
+    ("bf16", 1, 1, 12352, 128, 8, "chunkmean"),  # 193 chunks, d=128
 ]
 
 
