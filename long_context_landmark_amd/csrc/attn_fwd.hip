@@ -234,10 +234,10 @@ __global__ __launch_bounds__(256) void chunk_attn_fwd_kernel(const T* __restrict
 #pragma unroll
       for (int it = 0; it < 16 / RPI; ++it) {
         const int row = it * RPI + lane / PPR, pc = lane % PPR;
-        const uint4 v = *reinterpret_cast<const uint4*>(rowbuf + row * RSB + 8 * pc);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(rowbuf + row * RSB + 8 * pc);
         const int pidx = base + 16 * w_ + row;
         uint16_t* dst = pidx < p1 ? partial + ((int64_t)bh * L * k + pidx) * D : trash;
-        *reinterpret_cast<uint4*>(dst + 8 * pc) = v;
+        *reinterpret_cast<u32x4_t*>(dst + 8 * pc) = v;
       }
       __builtin_amdgcn_wave_barrier();
     } else {
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(256) void own_combine_kernel(const T* __restrict__ 
 #pragma unroll
   for (int r0 = 0; r0 < 16; r0 += SB) {
     if (r0 >= m) break;
-    uint4 v[NI][SB];
+    u32x4_t v[NI][SB];
     bool kept[NI][SB];
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
@@ -361,14 +361,14 @@ __global__ __launch_bounds__(256) void own_combine_kernel(const T* __restrict__ 
       for (int sb = 0; sb < SB; ++sb) {
         const int p = pos_s[q][r0 + sb];
         kept[it][sb] = p >= 0;
-        v[it][sb] = *reinterpret_cast<const uint4*>(partial + (pbase + max(p, 0)) * D + 8 * pc);
+        v[it][sb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(partial + (pbase + max(p, 0)) * D + 8 * pc));
       }
     }
 #pragma unroll
     for (int it = 0; it < NI; ++it)
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
-        const uint32_t wds[4] = {v[it][sb].x, v[it][sb].y, v[it][sb].z, v[it][sb].w};
+        const uint32_t wds[4] = {v[it][sb][0], v[it][sb][1], v[it][sb][2], v[it][sb][3]};
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           acc[it][2 * x] += kept[it][sb] ? __uint_as_float(wds[x] << 16) : 0.f;

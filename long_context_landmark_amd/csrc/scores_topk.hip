@@ -330,33 +330,43 @@ __global__ __launch_bounds__(256, 3) void topk_select_kernel(const T* __restrict
   }
   __syncthreads();
 
-  // fusion weights and outputs
-  {
-    const int q = tid >> 2, part = tid & 3;
+  // fusion weights and outputs: the softmax statistics per query, then the 64 query rows of
+  // each output, which are consecutive in memory, written element by element across the
+  // workgroup (coalesced)
+  __shared__ float mx_s[64], inv_s[64];
+  if (tid < 64) {
+    const int q = tid;
     const float s_own = own_s[q];
-    if (part == 0) {
-      const int64_t row = ((int64_t)bh * L + (int64_t)c * 64 + q) * k1;
-      float mx = s_own;
-      for (int r = 0; r < m; ++r) mx = fmaxf(mx, key_score(top_s[q][r]));
-      float den = __expf(s_own - mx);
-      for (int r = 0; r < m; ++r) den += __expf(key_score(top_s[q][r]) - mx);
-      const float inv = 1.f / den;
-      for (int r = 0; r < k; ++r) {
-        if (r < m) {
-          const float s = key_score(top_s[q][r]);
-          idx[row + r] = key_index(top_s[q][r]);
-          sel[row + r] = s;
-          if (wout) wout[row + r] = __expf(s - mx) * inv;
-        } else {
-          idx[row + r] = -1;
-          sel[row + r] = -INFINITY;
-          if (wout) wout[row + r] = 0.f;
-        }
-      }
-      idx[row + k] = c;
-      sel[row + k] = s_own;
-      if (wout) wout[row + k] = __expf(s_own - mx) * inv;
+    float mx = s_own;
+    for (int r = 0; r < m; ++r) mx = fmaxf(mx, key_score(top_s[q][r]));
+    float den = __expf(s_own - mx);
+    for (int r = 0; r < m; ++r) den += __expf(key_score(top_s[q][r]) - mx);
+    mx_s[q] = mx;
+    inv_s[q] = 1.f / den;
+  }
+  __syncthreads();
+  const int64_t base = ((int64_t)bh * L + (int64_t)c * 64) * k1;
+  for (int e = tid; e < 64 * k1; e += 256) {
+    const int q = e / k1, r = e % k1;
+    int ix;
+    float sv, wv;
+    if (r == k) {
+      ix = c;
+      sv = own_s[q];
+      wv = __expf(sv - mx_s[q]) * inv_s[q];
+    } else if (r < m) {
+      const uint64_t key = top_s[q][r];
+      ix = key_index(key);
+      sv = key_score(key);
+      wv = __expf(sv - mx_s[q]) * inv_s[q];
+    } else {
+      ix = -1;
+      sv = -INFINITY;
+      wv = 0.f;
     }
+    idx[base + e] = ix;
+    sel[base + e] = sv;
+    if (wout) wout[base + e] = wv;
   }
 }
 
