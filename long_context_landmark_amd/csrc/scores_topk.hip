@@ -76,7 +76,7 @@ constexpr int TK_CAP = 64;  // survivor slots per query (16 per sorting lane)
 // SMALL: every query chunk has at most two landmark tiles of candidates (N <= 129 chunks);
 // the score tiles of sweep 1 are then kept in registers for sweep 2.
 template <typename T, int D, bool SMALL>
-__global__ __launch_bounds__(256, 3) void topk_select_kernel(const T* __restrict__ Q, const T* __restrict__ Klm,
+__global__ __launch_bounds__(256, (SMALL && D == 64) ? 4 : 3) void topk_select_kernel(const T* __restrict__ Q, const T* __restrict__ Klm,
                                                           int32_t* __restrict__ idx, float* __restrict__ sel,
                                                           float* __restrict__ wout, int L, int N, int k,
                                                           float scale) {
@@ -90,14 +90,15 @@ __global__ __launch_bounds__(256, 3) void topk_select_kernel(const T* __restrict
   const T* Qb = Q + ((int64_t)bh * L + (int64_t)c * 64) * D;
   const T* Kb = Klm + (int64_t)bh * N * D;
 
-  // the group maxima (sweep 1) and the survivors (sweep 2) share storage
+  // the group maxima (sweep 1), the survivors (sweep 2) and the sorted top keys share storage
   __shared__ union {
     float gmax[64][65];
     uint64_t surv[64][TK_CAP];
+    uint64_t top[64][16];
   } u_s;
-  __shared__ uint64_t top_s[64][16];
   auto& gmax_s = u_s.gmax;
   auto& surv = u_s.surv;
+  auto& top_s = u_s.top;
   __shared__ int cnt_s[64];
   __shared__ float tau_s[64];
   __shared__ int ovf_s;
@@ -268,10 +269,15 @@ __global__ __launch_bounds__(256, 3) void topk_select_kernel(const T* __restrict
       sweep([&](int tile, f32x4_t(&acc)[4]) { survive(tile, acc); });
     }
     __syncthreads();
-    // exact top-m among the survivors: 4 lanes per query, 16 slots each
+    // exact top-m among the survivors: 4 lanes per query, 16 slots each.  When every query
+    // of the wavefront has at most 16 (or 32) survivors, one (two) of its lanes hold them all
+    // and the merges between lanes that hold nothing are skipped.
     {
       const int q = tid >> 2, part = tid & 3;
       const int n = cnt_s[q];
+      int nmax = n;
+#pragma unroll
+      for (int msk = 1; msk < 64; msk <<= 1) nmax = max(nmax, lane_xor(nmax, msk));
       uint64_t v[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -279,8 +285,9 @@ __global__ __launch_bounds__(256, 3) void topk_select_kernel(const T* __restrict
         v[e] = (p < n && p < TK_CAP) ? surv[q][p] : 0ull;
       }
       sort16_desc(v);
-      merge16_with_lane(v, 1);
-      merge16_with_lane(v, 2);
+      if (nmax > 16) merge16_with_lane(v, 1);
+      if (nmax > 32) merge16_with_lane(v, 2);
+      __syncthreads();  // every survivor has been read: the sorted keys overwrite the buffer
       if (part == 0) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) top_s[q][e] = v[e];
