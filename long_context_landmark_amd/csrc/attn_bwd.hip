@@ -53,7 +53,8 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
                                                         const float* __restrict__ lse,
                                                         const int* __restrict__ chunk_off,
                                                         const int* __restrict__ pairs, uint16_t* __restrict__ dq_part,
-                                                        float* __restrict__ Dpart, float* __restrict__ dK,
+                                                        float* __restrict__ Dpart, uint16_t* __restrict__ trash,
+                                                        float* __restrict__ trash_f, float* __restrict__ dK,
                                                         float* __restrict__ dV, int L, int N, int k, float scale) {
   using S = BwdLds<T, D>;
   int j, bh;
@@ -82,6 +83,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
   const int p_begin = co[j], p_end = co[j + 1];
   const int ntiles = 1 + (p_end - p_begin + 63) / 64;
   const int* pl = pairs + (int64_t)bh * L * k;
+  const int64_t npl = (int64_t)L * k;
   const T* Qb = Q + (int64_t)bh * L * D;
   const T* Gb = dO + (int64_t)bh * L * D;
   const int qi = 16 * wv + r16;  // this lane's query slot in the tile
@@ -92,36 +94,49 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
     accV[db] = zero4();
     accK[db] = zero4();
   }
-  for (int tile = 0; tile < ntiles; ++tile) {
-    int t, slot, causal;
-    bool valid;
-    if (tile == 0) {
-      t = j * 64 + qi;
-      slot = k;
-      causal = qi;
-      valid = true;
-    } else {
-      const int p = p_begin + (tile - 1) * 64 + qi;
-      valid = p < p_end;
-      const int pe = valid ? pl[p] : 0;
-      t = pe >> 5;
-      slot = pe & 31;
-      causal = -1;
-    }
-    const int64_t row = (int64_t)bh * L + t;
+  // Software pipeline over the tiles (tile 0: the chunk's own queries, causal; tile i >= 1:
+  // routed pairs 64(i-1) .. 64i-1) with two input sets used in turn: while a tile runs, the
+  // query and upstream-gradient rows and the softmax statistics of the next tile load into
+  // the other set, and the pair entries of the tile after it are read.  Every load is
+  // unconditional (entries are read at clamped positions inside the list buffer, rows and
+  // statistics at valid rows); lanes without a pair compute with p = 0 and store to scratch.
+  struct TileIn {
     Frag<T> qf[D / 32], gf[D / 32];
+    float lse, w;
+    int t, slot;
+    bool valid;
+  };
+  auto entry = [&](int tile) {
+    const int64_t p = (int64_t)p_begin + (int64_t)(tile - 1) * 64 + qi;
+    return pl[p < 0 ? 0 : (p < npl ? p : npl - 1)];
+  };
+  auto fetch = [&](int tile, int pe, TileIn& in) {
+    if (tile == 0) {
+      in.t = j * 64 + qi;
+      in.slot = k;
+      in.valid = true;
+    } else {
+      // list positions past the chunk's range may lie past the filled part of the list, whose
+      // entries are undefined: lanes without a pair use their own-chunk row instead
+      in.valid = p_begin + (tile - 1) * 64 + qi < p_end;
+      in.t = in.valid ? (pe >> 5) : j * 64 + qi;
+      in.slot = in.valid ? (pe & 31) : k;
+    }
+    const int64_t row = (int64_t)bh * L + in.t;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
-      if (valid) {
-        qf[ks].load(Qb + (int64_t)t * D + ks * 32 + 8 * g);
-        gf[ks].load(Gb + (int64_t)t * D + ks * 32 + 8 * g);
-      } else {
-        qf[ks].zero();
-        gf[ks].zero();
-      }
+      in.qf[ks].load(Qb + (int64_t)in.t * D + ks * 32 + 8 * g);
+      in.gf[ks].load(Gb + (int64_t)in.t * D + ks * 32 + 8 * g);
     }
-    const float lse_q = valid ? lse[row * k1 + slot] : 0.f;
-    const float w_q = valid ? w[row * k1 + slot] : 0.f;
+    in.lse = lse[row * k1 + in.slot];
+    in.w = w[row * k1 + in.slot];
+  };
+  auto process = [&](const TileIn& in, int tile) {
+    const bool valid = in.valid;
+    const int causal = tile == 0 ? qi : -1;
+    const int64_t row = (int64_t)bh * L + in.t;
+    const float lse_q = in.lse;
+    const float w_q = valid ? in.w : 0.f;
     // S^T = K Q^T and dP^T = V dO^T: lane holds query qi, keys 16cb + 4g + i
     f32x4_t sc[4], dp[4];
 #pragma unroll
@@ -133,8 +148,8 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
         Frag<T> a, b;
         a.load(&s.k[(16 * cb + r16) * S::KS + ks * 32 + 8 * g]);
         b.load(&s.v[(16 * cb + r16) * S::KS + ks * 32 + 8 * g]);
-        mma(sc[cb], a, qf[ks]);
-        mma(dp[cb], b, gf[ks]);
+        mma(sc[cb], a, in.qf[ks]);
+        mma(dp[cb], b, in.gf[ks]);
       }
     }
     float Dj = 0.f;
@@ -149,7 +164,8 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
       }
     Dj += lane_xor(Dj, 16);
     Dj += lane_xor(Dj, 32);
-    if (valid && g == 0) Dpart[row * k1 + slot] = Dj;
+    // the four lane groups hold the same D_j
+    *(valid ? Dpart + row * k1 + in.slot : trash_f) = Dj;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -164,6 +180,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
         for (int e = 0; e < 8; ++e) v8[e] = dp[2 * h + e / 4][e % 4];
         daf[h].set(v8);
       }
+      uint16_t* dst = valid ? dq_part + (row * k1 + in.slot) * D : trash;
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
         f32x4_t dq = zero4();
@@ -174,12 +191,10 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
           a.load4x2(rowp, rowp + 16);
           mma(dq, a, daf[h]);
         }
-        if (valid) {
-          u16x4_t h4;
+        u16x4_t h4;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) h4[i] = __builtin_bit_cast(uint16_t, (_Float16)(scale * dq[i]));
-          *reinterpret_cast<u16x4_t*>(dq_part + (row * k1 + slot) * D + 16 * db + 4 * g) = h4;
-        }
+        for (int i = 0; i < 4; ++i) h4[i] = __builtin_bit_cast(uint16_t, (_Float16)(scale * dq[i]));
+        *reinterpret_cast<u16x4_t*>(dst + 16 * db + 4 * g) = h4;
       }
     }
     __syncthreads();  // previous tile's readers of the transposed buffers are done
@@ -187,8 +202,8 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
     for (int ks = 0; ks < D / 32; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        Elem<T>::store(s.qt, (ks * 32 + 8 * g + e) * S::TS + qi, qf[ks].get(e));
-        Elem<T>::store(s.gt, (ks * 32 + 8 * g + e) * S::TS + qi, gf[ks].get(e));
+        Elem<T>::store(s.qt, (ks * 32 + 8 * g + e) * S::TS + qi, in.qf[ks].get(e));
+        Elem<T>::store(s.gt, (ks * 32 + 8 * g + e) * S::TS + qi, in.gf[ks].get(e));
       }
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
@@ -214,6 +229,19 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
         mma(accK[db], ad, bq);
       }
     }
+  };
+  TileIn A, B;
+  int e1 = entry(1);
+  fetch(0, 0, A);
+  for (int tile = 0;; tile += 2) {
+    fetch(tile + 1, e1, B);
+    const int e2 = entry(tile + 2);
+    process(A, tile);
+    if (tile + 1 >= ntiles) break;
+    fetch(tile + 2, e2, A);
+    e1 = entry(tile + 3);
+    process(B, tile + 1);
+    if (tile + 2 >= ntiles) break;
   }
   // write dK, dV of this chunk: lane holds d = 16db + r16, keys 16wv + 4g + i
   const int64_t krow0 = (int64_t)bh * L + (int64_t)j * 64 + 16 * wv + 4 * g;
@@ -343,7 +371,7 @@ static hipError_t bwd_t(const void* Q, const void* K, const void* V, const void*
   if (e != hipSuccess) return e;
   HILS_LAUNCH("chunk_bwd", (chunk_bwd_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)Q, (const T*)K,
               (const T*)V, (const T*)Klm, (const T*)dO, w, lse, ws.rb.chunk_off, ws.rb.pairs, ws.dq_part, ws.Dpart,
-              dK, dV, L, N, k, scale);
+              ws.trash, ws.trash_f, dK, dV, L, N, k, scale);
   HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D>), dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, st,
               ws.dq_part, ws.Dpart, idx, w, (const T*)Klm, ws.ds, dQ, rows, L, N, k, scale);
   HILS_LAUNCH("klm_bwd", (klm_bwd_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)Q, ws.ds, ws.rb.chunk_off,

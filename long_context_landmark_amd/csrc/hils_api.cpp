@@ -126,6 +126,8 @@ size_t carve_bwd(void* base, const Dims& D, hils::BwdBufs* ws) {
   ws->dq_part = cv.take<uint16_t>((size_t)BH * D.L * (D.k + 1) * D.d);
   ws->Dpart = cv.take<float>((size_t)BH * D.L * (D.k + 1));
   ws->ds = cv.take<float>((size_t)BH * D.L * (D.k + 1));
+  ws->trash = cv.take<uint16_t>((size_t)D.d);
+  ws->trash_f = cv.take<float>(64);
   return cv.off;
 }
 

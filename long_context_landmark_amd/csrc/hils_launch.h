@@ -68,6 +68,8 @@ struct BwdBufs {
   uint16_t* dq_part;  // [BH][L][k+1][d] fp16 in-chunk dQ contribution of every (query, slot)
   float* Dpart;    // [BH][L][k+1]    D_j = dO_t . o_tj of every (query, slot)
   float* ds;       // [BH][L][k+1]    fusion-score gradient of every (query, slot)
+  uint16_t* trash; // d elements: stores of lanes without a pair
+  float* trash_f;  // one float, likewise
 };
 hipError_t launch_bwd(int dt, int d, const void* Q, const void* K, const void* V, const void* Klm,
                       const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ, float* dK,
