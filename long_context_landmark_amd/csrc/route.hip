@@ -55,21 +55,28 @@ __global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restr
   for (int j = tid; j < N; j += 256) out[j] = hist[j];
 }
 
-// exclusive block scan of one int per thread (256 threads); returns the block total in *total
+// exclusive block scan of one int per thread (256 threads); returns the block total in *total.
+// Each wavefront scans its 64 values, then adds the totals of the wavefronts before it.
 __device__ int block_excl_scan(int v, int* buf, int* total) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    int add = tid >= off ? buf[tid - off] : 0;
-    __syncthreads();
-    buf[tid] += add;
-    __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
   }
-  const int incl = buf[tid];
-  *total = buf[255];
+  if (lane == 63) buf[wv] = incl;
   __syncthreads();
-  return incl - v;
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int tw = buf[w];
+    before += w < wv ? tw : 0;
+    all += tw;
+  }
+  *total = all;
+  __syncthreads();  // buf is reused by the next call
+  return before + incl - v;
 }
 
 __global__ __launch_bounds__(256) void route_scan_kernel(int* __restrict__ counts, int* __restrict__ chunk_off,
@@ -82,12 +89,12 @@ __global__ __launch_bounds__(256) void route_scan_kernel(int* __restrict__ count
     const int j = base + tid;
     int tot = 0;
     if (j < N) {
-      for (int s0 = 0; s0 < nseg; s0 += 8) {
-        int cv[8];
+      for (int s0 = 0; s0 < nseg; s0 += 32) {
+        int cv[32];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) cv[u] = s0 + u < nseg ? counts[((int64_t)bh * nseg + s0 + u) * N + j] : 0;
+        for (int u = 0; u < 32; ++u) cv[u] = s0 + u < nseg ? counts[((int64_t)bh * nseg + s0 + u) * N + j] : 0;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 32; ++u) {
           if (s0 + u < nseg) counts[((int64_t)bh * nseg + s0 + u) * N + j] = tot;
           tot += cv[u];
         }
@@ -112,22 +119,57 @@ __global__ __launch_bounds__(256) void route_scan_kernel(int* __restrict__ count
   }
 }
 
-__global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __restrict__ idx,
-                                                           const int* __restrict__ segoff,
-                                                           const int* __restrict__ chunk_off, int* __restrict__ pairs,
-                                                           int* __restrict__ pos_of, int L, int N, int k, int nseg,
-                                                           int nbits, int seg_q) {
-  extern __shared__ int cur[];
+// NW wavefronts per segment: wave w takes the w-th share of the segment's queries.  Each
+// wave first counts its pairs per chunk (LDS histogram); the cursors of wave w then start
+// after the pairs of waves 0..w-1 in every chunk, so the list keeps the (t, slot) order.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void route_scatter_kernel(const int32_t* __restrict__ idx,
+                                                                const int* __restrict__ segoff,
+                                                                const int* __restrict__ chunk_off,
+                                                                int* __restrict__ pairs, int* __restrict__ pos_of,
+                                                                int L, int N, int k, int nseg, int nbits, int seg_q) {
+  extern __shared__ int cur_all[];  // [NW][N]
   int seg, bh;
   xcd_map(seg, bh);  // a head's segments run in order on one XCD: its list writes merge in one L2
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int* so = segoff + ((int64_t)bh * nseg + seg) * N;
   const int* co = chunk_off + (int64_t)bh * (N + 1);
-  for (int j = lane; j < N; j += 64) cur[j] = co[j] + so[j];
+  const int t0 = seg * seg_q, t1 = min(L, t0 + seg_q);
+  const int qpw = (seg_q + NW - 1) / NW;
+  const int tw0 = min(t1, t0 + wv * qpw), tw1 = min(t1, tw0 + qpw);
+  const int total = (tw1 - tw0) * k;
+  const int32_t* idx_w = idx + ((int64_t)bh * L + tw0) * (k + 1);
+  int* cur = cur_all + wv * N;
+  if constexpr (NW > 1) {
+    for (int i = tid; i < NW * N; i += 64 * NW) cur_all[i] = 0;
+    __syncthreads();
+    for (int f0 = 0; f0 < total; f0 += 8 * 64) {
+      int jj[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int f = f0 + u * 64 + lane;
+        jj[u] = f < total ? idx_w[(f / k) * (k + 1) + f % k] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (jj[u] >= 0 && jj[u] < N) atomicAdd(&cur[jj[u]], 1);
+    }
+    __syncthreads();
+    for (int j = tid; j < N; j += 64 * NW) {
+      int run = co[j] + so[j];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int h = cur_all[w * N + j];
+        cur_all[w * N + j] = run;
+        run += h;
+      }
+    }
+  } else {
+    for (int j = lane; j < N; j += 64) cur[j] = co[j] + so[j];
+  }
   __syncthreads();
   int* out = pairs + (int64_t)bh * L * k;
-  const int t0 = seg * seg_q, t1 = min(L, t0 + seg_q);
-  const int total = (t1 - t0) * k;
+  int* pos_w = pos_of ? pos_of + ((int64_t)bh * L + tw0) * k : nullptr;
   const uint64_t below = (1ull << lane) - 1ull;
   constexpr int U = 8;  // batches whose chunk ids are loaded together
   for (int b0 = 0; b0 < total; b0 += U * 64) {
@@ -135,7 +177,7 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __rest
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int f = b0 + u * 64 + lane;
-      jj[u] = f < total ? idx[((int64_t)bh * L + t0 + f / k) * (k + 1) + f % k] : -1;
+      jj[u] = f < total ? idx_w[(f / k) * (k + 1) + f % k] : -1;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -144,7 +186,7 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __rest
       const bool act = j >= 0 && j < N;
       uint64_t peers = __ballot(act);
       if (peers == 0) {
-        if (pos_of && f < total) pos_of[((int64_t)bh * L + t0) * k + f] = -1;
+        if (pos_w && f < total) pos_w[f] = -1;
         continue;
       }
       for (int b = 0; b < nbits; ++b) {
@@ -159,8 +201,8 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(const int32_t* __rest
       __builtin_amdgcn_wave_barrier();
       if (act && (peers & below) == 0) cur[j] = pos + __popcll(peers);
       __builtin_amdgcn_wave_barrier();
-      if (act) out[pos] = ((t0 + f / k) << 5) | (f % k);
-      if (pos_of && f < total) pos_of[((int64_t)bh * L + t0) * k + f] = act ? pos : -1;
+      if (act) out[pos] = ((tw0 + f / k) << 5) | (f % k);
+      if (pos_w && f < total) pos_w[f] = act ? pos : -1;
     }
   }
 }
@@ -173,8 +215,13 @@ hipError_t launch_route(const int32_t* idx, const RouteBufs& rb, int BH, int L, 
                      rb.nseg, rb.pairs_per_item, rb.max_items);
   int nbits = 1;
   while ((1 << nbits) < N) ++nbits;
-  HILS_LAUNCH("route_scatter", route_scatter_kernel, dim3(rb.nseg, BH), dim3(64), lds, st, idx, rb.counts, rb.chunk_off,
-                     rb.pairs, rb.pos_of, L, N, k, rb.nseg, nbits, rb.seg_q);
+  // four wavefronts per segment while their cursor tables fit in LDS
+  if (N <= 2048)
+    HILS_LAUNCH("route_scatter", route_scatter_kernel<4>, dim3(rb.nseg, BH), dim3(256), 4 * lds, st, idx, rb.counts,
+                rb.chunk_off, rb.pairs, rb.pos_of, L, N, k, rb.nseg, nbits, rb.seg_q);
+  else
+    HILS_LAUNCH("route_scatter", route_scatter_kernel<1>, dim3(rb.nseg, BH), dim3(64), lds, st, idx, rb.counts,
+                rb.chunk_off, rb.pairs, rb.pos_of, L, N, k, rb.nseg, nbits, rb.seg_q);
   return hipGetLastError();
 }
 
