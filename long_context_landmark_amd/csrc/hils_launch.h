@@ -54,7 +54,7 @@ hipError_t launch_own_combine(int dt, int d, const void* Q, const void* K, const
                               const float* w, const uint16_t* partial, const float* lse_pair, void* O, float* lse,
                               int BH, int L, int N, int k, float scale, hipStream_t st);
 // pairs per chunk-major work item: short sequences favour balance, long ones fewer K/V re-reads
-inline int fwd_pairs_per_item(int N) { return N <= 1024 ? 256 : 1024; }
+inline int fwd_pairs_per_item(int N) { return N <= 1024 ? 512 : 1024; }
 
 struct DecodeBufs {
   uint64_t* lists;  // [BH][decode_max_slices()][decode_list_len()] best (score, chunk) keys of every slice

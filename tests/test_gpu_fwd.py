@@ -69,12 +69,12 @@ def test_topk_select(hils, gpu, dtype, B, H, L, d, k, klm):
     assert_close(np.take_along_axis(gw, order_g, 1), np.take_along_axis(rw, order_o, 1), "w", 1e-5, 1e-5)
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_topk_exact_ties_fallback(hils, gpu, d):
+@pytest.mark.parametrize("d,N,k", [(64, 200, 8), (128, 200, 8), (64, 100, 8), (128, 120, 16)])
+def test_topk_exact_ties_fallback(hils, gpu, d, N, k):
     """All landmarks equal: every candidate ties, the survivor buffer overflows and the exact fallback must
-    return the m lowest chunk indices."""
-    say(f"topk ties d={d}")
-    L, k = 64 * 200, 8
+    return the m lowest chunk indices (N <= 129 takes the short-sequence kernel)."""
+    say(f"topk ties d={d} N={N} k={k}")
+    L = 64 * N
     x = _inputs(1, 1, L, d, k, seed=3, klm="iid")
     Klm = np.broadcast_to(x["Klm"][:, :, :1], x["Klm"].shape).copy()
     idx, sel, w = hils.topk_select(dev(x["Q"]), dev(Klm), k)
