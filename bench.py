@@ -48,7 +48,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: (kernel, FETCH_SIZE KiB, WRITE_SIZE KiB, source digest)
-    "prefill_8k": ("chunk_attn_fwd", 30612.9, 126464.0, "bf0777efc24d5c2b"),
+    "prefill_8k": ("chunk_attn_fwd", 31225.8, 130569.7, "196d9ef442ba3c44"),
+    "prefill_128k": ("chunk_attn_fwd", 12079190.5, 17007150.3, "196d9ef442ba3c44"),
+    "train_8k": ("chunk_bwd", 246176.3, 912802.1, "f54c5de737790842"),
 }
 
 
