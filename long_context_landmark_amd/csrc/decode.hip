@@ -295,27 +295,31 @@ __device__ __forceinline__ void wave_attend_chunk(const T* __restrict__ Kc, cons
   }
 }
 
-// One 1024-thread workgroup per head.  Wave 0 merges the slice lists and computes the
-// fusion weights while wave 15 attends to the open chunk, which needs no selection; then
-// wavefront i attends to kept chunk i (split-K over the wavefronts), and the outputs are
-// fused in LDS in slot order.  No cross-workgroup communication.
+constexpr int DEC_SPLIT = 4;  // attention workgroups per head
+
+// DEC_SPLIT workgroups of four wavefronts per head, so that the kept chunks' key and value
+// reads spread over as many compute units.  In every workgroup wave 0 merges the slice lists
+// and computes the fusion weights (the same result everywhere); workgroup s, wave v then
+// attends to kept slot 4v + s, and workgroup 0's wave 3 attends to the open chunk meanwhile,
+// since that needs no selection.  Each workgroup writes its weighted partial sum (its slots in
+// order); decode_fuse adds the DEC_SPLIT partials.
 template <typename T, int D>
-__global__ __launch_bounds__(1024) void decode_attend_kernel(const T* __restrict__ q, const T* __restrict__ Kc,
-                                                             const T* __restrict__ Vc, const T* __restrict__ Klm,
-                                                             const uint64_t* __restrict__ lists, T* __restrict__ o,
-                                                             int32_t* __restrict__ idx, float* __restrict__ wout,
-                                                             int64_t n, int64_t Lmax, int64_t Nmax, int k,
-                                                             float scale) {
+__global__ __launch_bounds__(256) void decode_attend_kernel(const T* __restrict__ q, const T* __restrict__ Kc,
+                                                            const T* __restrict__ Vc, const T* __restrict__ Klm,
+                                                            const uint64_t* __restrict__ lists,
+                                                            float* __restrict__ part, int32_t* __restrict__ idx,
+                                                            float* __restrict__ wout, int64_t n, int64_t Lmax,
+                                                            int64_t Nmax, int k, float scale) {
   constexpr int EPP = 16 / Elem<T>::bytes;
   constexpr int PIECES = D / EPP;
-  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int sp = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c = (int)(n / 64);
   const int m = min(k, c);
   const int S = (c + DEC_ROWS - 1) / DEC_ROWS;
   __shared__ uint64_t top[16];
   __shared__ uint64_t surv[64];
-  __shared__ float sc_w[16][64];
-  __shared__ float po[17][D];
+  __shared__ float sc_w[4][64];
+  __shared__ float po[5][D];
   __shared__ float wsl[17];
   const int piece = lane % PIECES;
   float qv[EPP];
@@ -336,26 +340,43 @@ __global__ __launch_bounds__(1024) void decode_attend_kernel(const T* __restrict
     const float ev = used ? __expf(sv - smax) : 0.f;
     const float den = wave_sum(ev);
     if (lane < 17) wsl[lane] = ev / den;
-  } else if (wv == 15) {
-    wave_attend_chunk<T, D>(Kh, Vh, (int64_t)c * 64, (int)(n - (int64_t)c * 64) + 1, qv, scale, sc_w[wv], po[16],
+  } else if (wv == 3 && sp == 0) {
+    wave_attend_chunk<T, D>(Kh, Vh, (int64_t)c * 64, (int)(n - (int64_t)c * 64) + 1, qv, scale, sc_w[wv], po[4],
                             lane);
   }
   __syncthreads();
-  if (wv < m)
-    wave_attend_chunk<T, D>(Kh, Vh, (int64_t)key_index(top[wv]) * 64, 64, qv, scale, sc_w[wv], po[wv], lane);
+  const int slot = 4 * wv + sp;
+  if (slot < m)
+    wave_attend_chunk<T, D>(Kh, Vh, (int64_t)key_index(top[slot]) * 64, 64, qv, scale, sc_w[wv], po[wv], lane);
   __syncthreads();
-  for (int e = tid; e < D; e += 1024) {
+  for (int e = tid; e < D; e += 256) {
     float acc = 0.f;
-    for (int i = 0; i < m; ++i) acc += wsl[i] * po[i][e];
-    acc += wsl[16] * po[16][e];
-    Elem<T>::store(o, (int64_t)bh * D + e, acc);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (4 * v + sp < m) acc += wsl[4 * v + sp] * po[v][e];
+    if (sp == 0) acc += wsl[16] * po[4][e];
+    part[((int64_t)bh * DEC_SPLIT + sp) * D + e] = acc;
   }
-  if (tid <= k) {
+  if (sp == 0 && tid <= k) {
     const bool used = tid < m || tid == k;
     idx[(int64_t)bh * (k + 1) + tid] = tid == k ? c : (used ? key_index(top[tid]) : -1);
     wout[(int64_t)bh * (k + 1) + tid] = tid == k ? wsl[16] : (used ? wsl[tid] : 0.f);
   }
 }
+
+// o = the sum of a head's DEC_SPLIT partial outputs, in workgroup order.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void decode_fuse_kernel(const float* __restrict__ part, T* __restrict__ o) {
+  const int bh = blockIdx.x;
+  for (int e = threadIdx.x; e < D; e += 64) {
+    float acc = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < DEC_SPLIT; ++sp) acc += part[((int64_t)bh * DEC_SPLIT + sp) * D + e];
+    Elem<T>::store(o, (int64_t)bh * D + e, acc);
+  }
+}
+
+int decode_split() { return DEC_SPLIT; }
 
 template <typename T, int D>
 static hipError_t decode_t(const void* q, const void* k_new, const void* v_new, void* Kc, void* Vc, const void* Klm,
@@ -364,8 +385,9 @@ static hipError_t decode_t(const void* q, const void* k_new, const void* v_new, 
   const int S = decode_slices(n);
   HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D>), dim3(S > 0 ? S : 1, BH), dim3(256), 0, st, (const T*)q,
               (const T*)k_new, (const T*)v_new, (T*)Kc, (T*)Vc, (const T*)Klm, ws.lists, n, Lmax, Nmax, scale);
-  HILS_LAUNCH("decode_attend", (decode_attend_kernel<T, D>), dim3(BH), dim3(1024), 0, st, (const T*)q,
-              (const T*)Kc, (const T*)Vc, (const T*)Klm, ws.lists, (T*)o, idx, w, n, Lmax, Nmax, k, scale);
+  HILS_LAUNCH("decode_attend", (decode_attend_kernel<T, D>), dim3(DEC_SPLIT, BH), dim3(256), 0, st, (const T*)q,
+              (const T*)Kc, (const T*)Vc, (const T*)Klm, ws.lists, ws.part, idx, w, n, Lmax, Nmax, k, scale);
+  HILS_LAUNCH("decode_fuse", (decode_fuse_kernel<T, D>), dim3(BH), dim3(64), 0, st, ws.part, (T*)o);
   return hipGetLastError();
 }
 

@@ -134,8 +134,8 @@ size_t carve_bwd(void* base, const Dims& D, hils::BwdBufs* ws) {
 size_t carve_decode(void* base, int64_t BH, int64_t Lmax, int64_t d, int64_t k, hils::DecodeBufs* ws) {
   Carver cv(base);
   ws->lists = cv.take<uint64_t>((size_t)(BH * hils::decode_max_slices() * hils::decode_list_len()));
+  ws->part = cv.take<float>((size_t)(BH * hils::decode_split() * d));
   (void)Lmax;
-  (void)d;
   (void)k;
   return cv.off;
 }

@@ -58,7 +58,9 @@ inline int fwd_pairs_per_item(int N) { return N <= 1024 ? 512 : 1024; }
 
 struct DecodeBufs {
   uint64_t* lists;  // [BH][decode_max_slices()][decode_list_len()] best (score, chunk) keys of every slice
+  float* part;      // [BH][decode_split()][d] weighted partial outputs of the attention workgroups
 };
+int decode_split();
 int decode_slices(int64_t n_ctx);
 int decode_max_slices();
 int decode_list_len();
