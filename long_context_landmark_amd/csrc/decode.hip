@@ -295,16 +295,17 @@ __device__ __forceinline__ void wave_attend_chunk(const T* __restrict__ Kc, cons
   }
 }
 
-constexpr int DEC_SPLIT = 4;  // attention workgroups per head
+constexpr int DEC_SPLIT = 8;  // attention workgroups per head
+constexpr int DEC_NWV = 16 / DEC_SPLIT;  // wavefronts per attention workgroup (16 kept slots)
 
-// DEC_SPLIT workgroups of four wavefronts per head, so that the kept chunks' key and value
+// DEC_SPLIT workgroups of DEC_NWV wavefronts per head, so that the kept chunks' key and value
 // reads spread over as many compute units.  In every workgroup wave 0 merges the slice lists
 // and computes the fusion weights (the same result everywhere); workgroup s, wave v then
-// attends to kept slot 4v + s, and workgroup 0's wave 3 attends to the open chunk meanwhile,
-// since that needs no selection.  Each workgroup writes its weighted partial sum (its slots in
+// attends to kept slot DEC_SPLIT * v + s, and workgroup 0's last wave attends to the open
+// chunk meanwhile, since that needs no selection.  Each workgroup writes its weighted partial sum (its slots in
 // order); decode_fuse adds the DEC_SPLIT partials.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_attend_kernel(const T* __restrict__ q, const T* __restrict__ Kc,
+__global__ __launch_bounds__(64 * DEC_NWV) void decode_attend_kernel(const T* __restrict__ q, const T* __restrict__ Kc,
                                                             const T* __restrict__ Vc, const T* __restrict__ Klm,
                                                             const uint64_t* __restrict__ lists,
                                                             float* __restrict__ part, int32_t* __restrict__ idx,
@@ -318,8 +319,8 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(const T* __restrict_
   const int S = (c + DEC_ROWS - 1) / DEC_ROWS;
   __shared__ uint64_t top[16];
   __shared__ uint64_t surv[64];
-  __shared__ float sc_w[4][64];
-  __shared__ float po[5][D];
+  __shared__ float sc_w[DEC_NWV][64];
+  __shared__ float po[DEC_NWV + 1][D];
   __shared__ float wsl[17];
   const int piece = lane % PIECES;
   float qv[EPP];
@@ -340,21 +341,21 @@ __global__ __launch_bounds__(256) void decode_attend_kernel(const T* __restrict_
     const float ev = used ? __expf(sv - smax) : 0.f;
     const float den = wave_sum(ev);
     if (lane < 17) wsl[lane] = ev / den;
-  } else if (wv == 3 && sp == 0) {
-    wave_attend_chunk<T, D>(Kh, Vh, (int64_t)c * 64, (int)(n - (int64_t)c * 64) + 1, qv, scale, sc_w[wv], po[4],
-                            lane);
+  } else if (wv == DEC_NWV - 1 && sp == 0) {
+    wave_attend_chunk<T, D>(Kh, Vh, (int64_t)c * 64, (int)(n - (int64_t)c * 64) + 1, qv, scale, sc_w[wv],
+                            po[DEC_NWV], lane);
   }
   __syncthreads();
-  const int slot = 4 * wv + sp;
+  const int slot = DEC_SPLIT * wv + sp;
   if (slot < m)
     wave_attend_chunk<T, D>(Kh, Vh, (int64_t)key_index(top[slot]) * 64, 64, qv, scale, sc_w[wv], po[wv], lane);
   __syncthreads();
-  for (int e = tid; e < D; e += 256) {
+  for (int e = tid; e < D; e += 64 * DEC_NWV) {
     float acc = 0.f;
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      if (4 * v + sp < m) acc += wsl[4 * v + sp] * po[v][e];
-    if (sp == 0) acc += wsl[16] * po[4][e];
+    for (int v = 0; v < DEC_NWV; ++v)
+      if (DEC_SPLIT * v + sp < m) acc += wsl[DEC_SPLIT * v + sp] * po[v][e];
+    if (sp == 0) acc += wsl[16] * po[DEC_NWV][e];
     part[((int64_t)bh * DEC_SPLIT + sp) * D + e] = acc;
   }
   if (sp == 0 && tid <= k) {
@@ -385,7 +386,7 @@ static hipError_t decode_t(const void* q, const void* k_new, const void* v_new, 
   const int S = decode_slices(n);
   HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D>), dim3(S > 0 ? S : 1, BH), dim3(256), 0, st, (const T*)q,
               (const T*)k_new, (const T*)v_new, (T*)Kc, (T*)Vc, (const T*)Klm, ws.lists, n, Lmax, Nmax, scale);
-  HILS_LAUNCH("decode_attend", (decode_attend_kernel<T, D>), dim3(DEC_SPLIT, BH), dim3(256), 0, st, (const T*)q,
+  HILS_LAUNCH("decode_attend", (decode_attend_kernel<T, D>), dim3(DEC_SPLIT, BH), dim3(64 * DEC_NWV), 0, st, (const T*)q,
               (const T*)Kc, (const T*)Vc, (const T*)Klm, ws.lists, ws.part, idx, w, n, Lmax, Nmax, k, scale);
   HILS_LAUNCH("decode_fuse", (decode_fuse_kernel<T, D>), dim3(BH), dim3(64), 0, st, ws.part, (T*)o);
   return hipGetLastError();
