@@ -168,7 +168,7 @@ __device__ __forceinline__ void wave_chunk_attention(const ChunkLds<T, D>& s, co
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void chunk_attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(256, D == 64 ? 4 : 2) void chunk_attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                              const T* __restrict__ V, const int* __restrict__ chunk_off,
                                                              const int4* __restrict__ items,
                                                              const int* __restrict__ n_items,
