@@ -119,27 +119,32 @@ __global__ __launch_bounds__(256, (SMALL && D == 64) ? 4 : 3) void topk_select_k
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) a[ks].load(Kb + (int64_t)jrow * D + ks * 32 + 8 * g);
   };
+  // the four query blocks' products are independent: issuing them in turn keeps the
+  // MFMA pipeline full instead of waiting on each accumulator
   auto mma_tile = [&](const Frag<T>(&a)[D / 32], f32x4_t(&acc)[4]) {
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      acc[qb] = zero4();
+    for (int qb = 0; qb < 4; ++qb) acc[qb] = zero4();
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) mma(acc[qb], a[ks], qf[qb][ks]);
-    }
+    for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) mma(acc[qb], a[ks], qf[qb][ks]);
   };
   // the next tile is always requested (the last one again at the end) so that every wait
-  // covers exactly the tile about to be used
+  // covers exactly the tile about to be used; the scheduling barriers keep those requests
+  // ahead of the current tile's products, a whole tile of work before they are needed
   auto sweep_from = [&](Frag<T>(&a0)[D / 32], auto&& visit) {
     Frag<T> a1[D / 32];
-    for (int tile = 0; tile < ntile; tile += 2) {
+    for (int i = 0; i < ntile; i += 2) {
       f32x4_t acc[4];
-      load_tile(min(tile + 1, ntile - 1), a1);
+      load_tile(min(i + 1, ntile - 1), a1);
+      __builtin_amdgcn_sched_barrier(0);
       mma_tile(a0, acc);
-      visit(tile, acc);
-      load_tile(min(tile + 2, ntile - 1), a0);
-      if (tile + 1 < ntile) {
+      visit(i, acc);
+      load_tile(min(i + 2, ntile - 1), a0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < ntile) {
         mma_tile(a1, acc);
-        visit(tile + 1, acc);
+        visit(i + 1, acc);
       }
     }
   };
@@ -150,8 +155,11 @@ __global__ __launch_bounds__(256, (SMALL && D == 64) ? 4 : 3) void topk_select_k
   };
 
   // the first landmark tile and the own-chunk operands are requested before anything waits
-  Frag<T> first_tile[D / 32];
-  if (m > 0) load_tile(0, first_tile);
+  Frag<T> first_tile[D / 32], second_tile[SMALL ? D / 32 : 1];
+  if (m > 0) {
+    load_tile(0, first_tile);
+    if constexpr (SMALL) load_tile(min(1, ntile - 1), second_tile);
+  }
   __shared__ float own_s[64];
   {
     const int q = tid >> 2, part = tid & 3;
@@ -203,10 +211,8 @@ __global__ __launch_bounds__(256, (SMALL && D == 64) ? 4 : 3) void topk_select_k
       }
     };
     if constexpr (SMALL) {
-      Frag<T> a1[D / 32];
-      load_tile(min(1, ntile - 1), a1);
       mma_tile(first_tile, keep0);
-      mma_tile(a1, keep1);
+      mma_tile(second_tile, keep1);
       group_max(0, keep0);
       if (ntile > 1) group_max(1, keep1);
     } else {
