@@ -103,7 +103,10 @@ hils_status hils_landmark_scores(const void* Q, const void* K_lm, float* S, int6
  * Causal top-k chunk selection fused with the scoring (ai-feeds summary
  * "Key modules" items 1-2: scores, top-k chunks, chunk-level softmax).
  * Writes idx, sel_score and (if w is non-null) the fusion weights w for every
- * query row.  Scores are never materialised.  No workspace.
+ * query row.  Scores are never materialised.  Workspace:
+ * hils_workspace_size(HILS_OP_TOPK, ...) bytes (16-byte aligned; the bf16
+ * path keeps a copy of K_lm there, rows in MFMA fragment order), owned by
+ * the caller and free again when the stream has run the call.
  */
 hils_status hils_topk_select(const void* Q, const void* K_lm, int32_t* idx, float* sel_score, float* w,
                              int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk, float scale,

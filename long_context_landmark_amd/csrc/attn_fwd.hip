@@ -168,7 +168,7 @@ __device__ __forceinline__ void wave_chunk_attention(const ChunkLds<T, D>& s, co
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, D == 64 ? 4 : 2) void chunk_attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 2) : 1) void chunk_attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                              const T* __restrict__ V, const int* __restrict__ chunk_off,
                                                              const int4* __restrict__ items,
                                                              const int* __restrict__ n_items,
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void chunk_attn_fwd_kernel(co
 // stored at the pairs' list positions (pos_of): every partial row is read as whole
 // 128-byte lines, and O and lse are written row by row.
 template <typename T, int D>
-__global__ __launch_bounds__(256, D == 64 ? 5 : 3) void own_combine_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 5 : 3) : 1) void own_combine_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                           const T* __restrict__ V, const int* __restrict__ pos_of,
                                                           const float* __restrict__ w,
                                                           const uint16_t* __restrict__ partial,

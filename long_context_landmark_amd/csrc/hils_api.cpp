@@ -89,6 +89,7 @@ struct FwdWs {
   float* trash_lse;
   float* lse_pair;  // [BH][L*k] chunk log-partition of every pair, in list order
   float* w_tmp;
+  void* klm_frag;   // landmarks in fragment order for the selection sweeps
 };
 
 size_t carve_route(Carver& cv, const Dims& D, hils::RouteBufs& rb, int ppi) {
@@ -116,6 +117,7 @@ size_t carve_fwd(void* base, const Dims& D, FwdWs* ws) {
   ws->w_tmp = cv.take<float>((size_t)BH * D.L * (D.k + 1));
   ws->trash = cv.take<uint16_t>((size_t)D.d);
   ws->trash_lse = cv.take<float>(64);
+  ws->klm_frag = cv.take<uint8_t>(hils::topk_workspace_bytes((int)BH, (int)D.N, (int)D.d));
   return cv.off;
 }
 
@@ -161,8 +163,10 @@ size_t hils_workspace_size(int op, int64_t B, int64_t H, int64_t L, int64_t d, i
   g_err[0] = 0;
   switch (op) {
     case HILS_OP_SCORES:
-    case HILS_OP_TOPK:
       return 0;
+    case HILS_OP_TOPK:
+      if (check_dims(B, H, L, d, C, topk, true, &D) != HILS_OK) return 0;
+      return hils::topk_workspace_bytes((int)(B * H), (int)D.N, (int)d);
     case HILS_OP_FWD: {
       if (check_dims(B, H, L, d, C, topk, true, &D) != HILS_OK) return 0;
       FwdWs ws;
@@ -204,8 +208,6 @@ hils_status hils_landmark_scores(const void* Q, const void* K_lm, float* S, int6
 hils_status hils_topk_select(const void* Q, const void* K_lm, int32_t* idx, float* sel_score, float* w, int64_t B,
                              int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk, float scale, hils_dtype dt,
                              void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   Dims D;
   hils_status st;
   if ((st = check_dims(B, H, L, d, C, topk, true, &D)) != HILS_OK) return st;
@@ -216,7 +218,8 @@ hils_status hils_topk_select(const void* Q, const void* K_lm, int32_t* idx, floa
   REQUIRE_PTR(sel_score);
   OPTIONAL_PTR(w);
   if (!(scale > 0.f)) return fail(HILS_ERR_INVALID_ARG, "scale must be positive");
-  return hip_status(hils::launch_topk(dt, (int)d, Q, K_lm, idx, sel_score, w, (int)(B * H), (int)L, (int)D.N,
+  if ((st = check_ws(ws, ws_bytes, hils::topk_workspace_bytes((int)(B * H), (int)D.N, (int)d))) != HILS_OK) return st;
+  return hip_status(hils::launch_topk(dt, (int)d, Q, K_lm, ws, idx, sel_score, w, (int)(B * H), (int)L, (int)D.N,
                                       (int)topk, scale, (hipStream_t)stream),
                     "hils_topk_select");
 }
@@ -248,7 +251,7 @@ hils_status hils_sparse_attn_fwd(const void* Q, const void* K, const void* V, co
   hipStream_t s = (hipStream_t)stream;
   float* w = w_out ? w_out : W.w_tmp;
   hipError_t e;
-  if (select) e = hils::launch_topk(dt, id, Q, K_lm, idx, sel_score, w, BH, iL, iN, ik, scale, s);
+  if (select) e = hils::launch_topk(dt, id, Q, K_lm, W.klm_frag, idx, sel_score, w, BH, iL, iN, ik, scale, s);
   else e = hils::launch_fixed_selection(dt, id, Q, K_lm, idx, sel_score, w, BH, iL, iN, ik, scale, s);
   if (e != hipSuccess) return hip_status(e, "hils_sparse_attn_fwd: selection");
   if ((e = hils::launch_route(idx, W.rb, BH, iL, iN, ik, s)) != hipSuccess)

@@ -20,8 +20,10 @@ void end(hipStream_t st);
 
 hipError_t launch_landmark_scores(int dt, int d, const void* Q, const void* Klm, float* S, int BH, int L, int N,
                                   float scale, hipStream_t st);
-hipError_t launch_topk(int dt, int d, const void* Q, const void* Klm, int32_t* idx, float* sel, float* w, int BH,
-                       int L, int N, int k, float scale, hipStream_t st);
+// frag_ws: topk_workspace_bytes(BH, N, d) bytes (bf16 only; unused for fp32)
+size_t topk_workspace_bytes(int BH, int N, int d);
+hipError_t launch_topk(int dt, int d, const void* Q, const void* Klm, void* frag_ws, int32_t* idx, float* sel,
+                       float* w, int BH, int L, int N, int k, float scale, hipStream_t st);
 // scores and weights of a caller-given selection (slots with idx < 0 are unused)
 hipError_t launch_fixed_selection(int dt, int d, const void* Q, const void* Klm, const int32_t* idx, float* sel,
                                   float* w, int BH, int L, int N, int k, float scale, hipStream_t st);

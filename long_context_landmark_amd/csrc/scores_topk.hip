@@ -68,7 +68,60 @@ __global__ __launch_bounds__(256) void landmark_scores_kernel(const T* __restric
   }
 }
 
+// ----------------------------------------------------------------------------
+// Landmark rows in MFMA fragment order (bf16).  The selection sweeps read every landmark
+// tile once per 64-query block; loaded straight from [N][D] rows, a fragment load has each
+// lane quad spread over four rows, which the vector memory path serves at a quarter of its
+// rate.  This copy stores, for every 16-row block and 32-element k-step, the 64 lanes'
+// 16-byte pieces one after another (lane = r16 + 16 g holds row r16, elements 8g..8g+7 of
+// the step), so one fragment load reads 1 KiB of consecutive bytes.  Rows are padded to a
+// multiple of 64 with zeros.  Layout: [BH][Npad / 16][D / 32][64][8].
+__host__ __device__ inline int klm_frag_rows(int N) { return (N + 63) / 64 * 64; }
+
+template <int D>
+__global__ __launch_bounds__(256) void klm_frag_kernel(const bf16_t* __restrict__ Klm, bf16_t* __restrict__ F, int N,
+                                                       int Npad, int64_t total_pieces) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p >= total_pieces) return;
+  constexpr int KS = D / 32;
+  const int lane = (int)(p & 63);
+  const int ks = (int)((p >> 6) % KS);
+  const int64_t blk_all = (p >> 6) / KS;  // bh * (Npad / 16) + block
+  const int nblk = Npad / 16;
+  const int64_t bh = blk_all / nblk;
+  const int row = (int)(blk_all % nblk) * 16 + (lane & 15);
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (row < N) v = *reinterpret_cast<const u32x4_t*>(Klm + (bh * N + row) * D + ks * 32 + 8 * (lane >> 4));
+  *reinterpret_cast<u32x4_t*>(F + p * 8) = v;
+}
+
+// Neighbouring floats in the order of the reals (-0 and +0 are adjacent steps).
+__device__ __forceinline__ float float_step(float x, int dir) {
+  const int i = __float_as_int(x);
+  int o = i >= 0 ? i : -(i & 0x7fffffff) - 1;
+  o += dir;
+  return __int_as_float(o >= 0 ? o : (int)((uint32_t)(-(o + 1)) | 0x80000000u));
+}
+// The least float a with fl(s * a) >= t, for s > 0: the rounded product is non-decreasing
+// in a, so fl(s * x) >= t exactly when x >= a.  Starts at t / s and steps to the boundary
+// (a few ulps at most).  Infinite t is returned as it is (the same test then holds).
+__device__ __forceinline__ float least_raw_bound(float t, float s) {
+  if (!(fabsf(t) < INFINITY)) return t;
+  float a = t / s;
+  if (s * a >= t) {
+    for (int it = 0; it < 64; ++it) {
+      const float b = float_step(a, -1);
+      if (!(s * b >= t)) break;
+      a = b;
+    }
+  } else {
+    for (int it = 0; it < 64 && !(s * a >= t); ++it) a = float_step(a, 1);
+  }
+  return a;
+}
+
 constexpr int TK_CAP = 64;  // survivor slots per query (16 per sorting lane)
+constexpr int TK_SMALL_N = 129;  // up to this many chunks a query chunk has at most two candidate tiles
 
 // One workgroup per (b,h, query chunk c): the 64 queries t = 64c .. 64c+63
 // share the candidate set {0..c-1}.  Wave w scores the 16-chunk block w of
@@ -76,10 +129,10 @@ constexpr int TK_CAP = 64;  // survivor slots per query (16 per sorting lane)
 // SMALL: every query chunk has at most two landmark tiles of candidates (N <= 129 chunks);
 // the score tiles of sweep 1 are then kept in registers for sweep 2.
 template <typename T, int D, bool SMALL>
-__global__ __launch_bounds__(256, (SMALL && D == 64) ? 4 : 3) void topk_select_kernel(const T* __restrict__ Q, const T* __restrict__ Klm,
-                                                          int32_t* __restrict__ idx, float* __restrict__ sel,
-                                                          float* __restrict__ wout, int L, int N, int k,
-                                                          float scale) {
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) : 1) void topk_select_kernel(const T* __restrict__ Q, const T* __restrict__ Klm,
+                                                          const T* __restrict__ F, int32_t* __restrict__ idx,
+                                                          float* __restrict__ sel, float* __restrict__ wout, int L,
+                                                          int N, int k, float scale) {
   const int nc = L / 64;
   int xi, bh;
   xcd_map(xi, bh);  // a head's landmark rows are re-read by all its query chunks: keep them in one L2
@@ -89,6 +142,10 @@ __global__ __launch_bounds__(256, (SMALL && D == 64) ? 4 : 3) void topk_select_k
   const int k1 = k + 1;
   const T* Qb = Q + ((int64_t)bh * L + (int64_t)c * 64) * D;
   const T* Kb = Klm + (int64_t)bh * N * D;
+  // bf16 landmarks of long candidate lists are read from their fragment-order copy (one
+  // 1 KiB run per fragment load); with at most two tiles the direct loads are kept
+  constexpr bool FRAG = sizeof(T) == 2 && !SMALL;
+  const T* Fb = FRAG ? F + (int64_t)bh * klm_frag_rows(N) * D : nullptr;
 
   // the group maxima (sweep 1), the survivors (sweep 2) and the sorted top keys share storage
   __shared__ union {
@@ -114,10 +171,18 @@ __global__ __launch_bounds__(256, (SMALL && D == 64) ? 4 : 3) void topk_select_k
   // fragments of the next tile are loaded while the current one is on the MFMA units
   // rows past the candidates (j >= c) load row c-1 instead: their scores are never used, and
   // unconditional loads let the compiler wait for exactly the tile it needs
+  // In the fragment-order copy every tile below ceil(c/64) is whole; its rows at or past c
+  // (later chunks, or zero padding) are scored but never used.
   auto load_tile = [&](int tile, Frag<T>(&a)[D / 32]) {
-    const int jrow = min(tile * 64 + 16 * w + r16, c - 1);
+    if constexpr (FRAG) {
+      const T* fp = Fb + ((int64_t)(4 * tile + w) * (D / 32) * 64 + lane) * 8;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) a[ks].load(Kb + (int64_t)jrow * D + ks * 32 + 8 * g);
+      for (int ks = 0; ks < D / 32; ++ks) a[ks].load(fp + ks * 64 * 8);
+    } else {
+      const int jrow = min(tile * 64 + 16 * w + r16, c - 1);
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) a[ks].load(Kb + (int64_t)jrow * D + ks * 32 + 8 * g);
+    }
   };
   // the four query blocks' products are independent: issuing them in turn keeps the
   // MFMA pipeline full instead of waiting on each accumulator
@@ -132,32 +197,37 @@ __global__ __launch_bounds__(256, (SMALL && D == 64) ? 4 : 3) void topk_select_k
   // the next tile is always requested (the last one again at the end) so that every wait
   // covers exactly the tile about to be used; the scheduling barriers keep those requests
   // ahead of the current tile's products, a whole tile of work before they are needed
+  // Workgroups of neighbouring query chunks run together on one XCD; each starts its sweep
+  // at another landmark tile (and wraps around), so that they do not all request the same
+  // few L2 lines at once.  The visits are order-independent (maxima, survivor sets).
+  const int t_start = SMALL ? 0 : c % max(ntile, 1);
+  auto tile_at = [&](int i) { return i + t_start < ntile ? i + t_start : i + t_start - ntile; };
   auto sweep_from = [&](Frag<T>(&a0)[D / 32], auto&& visit) {
     Frag<T> a1[D / 32];
     for (int i = 0; i < ntile; i += 2) {
       f32x4_t acc[4];
-      load_tile(min(i + 1, ntile - 1), a1);
+      load_tile(tile_at(min(i + 1, ntile - 1)), a1);
       __builtin_amdgcn_sched_barrier(0);
       mma_tile(a0, acc);
-      visit(i, acc);
-      load_tile(min(i + 2, ntile - 1), a0);
+      visit(tile_at(i), acc);
+      load_tile(tile_at(min(i + 2, ntile - 1)), a0);
       __builtin_amdgcn_sched_barrier(0);
       if (i + 1 < ntile) {
         mma_tile(a1, acc);
-        visit(i + 1, acc);
+        visit(tile_at(i + 1), acc);
       }
     }
   };
   auto sweep = [&](auto&& visit) {
     Frag<T> a0[D / 32];
-    load_tile(0, a0);
+    load_tile(tile_at(0), a0);
     sweep_from(a0, visit);
   };
 
   // the first landmark tile and the own-chunk operands are requested before anything waits
   Frag<T> first_tile[D / 32], second_tile[SMALL ? D / 32 : 1];
   if (m > 0) {
-    load_tile(0, first_tile);
+    load_tile(tile_at(0), first_tile);
     if constexpr (SMALL) load_tile(min(1, ntile - 1), second_tile);
   }
   __shared__ float own_s[64];
@@ -238,33 +308,44 @@ __global__ __launch_bounds__(256, (SMALL && D == 64) ? 4 : 3) void topk_select_k
       if (part == 0) tau_s[q] = tau;
     }
     __syncthreads();
-    // sweep 2: keep candidates at or above the bound.  A raw-accumulator bound a little below
-    // tau / scale first rejects whole rows of four (every score that reaches tau after the
-    // rounded scaling passes it: the margin exceeds the rounding of both quotients); the few
-    // that pass are then tested exactly on the scaled score.
-    float tau_r[4], raw_lo[4];
+    // sweep 2: keep the candidates at or above the bound.  The rounded product scale * a is
+    // non-decreasing in a, so "scale * acc >= tau" holds exactly when acc >= a0, the least
+    // float with that property: the test runs on the raw accumulators.  Each lane then
+    // walks its few passing elements (rarely more than one per tile), picks each one out of
+    // its sixteen accumulators with a select tree, and appends its key to the query's
+    // survivor list.
+    // (with at most two tiles the products are formed directly instead)
+    float a0[4];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      tau_r[qb] = tau_s[16 * qb + r16];
-      const float t = tau_r[qb] / scale;
-      raw_lo[qb] = t - fabsf(t) * 1e-6f - 1e-30f;
-    }
+    for (int qb = 0; qb < 4; ++qb) a0[qb] = SMALL ? tau_s[16 * qb + r16] : least_raw_bound(tau_s[16 * qb + r16], scale);
     __syncthreads();  // every lane has read its bounds: the survivor buffer may overwrite the maxima
     auto survive = [&](int tile, const f32x4_t(&acc)[4]) {
+      // in the last tile the rows past c hold scores of other chunks (or padding)
+      const bool whole = (tile + 1) * 64 <= c;
+      const int jb = tile * 64 + 16 * w + 4 * g;
+      uint32_t bits = 0;  // bit 4 qb + i
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
-        const float m4 = fmaxf(fmaxf(acc[qb][0], acc[qb][1]), fmaxf(acc[qb][2], acc[qb][3]));
-        if (m4 >= raw_lo[qb]) {
+      for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = tile * 64 + 16 * w + 4 * g + i;
-            const float sv = scale * acc[qb][i];
-            if (j < c && sv >= tau_r[qb]) {
-              const int q = 16 * qb + r16;
-              const int p = atomicAdd(&cnt_s[q], 1);
-              if (p < TK_CAP) surv[q][p] = make_key(sv, j);
-            }
-          }
+        for (int i = 0; i < 4; ++i)
+          bits |= ((SMALL ? scale * acc[qb][i] : acc[qb][i]) >= a0[qb] && (whole || jb + i < c)) ? (1u << (4 * qb + i))
+                                                                                            : 0u;
+      while (__any(bits != 0)) {
+        if (bits != 0) {
+          const int e = __builtin_ctz(bits);
+          bits &= bits - 1u;
+          // element e = 4 qb + i: select on bit 0, 1 (i), then 2, 3 (qb)
+          const bool b0 = (e & 1) != 0, b1 = (e & 2) != 0, b2 = (e & 4) != 0, b3 = (e & 8) != 0;
+          const float y0 = b0 ? acc[0][1] : acc[0][0], y1 = b0 ? acc[0][3] : acc[0][2];
+          const float y2 = b0 ? acc[1][1] : acc[1][0], y3 = b0 ? acc[1][3] : acc[1][2];
+          const float y4 = b0 ? acc[2][1] : acc[2][0], y5 = b0 ? acc[2][3] : acc[2][2];
+          const float y6 = b0 ? acc[3][1] : acc[3][0], y7 = b0 ? acc[3][3] : acc[3][2];
+          const float z0 = b1 ? y1 : y0, z1 = b1 ? y3 : y2, z2 = b1 ? y5 : y4, z3 = b1 ? y7 : y6;
+          const float u0 = b2 ? z1 : z0, u1 = b2 ? z3 : z2;
+          const float x = b3 ? u1 : u0;
+          const int q = 16 * (e >> 2) + r16;
+          const int p = atomicAdd(&cnt_s[q], 1);
+          if (p < TK_CAP) surv[q][p] = make_key(scale * x, jb + (e & 3));
         }
       }
     };
@@ -392,16 +473,26 @@ hipError_t launch_landmark_scores_t(const void* Q, const void* Klm, float* S, in
   return hipGetLastError();
 }
 
+size_t topk_workspace_bytes(int BH, int N, int d) { return (size_t)BH * klm_frag_rows(N) * d * sizeof(bf16_t); }
+
 template <typename T, int D>
-hipError_t launch_topk_t(const void* Q, const void* Klm, int32_t* idx, float* sel, float* w, int BH, int L, int N,
-                         int k, float scale, hipStream_t st) {
+hipError_t launch_topk_t(const void* Q, const void* Klm, void* frag_ws, int32_t* idx, float* sel, float* w, int BH,
+                         int L, int N, int k, float scale, hipStream_t st) {
+  const T* F = nullptr;
+  if (sizeof(T) == 2 && N > TK_SMALL_N) {
+    const int Npad = klm_frag_rows(N);
+    const int64_t pieces = (int64_t)BH * Npad * D / 8;
+    HILS_LAUNCH("klm_frag", klm_frag_kernel<D>, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st,
+                (const bf16_t*)Klm, (bf16_t*)frag_ws, N, Npad, pieces);
+    F = (const T*)frag_ws;
+  }
   dim3 grid(L / 64, BH);
-  if (N <= 129)
-    HILS_LAUNCH("topk_select", (topk_select_kernel<T, D, true>), grid, dim3(256), 0, st, (const T*)Q, (const T*)Klm, idx,
-                sel, w, L, N, k, scale);
+  if (N <= TK_SMALL_N)
+    HILS_LAUNCH("topk_select", (topk_select_kernel<T, D, true>), grid, dim3(256), 0, st, (const T*)Q, (const T*)Klm, F,
+                idx, sel, w, L, N, k, scale);
   else
-    HILS_LAUNCH("topk_select", (topk_select_kernel<T, D, false>), grid, dim3(256), 0, st, (const T*)Q, (const T*)Klm, idx,
-                sel, w, L, N, k, scale);
+    HILS_LAUNCH("topk_select", (topk_select_kernel<T, D, false>), grid, dim3(256), 0, st, (const T*)Q, (const T*)Klm, F,
+                idx, sel, w, L, N, k, scale);
   return hipGetLastError();
 }
 
@@ -413,12 +504,12 @@ hipError_t launch_landmark_scores(int dt, int d, const void* Q, const void* Klm,
                  : launch_landmark_scores_t<float, 128>(Q, Klm, S, BH, L, N, scale, st);
 }
 
-hipError_t launch_topk(int dt, int d, const void* Q, const void* Klm, int32_t* idx, float* sel, float* w, int BH,
-                       int L, int N, int k, float scale, hipStream_t st) {
-  if (dt == 0) return d == 64 ? launch_topk_t<bf16_t, 64>(Q, Klm, idx, sel, w, BH, L, N, k, scale, st)
-                              : launch_topk_t<bf16_t, 128>(Q, Klm, idx, sel, w, BH, L, N, k, scale, st);
-  return d == 64 ? launch_topk_t<float, 64>(Q, Klm, idx, sel, w, BH, L, N, k, scale, st)
-                 : launch_topk_t<float, 128>(Q, Klm, idx, sel, w, BH, L, N, k, scale, st);
+hipError_t launch_topk(int dt, int d, const void* Q, const void* Klm, void* frag_ws, int32_t* idx, float* sel,
+                       float* w, int BH, int L, int N, int k, float scale, hipStream_t st) {
+  if (dt == 0) return d == 64 ? launch_topk_t<bf16_t, 64>(Q, Klm, frag_ws, idx, sel, w, BH, L, N, k, scale, st)
+                              : launch_topk_t<bf16_t, 128>(Q, Klm, frag_ws, idx, sel, w, BH, L, N, k, scale, st);
+  return d == 64 ? launch_topk_t<float, 64>(Q, Klm, frag_ws, idx, sel, w, BH, L, N, k, scale, st)
+                 : launch_topk_t<float, 128>(Q, Klm, frag_ws, idx, sel, w, BH, L, N, k, scale, st);
 }
 
 }  // namespace hils

@@ -153,8 +153,9 @@ def topk_select(Q, K_lm, k, C=64, scale=None, with_weights=True):
     idx = torch.empty((B, H, L, k + 1), dtype=torch.int32, device=Q.device)
     sel = torch.empty((B, H, L, k + 1), dtype=torch.float32, device=Q.device)
     w = torch.empty_like(sel) if with_weights else None
+    wsb, n = _workspace(OP_TOPK, B, H, L, d, C, k, Q.device)
     _check(_lib.hils_topk_select(_p(Q), _p(K_lm), _p(idx), _p(sel), _p(w), B, H, L, d, C, k, _scale(d, scale),
-                                 _dt(Q), None, 0, _stream()))
+                                 _dt(Q), _p(wsb), n, _stream()))
     return idx, sel, w
 
 

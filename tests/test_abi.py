@@ -69,6 +69,14 @@ def test_topk_validation(lib, kw, status, msg):
     assert msg in lib.hils_last_error().decode()
 
 
+def test_topk_workspace_checks(lib, hils):
+    need = hils.workspace_size(hils.OP_TOPK, 1, 1, 128, 64, 64, 4)
+    args = [FAKE] * 4 + [None, 1, 1, 128, 64, 64, 4, 0.125, 0]
+    assert lib.hils_topk_select(*args, None, need, None) == WORKSPACE
+    assert lib.hils_topk_select(*args, FAKE, need - 16, None) == WORKSPACE
+    assert "too small" in lib.hils_last_error().decode()
+
+
 def test_fwd_workspace_checks(lib, hils):
     need = hils.workspace_size(hils.OP_FWD, 1, 2, 1024, 64, 64, 4)
     assert need > 0
@@ -85,7 +93,9 @@ def test_workspace_size_grows_with_problem(hils):
     b = hils.workspace_size(hils.OP_FWD, 1, 2, 1024, 64, 64, 4)
     c = hils.workspace_size(hils.OP_FWD, 1, 1, 2048, 128, 64, 8)
     assert 0 < a < b and a < c
-    assert hils.workspace_size(hils.OP_TOPK, 1, 1, 1024, 64, 64, 4) == 0
+    # the selection keeps a copy of the landmarks, rows padded to a multiple of 64
+    assert hils.workspace_size(hils.OP_TOPK, 1, 1, 1024, 64, 64, 4) == 64 * 64 * 2
+    assert hils.workspace_size(hils.OP_TOPK, 2, 3, 64 * 65, 128, 64, 4) == 6 * 128 * 128 * 2
     with pytest.raises(hils.HilsError):
         hils.workspace_size(hils.OP_FWD, 1, 1, 1000, 64, 64, 4)
 
