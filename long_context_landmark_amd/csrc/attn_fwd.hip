@@ -176,9 +176,18 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 2) : 1) void c
                                                              const float* __restrict__ w, float* __restrict__ lse_pair,
                                                              uint16_t* __restrict__ partial, uint16_t* __restrict__ trash,
                                                              float* __restrict__ trash_lse, int L, int N, int k,
-                                                             int max_items, int ppi, float scale) {
+                                                             int max_items, int ppi, float scale, int spread) {
+  // A head whose query rows fit in one XCD's L2 keeps all its items on that XCD (the rows
+  // gathered by its items are then read from HBM once).  Larger heads are spread over all
+  // XCDs, head after head, so the query rows of the few heads in flight stay in the
+  // memory-side cache.
   int item, bh;
-  xcd_map(item, bh);
+  if (spread) {
+    item = blockIdx.x;
+    bh = blockIdx.y;
+  } else {
+    xcd_map(item, bh);
+  }
   // the item (chunk, pair range) and the item count are read together; items past the count
   // hold stale data and are discarded
   const int4 it = items[(int64_t)bh * max_items + item];
@@ -197,12 +206,19 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 2) : 1) void c
   // tiles i+1 and i+2 are in flight in the other two and the pair entries of tile i+3 are
   // read.  Loads are unconditional (clamped to valid rows; rows of absent pairs are computed
   // and dropped) so that every wait covers exactly the data about to be used.
+  // bf16 query rows of d = 128 are gathered a quad per row and assembled into fragments
+  // with a lane permutation just before use (the pair entry of the row a lane loads is read
+  // for it).  At d = 64 the direct fragment loads measured faster.
+  constexpr bool QUAD = sizeof(T) == 2 && D == 128;
+  const int qrow = QUAD ? quad_row(lane) : r16, qpc = QUAD ? quad_piece(lane) : g;
   auto pair_raw = [&](int base) { return pl[min(base + 16 * w_ + r16, p1 - 1)]; };
   auto pair_ok = [&](int base) { return base + 16 * w_ + r16 < p1; };
+  auto gat_raw = [&](int base) { return pl[min(base + 16 * w_ + qrow, p1 - 1)]; };
+  auto gat_ok = [&](int base) { return base + 16 * w_ + qrow < p1; };
   auto load_q = [&](int pe, Frag<T>(&qf)[D / 32]) {
     const int64_t t = pe >= 0 ? (pe >> 5) : 0;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) qf[ks].load(Qb + t * D + ks * 32 + 8 * g);
+    for (int ks = 0; ks < D / 32; ++ks) qf[ks].load(Qb + t * D + ks * 32 + 8 * qpc);
   };
   auto load_w = [&](int pe) {
     const int64_t t = pe >= 0 ? (pe >> 5) : 0;
@@ -219,9 +235,15 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 2) : 1) void c
   uint16_t* rowbuf = reinterpret_cast<uint16_t*>(&s) + w_ * 16 * RSB;
   static_assert(!ROWS || 4 * 16 * RSB * 2 <= (int)sizeof(ChunkLds<T, D>), "turnaround buffer fits the staging LDS");
   auto tile = [&](const Frag<T>(&qf)[D / 32], float wf, int pe, int base) {
+    Frag<T> qx[D / 32];
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      qx[ks] = qf[ks];
+      if constexpr (QUAD) frag_from_quads(qx[ks], lane);
+    }
     f32x4_t o[D / 16];
     float mx, sum;
-    wave_chunk_attention(s, cf, qf, scale, -1, wf, o, mx, sum);
+    wave_chunk_attention(s, cf, qx, scale, -1, wf, o, mx, sum);
     const bool ok = pe >= 0;
     const int64_t prow = (int64_t)bh * L * k + base + 16 * w_ + r16;
     if constexpr (ROWS) {
@@ -256,11 +278,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 2) : 1) void c
   int pe0 = pair_ok(p0) ? pair_raw(p0) : -1;
   int pe1 = pair_ok(p0 + 64) ? pair_raw(p0 + 64) : -1;
   int pe2;
-  load_q(pe0, q0);
+  load_q(gat_ok(p0) ? gat_raw(p0) : -1, q0);
   w0 = load_w(pe0);
-  load_q(pe1, q1);
+  load_q(gat_ok(p0 + 64) ? gat_raw(p0 + 64) : -1, q1);
   w1 = load_w(pe1);
-  int raw = pair_raw(p0 + 128);
+  int raw = pair_raw(p0 + 128), graw = gat_raw(p0 + 128);
   stage_chunk<T, D>(s, K + (int64_t)bh * L * D, V + (int64_t)bh * L * D, (int64_t)j * 64);
   __syncthreads();
   cf.init(s);
@@ -269,9 +291,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 2) : 1) void c
   // entry of tile base+192, run tile base
 #define HILS_FWD_STEP(QU, WU, PU, QF, WF, PF)                  \
   PF = pair_ok(base + 128) ? raw : -1;                         \
-  load_q(PF, QF);                                              \
+  load_q(gat_ok(base + 128) ? graw : -1, QF);                  \
   WF = load_w(PF);                                             \
   raw = pair_raw(base + 192);                                  \
+  graw = gat_raw(base + 192);                                  \
   tile(QU, WU, PU, base);                                      \
   base += 64;                                                  \
   if (base >= p1) break;
@@ -427,9 +450,10 @@ template <typename T, int D>
 static hipError_t chunk_attn_t(const void* Q, const void* K, const void* V, const RouteBufs& rb, const float* w,
                                float* lse, uint16_t* partial, uint16_t* trash, float* trash_lse, int BH, int L, int N,
                                int k, float scale, hipStream_t st) {
+  const int spread = (int64_t)L * D * sizeof(T) > L2_BYTES_PER_XCD;
   HILS_LAUNCH("chunk_attn_fwd", (chunk_attn_fwd_kernel<T, D>), dim3(rb.max_items, BH), dim3(256), 0, st, (const T*)Q,
                      (const T*)K, (const T*)V, rb.chunk_off, rb.items, rb.n_items, rb.pairs, w, lse, partial, trash,
-                     trash_lse, L, N, k, rb.max_items, rb.pairs_per_item, scale);
+                     trash_lse, L, N, k, rb.max_items, rb.pairs_per_item, scale, spread);
   return hipGetLastError();
 }
 

@@ -96,6 +96,22 @@ template <> struct Frag<float> {
   __device__ __forceinline__ float get(int e) const { return v[e]; }
 };
 
+// Gathered rows as MFMA fragments.  A fragment holds row r16 = lane & 15 in every lane, so
+// loading it directly has each quad of neighbouring lanes read four different rows, which
+// the vector memory path serves at a quarter of its rate.  Instead lane 4a + b loads the
+// 16 bytes at elements 8b.. of each 32-element step of row a (a quad reads 64 consecutive
+// bytes), and the fragment is then assembled across lanes: lane (r16, g) takes the value
+// of lane 4 r16 + g, which holds the same elements of the same row.
+__device__ __forceinline__ int quad_row(int lane) { return lane >> 2; }
+__device__ __forceinline__ int quad_piece(int lane) { return lane & 3; }
+__device__ __forceinline__ void frag_from_quads(Frag<bf16_t>& f, int lane) {
+  const int src = (4 * (lane & 15) + (lane >> 4)) * 4;  // byte address of the source lane
+  u32x4_t u = __builtin_bit_cast(u32x4_t, f.v);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) u[e] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)u[e]);
+  f.v = __builtin_bit_cast(bf16x8_t, u);
+}
+
 // acc += A(16x32) * B(32x16) for one k block
 __device__ __forceinline__ void mma(f32x4_t& acc, const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
@@ -261,6 +277,7 @@ __device__ __forceinline__ float wave_max_xor(float v, int from_mask, int to_mas
 // that all workgroups of a head run on one XCD, in x order: the head's data then
 // stays in one L2 instead of eight.  Otherwise the plain mapping is kept.
 constexpr int NUM_XCD = 8;
+constexpr int64_t L2_BYTES_PER_XCD = 4 << 20;
 __device__ __forceinline__ void xcd_map(int& x, int& y) {
   const int gx = (int)gridDim.x, gy = (int)gridDim.y;
   x = (int)blockIdx.x;
