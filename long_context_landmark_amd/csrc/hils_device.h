@@ -170,6 +170,41 @@ template <typename K> __device__ __forceinline__ void sort16_desc(K (&a)[16]) {
   }
 }
 
+// Sort the first 8 of N values descending: the 19-comparator network of depth 6 (optimal
+// for 8 inputs; checked on all 0/1 inputs).
+template <typename K, int N> __device__ __forceinline__ void sort8_desc(K (&a)[N]) {
+  static_assert(N >= 8, "needs 8 values");
+  constexpr int net[19][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}, {0, 4}, {1, 5}, {2, 6}, {3, 7}, {0, 1}, {2, 3},
+                              {4, 5}, {6, 7}, {2, 4}, {3, 5}, {1, 4}, {3, 6}, {1, 2}, {3, 4}, {5, 6}};
+#pragma unroll
+  for (int c = 0; c < 19; ++c) cmpswap_desc(a[net[c][0]], a[net[c][1]]);
+}
+
+// The first 8 values are bitonic; sort them descending.
+template <typename K, int N> __device__ __forceinline__ void bitonic_merge8_desc(K (&a)[N]) {
+#pragma unroll
+  for (int stride = 4; stride > 0; stride >>= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int p = i ^ stride;
+      if (p > i) cmpswap_desc(a[i], a[p]);
+    }
+  }
+}
+
+// The 8 largest of 16 values, sorted descending, into a[0..7] (a[8..15] are left unordered).
+template <typename K> __device__ __forceinline__ void top8_of16_desc(K (&a)[16]) {
+  K b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[i] = a[8 + i];
+  sort8_desc(a);
+  sort8_desc(b);
+  // a[i] vs b[7-i]: the larger halves form a bitonic sequence holding the top 8
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = a[i] > b[7 - i] ? a[i] : b[7 - i];
+  bitonic_merge8_desc(a);
+}
+
 // a is bitonic; sort it descending.
 template <typename K> __device__ __forceinline__ void bitonic_merge16_desc(K (&a)[16]) {
 #pragma unroll
@@ -263,6 +298,17 @@ template <typename K> __device__ __forceinline__ void merge16_with_lane(K (&a)[1
 #pragma unroll
   for (int i = 0; i < 16; ++i) a[i] = a[i] > b[15 - i] ? a[i] : b[15 - i];
   bitonic_merge16_desc(a);
+}
+
+// The first 8 values of this lane and of lane (l ^ mask), both sorted descending: keep the 8
+// largest of the 16, sorted descending, in a[0..7].
+template <typename K, int N> __device__ __forceinline__ void merge8_with_lane(K (&a)[N], int mask) {
+  K b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[i] = shfl_xor_any(a[i], mask);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = a[i] > b[7 - i] ? a[i] : b[7 - i];
+  bitonic_merge8_desc(a);
 }
 
 __device__ __forceinline__ float wave_max_xor(float v, int from_mask, int to_mask) {

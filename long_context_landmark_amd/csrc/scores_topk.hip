@@ -298,9 +298,17 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
       float v[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) v[e] = gmax_s[q][16 * part + e];
-      sort16_desc(v);
-      merge16_with_lane(v, 1);
-      merge16_with_lane(v, 2);
+      // the m-th largest of the 64 maxima is among every lane's m largest: with m <= 8 the
+      // lanes keep and merge their top 8 only
+      if (m <= 8) {
+        top8_of16_desc(v);
+        merge8_with_lane(v, 1);
+        merge8_with_lane(v, 2);
+      } else {
+        sort16_desc(v);
+        merge16_with_lane(v, 1);
+        merge16_with_lane(v, 2);
+      }
       float tau = v[0];
 #pragma unroll
       for (int e = 0; e < 16; ++e)
@@ -366,14 +374,24 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
 #pragma unroll
       for (int msk = 1; msk < 64; msk <<= 1) nmax = max(nmax, lane_xor(nmax, msk));
       uint64_t v[16];
+      if (nmax <= 8) {
+        // at most 8 survivors per query (the common case for k <= 8): they sit in the first
+        // 8 slots of part 0; an 8-input network sorts them
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int p = 16 * part + e;
-        v[e] = (p < n && p < TK_CAP) ? surv[q][p] : 0ull;
+        for (int e = 0; e < 8; ++e) v[e] = (part == 0 && e < n) ? surv[q][e] : 0ull;
+        sort8_desc(v);
+#pragma unroll
+        for (int e = 8; e < 16; ++e) v[e] = 0ull;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int p = 16 * part + e;
+          v[e] = (p < n && p < TK_CAP) ? surv[q][p] : 0ull;
+        }
+        sort16_desc(v);
+        if (nmax > 16) merge16_with_lane(v, 1);
+        if (nmax > 32) merge16_with_lane(v, 2);
       }
-      sort16_desc(v);
-      if (nmax > 16) merge16_with_lane(v, 1);
-      if (nmax > 32) merge16_with_lane(v, 2);
       __syncthreads();  // every survivor has been read: the sorted keys overwrite the buffer
       if (part == 0) {
 #pragma unroll
