@@ -230,23 +230,25 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
     load_tile(tile_at(0), first_tile);
     if constexpr (SMALL) load_tile(min(1, ntile - 1), second_tile);
   }
+  // own-chunk scores from the query fragments already held (wave 0): lane (r16, g) takes
+  // the elements 8g.. of every 32-element step of query 16 qb + r16, the four lane groups
+  // then add their partial products
   __shared__ float own_s[64];
-  {
-    const int q = tid >> 2, part = tid & 3;
-    Frag<T> oq[D / 32], ol[D / 32];
+  if (w == 0) {
+    Frag<T> lf[D / 32];
 #pragma unroll
-    for (int u = 0; u < D / 32; ++u) {
-      oq[u].load(Qb + (int64_t)q * D + part * (D / 4) + 8 * u);
-      ol[u].load(Kb + (int64_t)c * D + part * (D / 4) + 8 * u);
+    for (int ks = 0; ks < D / 32; ++ks) lf[ks].load(Kb + (int64_t)c * D + ks * 32 + 8 * g);
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      float dot = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dot += qf[qb][ks].get(e) * lf[ks].get(e);
+      dot += lane_xor(dot, 16);
+      dot += lane_xor(dot, 32);
+      if (g == 0) own_s[16 * qb + r16] = scale * dot;
     }
-    float dot = 0.f;
-#pragma unroll
-    for (int u = 0; u < D / 32; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dot += oq[u].get(e) * ol[u].get(e);
-    dot += lane_xor(dot, 1);
-    dot += lane_xor(dot, 2);
-    if (part == 0) own_s[q] = scale * dot;
   }
 
   if (tid == 0) ovf_s = 0;
