@@ -15,12 +15,14 @@
 //   chunk_attn_fwd  chunk-major: a workgroup holds one past chunk's K and V^T in
 //                   LDS and runs 64-query tiles of the queries that selected it
 //                   (gathered through the routing lists) on bf16 MFMA.  Each
-//                   pair writes its pre-weighted partial w_tj * o_tj (bf16) and
-//                   the chunk log-partition lse_tj.
+//                   pair writes its chunk output o_tj (bf16) and the chunk
+//                   log-partition lse_tj.  The fusion weights are applied in
+//                   the combine, which reads them per query row: gathered per
+//                   pair here they would cost a cache line each.
 //   own_combine     query-major: a workgroup takes the 64 queries of one chunk,
 //                   computes their causal own-chunk attention (one 64x64 MFMA
-//                   tile), adds the partials of the past chunks in slot order
-//                   and writes O.
+//                   tile), adds the weighted chunk outputs of the past chunks in
+//                   slot order and writes O.
 #include "hils_device.h"
 #include "hils_launch.h"
 
@@ -172,8 +174,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 2) : 1) void c
                                                              const T* __restrict__ V, const int* __restrict__ chunk_off,
                                                              const int4* __restrict__ items,
                                                              const int* __restrict__ n_items,
-                                                             const int* __restrict__ pairs,
-                                                             const float* __restrict__ w, float* __restrict__ lse_pair,
+                                                             const int* __restrict__ pairs, float* __restrict__ lse_pair,
                                                              uint16_t* __restrict__ partial, uint16_t* __restrict__ trash,
                                                              float* __restrict__ trash_lse, int L, int N, int k,
                                                              int max_items, int ppi, float scale, int spread) {
@@ -200,9 +201,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 2) : 1) void c
   const int tid = threadIdx.x, w_ = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
   const int* pl = pairs + (int64_t)bh * L * k;
   const T* Qb = Q + (int64_t)bh * L * D;
-  const int k1 = k + 1;
   // Software pipeline over 64-pair tiles with three register sets used in turn, so no loaded
-  // value is ever copied: while tile i runs on one set, the query rows and fusion weights of
+  // value is ever copied: while tile i runs on one set, the query rows of
   // tiles i+1 and i+2 are in flight in the other two and the pair entries of tile i+3 are
   // read.  Loads are unconditional (clamped to valid rows; rows of absent pairs are computed
   // and dropped) so that every wait covers exactly the data about to be used.
@@ -220,10 +220,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 2) : 1) void c
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) qf[ks].load(Qb + t * D + ks * 32 + 8 * qpc);
   };
-  auto load_w = [&](int pe) {
-    const int64_t t = pe >= 0 ? (pe >> 5) : 0;
-    return w[((int64_t)bh * L + t) * k1 + (pe >= 0 ? (pe & 31) : 0)];
-  };
   ChunkFrags<T, D, frags_in_regs<T, D>()> cf;
   // Results go to the pairs' own positions in the list, so a tile's 64 rows are consecutive.
   // With the chunk's fragments in registers the staging LDS is free after they are read: each
@@ -234,7 +230,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 2) : 1) void c
   constexpr int RSB = D + 8;  // row stride of the turnaround buffer (bf16 elements)
   uint16_t* rowbuf = reinterpret_cast<uint16_t*>(&s) + w_ * 16 * RSB;
   static_assert(!ROWS || 4 * 16 * RSB * 2 <= (int)sizeof(ChunkLds<T, D>), "turnaround buffer fits the staging LDS");
-  auto tile = [&](const Frag<T>(&qf)[D / 32], float wf, int pe, int base) {
+  auto tile = [&](const Frag<T>(&qf)[D / 32], int pe, int base) {
     Frag<T> qx[D / 32];
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
@@ -243,7 +239,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 2) : 1) void c
     }
     f32x4_t o[D / 16];
     float mx, sum;
-    wave_chunk_attention(s, cf, qx, scale, -1, wf, o, mx, sum);
+    wave_chunk_attention(s, cf, qx, scale, -1, 1.f, o, mx, sum);
     const bool ok = pe >= 0;
     const int64_t prow = (int64_t)bh * L * k + base + 16 * w_ + r16;
     if constexpr (ROWS) {
@@ -274,14 +270,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 2) : 1) void c
     *(ok ? lse_pair + prow : trash_lse) = mx + __logf(sum);
   };
   Frag<T> q0[D / 32], q1[D / 32], q2[D / 32];
-  float w0, w1, w2;
   int pe0 = pair_ok(p0) ? pair_raw(p0) : -1;
   int pe1 = pair_ok(p0 + 64) ? pair_raw(p0 + 64) : -1;
   int pe2;
   load_q(gat_ok(p0) ? gat_raw(p0) : -1, q0);
-  w0 = load_w(pe0);
   load_q(gat_ok(p0 + 64) ? gat_raw(p0 + 64) : -1, q1);
-  w1 = load_w(pe1);
   int raw = pair_raw(p0 + 128), graw = gat_raw(p0 + 128);
   stage_chunk<T, D>(s, K + (int64_t)bh * L * D, V + (int64_t)bh * L * D, (int64_t)j * 64);
   __syncthreads();
@@ -289,28 +282,27 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 2) : 1) void c
   if constexpr (ROWS) __syncthreads();  // every wave holds its fragments: the staging LDS is reused
   // one step: resolve the entry of tile base+128, start its loads into the free set, read the
   // entry of tile base+192, run tile base
-#define HILS_FWD_STEP(QU, WU, PU, QF, WF, PF)                  \
+#define HILS_FWD_STEP(QU, PU, QF, PF)                           \
   PF = pair_ok(base + 128) ? raw : -1;                         \
   load_q(gat_ok(base + 128) ? graw : -1, QF);                  \
-  WF = load_w(PF);                                             \
   raw = pair_raw(base + 192);                                  \
   graw = gat_raw(base + 192);                                  \
-  tile(QU, WU, PU, base);                                      \
+  tile(QU, PU, base);                                          \
   base += 64;                                                  \
   if (base >= p1) break;
   for (int base = p0;;) {
-    HILS_FWD_STEP(q0, w0, pe0, q2, w2, pe2)
-    HILS_FWD_STEP(q1, w1, pe1, q0, w0, pe0)
-    HILS_FWD_STEP(q2, w2, pe2, q1, w1, pe1)
+    HILS_FWD_STEP(q0, pe0, q2, pe2)
+    HILS_FWD_STEP(q1, pe1, q0, pe0)
+    HILS_FWD_STEP(q2, pe2, q1, pe1)
   }
 #undef HILS_FWD_STEP
 }
 
 // Per query chunk: the causal own-chunk tile on MFMA, then the fusion sum in row layout.
 // The weighted own output goes through LDS into rows; each thread then owns 16-byte pieces
-// of output rows and adds the same piece of the query's partial rows, which chunk_attn_fwd
-// stored at the pairs' list positions (pos_of): every partial row is read as whole
-// 128-byte lines, and O and lse are written row by row.
+// of output rows and adds the same piece of the query's chunk outputs, each times its fusion
+// weight; chunk_attn_fwd stored them at the pairs' list positions (pos_of): every partial
+// row is read as whole 128-byte lines, and O and lse are written row by row.
 template <typename T, int D>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 5 : 3) : 1) void own_combine_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                           const T* __restrict__ V, const int* __restrict__ pos_of,
@@ -328,6 +320,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 5 : 3) : 1) void o
     float orow[64 * RS];
   } u;
   __shared__ int pos_s[64][16];
+  __shared__ float w_s[64][16];
   __shared__ float own_lse[64];
   const int tid = threadIdx.x, w_ = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
   const int qi = 16 * w_ + r16;  // query inside the chunk (MFMA layout)
@@ -340,14 +333,19 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 5 : 3) : 1) void o
   for (int ks = 0; ks < D / 32; ++ks) qf[ks].load(Q + (row0 + qi) * D + ks * 32 + 8 * g);
   const float w_own = w[(row0 + qi) * k1 + k];
   int pv[4];
+  float wv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = tid + 256 * i;  // (query, slot) = (e / 16, e % 16); slots >= k are unused
     pv[i] = (e % 16) < k ? pos_of[(row0 + e / 16) * k + (e % 16)] : -1;
+    wv[i] = (e % 16) < k ? w[(row0 + e / 16) * k1 + (e % 16)] : 0.f;
   }
   stage_chunk<T, D>(u.s, K + (int64_t)bh * L * D, V + (int64_t)bh * L * D, (int64_t)c * 64);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pos_s[(tid + 256 * i) / 16][(tid + 256 * i) % 16] = pv[i];
+  for (int i = 0; i < 4; ++i) {
+    pos_s[(tid + 256 * i) / 16][(tid + 256 * i) % 16] = pv[i];
+    w_s[(tid + 256 * i) / 16][(tid + 256 * i) % 16] = wv[i];
+  }
   __syncthreads();
   f32x4_t o[D / 16];
   float mx, sum;
@@ -377,6 +375,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 5 : 3) : 1) void o
     if (r0 >= m) break;
     u32x4_t v[NI][SB];
     bool kept[NI][SB];
+    float wt[NI][SB];
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
       const int e = tid + 256 * it, q = e / PPR, pc = e % PPR;
@@ -384,6 +383,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 5 : 3) : 1) void o
       for (int sb = 0; sb < SB; ++sb) {
         const int p = pos_s[q][r0 + sb];
         kept[it][sb] = p >= 0;
+        wt[it][sb] = w_s[q][r0 + sb];
         v[it][sb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(partial + (pbase + max(p, 0)) * D + 8 * pc));
       }
     }
@@ -394,8 +394,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 5 : 3) : 1) void o
         const uint32_t wds[4] = {v[it][sb][0], v[it][sb][1], v[it][sb][2], v[it][sb][3]};
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          acc[it][2 * x] += kept[it][sb] ? __uint_as_float(wds[x] << 16) : 0.f;
-          acc[it][2 * x + 1] += kept[it][sb] ? __uint_as_float(wds[x] & 0xFFFF0000u) : 0.f;
+          acc[it][2 * x] += kept[it][sb] ? wt[it][sb] * __uint_as_float(wds[x] << 16) : 0.f;
+          acc[it][2 * x + 1] += kept[it][sb] ? wt[it][sb] * __uint_as_float(wds[x] & 0xFFFF0000u) : 0.f;
         }
       }
   }
@@ -447,12 +447,11 @@ __global__ __launch_bounds__(256) void fixed_selection_kernel(const T* __restric
 }
 
 template <typename T, int D>
-static hipError_t chunk_attn_t(const void* Q, const void* K, const void* V, const RouteBufs& rb, const float* w,
-                               float* lse, uint16_t* partial, uint16_t* trash, float* trash_lse, int BH, int L, int N,
+static hipError_t chunk_attn_t(const void* Q, const void* K, const void* V, const RouteBufs& rb, float* lse, uint16_t* partial, uint16_t* trash, float* trash_lse, int BH, int L, int N,
                                int k, float scale, hipStream_t st) {
   const int spread = (int64_t)L * D * sizeof(T) > L2_BYTES_PER_XCD;
   HILS_LAUNCH("chunk_attn_fwd", (chunk_attn_fwd_kernel<T, D>), dim3(rb.max_items, BH), dim3(256), 0, st, (const T*)Q,
-                     (const T*)K, (const T*)V, rb.chunk_off, rb.items, rb.n_items, rb.pairs, w, lse, partial, trash,
+                     (const T*)K, (const T*)V, rb.chunk_off, rb.items, rb.n_items, rb.pairs, lse, partial, trash,
                      trash_lse, L, N, k, rb.max_items, rb.pairs_per_item, scale, spread);
   return hipGetLastError();
 }
@@ -467,13 +466,13 @@ static hipError_t own_combine_t(const void* Q, const void* K, const void* V, con
 }
 
 hipError_t launch_chunk_attn_fwd(int dt, int d, const void* Q, const void* K, const void* V, const RouteBufs& rb,
-                                 const float* w, float* lse, uint16_t* partial, uint16_t* trash, float* trash_lse,
+                                 float* lse, uint16_t* partial, uint16_t* trash, float* trash_lse,
                                  int BH, int L, int N, int k, float scale, hipStream_t st) {
   if (dt == 0)
-    return d == 64 ? chunk_attn_t<bf16_t, 64>(Q, K, V, rb, w, lse, partial, trash, trash_lse, BH, L, N, k, scale, st)
-                   : chunk_attn_t<bf16_t, 128>(Q, K, V, rb, w, lse, partial, trash, trash_lse, BH, L, N, k, scale, st);
-  return d == 64 ? chunk_attn_t<float, 64>(Q, K, V, rb, w, lse, partial, trash, trash_lse, BH, L, N, k, scale, st)
-                 : chunk_attn_t<float, 128>(Q, K, V, rb, w, lse, partial, trash, trash_lse, BH, L, N, k, scale, st);
+    return d == 64 ? chunk_attn_t<bf16_t, 64>(Q, K, V, rb, lse, partial, trash, trash_lse, BH, L, N, k, scale, st)
+                   : chunk_attn_t<bf16_t, 128>(Q, K, V, rb, lse, partial, trash, trash_lse, BH, L, N, k, scale, st);
+  return d == 64 ? chunk_attn_t<float, 64>(Q, K, V, rb, lse, partial, trash, trash_lse, BH, L, N, k, scale, st)
+                 : chunk_attn_t<float, 128>(Q, K, V, rb, lse, partial, trash, trash_lse, BH, L, N, k, scale, st);
 }
 
 hipError_t launch_own_combine(int dt, int d, const void* Q, const void* K, const void* V, const int* pos_of,

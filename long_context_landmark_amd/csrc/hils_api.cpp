@@ -256,7 +256,7 @@ hils_status hils_sparse_attn_fwd(const void* Q, const void* K, const void* V, co
   if (e != hipSuccess) return hip_status(e, "hils_sparse_attn_fwd: selection");
   if ((e = hils::launch_route(idx, W.rb, BH, iL, iN, ik, s)) != hipSuccess)
     return hip_status(e, "hils_sparse_attn_fwd: routing");
-  if ((e = hils::launch_chunk_attn_fwd(dt, id, Q, K, V, W.rb, w, W.lse_pair, W.partial, W.trash, W.trash_lse, BH, iL,
+  if ((e = hils::launch_chunk_attn_fwd(dt, id, Q, K, V, W.rb, W.lse_pair, W.partial, W.trash, W.trash_lse, BH, iL,
                                        iN, ik, scale, s)) != hipSuccess)
     return hip_status(e, "hils_sparse_attn_fwd: chunk attention");
   if ((e = hils::launch_own_combine(dt, id, Q, K, V, W.rb.pos_of, w, W.partial, W.lse_pair, O, lse_out, BH, iL, iN,

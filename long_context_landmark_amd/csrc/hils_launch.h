@@ -43,12 +43,12 @@ int route_seg_q(int L);
 int route_max_items(int L, int N, int k, int pairs_per_item);
 hipError_t launch_route(const int32_t* idx, const RouteBufs& rb, int BH, int L, int N, int k, hipStream_t st);
 
-// Writes, for every pair at position p of the routing lists, the weighted partial output
-// partial[bh][p][d] (bf16) and the chunk log-partition lse_pair[bh][p]: consecutive pairs of a
+// Writes, for every pair at position p of the routing lists, the chunk output (softmax
+// attention of the query over the chunk, not yet weighted) partial[bh][p][d] (bf16) and the chunk log-partition lse_pair[bh][p]: consecutive pairs of a
 // work item land in consecutive rows.  trash (d elements) and trash_lse (one float) receive
 // the stores of absent pairs.
 hipError_t launch_chunk_attn_fwd(int dt, int d, const void* Q, const void* K, const void* V, const RouteBufs& rb,
-                                 const float* w, float* lse_pair, uint16_t* partial, uint16_t* trash, float* trash_lse,
+                                 float* lse_pair, uint16_t* partial, uint16_t* trash, float* trash_lse,
                                  int BH, int L, int N, int k, float scale, hipStream_t st);
 // partial and lse_pair are indexed by pair position (chunk-major, as chunk_attn_fwd writes
 // them); pos_of maps (query, slot) to that position
