@@ -169,7 +169,7 @@ __device__ __forceinline__ void wave_chunk_attention(const ChunkLds<T, D>& s, co
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool STREAM_OUT>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 2) : 1) void chunk_attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                              const T* __restrict__ V, const int* __restrict__ chunk_off,
                                                              const int4* __restrict__ items,
@@ -222,6 +222,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 2) : 1) void c
   };
   ChunkFrags<T, D, frags_in_regs<T, D>()> cf;
   // Results go to the pairs' own positions in the list, so a tile's 64 rows are consecutive.
+  // When all partial rows together exceed the memory-side cache they are stored as streaming
+  // (non-temporal) data, which keeps the cache for the gathered query rows; smaller sets stay
+  // cached for the combine, which reads them right after.
   // With the chunk's fragments in registers the staging LDS is free after they are read: each
   // wave then turns its 16 output rows around there and stores them as whole rows (16 bytes a
   // lane, 1 KiB a store).  Rows of absent pairs go to a scratch row: every lane stores, so
@@ -255,7 +258,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 2) : 1) void c
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(rowbuf + row * RSB + 8 * pc);
         const int pidx = base + 16 * w_ + row;
         uint16_t* dst = pidx < p1 ? partial + ((int64_t)bh * L * k + pidx) * D : trash;
-        *reinterpret_cast<u32x4_t*>(dst + 8 * pc) = v;
+        if constexpr (STREAM_OUT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst + 8 * pc));
+        else *reinterpret_cast<u32x4_t*>(dst + 8 * pc) = v;
       }
       __builtin_amdgcn_wave_barrier();
     } else {
@@ -450,9 +454,14 @@ template <typename T, int D>
 static hipError_t chunk_attn_t(const void* Q, const void* K, const void* V, const RouteBufs& rb, float* lse, uint16_t* partial, uint16_t* trash, float* trash_lse, int BH, int L, int N,
                                int k, float scale, hipStream_t st) {
   const int spread = (int64_t)L * D * sizeof(T) > L2_BYTES_PER_XCD;
-  HILS_LAUNCH("chunk_attn_fwd", (chunk_attn_fwd_kernel<T, D>), dim3(rb.max_items, BH), dim3(256), 0, st, (const T*)Q,
-                     (const T*)K, (const T*)V, rb.chunk_off, rb.items, rb.n_items, rb.pairs, lse, partial, trash,
-                     trash_lse, L, N, k, rb.max_items, rb.pairs_per_item, scale, spread);
+  if ((int64_t)BH * L * k * D * 2 > MALL_BYTES)
+    HILS_LAUNCH("chunk_attn_fwd", (chunk_attn_fwd_kernel<T, D, true>), dim3(rb.max_items, BH), dim3(256), 0, st,
+                (const T*)Q, (const T*)K, (const T*)V, rb.chunk_off, rb.items, rb.n_items, rb.pairs, lse, partial,
+                trash, trash_lse, L, N, k, rb.max_items, rb.pairs_per_item, scale, spread);
+  else
+    HILS_LAUNCH("chunk_attn_fwd", (chunk_attn_fwd_kernel<T, D, false>), dim3(rb.max_items, BH), dim3(256), 0, st,
+                (const T*)Q, (const T*)K, (const T*)V, rb.chunk_off, rb.items, rb.n_items, rb.pairs, lse, partial,
+                trash, trash_lse, L, N, k, rb.max_items, rb.pairs_per_item, scale, spread);
   return hipGetLastError();
 }
 

@@ -324,6 +324,7 @@ __device__ __forceinline__ float wave_max_xor(float v, int from_mask, int to_mas
 // stays in one L2 instead of eight.  Otherwise the plain mapping is kept.
 constexpr int NUM_XCD = 8;
 constexpr int64_t L2_BYTES_PER_XCD = 4 << 20;
+constexpr int64_t MALL_BYTES = (int64_t)256 << 20;  // memory-side (Infinity) cache
 __device__ __forceinline__ void xcd_map(int& x, int& y) {
   const int gx = (int)gridDim.x, gy = (int)gridDim.y;
   x = (int)blockIdx.x;
