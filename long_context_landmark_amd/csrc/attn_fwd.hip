@@ -65,11 +65,12 @@ __device__ __forceinline__ void stage_chunk(ChunkLds<T, D>& s, const T* __restri
 }
 
 // The MFMA operand fragments of one staged chunk as a wave uses them: K rows (A operand of
-// S^T = K Q^T) and V^T rows (A operand of O^T = V^T P^T).  With REG they are read from LDS
+// S^T = K Q^T) and V^T rows (A operand of O^T = V^T P^T).  REG = 2: both are read from LDS
 // once and stay in registers for every query tile the wave runs against the chunk (64 + 64
-// registers at d = 128 in bf16); otherwise each use reads LDS.
-template <typename T, int D, bool REG> struct ChunkFrags;
-template <typename T, int D> struct ChunkFrags<T, D, true> {
+// registers at d = 128 in bf16); REG = 1: the K fragments stay in registers and V^T is read
+// from LDS at each use (fewer registers, more waves per CU); REG = 0: every use reads LDS.
+template <typename T, int D, int REG> struct ChunkFrags;
+template <typename T, int D> struct ChunkFrags<T, D, 2> {
   Frag<T> kf[4][D / 32];
   Frag<T> vf[D / 16][2];
   __device__ __forceinline__ void init(const ChunkLds<T, D>& s) {
@@ -89,7 +90,7 @@ template <typename T, int D> struct ChunkFrags<T, D, true> {
   __device__ __forceinline__ const Frag<T>& k(const ChunkLds<T, D>&, int cb, int ks) const { return kf[cb][ks]; }
   __device__ __forceinline__ const Frag<T>& v(const ChunkLds<T, D>&, int db, int h) const { return vf[db][h]; }
 };
-template <typename T, int D> struct ChunkFrags<T, D, false> {
+template <typename T, int D> struct ChunkFrags<T, D, 0> {
   __device__ __forceinline__ void init(const ChunkLds<T, D>&) {}
   __device__ __forceinline__ Frag<T> k(const ChunkLds<T, D>& s, int cb, int ks) const {
     const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
@@ -105,8 +106,30 @@ template <typename T, int D> struct ChunkFrags<T, D, false> {
     return a;
   }
 };
-// fragments in registers except for fp32 at d = 128, which would need 256 registers for them
-template <typename T, int D> constexpr bool frags_in_regs() { return Elem<T>::bytes == 2 || D == 64; }
+template <typename T, int D> struct ChunkFrags<T, D, 1> {
+  Frag<T> kf[4][D / 32];
+  __device__ __forceinline__ void init(const ChunkLds<T, D>& s) {
+    const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) kf[cb][ks].load(&s.k[(16 * cb + r16) * ChunkLds<T, D>::KS + ks * 32 + 8 * g]);
+  }
+  __device__ __forceinline__ const Frag<T>& k(const ChunkLds<T, D>&, int cb, int ks) const { return kf[cb][ks]; }
+  __device__ __forceinline__ Frag<T> v(const ChunkLds<T, D>& s, int db, int h) const {
+    const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+    Frag<T> a;
+    const T* row = &s.vt[(16 * db + r16) * ChunkLds<T, D>::VS + 32 * h + 4 * g];
+    a.load4x2(row, row + 16);
+    return a;
+  }
+};
+// K fragments in registers for the chunk kernel (the K staging area is then free for the
+// output turnaround); V^T too except for bf16 at d = 128, where keeping it in LDS lets three
+// workgroups share a CU; fp32 at d = 128 keeps both in LDS.
+template <typename T, int D> constexpr int frags_in_regs() {
+  return Elem<T>::bytes == 2 ? (D == 128 ? 1 : 2) : (D == 64 ? 2 : 0);
+}
 
 // One wave: attention of 16 query rows (given as B fragments) over the 64 keys of a chunk.
 // causal_q >= 0 applies the causal mask key <= causal_q (the lane's query index inside the
@@ -114,7 +137,7 @@ template <typename T, int D> constexpr bool frags_in_regs() { return Elem<T>::by
 // lane's query weight), the row's scaled maximum and its sum of exponentials relative to it.
 // The exponentials are exp2 of one fused multiply-add: scale * log2(e) is folded into the
 // raw scores, and wt / sum into the probabilities before they are rounded for the PV product.
-template <typename T, int D, bool REG>
+template <typename T, int D, int REG>
 __device__ __forceinline__ void wave_chunk_attention(const ChunkLds<T, D>& s, const ChunkFrags<T, D, REG>& cf,
                                                      const Frag<T> (&qf)[D / 32], float scale, int causal_q, float wt,
                                                      f32x4_t (&o)[D / 16], float& mx, float& sum) {
@@ -170,7 +193,7 @@ __device__ __forceinline__ void wave_chunk_attention(const ChunkLds<T, D>& s, co
 }
 
 template <typename T, int D, bool STREAM_OUT>
-__global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 2) : 1) void chunk_attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 3) : 1) void chunk_attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                              const T* __restrict__ V, const int* __restrict__ chunk_off,
                                                              const int4* __restrict__ items,
                                                              const int* __restrict__ n_items,
@@ -229,10 +252,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 2) : 1) void c
   // wave then turns its 16 output rows around there and stores them as whole rows (16 bytes a
   // lane, 1 KiB a store).  Rows of absent pairs go to a scratch row: every lane stores, so
   // the waits on the loads of the next tiles can count the stores.
-  constexpr bool ROWS = frags_in_regs<T, D>();
+  constexpr bool ROWS = frags_in_regs<T, D>() > 0;
   constexpr int RSB = D + 8;  // row stride of the turnaround buffer (bf16 elements)
   uint16_t* rowbuf = reinterpret_cast<uint16_t*>(&s) + w_ * 16 * RSB;
-  static_assert(!ROWS || 4 * 16 * RSB * 2 <= (int)sizeof(ChunkLds<T, D>), "turnaround buffer fits the staging LDS");
+  static_assert(!ROWS || 4 * 16 * RSB * 2 <= 64 * ChunkLds<T, D>::KS * (int)sizeof(T),
+                "turnaround buffer fits the K staging area");
   auto tile = [&](const Frag<T>(&qf)[D / 32], int pe, int base) {
     Frag<T> qx[D / 32];
 #pragma unroll
@@ -353,7 +377,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 5 : 3) : 1) void o
   __syncthreads();
   f32x4_t o[D / 16];
   float mx, sum;
-  ChunkFrags<T, D, false> cf;  // one tile: the fragments are read once either way
+  ChunkFrags<T, D, 0> cf;  // one tile: the fragments are read once either way
   wave_chunk_attention(u.s, cf, qf, scale, qi, w_own, o, mx, sum);
   __syncthreads();  // every wave is done with the keys and values: the rows reuse their space
 #pragma unroll
