@@ -158,6 +158,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
   auto& top_s = u_s.top;
   __shared__ int cnt_s[64];
   __shared__ float tau_s[64];
+  __shared__ f32x4_t park_s[SMALL ? 1 : 4][4][64];  // survivor sweep: a wave's accumulators
   __shared__ int ovf_s;
 
   Frag<T> qf[4][D / 32];
@@ -340,19 +341,31 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
         for (int i = 0; i < 4; ++i)
           bits |= ((SMALL ? scale * acc[qb][i] : acc[qb][i]) >= a0[qb] && (whole || jb + i < c)) ? (1u << (4 * qb + i))
                                                                                             : 0u;
+      if (!__any(bits != 0)) return;
+      // long lists: the wave parks its accumulators in LDS (four 16-byte stores a lane) and
+      // each survivor reads its value back by index; short ones pick it with a select tree
+      if constexpr (!SMALL) {
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) park_s[w][qb][lane] = acc[qb];
+      }
       while (__any(bits != 0)) {
         if (bits != 0) {
           const int e = __builtin_ctz(bits);
           bits &= bits - 1u;
-          // element e = 4 qb + i: select on bit 0, 1 (i), then 2, 3 (qb)
-          const bool b0 = (e & 1) != 0, b1 = (e & 2) != 0, b2 = (e & 4) != 0, b3 = (e & 8) != 0;
-          const float y0 = b0 ? acc[0][1] : acc[0][0], y1 = b0 ? acc[0][3] : acc[0][2];
-          const float y2 = b0 ? acc[1][1] : acc[1][0], y3 = b0 ? acc[1][3] : acc[1][2];
-          const float y4 = b0 ? acc[2][1] : acc[2][0], y5 = b0 ? acc[2][3] : acc[2][2];
-          const float y6 = b0 ? acc[3][1] : acc[3][0], y7 = b0 ? acc[3][3] : acc[3][2];
-          const float z0 = b1 ? y1 : y0, z1 = b1 ? y3 : y2, z2 = b1 ? y5 : y4, z3 = b1 ? y7 : y6;
-          const float u0 = b2 ? z1 : z0, u1 = b2 ? z3 : z2;
-          const float x = b3 ? u1 : u0;
+          float x;
+          if constexpr (!SMALL) {
+            x = reinterpret_cast<const float*>(&park_s[w][e >> 2][lane])[e & 3];
+          } else {
+            // element e = 4 qb + i: select on bit 0, 1 (i), then 2, 3 (qb)
+            const bool b0 = (e & 1) != 0, b1 = (e & 2) != 0, b2 = (e & 4) != 0, b3 = (e & 8) != 0;
+            const float y0 = b0 ? acc[0][1] : acc[0][0], y1 = b0 ? acc[0][3] : acc[0][2];
+            const float y2 = b0 ? acc[1][1] : acc[1][0], y3 = b0 ? acc[1][3] : acc[1][2];
+            const float y4 = b0 ? acc[2][1] : acc[2][0], y5 = b0 ? acc[2][3] : acc[2][2];
+            const float y6 = b0 ? acc[3][1] : acc[3][0], y7 = b0 ? acc[3][3] : acc[3][2];
+            const float z0 = b1 ? y1 : y0, z1 = b1 ? y3 : y2, z2 = b1 ? y5 : y4, z3 = b1 ? y7 : y6;
+            const float u0 = b2 ? z1 : z0, u1 = b2 ? z3 : z2;
+            x = b3 ? u1 : u0;
+          }
           const int q = 16 * (e >> 2) + r16;
           const int p = atomicAdd(&cnt_s[q], 1);
           if (p < TK_CAP) surv[q][p] = make_key(scale * x, jb + (e & 3));
