@@ -48,9 +48,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: (kernel, FETCH_SIZE KiB, WRITE_SIZE KiB, source digest)
-    "prefill_8k": ("chunk_attn_fwd", 31225.8, 130569.7, "196d9ef442ba3c44"),
-    "prefill_128k": ("chunk_attn_fwd", 12079190.5, 17007150.3, "196d9ef442ba3c44"),
-    "train_8k": ("chunk_bwd", 246176.3, 912802.1, "f54c5de737790842"),
+    "prefill_8k": ("chunk_attn_fwd", 28616.9, 130576.9, "d6c73f5a57e96318"),
+    "prefill_128k": ("chunk_attn_fwd", 8510262.1, 17022035.8, "d6c73f5a57e96318"),
+    "train_8k": ("chunk_bwd", 248503.6, 920959.8, "05edf7bb371417ea"),
 }
 
 
