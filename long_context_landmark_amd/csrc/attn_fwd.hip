@@ -194,13 +194,12 @@ __device__ __forceinline__ void wave_chunk_attention(const ChunkLds<T, D>& s, co
 
 template <typename T, int D, bool STREAM_OUT>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 3) : 1) void chunk_attn_fwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
-                                                             const T* __restrict__ V, const int* __restrict__ chunk_off,
-                                                             const int4* __restrict__ items,
+                                                             const T* __restrict__ V, const int4* __restrict__ items,
                                                              const int* __restrict__ n_items,
                                                              const int* __restrict__ pairs, float* __restrict__ lse_pair,
                                                              uint16_t* __restrict__ partial, uint16_t* __restrict__ trash,
                                                              float* __restrict__ trash_lse, int L, int N, int k,
-                                                             int max_items, int ppi, float scale, int spread) {
+                                                             int max_items, float scale, int spread) {
   // A head whose query rows fit in one XCD's L2 keeps all its items on that XCD (the rows
   // gathered by its items are then read from HBM once).  Larger heads are spread over all
   // XCDs, head after head, so the query rows of the few heads in flight stay in the
@@ -218,8 +217,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 3) : 1) void c
   if (item >= n_items[bh]) return;
   const int j = it.x;
   const int p0 = it.y, p1 = it.z;
-  (void)chunk_off;
-  (void)ppi;
   __shared__ ChunkLds<T, D> s;
   const int tid = threadIdx.x, w_ = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
   const int* pl = pairs + (int64_t)bh * L * k;
@@ -480,12 +477,12 @@ static hipError_t chunk_attn_t(const void* Q, const void* K, const void* V, cons
   const int spread = (int64_t)L * D * sizeof(T) > L2_BYTES_PER_XCD;
   if ((int64_t)BH * L * k * D * 2 > MALL_BYTES)
     HILS_LAUNCH("chunk_attn_fwd", (chunk_attn_fwd_kernel<T, D, true>), dim3(rb.max_items, BH), dim3(256), 0, st,
-                (const T*)Q, (const T*)K, (const T*)V, rb.chunk_off, rb.items, rb.n_items, rb.pairs, lse, partial,
-                trash, trash_lse, L, N, k, rb.max_items, rb.pairs_per_item, scale, spread);
+                (const T*)Q, (const T*)K, (const T*)V, rb.items, rb.n_items, rb.pairs, lse, partial,
+                trash, trash_lse, L, N, k, rb.max_items, scale, spread);
   else
     HILS_LAUNCH("chunk_attn_fwd", (chunk_attn_fwd_kernel<T, D, false>), dim3(rb.max_items, BH), dim3(256), 0, st,
-                (const T*)Q, (const T*)K, (const T*)V, rb.chunk_off, rb.items, rb.n_items, rb.pairs, lse, partial,
-                trash, trash_lse, L, N, k, rb.max_items, rb.pairs_per_item, scale, spread);
+                (const T*)Q, (const T*)K, (const T*)V, rb.items, rb.n_items, rb.pairs, lse, partial,
+                trash, trash_lse, L, N, k, rb.max_items, scale, spread);
   return hipGetLastError();
 }
 
