@@ -11,7 +11,8 @@
 // A deterministic counting sort per (b,h):
 //   count    per segment of queries, an LDS histogram over chunks;
 //   scan     per chunk, exclusive offsets over segments and a global
-//            exclusive scan over chunks; also the chunk-major work items;
+//            exclusive scan over chunks; also the chunk-major work items
+//            (for short sequences folded into the scatter workgroups);
 //   scatter  one wavefront per segment walks its pairs in (t, slot) order and
 //            ranks equal chunks inside each 64-pair batch with ballots, so the
 //            list of every chunk is sorted by (t, slot) on every run; it also
@@ -122,18 +123,65 @@ __global__ __launch_bounds__(256) void route_scan_kernel(int* __restrict__ count
 // NW wavefronts per segment: wave w takes the w-th share of the segment's queries.  Each
 // wave first counts its pairs per chunk (LDS histogram); the cursors of wave w then start
 // after the pairs of waves 0..w-1 in every chunk, so the list keeps the (t, slot) order.
-template <int NW>
+//
+// FUSED (short sequences, N <= 256 chunks and at most 64 segments): there is no scan pass;
+// every segment's workgroup reads the head's raw counts itself (thread j: chunk j), forms
+// its segment offsets and, with a block scan, the chunk offsets, and the first segment's
+// workgroup also writes the chunk offsets and the work items.
+constexpr int ROUTE_FUSED_MAX_N = 256, ROUTE_FUSED_MAX_SEG = 64;
+
+template <int NW, bool FUSED>
 __global__ __launch_bounds__(64 * NW) void route_scatter_kernel(const int32_t* __restrict__ idx,
                                                                 const int* __restrict__ segoff,
-                                                                const int* __restrict__ chunk_off,
+                                                                int* __restrict__ chunk_off,
+                                                                int4* __restrict__ items, int* __restrict__ n_items,
                                                                 int* __restrict__ pairs, int* __restrict__ pos_of,
-                                                                int L, int N, int k, int nseg, int nbits, int seg_q) {
+                                                                int L, int N, int k, int nseg, int nbits, int seg_q,
+                                                                int ppi, int max_items) {
   extern __shared__ int cur_all[];  // [NW][N]
   int seg, bh;
   xcd_map(seg, bh);  // a head's segments run in order on one XCD: its list writes merge in one L2
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int* so = segoff + ((int64_t)bh * nseg + seg) * N;
   const int* co = chunk_off + (int64_t)bh * (N + 1);
+  __shared__ int so_s[FUSED ? ROUTE_FUSED_MAX_N : 1], co_s[FUSED ? ROUTE_FUSED_MAX_N : 1];
+  if constexpr (FUSED) {
+    static_assert(64 * NW == 256, "one thread per chunk");
+    __shared__ int buf[4];
+    const int j = tid;
+    int before = 0, tot = 0;
+    {
+      int cv[ROUTE_FUSED_MAX_SEG];
+#pragma unroll
+      for (int u = 0; u < ROUTE_FUSED_MAX_SEG; ++u)
+        cv[u] = (j < N && u < nseg) ? segoff[((int64_t)bh * nseg + u) * N + j] : 0;
+#pragma unroll
+      for (int u = 0; u < ROUTE_FUSED_MAX_SEG; ++u) {
+        before += u < seg ? cv[u] : 0;
+        tot += cv[u];
+      }
+    }
+    int all, sum_i;
+    const int off = block_excl_scan(tot, buf, &all);
+    const int nit = j < N ? (tot + ppi - 1) / ppi : 0;
+    const int ex_i = block_excl_scan(nit, buf, &sum_i);
+    if (j < N) {
+      so_s[j] = before;
+      co_s[j] = off;
+      if (seg == 0) {
+        chunk_off[(int64_t)bh * (N + 1) + j] = off;
+        int4* it = items + (int64_t)bh * max_items + ex_i;
+        for (int u = 0; u < nit; ++u) it[u] = make_int4(j, off + u * ppi, min(off + tot, off + (u + 1) * ppi), 0);
+      }
+    }
+    if (seg == 0 && tid == 0) {
+      chunk_off[(int64_t)bh * (N + 1) + N] = all;
+      n_items[bh] = sum_i;
+    }
+    __syncthreads();
+  }
+  auto seg_off = [&](int j) { if constexpr (FUSED) return so_s[j]; else return so[j]; };
+  auto chunk_start = [&](int j) { if constexpr (FUSED) return co_s[j]; else return co[j]; };
   const int t0 = seg * seg_q, t1 = min(L, t0 + seg_q);
   const int qpw = (seg_q + NW - 1) / NW;
   const int tw0 = min(t1, t0 + wv * qpw), tw1 = min(t1, tw0 + qpw);
@@ -156,7 +204,7 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_kernel(const int32_t* _
     }
     __syncthreads();
     for (int j = tid; j < N; j += 64 * NW) {
-      int run = co[j] + so[j];
+      int run = chunk_start(j) + seg_off(j);
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const int h = cur_all[w * N + j];
@@ -165,7 +213,7 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_kernel(const int32_t* _
       }
     }
   } else {
-    for (int j = lane; j < N; j += 64) cur[j] = co[j] + so[j];
+    for (int j = lane; j < N; j += 64) cur[j] = chunk_start(j) + seg_off(j);
   }
   __syncthreads();
   int* out = pairs + (int64_t)bh * L * k;
@@ -211,17 +259,25 @@ hipError_t launch_route(const int32_t* idx, const RouteBufs& rb, int BH, int L, 
   const size_t lds = (size_t)N * sizeof(int);
   HILS_LAUNCH("route_count", route_count_kernel, dim3(rb.nseg, BH), dim3(256), lds, st, idx, rb.counts, L, N, k, rb.nseg,
               rb.seg_q);
-  HILS_LAUNCH("route_scan", route_scan_kernel, dim3(BH), dim3(256), 0, st, rb.counts, rb.chunk_off, rb.items, rb.n_items, N,
-                     rb.nseg, rb.pairs_per_item, rb.max_items);
   int nbits = 1;
   while ((1 << nbits) < N) ++nbits;
+  if (N <= ROUTE_FUSED_MAX_N && rb.nseg <= ROUTE_FUSED_MAX_SEG) {
+    HILS_LAUNCH("route_scatter", (route_scatter_kernel<4, true>), dim3(rb.nseg, BH), dim3(256), 4 * lds, st, idx,
+                rb.counts, rb.chunk_off, rb.items, rb.n_items, rb.pairs, rb.pos_of, L, N, k, rb.nseg, nbits, rb.seg_q,
+                rb.pairs_per_item, rb.max_items);
+    return hipGetLastError();
+  }
+  HILS_LAUNCH("route_scan", route_scan_kernel, dim3(BH), dim3(256), 0, st, rb.counts, rb.chunk_off, rb.items, rb.n_items, N,
+                     rb.nseg, rb.pairs_per_item, rb.max_items);
   // four wavefronts per segment while their cursor tables fit in LDS
   if (N <= 2048)
-    HILS_LAUNCH("route_scatter", route_scatter_kernel<4>, dim3(rb.nseg, BH), dim3(256), 4 * lds, st, idx, rb.counts,
-                rb.chunk_off, rb.pairs, rb.pos_of, L, N, k, rb.nseg, nbits, rb.seg_q);
+    HILS_LAUNCH("route_scatter", (route_scatter_kernel<4, false>), dim3(rb.nseg, BH), dim3(256), 4 * lds, st, idx,
+                rb.counts, rb.chunk_off, rb.items, rb.n_items, rb.pairs, rb.pos_of, L, N, k, rb.nseg, nbits, rb.seg_q,
+                rb.pairs_per_item, rb.max_items);
   else
-    HILS_LAUNCH("route_scatter", route_scatter_kernel<1>, dim3(rb.nseg, BH), dim3(64), lds, st, idx, rb.counts,
-                rb.chunk_off, rb.pairs, rb.pos_of, L, N, k, rb.nseg, nbits, rb.seg_q);
+    HILS_LAUNCH("route_scatter", (route_scatter_kernel<1, false>), dim3(rb.nseg, BH), dim3(64), lds, st, idx,
+                rb.counts, rb.chunk_off, rb.items, rb.n_items, rb.pairs, rb.pos_of, L, N, k, rb.nseg, nbits, rb.seg_q,
+                rb.pairs_per_item, rb.max_items);
   return hipGetLastError();
 }
 
