@@ -316,7 +316,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         if (e == m - 1) tau = v[e];
-      if (part == 0) tau_s[q] = tau;
+      // long lists test raw accumulators against the least float a0 with fl(scale * a0) >= tau
+      // (see below): one lane per query forms it, once
+      if (part == 0) tau_s[q] = SMALL ? tau : least_raw_bound(tau, scale);
     }
     __syncthreads();
     // sweep 2: keep the candidates at or above the bound.  The rounded product scale * a is
@@ -328,7 +330,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
     // (with at most two tiles the products are formed directly instead)
     float a0[4];
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) a0[qb] = SMALL ? tau_s[16 * qb + r16] : least_raw_bound(tau_s[16 * qb + r16], scale);
+    for (int qb = 0; qb < 4; ++qb) a0[qb] = tau_s[16 * qb + r16];
     __syncthreads();  // every lane has read its bounds: the survivor buffer may overwrite the maxima
     auto survive = [&](int tile, const f32x4_t(&acc)[4]) {
       // in the last tile the rows past c hold scores of other chunks (or padding)
