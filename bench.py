@@ -48,9 +48,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: (kernel, FETCH_SIZE KiB, WRITE_SIZE KiB, source digest)
-    "prefill_8k": ("chunk_attn_fwd", 28616.9, 130576.9, "d6c73f5a57e96318"),
-    "prefill_128k": ("chunk_attn_fwd", 8510262.1, 17022035.8, "d6c73f5a57e96318"),
-    "train_8k": ("chunk_bwd", 248503.6, 920959.8, "05edf7bb371417ea"),
+    "prefill_8k": ("chunk_attn_fwd", 28608.2, 130573.1, "51110afdcee90ece"),
+    "prefill_128k": ("chunk_attn_fwd", 8510607.5, 17018037.8, "51110afdcee90ece"),
+    "train_8k": ("chunk_bwd", 245543.7, 911926.5, "05edf7bb371417ea"),
 }
 
 
