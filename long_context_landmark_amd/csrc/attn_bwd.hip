@@ -46,6 +46,40 @@ template <typename T, int D> struct BwdLds {
   T dat[64 * TS]; // dA^T  [key][tile query]
 };
 
+// The chunk's K and V rows as A fragments of S^T = K Q^T and dP^T = V dO^T: held in registers
+// for every tile of the chunk (bf16 at d = 64: 64 registers) or read from LDS at each use.
+template <typename T, int D, bool REG> struct KVFrags;
+template <typename T, int D> struct KVFrags<T, D, true> {
+  Frag<T> kf[4][D / 32], vf[4][D / 32];
+  __device__ __forceinline__ void init(const BwdLds<T, D>& s) {
+    const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        kf[cb][ks].load(&s.k[(16 * cb + r16) * BwdLds<T, D>::KS + ks * 32 + 8 * g]);
+        vf[cb][ks].load(&s.v[(16 * cb + r16) * BwdLds<T, D>::KS + ks * 32 + 8 * g]);
+      }
+  }
+  __device__ __forceinline__ const Frag<T>& k(const BwdLds<T, D>&, int cb, int ks) const { return kf[cb][ks]; }
+  __device__ __forceinline__ const Frag<T>& v(const BwdLds<T, D>&, int cb, int ks) const { return vf[cb][ks]; }
+};
+template <typename T, int D> struct KVFrags<T, D, false> {
+  __device__ __forceinline__ void init(const BwdLds<T, D>&) {}
+  __device__ __forceinline__ Frag<T> k(const BwdLds<T, D>& s, int cb, int ks) const {
+    const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+    Frag<T> a;
+    a.load(&s.k[(16 * cb + r16) * BwdLds<T, D>::KS + ks * 32 + 8 * g]);
+    return a;
+  }
+  __device__ __forceinline__ Frag<T> v(const BwdLds<T, D>& s, int cb, int ks) const {
+    const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+    Frag<T> a;
+    a.load(&s.v[(16 * cb + r16) * BwdLds<T, D>::KS + ks * 32 + 8 * g]);
+    return a;
+  }
+};
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                         const T* __restrict__ V, const T* __restrict__ Klm,
@@ -57,6 +91,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
                                                         float* __restrict__ trash_f, float* __restrict__ dK,
                                                         float* __restrict__ dV, int L, int N, int k, float scale) {
   using S = BwdLds<T, D>;
+  constexpr bool KV_IN_REGS = sizeof(T) == 2 && D == 64;
   int j, bh;
   xcd_map(j, bh);
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
@@ -78,6 +113,8 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
     }
   }
   __syncthreads();
+  KVFrags<T, D, KV_IN_REGS> kv;
+  kv.init(s);
 
   const int* co = chunk_off + (int64_t)bh * (N + 1);
   const int p_begin = co[j], p_end = co[j + 1];
@@ -145,11 +182,8 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
       dp[cb] = zero4();
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
-        Frag<T> a, b;
-        a.load(&s.k[(16 * cb + r16) * S::KS + ks * 32 + 8 * g]);
-        b.load(&s.v[(16 * cb + r16) * S::KS + ks * 32 + 8 * g]);
-        mma(sc[cb], a, in.qf[ks]);
-        mma(dp[cb], b, in.gf[ks]);
+        mma(sc[cb], kv.k(s, cb, ks), in.qf[ks]);
+        mma(dp[cb], kv.v(s, cb, ks), in.gf[ks]);
       }
     }
     float Dj = 0.f;
