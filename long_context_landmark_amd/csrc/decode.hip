@@ -33,6 +33,14 @@ int decode_slices(int64_t n_ctx) { return (int)((n_ctx / 64 + DEC_ROWS - 1) / DE
 int decode_max_slices() { return DEC_MAX_SLICES; }
 int decode_list_len() { return DEC_LIST; }
 
+// Lanes 0 .. n-1 hold keys (n <= 64, wave-uniform), the others 0: sorts them descending over
+// the fewest lanes that hold them (a 16- or 32-lane network has 10 or 15 stages, not 21).
+__device__ __forceinline__ uint64_t sort_first_desc(uint64_t v, int n, int lane) {
+  if (n <= 16) return wave_sort_desc<uint64_t, 16>(v, lane);
+  if (n <= 32) return wave_sort_desc<uint64_t, 32>(v, lane);
+  return wave_sort_desc<uint64_t, 64>(v, lane);
+}
+
 __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
@@ -128,7 +136,7 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ 
     for (int u = 0; u < 4; ++u)
       if (ob[u] != 0u && ob[u] >= tau) surv[p++] = make_key(vv[u], j0 + 4 * lane + u);
     __builtin_amdgcn_wave_barrier();
-    const uint64_t key = wave_sort_desc<uint64_t>(lane < total ? surv[lane] : 0ull, lane);
+    const uint64_t key = sort_first_desc(lane < total ? surv[lane] : 0ull, total, lane);
     if (lane < DEC_LIST) out[lane] = key;
   } else {
     // many scores tied at the bound: a tournament between the lanes' sorted quadruples
@@ -162,22 +170,27 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ 
 // the bound is taken on the keys' upper halves (the score order bits), which can only
 // let in more keys.  When more than 64 keys reach it, m rounds of a tournament between
 // the list heads give the same answer.
-__device__ void wave_merge_lists(const uint64_t* __restrict__ lists, int S, int m, uint64_t* top, uint64_t* surv,
-                                 int lane) {
+// The lane's list (lane < S) and its bound key's upper half, requested ahead of other work.
+struct MergeIn {
+  uint32_t bhi;
+  uint64_t mine[DEC_LIST];
+};
+__device__ __forceinline__ void merge_load(const uint64_t* __restrict__ lists, int S, int m, int lane, MergeIn& in) {
   const int R = (m + S - 1) / S;
   const int nb = S * R;  // <= 64: S if S >= m, else below m + S
   const uint32_t* hi_words = reinterpret_cast<const uint32_t*>(lists);
-  const uint32_t bhi = lane < nb ? hi_words[2 * ((lane % S) * DEC_LIST + lane / S) + 1] : 0u;
-  uint64_t mine[DEC_LIST];
-  {
-    const ulonglong2* lp = reinterpret_cast<const ulonglong2*>(lists + lane * DEC_LIST);
+  in.bhi = lane < nb ? hi_words[2 * ((lane % S) * DEC_LIST + lane / S) + 1] : 0u;
+  const ulonglong2* lp = reinterpret_cast<const ulonglong2*>(lists + lane * DEC_LIST);
 #pragma unroll
-    for (int u = 0; u < DEC_LIST / 2; ++u) {
-      const ulonglong2 v2 = lane < S ? lp[u] : make_ulonglong2(0ull, 0ull);
-      mine[2 * u] = v2.x;
-      mine[2 * u + 1] = v2.y;
-    }
+  for (int u = 0; u < DEC_LIST / 2; ++u) {
+    const ulonglong2 v2 = lane < S ? lp[u] : make_ulonglong2(0ull, 0ull);
+    in.mine[2 * u] = v2.x;
+    in.mine[2 * u + 1] = v2.y;
   }
+}
+__device__ void wave_merge_lists(const MergeIn& in, int m, uint64_t* top, uint64_t* surv, int lane) {
+  const uint32_t bhi = in.bhi;
+  const uint64_t(&mine)[DEC_LIST] = in.mine;
   const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)wave_sort_desc<uint32_t>(bhi, lane), m - 1);
   int cnt = 0;
 #pragma unroll
@@ -189,7 +202,7 @@ __device__ void wave_merge_lists(const uint64_t* __restrict__ lists, int S, int 
     for (int r = 0; r < DEC_LIST; ++r)
       if (r < cnt) surv[pre + r] = mine[r];
     __builtin_amdgcn_wave_barrier();
-    const uint64_t key = wave_sort_desc<uint64_t>(lane < total ? surv[lane] : 0ull, lane);
+    const uint64_t key = sort_first_desc(lane < total ? surv[lane] : 0ull, total, lane);
     if (lane < m) top[lane] = key;
   } else {
     int ptr = 0;
@@ -329,12 +342,15 @@ __global__ __launch_bounds__(64 * DEC_NWV) void decode_attend_kernel(const T* __
   const T* Kh = Kc + (int64_t)bh * Lmax * D;
   const T* Vh = Vc + (int64_t)bh * Lmax * D;
   if (wv == 0) {
-    // score of the open chunk (its landmark row is given), then the selection and the weights
+    // the slice lists are requested first; the score of the open chunk (its landmark row is
+    // given) is formed meanwhile, then the selection and the weights
+    MergeIn mi;
+    if (m > 0) merge_load(lists + (int64_t)bh * DEC_MAX_SLICES * DEC_LIST, S, m, lane, mi);
     float dot = 0.f;
     for (int e = lane; e < D; e += 64)
       dot += Elem<T>::to_f32(q, (int64_t)bh * D + e) * Elem<T>::to_f32(Klm, ((int64_t)bh * Nmax + c) * D + e);
     const float s_own = scale * wave_sum(dot);
-    if (m > 0) wave_merge_lists(lists + (int64_t)bh * DEC_MAX_SLICES * DEC_LIST, S, m, top, surv, lane);
+    if (m > 0) wave_merge_lists(mi, m, top, surv, lane);
     const bool used = lane < m || lane == 16;
     const float sv = lane < m ? key_score(top[lane]) : (lane == 16 ? s_own : -INFINITY);
     const float smax = wave_max(sv);

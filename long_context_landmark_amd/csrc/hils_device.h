@@ -263,10 +263,11 @@ __device__ __forceinline__ uint32_t shfl_xor_any(uint32_t v, int m) { return lan
 
 // Wave-wide bitonic sort, descending: afterwards lane i holds the i-th largest value.
 // Each stage keeps, per lane, the partner's value when it is larger and this lane
-// keeps the maximum of the pair, or smaller and it keeps the minimum.
-template <typename K> __device__ __forceinline__ K wave_sort_desc(K v, int lane) {
+// keeps the maximum of the pair, or smaller and it keeps the minimum.  With W < 64 every
+// group of W consecutive lanes is sorted on its own (lane W g + i holds its i-th largest).
+template <typename K, int W = 64> __device__ __forceinline__ K wave_sort_desc(K v, int lane) {
 #pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
+  for (int size = 2; size <= W; size <<= 1) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       const K o = shfl_xor_any(v, stride);
