@@ -56,9 +56,9 @@ __global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restr
   for (int j = tid; j < N; j += 256) out[j] = hist[j];
 }
 
-// exclusive block scan of one int per thread (256 threads); returns the block total in *total.
+// exclusive block scan of one int per thread (NW wavefronts); returns the block total in *total.
 // Each wavefront scans its 64 values, then adds the totals of the wavefronts before it.
-__device__ int block_excl_scan(int v, int* buf, int* total) {
+template <int NW = 4> __device__ int block_excl_scan(int v, int* buf, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int incl = v;
 #pragma unroll
@@ -70,7 +70,7 @@ __device__ int block_excl_scan(int v, int* buf, int* total) {
   __syncthreads();
   int before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int tw = buf[w];
     before += w < wv ? tw : 0;
     all += tw;
@@ -255,6 +255,156 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_kernel(const int32_t* _
   }
 }
 
+// Long sequences (many chunks): the pairs of one segment reach every chunk's list in runs of a
+// few entries, and 4-byte stores scattered over the head's whole list (larger than an L2)
+// would each cost a partial memory write.  This variant ranks the pairs exactly as above but
+// stages the segment's part of every list in LDS, in list order, then copies it out: the runs
+// of consecutive entries of one list are stored together by neighbouring lanes.
+// LDS (16-bit where the values are local positions below seg_q * k <= 16384):
+//   cur[NW][N]  per-wave histogram, then per-wave cursors (local positions)
+//   lbase[N+1]  start of each chunk's run in the staged segment
+//   delta[N]    list position minus local position, per chunk
+//   stage[seg_q * k]  (local query << 5) | slot, in list order
+constexpr int ROUTE_STAGED_MAX_N = 2048;
+constexpr int ROUTE_STAGED_NW = 8;
+inline size_t route_staged_lds(int N, int seg_q, int k, int nw) {
+  auto al = [](size_t b) { return (b + 15) & ~(size_t)15; };
+  return al((size_t)nw * N * 2) + al((size_t)(N + 1) * 2) + al((size_t)N * 4) + al((size_t)seg_q * k * 2);
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void route_scatter_staged_kernel(const int32_t* __restrict__ idx,
+                                                                       const int* __restrict__ segoff,
+                                                                       const int* __restrict__ chunk_off,
+                                                                       int* __restrict__ pairs,
+                                                                       int* __restrict__ pos_of, int L, int N, int k,
+                                                                       int nseg, int nbits, int seg_q) {
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  auto al = [](size_t b) { return (b + 15) & ~(size_t)15; };
+  uint16_t* cur_all = reinterpret_cast<uint16_t*>(lds_raw);
+  uint16_t* lbase = reinterpret_cast<uint16_t*>(lds_raw + al((size_t)NW * N * 2));
+  int* delta = reinterpret_cast<int*>(lds_raw + al((size_t)NW * N * 2) + al((size_t)(N + 1) * 2));
+  uint16_t* stage = reinterpret_cast<uint16_t*>(lds_raw + al((size_t)NW * N * 2) + al((size_t)(N + 1) * 2) +
+                                                al((size_t)N * 4));
+  int seg, bh;
+  xcd_map(seg, bh);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int* so = segoff + ((int64_t)bh * nseg + seg) * N;
+  const int* co = chunk_off + (int64_t)bh * (N + 1);
+  const int t0 = seg * seg_q, t1 = min(L, t0 + seg_q);
+  const int qpw = (seg_q + NW - 1) / NW;
+  const int tw0 = min(t1, t0 + wv * qpw), tw1 = min(t1, tw0 + qpw);
+  const int total = (tw1 - tw0) * k;
+  const int32_t* idx_w = idx + ((int64_t)bh * L + tw0) * (k + 1);
+  uint32_t* cur_words = reinterpret_cast<uint32_t*>(cur_all);
+  for (int i = tid; i < (NW * N + 1) / 2; i += 64 * NW) cur_words[i] = 0u;
+  __syncthreads();
+  // per-wave histograms (16-bit counters, added as halves of 32-bit words)
+  uint16_t* cur = cur_all + wv * N;
+  constexpr int UH = 16;  // batches of chunk ids in flight
+  for (int f0 = 0; f0 < total; f0 += UH * 64) {
+    int jj[UH];
+#pragma unroll
+    for (int u = 0; u < UH; ++u) {
+      const int f = f0 + u * 64 + lane;
+      jj[u] = f < total ? idx_w[(f / k) * (k + 1) + f % k] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < UH; ++u)
+      if (jj[u] >= 0 && jj[u] < N) {
+        const int e = wv * N + jj[u];
+        atomicAdd(&cur_words[e >> 1], 1u << (16 * (e & 1)));
+      }
+  }
+  __syncthreads();
+  // the segment's run of every chunk: exclusive scan of the chunk totals (CPT chunks a
+  // thread), then the per-wave cursors inside each run
+  {
+    constexpr int CPT = ROUTE_STAGED_MAX_N / (64 * NW);
+    int tot[CPT];
+    int sum = 0;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int j = tid * CPT + u;
+      int t = 0;
+      if (j < N) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) t += cur_all[w * N + j];
+      }
+      tot[u] = t;
+      sum += t;
+    }
+    __shared__ int buf[NW];
+    int all;
+    int run = block_excl_scan<NW>(sum, buf, &all);
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int j = tid * CPT + u;
+      if (j < N) {
+        lbase[j] = (uint16_t)run;
+        delta[j] = co[j] + so[j] - run;
+        int r = run;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const int h = cur_all[w * N + j];
+          cur_all[w * N + j] = (uint16_t)r;
+          r += h;
+        }
+      }
+      run += tot[u];
+    }
+    if (tid == 0) lbase[N] = (uint16_t)all;
+  }
+  __syncthreads();
+  int* pos_w = pos_of ? pos_of + ((int64_t)bh * L + tw0) * k : nullptr;
+  const uint64_t below = (1ull << lane) - 1ull;
+  constexpr int U = 8;  // batches whose chunk ids are loaded together
+  for (int b0 = 0; b0 < total; b0 += U * 64) {
+    int jj[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int f = b0 + u * 64 + lane;
+      jj[u] = f < total ? idx_w[(f / k) * (k + 1) + f % k] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int f = b0 + u * 64 + lane;
+      const int j = jj[u];
+      const bool act = j >= 0 && j < N;
+      uint64_t peers = __ballot(act);
+      if (peers == 0) {
+        if (pos_w && f < total) pos_w[f] = -1;
+        continue;
+      }
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = act && ((j >> b) & 1);
+        const uint64_t ones = __ballot(bit);
+        peers &= bit ? ones : ~ones;
+      }
+      int lpos = 0;
+      if (act) lpos = cur[j] + __popcll(peers & below);
+      // LDS instructions of one wavefront execute in order: every lane's read of cur[j]
+      // precedes the leader's update below
+      __builtin_amdgcn_wave_barrier();
+      if (act && (peers & below) == 0) cur[j] = (uint16_t)(lpos + __popcll(peers));
+      __builtin_amdgcn_wave_barrier();
+      if (act) stage[lpos] = (uint16_t)(((tw0 - t0 + f / k) << 5) | (f % k));
+      if (pos_w && f < total) pos_w[f] = act ? lpos + delta[j] : -1;
+    }
+  }
+  __syncthreads();
+  // copy-out, eight lanes per chunk: each chunk's run goes to its list as one piece
+  int* out = pairs + (int64_t)bh * L * k;
+  const int sub = lane & 7;
+  for (int j = wv * 8 + (lane >> 3); j < N; j += NW * 8) {
+    const int p0 = lbase[j], p1 = lbase[j + 1], dj = delta[j];
+    for (int p = p0 + sub; p < p1; p += 8) {
+      const int v = stage[p];
+      out[p + dj] = ((t0 + (v >> 5)) << 5) | (v & 31);
+    }
+  }
+}
+
 hipError_t launch_route(const int32_t* idx, const RouteBufs& rb, int BH, int L, int N, int k, hipStream_t st) {
   const size_t lds = (size_t)N * sizeof(int);
   HILS_LAUNCH("route_count", route_count_kernel, dim3(rb.nseg, BH), dim3(256), lds, st, idx, rb.counts, L, N, k, rb.nseg,
@@ -269,6 +419,20 @@ hipError_t launch_route(const int32_t* idx, const RouteBufs& rb, int BH, int L, 
   }
   HILS_LAUNCH("route_scan", route_scan_kernel, dim3(BH), dim3(256), 0, st, rb.counts, rb.chunk_off, rb.items, rb.n_items, N,
                      rb.nseg, rb.pairs_per_item, rb.max_items);
+  if (N <= ROUTE_STAGED_MAX_N && rb.seg_q * k <= 16384) {
+    static bool lds_set = false;  // more than 64 KiB of dynamic LDS per workgroup is opted into once
+    if (!lds_set) {
+      const hipError_t e = hipFuncSetAttribute((const void*)route_scatter_staged_kernel<ROUTE_STAGED_NW>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)route_staged_lds(ROUTE_STAGED_MAX_N, 1024, 16, ROUTE_STAGED_NW));
+      if (e != hipSuccess) return e;
+      lds_set = true;
+    }
+    HILS_LAUNCH("route_scatter", route_scatter_staged_kernel<ROUTE_STAGED_NW>, dim3(rb.nseg, BH),
+                dim3(64 * ROUTE_STAGED_NW), route_staged_lds(N, rb.seg_q, k, ROUTE_STAGED_NW), st, idx, rb.counts, rb.chunk_off, rb.pairs, rb.pos_of, L, N, k,
+                rb.nseg, nbits, rb.seg_q);
+    return hipGetLastError();
+  }
   // four wavefronts per segment while their cursor tables fit in LDS
   if (N <= 2048)
     HILS_LAUNCH("route_scatter", (route_scatter_kernel<4, false>), dim3(rb.nseg, BH), dim3(256), 4 * lds, st, idx,

@@ -142,8 +142,9 @@ def test_fwd_fixed_selection(hils, gpu):
     assert_close(f32(w), want["w"], "w (fixed selection)", 1e-5, 1e-5)
 
 
-def test_fwd_deterministic(hils, gpu):
-    B, H, L, d, k = 1, 4, 4096, 128, 16
+@pytest.mark.parametrize("H,L,d,k", [(4, 4096, 128, 16), (2, 19200, 64, 16)])  # one- and two-pass routing
+def test_fwd_deterministic(hils, gpu, H, L, d, k):
+    B = 1
     say(f"determinism B={B} H={H} L={L} d={d} k={k}")
     x = _inputs(B, H, L, d, k, seed=5, klm="chunkmean")
     t = to_inputs(x)
