@@ -265,11 +265,13 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_kernel(const int32_t* _
 //   lbase[N+1]  start of each chunk's run in the staged segment
 //   delta[N]    list position minus local position, per chunk
 //   stage[seg_q * k]  (local query << 5) | slot, in list order
+//   tag[N]      lane of the last store per chunk (8-bit): finds batches without repeated chunks
 constexpr int ROUTE_STAGED_MAX_N = 2048;
 constexpr int ROUTE_STAGED_NW = 8;
 inline size_t route_staged_lds(int N, int seg_q, int k, int nw) {
   auto al = [](size_t b) { return (b + 15) & ~(size_t)15; };
-  return al((size_t)nw * N * 2) + al((size_t)(N + 1) * 2) + al((size_t)N * 4) + al((size_t)seg_q * k * 2);
+  return al((size_t)nw * N * 2) + al((size_t)(N + 1) * 2) + al((size_t)N * 4) + al((size_t)seg_q * k * 2) +
+         al((size_t)N);
 }
 
 template <int NW>
@@ -286,6 +288,8 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_staged_kernel(const int
   int* delta = reinterpret_cast<int*>(lds_raw + al((size_t)NW * N * 2) + al((size_t)(N + 1) * 2));
   uint16_t* stage = reinterpret_cast<uint16_t*>(lds_raw + al((size_t)NW * N * 2) + al((size_t)(N + 1) * 2) +
                                                 al((size_t)N * 4));
+  uint8_t* tag = reinterpret_cast<uint8_t*>(lds_raw + al((size_t)NW * N * 2) + al((size_t)(N + 1) * 2) +
+                                            al((size_t)N * 4) + al((size_t)seg_q * k * 2));
   int seg, bh;
   xcd_map(seg, bh);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -296,26 +300,25 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_staged_kernel(const int
   const int tw0 = min(t1, t0 + wv * qpw), tw1 = min(t1, tw0 + qpw);
   const int total = (tw1 - tw0) * k;
   const int32_t* idx_w = idx + ((int64_t)bh * L + tw0) * (k + 1);
+  // the wave's chunk ids, all requested at once and kept for the ranking pass
+  constexpr int UB = 1024 * 16 / (NW * 64);  // batches of 64 pairs a wave holds at most
+  int jr[UB];
+#pragma unroll
+  for (int u = 0; u < UB; ++u) {
+    const int f = u * 64 + lane;
+    jr[u] = f < total ? idx_w[(f / k) * (k + 1) + f % k] : -1;
+  }
   uint32_t* cur_words = reinterpret_cast<uint32_t*>(cur_all);
   for (int i = tid; i < (NW * N + 1) / 2; i += 64 * NW) cur_words[i] = 0u;
   __syncthreads();
   // per-wave histograms (16-bit counters, added as halves of 32-bit words)
   uint16_t* cur = cur_all + wv * N;
-  constexpr int UH = 16;  // batches of chunk ids in flight
-  for (int f0 = 0; f0 < total; f0 += UH * 64) {
-    int jj[UH];
 #pragma unroll
-    for (int u = 0; u < UH; ++u) {
-      const int f = f0 + u * 64 + lane;
-      jj[u] = f < total ? idx_w[(f / k) * (k + 1) + f % k] : -1;
+  for (int u = 0; u < UB; ++u)
+    if (jr[u] >= 0 && jr[u] < N) {
+      const int e = wv * N + jr[u];
+      atomicAdd(&cur_words[e >> 1], 1u << (16 * (e & 1)));
     }
-#pragma unroll
-    for (int u = 0; u < UH; ++u)
-      if (jj[u] >= 0 && jj[u] < N) {
-        const int e = wv * N + jj[u];
-        atomicAdd(&cur_words[e >> 1], 1u << (16 * (e & 1)));
-      }
-  }
   __syncthreads();
   // the segment's run of every chunk: exclusive scan of the chunk totals (CPT chunks a
   // thread), then the per-wave cursors inside each run
@@ -358,35 +361,43 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_staged_kernel(const int
   __syncthreads();
   int* pos_w = pos_of ? pos_of + ((int64_t)bh * L + tw0) * k : nullptr;
   const uint64_t below = (1ull << lane) - 1ull;
-  constexpr int U = 8;  // batches whose chunk ids are loaded together
-  for (int b0 = 0; b0 < total; b0 += U * 64) {
-    int jj[U];
+  {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int f = b0 + u * 64 + lane;
-      jj[u] = f < total ? idx_w[(f / k) * (k + 1) + f % k] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int f = b0 + u * 64 + lane;
-      const int j = jj[u];
+    for (int u = 0; u < UB; ++u) {
+      if (u * 64 >= total) break;
+      const int f = u * 64 + lane;
+      const int j = jr[u];
       const bool act = j >= 0 && j < N;
       uint64_t peers = __ballot(act);
       if (peers == 0) {
         if (pos_w && f < total) pos_w[f] = -1;
         continue;
       }
-      for (int b = 0; b < nbits; ++b) {
-        const bool bit = act && ((j >> b) & 1);
-        const uint64_t ones = __ballot(bit);
-        peers &= bit ? ones : ~ones;
-      }
-      int lpos = 0;
-      if (act) lpos = cur[j] + __popcll(peers & below);
-      // LDS instructions of one wavefront execute in order: every lane's read of cur[j]
-      // precedes the leader's update below
+      // Most batches name every chunk once.  Each lane stores its number in its chunk's tag
+      // and reads it back: lanes of this wave that share a chunk read one value in the same
+      // instruction, so at least one of them sees another lane's number (another wave's
+      // store can only add false alarms).  Without a repeat every lane takes one slot.
+      if (act) tag[j] = (uint8_t)lane;
       __builtin_amdgcn_wave_barrier();
-      if (act && (peers & below) == 0) cur[j] = (uint16_t)(lpos + __popcll(peers));
+      const bool repeat = __any(act && tag[j] != lane);
+      int lpos = 0;
+      if (!repeat) {
+        if (act) {
+          lpos = cur[j];
+          cur[j] = (uint16_t)(lpos + 1);
+        }
+      } else {
+        for (int b = 0; b < nbits; ++b) {
+          const bool bit = act && ((j >> b) & 1);
+          const uint64_t ones = __ballot(bit);
+          peers &= bit ? ones : ~ones;
+        }
+        if (act) lpos = cur[j] + __popcll(peers & below);
+        // LDS instructions of one wavefront execute in order: every lane's read of cur[j]
+        // precedes the leader's update below
+        __builtin_amdgcn_wave_barrier();
+        if (act && (peers & below) == 0) cur[j] = (uint16_t)(lpos + __popcll(peers));
+      }
       __builtin_amdgcn_wave_barrier();
       if (act) stage[lpos] = (uint16_t)(((tw0 - t0 + f / k) << 5) | (f % k));
       if (pos_w && f < total) pos_w[f] = act ? lpos + delta[j] : -1;
