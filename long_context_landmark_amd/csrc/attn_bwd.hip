@@ -289,49 +289,70 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
 }
 
 // Eight consecutive d of one query row per thread: D = sum_j w_j D_j, ds_j = w_j (D_j - D),
-// dQ = sum_j (in-chunk part_j + scale ds_j Klm_j) in slot order.
-template <typename T, int D>
+// dQ = sum_j (in-chunk part_j + scale ds_j Klm_j) in slot order.  K1M >= k + 1 slots are
+// held in registers and every load of a row is issued before any is used (slots past k + 1
+// and dropped slots read a valid address and are not used): two memory round trips per
+// thread, the landmark rows once the indices are in.
+template <typename T, int D, int K1M>
 __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* __restrict__ dq_part,
                                                         const float* __restrict__ Dpart,
                                                         const int32_t* __restrict__ idx, const float* __restrict__ w,
                                                         const T* __restrict__ Klm, float* __restrict__ ds_out,
                                                         float* __restrict__ dQ, int64_t rows, int L, int N, int k,
                                                         float scale) {
-  constexpr int V8 = D / 8;  // threads per row
+  constexpr int V8 = D / 8;                    // threads per row
+  constexpr int LW = 2 * Elem<T>::bytes;       // 32-bit words of eight landmark elements
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gid / V8;
   const int c8 = (int)(gid % V8);
   if (row >= rows) return;
   const int k1 = k + 1;
   const int64_t bh = row / L;
-  int jr[17];
-  float wr[17], dr[17];
+  int jr[K1M];
+  float wr[K1M], dr[K1M];
+  uint4 raw[K1M];
 #pragma unroll
-  for (int r = 0; r < 17; ++r) {
-    if (r < k1) {
-      jr[r] = idx[row * k1 + r];
-      wr[r] = w[row * k1 + r];
-      dr[r] = Dpart[row * k1 + r];
-    }
+  for (int r = 0; r < K1M; ++r) {
+    const int64_t e = row * k1 + (r < k1 ? r : 0);
+    jr[r] = idx[e];
+    wr[r] = w[e];
+    dr[r] = Dpart[e];
+    raw[r] = *reinterpret_cast<const uint4*>(dq_part + e * D + 8 * c8);
   }
+  bool ok[K1M];
   float Dsum = 0.f;
 #pragma unroll
-  for (int r = 0; r < 17; ++r)
-    if (r < k1 && (r == k || (jr[r] >= 0 && jr[r] < N))) Dsum += wr[r] * dr[r];
+  for (int r = 0; r < K1M; ++r) {
+    ok[r] = r < k1 && (r == k || (jr[r] >= 0 && jr[r] < N));
+    if (ok[r]) Dsum += wr[r] * dr[r];
+  }
+  uint32_t lw[K1M][LW];
+#pragma unroll
+  for (int r = 0; r < K1M; ++r) {
+    const uint4* lp = reinterpret_cast<const uint4*>(Klm + (bh * N + (ok[r] ? jr[r] : 0)) * D + 8 * c8);
+#pragma unroll
+    for (int v = 0; v < LW / 4; ++v) {
+      const uint4 x = lp[v];
+      lw[r][4 * v] = x.x;
+      lw[r][4 * v + 1] = x.y;
+      lw[r][4 * v + 2] = x.z;
+      lw[r][4 * v + 3] = x.w;
+    }
+  }
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
-  for (int r = 0; r < 17; ++r) {
-    if (r >= k1 || (r < k && (jr[r] < 0 || jr[r] >= N))) continue;
+  for (int r = 0; r < K1M; ++r) {
+    if (!ok[r]) continue;
     const float ds = wr[r] * (dr[r] - Dsum);
     if (c8 == 0) ds_out[row * k1 + r] = ds;
-    const uint4 raw = *reinterpret_cast<const uint4*>(dq_part + (row * k1 + r) * D + 8 * c8);
     _Float16 h[8];
-    __builtin_memcpy(h, &raw, 16);
-    const int64_t lrow = (bh * N + jr[r]) * D + 8 * c8;
+    __builtin_memcpy(h, &raw[r], 16);
+    T lm[8];
+    __builtin_memcpy(lm, lw[r], 8 * sizeof(T));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += (float)h[e] + scale * ds * Elem<T>::to_f32(Klm, lrow + e);
+    for (int e = 0; e < 8; ++e) acc[e] += (float)h[e] + scale * ds * Elem<T>::to_f32(lm, e);
   }
   float4* out = reinterpret_cast<float4*>(dQ + row * D + 8 * c8);
   out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -406,8 +427,13 @@ static hipError_t bwd_t(const void* Q, const void* K, const void* V, const void*
   HILS_LAUNCH("chunk_bwd", (chunk_bwd_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)Q, (const T*)K,
               (const T*)V, (const T*)Klm, (const T*)dO, w, lse, ws.rb.chunk_off, ws.rb.pairs, ws.dq_part, ws.Dpart,
               ws.trash, ws.trash_f, dK, dV, L, N, k, scale);
-  HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D>), dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, st,
-              ws.dq_part, ws.Dpart, idx, w, (const T*)Klm, ws.ds, dQ, rows, L, N, k, scale);
+  const dim3 rgrid((unsigned)((rows * (D / 8) + 255) / 256));
+  if (k <= 8)
+    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 9>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx, w,
+                (const T*)Klm, ws.ds, dQ, rows, L, N, k, scale);
+  else
+    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 17>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx, w,
+                (const T*)Klm, ws.ds, dQ, rows, L, N, k, scale);
   HILS_LAUNCH("klm_bwd", (klm_bwd_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)Q, ws.ds, ws.rb.chunk_off,
               ws.rb.pairs, dKlm, L, N, k, scale);
   return hipGetLastError();
