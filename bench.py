@@ -48,9 +48,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: (kernel, FETCH_SIZE KiB, WRITE_SIZE KiB, source digest)
-    "prefill_8k": ("chunk_attn_fwd", 28608.2, 130573.1, "51110afdcee90ece"),
-    "prefill_128k": ("chunk_attn_fwd", 8510607.5, 17018037.8, "51110afdcee90ece"),
-    "train_8k": ("chunk_bwd", 245543.7, 911926.5, "05edf7bb371417ea"),
+    "prefill_8k": ("chunk_attn_fwd", 28616.5, 130577.4, "69c120a52a1d4059"),
+    "prefill_128k": ("chunk_attn_fwd", 8509166.8, 17017979.6, "69c120a52a1d4059"),
+    "train_8k": ("chunk_bwd", 243256.8, 909852.7, "6dc52f877fbd29d5"),
 }
 
 
