@@ -146,8 +146,8 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_kernel(const int32_t* _
   const int* co = chunk_off + (int64_t)bh * (N + 1);
   __shared__ int so_s[FUSED ? ROUTE_FUSED_MAX_N : 1], co_s[FUSED ? ROUTE_FUSED_MAX_N : 1];
   if constexpr (FUSED) {
-    static_assert(64 * NW == 256, "one thread per chunk");
-    __shared__ int buf[4];
+    static_assert(64 * NW >= ROUTE_FUSED_MAX_N, "one thread per chunk");
+    __shared__ int buf[NW];
     const int j = tid;
     int before = 0, tot = 0;
     {
@@ -162,9 +162,9 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_kernel(const int32_t* _
       }
     }
     int all, sum_i;
-    const int off = block_excl_scan(tot, buf, &all);
+    const int off = block_excl_scan<NW>(tot, buf, &all);
     const int nit = j < N ? (tot + ppi - 1) / ppi : 0;
-    const int ex_i = block_excl_scan(nit, buf, &sum_i);
+    const int ex_i = block_excl_scan<NW>(nit, buf, &sum_i);
     if (j < N) {
       so_s[j] = before;
       co_s[j] = off;
@@ -188,19 +188,36 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_kernel(const int32_t* _
   const int total = (tw1 - tw0) * k;
   const int32_t* idx_w = idx + ((int64_t)bh * L + tw0) * (k + 1);
   int* cur = cur_all + wv * N;
+  // short sequences: the wave's chunk ids (at most 256 queries x 16 slots per segment) are read
+  // once, for the histogram and the ranking
+  constexpr int UBF = FUSED ? 256 * 16 / (NW * 64) : 1;
+  int jr[UBF];
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int u = 0; u < UBF; ++u) {
+      const int f = u * 64 + lane;
+      jr[u] = f < total ? idx_w[(f / k) * (k + 1) + f % k] : -1;
+    }
+  }
   if constexpr (NW > 1) {
     for (int i = tid; i < NW * N; i += 64 * NW) cur_all[i] = 0;
     __syncthreads();
-    for (int f0 = 0; f0 < total; f0 += 8 * 64) {
-      int jj[8];
+    if constexpr (FUSED) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int f = f0 + u * 64 + lane;
-        jj[u] = f < total ? idx_w[(f / k) * (k + 1) + f % k] : -1;
+      for (int u = 0; u < UBF; ++u)
+        if (jr[u] >= 0 && jr[u] < N) atomicAdd(&cur[jr[u]], 1);
+    } else {
+      for (int f0 = 0; f0 < total; f0 += 8 * 64) {
+        int jj[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int f = f0 + u * 64 + lane;
+          jj[u] = f < total ? idx_w[(f / k) * (k + 1) + f % k] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (jj[u] >= 0 && jj[u] < N) atomicAdd(&cur[jj[u]], 1);
       }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (jj[u] >= 0 && jj[u] < N) atomicAdd(&cur[jj[u]], 1);
     }
     __syncthreads();
     for (int j = tid; j < N; j += 64 * NW) {
@@ -219,38 +236,46 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_kernel(const int32_t* _
   int* out = pairs + (int64_t)bh * L * k;
   int* pos_w = pos_of ? pos_of + ((int64_t)bh * L + tw0) * k : nullptr;
   const uint64_t below = (1ull << lane) - 1ull;
-  constexpr int U = 8;  // batches whose chunk ids are loaded together
-  for (int b0 = 0; b0 < total; b0 += U * 64) {
-    int jj[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int f = b0 + u * 64 + lane;
-      jj[u] = f < total ? idx_w[(f / k) * (k + 1) + f % k] : -1;
+  // one 64-pair batch: rank equal chunks by lane (ballots over the chunk bits), take the slots
+  auto place = [&](int f, int j) {
+    const bool act = j >= 0 && j < N;
+    uint64_t peers = __ballot(act);
+    if (peers == 0) {
+      if (pos_w && f < total) pos_w[f] = -1;
+      return;
     }
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = act && ((j >> b) & 1);
+      const uint64_t ones = __ballot(bit);
+      peers &= bit ? ones : ~ones;
+    }
+    int pos = 0;
+    if (act) pos = cur[j] + __popcll(peers & below);
+    // LDS instructions of one wavefront execute in order: every lane's read of cur[j]
+    // precedes the leader's update below
+    __builtin_amdgcn_wave_barrier();
+    if (act && (peers & below) == 0) cur[j] = pos + __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+    if (act) out[pos] = ((tw0 + f / k) << 5) | (f % k);
+    if (pos_w && f < total) pos_w[f] = act ? pos : -1;
+  };
+  if constexpr (FUSED) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int f = b0 + u * 64 + lane;
-      const int j = jj[u];
-      const bool act = j >= 0 && j < N;
-      uint64_t peers = __ballot(act);
-      if (peers == 0) {
-        if (pos_w && f < total) pos_w[f] = -1;
-        continue;
+    for (int u = 0; u < UBF; ++u) {
+      if (u * 64 >= total) break;
+      place(u * 64 + lane, jr[u]);
+    }
+  } else {
+    constexpr int U = 8;  // batches whose chunk ids are loaded together
+    for (int b0 = 0; b0 < total; b0 += U * 64) {
+      int jj[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int f = b0 + u * 64 + lane;
+        jj[u] = f < total ? idx_w[(f / k) * (k + 1) + f % k] : -1;
       }
-      for (int b = 0; b < nbits; ++b) {
-        const bool bit = act && ((j >> b) & 1);
-        const uint64_t ones = __ballot(bit);
-        peers &= bit ? ones : ~ones;
-      }
-      int pos = 0;
-      if (act) pos = cur[j] + __popcll(peers & below);
-      // LDS instructions of one wavefront execute in order: every lane's read of cur[j]
-      // precedes the leader's update below
-      __builtin_amdgcn_wave_barrier();
-      if (act && (peers & below) == 0) cur[j] = pos + __popcll(peers);
-      __builtin_amdgcn_wave_barrier();
-      if (act) out[pos] = ((tw0 + f / k) << 5) | (f % k);
-      if (pos_w && f < total) pos_w[f] = act ? pos : -1;
+#pragma unroll
+      for (int u = 0; u < U; ++u) place(b0 + u * 64 + lane, jj[u]);
     }
   }
 }
@@ -422,10 +447,17 @@ hipError_t launch_route(const int32_t* idx, const RouteBufs& rb, int BH, int L, 
               rb.seg_q);
   int nbits = 1;
   while ((1 << nbits) < N) ++nbits;
-  if (N <= ROUTE_FUSED_MAX_N && rb.nseg <= ROUTE_FUSED_MAX_SEG) {
-    HILS_LAUNCH("route_scatter", (route_scatter_kernel<4, true>), dim3(rb.nseg, BH), dim3(256), 4 * lds, st, idx,
-                rb.counts, rb.chunk_off, rb.items, rb.n_items, rb.pairs, rb.pos_of, L, N, k, rb.nseg, nbits, rb.seg_q,
-                rb.pairs_per_item, rb.max_items);
+  if (N <= ROUTE_FUSED_MAX_N && rb.nseg <= ROUTE_FUSED_MAX_SEG && rb.seg_q <= 256) {
+    // eight wavefronts per segment (shorter ranking chains) while the grid is one round of
+    // workgroups; four when there are many segments
+    if ((int64_t)rb.nseg * BH <= 512)
+      HILS_LAUNCH("route_scatter", (route_scatter_kernel<8, true>), dim3(rb.nseg, BH), dim3(512), 8 * lds, st, idx,
+                  rb.counts, rb.chunk_off, rb.items, rb.n_items, rb.pairs, rb.pos_of, L, N, k, rb.nseg, nbits,
+                  rb.seg_q, rb.pairs_per_item, rb.max_items);
+    else
+      HILS_LAUNCH("route_scatter", (route_scatter_kernel<4, true>), dim3(rb.nseg, BH), dim3(256), 4 * lds, st, idx,
+                  rb.counts, rb.chunk_off, rb.items, rb.n_items, rb.pairs, rb.pos_of, L, N, k, rb.nseg, nbits,
+                  rb.seg_q, rb.pairs_per_item, rb.max_items);
     return hipGetLastError();
   }
   HILS_LAUNCH("route_scan", route_scan_kernel, dim3(BH), dim3(256), 0, st, rb.counts, rb.chunk_off, rb.items, rb.n_items, N,
@@ -440,19 +472,14 @@ hipError_t launch_route(const int32_t* idx, const RouteBufs& rb, int BH, int L, 
       lds_set = true;
     }
     HILS_LAUNCH("route_scatter", route_scatter_staged_kernel<ROUTE_STAGED_NW>, dim3(rb.nseg, BH),
-                dim3(64 * ROUTE_STAGED_NW), route_staged_lds(N, rb.seg_q, k, ROUTE_STAGED_NW), st, idx, rb.counts, rb.chunk_off, rb.pairs, rb.pos_of, L, N, k,
-                rb.nseg, nbits, rb.seg_q);
+                dim3(64 * ROUTE_STAGED_NW), route_staged_lds(N, rb.seg_q, k, ROUTE_STAGED_NW), st, idx, rb.counts,
+                rb.chunk_off, rb.pairs, rb.pos_of, L, N, k, rb.nseg, nbits, rb.seg_q);
     return hipGetLastError();
   }
-  // four wavefronts per segment while their cursor tables fit in LDS
-  if (N <= 2048)
-    HILS_LAUNCH("route_scatter", (route_scatter_kernel<4, false>), dim3(rb.nseg, BH), dim3(256), 4 * lds, st, idx,
-                rb.counts, rb.chunk_off, rb.items, rb.n_items, rb.pairs, rb.pos_of, L, N, k, rb.nseg, nbits, rb.seg_q,
-                rb.pairs_per_item, rb.max_items);
-  else
-    HILS_LAUNCH("route_scatter", (route_scatter_kernel<1, false>), dim3(rb.nseg, BH), dim3(64), lds, st, idx,
-                rb.counts, rb.chunk_off, rb.items, rb.n_items, rb.pairs, rb.pos_of, L, N, k, rb.nseg, nbits, rb.seg_q,
-                rb.pairs_per_item, rb.max_items);
+  // longer sequences: one wavefront per segment
+  HILS_LAUNCH("route_scatter", (route_scatter_kernel<1, false>), dim3(rb.nseg, BH), dim3(64), lds, st, idx,
+              rb.counts, rb.chunk_off, rb.items, rb.n_items, rb.pairs, rb.pos_of, L, N, k, rb.nseg, nbits, rb.seg_q,
+              rb.pairs_per_item, rb.max_items);
   return hipGetLastError();
 }
 
