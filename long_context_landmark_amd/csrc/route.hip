@@ -19,6 +19,8 @@
 //            records where each pair went (the inverse map, written in query
 //            order), so per-pair results stored in list order can be gathered
 //            back per query.
+#include <atomic>
+
 #include "hils_device.h"
 #include "hils_launch.h"
 
@@ -463,13 +465,18 @@ hipError_t launch_route(const int32_t* idx, const RouteBufs& rb, int BH, int L, 
   HILS_LAUNCH("route_scan", route_scan_kernel, dim3(BH), dim3(256), 0, st, rb.counts, rb.chunk_off, rb.items, rb.n_items, N,
                      rb.nseg, rb.pairs_per_item, rb.max_items);
   if (N <= ROUTE_STAGED_MAX_N && rb.seg_q * k <= 16384) {
-    static bool lds_set = false;  // more than 64 KiB of dynamic LDS per workgroup is opted into once
-    if (!lds_set) {
-      const hipError_t e = hipFuncSetAttribute((const void*)route_scatter_staged_kernel<ROUTE_STAGED_NW>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)route_staged_lds(ROUTE_STAGED_MAX_N, 1024, 16, ROUTE_STAGED_NW));
+    // more than 64 KiB of dynamic LDS per workgroup is opted into once per device
+    static std::atomic<uint64_t> lds_set{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev < 64 ? (1ull << dev) : 0ull;
+    if (!bit || !(lds_set.load() & bit)) {
+      e = hipFuncSetAttribute((const void*)route_scatter_staged_kernel<ROUTE_STAGED_NW>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)route_staged_lds(ROUTE_STAGED_MAX_N, 1024, 16, ROUTE_STAGED_NW));
       if (e != hipSuccess) return e;
-      lds_set = true;
+      lds_set.fetch_or(bit);
     }
     HILS_LAUNCH("route_scatter", route_scatter_staged_kernel<ROUTE_STAGED_NW>, dim3(rb.nseg, BH),
                 dim3(64 * ROUTE_STAGED_NW), route_staged_lds(N, rb.seg_q, k, ROUTE_STAGED_NW), st, idx, rb.counts,
