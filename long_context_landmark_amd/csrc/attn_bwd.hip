@@ -34,16 +34,21 @@
 
 namespace hils {
 
+// 16-bit inputs (TR): the tile's Q, dO, w P and dA are staged row-major by tile query (16- and
+// 8-byte stores) and the dV, dK operands are read through transposing LDS loads; fp32 inputs
+// stage them transposed, element by element.
 template <typename T, int D> struct BwdLds {
+  static constexpr bool TR = Elem<T>::bytes == 2;
   static constexpr int KS = D + (Elem<T>::bytes == 2 ? 8 : 4);   // rows indexed by key, d inside
   static constexpr int TS = 64 + (Elem<T>::bytes == 2 ? 8 : 4);  // rows of 64 (keys or tile queries)
+  static constexpr int QS = D + 8;                               // TR: rows of D (tile query, d)
   T k[64 * KS];
   T v[64 * KS];
-  T kt[D * TS];   // K^T   [d][key]
-  T qt[D * TS];   // Q^T   [d][tile query]
-  T gt[D * TS];   // dO^T  [d][tile query]
-  T pt[64 * TS];  // (w P)^T [key][tile query]
-  T dat[64 * TS]; // dA^T  [key][tile query]
+  T kt[D * TS];               // K^T   [d][key]
+  T qt[TR ? 64 * QS : D * TS];  // TR: Q  [tile query][d];   fp32: Q^T  [d][tile query]
+  T gt[TR ? 64 * QS : D * TS];  // TR: dO [tile query][d];   fp32: dO^T [d][tile query]
+  T pt[64 * TS];              // TR: w P [tile query][key]; fp32: (w P)^T [key][tile query]
+  T dat[64 * TS];             // TR: dA  [tile query][key]; fp32: dA^T  [key][tile query]
 };
 
 // The chunk's K and V rows as A fragments of S^T = K Q^T and dP^T = V dO^T: held in registers
@@ -231,34 +236,63 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
         *reinterpret_cast<u16x4_t*>(dst + 16 * db + 4 * g) = h4;
       }
     }
-    __syncthreads();  // previous tile's readers of the transposed buffers are done
+    __syncthreads();  // previous tile's readers of the staged buffers are done
+    if constexpr (S::TR) {
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        Elem<T>::store(s.qt, (ks * 32 + 8 * g + e) * S::TS + qi, in.qf[ks].get(e));
-        Elem<T>::store(s.gt, (ks * 32 + 8 * g + e) * S::TS + qi, in.gf[ks].get(e));
+      for (int ks = 0; ks < D / 32; ++ks) {
+        *reinterpret_cast<bf16x8_t*>(&s.qt[qi * S::QS + ks * 32 + 8 * g]) = in.qf[ks].v;
+        *reinterpret_cast<bf16x8_t*>(&s.gt[qi * S::QS + ks * 32 + 8 * g]) = in.gf[ks].v;
       }
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+      for (int cb = 0; cb < 4; ++cb) {
+        u16x4_t pw, da;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = 16 * cb + 4 * g + i;
-        Elem<T>::store(s.pt, key * S::TS + qi, w_q * sc[cb][i]);
-        Elem<T>::store(s.dat, key * S::TS + qi, dp[cb][i]);
+        for (int i = 0; i < 4; ++i) {
+          pw[i] = f32_to_bf16(w_q * sc[cb][i]);
+          da[i] = f32_to_bf16(dp[cb][i]);
+        }
+        *reinterpret_cast<u16x4_t*>(&s.pt[qi * S::TS + 16 * cb + 4 * g]) = pw;
+        *reinterpret_cast<u16x4_t*>(&s.dat[qi * S::TS + 16 * cb + 4 * g]) = da;
       }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          Elem<T>::store(s.qt, (ks * 32 + 8 * g + e) * S::TS + qi, in.qf[ks].get(e));
+          Elem<T>::store(s.gt, (ks * 32 + 8 * g + e) * S::TS + qi, in.gf[ks].get(e));
+        }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 16 * cb + 4 * g + i;
+          Elem<T>::store(s.pt, key * S::TS + qi, w_q * sc[cb][i]);
+          Elem<T>::store(s.dat, key * S::TS + qi, dp[cb][i]);
+        }
+    }
     __syncthreads();
     // this wave's 16 keys: dV += (wP)^T dO, dK += dA^T Q (contraction over the 64 tile queries)
 #pragma unroll
     for (int kq = 0; kq < 2; ++kq) {
       Frag<T> ap, ad;
-      ap.load(&s.pt[(16 * wv + r16) * S::TS + kq * 32 + 8 * g]);
-      ad.load(&s.dat[(16 * wv + r16) * S::TS + kq * 32 + 8 * g]);
+      if constexpr (S::TR) {
+        ap.load_tr(s.pt, S::TS, kq * 32 + 8 * g, 16 * wv, lane);
+        ad.load_tr(s.dat, S::TS, kq * 32 + 8 * g, 16 * wv, lane);
+      } else {
+        ap.load(&s.pt[(16 * wv + r16) * S::TS + kq * 32 + 8 * g]);
+        ad.load(&s.dat[(16 * wv + r16) * S::TS + kq * 32 + 8 * g]);
+      }
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
         Frag<T> bg, bq;
-        bg.load(&s.gt[(16 * db + r16) * S::TS + kq * 32 + 8 * g]);
-        bq.load(&s.qt[(16 * db + r16) * S::TS + kq * 32 + 8 * g]);
+        if constexpr (S::TR) {
+          bg.load_tr(s.gt, S::QS, kq * 32 + 8 * g, 16 * db, lane);
+          bq.load_tr(s.qt, S::QS, kq * 32 + 8 * g, 16 * db, lane);
+        } else {
+          bg.load(&s.gt[(16 * db + r16) * S::TS + kq * 32 + 8 * g]);
+          bq.load(&s.qt[(16 * db + r16) * S::TS + kq * 32 + 8 * g]);
+        }
         mma(accV[db], ap, bg);
         mma(accK[db], ad, bq);
       }

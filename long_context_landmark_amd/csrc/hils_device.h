@@ -70,6 +70,23 @@ template <> struct Frag<bf16_t> {
     u16x8_t c = __builtin_bit_cast(u16x8_t, v);
     return bf16_to_f32(c[e]);
   }
+  // Fragment of the transpose of a row-major LDS matrix X (row stride `stride` elements, a
+  // multiple of 4; c0 a multiple of 4): lane l receives X[r0 + e][c0 + l % 16] for e = 0..7, where
+  // r0 differs per group of 16 lanes.  Uses the transposing LDS read: in each 16-lane group, lane
+  // i receives element i % 4 of the 8-byte pieces addressed by lanes 4e + i / 4 (e = 0..3) of the
+  // group, so lane s addresses row r0 + s / 4, columns c0 + 4 (s % 4) .. + 3 (checked on the device
+  // with an in-bounds probe).
+  __device__ __forceinline__ void load_tr(const bf16_t* X, int stride, int r0, int c0, int lane) {
+    typedef short i16x4_t __attribute__((ext_vector_type(4)));
+    const int s = lane & 15;
+    const bf16_t* p = X + (r0 + (s >> 2)) * stride + c0 + 4 * (s & 3);
+    const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
+    const i16x4_t b =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p + 4 * stride));
+    const u16x8_t c = {(uint16_t)a[0], (uint16_t)a[1], (uint16_t)a[2], (uint16_t)a[3],
+                       (uint16_t)b[0], (uint16_t)b[1], (uint16_t)b[2], (uint16_t)b[3]};
+    v = __builtin_bit_cast(bf16x8_t, c);
+  }
 };
 template <> struct Frag<float> {
   float v[8];
