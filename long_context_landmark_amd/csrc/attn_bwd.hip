@@ -37,7 +37,7 @@ namespace hils {
 // 16-bit inputs (TR): the tile's Q, dO, w P and dA are staged row-major by tile query (16- and
 // 8-byte stores) and the dV, dK operands are read through transposing LDS loads; fp32 inputs
 // stage them transposed, element by element.
-template <typename T, int D> struct BwdLds {
+template <typename T, int D> struct alignas(16) BwdLds {
   static constexpr bool TR = Elem<T>::bytes == 2;
   static constexpr int KS = D + (Elem<T>::bytes == 2 ? 8 : 4);   // rows indexed by key, d inside
   static constexpr int TS = 64 + (Elem<T>::bytes == 2 ? 8 : 4);  // rows of 64 (keys or tile queries)

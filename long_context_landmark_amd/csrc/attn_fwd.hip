@@ -28,7 +28,7 @@
 
 namespace hils {
 
-template <typename T, int D> struct ChunkLds {
+template <typename T, int D> struct alignas(16) ChunkLds {
   static constexpr int KS = D + (Elem<T>::bytes == 2 ? 8 : 4);  // row stride of K  [key][d]
   static constexpr int VS = 64 + (Elem<T>::bytes == 2 ? 4 : 4);  // row stride of V^T [d][key]
   T k[64 * KS];
