@@ -150,8 +150,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
   // the group maxima (sweep 1), the survivors (sweep 2) and the sorted top keys share storage
   __shared__ union {
     float gmax[64][65];
-    uint64_t surv[64][TK_CAP];
-    uint64_t top[64][16];
+    uint64_t surv[64][TK_CAP + 1];  // rows padded by one key: the lanes of a wave read different
+    uint64_t top[64][17];           // queries' rows, which would otherwise share LDS banks
   } u_s;
   auto& gmax_s = u_s.gmax;
   auto& surv = u_s.surv;
