@@ -459,43 +459,42 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
   }
   __syncthreads();
 
-  // fusion weights and outputs: the softmax statistics per query, then the 64 query rows of
-  // each output, which are consecutive in memory, written element by element across the
-  // workgroup (coalesced)
-  __shared__ float mx_s[64], inv_s[64];
-  if (tid < 64) {
-    const int q = tid;
+  // fusion weights and outputs: four lanes per query (slots part, part + 4, ...; the own chunk
+  // in the first), the softmax statistics reduced over the four
+  {
+    const int q = tid >> 2, part = tid & 3;
     const float s_own = own_s[q];
     float mx = s_own;
-    for (int r = 0; r < m; ++r) mx = fmaxf(mx, key_score(top_s[q][r]));
-    float den = __expf(s_own - mx);
-    for (int r = 0; r < m; ++r) den += __expf(key_score(top_s[q][r]) - mx);
-    mx_s[q] = mx;
-    inv_s[q] = 1.f / den;
-  }
-  __syncthreads();
-  const int64_t base = ((int64_t)bh * L + (int64_t)c * 64) * k1;
-  for (int e = tid; e < 64 * k1; e += 256) {
-    const int q = e / k1, r = e % k1;
-    int ix;
-    float sv, wv;
-    if (r == k) {
-      ix = c;
-      sv = own_s[q];
-      wv = __expf(sv - mx_s[q]) * inv_s[q];
-    } else if (r < m) {
-      const uint64_t key = top_s[q][r];
-      ix = key_index(key);
-      sv = key_score(key);
-      wv = __expf(sv - mx_s[q]) * inv_s[q];
-    } else {
-      ix = -1;
-      sv = -INFINITY;
-      wv = 0.f;
+    for (int r = part; r < m; r += 4) mx = fmaxf(mx, key_score(top_s[q][r]));
+    mx = fmaxf(mx, lane_xor(mx, 1));
+    mx = fmaxf(mx, lane_xor(mx, 2));
+    float den = part == 0 ? __expf(s_own - mx) : 0.f;
+    for (int r = part; r < m; r += 4) den += __expf(key_score(top_s[q][r]) - mx);
+    den += lane_xor(den, 1);
+    den += lane_xor(den, 2);
+    const float inv = 1.f / den;
+    const int64_t base = ((int64_t)bh * L + (int64_t)c * 64 + q) * k1;
+    for (int r = part; r <= k; r += 4) {
+      int ix;
+      float sv, wv;
+      if (r == k) {
+        ix = c;
+        sv = s_own;
+        wv = __expf(sv - mx) * inv;
+      } else if (r < m) {
+        const uint64_t key = top_s[q][r];
+        ix = key_index(key);
+        sv = key_score(key);
+        wv = __expf(sv - mx) * inv;
+      } else {
+        ix = -1;
+        sv = -INFINITY;
+        wv = 0.f;
+      }
+      idx[base + r] = ix;
+      sel[base + r] = sv;
+      if (wout) wout[base + r] = wv;
     }
-    idx[base + e] = ix;
-    sel[base + e] = sv;
-    if (wout) wout[base + e] = wv;
   }
 }
 
