@@ -48,9 +48,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: (kernel, FETCH_SIZE KiB, WRITE_SIZE KiB, source digest)
-    "prefill_8k": ("chunk_attn_fwd", 28616.5, 130577.4, "69c120a52a1d4059"),
-    "prefill_128k": ("chunk_attn_fwd", 8509166.8, 17017979.6, "69c120a52a1d4059"),
-    "train_8k": ("chunk_bwd", 243256.8, 909852.7, "6dc52f877fbd29d5"),
+    "prefill_8k": ("chunk_attn_fwd", 28621.9, 130576.2, "79664decdcc7b0e9"),
+    "prefill_128k": ("chunk_attn_fwd", 8509302.0, 17021942.0, "79664decdcc7b0e9"),
+    "train_8k": ("chunk_bwd", 237992.0, 902533.8, "2a8888f1bc2af317"),
 }
 
 
