@@ -7,8 +7,13 @@ check -- the HIP library and the CPU oracle -- receive the same bytes from here.
 Recipe (the stand-in for the pages' long-context workloads; the evaluation
 suites themselves are not available and are not reproduced):
   * ``numpy.random.default_rng(seed)``; draw order Q, K, V, landmark noise,
-    needle choices, decode per-step draws, dO.  Each draw is float32
-    ``standard_normal`` of the full shape in C order, then scaled.
+    needle choices, decode per-step draws, dO, retrieval-query noise.  Each
+    draw is float32 ``standard_normal`` of the full shape in C order, then
+    scaled.
+  * retrieval queries (optional, for the low-rank query calibration of the
+    "Method" section's input stage): Q_ret = 0.6 Q + 0.8 n, n a fresh
+    standard-normal draw of Q's shape, formed in float32 from Q before Q is
+    rounded, so Q_ret is correlated with Q but not equal to it.
   * bf16 tensors are rounded from float32 with round-to-nearest-even and are
     carried on the host as uint16 bit patterns.
   * ``klm="chunkmean"``: each landmark row is the mean of its chunk's keys
@@ -61,7 +66,7 @@ def _align(x: np.ndarray, u: np.ndarray, cos: float = 0.9) -> np.ndarray:
 
 
 def prefill_inputs(B, H, L, d, C=64, seed=0, dtype="bf16", qkv_std=1.0, klm="iid", klm_noise=0.1,
-                   needles=0, needle_window=256, with_dO=False):
+                   needles=0, needle_window=256, with_dO=False, with_qret=False):
     """Inputs of one prefill (or training) call.
 
     Returns a dict with Q, K, V [B,H,L,d], Klm [B,H,N,d] (uint16 bf16 bits or
@@ -107,10 +112,17 @@ def prefill_inputs(B, H, L, d, C=64, seed=0, dtype="bf16", qkv_std=1.0, klm="iid
     }
     if with_dO:
         out["dO"] = _finish(rng.standard_normal(shp, dtype=np.float32), dtype)
+    if with_qret:
+        out["Q_ret"] = _retrieval(rng, Q, dtype)
     return out
 
 
-def decode_inputs(B, H, d, ctx, steps, C=64, seed=0, dtype="bf16", needle=True):
+def _retrieval(rng, q, dtype):
+    n = rng.standard_normal(q.shape, dtype=np.float32)
+    return _finish(np.float32(0.6) * q.astype(np.float32) + np.float32(0.8) * n, dtype)
+
+
+def decode_inputs(B, H, d, ctx, steps, C=64, seed=0, dtype="bf16", needle=True, with_qret=False):
     """Inputs of a decode run: caches filled to ``ctx`` rows, then ``steps`` new tokens.
 
     Returns K_cache, V_cache [B,H,Lmax,d] (rows >= ctx zero until appended),
@@ -140,7 +152,7 @@ def decode_inputs(B, H, d, ctx, steps, C=64, seed=0, dtype="bf16", needle=True):
     v_new = rng.standard_normal((steps, B, H, d), dtype=np.float32)
     if needle:
         q = _align(q, u[None])
-    return {
+    out = {
         "K_cache": _finish(Kc, dtype),
         "V_cache": _finish(Vc, dtype),
         "Klm": _finish(Klm.astype(np.float32), dtype),
@@ -150,6 +162,9 @@ def decode_inputs(B, H, d, ctx, steps, C=64, seed=0, dtype="bf16", needle=True):
         "needle_chunk": nch,
         "ctx": ctx,
     }
+    if with_qret:
+        out["q_ret"] = _retrieval(rng, q, dtype)
+    return out
 
 
 @dataclass(frozen=True)
@@ -210,7 +225,7 @@ def _torch_gen(seed, device):
     return g
 
 
-def torch_prefill_inputs(w: Workload, device="cuda:0", seed=None, with_dO=None):
+def torch_prefill_inputs(w: Workload, device="cuda:0", seed=None, with_dO=None, with_qret=False):
     """Inputs of a prefill / training workload generated on the device (torch tensors)."""
     import torch
 
@@ -249,6 +264,8 @@ def torch_prefill_inputs(w: Workload, device="cuda:0", seed=None, with_dO=None):
     out = {"Q": Q.to(dt).contiguous(), "K": K.contiguous(), "V": V.contiguous(), "Klm": Klm.to(dt).contiguous()}
     if with_dO if with_dO is not None else w.gen.get("with_dO", False):
         out["dO"] = normal((B, H, L, d)).to(dt)
+    if with_qret:
+        out["Q_ret"] = (0.6 * Q + 0.8 * normal((B, H, L, d))).to(dt).contiguous()
     return out
 
 

@@ -16,6 +16,8 @@ Parity status of each function (what pins it is in ``tests/test_oracle_*.py``):
                    single-chunk reduction, equal-score mean, invariances)
   decode           pinned (single-chunk reduction; prefill-row consistency)
   bwd              pinned (central finite differences, closed-form sums)
+  retrieval query  pinned (Q_ret = Q reproduces the plain operator; selection depends on
+                   Q_ret only; finite differences of dQ_ret, dQ and dKlm)
 """
 from __future__ import annotations
 
@@ -58,14 +60,14 @@ def _load():
     lib.oracle_landmark_scores.restype = None
     lib.oracle_landmark_scores_rows.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, dbl, ip, vp, i64, ip]
     lib.oracle_landmark_scores_rows.restype = None
-    lib.oracle_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, ip, vp, i64, ip, vp,
+    lib.oracle_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, ip, vp, i64, ip, vp,
                                vp, vp, vp, vp, vp, ip]
     lib.oracle_fwd.restype = ip
-    lib.oracle_decode.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, dbl, ip,
-                                  vp, vp, vp, vp, vp, ip]
+    lib.oracle_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, dbl,
+                                  ip, vp, vp, vp, vp, vp, ip]
     lib.oracle_decode.restype = ip
-    lib.oracle_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, ip, vp, vp, vp,
-                               vp, ip]
+    lib.oracle_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, ip, vp, vp,
+                               vp, vp, vp, ip]
     lib.oracle_bwd.restype = ip
     _lib = lib
     return lib
@@ -115,16 +117,20 @@ def landmark_scores_rows(Q, Klm, C, rows, scale=None, nthreads=0):
     return S
 
 
-def fwd(Q, K, V, Klm, C, k, scale=None, rows=None, idx=None, override_scores=None, nthreads=0):
+def fwd(Q, K, V, Klm, C, k, scale=None, rows=None, idx=None, override_scores=None, nthreads=0, Q_ret=None):
     """Forward of every row (or of the flattened rows listed in ``rows``).
 
     Returns a dict with idx [.., k+1] int32, sel / w / lse [.., k+1] float64,
     O [.., d] float64 and ``threads`` (threads used).  With ``rows`` the leading
     shape is [len(rows)].  ``idx`` (same shape as the output idx) fixes the
     selection; ``override_scores`` [B,H,L,N] float64 replaces the landmark
-    scores for selection and fusion.
+    scores for selection and fusion.  ``Q_ret`` (same shape and type as Q):
+    retrieval queries used for the landmark scores instead of Q.
     """
     Q, K, V, Klm = _c(Q), _c(K), _c(V), _c(Klm)
+    Qr = _c(Q_ret) if Q_ret is not None else None
+    if Qr is not None and (Qr.shape != Q.shape or Qr.dtype != Q.dtype):
+        raise ValueError("Q_ret must match Q in shape and type")
     B, H, L, d = Q.shape
     N = Klm.shape[2]
     if N != (L + C - 1) // C:
@@ -143,20 +149,23 @@ def fwd(Q, K, V, Klm, C, k, scale=None, rows=None, idx=None, override_scores=Non
     lse = np.empty(lead + (k1,), np.float64)
     O = np.empty(lead + (d,), np.float64)
     ov = _c(np.asarray(override_scores, np.float64)) if override_scores is not None else None
-    used = _load().oracle_fwd(_p(Q), _p(K), _p(V), _p(Klm), B, H, L, d, C, k, scale, _dt(Q, K, V, Klm),
+    used = _load().oracle_fwd(_p(Q), _p(Qr), _p(K), _p(V), _p(Klm), B, H, L, d, C, k, scale, _dt(Q, K, V, Klm),
                               _p(rows), 0 if rows is None else rows.shape[0], int(use_idx), _p(ov),
                               _p(idx_out), _p(sel), _p(w), _p(lse), _p(O), nthreads)
     return {"idx": idx_out, "sel": sel, "w": w, "lse": lse, "O": O, "threads": used}
 
 
-def decode(q, k_new, v_new, Kc, Vc, Klm, n, C, k, scale=None, nthreads=0):
+def decode(q, k_new, v_new, Kc, Vc, Klm, n, C, k, scale=None, nthreads=0, q_ret=None):
     """One decode step at position n for every (b,h).
 
     Writes k_new / v_new into row n of ``Kc`` / ``Vc`` in place (these are the
     caller's host arrays, [B,H,Lmax,d]) and returns idx / sel / w / lse [B,H,k+1]
-    and o [B,H,d].
+    and o [B,H,d].  ``q_ret`` (like q): retrieval queries for the landmark scores.
     """
     q, k_new, v_new, Klm = _c(q), _c(k_new), _c(v_new), _c(Klm)
+    qr = _c(q_ret) if q_ret is not None else None
+    if qr is not None and (qr.shape != q.shape or qr.dtype != q.dtype):
+        raise ValueError("q_ret must match q in shape and type")
     if not (Kc.flags.c_contiguous and Vc.flags.c_contiguous):
         raise ValueError("caches must be C-contiguous (they are updated in place)")
     B, H, d = q.shape
@@ -171,15 +180,22 @@ def decode(q, k_new, v_new, Kc, Vc, Klm, n, C, k, scale=None, nthreads=0):
     w = np.empty((B, H, k1), np.float64)
     lse = np.empty((B, H, k1), np.float64)
     o = np.empty((B, H, d), np.float64)
-    used = _load().oracle_decode(_p(q), _p(k_new), _p(v_new), _p(Kc), _p(Vc), _p(Klm), n, Lmax, Nmax, B, H,
+    used = _load().oracle_decode(_p(q), _p(qr), _p(k_new), _p(v_new), _p(Kc), _p(Vc), _p(Klm), n, Lmax, Nmax, B, H,
                                  d, C, k, scale, _dt(q, k_new, v_new, Kc, Vc, Klm), _p(idx), _p(sel), _p(w),
                                  _p(lse), _p(o), nthreads)
     return {"idx": idx, "sel": sel, "w": w, "lse": lse, "o": o, "threads": used}
 
 
-def bwd(Q, K, V, Klm, dO, idx, C, k, scale=None, nthreads=0):
-    """Gradients dQ, dK, dV [B,H,L,d] and dKlm [B,H,N,d] (float64), selection fixed by idx."""
+def bwd(Q, K, V, Klm, dO, idx, C, k, scale=None, nthreads=0, Q_ret=None):
+    """Gradients dQ, dK, dV [B,H,L,d] and dKlm [B,H,N,d] (float64), selection fixed by idx.
+
+    With ``Q_ret`` (retrieval queries for the landmark scores) the score gradients go to a
+    separate ``dQ_ret`` [B,H,L,d] and dQ holds the in-chunk attention terms only.
+    """
     Q, K, V, Klm, dO = _c(Q), _c(K), _c(V), _c(Klm), _c(dO)
+    Qr = _c(Q_ret) if Q_ret is not None else None
+    if Qr is not None and (Qr.shape != Q.shape or Qr.dtype != Q.dtype):
+        raise ValueError("Q_ret must match Q in shape and type")
     B, H, L, d = Q.shape
     N = Klm.shape[2]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
@@ -190,6 +206,10 @@ def bwd(Q, K, V, Klm, dO, idx, C, k, scale=None, nthreads=0):
     dK = np.empty((B, H, L, d), np.float64)
     dV = np.empty((B, H, L, d), np.float64)
     dKlm = np.empty((B, H, N, d), np.float64)
-    used = _load().oracle_bwd(_p(Q), _p(K), _p(V), _p(Klm), _p(dO), _p(idx), B, H, L, d, C, k, scale,
-                              _dt(Q, K, V, Klm, dO), _p(dQ), _p(dK), _p(dV), _p(dKlm), nthreads)
-    return {"dQ": dQ, "dK": dK, "dV": dV, "dKlm": dKlm, "threads": used}
+    dQr = np.empty((B, H, L, d), np.float64) if Qr is not None else None
+    used = _load().oracle_bwd(_p(Q), _p(Qr), _p(K), _p(V), _p(Klm), _p(dO), _p(idx), B, H, L, d, C, k, scale,
+                              _dt(Q, K, V, Klm, dO), _p(dQ), _p(dQr), _p(dK), _p(dV), _p(dKlm), nthreads)
+    out = {"dQ": dQ, "dK": dK, "dV": dV, "dKlm": dKlm, "threads": used}
+    if Qr is not None:
+        out["dQ_ret"] = dQr
+    return out

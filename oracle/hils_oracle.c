@@ -18,6 +18,12 @@
  *   [HiLS-p2] paper.oopus.info review, section 2 "Core method" (landmark per
  *             chunk, score, in-chunk attention, weighted fusion) and section 3
  *             (head dim 64, chunk size 64).
+ *   [HiLS-p1] "Method" > "Input & chunking" also names a low-rank query
+ *             calibration: a learned affine map of Q that serves retrieval.
+ *             Read as an optional retrieval query Qr (same layout as Q, made
+ *             outside the operator) that replaces Q in the landmark scores,
+ *             and so in the selection and the fusion weights, while the
+ *             per-chunk attention keeps Q.  Without Qr the scores use Q.
  * Points the pages leave open are fixed as follows (one landmark key per
  * chunk; scale 1/sqrt(d) on both softmax levels; top-k ties go to the lower
  * chunk index; the query's own chunk is always in the set, is not counted in
@@ -67,6 +73,7 @@ static double dot_row(const void* A, int64_t ra, const void* Bm, int64_t rb, int
 
 typedef struct {
   const void *Q, *K, *V, *Klm;
+  const void* Qr;  /* retrieval queries for the landmark scores (NULL: the attention queries) */
   int64_t B, H, L, d, C, k, N;
   int64_t Lkv;  /* rows per (b,h) in K/V (L for prefill, Lmax for a decode cache) */
   int64_t Nlm;  /* rows per (b,h) in Klm */
@@ -88,7 +95,8 @@ static int cand_cmp(const void* a, const void* b) {
 /* chunk score of query row t against landmark j (HiLS-p2 section 2, step 1):
  * scale * <q_t, Klm_j>, computed in double and rounded to fp32 */
 static float chunk_score(const prob_t* P, const void* q, int64_t qrow, int64_t bh, int64_t j) {
-  return (float)(P->scale * dot_row(q, qrow, P->Klm, bh * P->Nlm + j, P->d, P->dt));
+  const void* qs = P->Qr ? P->Qr : q;
+  return (float)(P->scale * dot_row(qs, qrow, P->Klm, bh * P->Nlm + j, P->d, P->dt));
 }
 
 /*
@@ -194,7 +202,7 @@ static int set_threads(int nthreads) {
 /* Landmark scores S[b,h,t,j] = fp32(scale <q_t, Klm_j>) for j <= t/C, -inf otherwise. */
 void oracle_landmark_scores(const void* Q, const void* Klm, double* S, int64_t B, int64_t H,
                             int64_t L, int64_t d, int64_t C, double scale, int dt, int nthreads) {
-  prob_t P = {Q, NULL, NULL, Klm, B, H, L, d, C, 0, (L + C - 1) / C, L, (L + C - 1) / C, scale, dt};
+  prob_t P = {Q, NULL, NULL, Klm, NULL, B, H, L, d, C, 0, (L + C - 1) / C, L, (L + C - 1) / C, scale, dt};
   set_threads(nthreads);
 #pragma omp parallel for schedule(dynamic, 64)
   for (int64_t row = 0; row < B * H * L; ++row) {
@@ -208,7 +216,7 @@ void oracle_landmark_scores(const void* Q, const void* Klm, double* S, int64_t B
 void oracle_landmark_scores_rows(const void* Q, const void* Klm, double* S, int64_t B, int64_t H, int64_t L,
                                  int64_t d, int64_t C, double scale, int dt, const int64_t* rows, int64_t nrows,
                                  int nthreads) {
-  prob_t P = {Q, NULL, NULL, Klm, B, H, L, d, C, 0, (L + C - 1) / C, L, (L + C - 1) / C, scale, dt};
+  prob_t P = {Q, NULL, NULL, Klm, NULL, B, H, L, d, C, 0, (L + C - 1) / C, L, (L + C - 1) / C, scale, dt};
   set_threads(nthreads);
 #pragma omp parallel for schedule(dynamic, 16)
   for (int64_t r = 0; r < nrows; ++r) {
@@ -226,12 +234,12 @@ void oracle_landmark_scores_rows(const void* Q, const void* Klm, double* S, int6
  * landmark scores for both selection and fusion (a test hook).
  * Returns the number of threads used.
  */
-int oracle_fwd(const void* Q, const void* K, const void* V, const void* Klm,
+int oracle_fwd(const void* Q, const void* Qr, const void* K, const void* V, const void* Klm,
                int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t k, double scale,
                int dt, const int64_t* rows, int64_t nrows, int use_idx, const double* override_s,
                int32_t* idx, double* sel, double* w, double* lse, double* O, int nthreads) {
   int64_t N = (L + C - 1) / C;
-  prob_t P = {Q, K, V, Klm, B, H, L, d, C, k, N, L, N, scale, dt};
+  prob_t P = {Q, K, V, Klm, Qr, B, H, L, d, C, k, N, L, N, scale, dt};
   int used = set_threads(nthreads);
   int64_t total = rows ? nrows : B * H * L;
   int64_t k1 = k + 1;
@@ -252,7 +260,7 @@ int oracle_fwd(const void* Q, const void* K, const void* V, const void* Klm,
  * open chunk n/C is read as the caller supplied it.
  * Caches are [B,H,Lmax,d]; Klm is [B,H,Nmax,d].
  */
-int oracle_decode(const void* q, const void* k_new, const void* v_new, void* Kc, void* Vc,
+int oracle_decode(const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc, void* Vc,
                   const void* Klm, int64_t n, int64_t Lmax, int64_t Nmax, int64_t B, int64_t H,
                   int64_t d, int64_t C, int64_t k, double scale, int dt, int32_t* idx,
                   double* sel, double* w, double* lse, double* o, int nthreads) {
@@ -261,7 +269,7 @@ int oracle_decode(const void* q, const void* k_new, const void* v_new, void* Kc,
     memcpy((char*)Kc + ((bh * Lmax + n) * d) * esz, (const char*)k_new + bh * d * esz, (size_t)(d * esz));
     memcpy((char*)Vc + ((bh * Lmax + n) * d) * esz, (const char*)v_new + bh * d * esz, (size_t)(d * esz));
   }
-  prob_t P = {q, Kc, Vc, Klm, B, H, n + 1, d, C, k, Nmax, Lmax, Nmax, scale, dt};
+  prob_t P = {q, Kc, Vc, Klm, qr, B, H, n + 1, d, C, k, Nmax, Lmax, Nmax, scale, dt};
   int used = set_threads(nthreads);
   int64_t k1 = k + 1;
 #pragma omp parallel for schedule(static)
@@ -283,19 +291,24 @@ int oracle_decode(const void* q, const void* k_new, const void* v_new, void* Kc,
  * in-chunk softmax and both dot-product scores; the hard selection carries no
  * gradient).  dQ, dK, dV are [B,H,L,d]; dKlm is [B,H,N,d].  Work is split
  * across (b,h) only, so every accumulation is sequential in row order.
+ * With retrieval queries Qr the scores are scale <qr_t, Klm_j>: the ds terms
+ * then give dQr_t = scale sum_j ds_j Klm_j (written to dQr, [B,H,L,d]) and
+ * dKlm_j += scale ds_j qr_t, and dQ keeps the in-chunk terms only.
  */
-int oracle_bwd(const void* Q, const void* K, const void* V, const void* Klm, const void* dO,
+int oracle_bwd(const void* Q, const void* Qr, const void* K, const void* V, const void* Klm, const void* dO,
                const int32_t* idx_in, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
-               int64_t k, double scale, int dt, double* dQ, double* dK, double* dV, double* dKlm,
+               int64_t k, double scale, int dt, double* dQ, double* dQr, double* dK, double* dV, double* dKlm,
                int nthreads) {
   int64_t N = (L + C - 1) / C;
-  prob_t P = {Q, K, V, Klm, B, H, L, d, C, k, N, L, N, scale, dt};
+  prob_t P = {Q, K, V, Klm, Qr, B, H, L, d, C, k, N, L, N, scale, dt};
   int used = set_threads(nthreads);
   int64_t k1 = k + 1;
   memset(dQ, 0, sizeof(double) * (size_t)(B * H * L * d));
   memset(dK, 0, sizeof(double) * (size_t)(B * H * L * d));
   memset(dV, 0, sizeof(double) * (size_t)(B * H * L * d));
   memset(dKlm, 0, sizeof(double) * (size_t)(B * H * N * d));
+  if (dQr) memset(dQr, 0, sizeof(double) * (size_t)(B * H * L * d));
+  double* dS = dQr ? dQr : dQ;  /* where the score gradients go */
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t bh = 0; bh < B * H; ++bh) {
     int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)k1);
@@ -308,11 +321,16 @@ int oracle_bwd(const void* Q, const void* K, const void* V, const void* Klm, con
     double* abuf = (double*)malloc(sizeof(double) * (size_t)C);
     double* g = (double*)malloc(sizeof(double) * (size_t)d);
     double* qv = (double*)malloc(sizeof(double) * (size_t)d);
+    double* qrv = (double*)malloc(sizeof(double) * (size_t)d);
     for (int64_t t = 0; t < L; ++t) {
       int64_t row = bh * L + t;
       memcpy(idx, idx_in + row * k1, sizeof(int32_t) * (size_t)k1);
       row_forward(&P, Q, row, bh, t, 1, NULL, idx, sel, w, lse, o);
-      for (int64_t e = 0; e < d; ++e) { g[e] = elem(dO, row * d + e, dt); qv[e] = elem(Q, row * d + e, dt); }
+      for (int64_t e = 0; e < d; ++e) {
+        g[e] = elem(dO, row * d + e, dt);
+        qv[e] = elem(Q, row * d + e, dt);
+        qrv[e] = elem(Qr ? Qr : Q, row * d + e, dt);
+      }
       /* per-chunk outputs o_j and D_j = g.o_j */
       double D = 0.0;
       for (int64_t r = 0; r < k1; ++r) {
@@ -327,8 +345,8 @@ int oracle_bwd(const void* Q, const void* K, const void* V, const void* Klm, con
         int64_t j = idx[r];
         double ds = w[r] * (Dj[r] - D);
         for (int64_t e = 0; e < d; ++e) {
-          dQ[row * d + e] += scale * ds * elem(Klm, (bh * N + j) * d + e, dt);
-          dKlm[(bh * N + j) * d + e] += scale * ds * qv[e];
+          dS[row * d + e] += scale * ds * elem(Klm, (bh * N + j) * d + e, dt);
+          dKlm[(bh * N + j) * d + e] += scale * ds * qrv[e];
         }
         int64_t lo = j * C;
         int64_t hi = (j == t / C) ? t : lo + C - 1;
@@ -346,7 +364,7 @@ int oracle_bwd(const void* Q, const void* K, const void* V, const void* Klm, con
         }
       }
     }
-    free(idx); free(sel); free(w); free(lse); free(o); free(oj); free(Dj); free(abuf); free(g); free(qv);
+    free(idx); free(sel); free(w); free(lse); free(o); free(oj); free(Dj); free(abuf); free(g); free(qv); free(qrv);
   }
   return used;
 }

@@ -279,26 +279,31 @@ def test_row_subset_matches_full(oracle_mod):
 # --------------------------------------------------------------------------- decode
 
 
-def test_decode_matches_prefill_rows(oracle_mod):
+@pytest.mark.parametrize("qret", [False, True])
+def test_decode_matches_prefill_rows(oracle_mod, qret):
     B, H, d, C, k = 1, 2, 16, 64, 3
     ctx, steps = 256, 80
-    x = synth.decode_inputs(B, H, d, ctx, steps, C=C, seed=15, dtype="bf16")
+    x = synth.decode_inputs(B, H, d, ctx, steps, C=C, seed=15, dtype="bf16", with_qret=qret)
     Kc, Vc = x["K_cache"].copy(), x["V_cache"].copy()
     outs = []
     for s in range(steps):
-        outs.append(oracle_mod.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc, Vc, x["Klm"], ctx + s, C, k))
+        outs.append(oracle_mod.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc, Vc, x["Klm"], ctx + s, C, k,
+                                      q_ret=x["q_ret"][s] if qret else None))
     L = ctx + steps
     L_pad = ((L + C - 1) // C) * C
     Q = np.zeros((B, H, L_pad, d), np.uint16)
+    Qr = np.zeros_like(Q)
     for s in range(steps):
         Q[:, :, ctx + s] = x["q"][s]
+        if qret:
+            Qr[:, :, ctx + s] = x["q_ret"][s]
     K = np.zeros_like(Q)
     V = np.zeros_like(Q)
     K[:, :, :L] = Kc[:, :, :L]
     V[:, :, :L] = Vc[:, :, :L]
     Klm = x["Klm"][:, :, :L_pad // C]
     rows = np.array([bh * L_pad + ctx + s for s in range(steps) for bh in range(B * H)])
-    ref = oracle_mod.fwd(Q, K, V, Klm, C, k, rows=rows)
+    ref = oracle_mod.fwd(Q, K, V, Klm, C, k, rows=rows, Q_ret=Qr if qret else None)
     for i, (s, bh) in enumerate((s, bh) for s in range(steps) for bh in range(B * H)):
         np.testing.assert_array_equal(outs[s]["idx"].reshape(-1, k + 1)[bh], ref["idx"][i])
         np.testing.assert_array_equal(outs[s]["o"].reshape(-1, d)[bh], ref["O"][i])
@@ -381,3 +386,91 @@ def test_bwd_single_chunk_matches_autograd_dense(oracle_mod):
     np.testing.assert_allclose(g["dK"], k.grad.numpy(), atol=1e-11)
     np.testing.assert_allclose(g["dV"], v.grad.numpy(), atol=1e-11)
     np.testing.assert_array_equal(g["dKlm"], 0.0)
+
+
+# --------------------------------------------------------------------------- retrieval query
+# Low-rank query calibration ("Method" > "Input & chunking" of the ai-feeds summary): a
+# separate retrieval query scores the landmarks; the in-chunk attention keeps Q.
+
+
+def test_retrieval_query_equal_to_q_is_the_plain_operator(oracle_mod):
+    B, H, L, d, C, k = 1, 2, 512, 16, 64, 3
+    x = rand_inputs(B, H, L, d, C=C, seed=31, dtype="bf16", with_dO=True)
+    a = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], C, k)
+    b = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], C, k, Q_ret=x["Q"].copy())
+    for key in ("idx", "sel", "w", "lse", "O"):
+        np.testing.assert_array_equal(a[key], b[key])
+    ga = oracle_mod.bwd(x["Q"], x["K"], x["V"], x["Klm"], x["dO"], a["idx"], C, k)
+    gb = oracle_mod.bwd(x["Q"], x["K"], x["V"], x["Klm"], x["dO"], a["idx"], C, k, Q_ret=x["Q"].copy())
+    for key in ("dK", "dV", "dKlm"):
+        np.testing.assert_array_equal(ga[key], gb[key])
+    np.testing.assert_allclose(gb["dQ"] + gb["dQ_ret"], ga["dQ"], rtol=0, atol=1e-12)
+
+
+def test_retrieval_query_decides_selection_alone(oracle_mod):
+    B, H, L, d, C, k = 1, 2, 1024, 16, 64, 4
+    x = rand_inputs(B, H, L, d, C=C, seed=32, with_qret=True)
+    r = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], C, k, Q_ret=x["Q_ret"])
+    S = np.einsum("bhtd,bhjd->bhtj", f64(x["Q_ret"]), f64(x["Klm"])) / math.sqrt(d)
+    for b in range(B):
+        for h in range(H):
+            for t in range(0, L, 5):
+                c = t // C
+                m = min(k, c)
+                s = S[b, h, t, :c + 1].astype(np.float32)
+                order = np.lexsort((np.arange(c), -s[:c]))[:m]
+                np.testing.assert_array_equal(r["idx"][b, h, t, :m], order)
+                np.testing.assert_allclose(r["sel"][b, h, t, :m], s[order], rtol=2e-6, atol=2e-6)
+                assert r["idx"][b, h, t, k] == c
+    # another Q with the same Q_ret: same selection and fusion weights, other outputs
+    y = rand_inputs(B, H, L, d, C=C, seed=33)
+    r2 = oracle_mod.fwd(y["Q"], x["K"], x["V"], x["Klm"], C, k, Q_ret=x["Q_ret"])
+    for key in ("idx", "sel", "w"):
+        np.testing.assert_array_equal(r[key], r2[key])
+    assert np.abs(r["O"] - r2["O"]).max() > 1e-2
+
+
+def test_retrieval_query_output_is_fused_chunk_attention(oracle_mod):
+    """O_t = sum_j w_tj attn(q_t, chunk j), w the softmax over sigma(Q_ret . Klm) of the selected set."""
+    B, H, L, d, C, k = 1, 1, 512, 16, 64, 3
+    x = rand_inputs(B, H, L, d, C=C, seed=34, with_qret=True)
+    r = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], C, k, Q_ret=x["Q_ret"])
+    q, K, V = f64(x["Q"])[0, 0], f64(x["K"])[0, 0], f64(x["V"])[0, 0]
+    S = np.einsum("td,jd->tj", f64(x["Q_ret"])[0, 0], f64(x["Klm"])[0, 0]) / math.sqrt(d)
+    rng = np.random.default_rng(5)
+    for t in sorted(rng.choice(L, 40, replace=False)):
+        c = t // C
+        chosen = [j for j in r["idx"][0, 0, t] if j >= 0]
+        s = S[t, chosen].astype(np.float32).astype(np.float64)
+        wt = np.exp(s - s.max())
+        wt /= wt.sum()
+        o = np.zeros(d)
+        for wj, j in zip(wt, chosen):
+            hi = min((j + 1) * C, t + 1) if j == c else (j + 1) * C
+            o += wj * attn_one(q[t], K[j * C:hi], V[j * C:hi])
+        np.testing.assert_allclose(r["O"][0, 0, t], o, rtol=1e-9, atol=1e-10)
+
+
+def test_retrieval_query_central_differences(oracle_mod):
+    B, H, L, d, C, k = 1, 1, 256, 8, 64, 2
+    x = rand_inputs(B, H, L, d, C=C, seed=35, with_dO=True, with_qret=True)
+    G = x["dO"]
+    idx = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], C, k, Q_ret=x["Q_ret"])["idx"]
+    g = oracle_mod.bwd(x["Q"], x["K"], x["V"], x["Klm"], G, idx, C, k, Q_ret=x["Q_ret"])
+    h = 2.0 ** -10
+    rng = np.random.default_rng(1)
+    names = {"Q": "dQ", "Q_ret": "dQ_ret", "K": "dK", "V": "dV", "Klm": "dKlm"}
+    for name, gname in names.items():
+        for _ in range(10):
+            pos = tuple(int(rng.integers(0, s)) for s in x[name].shape)
+            vals = []
+            for sgn in (1, -1):
+                p = {n: x[n] for n in names}
+                a = x[name].copy()
+                a[pos] = np.float32(a[pos] + sgn * h)
+                p[name] = a
+                O = oracle_mod.fwd(p["Q"], p["K"], p["V"], p["Klm"], C, k, idx=idx, Q_ret=p["Q_ret"])["O"]
+                vals.append(float(np.sum(O * G.astype(np.float64))))
+            fd = (vals[0] - vals[1]) / (2 * h)
+            an = g[gname][pos]
+            assert abs(fd - an) <= 2e-4 * max(1.0, abs(an)), (name, pos, fd, an)
