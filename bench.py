@@ -209,17 +209,18 @@ def kernel_times(hils, fn, steps):
 # ----------------------------------------------------------------------------- workloads
 
 
-def bench_prefill(hils, synth, name, steps, warmup):
+def bench_prefill(hils, synth, name, steps, warmup, rq=False):
+    """rq: separate retrieval queries score the landmarks (low-rank query calibration)."""
     import torch
 
     w = synth.WORKLOADS[name]
-    x = synth.torch_prefill_inputs(w)
+    x = synth.torch_prefill_inputs(w, with_qret=rq)
     ws = torch.empty(hils.workspace_size(hils.OP_FWD, w.B, w.H, w.L, w.d, w.C, w.k), dtype=torch.uint8,
                      device="cuda:0")
     O = torch.empty_like(x["Q"])
 
     def step():
-        hils.sparse_attn_fwd(x["Q"], x["K"], x["V"], x["Klm"], w.k, ws=ws, out=O)
+        hils.sparse_attn_fwd(x["Q"], x["K"], x["V"], x["Klm"], w.k, ws=ws, out=O, Q_ret=x.get("Q_ret"))
 
     ms_eager, _ = timed(step, steps, warmup)
     ms, wall, graph = timed_graph(step, steps, warmup)
@@ -228,7 +229,7 @@ def bench_prefill(hils, synth, name, steps, warmup):
     work = prefill_work(w.B, w.H, w.L, w.d, w.k, w.C)
     nsteps = max(1, min(steps, 10))
     per_kernel = {n: round(t / c * 1e3, 3) for n, (t, c) in kt.items()}
-    rl = roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()}, name)
+    rl = roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()}, None if rq else name)
     res = {
         "tokens_per_s": w.B * w.L / (ms * 1e-3),
         "ms_per_step": ms,
@@ -241,18 +242,19 @@ def bench_prefill(hils, synth, name, steps, warmup):
         "pairs": work["pairs"],
         "kernel_us": per_kernel,
         "roofline": rl,
-        "config": {"workload": name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "C": w.C, "k": w.k},
+        "config": {"workload": name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "C": w.C, "k": w.k,
+                   **({"retrieval_query": True} if rq else {})},
     }
     del x, ws, O
     torch.cuda.empty_cache()
     return res
 
 
-def bench_train(hils, synth, name, steps, warmup):
+def bench_train(hils, synth, name, steps, warmup, rq=False):
     import torch
 
     w = synth.WORKLOADS[name]
-    x = synth.torch_prefill_inputs(w, with_dO=True)
+    x = synth.torch_prefill_inputs(w, with_dO=True, with_qret=rq)
     wsf = torch.empty(hils.workspace_size(hils.OP_FWD, w.B, w.H, w.L, w.d, w.C, w.k), dtype=torch.uint8,
                       device="cuda:0")
     wsb = torch.empty(hils.workspace_size(hils.OP_BWD, w.B, w.H, w.L, w.d, w.C, w.k), dtype=torch.uint8,
@@ -265,6 +267,7 @@ def bench_train(hils, synth, name, steps, warmup):
     idx = torch.empty((B, H, L, k1), dtype=torch.int32, device="cuda:0")
     sel, wt, lse = (torch.empty((B, H, L, k1), **f32) for _ in range(3))
     grads = [torch.empty((B, H, L, d), **f32) for _ in range(3)] + [torch.empty((B, H, L // w.C, d), **f32)]
+    dQr = torch.empty((B, H, L, d), **f32) if rq else None
     import ctypes
 
     lib = hils._lib
@@ -272,12 +275,22 @@ def bench_train(hils, synth, name, steps, warmup):
 
     def step():
         s_ = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        hils._check(lib.hils_sparse_attn_fwd(P(x["Q"]), P(x["K"]), P(x["V"]), P(x["Klm"]), P(idx), P(sel), 1, P(O),
-                                             P(wt), P(lse), B, H, L, d, w.C, w.k, 1.0 / math.sqrt(d), 0, P(wsf),
-                                             wsf.numel(), s_))
-        hils._check(lib.hils_sparse_attn_bwd(P(x["Q"]), P(x["K"]), P(x["V"]), P(x["Klm"]), P(x["dO"]), P(idx),
-                                             P(wt), P(lse), *(P(g_) for g_ in grads), B, H, L, d, w.C, w.k,
-                                             1.0 / math.sqrt(d), 0, P(wsb), wsb.numel(), s_))
+        scale = 1.0 / math.sqrt(d)
+        if not rq:
+            hils._check(lib.hils_sparse_attn_fwd(P(x["Q"]), P(x["K"]), P(x["V"]), P(x["Klm"]), P(idx), P(sel), 1,
+                                                 P(O), P(wt), P(lse), B, H, L, d, w.C, w.k, scale, 0, P(wsf),
+                                                 wsf.numel(), s_))
+            hils._check(lib.hils_sparse_attn_bwd(P(x["Q"]), P(x["K"]), P(x["V"]), P(x["Klm"]), P(x["dO"]), P(idx),
+                                                 P(wt), P(lse), *(P(g_) for g_ in grads), B, H, L, d, w.C, w.k,
+                                                 scale, 0, P(wsb), wsb.numel(), s_))
+            return
+        hils._check(lib.hils_sparse_attn_fwd_rq(P(x["Q"]), P(x["Q_ret"]), P(x["K"]), P(x["V"]), P(x["Klm"]), P(idx),
+                                                P(sel), 1, P(O), P(wt), P(lse), B, H, L, d, w.C, w.k, scale, 0,
+                                                P(wsf), wsf.numel(), s_))
+        hils._check(lib.hils_sparse_attn_bwd_rq(P(x["Q"]), P(x["Q_ret"]), P(x["K"]), P(x["V"]), P(x["Klm"]),
+                                                P(x["dO"]), P(idx), P(wt), P(lse), P(grads[0]), P(dQr),
+                                                *(P(g_) for g_ in grads[1:]), B, H, L, d, w.C, w.k, scale, 0,
+                                                P(wsb), wsb.numel(), s_))
 
     ms_eager, _ = timed(step, steps, warmup)
     ms, wall, graph = timed_graph(step, steps, warmup)
@@ -294,9 +307,9 @@ def bench_train(hils, synth, name, steps, warmup):
         "tflops": work["flops"] / (ms * 1e-3) / 1e12,
         "algorithmic_gflop": work["flops"] / 1e9,
         "kernel_us": {n: round(t / c * 1e3, 3) for n, (t, c) in kt.items()},
-        "roofline": roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()}, name),
+        "roofline": roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()}, None if rq else name),
         "config": {"workload": name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "C": w.C, "k": w.k,
-                   "step": "forward + backward"},
+                   "step": "forward + backward", **({"retrieval_query": True} if rq else {})},
     }
     del x, wsf, wsb
     torch.cuda.empty_cache()
@@ -400,7 +413,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--skip", default="", help="comma list of workloads to skip")
     ap.add_argument("--only", default="", help="run only this workload (prefill_8k, prefill_128k, decode_512k, "
-                                               "train_8k) and print its result object; for profiling runs")
+                                               "train_8k; a _retrieval suffix on a prefill or train workload "
+                                               "adds separate retrieval queries) and print its result object; "
+                                               "for profiling runs")
     ap.add_argument("--decode-replicas", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -428,12 +443,14 @@ def main():
             torch.cuda.synchronize()
             print(json.dumps({"workload": "copy_calibration", "bytes_per_copy": nbytes, "copies": 3}), flush=True)
             return
-        if args.only.startswith("prefill"):
-            res = bench_prefill(hils, synth, args.only, args.steps, args.warmup)
+        rq = args.only.endswith("_retrieval")
+        name = args.only[:-len("_retrieval")] if rq else args.only
+        if name.startswith("prefill"):
+            res = bench_prefill(hils, synth, name, args.steps, args.warmup, rq=rq)
         elif args.only.startswith("decode"):
             res = bench_decode(hils, synth, args.only, args.decode_replicas, args.warmup)
-        elif args.only.startswith("train"):
-            res = bench_train(hils, synth, args.only, args.steps, args.warmup)
+        elif name.startswith("train"):
+            res = bench_train(hils, synth, name, args.steps, args.warmup, rq=rq)
         else:
             raise SystemExit(f"unknown workload {args.only}")
         print(json.dumps({"workload": args.only, **res}), flush=True)
@@ -456,6 +473,14 @@ def main():
         log("[bench] train_8k")
         extra["train_8k"] = bench_train(hils, synth, "train_8k", max(3, min(args.steps, 20)), 2)
         log(f"[bench] train_8k {extra['train_8k']['ms_per_step']*1e3:.1f} us/step")
+    if "retrieval" not in skip:
+        # separate retrieval queries score the landmarks (low-rank query calibration)
+        log("[bench] prefill_8k and train_8k with retrieval queries")
+        extra["prefill_8k_retrieval"] = bench_prefill(hils, synth, "prefill_8k", max(3, min(args.steps, 20)), 2,
+                                                      rq=True)
+        extra["train_8k_retrieval"] = bench_train(hils, synth, "train_8k", max(3, min(args.steps, 20)), 2, rq=True)
+        log(f"[bench] prefill_8k_retrieval {extra['prefill_8k_retrieval']['ms_per_step']*1e3:.1f} us/step, "
+            f"train_8k_retrieval {extra['train_8k_retrieval']['ms_per_step']*1e3:.1f} us/step")
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")

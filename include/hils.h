@@ -164,6 +164,39 @@ hils_status hils_sparse_attn_bwd(const void* Q, const void* K, const void* V, co
                                  int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Separate retrieval queries (the low-rank query calibration that the
+ * ai-feeds summary names under "Method" > "Input & chunking": an affine map
+ * of Q, made by the caller, that serves the chunk retrieval).  Q_ret / q_ret
+ * has Q's / q's layout and element type; it replaces Q in the landmark
+ * scores, so in the selection and in the fusion weights, while the per-chunk
+ * attention keeps Q.  A null Q_ret / q_ret is the plain entry point.
+ *   hils_sparse_attn_fwd_rq : as hils_sparse_attn_fwd; with select = 0 the
+ *                             caller's idx is scored with Q_ret.
+ *   hils_decode_step_rq     : as hils_decode_step.
+ *   hils_sparse_attn_bwd_rq : as hils_sparse_attn_bwd; dQ_ret [B][H][L][d]
+ *                             float receives the score-path gradient
+ *                             (sum_j ds_tj scale K_lm_j) and dQ the in-chunk
+ *                             attention terms only; dK_lm sums ds_tj Q_ret_t.
+ *                             Q_ret and dQ_ret are given together or both
+ *                             null (else HILS_ERR_INVALID_ARG).
+ * Workspaces are those of the plain entry points.  Pointers: 16-byte aligned.
+ */
+hils_status hils_sparse_attn_fwd_rq(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm,
+                                    int32_t* idx, float* sel_score, int select, void* O, float* w_out,
+                                    float* lse_out, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
+                                    int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
+                                    void* stream);
+hils_status hils_decode_step_rq(const void* q, const void* q_ret, const void* k_new, const void* v_new,
+                                void* K_cache, void* V_cache, const void* K_lm_cache, int64_t n_ctx, int64_t L_max,
+                                void* o, int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C,
+                                int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes, void* stream);
+hils_status hils_sparse_attn_bwd_rq(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm,
+                                    const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
+                                    float* dQ_ret, float* dK, float* dV, float* dK_lm, int64_t B, int64_t H,
+                                    int64_t L, int64_t d, int64_t C, int64_t topk, float scale, hils_dtype dt,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Optional per-kernel timing, for measurement only (off by default; not a
  * step of the method).  While enabled, every kernel an entry point launches is
  * bracketed by a pair of HIP events recorded on the caller's stream, which

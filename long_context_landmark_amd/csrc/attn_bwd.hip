@@ -327,13 +327,13 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
 // held in registers and every load of a row is issued before any is used (slots past k + 1
 // and dropped slots read a valid address and are not used): two memory round trips per
 // thread, the landmark rows once the indices are in.
-template <typename T, int D, int K1M>
+template <typename T, int D, int K1M, bool RQ>
 __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* __restrict__ dq_part,
                                                         const float* __restrict__ Dpart,
                                                         const int32_t* __restrict__ idx, const float* __restrict__ w,
                                                         const T* __restrict__ Klm, float* __restrict__ ds_out,
-                                                        float* __restrict__ dQ, int64_t rows, int L, int N, int k,
-                                                        float scale) {
+                                                        float* __restrict__ dQ, float* __restrict__ dQr, int64_t rows,
+                                                        int L, int N, int k, float scale) {
   constexpr int V8 = D / 8;                    // threads per row
   constexpr int LW = 2 * Elem<T>::bytes;       // 32-bit words of eight landmark elements
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -373,9 +373,11 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* __restri
       lw[r][4 * v + 3] = x.w;
     }
   }
-  float acc[8];
+  // RQ: the landmark scores came from separate retrieval queries, whose gradient (the
+  // ds * Klm terms) goes to dQr; dQ then keeps the in-chunk attention terms only
+  float acc[8], accr[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int e = 0; e < 8; ++e) acc[e] = accr[e] = 0.f;
 #pragma unroll
   for (int r = 0; r < K1M; ++r) {
     if (!ok[r]) continue;
@@ -386,11 +388,23 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* __restri
     T lm[8];
     __builtin_memcpy(lm, lw[r], 8 * sizeof(T));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += (float)h[e] + scale * ds * Elem<T>::to_f32(lm, e);
+    for (int e = 0; e < 8; ++e) {
+      if (RQ) {
+        acc[e] += (float)h[e];
+        accr[e] += scale * ds * Elem<T>::to_f32(lm, e);
+      } else {
+        acc[e] += (float)h[e] + scale * ds * Elem<T>::to_f32(lm, e);
+      }
+    }
   }
   float4* out = reinterpret_cast<float4*>(dQ + row * D + 8 * c8);
   out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
   out[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  if (RQ) {
+    float4* outr = reinterpret_cast<float4*>(dQr + row * D + 8 * c8);
+    outr[0] = make_float4(accr[0], accr[1], accr[2], accr[3]);
+    outr[1] = make_float4(accr[4], accr[5], accr[6], accr[7]);
+  }
 }
 
 // dKlm_j = scale * sum over the chunk's own tile and its routed pairs of ds_tj q_t.
@@ -452,9 +466,10 @@ __global__ __launch_bounds__(256) void klm_bwd_kernel(const T* __restrict__ Q, c
 }
 
 template <typename T, int D>
-static hipError_t bwd_t(const void* Q, const void* K, const void* V, const void* Klm, const void* dO,
-                        const int32_t* idx, const float* w, const float* lse, float* dQ, float* dK, float* dV,
-                        float* dKlm, int BH, int L, int N, int k, float scale, const BwdBufs& ws, hipStream_t st) {
+static hipError_t bwd_t(const void* Q, const void* Qr, const void* K, const void* V, const void* Klm,
+                        const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ, float* dQr,
+                        float* dK, float* dV, float* dKlm, int BH, int L, int N, int k, float scale,
+                        const BwdBufs& ws, hipStream_t st) {
   const int64_t rows = (int64_t)BH * L;
   hipError_t e = launch_route(idx, ws.rb, BH, L, N, k, st);
   if (e != hipSuccess) return e;
@@ -462,26 +477,38 @@ static hipError_t bwd_t(const void* Q, const void* K, const void* V, const void*
               (const T*)V, (const T*)Klm, (const T*)dO, w, lse, ws.rb.chunk_off, ws.rb.pairs, ws.dq_part, ws.Dpart,
               ws.trash, ws.trash_f, dK, dV, L, N, k, scale);
   const dim3 rgrid((unsigned)((rows * (D / 8) + 255) / 256));
-  if (k <= 8)
-    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 9>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx, w,
-                (const T*)Klm, ws.ds, dQ, rows, L, N, k, scale);
+  const bool rq = Qr != nullptr;
+  if (k <= 8 && !rq)
+    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 9, false>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx,
+                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale);
+  else if (!rq)
+    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 17, false>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx,
+                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale);
+  else if (k <= 8)
+    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 9, true>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx,
+                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale);
   else
-    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 17>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx, w,
-                (const T*)Klm, ws.ds, dQ, rows, L, N, k, scale);
-  HILS_LAUNCH("klm_bwd", (klm_bwd_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)Q, ws.ds, ws.rb.chunk_off,
-              ws.rb.pairs, dKlm, L, N, k, scale);
+    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 17, true>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx,
+                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale);
+  // dKlm_j sums ds_tj times the query that scored the landmark
+  HILS_LAUNCH("klm_bwd", (klm_bwd_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)(rq ? Qr : Q), ws.ds,
+              ws.rb.chunk_off, ws.rb.pairs, dKlm, L, N, k, scale);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(int dt, int d, const void* Q, const void* K, const void* V, const void* Klm, const void* dO,
-                      const int32_t* idx, const float* w, const float* lse, float* dQ, float* dK, float* dV,
-                      float* dKlm, int BH, int L, int N, int k, float scale, const BwdBufs& ws, hipStream_t st) {
+hipError_t launch_bwd(int dt, int d, const void* Q, const void* Qr, const void* K, const void* V, const void* Klm,
+                      const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ, float* dQr,
+                      float* dK, float* dV, float* dKlm, int BH, int L, int N, int k, float scale, const BwdBufs& ws,
+                      hipStream_t st) {
+  if ((Qr == nullptr) != (dQr == nullptr)) return hipErrorInvalidValue;
   if (dt == 0)
-    return d == 64 ? bwd_t<bf16_t, 64>(Q, K, V, Klm, dO, idx, w, lse, dQ, dK, dV, dKlm, BH, L, N, k, scale, ws, st)
-                   : bwd_t<bf16_t, 128>(Q, K, V, Klm, dO, idx, w, lse, dQ, dK, dV, dKlm, BH, L, N, k, scale, ws, st);
+    return d == 64 ? bwd_t<bf16_t, 64>(Q, Qr, K, V, Klm, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k, scale,
+                                       ws, st)
+                   : bwd_t<bf16_t, 128>(Q, Qr, K, V, Klm, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k, scale,
+                                        ws, st);
   // fp32 inputs: head dim 64 only (the fp32 LDS tiles of d = 128 exceed a workgroup's LDS)
   if (d != 64) return hipErrorInvalidValue;
-  return bwd_t<float, 64>(Q, K, V, Klm, dO, idx, w, lse, dQ, dK, dV, dKlm, BH, L, N, k, scale, ws, st);
+  return bwd_t<float, 64>(Q, Qr, K, V, Klm, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k, scale, ws, st);
 }
 
 }  // namespace hils

@@ -318,7 +318,8 @@ constexpr int DEC_NWV = 16 / DEC_SPLIT;  // wavefronts per attention workgroup (
 // chunk meanwhile, since that needs no selection.  Each workgroup writes its weighted partial sum (its slots in
 // order); decode_fuse adds the DEC_SPLIT partials.
 template <typename T, int D>
-__global__ __launch_bounds__(64 * DEC_NWV) void decode_attend_kernel(const T* __restrict__ q, const T* __restrict__ Kc,
+__global__ __launch_bounds__(64 * DEC_NWV) void decode_attend_kernel(const T* __restrict__ q, const T* __restrict__ qr,
+                                                            const T* __restrict__ Kc,
                                                             const T* __restrict__ Vc, const T* __restrict__ Klm,
                                                             const uint64_t* __restrict__ lists,
                                                             float* __restrict__ part, int32_t* __restrict__ idx,
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(64 * DEC_NWV) void decode_attend_kernel(const T* __
     if (m > 0) merge_load(lists + (int64_t)bh * DEC_MAX_SLICES * DEC_LIST, S, m, lane, mi);
     float dot = 0.f;
     for (int e = lane; e < D; e += 64)
-      dot += Elem<T>::to_f32(q, (int64_t)bh * D + e) * Elem<T>::to_f32(Klm, ((int64_t)bh * Nmax + c) * D + e);
+      dot += Elem<T>::to_f32(qr, (int64_t)bh * D + e) * Elem<T>::to_f32(Klm, ((int64_t)bh * Nmax + c) * D + e);
     const float s_own = scale * wave_sum(dot);
     if (m > 0) wave_merge_lists(mi, m, top, surv, lane);
     const bool used = lane < m || lane == 16;
@@ -396,27 +397,31 @@ __global__ __launch_bounds__(64) void decode_fuse_kernel(const float* __restrict
 int decode_split() { return DEC_SPLIT; }
 
 template <typename T, int D>
-static hipError_t decode_t(const void* q, const void* k_new, const void* v_new, void* Kc, void* Vc, const void* Klm,
-                           int64_t n, int64_t Lmax, int64_t Nmax, void* o, int32_t* idx, float* w, int BH, int k,
-                           float scale, const DecodeBufs& ws, hipStream_t st) {
+static hipError_t decode_t(const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc, void* Vc,
+                           const void* Klm, int64_t n, int64_t Lmax, int64_t Nmax, void* o, int32_t* idx, float* w,
+                           int BH, int k, float scale, const DecodeBufs& ws, hipStream_t st) {
   const int S = decode_slices(n);
-  HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D>), dim3(S > 0 ? S : 1, BH), dim3(256), 0, st, (const T*)q,
+  // the landmark scores use the retrieval query (the attention query when none is given)
+  const T* qs = (const T*)(qr ? qr : q);
+  HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D>), dim3(S > 0 ? S : 1, BH), dim3(256), 0, st, qs,
               (const T*)k_new, (const T*)v_new, (T*)Kc, (T*)Vc, (const T*)Klm, ws.lists, n, Lmax, Nmax, scale);
   HILS_LAUNCH("decode_attend", (decode_attend_kernel<T, D>), dim3(DEC_SPLIT, BH), dim3(64 * DEC_NWV), 0, st, (const T*)q,
-              (const T*)Kc, (const T*)Vc, (const T*)Klm, ws.lists, ws.part, idx, w, n, Lmax, Nmax, k, scale);
+              qs, (const T*)Kc, (const T*)Vc, (const T*)Klm, ws.lists, ws.part, idx, w, n, Lmax, Nmax, k, scale);
   HILS_LAUNCH("decode_fuse", (decode_fuse_kernel<T, D>), dim3(BH), dim3(64), 0, st, ws.part, (T*)o);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(int dt, int d, const void* q, const void* k_new, const void* v_new, void* Kc, void* Vc,
-                         const void* Klm, int64_t n, int64_t Lmax, int64_t Nmax, void* o, int32_t* idx, float* w,
-                         int BH, int k, float scale, const DecodeBufs& ws, hipStream_t st) {
+hipError_t launch_decode(int dt, int d, const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc,
+                         void* Vc, const void* Klm, int64_t n, int64_t Lmax, int64_t Nmax, void* o, int32_t* idx,
+                         float* w, int BH, int k, float scale, const DecodeBufs& ws, hipStream_t st) {
   if (dt == 0)
-    return d == 64 ? decode_t<bf16_t, 64>(q, k_new, v_new, Kc, Vc, Klm, n, Lmax, Nmax, o, idx, w, BH, k, scale, ws, st)
-                   : decode_t<bf16_t, 128>(q, k_new, v_new, Kc, Vc, Klm, n, Lmax, Nmax, o, idx, w, BH, k, scale, ws,
-                                           st);
-  return d == 64 ? decode_t<float, 64>(q, k_new, v_new, Kc, Vc, Klm, n, Lmax, Nmax, o, idx, w, BH, k, scale, ws, st)
-                 : decode_t<float, 128>(q, k_new, v_new, Kc, Vc, Klm, n, Lmax, Nmax, o, idx, w, BH, k, scale, ws, st);
+    return d == 64 ? decode_t<bf16_t, 64>(q, qr, k_new, v_new, Kc, Vc, Klm, n, Lmax, Nmax, o, idx, w, BH, k, scale,
+                                          ws, st)
+                   : decode_t<bf16_t, 128>(q, qr, k_new, v_new, Kc, Vc, Klm, n, Lmax, Nmax, o, idx, w, BH, k, scale,
+                                           ws, st);
+  return d == 64
+             ? decode_t<float, 64>(q, qr, k_new, v_new, Kc, Vc, Klm, n, Lmax, Nmax, o, idx, w, BH, k, scale, ws, st)
+             : decode_t<float, 128>(q, qr, k_new, v_new, Kc, Vc, Klm, n, Lmax, Nmax, o, idx, w, BH, k, scale, ws, st);
 }
 
 }  // namespace hils

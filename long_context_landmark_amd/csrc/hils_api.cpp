@@ -228,11 +228,21 @@ hils_status hils_sparse_attn_fwd(const void* Q, const void* K, const void* V, co
                                  float* sel_score, int select, void* O, float* w_out, float* lse_out, int64_t B,
                                  int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk, float scale,
                                  hils_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+  return hils_sparse_attn_fwd_rq(Q, nullptr, K, V, K_lm, idx, sel_score, select, O, w_out, lse_out, B, H, L, d, C,
+                                 topk, scale, dt, ws, ws_bytes, stream);
+}
+
+hils_status hils_sparse_attn_fwd_rq(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm,
+                                    int32_t* idx, float* sel_score, int select, void* O, float* w_out,
+                                    float* lse_out, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
+                                    int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
+                                    void* stream) {
   Dims D;
   hils_status st;
   if ((st = check_dims(B, H, L, d, C, topk, true, &D)) != HILS_OK) return st;
   if ((st = check_dt(dt)) != HILS_OK) return st;
   REQUIRE_PTR(Q);
+  OPTIONAL_PTR(Q_ret);
   REQUIRE_PTR(K);
   REQUIRE_PTR(V);
   REQUIRE_PTR(K_lm);
@@ -251,8 +261,10 @@ hils_status hils_sparse_attn_fwd(const void* Q, const void* K, const void* V, co
   hipStream_t s = (hipStream_t)stream;
   float* w = w_out ? w_out : W.w_tmp;
   hipError_t e;
-  if (select) e = hils::launch_topk(dt, id, Q, K_lm, W.klm_frag, idx, sel_score, w, BH, iL, iN, ik, scale, s);
-  else e = hils::launch_fixed_selection(dt, id, Q, K_lm, idx, sel_score, w, BH, iL, iN, ik, scale, s);
+  // the landmark scores (selection and fusion weights) use the retrieval queries when given
+  const void* Qs = Q_ret ? Q_ret : Q;
+  if (select) e = hils::launch_topk(dt, id, Qs, K_lm, W.klm_frag, idx, sel_score, w, BH, iL, iN, ik, scale, s);
+  else e = hils::launch_fixed_selection(dt, id, Qs, K_lm, idx, sel_score, w, BH, iL, iN, ik, scale, s);
   if (e != hipSuccess) return hip_status(e, "hils_sparse_attn_fwd: selection");
   if ((e = hils::launch_route(idx, W.rb, BH, iL, iN, ik, s)) != hipSuccess)
     return hip_status(e, "hils_sparse_attn_fwd: routing");
@@ -269,6 +281,15 @@ hils_status hils_decode_step(const void* q, const void* k_new, const void* v_new
                              const void* K_lm_cache, int64_t n_ctx, int64_t L_max, void* o, int32_t* idx, float* w,
                              int64_t B, int64_t H, int64_t d, int64_t C, int64_t topk, float scale, hils_dtype dt,
                              void* ws, size_t ws_bytes, void* stream) {
+  return hils_decode_step_rq(q, nullptr, k_new, v_new, K_cache, V_cache, K_lm_cache, n_ctx, L_max, o, idx, w, B, H,
+                             d, C, topk, scale, dt, ws, ws_bytes, stream);
+}
+
+hils_status hils_decode_step_rq(const void* q, const void* q_ret, const void* k_new, const void* v_new,
+                                void* K_cache, void* V_cache, const void* K_lm_cache, int64_t n_ctx, int64_t L_max,
+                                void* o, int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C,
+                                int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
+                                void* stream) {
   Dims D;
   hils_status st;
   if (L_max < 1) return fail(HILS_ERR_INVALID_ARG, "L_max must be >= 1 (got %lld)", (long long)L_max);
@@ -279,6 +300,7 @@ hils_status hils_decode_step(const void* q, const void* k_new, const void* v_new
   if (n_ctx < 0 || n_ctx >= L_max)
     return fail(HILS_ERR_INVALID_ARG, "n_ctx (%lld) must be in [0, L_max=%lld)", (long long)n_ctx, (long long)L_max);
   REQUIRE_PTR(q);
+  OPTIONAL_PTR(q_ret);
   REQUIRE_PTR(k_new);
   REQUIRE_PTR(v_new);
   REQUIRE_PTR(K_cache);
@@ -292,8 +314,9 @@ hils_status hils_decode_step(const void* q, const void* k_new, const void* v_new
   const size_t need = carve_decode(nullptr, B * H, L_max, d, topk, &W);
   if ((st = check_ws(ws, ws_bytes, need)) != HILS_OK) return st;
   carve_decode(ws, B * H, L_max, d, topk, &W);
-  return hip_status(hils::launch_decode(dt, (int)d, q, k_new, v_new, K_cache, V_cache, K_lm_cache, n_ctx, L_max, Nmax,
-                                        o, idx, w, (int)(B * H), (int)topk, scale, W, (hipStream_t)stream),
+  return hip_status(hils::launch_decode(dt, (int)d, q, q_ret, k_new, v_new, K_cache, V_cache, K_lm_cache, n_ctx,
+                                        L_max, Nmax, o, idx, w, (int)(B * H), (int)topk, scale, W,
+                                        (hipStream_t)stream),
                     "hils_decode_step");
 }
 
@@ -301,11 +324,24 @@ hils_status hils_sparse_attn_bwd(const void* Q, const void* K, const void* V, co
                                  float* dK, float* dV, float* dK_lm, int64_t B, int64_t H, int64_t L, int64_t d,
                                  int64_t C, int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
                                  void* stream) {
+  return hils_sparse_attn_bwd_rq(Q, nullptr, K, V, K_lm, dO, idx, w, lse, dQ, nullptr, dK, dV, dK_lm, B, H, L, d, C,
+                                 topk, scale, dt, ws, ws_bytes, stream);
+}
+
+hils_status hils_sparse_attn_bwd_rq(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm,
+                                    const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
+                                    float* dQ_ret, float* dK, float* dV, float* dK_lm, int64_t B, int64_t H,
+                                    int64_t L, int64_t d, int64_t C, int64_t topk, float scale, hils_dtype dt,
+                                    void* ws, size_t ws_bytes, void* stream) {
   Dims D;
   hils_status st;
   if ((st = check_dims(B, H, L, d, C, topk, true, &D)) != HILS_OK) return st;
   if ((st = check_dt(dt)) != HILS_OK) return st;
   if (dt == HILS_FP32 && d != 64) return fail(HILS_ERR_UNSUPPORTED, "fp32 backward supports head dim 64 only");
+  if ((Q_ret == nullptr) != (dQ_ret == nullptr))
+    return fail(HILS_ERR_INVALID_ARG, "Q_ret and dQ_ret must be given together");
+  OPTIONAL_PTR(Q_ret);
+  OPTIONAL_PTR(dQ_ret);
   REQUIRE_PTR(Q);
   REQUIRE_PTR(K);
   REQUIRE_PTR(V);
@@ -323,8 +359,8 @@ hils_status hils_sparse_attn_bwd(const void* Q, const void* K, const void* V, co
   const size_t need = carve_bwd(nullptr, D, &W);
   if ((st = check_ws(ws, ws_bytes, need)) != HILS_OK) return st;
   carve_bwd(ws, D, &W);
-  return hip_status(hils::launch_bwd(dt, (int)d, Q, K, V, K_lm, dO, idx, w, lse, dQ, dK, dV, dK_lm, (int)(B * H),
-                                     (int)L, (int)D.N, (int)topk, scale, W, (hipStream_t)stream),
+  return hip_status(hils::launch_bwd(dt, (int)d, Q, Q_ret, K, V, K_lm, dO, idx, w, lse, dQ, dQ_ret, dK, dV, dK_lm,
+                                     (int)(B * H), (int)L, (int)D.N, (int)topk, scale, W, (hipStream_t)stream),
                     "hils_sparse_attn_bwd");
 }
 

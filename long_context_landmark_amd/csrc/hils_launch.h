@@ -75,12 +75,15 @@ struct BwdBufs {
   uint16_t* trash; // d elements: stores of lanes without a pair
   float* trash_f;  // one float, likewise
 };
-hipError_t launch_bwd(int dt, int d, const void* Q, const void* K, const void* V, const void* Klm,
-                      const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ, float* dK,
-                      float* dV, float* dKlm, int BH, int L, int N, int k, float scale, const BwdBufs& ws,
+// Qr / dQr: retrieval queries that scored the landmarks and their gradient (both null: Q scored them,
+// and dQ takes the whole gradient)
+hipError_t launch_bwd(int dt, int d, const void* Q, const void* Qr, const void* K, const void* V, const void* Klm,
+                      const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ, float* dQr,
+                      float* dK, float* dV, float* dKlm, int BH, int L, int N, int k, float scale, const BwdBufs& ws,
                       hipStream_t st);
-hipError_t launch_decode(int dt, int d, const void* q, const void* k_new, const void* v_new, void* Kc, void* Vc,
-                         const void* Klm, int64_t n, int64_t Lmax, int64_t Nmax, void* o, int32_t* idx, float* w,
-                         int BH, int k, float scale, const DecodeBufs& ws, hipStream_t st);
+// qr: retrieval query for the landmark scores (null: q)
+hipError_t launch_decode(int dt, int d, const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc,
+                         void* Vc, const void* Klm, int64_t n, int64_t Lmax, int64_t Nmax, void* o, int32_t* idx,
+                         float* w, int BH, int k, float scale, const DecodeBufs& ws, hipStream_t st);
 
 }  // namespace hils

@@ -36,6 +36,10 @@ _lib.hils_decode_step.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp,
                                   _i64, _f, _int, _vp, _sz, _vp]
 _lib.hils_sparse_attn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
                                       _i64, _i64, _i64, _i64, _f, _int, _vp, _sz, _vp]
+_lib.hils_sparse_attn_fwd_rq.argtypes = [_vp] + _lib.hils_sparse_attn_fwd.argtypes
+_lib.hils_decode_step_rq.argtypes = [_vp] + _lib.hils_decode_step.argtypes
+_lib.hils_sparse_attn_bwd_rq.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
+                                         _i64, _i64, _i64, _i64, _i64, _f, _int, _vp, _sz, _vp]
 _lib.hils_profile_enable.argtypes = [_int]
 _lib.hils_profile_enable.restype = None
 _lib.hils_profile_read.argtypes = [ctypes.c_char_p, _int, ctypes.POINTER(ctypes.c_double),
@@ -139,6 +143,11 @@ def _contig(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _like(ret, ref, name):
+    if ret is not None and (ret.shape != ref.shape or ret.dtype != ref.dtype or ret.device != ref.device):
+        raise ValueError(f"{name} must match the query in shape, dtype and device")
+
+
 def landmark_scores(Q, K_lm, C=64, scale=None):
     _contig(Q, K_lm)
     B, H, L, d = _dims(Q, K_lm, C)
@@ -159,9 +168,13 @@ def topk_select(Q, K_lm, k, C=64, scale=None, with_weights=True):
     return idx, sel, w
 
 
-def sparse_attn_fwd(Q, K, V, K_lm, k, C=64, scale=None, idx=None, save_for_backward=False, ws=None, out=None):
-    """Returns (O, idx, sel_score, w, lse); w and lse are None unless save_for_backward."""
-    _contig(Q, K, V, K_lm, idx)
+def sparse_attn_fwd(Q, K, V, K_lm, k, C=64, scale=None, idx=None, save_for_backward=False, ws=None, out=None,
+                    Q_ret=None):
+    """Returns (O, idx, sel_score, w, lse); w and lse are None unless save_for_backward.
+
+    ``Q_ret``: retrieval queries (Q's shape and dtype) that score the landmarks instead of Q."""
+    _contig(Q, K, V, K_lm, idx, Q_ret)
+    _like(Q_ret, Q, "Q_ret")
     B, H, L, d = _dims(Q, K_lm, C)
     for t in (K, V):
         if t.shape != Q.shape or t.dtype != Q.dtype:
@@ -178,41 +191,63 @@ def sparse_attn_fwd(Q, K, V, K_lm, k, C=64, scale=None, idx=None, save_for_backw
     lse = torch.empty_like(sel) if save_for_backward else None
     O = out if out is not None else torch.empty_like(Q)
     wsb, n = _workspace(OP_FWD, B, H, L, d, C, k, Q.device, ws)
-    _check(_lib.hils_sparse_attn_fwd(_p(Q), _p(K), _p(V), _p(K_lm), _p(idx), _p(sel), select, _p(O), _p(w), _p(lse),
-                                     B, H, L, d, C, k, _scale(d, scale), _dt(Q), _p(wsb), n, _stream()))
+    args = (_p(K), _p(V), _p(K_lm), _p(idx), _p(sel), select, _p(O), _p(w), _p(lse), B, H, L, d, C, k,
+            _scale(d, scale), _dt(Q), _p(wsb), n, _stream())
+    if Q_ret is None:
+        _check(_lib.hils_sparse_attn_fwd(_p(Q), *args))
+    else:
+        _check(_lib.hils_sparse_attn_fwd_rq(_p(Q), _p(Q_ret), *args))
     return O, idx, sel, w, lse
 
 
 def decode_step(q, k_new, v_new, K_cache, V_cache, K_lm_cache, n_ctx, k, C=64, scale=None, ws=None, out=None,
-                idx=None, w=None):
-    """One decode step at position n_ctx; returns (o, idx, w).  The caches are updated in place."""
-    _contig(q, k_new, v_new, K_cache, V_cache, K_lm_cache)
+                idx=None, w=None, q_ret=None):
+    """One decode step at position n_ctx; returns (o, idx, w).  The caches are updated in place.
+    ``q_ret``: retrieval query (q's shape and dtype) that scores the landmarks instead of q."""
+    _contig(q, k_new, v_new, K_cache, V_cache, K_lm_cache, q_ret)
+    _like(q_ret, q, "q_ret")
     B, H, d = q.shape
     L_max = K_cache.shape[2]
     o = out if out is not None else torch.empty_like(q)
     idx = idx if idx is not None else torch.empty((B, H, k + 1), dtype=torch.int32, device=q.device)
     w = w if w is not None else torch.empty((B, H, k + 1), dtype=torch.float32, device=q.device)
     wsb, n = _workspace(OP_DECODE, B, H, L_max, d, C, k, q.device, ws)
-    _check(_lib.hils_decode_step(_p(q), _p(k_new), _p(v_new), _p(K_cache), _p(V_cache), _p(K_lm_cache), n_ctx, L_max,
-                                 _p(o), _p(idx), _p(w), B, H, d, C, k, _scale(d, scale), _dt(q), _p(wsb), n,
-                                 _stream()))
+    args = (_p(k_new), _p(v_new), _p(K_cache), _p(V_cache), _p(K_lm_cache), n_ctx, L_max, _p(o), _p(idx), _p(w), B,
+            H, d, C, k, _scale(d, scale), _dt(q), _p(wsb), n, _stream())
+    if q_ret is None:
+        _check(_lib.hils_decode_step(_p(q), *args))
+    else:
+        _check(_lib.hils_decode_step_rq(_p(q), _p(q_ret), *args))
     return o, idx, w
 
 
-def sparse_attn_bwd(Q, K, V, K_lm, dO, idx, w, lse, k, C=64, scale=None, ws=None, out=None):
-    """Returns (dQ, dK, dV, dK_lm) in float32, selection held fixed."""
-    _contig(Q, K, V, K_lm, dO, idx, w, lse)
+def sparse_attn_bwd(Q, K, V, K_lm, dO, idx, w, lse, k, C=64, scale=None, ws=None, out=None, Q_ret=None):
+    """Returns (dQ, dK, dV, dK_lm) in float32, selection held fixed.
+
+    With ``Q_ret`` (the forward's retrieval queries) returns (dQ, dQ_ret, dK, dV, dK_lm): dQ_ret
+    takes the gradient of the landmark scores and dQ the in-chunk attention terms."""
+    _contig(Q, K, V, K_lm, dO, idx, w, lse, Q_ret)
+    _like(Q_ret, Q, "Q_ret")
     B, H, L, d = _dims(Q, K_lm, C)
     f32 = dict(dtype=torch.float32, device=Q.device)
+    dQr = None
     if out is not None:
-        dQ, dK, dV, dKlm = out
+        if Q_ret is None:
+            dQ, dK, dV, dKlm = out
+        else:
+            dQ, dQr, dK, dV, dKlm = out
     else:
         dQ = torch.empty((B, H, L, d), **f32)
         dK = torch.empty((B, H, L, d), **f32)
         dV = torch.empty((B, H, L, d), **f32)
         dKlm = torch.empty((B, H, L // C, d), **f32)
+        if Q_ret is not None:
+            dQr = torch.empty((B, H, L, d), **f32)
     wsb, n = _workspace(OP_BWD, B, H, L, d, C, k, Q.device, ws)
-    _check(_lib.hils_sparse_attn_bwd(_p(Q), _p(K), _p(V), _p(K_lm), _p(dO), _p(idx), _p(w), _p(lse), _p(dQ),
-                                     _p(dK), _p(dV), _p(dKlm), B, H, L, d, C, k, _scale(d, scale), _dt(Q), _p(wsb), n,
-                                     _stream()))
-    return dQ, dK, dV, dKlm
+    tail = (_p(dK), _p(dV), _p(dKlm), B, H, L, d, C, k, _scale(d, scale), _dt(Q), _p(wsb), n, _stream())
+    head = (_p(K), _p(V), _p(K_lm), _p(dO), _p(idx), _p(w), _p(lse))
+    if Q_ret is None:
+        _check(_lib.hils_sparse_attn_bwd(_p(Q), *head, _p(dQ), *tail))
+        return dQ, dK, dV, dKlm
+    _check(_lib.hils_sparse_attn_bwd_rq(_p(Q), _p(Q_ret), *head, _p(dQ), _p(dQr), *tail))
+    return dQ, dQr, dK, dV, dKlm

@@ -103,3 +103,25 @@ def test_workspace_size_grows_with_problem(hils):
 def test_scores_validation(lib):
     assert lib.hils_landmark_scores(FAKE, FAKE, None, 1, 1, 128, 64, 64, 0.125, 0, None) == INVALID
     assert lib.hils_landmark_scores(FAKE, FAKE, FAKE, 1, 1, 128, 80, 64, 0.125, 0, None) == UNSUPPORTED
+
+
+def test_retrieval_query_entry_points_validate(lib, hils):
+    need = hils.workspace_size(hils.OP_FWD, 1, 2, 1024, 64, 64, 4)
+    tail = [1, FAKE, None, None, 1, 2, 1024, 64, 64, 4, 0.125, 0]
+    # a misaligned retrieval query is rejected; a null one is the plain entry point's workspace check
+    assert lib.hils_sparse_attn_fwd_rq(FAKE, MISALIGNED, *([FAKE] * 5), *tail, FAKE, need, None) == INVALID
+    assert "Q_ret" in lib.hils_last_error().decode()
+    assert lib.hils_sparse_attn_fwd_rq(FAKE, None, *([FAKE] * 5), *tail, None, need, None) == WORKSPACE
+    # backward: Q_ret and dQ_ret come together
+    nb = hils.workspace_size(hils.OP_BWD, 1, 2, 1024, 64, 64, 4)
+    dims = [1, 2, 1024, 64, 64, 4, 0.125, 0]
+    assert lib.hils_sparse_attn_bwd_rq(FAKE, FAKE, *([FAKE] * 8), None, *([FAKE] * 3), *dims, FAKE, nb,
+                                       None) == INVALID
+    assert "together" in lib.hils_last_error().decode()
+    assert lib.hils_sparse_attn_bwd_rq(FAKE, None, *([FAKE] * 8), FAKE, *([FAKE] * 3), *dims, FAKE, nb,
+                                       None) == INVALID
+    # decode: misaligned q_ret
+    nd = hils.workspace_size(hils.OP_DECODE, 1, 2, 1024, 64, 64, 4)
+    assert lib.hils_decode_step_rq(FAKE, MISALIGNED, *([FAKE] * 5), 100, 1024, FAKE, FAKE, FAKE, 1, 2, 64, 64, 4,
+                                   0.125, 0, FAKE, nd, None) == INVALID
+    assert "q_ret" in lib.hils_last_error().decode()

@@ -42,16 +42,21 @@ def _run_decode(hils, x, k, steps, check_every=1, tol=(2e-2, 1e-2)):
     Kc_h, Vc_h = x["K_cache"].copy(), x["V_cache"].copy()
     ws = torch.empty(hils.workspace_size(hils.OP_DECODE, B, H, Lmax, d, 64, k), dtype=torch.uint8, device="cuda:0")
     q_all, k_all, v_all = dev(x["q"]), dev(x["k_new"]), dev(x["v_new"])
+    # optional retrieval queries: they score the landmarks, q keeps the attention
+    rq = "q_ret" in x
+    qr_all = dev(x["q_ret"]) if rq else None
     n_differ = 0
     for s in range(steps):
         n = ctx + s
-        o, idx, w = hils.decode_step(q_all[s], k_all[s], v_all[s], Kc_g, Vc_g, Klm_g, n, k, ws=ws)
-        ref = oracle.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc_h, Vc_h, x["Klm"], n, 64, k)
+        o, idx, w = hils.decode_step(q_all[s], k_all[s], v_all[s], Kc_g, Vc_g, Klm_g, n, k, ws=ws,
+                                     q_ret=qr_all[s] if rq else None)
+        ref = oracle.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc_h, Vc_h, x["Klm"], n, 64, k,
+                            q_ret=x["q_ret"][s] if rq else None)
         if s % check_every and s != steps - 1:
             continue
         torch.cuda.synchronize()
         gi = idx.cpu().numpy()
-        differ = _check_step(s, n, gi, f32(w), f32(o), ref, x["Klm"], x["q"][s], k, d)
+        differ = _check_step(s, n, gi, f32(w), f32(o), ref, x["Klm"], x["q_ret" if rq else "q"][s], k, d)
         ro = ref["o"].reshape(B * H, d).copy()
         rw = ref["w"].reshape(B * H, k + 1).copy()
         for bh in differ:
@@ -61,10 +66,14 @@ def _run_decode(hils, x, k, steps, check_every=1, tol=(2e-2, 1e-2)):
             L = ((n // 64) + 1) * 64
             Qp = np.zeros((1, 1, L, d), x["q"].dtype)
             Qp[0, 0, n] = x["q"][s][b, h]
+            Qr = None
+            if rq:
+                Qr = np.zeros_like(Qp)
+                Qr[0, 0, n] = x["q_ret"][s][b, h]
             Kp = np.ascontiguousarray(Kc_h[b:b + 1, h:h + 1, :L])
             Vp = np.ascontiguousarray(Vc_h[b:b + 1, h:h + 1, :L])
             Lp = np.ascontiguousarray(x["Klm"][b:b + 1, h:h + 1, :L // 64])
-            fx = oracle.fwd(Qp, Kp, Vp, Lp, 64, k, rows=[n], idx=gi.reshape(B * H, k + 1)[bh:bh + 1])
+            fx = oracle.fwd(Qp, Kp, Vp, Lp, 64, k, rows=[n], idx=gi.reshape(B * H, k + 1)[bh:bh + 1], Q_ret=Qr)
             ro[bh] = fx["O"][0]
             rw[bh] = fx["w"][0]
         assert_close(f32(o).reshape(B * H, d), ro, f"o step {s}", *tol)
@@ -96,6 +105,19 @@ def _run_decode(hils, x, k, steps, check_every=1, tol=(2e-2, 1e-2)):
 def test_decode_steps(hils, gpu, dtype, B, H, d, ctx, steps, k):
     say(f"decode dtype={dtype} B={B} H={H} d={d} ctx={ctx} steps={steps} k={k}")
     x = synth.decode_inputs(B, H, d, ctx, steps, C=64, seed=ctx + d, dtype=dtype)
+    tol = (5e-3, 3e-3) if dtype == "f32" else (2e-2, 1e-2)
+    _run_decode(hils, x, k, steps, tol=tol)
+
+
+@pytest.mark.parametrize("dtype,B,H,d,ctx,steps,k", [
+    ("bf16", 1, 2, 64, 64 * 40 + 10, 70, 4),
+    ("bf16", 2, 2, 128, 64 * 300 + 63, 3, 16),
+    ("f32", 1, 2, 64, 64 * 20, 20, 4),
+])
+def test_decode_steps_retrieval_query(hils, gpu, dtype, B, H, d, ctx, steps, k):
+    """Decode with a separate retrieval query scoring the landmarks."""
+    say(f"decode retrieval query dtype={dtype} B={B} H={H} d={d} ctx={ctx} steps={steps} k={k}")
+    x = synth.decode_inputs(B, H, d, ctx, steps, C=64, seed=ctx + d + 7, dtype=dtype, with_qret=True)
     tol = (5e-3, 3e-3) if dtype == "f32" else (2e-2, 1e-2)
     _run_decode(hils, x, k, steps, tol=tol)
 

@@ -1,0 +1,88 @@
+"""Parity of the retrieval-query entry points with the CPU oracle.
+
+Separate retrieval queries (the low-rank query calibration of the HiLS summary
+page, "Method" > "Input & chunking") score the landmarks, so they decide the
+selection and the fusion weights; the per-chunk attention keeps Q.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_landmark_amd import synth
+from gpu_util import assert_close, check_selection, dev, f32, say, to_inputs
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ("bf16", 1, 2, 2112, 64, 8),    # 33 chunks: ragged tiles
+    ("bf16", 1, 2, 1024, 128, 16),
+    ("f32", 1, 2, 1024, 64, 4),
+]
+
+
+def _tol(dtype):
+    return (5e-3, 3e-3) if dtype == "f32" else (2e-2, 1e-2)
+
+
+@pytest.mark.parametrize("dtype,B,H,L,d,k", CASES)
+def test_fwd_retrieval_query(hils, gpu, dtype, B, H, L, d, k):
+    say(f"fwd retrieval query dtype={dtype} B={B} H={H} L={L} d={d} k={k}")
+    x = synth.prefill_inputs(B, H, L, d, C=64, seed=500 + L + d, dtype=dtype, with_qret=True)
+    t = to_inputs(x, ("Q", "Q_ret", "K", "V", "Klm"))
+    O, idx, sel, w, lse = hils.sparse_attn_fwd(t["Q"], t["K"], t["V"], t["Klm"], k, save_for_backward=True,
+                                               Q_ret=t["Q_ret"])
+    # the selection outputs are those of the plain operator run with Q_ret as the query
+    _, idx2, sel2, w2, _ = hils.sparse_attn_fwd(t["Q_ret"], t["K"], t["V"], t["Klm"], k, save_for_backward=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(sel, sel2) and torch.equal(w, w2)
+    ref = oracle.fwd(x["Q"], x["K"], x["V"], x["Klm"], 64, k, Q_ret=x["Q_ret"])
+    gi = idx.cpu().numpy()
+    bad = check_selection(gi, ref["idx"], x["Q_ret"], x["Klm"], 64, k)
+    ro = ref["O"].reshape(-1, d).copy()
+    rw = ref["w"].reshape(-1, k + 1).copy()
+    if len(bad):
+        fix = oracle.fwd(x["Q"], x["K"], x["V"], x["Klm"], 64, k, rows=bad, idx=gi.reshape(-1, k + 1)[bad],
+                         Q_ret=x["Q_ret"])
+        ro[bad] = fix["O"]
+        rw[bad] = fix["w"]
+    assert_close(f32(O).reshape(-1, d), ro, "O", *_tol(dtype))
+    assert_close(f32(w).reshape(-1, k + 1), rw, "w", 1e-5, 1e-5)
+
+
+def test_fwd_retrieval_query_equal_to_q(hils, gpu):
+    """Q_ret = Q gives the plain entry point's results bit for bit."""
+    B, H, L, d, k = 1, 2, 2048, 64, 8
+    x = synth.prefill_inputs(B, H, L, d, C=64, seed=510, dtype="bf16", with_dO=True)
+    t = to_inputs(x, ("Q", "K", "V", "Klm", "dO"))
+    Qr = t["Q"].clone()
+    a = hils.sparse_attn_fwd(t["Q"], t["K"], t["V"], t["Klm"], k, save_for_backward=True)
+    b = hils.sparse_attn_fwd(t["Q"], t["K"], t["V"], t["Klm"], k, save_for_backward=True, Q_ret=Qr)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    O, idx, sel, w, lse = a
+    ga = hils.sparse_attn_bwd(t["Q"], t["K"], t["V"], t["Klm"], t["dO"], idx, w, lse, k)
+    gb = hils.sparse_attn_bwd(t["Q"], t["K"], t["V"], t["Klm"], t["dO"], idx, w, lse, k, Q_ret=Qr)
+    torch.cuda.synchronize()
+    for u, v in zip((ga[1], ga[2], ga[3]), (gb[2], gb[3], gb[4])):
+        assert torch.equal(u, v)
+    err = (gb[0] + gb[1] - ga[0]).abs().max().item()
+    say(f"  |dQ + dQ_ret - dQ| = {err:.2e}")
+    assert err < 1e-5
+
+
+@pytest.mark.parametrize("dtype,B,H,L,d,k", CASES)
+def test_bwd_retrieval_query(hils, gpu, dtype, B, H, L, d, k):
+    if dtype == "f32" and d != 64:
+        pytest.skip("fp32 backward: head dim 64 only")
+    say(f"bwd retrieval query dtype={dtype} B={B} H={H} L={L} d={d} k={k}")
+    x = synth.prefill_inputs(B, H, L, d, C=64, seed=520 + L + d, dtype=dtype, with_dO=True, with_qret=True)
+    t = to_inputs(x, ("Q", "Q_ret", "K", "V", "Klm", "dO"))
+    O, idx, sel, w, lse = hils.sparse_attn_fwd(t["Q"], t["K"], t["V"], t["Klm"], k, save_for_backward=True,
+                                               Q_ret=t["Q_ret"])
+    dQ, dQr, dK, dV, dKlm = hils.sparse_attn_bwd(t["Q"], t["K"], t["V"], t["Klm"], t["dO"], idx, w, lse, k,
+                                                 Q_ret=t["Q_ret"])
+    torch.cuda.synchronize()
+    ref = oracle.bwd(x["Q"], x["K"], x["V"], x["Klm"], x["dO"], idx.cpu().numpy(), 64, k, Q_ret=x["Q_ret"])
+    for name, got in (("dQ", dQ), ("dQ_ret", dQr), ("dK", dK), ("dV", dV), ("dKlm", dKlm)):
+        assert_close(f32(got), ref[name], name, *_tol(dtype))
