@@ -18,6 +18,9 @@ Parity status of each function (what pins it is in ``tests/test_oracle_*.py``):
   bwd              pinned (central finite differences, closed-form sums)
   retrieval query  pinned (Q_ret = Q reproduces the plain operator; selection depends on
                    Q_ret only; finite differences of dQ_ret, dQ and dKlm)
+  landmark-free    pinned (key means against numpy; rows ending a chunk equal the plain
+                   operator on numpy means; own score of a chunk's first row is the scaled
+                   q.k; own score against numpy prefix means; decode steps equal prefill rows)
 """
 from __future__ import annotations
 
@@ -69,6 +72,13 @@ def _load():
     lib.oracle_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, ip, vp, vp,
                                vp, vp, vp, ip]
     lib.oracle_bwd.restype = ip
+    lib.oracle_chunk_means.argtypes = [vp, i64, vp, i64, i64, i64, i64, i64, i64, ip, ip]
+    lib.oracle_chunk_means.restype = None
+    lib.oracle_fwd_lf.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, ip, vp, i64, ip,
+                                  vp, vp, vp, vp, vp, ip]
+    lib.oracle_fwd_lf.restype = ip
+    lib.oracle_decode_lf.argtypes = lib.oracle_decode.argtypes
+    lib.oracle_decode_lf.restype = ip
     _lib = lib
     return lib
 
@@ -155,14 +165,68 @@ def fwd(Q, K, V, Klm, C, k, scale=None, rows=None, idx=None, override_scores=Non
     return {"idx": idx_out, "sel": sel, "w": w, "lse": lse, "O": O, "threads": used}
 
 
-def decode(q, k_new, v_new, Kc, Vc, Klm, n, C, k, scale=None, nthreads=0, q_ret=None):
+def chunk_means(K, C, nchunks=None, Klm=None, nthreads=0):
+    """Landmark-free chunk keys: row j = mean of key rows jC..jC+C-1 of every (b,h), rounded to fp32 and
+    then to K's element type.  Fills ``Klm`` ([B,H,Nlm,d], K's type) in place for the first ``nchunks``
+    chunks (default: every complete chunk) or returns a new [B,H,L//C,d] array."""
+    K = _c(K)
+    B, H, Lk, d = K.shape
+    nchunks = Lk // C if nchunks is None else nchunks
+    if nchunks * C > Lk:
+        raise ValueError("nchunks exceeds the complete chunks of K")
+    if Klm is None:
+        Klm = np.zeros((B, H, Lk // C, d), K.dtype)
+    if not Klm.flags.c_contiguous or Klm.dtype != K.dtype or Klm.shape[2] < nchunks:
+        raise ValueError("Klm must be a C-contiguous array of K's type with room for the chunks")
+    _load().oracle_chunk_means(_p(K), Lk, _p(Klm), Klm.shape[2], B, H, nchunks, d, C, _dt(K), nthreads)
+    return Klm
+
+
+def fwd_lf(Q, K, V, C, k, scale=None, rows=None, idx=None, nthreads=0, Q_ret=None):
+    """Forward with landmark-free chunks: past chunks are scored by their key means, the own chunk by the
+    mean of its keys up to the query.  Returns what ``fwd`` returns plus ``Klm`` (the key means)."""
+    Q, K, V = _c(Q), _c(K), _c(V)
+    Qr = _c(Q_ret) if Q_ret is not None else None
+    if Qr is not None and (Qr.shape != Q.shape or Qr.dtype != Q.dtype):
+        raise ValueError("Q_ret must match Q in shape and type")
+    B, H, L, d = Q.shape
+    if L % C:
+        raise ValueError("L must be a multiple of C")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    k1 = k + 1
+    if rows is not None:
+        rows = _c(np.asarray(rows, np.int64))
+        lead = (rows.shape[0],)
+    else:
+        lead = (B, H, L)
+    use_idx = idx is not None
+    idx_out = _c(np.array(idx, np.int32, copy=True)).reshape(lead + (k1,)) if use_idx else np.empty(lead + (k1,), np.int32)
+    sel = np.empty(lead + (k1,), np.float64)
+    w = np.empty(lead + (k1,), np.float64)
+    lse = np.empty(lead + (k1,), np.float64)
+    O = np.empty(lead + (d,), np.float64)
+    Klm = np.zeros((B, H, L // C, d), K.dtype)
+    used = _load().oracle_fwd_lf(_p(Q), _p(Qr), _p(K), _p(V), _p(Klm), B, H, L, d, C, k, scale, _dt(Q, K, V),
+                                 _p(rows), 0 if rows is None else rows.shape[0], int(use_idx),
+                                 _p(idx_out), _p(sel), _p(w), _p(lse), _p(O), nthreads)
+    if used < 0:
+        raise ValueError("unsupported shape")
+    return {"idx": idx_out, "sel": sel, "w": w, "lse": lse, "O": O, "Klm": Klm, "threads": used}
+
+
+def decode(q, k_new, v_new, Kc, Vc, Klm, n, C, k, scale=None, nthreads=0, q_ret=None, landmark_free=False):
     """One decode step at position n for every (b,h).
 
     Writes k_new / v_new into row n of ``Kc`` / ``Vc`` in place (these are the
     caller's host arrays, [B,H,Lmax,d]) and returns idx / sel / w / lse [B,H,k+1]
     and o [B,H,d].  ``q_ret`` (like q): retrieval queries for the landmark scores.
+    ``landmark_free``: landmark row n//C of ``Klm`` (updated in place) becomes the mean of the open
+    chunk's keys so far; earlier rows are read as given (the key means of their chunks).
     """
-    q, k_new, v_new, Klm = _c(q), _c(k_new), _c(v_new), _c(Klm)
+    q, k_new, v_new = _c(q), _c(k_new), _c(v_new)
+    if landmark_free and not Klm.flags.c_contiguous:
+        raise ValueError("Klm must be C-contiguous (it is updated in place)")
+    Klm = Klm if landmark_free else _c(Klm)
     qr = _c(q_ret) if q_ret is not None else None
     if qr is not None and (qr.shape != q.shape or qr.dtype != q.dtype):
         raise ValueError("q_ret must match q in shape and type")
@@ -180,9 +244,11 @@ def decode(q, k_new, v_new, Kc, Vc, Klm, n, C, k, scale=None, nthreads=0, q_ret=
     w = np.empty((B, H, k1), np.float64)
     lse = np.empty((B, H, k1), np.float64)
     o = np.empty((B, H, d), np.float64)
-    used = _load().oracle_decode(_p(q), _p(qr), _p(k_new), _p(v_new), _p(Kc), _p(Vc), _p(Klm), n, Lmax, Nmax, B, H,
-                                 d, C, k, scale, _dt(q, k_new, v_new, Kc, Vc, Klm), _p(idx), _p(sel), _p(w),
-                                 _p(lse), _p(o), nthreads)
+    fn = _load().oracle_decode_lf if landmark_free else _load().oracle_decode
+    used = fn(_p(q), _p(qr), _p(k_new), _p(v_new), _p(Kc), _p(Vc), _p(Klm), n, Lmax, Nmax, B, H, d, C, k, scale,
+              _dt(q, k_new, v_new, Kc, Vc, Klm), _p(idx), _p(sel), _p(w), _p(lse), _p(o), nthreads)
+    if used < 0:
+        raise ValueError("unsupported shape")
     return {"idx": idx, "sel": sel, "w": w, "lse": lse, "o": o, "threads": used}
 
 

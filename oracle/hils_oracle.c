@@ -24,6 +24,12 @@
  *             outside the operator) that replaces Q in the landmark scores,
  *             and so in the selection and the fusion weights, while the
  *             per-chunk attention keeps Q.  Without Qr the scores use Q.
+ *   [HiLS-p1] "Method" > "Input & chunking" further mentions a landmark-free
+ *             alternative.  Read as: the landmark of a chunk is the mean of
+ *             its keys (rounded to fp32, then to the element type); for the
+ *             query's own chunk only the keys up to the query are averaged,
+ *             so nothing after the query enters its scores and a decode step
+ *             equals the prefill row at the same position.
  * Points the pages leave open are fixed as follows (one landmark key per
  * chunk; scale 1/sqrt(d) on both softmax levels; top-k ties go to the lower
  * chunk index; the query's own chunk is always in the set, is not counted in
@@ -79,7 +85,38 @@ typedef struct {
   int64_t Nlm;  /* rows per (b,h) in Klm */
   double scale;
   int dt;
+  int lf;  /* landmark-free: the own chunk's landmark is the mean of its keys up to the query */
 } prob_t;
+
+#define MAX_D 256
+
+/* double -> fp32 (round to nearest even) -> element type (bf16: round to nearest even on the bits) */
+static double round_dt(double x, int dt) {
+  float f = (float)x;
+  if (dt == DT_F32) return (double)f;
+  uint32_t b;
+  memcpy(&b, &f, sizeof b);
+  b = (b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u;
+  memcpy(&f, &b, sizeof f);
+  return (double)f;
+}
+
+static void store_dt(void* p, int64_t i, double x, int dt) {
+  float f = (float)x;
+  if (dt == DT_F32) { ((float*)p)[i] = f; return; }
+  uint32_t b;
+  memcpy(&b, &f, sizeof b);
+  ((uint16_t*)p)[i] = (uint16_t)(b >> 16);
+}
+
+/* mean of key rows row0 .. row0+n-1, each element rounded as a landmark element */
+static void key_mean(const void* K, int64_t row0, int64_t n, int64_t d, int dt, double* out) {
+  for (int64_t e = 0; e < d; ++e) {
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i) s += elem(K, (row0 + i) * d + e, dt);
+    out[e] = round_dt(s / (double)n, dt);
+  }
+}
 
 typedef struct { float s; int32_t j; } cand_t;
 
@@ -93,9 +130,17 @@ static int cand_cmp(const void* a, const void* b) {
 }
 
 /* chunk score of query row t against landmark j (HiLS-p2 section 2, step 1):
- * scale * <q_t, Klm_j>, computed in double and rounded to fp32 */
-static float chunk_score(const prob_t* P, const void* q, int64_t qrow, int64_t bh, int64_t j) {
+ * scale * <q_t, Klm_j>, computed in double and rounded to fp32.  Landmark-free
+ * chunks: the own chunk's landmark is the mean of its keys jC..t. */
+static float chunk_score(const prob_t* P, const void* q, int64_t qrow, int64_t bh, int64_t t, int64_t j) {
   const void* qs = P->Qr ? P->Qr : q;
+  if (P->lf && j == t / P->C) {
+    double m[MAX_D];
+    key_mean(P->K, bh * P->Lkv + j * P->C, t - j * P->C + 1, P->d, P->dt, m);
+    double s = 0.0;
+    for (int64_t e = 0; e < P->d; ++e) s += elem(qs, qrow * P->d + e, P->dt) * m[e];
+    return (float)(P->scale * s);
+  }
   return (float)(P->scale * dot_row(qs, qrow, P->Klm, bh * P->Nlm + j, P->d, P->dt));
 }
 
@@ -110,7 +155,7 @@ static void select_chunks(const prob_t* P, const void* q, int64_t qrow, int64_t 
   int64_t m = c < P->k ? c : P->k;
   cand_t* cs = (cand_t*)malloc(sizeof(cand_t) * (size_t)(c > 0 ? c : 1));
   for (int64_t j = 0; j < c; ++j) {
-    cs[j].s = override_s ? (float)override_s[j] : chunk_score(P, q, qrow, bh, j);
+    cs[j].s = override_s ? (float)override_s[j] : chunk_score(P, q, qrow, bh, t, j);
     cs[j].j = (int32_t)j;
   }
   qsort(cs, (size_t)c, sizeof(cand_t), cand_cmp);
@@ -119,7 +164,7 @@ static void select_chunks(const prob_t* P, const void* q, int64_t qrow, int64_t 
     sel[r] = r < m ? (double)cs[r].s : -INFINITY;
   }
   idx[P->k] = (int32_t)c;
-  sel[P->k] = override_s ? (double)(float)override_s[c] : (double)chunk_score(P, q, qrow, bh, c);
+  sel[P->k] = override_s ? (double)(float)override_s[c] : (double)chunk_score(P, q, qrow, bh, t, c);
   free(cs);
 }
 
@@ -165,7 +210,7 @@ static void row_forward(const prob_t* P, const void* q, int64_t qrow, int64_t bh
     for (int64_t r = 0; r < k1; ++r) {
       if (idx[r] < 0) { sel[r] = -INFINITY; continue; }
       sel[r] = override_s ? (double)(float)override_s[idx[r]]
-                          : (double)chunk_score(P, q, qrow, bh, idx[r]);
+                          : (double)chunk_score(P, q, qrow, bh, t, idx[r]);
     }
   } else {
     select_chunks(P, q, qrow, bh, t, override_s, idx, sel);
@@ -208,7 +253,7 @@ void oracle_landmark_scores(const void* Q, const void* Klm, double* S, int64_t B
   for (int64_t row = 0; row < B * H * L; ++row) {
     int64_t bh = row / L, t = row % L;
     for (int64_t j = 0; j < P.N; ++j)
-      S[row * P.N + j] = (j <= t / C) ? (double)chunk_score(&P, Q, row, bh, j) : -INFINITY;
+      S[row * P.N + j] = (j <= t / C) ? (double)chunk_score(&P, Q, row, bh, t, j) : -INFINITY;
   }
 }
 
@@ -222,7 +267,7 @@ void oracle_landmark_scores_rows(const void* Q, const void* Klm, double* S, int6
   for (int64_t r = 0; r < nrows; ++r) {
     int64_t row = rows[r], bh = row / L, t = row % L;
     for (int64_t j = 0; j < P.N; ++j)
-      S[r * P.N + j] = (j <= t / C) ? (double)chunk_score(&P, Q, row, bh, j) : -INFINITY;
+      S[r * P.N + j] = (j <= t / C) ? (double)chunk_score(&P, Q, row, bh, t, j) : -INFINITY;
   }
 }
 
@@ -234,22 +279,63 @@ void oracle_landmark_scores_rows(const void* Q, const void* Klm, double* S, int6
  * landmark scores for both selection and fusion (a test hook).
  * Returns the number of threads used.
  */
+static void fwd_rows(const prob_t* P, const int64_t* rows, int64_t nrows, int use_idx, const double* override_s,
+                     int32_t* idx, double* sel, double* w, double* lse, double* O) {
+  int64_t total = rows ? nrows : P->B * P->H * P->L;
+  int64_t k1 = P->k + 1, L = P->L, N = P->N, d = P->d;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t r = 0; r < total; ++r) {
+    int64_t row = rows ? rows[r] : r;
+    int64_t bh = row / L, t = row % L;
+    row_forward(P, P->Q, row, bh, t, use_idx, override_s ? override_s + row * N : NULL,
+                idx + r * k1, sel + r * k1, w + r * k1, lse + r * k1, O + r * d);
+  }
+}
+
 int oracle_fwd(const void* Q, const void* Qr, const void* K, const void* V, const void* Klm,
                int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t k, double scale,
                int dt, const int64_t* rows, int64_t nrows, int use_idx, const double* override_s,
                int32_t* idx, double* sel, double* w, double* lse, double* O, int nthreads) {
   int64_t N = (L + C - 1) / C;
-  prob_t P = {Q, K, V, Klm, Qr, B, H, L, d, C, k, N, L, N, scale, dt};
+  prob_t P = {Q, K, V, Klm, Qr, B, H, L, d, C, k, N, L, N, scale, dt, 0};
   int used = set_threads(nthreads);
-  int64_t total = rows ? nrows : B * H * L;
-  int64_t k1 = k + 1;
-#pragma omp parallel for schedule(dynamic, 16)
-  for (int64_t r = 0; r < total; ++r) {
-    int64_t row = rows ? rows[r] : r;
-    int64_t bh = row / L, t = row % L;
-    row_forward(&P, Q, row, bh, t, use_idx, override_s ? override_s + row * N : NULL,
-                idx + r * k1, sel + r * k1, w + r * k1, lse + r * k1, O + r * d);
+  fwd_rows(&P, rows, nrows, use_idx, override_s, idx, sel, w, lse, O);
+  return used;
+}
+
+/*
+ * Landmark-free chunk keys: Klm row j of every (b,h) = the mean of key rows
+ * jC .. jC+C-1, rounded to fp32 and then to the element type, for the nchunks
+ * complete chunks.  K has Lk rows per (b,h), Klm has Nlm rows per (b,h).
+ */
+void oracle_chunk_means(const void* K, int64_t Lk, void* Klm, int64_t Nlm, int64_t B, int64_t H,
+                        int64_t nchunks, int64_t d, int64_t C, int dt, int nthreads) {
+  set_threads(nthreads);
+#pragma omp parallel for schedule(static)
+  for (int64_t bh = 0; bh < B * H; ++bh) {
+    double m[MAX_D];
+    for (int64_t j = 0; j < nchunks; ++j) {
+      key_mean(K, bh * Lk + j * C, C, d, dt, m);
+      for (int64_t e = 0; e < d; ++e) store_dt(Klm, (bh * Nlm + j) * d + e, m[e], dt);
+    }
   }
+}
+
+/*
+ * Forward with landmark-free chunks: the past chunks' landmarks are their key
+ * means (written to Klm_out, [B,H,N,d] in the element type), the own chunk's
+ * is the mean of its keys up to the query.  L must be a multiple of C.
+ */
+int oracle_fwd_lf(const void* Q, const void* Qr, const void* K, const void* V, void* Klm_out,
+                  int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t k, double scale,
+                  int dt, const int64_t* rows, int64_t nrows, int use_idx,
+                  int32_t* idx, double* sel, double* w, double* lse, double* O, int nthreads) {
+  if (L % C || d > MAX_D) return -1;
+  int64_t N = L / C;
+  oracle_chunk_means(K, L, Klm_out, N, B, H, N, d, C, dt, nthreads);
+  prob_t P = {Q, K, V, Klm_out, Qr, B, H, L, d, C, k, N, L, N, scale, dt, 1};
+  int used = set_threads(nthreads);
+  fwd_rows(&P, rows, nrows, use_idx, NULL, idx, sel, w, lse, O);
   return used;
 }
 
@@ -260,16 +346,25 @@ int oracle_fwd(const void* Q, const void* Qr, const void* K, const void* V, cons
  * open chunk n/C is read as the caller supplied it.
  * Caches are [B,H,Lmax,d]; Klm is [B,H,Nmax,d].
  */
-int oracle_decode(const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc, void* Vc,
-                  const void* Klm, int64_t n, int64_t Lmax, int64_t Nmax, int64_t B, int64_t H,
-                  int64_t d, int64_t C, int64_t k, double scale, int dt, int32_t* idx,
-                  double* sel, double* w, double* lse, double* o, int nthreads) {
+static int decode_common(const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc, void* Vc,
+                         void* Klm, int lf, int64_t n, int64_t Lmax, int64_t Nmax, int64_t B, int64_t H,
+                         int64_t d, int64_t C, int64_t k, double scale, int dt, int32_t* idx,
+                         double* sel, double* w, double* lse, double* o, int nthreads) {
   int64_t esz = dt == DT_F32 ? 4 : 2;
   for (int64_t bh = 0; bh < B * H; ++bh) {
     memcpy((char*)Kc + ((bh * Lmax + n) * d) * esz, (const char*)k_new + bh * d * esz, (size_t)(d * esz));
     memcpy((char*)Vc + ((bh * Lmax + n) * d) * esz, (const char*)v_new + bh * d * esz, (size_t)(d * esz));
   }
-  prob_t P = {q, Kc, Vc, Klm, qr, B, H, n + 1, d, C, k, Nmax, Lmax, Nmax, scale, dt};
+  if (lf) {
+    /* landmark-free: the open chunk's landmark row becomes the mean of its keys so far */
+    int64_t c = n / C;
+    double m[MAX_D];
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+      key_mean(Kc, bh * Lmax + c * C, n - c * C + 1, d, dt, m);
+      for (int64_t e = 0; e < d; ++e) store_dt(Klm, (bh * Nmax + c) * d + e, m[e], dt);
+    }
+  }
+  prob_t P = {q, Kc, Vc, Klm, qr, B, H, n + 1, d, C, k, Nmax, Lmax, Nmax, scale, dt, lf};
   int used = set_threads(nthreads);
   int64_t k1 = k + 1;
 #pragma omp parallel for schedule(static)
@@ -277,6 +372,29 @@ int oracle_decode(const void* q, const void* qr, const void* k_new, const void* 
     row_forward(&P, q, bh, bh, n, 0, NULL, idx + bh * k1, sel + bh * k1, w + bh * k1,
                 lse + bh * k1, o + bh * d);
   return used;
+}
+
+int oracle_decode(const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc, void* Vc,
+                  const void* Klm, int64_t n, int64_t Lmax, int64_t Nmax, int64_t B, int64_t H,
+                  int64_t d, int64_t C, int64_t k, double scale, int dt, int32_t* idx,
+                  double* sel, double* w, double* lse, double* o, int nthreads) {
+  return decode_common(q, qr, k_new, v_new, Kc, Vc, (void*)Klm, 0, n, Lmax, Nmax, B, H, d, C, k, scale, dt, idx,
+                       sel, w, lse, o, nthreads);
+}
+
+/*
+ * Decode step with landmark-free chunks: after the append, landmark row n/C
+ * of Klm (the caller's host array, updated in place) becomes the mean of the
+ * open chunk's keys so far; rows of earlier chunks are read as given (their
+ * key means).
+ */
+int oracle_decode_lf(const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc, void* Vc,
+                     void* Klm, int64_t n, int64_t Lmax, int64_t Nmax, int64_t B, int64_t H,
+                     int64_t d, int64_t C, int64_t k, double scale, int dt, int32_t* idx,
+                     double* sel, double* w, double* lse, double* o, int nthreads) {
+  if (d > MAX_D) return -1;
+  return decode_common(q, qr, k_new, v_new, Kc, Vc, Klm, 1, n, Lmax, Nmax, B, H, d, C, k, scale, dt, idx, sel, w,
+                       lse, o, nthreads);
 }
 
 /*

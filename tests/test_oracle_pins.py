@@ -474,3 +474,93 @@ def test_retrieval_query_central_differences(oracle_mod):
             fd = (vals[0] - vals[1]) / (2 * h)
             an = g[gname][pos]
             assert abs(fd - an) <= 2e-4 * max(1.0, abs(an)), (name, pos, fd, an)
+
+
+# --------------------------------------------------------------------------- landmark-free chunks
+# Reading of the landmark-free alternative ("Method" > "Input & chunking" of the ai-feeds summary):
+# a chunk's landmark is the mean of its keys; the own chunk averages only the keys up to the query.
+
+
+def _np_means(K, C):
+    """Key means per chunk with numpy (float64), rounded to fp32 and then to K's element type."""
+    Kf = f64(K)
+    B, H, L, d = Kf.shape
+    m = Kf.reshape(B, H, L // C, C, d).mean(axis=3).astype(np.float32)
+    return synth.f32_to_bf16_bits(m) if K.dtype == np.uint16 else m
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_chunk_means_match_numpy(oracle_mod, dtype):
+    x = rand_inputs(2, 2, 640, 32, C=64, seed=40, dtype=dtype)
+    np.testing.assert_array_equal(oracle_mod.chunk_means(x["K"], 64), _np_means(x["K"], 64))
+
+
+def test_landmark_free_rows_ending_a_chunk_are_the_plain_operator(oracle_mod):
+    B, H, L, d, C, k = 1, 2, 1024, 16, 64, 4
+    x = rand_inputs(B, H, L, d, C=C, seed=41, dtype="bf16")
+    lf = oracle_mod.fwd_lf(x["Q"], x["K"], x["V"], C, k)
+    means = _np_means(x["K"], C)
+    np.testing.assert_array_equal(lf["Klm"], means)
+    plain = oracle_mod.fwd(x["Q"], x["K"], x["V"], means, C, k)
+    # the own slot is fixed, so the past-chunk selection is the plain one on every row
+    np.testing.assert_array_equal(lf["idx"], plain["idx"])
+    np.testing.assert_array_equal(lf["sel"][..., :k], plain["sel"][..., :k])
+    # at the last row of a chunk the prefix mean is the chunk mean
+    ends = np.arange(C - 1, L, C)
+    for key in ("sel", "w", "lse", "O"):
+        np.testing.assert_array_equal(lf[key][:, :, ends], plain[key][:, :, ends])
+    assert np.abs(lf["O"] - plain["O"]).max() > 1e-3
+
+
+def test_landmark_free_own_scores_are_causal_prefix_means(oracle_mod):
+    B, H, L, d, C, k = 1, 1, 512, 16, 64, 3
+    x = rand_inputs(B, H, L, d, C=C, seed=42, dtype="bf16")
+    lf = oracle_mod.fwd_lf(x["Q"], x["K"], x["V"], C, k)
+    q, K = f64(x["Q"])[0, 0], f64(x["K"])[0, 0]
+    t = np.arange(L)
+    cs = np.cumsum(K.reshape(L // C, C, d), axis=1).reshape(L, d)
+    pm = (cs / ((t % C) + 1)[:, None]).astype(np.float32)
+    pm = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(pm)).astype(np.float64)
+    want = (np.einsum("td,td->t", q, pm) / math.sqrt(d)).astype(np.float32)
+    np.testing.assert_allclose(lf["sel"][0, 0, :, k], want, rtol=1e-6, atol=1e-7)
+    # first row of a chunk: the landmark is that row's own key
+    first = np.arange(0, L, C)
+    np.testing.assert_array_equal(lf["sel"][0, 0, first, k],
+                                  (np.einsum("td,td->t", q[first], K[first]) / math.sqrt(d)).astype(np.float32))
+    # no key after the query enters its outputs: changing the keys of later rows leaves row t unchanged
+    t0 = 64 * 5 + 17
+    K2 = x["K"].copy()
+    K2[:, :, t0 + 1:] = synth.f32_to_bf16_bits(np.float32(3.0) * synth.as_f32(K2[:, :, t0 + 1:]))
+    lf2 = oracle_mod.fwd_lf(x["Q"], K2, x["V"], C, k, rows=[t0])
+    np.testing.assert_array_equal(lf2["O"][0], lf["O"][0, 0, t0])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_landmark_free_decode_matches_prefill_rows(oracle_mod, dtype):
+    B, H, d, C, k = 1, 2, 16, 64, 3
+    ctx, steps = 64 * 3 + 40, 100
+    x = synth.decode_inputs(B, H, d, ctx, steps, C=C, seed=43, dtype=dtype)
+    Kc, Vc = x["K_cache"].copy(), x["V_cache"].copy()
+    Klm = np.zeros_like(x["Klm"])
+    oracle_mod.chunk_means(Kc, C, nchunks=ctx // C, Klm=Klm)
+    outs = []
+    for s in range(steps):
+        outs.append(oracle_mod.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc, Vc, Klm, ctx + s, C, k,
+                                      landmark_free=True))
+    L = ctx + steps
+    L_pad = ((L + C - 1) // C) * C
+    Q = np.zeros((B, H, L_pad, d), x["q"].dtype)
+    for s in range(steps):
+        Q[:, :, ctx + s] = x["q"][s]
+    K = np.zeros_like(Q)
+    V = np.zeros_like(Q)
+    K[:, :, :L] = Kc[:, :, :L]
+    V[:, :, :L] = Vc[:, :, :L]
+    rows = np.array([bh * L_pad + ctx + s for s in range(steps) for bh in range(B * H)])
+    ref = oracle_mod.fwd_lf(Q, K, V, C, k, rows=rows)
+    for i, (s, bh) in enumerate((s, bh) for s in range(steps) for bh in range(B * H)):
+        np.testing.assert_array_equal(outs[s]["idx"].reshape(-1, k + 1)[bh], ref["idx"][i])
+        np.testing.assert_array_equal(outs[s]["o"].reshape(-1, d)[bh], ref["O"][i])
+    # rows of the chunks completed meanwhile hold their key means
+    done = L // C
+    np.testing.assert_array_equal(Klm[:, :, :done], _np_means(Kc[:, :, :done * C], C))
