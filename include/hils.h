@@ -197,6 +197,43 @@ hils_status hils_sparse_attn_bwd_rq(const void* Q, const void* Q_ret, const void
                                     void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Landmark-free chunks (the landmark-free alternative the ai-feeds summary
+ * mentions under "Method" > "Input & chunking"): a chunk's landmark key is
+ * the mean of its C keys (fp32 sum, rounded to the element type); for the
+ * query's own chunk only the keys up to the query are averaged, so no key
+ * after the query enters its scores.
+ *   hils_chunk_means       : rows 0..n_chunks-1 of K_lm [B][H][N_lm][d] (dt)
+ *                            = means of the key rows of each chunk of K
+ *                            [B][H][L_k][d] (dt).  n_chunks*C <= L_k,
+ *                            n_chunks <= N_lm.  Use it to fill the landmark
+ *                            rows of the complete chunks of a decode cache.
+ *   hils_sparse_attn_fwd_lf: as hils_sparse_attn_fwd_rq (Q_ret may be null),
+ *                            but the landmarks are formed here: K_lm_out
+ *                            [B][H][N][d] (dt, caller-owned) receives the key
+ *                            means, which score the past chunks; the own
+ *                            slot's sel_score and all fusion weights use the
+ *                            causal mean of the own chunk.  Same workspace.
+ *   hils_decode_step_lf    : as hils_decode_step_rq (q_ret may be null); the
+ *                            step writes landmark row n_ctx/C of K_lm_cache
+ *                            (the mean of keys C*(n_ctx/C) .. n_ctx, k_new
+ *                            included) before reading it; rows of earlier
+ *                            chunks must hold their key means (from
+ *                            hils_chunk_means or from earlier steps).
+ * The backward pass of landmark-free chunks is not provided.
+ */
+hils_status hils_chunk_means(const void* K, void* K_lm, int64_t B, int64_t H, int64_t L_k, int64_t N_lm,
+                             int64_t n_chunks, int64_t d, int64_t C, hils_dtype dt, void* stream);
+hils_status hils_sparse_attn_fwd_lf(const void* Q, const void* Q_ret, const void* K, const void* V, void* K_lm_out,
+                                    int32_t* idx, float* sel_score, int select, void* O, float* w_out,
+                                    float* lse_out, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
+                                    int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
+                                    void* stream);
+hils_status hils_decode_step_lf(const void* q, const void* q_ret, const void* k_new, const void* v_new,
+                                void* K_cache, void* V_cache, void* K_lm_cache, int64_t n_ctx, int64_t L_max,
+                                void* o, int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C,
+                                int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Optional per-kernel timing, for measurement only (off by default; not a
  * step of the method).  While enabled, every kernel an entry point launches is
  * bracketed by a pair of HIP events recorded on the caller's stream, which

@@ -60,12 +60,15 @@ __device__ __forceinline__ int wave_excl_prefix_small(int v, int& total) {
   return pre;
 }
 
-template <typename T, int D>
+// LF (landmark-free chunks): the appending workgroup also writes the open chunk's landmark row,
+// the mean of its keys so far (rows c*64 .. n-1 from the cache, row n from k_new), rounded to the
+// element type; the scan reads only rows of earlier chunks, decode_attend reads this one.
+template <typename T, int D, bool LF>
 __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ q, const T* __restrict__ k_new,
                                                           const T* __restrict__ v_new, T* __restrict__ Kc,
                                                           T* __restrict__ Vc, const T* __restrict__ Klm,
-                                                          uint64_t* __restrict__ lists, int64_t n, int64_t Lmax,
-                                                          int64_t Nmax, float scale) {
+                                                          T* __restrict__ Klm_w, uint64_t* __restrict__ lists,
+                                                          int64_t n, int64_t Lmax, int64_t Nmax, float scale) {
   constexpr int EPP = 16 / Elem<T>::bytes;  // elements per 16-byte piece
   constexpr int PIECES = D / EPP;           // pieces per row
   constexpr int RPR = 256 / PIECES;         // rows per round
@@ -77,6 +80,23 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ 
     for (int e = tid; e < D; e += 256) {
       Kc[((int64_t)bh * Lmax + n) * D + e] = k_new[(int64_t)bh * D + e];
       Vc[((int64_t)bh * Lmax + n) * D + e] = v_new[(int64_t)bh * D + e];
+    }
+    if (LF) {
+      constexpr int G = 256 / D;
+      __shared__ float lfp[G][D];
+      const int e = tid % D, g = tid / D;
+      const int64_t r0 = (int64_t)bh * Lmax + (int64_t)c * 64;
+      const int cnt = (int)(n - (int64_t)c * 64);  // cached rows of the open chunk before row n
+      float acc = 0.f;
+      for (int r = g; r < cnt; r += G) acc += Elem<T>::to_f32(Kc, (r0 + r) * D + e);
+      lfp[g][e] = acc;
+      __syncthreads();
+      if (g == 0) {
+        float sum = Elem<T>::to_f32(k_new, (int64_t)bh * D + e);
+#pragma unroll
+        for (int i = 0; i < G; ++i) sum += lfp[i][e];
+        Elem<T>::store(Klm_w, ((int64_t)bh * Nmax + c) * D + e, sum / (float)(cnt + 1));
+      }
     }
   }
   const int j0 = s * DEC_ROWS;
@@ -398,13 +418,19 @@ int decode_split() { return DEC_SPLIT; }
 
 template <typename T, int D>
 static hipError_t decode_t(const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc, void* Vc,
-                           const void* Klm, int64_t n, int64_t Lmax, int64_t Nmax, void* o, int32_t* idx, float* w,
-                           int BH, int k, float scale, const DecodeBufs& ws, hipStream_t st) {
+                           const void* Klm, bool lf, int64_t n, int64_t Lmax, int64_t Nmax, void* o, int32_t* idx,
+                           float* w, int BH, int k, float scale, const DecodeBufs& ws, hipStream_t st) {
   const int S = decode_slices(n);
   // the landmark scores use the retrieval query (the attention query when none is given)
   const T* qs = (const T*)(qr ? qr : q);
-  HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D>), dim3(S > 0 ? S : 1, BH), dim3(256), 0, st, qs,
-              (const T*)k_new, (const T*)v_new, (T*)Kc, (T*)Vc, (const T*)Klm, ws.lists, n, Lmax, Nmax, scale);
+  if (lf)
+    HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D, true>), dim3(S > 0 ? S : 1, BH), dim3(256), 0, st, qs,
+                (const T*)k_new, (const T*)v_new, (T*)Kc, (T*)Vc, (const T*)Klm, (T*)Klm, ws.lists, n, Lmax, Nmax,
+                scale);
+  else
+    HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D, false>), dim3(S > 0 ? S : 1, BH), dim3(256), 0, st, qs,
+                (const T*)k_new, (const T*)v_new, (T*)Kc, (T*)Vc, (const T*)Klm, (T*)nullptr, ws.lists, n, Lmax,
+                Nmax, scale);
   HILS_LAUNCH("decode_attend", (decode_attend_kernel<T, D>), dim3(DEC_SPLIT, BH), dim3(64 * DEC_NWV), 0, st, (const T*)q,
               qs, (const T*)Kc, (const T*)Vc, (const T*)Klm, ws.lists, ws.part, idx, w, n, Lmax, Nmax, k, scale);
   HILS_LAUNCH("decode_fuse", (decode_fuse_kernel<T, D>), dim3(BH), dim3(64), 0, st, ws.part, (T*)o);
@@ -412,16 +438,17 @@ static hipError_t decode_t(const void* q, const void* qr, const void* k_new, con
 }
 
 hipError_t launch_decode(int dt, int d, const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc,
-                         void* Vc, const void* Klm, int64_t n, int64_t Lmax, int64_t Nmax, void* o, int32_t* idx,
-                         float* w, int BH, int k, float scale, const DecodeBufs& ws, hipStream_t st) {
+                         void* Vc, const void* Klm, bool lf, int64_t n, int64_t Lmax, int64_t Nmax, void* o,
+                         int32_t* idx, float* w, int BH, int k, float scale, const DecodeBufs& ws, hipStream_t st) {
   if (dt == 0)
-    return d == 64 ? decode_t<bf16_t, 64>(q, qr, k_new, v_new, Kc, Vc, Klm, n, Lmax, Nmax, o, idx, w, BH, k, scale,
-                                          ws, st)
-                   : decode_t<bf16_t, 128>(q, qr, k_new, v_new, Kc, Vc, Klm, n, Lmax, Nmax, o, idx, w, BH, k, scale,
-                                           ws, st);
-  return d == 64
-             ? decode_t<float, 64>(q, qr, k_new, v_new, Kc, Vc, Klm, n, Lmax, Nmax, o, idx, w, BH, k, scale, ws, st)
-             : decode_t<float, 128>(q, qr, k_new, v_new, Kc, Vc, Klm, n, Lmax, Nmax, o, idx, w, BH, k, scale, ws, st);
+    return d == 64 ? decode_t<bf16_t, 64>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, n, Lmax, Nmax, o, idx, w, BH, k,
+                                          scale, ws, st)
+                   : decode_t<bf16_t, 128>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, n, Lmax, Nmax, o, idx, w, BH, k,
+                                           scale, ws, st);
+  return d == 64 ? decode_t<float, 64>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, n, Lmax, Nmax, o, idx, w, BH, k, scale,
+                                       ws, st)
+                 : decode_t<float, 128>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, n, Lmax, Nmax, o, idx, w, BH, k, scale,
+                                        ws, st);
 }
 
 }  // namespace hils

@@ -152,6 +152,15 @@ hils_status check_ws(void* ws, size_t ws_bytes, size_t need) {
 
 }  // namespace
 
+static hils_status fwd_impl(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm, bool lf,
+                            int32_t* idx, float* sel_score, int select, void* O, float* w_out, float* lse_out,
+                            int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk, float scale,
+                            hils_dtype dt, void* ws, size_t ws_bytes, void* stream);
+static hils_status decode_impl(const void* q, const void* q_ret, const void* k_new, const void* v_new, void* K_cache,
+                               void* V_cache, const void* K_lm_cache, bool lf, int64_t n_ctx, int64_t L_max, void* o,
+                               int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C, int64_t topk,
+                               float scale, hils_dtype dt, void* ws, size_t ws_bytes, void* stream);
+
 extern "C" {
 
 const char* hils_last_error(void) { return g_err; }
@@ -237,6 +246,41 @@ hils_status hils_sparse_attn_fwd_rq(const void* Q, const void* Q_ret, const void
                                     float* lse_out, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
                                     int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
                                     void* stream) {
+  return fwd_impl(Q, Q_ret, K, V, K_lm, false, idx, sel_score, select, O, w_out, lse_out, B, H, L, d, C, topk, scale,
+                  dt, ws, ws_bytes, stream);
+}
+
+hils_status hils_sparse_attn_fwd_lf(const void* Q, const void* Q_ret, const void* K, const void* V, void* K_lm_out,
+                                    int32_t* idx, float* sel_score, int select, void* O, float* w_out,
+                                    float* lse_out, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
+                                    int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  return fwd_impl(Q, Q_ret, K, V, K_lm_out, true, idx, sel_score, select, O, w_out, lse_out, B, H, L, d, C, topk,
+                  scale, dt, ws, ws_bytes, stream);
+}
+
+hils_status hils_chunk_means(const void* K, void* K_lm, int64_t B, int64_t H, int64_t L_k, int64_t N_lm,
+                             int64_t n_chunks, int64_t d, int64_t C, hils_dtype dt, void* stream) {
+  hils_status st;
+  if (C != 64) return fail(HILS_ERR_UNSUPPORTED, "chunk size C must be 64 (got %lld)", (long long)C);
+  if (d != 64 && d != 128) return fail(HILS_ERR_UNSUPPORTED, "head dim must be 64 or 128 (got %lld)", (long long)d);
+  if ((st = check_dt(dt)) != HILS_OK) return st;
+  if (B < 1 || H < 1 || B * H > 65535) return fail(HILS_ERR_INVALID_ARG, "B and H must be >= 1 with B*H <= 65535");
+  if (n_chunks < 0 || n_chunks * C > L_k || n_chunks > N_lm || n_chunks > 65535)
+    return fail(HILS_ERR_INVALID_ARG, "n_chunks (%lld) must be in [0, min(L_k/C, N_lm, 65535)]", (long long)n_chunks);
+  REQUIRE_PTR(K);
+  REQUIRE_PTR(K_lm);
+  return hip_status(hils::launch_chunk_means(dt, (int)d, K, K_lm, (int)(B * H), L_k, N_lm, (int)n_chunks,
+                                             (hipStream_t)stream),
+                    "hils_chunk_means");
+}
+
+}  // extern "C"
+
+static hils_status fwd_impl(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm, bool lf,
+                            int32_t* idx, float* sel_score, int select, void* O, float* w_out, float* lse_out,
+                            int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk, float scale,
+                            hils_dtype dt, void* ws, size_t ws_bytes, void* stream) {
   Dims D;
   hils_status st;
   if ((st = check_dims(B, H, L, d, C, topk, true, &D)) != HILS_OK) return st;
@@ -263,9 +307,15 @@ hils_status hils_sparse_attn_fwd_rq(const void* Q, const void* Q_ret, const void
   hipError_t e;
   // the landmark scores (selection and fusion weights) use the retrieval queries when given
   const void* Qs = Q_ret ? Q_ret : Q;
+  // landmark-free chunks: the landmarks are the chunks' key means, formed here
+  if (lf && (e = hils::launch_chunk_means(dt, id, K, (void*)K_lm, BH, L, D.N, iN, s)) != hipSuccess)
+    return hip_status(e, "hils_sparse_attn_fwd: chunk means");
   if (select) e = hils::launch_topk(dt, id, Qs, K_lm, W.klm_frag, idx, sel_score, w, BH, iL, iN, ik, scale, s);
   else e = hils::launch_fixed_selection(dt, id, Qs, K_lm, idx, sel_score, w, BH, iL, iN, ik, scale, s);
   if (e != hipSuccess) return hip_status(e, "hils_sparse_attn_fwd: selection");
+  // ... and the own chunk is scored by the mean of its keys up to the query
+  if (lf && (e = hils::launch_lf_own(dt, id, Qs, K, idx, sel_score, w, BH, iL, ik, scale, s)) != hipSuccess)
+    return hip_status(e, "hils_sparse_attn_fwd: own chunk landmarks");
   if ((e = hils::launch_route(idx, W.rb, BH, iL, iN, ik, s)) != hipSuccess)
     return hip_status(e, "hils_sparse_attn_fwd: routing");
   if ((e = hils::launch_chunk_attn_fwd(dt, id, Q, K, V, W.rb, W.lse_pair, W.partial, W.trash, W.trash_lse, BH, iL,
@@ -276,6 +326,8 @@ hils_status hils_sparse_attn_fwd_rq(const void* Q, const void* Q_ret, const void
     return hip_status(e, "hils_sparse_attn_fwd: own chunk and fusion");
   return HILS_OK;
 }
+
+extern "C" {
 
 hils_status hils_decode_step(const void* q, const void* k_new, const void* v_new, void* K_cache, void* V_cache,
                              const void* K_lm_cache, int64_t n_ctx, int64_t L_max, void* o, int32_t* idx, float* w,
@@ -290,6 +342,25 @@ hils_status hils_decode_step_rq(const void* q, const void* q_ret, const void* k_
                                 void* o, int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C,
                                 int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
                                 void* stream) {
+  return decode_impl(q, q_ret, k_new, v_new, K_cache, V_cache, K_lm_cache, false, n_ctx, L_max, o, idx, w, B, H, d,
+                     C, topk, scale, dt, ws, ws_bytes, stream);
+}
+
+hils_status hils_decode_step_lf(const void* q, const void* q_ret, const void* k_new, const void* v_new,
+                                void* K_cache, void* V_cache, void* K_lm_cache, int64_t n_ctx, int64_t L_max,
+                                void* o, int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C,
+                                int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
+                                void* stream) {
+  return decode_impl(q, q_ret, k_new, v_new, K_cache, V_cache, K_lm_cache, true, n_ctx, L_max, o, idx, w, B, H, d,
+                     C, topk, scale, dt, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+static hils_status decode_impl(const void* q, const void* q_ret, const void* k_new, const void* v_new, void* K_cache,
+                               void* V_cache, const void* K_lm_cache, bool lf, int64_t n_ctx, int64_t L_max, void* o,
+                               int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C, int64_t topk,
+                               float scale, hils_dtype dt, void* ws, size_t ws_bytes, void* stream) {
   Dims D;
   hils_status st;
   if (L_max < 1) return fail(HILS_ERR_INVALID_ARG, "L_max must be >= 1 (got %lld)", (long long)L_max);
@@ -314,11 +385,13 @@ hils_status hils_decode_step_rq(const void* q, const void* q_ret, const void* k_
   const size_t need = carve_decode(nullptr, B * H, L_max, d, topk, &W);
   if ((st = check_ws(ws, ws_bytes, need)) != HILS_OK) return st;
   carve_decode(ws, B * H, L_max, d, topk, &W);
-  return hip_status(hils::launch_decode(dt, (int)d, q, q_ret, k_new, v_new, K_cache, V_cache, K_lm_cache, n_ctx,
+  return hip_status(hils::launch_decode(dt, (int)d, q, q_ret, k_new, v_new, K_cache, V_cache, K_lm_cache, lf, n_ctx,
                                         L_max, Nmax, o, idx, w, (int)(B * H), (int)topk, scale, W,
                                         (hipStream_t)stream),
                     "hils_decode_step");
 }
+
+extern "C" {
 
 hils_status hils_sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* K_lm, const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
                                  float* dK, float* dV, float* dK_lm, int64_t B, int64_t H, int64_t L, int64_t d,

@@ -81,9 +81,18 @@ hipError_t launch_bwd(int dt, int d, const void* Q, const void* Qr, const void* 
                       const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ, float* dQr,
                       float* dK, float* dV, float* dKlm, int BH, int L, int N, int k, float scale, const BwdBufs& ws,
                       hipStream_t st);
-// qr: retrieval query for the landmark scores (null: q)
+// qr: retrieval query for the landmark scores (null: q).  lf: landmark-free chunks, the step writes
+// the open chunk's landmark row (the mean of its keys so far) before it is read
 hipError_t launch_decode(int dt, int d, const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc,
-                         void* Vc, const void* Klm, int64_t n, int64_t Lmax, int64_t Nmax, void* o, int32_t* idx,
-                         float* w, int BH, int k, float scale, const DecodeBufs& ws, hipStream_t st);
+                         void* Vc, const void* Klm, bool lf, int64_t n, int64_t Lmax, int64_t Nmax, void* o,
+                         int32_t* idx, float* w, int BH, int k, float scale, const DecodeBufs& ws, hipStream_t st);
+// landmark-free chunk keys: rows 0..nchunks-1 of Klm ([BH][Nlm][d]) = means of the key rows of each chunk
+// (K: [BH][Lk][d])
+hipError_t launch_chunk_means(int dt, int d, const void* K, void* Klm, int BH, int64_t Lk, int64_t Nlm, int nchunks,
+                              hipStream_t st);
+// landmark-free own chunk: after the selection, each query's own-slot score against the mean of its chunk's
+// keys up to it, and the fusion weights from the kept past scores (L a multiple of 64)
+hipError_t launch_lf_own(int dt, int d, const void* Qs, const void* K, const int32_t* idx, float* sel, float* w,
+                         int BH, int L, int k, float scale, hipStream_t st);
 
 }  // namespace hils

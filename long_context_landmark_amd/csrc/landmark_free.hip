@@ -1,0 +1,164 @@
+// Landmark-free chunk keys: the landmark-free alternative that the HiLS summary page (ai-feeds,
+// "Method" > "Input & chunking") mentions, read as: a chunk's landmark is the mean of its keys,
+// and for the query's own chunk only the keys up to the query are averaged, so nothing after
+// the query enters its scores.
+//
+//   chunk_mean  one workgroup per (chunk, head): 16-byte loads of the chunk's 64 key rows, fp32
+//               sums per row group, the groups added in LDS, times 1/64 (exact), rounded to the
+//               element type.  Reads the keys once (HBM-bound, 2d B per key row for bf16).
+//   lf_own      one workgroup per (chunk, head), after the selection: prefix means of the chunk's
+//               keys in LDS (one sequential fp32 pass per element), the own-chunk score of each
+//               query against its prefix mean (four lanes per query), then the own slot's score
+//               and the fusion weights rewritten from the kept past scores.  Reads Q (or the
+//               retrieval queries) and K once, and the selection outputs once.
+#include "hils_device.h"
+#include "hils_launch.h"
+
+namespace hils {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void chunk_mean_kernel(const T* __restrict__ K, T* __restrict__ Klm, int64_t Lk,
+                                                         int64_t Nlm) {
+  constexpr int EPP = 16 / Elem<T>::bytes;  // elements per 16-byte piece
+  constexpr int PIECES = D / EPP;           // pieces per row
+  constexpr int G = 256 / PIECES;           // row groups
+  constexpr int RPG = 64 / G;               // rows per group
+  const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int piece = tid % PIECES, g = tid / PIECES;
+  const T* base = K + ((int64_t)bh * Lk + (int64_t)j * 64) * D + piece * EPP;
+  int4 raw[RPG];
+#pragma unroll
+  for (int i = 0; i < RPG; ++i) raw[i] = *reinterpret_cast<const int4*>(base + (int64_t)(g + i * G) * D);
+  float acc[EPP];
+#pragma unroll
+  for (int e = 0; e < EPP; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < RPG; ++i) {
+    T vals[EPP];
+    __builtin_memcpy(vals, &raw[i], 16);
+#pragma unroll
+    for (int e = 0; e < EPP; ++e) acc[e] += Elem<T>::to_f32(vals, e);
+  }
+  __shared__ float part[G][D];
+#pragma unroll
+  for (int e = 0; e < EPP; ++e) part[g][piece * EPP + e] = acc[e];
+  __syncthreads();
+  for (int e = tid; e < D; e += 256) {
+    float s = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < G; ++i) s += part[i][e];
+    Elem<T>::store(Klm, ((int64_t)bh * Nlm + j) * D + e, s * (1.f / 64.f));
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void lf_own_kernel(const T* __restrict__ Qs, const T* __restrict__ K,
+                                                     const int32_t* __restrict__ idx, float* __restrict__ sel,
+                                                     float* __restrict__ w, int L, int k, float scale) {
+  constexpr int EPP = 16 / Elem<T>::bytes;
+  constexpr int PIECES = D / EPP;
+  constexpr int RPR = 256 / PIECES;  // key rows per staging round
+  constexpr int KS = D + 1;          // padded LDS row
+  const int c = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int64_t row0 = (int64_t)bh * L + (int64_t)c * 64;
+  __shared__ float km[64 * KS];
+  // stage the chunk's keys as fp32
+  {
+    const int piece = tid % PIECES, rr = tid / PIECES;
+#pragma unroll
+    for (int r0 = 0; r0 < 64; r0 += RPR) {
+      const int r = r0 + rr;
+      const int4 raw = *reinterpret_cast<const int4*>(K + (row0 + r) * D + piece * EPP);
+      T vals[EPP];
+      __builtin_memcpy(vals, &raw, 16);
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) km[r * KS + piece * EPP + e] = Elem<T>::to_f32(vals, e);
+    }
+  }
+  __syncthreads();
+  // prefix means, rounded to the element type like a landmark row
+  for (int e = tid; e < D; e += 256) {
+    float s = 0.f;
+    for (int r = 0; r < 64; ++r) {
+      s += km[r * KS + e];
+      T m[1];
+      Elem<T>::store(m, 0, s / (float)(r + 1));
+      km[r * KS + e] = Elem<T>::to_f32(m, 0);
+    }
+  }
+  __syncthreads();
+  // own-chunk score of each query, then its fusion weights (four lanes per query)
+  const int q = tid >> 2, part = tid & 3;
+  constexpr int EQ = D / 4;  // elements per lane
+  const T* qp = Qs + (row0 + q) * D + part * EQ;
+  float dot = 0.f;
+#pragma unroll
+  for (int v = 0; v < EQ / EPP; ++v) {
+    const int4 raw = *reinterpret_cast<const int4*>(qp + v * EPP);
+    T vals[EPP];
+    __builtin_memcpy(vals, &raw, 16);
+#pragma unroll
+    for (int e = 0; e < EPP; ++e) dot += Elem<T>::to_f32(vals, e) * km[q * KS + part * EQ + v * EPP + e];
+  }
+  dot += lane_xor(dot, 1);
+  dot += lane_xor(dot, 2);
+  const float s_own = scale * dot;
+  const int k1 = k + 1;
+  const int64_t base = (row0 + q) * k1;
+  float mx = s_own;
+  for (int r = part; r < k; r += 4)
+    if (idx[base + r] >= 0) mx = fmaxf(mx, sel[base + r]);
+  mx = fmaxf(mx, lane_xor(mx, 1));
+  mx = fmaxf(mx, lane_xor(mx, 2));
+  float den = part == 0 ? __expf(s_own - mx) : 0.f;
+  for (int r = part; r < k; r += 4)
+    if (idx[base + r] >= 0) den += __expf(sel[base + r] - mx);
+  den += lane_xor(den, 1);
+  den += lane_xor(den, 2);
+  const float inv = 1.f / den;
+  for (int r = part; r <= k; r += 4) {
+    if (r == k) {
+      sel[base + r] = s_own;
+      w[base + r] = __expf(s_own - mx) * inv;
+    } else {
+      w[base + r] = idx[base + r] >= 0 ? __expf(sel[base + r] - mx) * inv : 0.f;
+    }
+  }
+}
+
+template <typename T, int D>
+static hipError_t chunk_means_t(const void* K, void* Klm, int BH, int64_t Lk, int64_t Nlm, int nchunks,
+                                hipStream_t st) {
+  if (nchunks <= 0) return hipSuccess;
+  HILS_LAUNCH("chunk_mean", (chunk_mean_kernel<T, D>), dim3(nchunks, BH), dim3(256), 0, st, (const T*)K, (T*)Klm,
+              Lk, Nlm);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_means(int dt, int d, const void* K, void* Klm, int BH, int64_t Lk, int64_t Nlm, int nchunks,
+                              hipStream_t st) {
+  if (dt == 0)
+    return d == 64 ? chunk_means_t<bf16_t, 64>(K, Klm, BH, Lk, Nlm, nchunks, st)
+                   : chunk_means_t<bf16_t, 128>(K, Klm, BH, Lk, Nlm, nchunks, st);
+  return d == 64 ? chunk_means_t<float, 64>(K, Klm, BH, Lk, Nlm, nchunks, st)
+                 : chunk_means_t<float, 128>(K, Klm, BH, Lk, Nlm, nchunks, st);
+}
+
+template <typename T, int D>
+static hipError_t lf_own_t(const void* Qs, const void* K, const int32_t* idx, float* sel, float* w, int BH, int L,
+                           int k, float scale, hipStream_t st) {
+  HILS_LAUNCH("lf_own", (lf_own_kernel<T, D>), dim3(L / 64, BH), dim3(256), 0, st, (const T*)Qs, (const T*)K, idx,
+              sel, w, L, k, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_lf_own(int dt, int d, const void* Qs, const void* K, const int32_t* idx, float* sel, float* w,
+                         int BH, int L, int k, float scale, hipStream_t st) {
+  if (dt == 0)
+    return d == 64 ? lf_own_t<bf16_t, 64>(Qs, K, idx, sel, w, BH, L, k, scale, st)
+                   : lf_own_t<bf16_t, 128>(Qs, K, idx, sel, w, BH, L, k, scale, st);
+  return d == 64 ? lf_own_t<float, 64>(Qs, K, idx, sel, w, BH, L, k, scale, st)
+                 : lf_own_t<float, 128>(Qs, K, idx, sel, w, BH, L, k, scale, st);
+}
+
+}  // namespace hils

@@ -40,6 +40,9 @@ _lib.hils_sparse_attn_fwd_rq.argtypes = [_vp] + _lib.hils_sparse_attn_fwd.argtyp
 _lib.hils_decode_step_rq.argtypes = [_vp] + _lib.hils_decode_step.argtypes
 _lib.hils_sparse_attn_bwd_rq.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                                          _i64, _i64, _i64, _i64, _i64, _f, _int, _vp, _sz, _vp]
+_lib.hils_chunk_means.argtypes = [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _int, _vp]
+_lib.hils_sparse_attn_fwd_lf.argtypes = _lib.hils_sparse_attn_fwd_rq.argtypes
+_lib.hils_decode_step_lf.argtypes = _lib.hils_decode_step_rq.argtypes
 _lib.hils_profile_enable.argtypes = [_int]
 _lib.hils_profile_enable.restype = None
 _lib.hils_profile_read.argtypes = [ctypes.c_char_p, _int, ctypes.POINTER(ctypes.c_double),
@@ -200,10 +203,59 @@ def sparse_attn_fwd(Q, K, V, K_lm, k, C=64, scale=None, idx=None, save_for_backw
     return O, idx, sel, w, lse
 
 
+def chunk_means(K, C=64, n_chunks=None, K_lm=None):
+    """Landmark-free chunk keys: rows 0..n_chunks-1 of K_lm [B,H,N_lm,d] become the key means of each chunk of K
+    [B,H,L_k,d] (default: every complete chunk, into a new [B,H,L_k//C,d] tensor).  Returns K_lm."""
+    _contig(K, K_lm)
+    B, H, Lk, d = K.shape
+    n_chunks = Lk // C if n_chunks is None else n_chunks
+    if K_lm is None:
+        K_lm = torch.empty((B, H, Lk // C, d), dtype=K.dtype, device=K.device)
+    if K_lm.dtype != K.dtype or K_lm.shape[:2] != (B, H) or K_lm.shape[3] != d:
+        raise ValueError("K_lm must be [B,H,N_lm,d] of K's dtype")
+    _check(_lib.hils_chunk_means(_p(K), _p(K_lm), B, H, Lk, K_lm.shape[2], n_chunks, d, C, _dt(K), _stream()))
+    return K_lm
+
+
+def sparse_attn_fwd_lf(Q, K, V, k, C=64, scale=None, idx=None, save_for_backward=False, ws=None, out=None,
+                       Q_ret=None, K_lm=None):
+    """Forward with landmark-free chunks (landmarks = key means, the own chunk's the causal mean).
+    Returns (O, idx, sel_score, w, lse, K_lm); K_lm holds the chunks' key means."""
+    _contig(Q, K, V, idx, Q_ret, K_lm)
+    _like(Q_ret, Q, "Q_ret")
+    B, H, L, d = Q.shape
+    if L % C:
+        raise ValueError("L must be a multiple of C")
+    for t in (K, V):
+        if t.shape != Q.shape or t.dtype != Q.dtype:
+            raise ValueError("Q, K, V must share shape and dtype")
+    K_lm = K_lm if K_lm is not None else torch.empty((B, H, L // C, d), dtype=Q.dtype, device=Q.device)
+    if K_lm.shape != (B, H, L // C, d) or K_lm.dtype != Q.dtype:
+        raise ValueError("K_lm must be [B,H,L/C,d] of Q's dtype")
+    select = 1
+    if idx is None:
+        idx = torch.empty((B, H, L, k + 1), dtype=torch.int32, device=Q.device)
+    else:
+        select = 0
+        if idx.shape != (B, H, L, k + 1) or idx.dtype != torch.int32:
+            raise ValueError("idx must be int32 [B,H,L,k+1]")
+    sel = torch.empty((B, H, L, k + 1), dtype=torch.float32, device=Q.device)
+    w = torch.empty_like(sel) if save_for_backward else None
+    lse = torch.empty_like(sel) if save_for_backward else None
+    O = out if out is not None else torch.empty_like(Q)
+    wsb, n = _workspace(OP_FWD, B, H, L, d, C, k, Q.device, ws)
+    _check(_lib.hils_sparse_attn_fwd_lf(_p(Q), _p(Q_ret), _p(K), _p(V), _p(K_lm), _p(idx), _p(sel), select, _p(O),
+                                        _p(w), _p(lse), B, H, L, d, C, k, _scale(d, scale), _dt(Q), _p(wsb), n,
+                                        _stream()))
+    return O, idx, sel, w, lse, K_lm
+
+
 def decode_step(q, k_new, v_new, K_cache, V_cache, K_lm_cache, n_ctx, k, C=64, scale=None, ws=None, out=None,
-                idx=None, w=None, q_ret=None):
+                idx=None, w=None, q_ret=None, landmark_free=False):
     """One decode step at position n_ctx; returns (o, idx, w).  The caches are updated in place.
-    ``q_ret``: retrieval query (q's shape and dtype) that scores the landmarks instead of q."""
+    ``q_ret``: retrieval query (q's shape and dtype) that scores the landmarks instead of q.
+    ``landmark_free``: the step writes landmark row n_ctx // C of K_lm_cache (the mean of the open chunk's
+    keys so far); earlier rows must hold their chunks' key means."""
     _contig(q, k_new, v_new, K_cache, V_cache, K_lm_cache, q_ret)
     _like(q_ret, q, "q_ret")
     B, H, d = q.shape
@@ -214,7 +266,9 @@ def decode_step(q, k_new, v_new, K_cache, V_cache, K_lm_cache, n_ctx, k, C=64, s
     wsb, n = _workspace(OP_DECODE, B, H, L_max, d, C, k, q.device, ws)
     args = (_p(k_new), _p(v_new), _p(K_cache), _p(V_cache), _p(K_lm_cache), n_ctx, L_max, _p(o), _p(idx), _p(w), B,
             H, d, C, k, _scale(d, scale), _dt(q), _p(wsb), n, _stream())
-    if q_ret is None:
+    if landmark_free:
+        _check(_lib.hils_decode_step_lf(_p(q), _p(q_ret), *args))
+    elif q_ret is None:
         _check(_lib.hils_decode_step(_p(q), *args))
     else:
         _check(_lib.hils_decode_step_rq(_p(q), _p(q_ret), *args))

@@ -125,3 +125,21 @@ def test_retrieval_query_entry_points_validate(lib, hils):
     assert lib.hils_decode_step_rq(FAKE, MISALIGNED, *([FAKE] * 5), 100, 1024, FAKE, FAKE, FAKE, 1, 2, 64, 64, 4,
                                    0.125, 0, FAKE, nd, None) == INVALID
     assert "q_ret" in lib.hils_last_error().decode()
+
+
+def test_landmark_free_entry_points_validate(lib, hils):
+    # chunk means: more chunks than the keys hold, or than K_lm has rows
+    assert lib.hils_chunk_means(FAKE, FAKE, 1, 2, 640, 10, 11, 64, 64, 0, None) == INVALID
+    assert lib.hils_chunk_means(FAKE, FAKE, 1, 2, 1024, 8, 9, 64, 64, 0, None) == INVALID
+    assert "n_chunks" in lib.hils_last_error().decode()
+    assert lib.hils_chunk_means(FAKE, FAKE, 1, 2, 640, 10, 10, 96, 64, 0, None) == UNSUPPORTED
+    assert lib.hils_chunk_means(FAKE, None, 1, 2, 640, 10, 10, 64, 64, 0, None) == INVALID
+    # forward: the landmark output is required
+    need = hils.workspace_size(hils.OP_FWD, 1, 2, 1024, 64, 64, 4)
+    tail = [1, FAKE, None, None, 1, 2, 1024, 64, 64, 4, 0.125, 0]
+    assert lib.hils_sparse_attn_fwd_lf(FAKE, None, FAKE, FAKE, None, FAKE, FAKE, *tail, FAKE, need, None) == INVALID
+    assert lib.hils_sparse_attn_fwd_lf(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, *tail, None, need, None) == WORKSPACE
+    nd = hils.workspace_size(hils.OP_DECODE, 1, 2, 1024, 64, 64, 4)
+    assert lib.hils_decode_step_lf(FAKE, None, *([FAKE] * 5), 1024, 1024, FAKE, FAKE, FAKE, 1, 2, 64, 64, 4,
+                                   0.125, 0, FAKE, nd, None) == INVALID
+    assert "n_ctx" in lib.hils_last_error().decode()
