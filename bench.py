@@ -97,6 +97,9 @@ def prefill_work(B, H, L, d, k, C=64):
             "route_count": ("hbm", 0, BH * L * k * 4),
             "route_scan": ("hbm", 0, BH * 2 * N * 4 * max(1, L // 1024)),
             "route_scatter": ("hbm", 0, BH * L * k * 8),
+            # landmark-free chunks only
+            "chunk_mean": ("hbm", 0, BH * (L * d * 2 + N * d * 2)),
+            "lf_own": ("hbm", BH * L * 2 * d, BH * L * (2 * d * 2 + k1 * 12)),
         },
     }
 
@@ -209,18 +212,23 @@ def kernel_times(hils, fn, steps):
 # ----------------------------------------------------------------------------- workloads
 
 
-def bench_prefill(hils, synth, name, steps, warmup, rq=False):
-    """rq: separate retrieval queries score the landmarks (low-rank query calibration)."""
+def bench_prefill(hils, synth, name, steps, warmup, rq=False, lf=False):
+    """rq: separate retrieval queries score the landmarks (low-rank query calibration).
+    lf: landmark-free chunks, the landmarks formed inside the step as the chunks' key means."""
     import torch
 
     w = synth.WORKLOADS[name]
     x = synth.torch_prefill_inputs(w, with_qret=rq)
+    klm_out = torch.empty_like(x["Klm"]) if lf else None
     ws = torch.empty(hils.workspace_size(hils.OP_FWD, w.B, w.H, w.L, w.d, w.C, w.k), dtype=torch.uint8,
                      device="cuda:0")
     O = torch.empty_like(x["Q"])
 
     def step():
-        hils.sparse_attn_fwd(x["Q"], x["K"], x["V"], x["Klm"], w.k, ws=ws, out=O, Q_ret=x.get("Q_ret"))
+        if lf:
+            hils.sparse_attn_fwd_lf(x["Q"], x["K"], x["V"], w.k, ws=ws, out=O, Q_ret=x.get("Q_ret"), K_lm=klm_out)
+        else:
+            hils.sparse_attn_fwd(x["Q"], x["K"], x["V"], x["Klm"], w.k, ws=ws, out=O, Q_ret=x.get("Q_ret"))
 
     ms_eager, _ = timed(step, steps, warmup)
     ms, wall, graph = timed_graph(step, steps, warmup)
@@ -229,7 +237,7 @@ def bench_prefill(hils, synth, name, steps, warmup, rq=False):
     work = prefill_work(w.B, w.H, w.L, w.d, w.k, w.C)
     nsteps = max(1, min(steps, 10))
     per_kernel = {n: round(t / c * 1e3, 3) for n, (t, c) in kt.items()}
-    rl = roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()}, None if rq else name)
+    rl = roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()}, None if rq or lf else name)
     res = {
         "tokens_per_s": w.B * w.L / (ms * 1e-3),
         "ms_per_step": ms,
@@ -243,7 +251,7 @@ def bench_prefill(hils, synth, name, steps, warmup, rq=False):
         "kernel_us": per_kernel,
         "roofline": rl,
         "config": {"workload": name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "C": w.C, "k": w.k,
-                   **({"retrieval_query": True} if rq else {})},
+                   **({"retrieval_query": True} if rq else {}), **({"landmark_free": True} if lf else {})},
     }
     del x, ws, O
     torch.cuda.empty_cache()
@@ -316,12 +324,17 @@ def bench_train(hils, synth, name, steps, warmup, rq=False):
     return res
 
 
-def bench_decode(hils, synth, name, replicas, warmup):
+def bench_decode(hils, synth, name, replicas, warmup, lf=False):
+    """lf: landmark-free chunks; each replica's landmark rows start as its chunks' key means and the step
+    maintains the open chunk's row."""
     import torch
 
     w = synth.WORKLOADS[name]
     x = synth.torch_decode_inputs(w, replicas=replicas)
     reps = x["replicas"]
+    if lf:
+        for r in reps:
+            hils.chunk_means(r["K_cache"], w.C, n_chunks=w.L // w.C, K_lm=r["Klm"])
     B, H, d = w.B, w.H, w.d
     Lmax = w.L + w.steps
     ws = torch.empty(hils.workspace_size(hils.OP_DECODE, B, H, Lmax, d, w.C, w.k), dtype=torch.uint8,
@@ -333,7 +346,7 @@ def bench_decode(hils, synth, name, replicas, warmup):
     def token(s):
         for r in reps:
             hils.decode_step(x["q"][s], x["k_new"][s], x["v_new"][s], r["K_cache"], r["V_cache"], r["Klm"],
-                             w.L + s, w.k, ws=ws, out=o, idx=idx, w=wt)
+                             w.L + s, w.k, ws=ws, out=o, idx=idx, w=wt, landmark_free=lf)
 
     for s in range(warmup):
         token(s)
@@ -380,9 +393,10 @@ def bench_decode(hils, synth, name, replicas, warmup):
         "calls": calls,
         "wall_s": wall,
         "kernel_us": {n: round(t / c * 1e3, 3) for n, (t, c) in kt.items()},
-        "roofline": roofline(kt, work, {n: 1 for n in kt}, name),
+        "roofline": roofline(kt, work, {n: 1 for n in kt}, None if lf else name),
         "config": {"workload": name, "B": B, "H": H, "d": d, "context": w.L, "steps": w.steps, "k": w.k,
-                   "replicas": len(reps), "protocol": "cold" if len(reps) > 1 else "warm"},
+                   "replicas": len(reps), "protocol": "cold" if len(reps) > 1 else "warm",
+                   **({"landmark_free": True} if lf else {})},
     }
     del x, reps, ws
     torch.cuda.empty_cache()
@@ -414,8 +428,9 @@ def main():
     ap.add_argument("--skip", default="", help="comma list of workloads to skip")
     ap.add_argument("--only", default="", help="run only this workload (prefill_8k, prefill_128k, decode_512k, "
                                                "train_8k; a _retrieval suffix on a prefill or train workload "
-                                               "adds separate retrieval queries) and print its result object; "
-                                               "for profiling runs")
+                                               "adds separate retrieval queries, a _landmark_free suffix on a "
+                                               "prefill or decode workload uses key-mean landmarks) and print "
+                                               "its result object; for profiling runs")
     ap.add_argument("--decode-replicas", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -444,11 +459,12 @@ def main():
             print(json.dumps({"workload": "copy_calibration", "bytes_per_copy": nbytes, "copies": 3}), flush=True)
             return
         rq = args.only.endswith("_retrieval")
-        name = args.only[:-len("_retrieval")] if rq else args.only
+        lf = args.only.endswith("_landmark_free")
+        name = args.only[:-len("_retrieval")] if rq else args.only[:-len("_landmark_free")] if lf else args.only
         if name.startswith("prefill"):
-            res = bench_prefill(hils, synth, name, args.steps, args.warmup, rq=rq)
-        elif args.only.startswith("decode"):
-            res = bench_decode(hils, synth, args.only, args.decode_replicas, args.warmup)
+            res = bench_prefill(hils, synth, name, args.steps, args.warmup, rq=rq, lf=lf)
+        elif name.startswith("decode"):
+            res = bench_decode(hils, synth, name, args.decode_replicas, args.warmup, lf=lf)
         elif name.startswith("train"):
             res = bench_train(hils, synth, name, args.steps, args.warmup, rq=rq)
         else:
@@ -481,6 +497,15 @@ def main():
         extra["train_8k_retrieval"] = bench_train(hils, synth, "train_8k", max(3, min(args.steps, 20)), 2, rq=True)
         log(f"[bench] prefill_8k_retrieval {extra['prefill_8k_retrieval']['ms_per_step']*1e3:.1f} us/step, "
             f"train_8k_retrieval {extra['train_8k_retrieval']['ms_per_step']*1e3:.1f} us/step")
+    if "landmark_free" not in skip:
+        # landmark-free chunks: key-mean landmarks formed inside the step (prefill) or by the step (decode)
+        log("[bench] prefill_8k and decode_512k with landmark-free chunks")
+        extra["prefill_8k_landmark_free"] = bench_prefill(hils, synth, "prefill_8k", max(3, min(args.steps, 20)), 2,
+                                                          lf=True)
+        extra["decode_512k_landmark_free"] = bench_decode(hils, synth, "decode_512k", args.decode_replicas, 4,
+                                                          lf=True)
+        log(f"[bench] prefill_8k_landmark_free {extra['prefill_8k_landmark_free']['ms_per_step']*1e3:.1f} us/step, "
+            f"decode_512k_landmark_free {extra['decode_512k_landmark_free']['us_per_token']:.2f} us/token")
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")

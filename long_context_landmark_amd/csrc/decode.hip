@@ -62,7 +62,9 @@ __device__ __forceinline__ int wave_excl_prefix_small(int v, int& total) {
 
 // LF (landmark-free chunks): the appending workgroup also writes the open chunk's landmark row,
 // the mean of its keys so far (rows c*64 .. n-1 from the cache, row n from k_new), rounded to the
-// element type; the scan reads only rows of earlier chunks, decode_attend reads this one.
+// element type; the scan reads only rows of earlier chunks, decode_attend reads this one.  With LF
+// the grid has one workgroup more than there are slices, and that last one appends (so the slices
+// do not wait for the mean).
 template <typename T, int D, bool LF>
 __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ q, const T* __restrict__ k_new,
                                                           const T* __restrict__ v_new, T* __restrict__ Kc,
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ 
   constexpr int ROUNDS = DEC_ROWS / RPR;
   const int s = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int c = (int)(n / 64);
-  if (s == 0) {
+  if (LF ? s == (int)gridDim.x - 1 : s == 0) {
     // append the new key and value (idempotent)
     for (int e = tid; e < D; e += 256) {
       Kc[((int64_t)bh * Lmax + n) * D + e] = k_new[(int64_t)bh * D + e];
@@ -88,7 +90,11 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ 
       const int64_t r0 = (int64_t)bh * Lmax + (int64_t)c * 64;
       const int cnt = (int)(n - (int64_t)c * 64);  // cached rows of the open chunk before row n
       float acc = 0.f;
-      for (int r = g; r < cnt; r += G) acc += Elem<T>::to_f32(Kc, (r0 + r) * D + e);
+#pragma unroll
+      for (int i = 0; i < 64 / G; ++i) {
+        const int r = g + i * G;
+        if (r < cnt) acc += Elem<T>::to_f32(Kc, (r0 + r) * D + e);
+      }
       lfp[g][e] = acc;
       __syncthreads();
       if (g == 0) {
@@ -424,7 +430,7 @@ static hipError_t decode_t(const void* q, const void* qr, const void* k_new, con
   // the landmark scores use the retrieval query (the attention query when none is given)
   const T* qs = (const T*)(qr ? qr : q);
   if (lf)
-    HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D, true>), dim3(S > 0 ? S : 1, BH), dim3(256), 0, st, qs,
+    HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D, true>), dim3(S + 1, BH), dim3(256), 0, st, qs,
                 (const T*)k_new, (const T*)v_new, (T*)Kc, (T*)Vc, (const T*)Klm, (T*)Klm, ws.lists, n, Lmax, Nmax,
                 scale);
   else

@@ -6,11 +6,12 @@
 //   chunk_mean  one workgroup per (chunk, head): 16-byte loads of the chunk's 64 key rows, fp32
 //               sums per row group, the groups added in LDS, times 1/64 (exact), rounded to the
 //               element type.  Reads the keys once (HBM-bound, 2d B per key row for bf16).
-//   lf_own      one workgroup per (chunk, head), after the selection: prefix means of the chunk's
-//               keys in LDS (one sequential fp32 pass per element), the own-chunk score of each
-//               query against its prefix mean (four lanes per query), then the own slot's score
-//               and the fusion weights rewritten from the kept past scores.  Reads Q (or the
-//               retrieval queries) and K once, and the selection outputs once.
+//   lf_own      one workgroup per (chunk, head), after the selection: the lanes first request their
+//               query elements and kept past scores, then prefix means of the chunk's keys in LDS
+//               (fp32, row segments scanned at once), the own-chunk score of each query against its
+//               prefix mean (four lanes per query), and the own slot's score and the fusion
+//               weights rewritten.  Reads Q (or the retrieval queries) and K once, and the
+//               selection outputs once.
 #include "hils_device.h"
 #include "hils_launch.h"
 
@@ -59,10 +60,30 @@ __global__ __launch_bounds__(256) void lf_own_kernel(const T* __restrict__ Qs, c
   constexpr int PIECES = D / EPP;
   constexpr int RPR = 256 / PIECES;  // key rows per staging round
   constexpr int KS = D + 1;          // padded LDS row
+  constexpr int EQ = D / 4;          // query elements per lane (four lanes per query)
+  constexpr int SEG = 256 / D;       // row segments of the prefix scan
+  constexpr int RS = 64 / SEG;       // rows per segment
   const int c = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int64_t row0 = (int64_t)bh * L + (int64_t)c * 64;
+  const int q = tid >> 2, part = tid & 3;
+  const int k1 = k + 1;
+  const int64_t base = (row0 + q) * k1;
   __shared__ float km[64 * KS];
-  // stage the chunk's keys as fp32
+  __shared__ float segsum[SEG][D];
+  // this lane's query elements and kept past slots are requested first
+  int4 qraw[EQ / EPP];
+#pragma unroll
+  for (int v = 0; v < EQ / EPP; ++v)
+    qraw[v] = *reinterpret_cast<const int4*>(Qs + (row0 + q) * D + part * EQ + v * EPP);
+  int ix[4];
+  float sv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = part + 4 * i;
+    ix[i] = r < k ? idx[base + r] : -1;
+    sv[i] = r < k ? sel[base + r] : 0.f;
+  }
+  // the chunk's keys as fp32
   {
     const int piece = tid % PIECES, rr = tid / PIECES;
 #pragma unroll
@@ -76,53 +97,63 @@ __global__ __launch_bounds__(256) void lf_own_kernel(const T* __restrict__ Qs, c
     }
   }
   __syncthreads();
-  // prefix means, rounded to the element type like a landmark row
-  for (int e = tid; e < D; e += 256) {
-    float s = 0.f;
-    for (int r = 0; r < 64; ++r) {
-      s += km[r * KS + e];
+  // prefix sums per element: SEG row segments scanned at once, then offset by the earlier segments
+  {
+    const int e = tid % D, sg = tid / D;
+    float run = 0.f;
+#pragma unroll
+    for (int i = 0; i < RS; ++i) {
+      const int r = sg * RS + i;
+      run += km[r * KS + e];
+      km[r * KS + e] = run;
+    }
+    segsum[sg][e] = run;
+    __syncthreads();
+    float off = 0.f;
+    for (int j = 0; j < sg; ++j) off += segsum[j][e];
+#pragma unroll
+    for (int i = 0; i < RS; ++i) {
+      const int r = sg * RS + i;
+      // the causal mean of rows 0..r, rounded to the element type like a landmark row
       T m[1];
-      Elem<T>::store(m, 0, s / (float)(r + 1));
+      Elem<T>::store(m, 0, (km[r * KS + e] + off) / (float)(r + 1));
       km[r * KS + e] = Elem<T>::to_f32(m, 0);
     }
   }
   __syncthreads();
-  // own-chunk score of each query, then its fusion weights (four lanes per query)
-  const int q = tid >> 2, part = tid & 3;
-  constexpr int EQ = D / 4;  // elements per lane
-  const T* qp = Qs + (row0 + q) * D + part * EQ;
+  // own-chunk score of each query, then its fusion weights
   float dot = 0.f;
 #pragma unroll
   for (int v = 0; v < EQ / EPP; ++v) {
-    const int4 raw = *reinterpret_cast<const int4*>(qp + v * EPP);
     T vals[EPP];
-    __builtin_memcpy(vals, &raw, 16);
+    __builtin_memcpy(vals, &qraw[v], 16);
 #pragma unroll
     for (int e = 0; e < EPP; ++e) dot += Elem<T>::to_f32(vals, e) * km[q * KS + part * EQ + v * EPP + e];
   }
   dot += lane_xor(dot, 1);
   dot += lane_xor(dot, 2);
   const float s_own = scale * dot;
-  const int k1 = k + 1;
-  const int64_t base = (row0 + q) * k1;
   float mx = s_own;
-  for (int r = part; r < k; r += 4)
-    if (idx[base + r] >= 0) mx = fmaxf(mx, sel[base + r]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (ix[i] >= 0) mx = fmaxf(mx, sv[i]);
   mx = fmaxf(mx, lane_xor(mx, 1));
   mx = fmaxf(mx, lane_xor(mx, 2));
   float den = part == 0 ? __expf(s_own - mx) : 0.f;
-  for (int r = part; r < k; r += 4)
-    if (idx[base + r] >= 0) den += __expf(sel[base + r] - mx);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (ix[i] >= 0) den += __expf(sv[i] - mx);
   den += lane_xor(den, 1);
   den += lane_xor(den, 2);
   const float inv = 1.f / den;
-  for (int r = part; r <= k; r += 4) {
-    if (r == k) {
-      sel[base + r] = s_own;
-      w[base + r] = __expf(s_own - mx) * inv;
-    } else {
-      w[base + r] = idx[base + r] >= 0 ? __expf(sel[base + r] - mx) * inv : 0.f;
-    }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = part + 4 * i;
+    if (r < k) w[base + r] = ix[i] >= 0 ? __expf(sv[i] - mx) * inv : 0.f;
+  }
+  if (part == (k & 3)) {
+    sel[base + k] = s_own;
+    w[base + k] = __expf(s_own - mx) * inv;
   }
 }
 
