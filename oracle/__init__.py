@@ -79,6 +79,9 @@ def _load():
     lib.oracle_fwd_lf.restype = ip
     lib.oracle_decode_lf.argtypes = lib.oracle_decode.argtypes
     lib.oracle_decode_lf.restype = ip
+    lib.oracle_bwd_lf.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, ip, vp, vp, vp, vp,
+                                  vp, ip]
+    lib.oracle_bwd_lf.restype = ip
     _lib = lib
     return lib
 
@@ -275,6 +278,33 @@ def bwd(Q, K, V, Klm, dO, idx, C, k, scale=None, nthreads=0, Q_ret=None):
     dQr = np.empty((B, H, L, d), np.float64) if Qr is not None else None
     used = _load().oracle_bwd(_p(Q), _p(Qr), _p(K), _p(V), _p(Klm), _p(dO), _p(idx), B, H, L, d, C, k, scale,
                               _dt(Q, K, V, Klm, dO), _p(dQ), _p(dQr), _p(dK), _p(dV), _p(dKlm), nthreads)
+    out = {"dQ": dQ, "dK": dK, "dV": dV, "dKlm": dKlm, "threads": used}
+    if Qr is not None:
+        out["dQ_ret"] = dQr
+    return out
+
+
+def bwd_lf(Q, K, V, dO, idx, C, k, scale=None, nthreads=0, Q_ret=None):
+    """Backward of ``fwd_lf`` with the selection fixed by idx: dQ, dK, dV [B,H,L,d] (float64), dK including the
+    landmark paths (the key means), and dKlm [B,H,N,d], the gradient with respect to the past chunks' means.
+    With ``Q_ret`` the score gradients go to ``dQ_ret``."""
+    Q, K, V, dO = _c(Q), _c(K), _c(V), _c(dO)
+    Qr = _c(Q_ret) if Q_ret is not None else None
+    if Qr is not None and (Qr.shape != Q.shape or Qr.dtype != Q.dtype):
+        raise ValueError("Q_ret must match Q in shape and type")
+    B, H, L, d = Q.shape
+    if L % C:
+        raise ValueError("L must be a multiple of C")
+    N = L // C
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    idx = _c(np.asarray(idx, np.int32))
+    dQ, dK, dV = (np.empty((B, H, L, d), np.float64) for _ in range(3))
+    dKlm = np.empty((B, H, N, d), np.float64)
+    dQr = np.empty((B, H, L, d), np.float64) if Qr is not None else None
+    used = _load().oracle_bwd_lf(_p(Q), _p(Qr), _p(K), _p(V), _p(dO), _p(idx), B, H, L, d, C, k, scale,
+                                 _dt(Q, K, V, dO), _p(dQ), _p(dQr), _p(dK), _p(dV), _p(dKlm), nthreads)
+    if used < 0:
+        raise ValueError("unsupported shape")
     out = {"dQ": dQ, "dK": dK, "dV": dV, "dKlm": dKlm, "threads": used}
     if Qr is not None:
         out["dQ_ret"] = dQr

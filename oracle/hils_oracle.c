@@ -413,12 +413,12 @@ int oracle_decode_lf(const void* q, const void* qr, const void* k_new, const voi
  * then give dQr_t = scale sum_j ds_j Klm_j (written to dQr, [B,H,L,d]) and
  * dKlm_j += scale ds_j qr_t, and dQ keeps the in-chunk terms only.
  */
-int oracle_bwd(const void* Q, const void* Qr, const void* K, const void* V, const void* Klm, const void* dO,
-               const int32_t* idx_in, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
-               int64_t k, double scale, int dt, double* dQ, double* dQr, double* dK, double* dV, double* dKlm,
-               int nthreads) {
+static int bwd_common(const void* Q, const void* Qr, const void* K, const void* V, const void* Klm, int lf,
+                      const void* dO, const int32_t* idx_in, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
+                      int64_t k, double scale, int dt, double* dQ, double* dQr, double* dK, double* dV,
+                      double* dKlm, int nthreads) {
   int64_t N = (L + C - 1) / C;
-  prob_t P = {Q, K, V, Klm, Qr, B, H, L, d, C, k, N, L, N, scale, dt};
+  prob_t P = {Q, K, V, Klm, Qr, B, H, L, d, C, k, N, L, N, scale, dt, lf};
   int used = set_threads(nthreads);
   int64_t k1 = k + 1;
   memset(dQ, 0, sizeof(double) * (size_t)(B * H * L * d));
@@ -462,9 +462,21 @@ int oracle_bwd(const void* Q, const void* Qr, const void* K, const void* V, cons
         if (idx[r] < 0) continue;
         int64_t j = idx[r];
         double ds = w[r] * (Dj[r] - D);
-        for (int64_t e = 0; e < d; ++e) {
-          dS[row * d + e] += scale * ds * elem(Klm, (bh * N + j) * d + e, dt);
-          dKlm[(bh * N + j) * d + e] += scale * ds * qrv[e];
+        if (lf && r == k) {
+          /* landmark-free own chunk: the landmark is the mean m of keys jC..t (its rounding
+           * passed straight through), so dS_t += scale ds m and every averaged key gets
+           * scale ds qr_t / count */
+          double m[MAX_D];
+          int64_t cnt = t - j * C + 1;
+          key_mean(K, bh * L + j * C, cnt, d, dt, m);
+          for (int64_t e = 0; e < d; ++e) dS[row * d + e] += scale * ds * m[e];
+          for (int64_t i = j * C; i <= t; ++i)
+            for (int64_t e = 0; e < d; ++e) dK[(bh * L + i) * d + e] += scale * ds * qrv[e] / (double)cnt;
+        } else {
+          for (int64_t e = 0; e < d; ++e) {
+            dS[row * d + e] += scale * ds * elem(Klm, (bh * N + j) * d + e, dt);
+            dKlm[(bh * N + j) * d + e] += scale * ds * qrv[e];
+          }
         }
         int64_t lo = j * C;
         int64_t hi = (j == t / C) ? t : lo + C - 1;
@@ -482,7 +494,39 @@ int oracle_bwd(const void* Q, const void* Qr, const void* K, const void* V, cons
         }
       }
     }
+    if (lf) {
+      /* a past chunk's landmark is the mean of its C keys: each key gets dKlm_j / C */
+      for (int64_t j = 0; j < N; ++j)
+        for (int64_t i = j * C; i < (j + 1) * C && i < L; ++i)
+          for (int64_t e = 0; e < d; ++e) dK[(bh * L + i) * d + e] += dKlm[(bh * N + j) * d + e] / (double)C;
+    }
     free(idx); free(sel); free(w); free(lse); free(o); free(oj); free(Dj); free(abuf); free(g); free(qv); free(qrv);
   }
+  return used;
+}
+
+int oracle_bwd(const void* Q, const void* Qr, const void* K, const void* V, const void* Klm, const void* dO,
+               const int32_t* idx_in, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
+               int64_t k, double scale, int dt, double* dQ, double* dQr, double* dK, double* dV, double* dKlm,
+               int nthreads) {
+  return bwd_common(Q, Qr, K, V, Klm, 0, dO, idx_in, B, H, L, d, C, k, scale, dt, dQ, dQr, dK, dV, dKlm, nthreads);
+}
+
+/*
+ * Backward of the landmark-free forward (selection fixed by idx): the landmarks are the key
+ * means (formed here, as the forward forms them), so the score gradients reach the keys.
+ * dKlm receives the gradient with respect to the past chunks' means (already folded into dK).
+ */
+int oracle_bwd_lf(const void* Q, const void* Qr, const void* K, const void* V, const void* dO,
+                  const int32_t* idx_in, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
+                  int64_t k, double scale, int dt, double* dQ, double* dQr, double* dK, double* dV, double* dKlm,
+                  int nthreads) {
+  if (L % C || d > MAX_D) return -1;
+  int64_t N = L / C;
+  void* Klm = malloc((size_t)(B * H * N * d) * (dt == DT_F32 ? 4 : 2));
+  oracle_chunk_means(K, L, Klm, N, B, H, N, d, C, dt, nthreads);
+  int used = bwd_common(Q, Qr, K, V, Klm, 1, dO, idx_in, B, H, L, d, C, k, scale, dt, dQ, dQr, dK, dV, dKlm,
+                        nthreads);
+  free(Klm);
   return used;
 }

@@ -564,3 +564,35 @@ def test_landmark_free_decode_matches_prefill_rows(oracle_mod, dtype):
     # rows of the chunks completed meanwhile hold their key means
     done = L // C
     np.testing.assert_array_equal(Klm[:, :, :done], _np_means(Kc[:, :, :done * C], C))
+
+
+@pytest.mark.parametrize("qret", [False, True])
+def test_landmark_free_central_differences(oracle_mod, qret):
+    """fp32 inputs, so that a key perturbation moves the (fp32-rounded) means."""
+    B, H, L, d, C, k = 1, 1, 256, 8, 64, 2
+    x = rand_inputs(B, H, L, d, C=C, seed=44 + qret, dtype="f32", with_dO=True, with_qret=qret)
+    G = x["dO"]
+    Qr = x["Q_ret"] if qret else None
+    idx = oracle_mod.fwd_lf(x["Q"], x["K"], x["V"], C, k, Q_ret=Qr)["idx"]
+    g = oracle_mod.bwd_lf(x["Q"], x["K"], x["V"], G, idx, C, k, Q_ret=Qr)
+    h = 2.0 ** -10
+    rng = np.random.default_rng(2)
+    names = {"Q": "dQ", "K": "dK", "V": "dV"}
+    if qret:
+        names["Q_ret"] = "dQ_ret"
+    for name, gname in names.items():
+        for _ in range(12):
+            pos = tuple(int(rng.integers(0, s)) for s in x[name].shape)
+            vals = []
+            for sgn in (1, -1):
+                p = {n: x[n] for n in names}
+                a = x[name].copy()
+                a[pos] = np.float32(a[pos] + sgn * h)
+                p[name] = a
+                O = oracle_mod.fwd_lf(p["Q"], p["K"], p["V"], C, k, idx=idx, Q_ret=p.get("Q_ret"))["O"]
+                vals.append(float(np.sum(O * G.astype(np.float64))))
+            fd = (vals[0] - vals[1]) / (2 * h)
+            an = g[gname][pos]
+            assert abs(fd - an) <= 2e-4 * max(1.0, abs(an)), (name, pos, fd, an)
+    # the past chunks' mean gradient is returned beside dK (which already holds it)
+    assert np.abs(g["dKlm"]).max() > 0
