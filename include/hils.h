@@ -219,7 +219,14 @@ hils_status hils_sparse_attn_bwd_rq(const void* Q, const void* Q_ret, const void
  *                            included) before reading it; rows of earlier
  *                            chunks must hold their key means (from
  *                            hils_chunk_means or from earlier steps).
- * The backward pass of landmark-free chunks is not provided.
+ *   hils_sparse_attn_bwd_lf: as hils_sparse_attn_bwd_rq for the forward
+ *                            above: K_lm is that forward's K_lm_out; dK also
+ *                            carries the landmark paths (each past chunk's
+ *                            mean gradient / C to its keys, and the own
+ *                            slot's gradient to the keys it averaged, the
+ *                            rounding of the means passed straight through);
+ *                            dK_lm [B][H][N][d] float receives the past
+ *                            chunks' mean gradient (already inside dK).
  */
 hils_status hils_chunk_means(const void* K, void* K_lm, int64_t B, int64_t H, int64_t L_k, int64_t N_lm,
                              int64_t n_chunks, int64_t d, int64_t C, hils_dtype dt, void* stream);
@@ -228,6 +235,11 @@ hils_status hils_sparse_attn_fwd_lf(const void* Q, const void* Q_ret, const void
                                     float* lse_out, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
                                     int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
                                     void* stream);
+hils_status hils_sparse_attn_bwd_lf(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm,
+                                    const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
+                                    float* dQ_ret, float* dK, float* dV, float* dK_lm, int64_t B, int64_t H,
+                                    int64_t L, int64_t d, int64_t C, int64_t topk, float scale, hils_dtype dt,
+                                    void* ws, size_t ws_bytes, void* stream);
 hils_status hils_decode_step_lf(const void* q, const void* q_ret, const void* k_new, const void* v_new,
                                 void* K_cache, void* V_cache, void* K_lm_cache, int64_t n_ctx, int64_t L_max,
                                 void* o, int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C,

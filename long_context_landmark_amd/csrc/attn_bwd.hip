@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* __restri
                                                         const int32_t* __restrict__ idx, const float* __restrict__ w,
                                                         const T* __restrict__ Klm, float* __restrict__ ds_out,
                                                         float* __restrict__ dQ, float* __restrict__ dQr, int64_t rows,
-                                                        int L, int N, int k, float scale) {
+                                                        int L, int N, int k, float scale, int lf) {
   constexpr int V8 = D / 8;                    // threads per row
   constexpr int LW = 2 * Elem<T>::bytes;       // 32-bit words of eight landmark elements
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -374,7 +374,8 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* __restri
     }
   }
   // RQ: the landmark scores came from separate retrieval queries, whose gradient (the
-  // ds * Klm terms) goes to dQr; dQ then keeps the in-chunk attention terms only
+  // ds * Klm terms) goes to dQr; dQ then keeps the in-chunk attention terms only.
+  // lf (landmark-free chunks): the own slot's landmark is not a K_lm row; lf_bwd adds its term
   float acc[8], accr[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = accr[e] = 0.f;
@@ -383,6 +384,7 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* __restri
     if (!ok[r]) continue;
     const float ds = wr[r] * (dr[r] - Dsum);
     if (c8 == 0) ds_out[row * k1 + r] = ds;
+    const float sds = (lf && r == k) ? 0.f : scale * ds;
     _Float16 h[8];
     __builtin_memcpy(h, &raw[r], 16);
     T lm[8];
@@ -391,9 +393,9 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* __restri
     for (int e = 0; e < 8; ++e) {
       if (RQ) {
         acc[e] += (float)h[e];
-        accr[e] += scale * ds * Elem<T>::to_f32(lm, e);
+        accr[e] += sds * Elem<T>::to_f32(lm, e);
       } else {
-        acc[e] += (float)h[e] + scale * ds * Elem<T>::to_f32(lm, e);
+        acc[e] += (float)h[e] + sds * Elem<T>::to_f32(lm, e);
       }
     }
   }
@@ -413,7 +415,8 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* __restri
 template <typename T, int D>
 __global__ __launch_bounds__(256) void klm_bwd_kernel(const T* __restrict__ Q, const float* __restrict__ ds,
                                                       const int* __restrict__ chunk_off, const int* __restrict__ pairs,
-                                                      float* __restrict__ dKlm, int L, int N, int k, float scale) {
+                                                      float* __restrict__ dKlm, int L, int N, int k, float scale,
+                                                      int lf) {
   constexpr int QD = D / 4;                   // elements per thread
   constexpr int EPP = 16 / Elem<T>::bytes;    // elements per 16-byte load
   __shared__ float red[64][D + 1];
@@ -429,7 +432,9 @@ __global__ __launch_bounds__(256) void klm_bwd_kernel(const T* __restrict__ Q, c
   float acc[QD];
 #pragma unroll
   for (int e = 0; e < QD; ++e) acc[e] = 0.f;
-  for (int tile = 0; tile < ntiles; ++tile) {
+  // tile 0 holds the chunk's own queries (their own slot), which do not score K_lm_j when chunks are
+  // landmark-free
+  for (int tile = lf ? 1 : 0; tile < ntiles; ++tile) {
     int t, slot;
     bool valid = true;
     if (tile == 0) {
@@ -466,7 +471,7 @@ __global__ __launch_bounds__(256) void klm_bwd_kernel(const T* __restrict__ Q, c
 }
 
 template <typename T, int D>
-static hipError_t bwd_t(const void* Q, const void* Qr, const void* K, const void* V, const void* Klm,
+static hipError_t bwd_t(const void* Q, const void* Qr, const void* K, const void* V, const void* Klm, bool lf,
                         const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ, float* dQr,
                         float* dK, float* dV, float* dKlm, int BH, int L, int N, int k, float scale,
                         const BwdBufs& ws, hipStream_t st) {
@@ -480,35 +485,41 @@ static hipError_t bwd_t(const void* Q, const void* Qr, const void* K, const void
   const bool rq = Qr != nullptr;
   if (k <= 8 && !rq)
     HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 9, false>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx,
-                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale);
+                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, (int)lf);
   else if (!rq)
     HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 17, false>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx,
-                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale);
+                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, (int)lf);
   else if (k <= 8)
     HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 9, true>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx,
-                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale);
+                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, (int)lf);
   else
     HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 17, true>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx,
-                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale);
+                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, (int)lf);
   // dKlm_j sums ds_tj times the query that scored the landmark
   HILS_LAUNCH("klm_bwd", (klm_bwd_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)(rq ? Qr : Q), ws.ds,
-              ws.rb.chunk_off, ws.rb.pairs, dKlm, L, N, k, scale);
+              ws.rb.chunk_off, ws.rb.pairs, dKlm, L, N, k, scale, (int)lf);
+  if (lf) {
+    hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return e2;
+    return launch_lf_bwd(Elem<T>::bytes == 2 ? 0 : 1, D, rq ? Qr : Q, K, ws.ds, dKlm, rq ? dQr : dQ, dK, BH, L, N,
+                         k, scale, st);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd(int dt, int d, const void* Q, const void* Qr, const void* K, const void* V, const void* Klm,
-                      const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ, float* dQr,
-                      float* dK, float* dV, float* dKlm, int BH, int L, int N, int k, float scale, const BwdBufs& ws,
-                      hipStream_t st) {
+                      bool lf, const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
+                      float* dQr, float* dK, float* dV, float* dKlm, int BH, int L, int N, int k, float scale,
+                      const BwdBufs& ws, hipStream_t st) {
   if ((Qr == nullptr) != (dQr == nullptr)) return hipErrorInvalidValue;
   if (dt == 0)
-    return d == 64 ? bwd_t<bf16_t, 64>(Q, Qr, K, V, Klm, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k, scale,
-                                       ws, st)
-                   : bwd_t<bf16_t, 128>(Q, Qr, K, V, Klm, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k, scale,
-                                        ws, st);
+    return d == 64 ? bwd_t<bf16_t, 64>(Q, Qr, K, V, Klm, lf, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k,
+                                       scale, ws, st)
+                   : bwd_t<bf16_t, 128>(Q, Qr, K, V, Klm, lf, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k,
+                                        scale, ws, st);
   // fp32 inputs: head dim 64 only (the fp32 LDS tiles of d = 128 exceed a workgroup's LDS)
   if (d != 64) return hipErrorInvalidValue;
-  return bwd_t<float, 64>(Q, Qr, K, V, Klm, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k, scale, ws, st);
+  return bwd_t<float, 64>(Q, Qr, K, V, Klm, lf, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k, scale, ws, st);
 }
 
 }  // namespace hils

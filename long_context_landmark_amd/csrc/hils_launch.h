@@ -77,10 +77,16 @@ struct BwdBufs {
 };
 // Qr / dQr: retrieval queries that scored the landmarks and their gradient (both null: Q scored them,
 // and dQ takes the whole gradient)
+// lf: landmark-free chunks (Klm holds the key means); the score gradients are carried into dK as well,
+// and dKlm receives the past chunks' mean gradient
 hipError_t launch_bwd(int dt, int d, const void* Q, const void* Qr, const void* K, const void* V, const void* Klm,
-                      const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ, float* dQr,
-                      float* dK, float* dV, float* dKlm, int BH, int L, int N, int k, float scale, const BwdBufs& ws,
-                      hipStream_t st);
+                      bool lf, const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
+                      float* dQr, float* dK, float* dV, float* dKlm, int BH, int L, int N, int k, float scale,
+                      const BwdBufs& ws, hipStream_t st);
+// landmark-free backward tail, per (chunk, head): the own slot's ds against the causal means into dQs, and
+// the mean paths (own slots and the past chunk's dKlm) into dK
+hipError_t launch_lf_bwd(int dt, int d, const void* Qs, const void* K, const float* ds, const float* dKlm, float* dQs,
+                         float* dK, int BH, int L, int N, int k, float scale, hipStream_t st);
 // qr: retrieval query for the landmark scores (null: q).  lf: landmark-free chunks, the step writes
 // the open chunk's landmark row (the mean of its keys so far) before it is read
 hipError_t launch_decode(int dt, int d, const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc,

@@ -12,6 +12,9 @@
 //               prefix mean (four lanes per query), and the own slot's score and the fusion
 //               weights rewritten.  Reads Q (or the retrieval queries) and K once, and the
 //               selection outputs once.
+//   lf_bwd      the backward's tail, per (chunk, head): the own slot's score gradient against the
+//               causal means into dQ (or dQ_ret), and the mean paths into dK (reverse prefix sums
+//               over the chunk's queries plus the past chunk's mean gradient / 64).
 #include "hils_device.h"
 #include "hils_launch.h"
 
@@ -52,17 +55,62 @@ __global__ __launch_bounds__(256) void chunk_mean_kernel(const T* __restrict__ K
   }
 }
 
+// The chunk's keys (rows row0 .. row0+63) staged as fp32 in km (row stride D + 1), then replaced by
+// their causal means: row r becomes the mean of rows 0..r, rounded to the element type like a
+// landmark row.  The prefix sums run as 256/D row segments at once, offset by the earlier segments.
+// Ends with a barrier.
+template <typename T, int D>
+__device__ __forceinline__ void stage_prefix_means(const T* __restrict__ K, int64_t row0, float* km,
+                                                   float (*segsum)[D], int tid) {
+  constexpr int EPP = 16 / Elem<T>::bytes;
+  constexpr int PIECES = D / EPP;
+  constexpr int RPR = 256 / PIECES;
+  constexpr int KS = D + 1;
+  constexpr int SEG = 256 / D;
+  constexpr int RS = 64 / SEG;
+  {
+    const int piece = tid % PIECES, rr = tid / PIECES;
+#pragma unroll
+    for (int r0 = 0; r0 < 64; r0 += RPR) {
+      const int r = r0 + rr;
+      const int4 raw = *reinterpret_cast<const int4*>(K + (row0 + r) * D + piece * EPP);
+      T vals[EPP];
+      __builtin_memcpy(vals, &raw, 16);
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) km[r * KS + piece * EPP + e] = Elem<T>::to_f32(vals, e);
+    }
+  }
+  __syncthreads();
+  const int e = tid % D, sg = tid / D;
+  float run = 0.f;
+#pragma unroll
+  for (int i = 0; i < RS; ++i) {
+    const int r = sg * RS + i;
+    run += km[r * KS + e];
+    km[r * KS + e] = run;
+  }
+  segsum[sg][e] = run;
+  __syncthreads();
+  float off = 0.f;
+  for (int j = 0; j < sg; ++j) off += segsum[j][e];
+#pragma unroll
+  for (int i = 0; i < RS; ++i) {
+    const int r = sg * RS + i;
+    T m[1];
+    Elem<T>::store(m, 0, (km[r * KS + e] + off) / (float)(r + 1));
+    km[r * KS + e] = Elem<T>::to_f32(m, 0);
+  }
+  __syncthreads();
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void lf_own_kernel(const T* __restrict__ Qs, const T* __restrict__ K,
                                                      const int32_t* __restrict__ idx, float* __restrict__ sel,
                                                      float* __restrict__ w, int L, int k, float scale) {
   constexpr int EPP = 16 / Elem<T>::bytes;
-  constexpr int PIECES = D / EPP;
-  constexpr int RPR = 256 / PIECES;  // key rows per staging round
-  constexpr int KS = D + 1;          // padded LDS row
-  constexpr int EQ = D / 4;          // query elements per lane (four lanes per query)
-  constexpr int SEG = 256 / D;       // row segments of the prefix scan
-  constexpr int RS = 64 / SEG;       // rows per segment
+  constexpr int KS = D + 1;     // padded LDS row
+  constexpr int EQ = D / 4;     // query elements per lane (four lanes per query)
+  constexpr int SEG = 256 / D;  // row segments of the prefix scan
   const int c = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int64_t row0 = (int64_t)bh * L + (int64_t)c * 64;
   const int q = tid >> 2, part = tid & 3;
@@ -83,44 +131,7 @@ __global__ __launch_bounds__(256) void lf_own_kernel(const T* __restrict__ Qs, c
     ix[i] = r < k ? idx[base + r] : -1;
     sv[i] = r < k ? sel[base + r] : 0.f;
   }
-  // the chunk's keys as fp32
-  {
-    const int piece = tid % PIECES, rr = tid / PIECES;
-#pragma unroll
-    for (int r0 = 0; r0 < 64; r0 += RPR) {
-      const int r = r0 + rr;
-      const int4 raw = *reinterpret_cast<const int4*>(K + (row0 + r) * D + piece * EPP);
-      T vals[EPP];
-      __builtin_memcpy(vals, &raw, 16);
-#pragma unroll
-      for (int e = 0; e < EPP; ++e) km[r * KS + piece * EPP + e] = Elem<T>::to_f32(vals, e);
-    }
-  }
-  __syncthreads();
-  // prefix sums per element: SEG row segments scanned at once, then offset by the earlier segments
-  {
-    const int e = tid % D, sg = tid / D;
-    float run = 0.f;
-#pragma unroll
-    for (int i = 0; i < RS; ++i) {
-      const int r = sg * RS + i;
-      run += km[r * KS + e];
-      km[r * KS + e] = run;
-    }
-    segsum[sg][e] = run;
-    __syncthreads();
-    float off = 0.f;
-    for (int j = 0; j < sg; ++j) off += segsum[j][e];
-#pragma unroll
-    for (int i = 0; i < RS; ++i) {
-      const int r = sg * RS + i;
-      // the causal mean of rows 0..r, rounded to the element type like a landmark row
-      T m[1];
-      Elem<T>::store(m, 0, (km[r * KS + e] + off) / (float)(r + 1));
-      km[r * KS + e] = Elem<T>::to_f32(m, 0);
-    }
-  }
-  __syncthreads();
+  stage_prefix_means<T, D>(K, row0, km, segsum, tid);
   // own-chunk score of each query, then its fusion weights
   float dot = 0.f;
 #pragma unroll
@@ -155,6 +166,93 @@ __global__ __launch_bounds__(256) void lf_own_kernel(const T* __restrict__ Qs, c
     sel[base + k] = s_own;
     w[base + k] = __expf(s_own - mx) * inv;
   }
+}
+
+// Backward tail of landmark-free chunks, per (chunk c, head), after klm_bwd:
+//   own slot:  dQs_t += scale ds_t,own m_t (m_t the causal mean the forward used), and each key i <= t
+//              of the chunk gets scale ds_t,own qs_t / (t - 64c + 1): a reverse prefix sum over t;
+//   past use:  each key of the chunk gets dKlm_c / 64 (dKlm_c from klm_bwd, past pairs only).
+// The rounding of the means is passed straight through.  dQs and dK are read, added to and written.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void lf_bwd_kernel(const T* __restrict__ Qs, const T* __restrict__ K,
+                                                     const float* __restrict__ ds, const float* __restrict__ dKlm,
+                                                     float* __restrict__ dQs, float* __restrict__ dK, int L, int N,
+                                                     int k, float scale) {
+  constexpr int EPP = 16 / Elem<T>::bytes;
+  constexpr int KS = D + 1;
+  constexpr int EQ = D / 4;
+  constexpr int SEG = 256 / D;
+  constexpr int RS = 64 / SEG;
+  const int c = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int64_t row0 = (int64_t)bh * L + (int64_t)c * 64;
+  const int q = tid >> 2, part = tid & 3;
+  __shared__ float km[64 * KS];
+  __shared__ float gm[64 * KS];
+  __shared__ float segsum[SEG][D];
+  int4 qraw[EQ / EPP];
+#pragma unroll
+  for (int v = 0; v < EQ / EPP; ++v)
+    qraw[v] = *reinterpret_cast<const int4*>(Qs + (row0 + q) * D + part * EQ + v * EPP);
+  const float sds = scale * ds[(row0 + q) * (k + 1) + k];
+  stage_prefix_means<T, D>(K, row0, km, segsum, tid);
+  // own-slot term of dQs, and g_t = scale ds_t qs_t / (t + 1) for the keys
+  {
+    float* dq = dQs + (row0 + q) * D + part * EQ;
+    const float inv_cnt = 1.f / (float)(q + 1);
+#pragma unroll
+    for (int v = 0; v < EQ / EPP; ++v) {
+      T vals[EPP];
+      __builtin_memcpy(vals, &qraw[v], 16);
+#pragma unroll
+      for (int e4 = 0; e4 < EPP; e4 += 4) {
+        float4 a = *reinterpret_cast<float4*>(dq + v * EPP + e4);
+        const int eb = part * EQ + v * EPP + e4;
+        a.x += sds * km[q * KS + eb];
+        a.y += sds * km[q * KS + eb + 1];
+        a.z += sds * km[q * KS + eb + 2];
+        a.w += sds * km[q * KS + eb + 3];
+        *reinterpret_cast<float4*>(dq + v * EPP + e4) = a;
+      }
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) gm[q * KS + part * EQ + v * EPP + e] = sds * Elem<T>::to_f32(vals, e) * inv_cnt;
+    }
+  }
+  __syncthreads();
+  // key i receives sum over t >= i of g_t: reverse prefix sums in SEG row segments, offset by the later ones
+  const int e = tid % D, sg = tid / D;
+  float run = 0.f;
+#pragma unroll
+  for (int i = RS - 1; i >= 0; --i) {
+    const int r = sg * RS + i;
+    run += gm[r * KS + e];
+    gm[r * KS + e] = run;
+  }
+  segsum[sg][e] = run;
+  __syncthreads();
+  float off = dKlm[((int64_t)bh * N + c) * D + e] * (1.f / 64.f);
+  for (int j = sg + 1; j < SEG; ++j) off += segsum[j][e];
+#pragma unroll
+  for (int i = 0; i < RS; ++i) {
+    const int r = sg * RS + i;
+    dK[(row0 + r) * D + e] += gm[r * KS + e] + off;
+  }
+}
+
+template <typename T, int D>
+static hipError_t lf_bwd_t(const void* Qs, const void* K, const float* ds, const float* dKlm, float* dQs, float* dK,
+                           int BH, int L, int N, int k, float scale, hipStream_t st) {
+  HILS_LAUNCH("lf_bwd", (lf_bwd_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)Qs, (const T*)K, ds, dKlm,
+              dQs, dK, L, N, k, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_lf_bwd(int dt, int d, const void* Qs, const void* K, const float* ds, const float* dKlm, float* dQs,
+                         float* dK, int BH, int L, int N, int k, float scale, hipStream_t st) {
+  if (dt == 0)
+    return d == 64 ? lf_bwd_t<bf16_t, 64>(Qs, K, ds, dKlm, dQs, dK, BH, L, N, k, scale, st)
+                   : lf_bwd_t<bf16_t, 128>(Qs, K, ds, dKlm, dQs, dK, BH, L, N, k, scale, st);
+  return d == 64 ? lf_bwd_t<float, 64>(Qs, K, ds, dKlm, dQs, dK, BH, L, N, k, scale, st)
+                 : lf_bwd_t<float, 128>(Qs, K, ds, dKlm, dQs, dK, BH, L, N, k, scale, st);
 }
 
 template <typename T, int D>

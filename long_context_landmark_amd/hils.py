@@ -43,6 +43,7 @@ _lib.hils_sparse_attn_bwd_rq.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
 _lib.hils_chunk_means.argtypes = [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _int, _vp]
 _lib.hils_sparse_attn_fwd_lf.argtypes = _lib.hils_sparse_attn_fwd_rq.argtypes
 _lib.hils_decode_step_lf.argtypes = _lib.hils_decode_step_rq.argtypes
+_lib.hils_sparse_attn_bwd_lf.argtypes = _lib.hils_sparse_attn_bwd_rq.argtypes
 _lib.hils_profile_enable.argtypes = [_int]
 _lib.hils_profile_enable.restype = None
 _lib.hils_profile_read.argtypes = [ctypes.c_char_p, _int, ctypes.POINTER(ctypes.c_double),
@@ -304,4 +305,24 @@ def sparse_attn_bwd(Q, K, V, K_lm, dO, idx, w, lse, k, C=64, scale=None, ws=None
         _check(_lib.hils_sparse_attn_bwd(_p(Q), *head, _p(dQ), *tail))
         return dQ, dK, dV, dKlm
     _check(_lib.hils_sparse_attn_bwd_rq(_p(Q), _p(Q_ret), *head, _p(dQ), _p(dQr), *tail))
+    return dQ, dQr, dK, dV, dKlm
+
+
+def sparse_attn_bwd_lf(Q, K, V, K_lm, dO, idx, w, lse, k, C=64, scale=None, ws=None, Q_ret=None):
+    """Backward of ``sparse_attn_fwd_lf`` (K_lm: its key means), selection held fixed.  Returns
+    (dQ, dK, dV, dK_lm), or (dQ, dQ_ret, dK, dV, dK_lm) with ``Q_ret``; dK carries the landmark paths and
+    dK_lm is the past chunks' mean gradient (already inside dK)."""
+    _contig(Q, K, V, K_lm, dO, idx, w, lse, Q_ret)
+    _like(Q_ret, Q, "Q_ret")
+    B, H, L, d = _dims(Q, K_lm, C)
+    f32 = dict(dtype=torch.float32, device=Q.device)
+    dQ, dK, dV = (torch.empty((B, H, L, d), **f32) for _ in range(3))
+    dKlm = torch.empty((B, H, L // C, d), **f32)
+    dQr = torch.empty((B, H, L, d), **f32) if Q_ret is not None else None
+    wsb, n = _workspace(OP_BWD, B, H, L, d, C, k, Q.device, ws)
+    _check(_lib.hils_sparse_attn_bwd_lf(_p(Q), _p(Q_ret), _p(K), _p(V), _p(K_lm), _p(dO), _p(idx), _p(w), _p(lse),
+                                        _p(dQ), _p(dQr), _p(dK), _p(dV), _p(dKlm), B, H, L, d, C, k, _scale(d, scale),
+                                        _dt(Q), _p(wsb), n, _stream()))
+    if Q_ret is None:
+        return dQ, dK, dV, dKlm
     return dQ, dQr, dK, dV, dKlm

@@ -143,3 +143,13 @@ def test_landmark_free_entry_points_validate(lib, hils):
     assert lib.hils_decode_step_lf(FAKE, None, *([FAKE] * 5), 1024, 1024, FAKE, FAKE, FAKE, 1, 2, 64, 64, 4,
                                    0.125, 0, FAKE, nd, None) == INVALID
     assert "n_ctx" in lib.hils_last_error().decode()
+
+
+def test_landmark_free_backward_validates(lib, hils):
+    nb = hils.workspace_size(hils.OP_BWD, 1, 2, 1024, 64, 64, 4)
+    dims = [1, 2, 1024, 64, 64, 4, 0.125, 0]
+    # Q_ret without dQ_ret, and the fp32 head-dim limit
+    assert lib.hils_sparse_attn_bwd_lf(FAKE, FAKE, *([FAKE] * 8), None, *([FAKE] * 3), *dims, FAKE, nb,
+                                       None) == INVALID
+    assert lib.hils_sparse_attn_bwd_lf(FAKE, None, *([FAKE] * 8), None, *([FAKE] * 3), 1, 2, 1024, 128, 64, 4,
+                                       0.125, 1, FAKE, nb, None) == UNSUPPORTED

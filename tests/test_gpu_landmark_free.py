@@ -128,3 +128,24 @@ def test_decode_landmark_free(hils, gpu, dtype, B, H, d, ctx, steps, k, rq):
     # the landmark rows the steps maintained
     last = (ctx + steps - 1) // 64
     _means_close(host(Klm_g)[:, :, :last + 1], Klm_h[:, :, :last + 1], dtype, "K_lm cache")
+
+
+@pytest.mark.parametrize("dtype,B,H,L,d,k,rq", [
+    ("bf16", 1, 2, 2112, 64, 8, False),
+    ("bf16", 1, 2, 1024, 128, 16, False),
+    ("f32", 1, 2, 1024, 64, 4, False),
+    ("bf16", 1, 2, 2112, 64, 8, True),
+])
+def test_bwd_landmark_free(hils, gpu, dtype, B, H, L, d, k, rq):
+    say(f"bwd landmark-free dtype={dtype} B={B} H={H} L={L} d={d} k={k} retrieval={rq}")
+    x = synth.prefill_inputs(B, H, L, d, C=64, seed=630 + L + d + rq, dtype=dtype, with_dO=True, with_qret=rq)
+    t = to_inputs(x, ("Q", "K", "V", "dO") + (("Q_ret",) if rq else ()))
+    O, idx, sel, w, lse, Klm = hils.sparse_attn_fwd_lf(t["Q"], t["K"], t["V"], k, save_for_backward=True,
+                                                       Q_ret=t.get("Q_ret"))
+    grads = hils.sparse_attn_bwd_lf(t["Q"], t["K"], t["V"], Klm, t["dO"], idx, w, lse, k, Q_ret=t.get("Q_ret"))
+    torch.cuda.synchronize()
+    names = ("dQ", "dQ_ret", "dK", "dV", "dKlm") if rq else ("dQ", "dK", "dV", "dKlm")
+    ref = oracle.bwd_lf(x["Q"], x["K"], x["V"], x["dO"], idx.cpu().numpy(), 64, k,
+                        Q_ret=x["Q_ret"] if rq else None)
+    for name, got in zip(names, grads):
+        assert_close(f32(got), ref[name], name, *_tol(dtype))
