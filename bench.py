@@ -128,6 +128,8 @@ def train_work(B, H, L, d, k, C=64):
     kern["chunk_bwd"] = ("hbm", f_bwd, pairs_all * (2 * d * 2 + 4 * d + 12) + BH * N * C * d * (2 * 2 + 4 * 2))
     kern["dq_reduce"] = ("hbm", 0, pairs_all * (4 * d + 2 * d + 12) + BH * L * d * 4)
     kern["klm_bwd"] = ("hbm", 0, pairs_all * (2 * d + 8) + BH * N * d * 4)
+    # landmark-free chunks only: q and k read, dQ and dK read and written, per row
+    kern["lf_bwd"] = ("hbm", 0, BH * L * (2 * d * 2 + 4 + 4 * d * 4) + BH * N * d * 4)
     return {"flops": fw["flops"] + f_bwd, "bytes": fw["bytes"] + b_bwd, "kernels": kern}
 
 
@@ -258,7 +260,7 @@ def bench_prefill(hils, synth, name, steps, warmup, rq=False, lf=False):
     return res
 
 
-def bench_train(hils, synth, name, steps, warmup, rq=False):
+def bench_train(hils, synth, name, steps, warmup, rq=False, lf=False):
     import torch
 
     w = synth.WORKLOADS[name]
@@ -276,6 +278,7 @@ def bench_train(hils, synth, name, steps, warmup, rq=False):
     sel, wt, lse = (torch.empty((B, H, L, k1), **f32) for _ in range(3))
     grads = [torch.empty((B, H, L, d), **f32) for _ in range(3)] + [torch.empty((B, H, L // w.C, d), **f32)]
     dQr = torch.empty((B, H, L, d), **f32) if rq else None
+    klm_lf = torch.empty_like(x["Klm"]) if lf else None
     import ctypes
 
     lib = hils._lib
@@ -284,6 +287,16 @@ def bench_train(hils, synth, name, steps, warmup, rq=False):
     def step():
         s_ = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         scale = 1.0 / math.sqrt(d)
+        if lf:
+            qr = P(x["Q_ret"]) if rq else None
+            hils._check(lib.hils_sparse_attn_fwd_lf(P(x["Q"]), qr, P(x["K"]), P(x["V"]), P(klm_lf), P(idx), P(sel), 1,
+                                                    P(O), P(wt), P(lse), B, H, L, d, w.C, w.k, scale, 0, P(wsf),
+                                                    wsf.numel(), s_))
+            hils._check(lib.hils_sparse_attn_bwd_lf(P(x["Q"]), qr, P(x["K"]), P(x["V"]), P(klm_lf), P(x["dO"]), P(idx),
+                                                    P(wt), P(lse), P(grads[0]), P(dQr) if rq else None,
+                                                    *(P(g_) for g_ in grads[1:]), B, H, L, d, w.C, w.k, scale, 0,
+                                                    P(wsb), wsb.numel(), s_))
+            return
         if not rq:
             hils._check(lib.hils_sparse_attn_fwd(P(x["Q"]), P(x["K"]), P(x["V"]), P(x["Klm"]), P(idx), P(sel), 1,
                                                  P(O), P(wt), P(lse), B, H, L, d, w.C, w.k, scale, 0, P(wsf),
@@ -315,9 +328,10 @@ def bench_train(hils, synth, name, steps, warmup, rq=False):
         "tflops": work["flops"] / (ms * 1e-3) / 1e12,
         "algorithmic_gflop": work["flops"] / 1e9,
         "kernel_us": {n: round(t / c * 1e3, 3) for n, (t, c) in kt.items()},
-        "roofline": roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()}, None if rq else name),
+        "roofline": roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()}, None if rq or lf else name),
         "config": {"workload": name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "C": w.C, "k": w.k,
-                   "step": "forward + backward", **({"retrieval_query": True} if rq else {})},
+                   "step": "forward + backward", **({"retrieval_query": True} if rq else {}),
+                   **({"landmark_free": True} if lf else {})},
     }
     del x, wsf, wsb
     torch.cuda.empty_cache()
@@ -429,7 +443,7 @@ def main():
     ap.add_argument("--only", default="", help="run only this workload (prefill_8k, prefill_128k, decode_512k, "
                                                "train_8k; a _retrieval suffix on a prefill or train workload "
                                                "adds separate retrieval queries, a _landmark_free suffix on a "
-                                               "prefill or decode workload uses key-mean landmarks) and print "
+                                               "prefill, decode or train workload uses key-mean landmarks) and print "
                                                "its result object; for profiling runs")
     ap.add_argument("--decode-replicas", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -466,7 +480,7 @@ def main():
         elif name.startswith("decode"):
             res = bench_decode(hils, synth, name, args.decode_replicas, args.warmup, lf=lf)
         elif name.startswith("train"):
-            res = bench_train(hils, synth, name, args.steps, args.warmup, rq=rq)
+            res = bench_train(hils, synth, name, args.steps, args.warmup, rq=rq, lf=lf)
         else:
             raise SystemExit(f"unknown workload {args.only}")
         print(json.dumps({"workload": args.only, **res}), flush=True)
@@ -504,6 +518,7 @@ def main():
                                                           lf=True)
         extra["decode_512k_landmark_free"] = bench_decode(hils, synth, "decode_512k", args.decode_replicas, 4,
                                                           lf=True)
+        extra["train_8k_landmark_free"] = bench_train(hils, synth, "train_8k", max(3, min(args.steps, 20)), 2, lf=True)
         log(f"[bench] prefill_8k_landmark_free {extra['prefill_8k_landmark_free']['ms_per_step']*1e3:.1f} us/step, "
             f"decode_512k_landmark_free {extra['decode_512k_landmark_free']['us_per_token']:.2f} us/token")
     cpu = None
