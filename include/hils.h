@@ -246,6 +246,36 @@ hils_status hils_decode_step_lf(const void* q, const void* q_ret, const void* k_
                                 int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Batched decode over a paged cache (serving shapes: B sequences at their own
+ * positions, pages of one chunk).  The same step as hils_decode_step_rq /
+ * hils_decode_step_lf (ai-feeds summary "Limitations": the per-step landmark
+ * scan; "Method" > "Key modules" items 1-3) for each sequence b at position
+ * n_ctx[b], with the caches held in page pools:
+ *   K_pages, V_pages : [n_pages][H][64][d] (dt); page p holds, for every head,
+ *                      the 64 key / value rows of one chunk
+ *   K_lm_pages       : [n_pages][H][d] (dt); the landmark row of that chunk
+ *   page_table       : [B][max_pages] int32 (device): pool page of chunk j of
+ *                      sequence b, for every chunk 0 .. n_ctx[b]/64
+ *   n_ctx            : [B] int64 (device): each sequence's position; the new
+ *                      k_new / v_new row is appended at it
+ *   n_ctx_max        : host value >= every n_ctx[b], < max_pages*64; it sizes
+ *                      the landmark scan
+ *   q, q_ret, k_new, v_new: [B][H][d]; o [B][H][d]; idx, w [B][H][k+1]
+ * landmark_free = 1 maintains the open chunk's landmark row as in
+ * hils_decode_step_lf.  The table and positions are read on the device:
+ * positions, chunk indices and page ids outside their ranges are clamped into
+ * them (wrong results, never an access outside the pools); a page must not be
+ * shared by two sequences' open chunks.  Workspace:
+ * hils_workspace_size(HILS_OP_DECODE, B, H, max_pages*64, d, C, topk).
+ */
+hils_status hils_decode_step_paged(const void* q, const void* q_ret, const void* k_new, const void* v_new,
+                                   void* K_pages, void* V_pages, void* K_lm_pages, const int32_t* page_table,
+                                   int64_t n_pages, int64_t max_pages, const int64_t* n_ctx, int64_t n_ctx_max,
+                                   int landmark_free, void* o, int32_t* idx, float* w, int64_t B, int64_t H,
+                                   int64_t d, int64_t C, int64_t topk, float scale, hils_dtype dt, void* ws,
+                                   size_t ws_bytes, void* stream);
+
+/*
  * Optional per-kernel timing, for measurement only (off by default; not a
  * step of the method).  While enabled, every kernel an entry point launches is
  * bracketed by a pair of HIP events recorded on the caller's stream, which

@@ -30,6 +30,35 @@ constexpr int DEC_LIST = 16;                           // keys kept per slice: t
 constexpr int DEC_MAX_SLICES = 16384 / DEC_ROWS;       // slices at the library's chunk limit
 
 int decode_slices(int64_t n_ctx) { return (int)((n_ctx / 64 + DEC_ROWS - 1) / DEC_ROWS); }
+
+// Row addressing of the caches (PG = paged).  Contiguous caches: the rows of (b,h) start at
+// bh*Lmax, its landmarks at bh*Nmax, one position n for every sequence.  Paged caches (serving
+// caches whose pages are chunks): chunk j of sequence b lives in pool page pt[b][j], whose rows
+// for head h start at (page*H + h)*64 and whose landmark row is page*H + h; each sequence has its
+// own position npos[b].  Positions, chunk indices and page ids are clamped into the table and the
+// pool, so a bad table gives wrong results but no access outside the arrays.
+template <bool PG>
+__device__ __forceinline__ int64_t dec_pos(const DecAddr& a, int bh, int64_t n) {
+  if (!PG) return n;
+  const int64_t v = a.npos[bh / a.H];
+  return v < 0 ? 0 : (v > (int64_t)a.max_pages * 64 - 1 ? (int64_t)a.max_pages * 64 - 1 : v);
+}
+__device__ __forceinline__ int64_t dec_page_row(const DecAddr& a, int bh, int j) {
+  const int b = bh / a.H, h = bh - b * a.H;
+  j = j < 0 ? 0 : (j >= a.max_pages ? a.max_pages - 1 : j);
+  int64_t p = a.pt[(int64_t)b * a.max_pages + j];
+  p = p < 0 ? 0 : (p >= a.pages ? a.pages - 1 : p);
+  return p * a.H + h;
+}
+// first K/V row of chunk j of (b,h), and its landmark row
+template <bool PG>
+__device__ __forceinline__ int64_t dec_chunk_row(const DecAddr& a, int bh, int j, int64_t Lmax) {
+  return PG ? dec_page_row(a, bh, j) * 64 : (int64_t)bh * Lmax + (int64_t)j * 64;
+}
+template <bool PG>
+__device__ __forceinline__ int64_t dec_lm_row(const DecAddr& a, int bh, int j, int64_t Nmax) {
+  return PG ? dec_page_row(a, bh, j) : (int64_t)bh * Nmax + j;
+}
 int decode_max_slices() { return DEC_MAX_SLICES; }
 int decode_list_len() { return DEC_LIST; }
 
@@ -65,29 +94,32 @@ __device__ __forceinline__ int wave_excl_prefix_small(int v, int& total) {
 // element type; the scan reads only rows of earlier chunks, decode_attend reads this one.  With LF
 // the grid has one workgroup more than there are slices, and that last one appends (so the slices
 // do not wait for the mean).
-template <typename T, int D, bool LF>
+template <typename T, int D, bool LF, bool PG>
 __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ q, const T* __restrict__ k_new,
                                                           const T* __restrict__ v_new, T* __restrict__ Kc,
                                                           T* __restrict__ Vc, const T* __restrict__ Klm,
                                                           T* __restrict__ Klm_w, uint64_t* __restrict__ lists,
-                                                          int64_t n, int64_t Lmax, int64_t Nmax, float scale) {
+                                                          int64_t n_in, int64_t Lmax, int64_t Nmax, float scale,
+                                                          DecAddr A) {
   constexpr int EPP = 16 / Elem<T>::bytes;  // elements per 16-byte piece
   constexpr int PIECES = D / EPP;           // pieces per row
   constexpr int RPR = 256 / PIECES;         // rows per round
   constexpr int ROUNDS = DEC_ROWS / RPR;
   const int s = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int64_t n = dec_pos<PG>(A, bh, n_in);
   const int c = (int)(n / 64);
   if (LF ? s == (int)gridDim.x - 1 : s == 0) {
     // append the new key and value (idempotent)
+    const int64_t r0 = dec_chunk_row<PG>(A, bh, c, Lmax);
+    const int64_t rn = r0 + (n - (int64_t)c * 64);
     for (int e = tid; e < D; e += 256) {
-      Kc[((int64_t)bh * Lmax + n) * D + e] = k_new[(int64_t)bh * D + e];
-      Vc[((int64_t)bh * Lmax + n) * D + e] = v_new[(int64_t)bh * D + e];
+      Kc[rn * D + e] = k_new[(int64_t)bh * D + e];
+      Vc[rn * D + e] = v_new[(int64_t)bh * D + e];
     }
     if (LF) {
       constexpr int G = 256 / D;
       __shared__ float lfp[G][D];
       const int e = tid % D, g = tid / D;
-      const int64_t r0 = (int64_t)bh * Lmax + (int64_t)c * 64;
       const int cnt = (int)(n - (int64_t)c * 64);  // cached rows of the open chunk before row n
       float acc = 0.f;
 #pragma unroll
@@ -101,7 +133,7 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ 
         float sum = Elem<T>::to_f32(k_new, (int64_t)bh * D + e);
 #pragma unroll
         for (int i = 0; i < G; ++i) sum += lfp[i][e];
-        Elem<T>::store(Klm_w, ((int64_t)bh * Nmax + c) * D + e, sum / (float)(cnt + 1));
+        Elem<T>::store(Klm_w, dec_lm_row<PG>(A, bh, c, Nmax) * D + e, sum / (float)(cnt + 1));
       }
     }
   }
@@ -116,7 +148,8 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ 
 #pragma unroll
   for (int round = 0; round < ROUNDS; ++round) {
     const int j = j0 + round * RPR + rr;
-    raw[round] = j < c ? *reinterpret_cast<const int4*>(base + (int64_t)j * D) : make_int4(0, 0, 0, 0);
+    const T* rp = PG ? Klm + dec_lm_row<PG>(A, bh, j, Nmax) * D + piece * EPP : base + (int64_t)j * D;
+    raw[round] = j < c ? *reinterpret_cast<const int4*>(rp) : make_int4(0, 0, 0, 0);
   }
   __shared__ __align__(16) float sc[DEC_ROWS];
 #pragma unroll
@@ -343,17 +376,18 @@ constexpr int DEC_NWV = 16 / DEC_SPLIT;  // wavefronts per attention workgroup (
 // attends to kept slot DEC_SPLIT * v + s, and workgroup 0's last wave attends to the open
 // chunk meanwhile, since that needs no selection.  Each workgroup writes its weighted partial sum (its slots in
 // order); decode_fuse adds the DEC_SPLIT partials.
-template <typename T, int D>
+template <typename T, int D, bool PG>
 __global__ __launch_bounds__(64 * DEC_NWV) void decode_attend_kernel(const T* __restrict__ q, const T* __restrict__ qr,
                                                             const T* __restrict__ Kc,
                                                             const T* __restrict__ Vc, const T* __restrict__ Klm,
                                                             const uint64_t* __restrict__ lists,
                                                             float* __restrict__ part, int32_t* __restrict__ idx,
-                                                            float* __restrict__ wout, int64_t n, int64_t Lmax,
-                                                            int64_t Nmax, int k, float scale) {
+                                                            float* __restrict__ wout, int64_t n_in, int64_t Lmax,
+                                                            int64_t Nmax, int k, float scale, DecAddr A) {
   constexpr int EPP = 16 / Elem<T>::bytes;
   constexpr int PIECES = D / EPP;
   const int sp = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t n = dec_pos<PG>(A, bh, n_in);
   const int c = (int)(n / 64);
   const int m = min(k, c);
   const int S = (c + DEC_ROWS - 1) / DEC_ROWS;
@@ -366,8 +400,6 @@ __global__ __launch_bounds__(64 * DEC_NWV) void decode_attend_kernel(const T* __
   float qv[EPP];
 #pragma unroll
   for (int e = 0; e < EPP; ++e) qv[e] = Elem<T>::to_f32(q, (int64_t)bh * D + piece * EPP + e);
-  const T* Kh = Kc + (int64_t)bh * Lmax * D;
-  const T* Vh = Vc + (int64_t)bh * Lmax * D;
   if (wv == 0) {
     // the slice lists are requested first; the score of the open chunk (its landmark row is
     // given) is formed meanwhile, then the selection and the weights
@@ -375,7 +407,7 @@ __global__ __launch_bounds__(64 * DEC_NWV) void decode_attend_kernel(const T* __
     if (m > 0) merge_load(lists + (int64_t)bh * DEC_MAX_SLICES * DEC_LIST, S, m, lane, mi);
     float dot = 0.f;
     for (int e = lane; e < D; e += 64)
-      dot += Elem<T>::to_f32(qr, (int64_t)bh * D + e) * Elem<T>::to_f32(Klm, ((int64_t)bh * Nmax + c) * D + e);
+      dot += Elem<T>::to_f32(qr, (int64_t)bh * D + e) * Elem<T>::to_f32(Klm, dec_lm_row<PG>(A, bh, c, Nmax) * D + e);
     const float s_own = scale * wave_sum(dot);
     if (m > 0) wave_merge_lists(mi, m, top, surv, lane);
     const bool used = lane < m || lane == 16;
@@ -385,13 +417,14 @@ __global__ __launch_bounds__(64 * DEC_NWV) void decode_attend_kernel(const T* __
     const float den = wave_sum(ev);
     if (lane < 17) wsl[lane] = ev / den;
   } else if (wv == DEC_NWV - 1 && sp == 0) {
-    wave_attend_chunk<T, D>(Kh, Vh, (int64_t)c * 64, (int)(n - (int64_t)c * 64) + 1, qv, scale, sc_w[wv],
-                            po[DEC_NWV], lane);
+    wave_attend_chunk<T, D>(Kc, Vc, dec_chunk_row<PG>(A, bh, c, Lmax), (int)(n - (int64_t)c * 64) + 1, qv, scale,
+                            sc_w[wv], po[DEC_NWV], lane);
   }
   __syncthreads();
   const int slot = DEC_SPLIT * wv + sp;
   if (slot < m)
-    wave_attend_chunk<T, D>(Kh, Vh, (int64_t)key_index(top[slot]) * 64, 64, qv, scale, sc_w[wv], po[wv], lane);
+    wave_attend_chunk<T, D>(Kc, Vc, dec_chunk_row<PG>(A, bh, (int)key_index(top[slot]), Lmax), 64, qv, scale,
+                            sc_w[wv], po[wv], lane);
   __syncthreads();
   for (int e = tid; e < D; e += 64 * DEC_NWV) {
     float acc = 0.f;
@@ -422,39 +455,61 @@ __global__ __launch_bounds__(64) void decode_fuse_kernel(const float* __restrict
 
 int decode_split() { return DEC_SPLIT; }
 
-template <typename T, int D>
+template <typename T, int D, bool PG>
 static hipError_t decode_t(const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc, void* Vc,
                            const void* Klm, bool lf, int64_t n, int64_t Lmax, int64_t Nmax, void* o, int32_t* idx,
-                           float* w, int BH, int k, float scale, const DecodeBufs& ws, hipStream_t st) {
+                           float* w, int BH, int k, float scale, const DecodeBufs& ws, const DecAddr& A,
+                           hipStream_t st) {
+  // n: the position (contiguous caches) or the largest position of the batch (paged), which sizes the scan
   const int S = decode_slices(n);
   // the landmark scores use the retrieval query (the attention query when none is given)
   const T* qs = (const T*)(qr ? qr : q);
   if (lf)
-    HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D, true>), dim3(S + 1, BH), dim3(256), 0, st, qs,
+    HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D, true, PG>), dim3(S + 1, BH), dim3(256), 0, st, qs,
                 (const T*)k_new, (const T*)v_new, (T*)Kc, (T*)Vc, (const T*)Klm, (T*)Klm, ws.lists, n, Lmax, Nmax,
-                scale);
+                scale, A);
   else
-    HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D, false>), dim3(S > 0 ? S : 1, BH), dim3(256), 0, st, qs,
+    HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D, false, PG>), dim3(S > 0 ? S : 1, BH), dim3(256), 0, st, qs,
                 (const T*)k_new, (const T*)v_new, (T*)Kc, (T*)Vc, (const T*)Klm, (T*)nullptr, ws.lists, n, Lmax,
-                Nmax, scale);
-  HILS_LAUNCH("decode_attend", (decode_attend_kernel<T, D>), dim3(DEC_SPLIT, BH), dim3(64 * DEC_NWV), 0, st, (const T*)q,
-              qs, (const T*)Kc, (const T*)Vc, (const T*)Klm, ws.lists, ws.part, idx, w, n, Lmax, Nmax, k, scale);
+                Nmax, scale, A);
+  HILS_LAUNCH("decode_attend", (decode_attend_kernel<T, D, PG>), dim3(DEC_SPLIT, BH), dim3(64 * DEC_NWV), 0, st,
+              (const T*)q, qs, (const T*)Kc, (const T*)Vc, (const T*)Klm, ws.lists, ws.part, idx, w, n, Lmax, Nmax, k,
+              scale, A);
   HILS_LAUNCH("decode_fuse", (decode_fuse_kernel<T, D>), dim3(BH), dim3(64), 0, st, ws.part, (T*)o);
   return hipGetLastError();
+}
+
+template <bool PG>
+static hipError_t decode_dispatch(int dt, int d, const void* q, const void* qr, const void* k_new, const void* v_new,
+                                  void* Kc, void* Vc, const void* Klm, bool lf, int64_t n, int64_t Lmax, int64_t Nmax,
+                                  void* o, int32_t* idx, float* w, int BH, int k, float scale, const DecodeBufs& ws,
+                                  const DecAddr& A, hipStream_t st) {
+  if (dt == 0)
+    return d == 64 ? decode_t<bf16_t, 64, PG>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, n, Lmax, Nmax, o, idx, w, BH, k,
+                                              scale, ws, A, st)
+                   : decode_t<bf16_t, 128, PG>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, n, Lmax, Nmax, o, idx, w, BH, k,
+                                               scale, ws, A, st);
+  return d == 64 ? decode_t<float, 64, PG>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, n, Lmax, Nmax, o, idx, w, BH, k,
+                                           scale, ws, A, st)
+                 : decode_t<float, 128, PG>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, n, Lmax, Nmax, o, idx, w, BH, k,
+                                            scale, ws, A, st);
+}
+
+hipError_t launch_decode_paged(int dt, int d, const void* q, const void* qr, const void* k_new, const void* v_new,
+                               void* Kp, void* Vp, void* Klm_p, bool lf, const int32_t* page_table, int max_pages,
+                               int64_t pages, const int64_t* n_ctx, int64_t n_max, int B, int H, void* o,
+                               int32_t* idx, float* w, int k, float scale, const DecodeBufs& ws, hipStream_t st) {
+  const DecAddr A{page_table, n_ctx, max_pages, H, pages};
+  return decode_dispatch<true>(dt, d, q, qr, k_new, v_new, Kp, Vp, Klm_p, lf, n_max, 0, 0, o, idx, w, B * H, k,
+                               scale, ws, A, st);
 }
 
 hipError_t launch_decode(int dt, int d, const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc,
                          void* Vc, const void* Klm, bool lf, int64_t n, int64_t Lmax, int64_t Nmax, void* o,
                          int32_t* idx, float* w, int BH, int k, float scale, const DecodeBufs& ws, hipStream_t st) {
-  if (dt == 0)
-    return d == 64 ? decode_t<bf16_t, 64>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, n, Lmax, Nmax, o, idx, w, BH, k,
-                                          scale, ws, st)
-                   : decode_t<bf16_t, 128>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, n, Lmax, Nmax, o, idx, w, BH, k,
-                                           scale, ws, st);
-  return d == 64 ? decode_t<float, 64>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, n, Lmax, Nmax, o, idx, w, BH, k, scale,
-                                       ws, st)
-                 : decode_t<float, 128>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, n, Lmax, Nmax, o, idx, w, BH, k, scale,
-                                        ws, st);
+  const DecAddr A{nullptr, nullptr, 0, 1, 0};
+  return decode_dispatch<false>(dt, d, q, qr, k_new, v_new, Kc, Vc, Klm, lf, n, Lmax, Nmax, o, idx, w, BH, k, scale,
+                                ws, A, st);
 }
 
 }  // namespace hils

@@ -461,3 +461,49 @@ static hils_status bwd_impl(const void* Q, const void* Q_ret, const void* K, con
                                      (int)(B * H), (int)L, (int)D.N, (int)topk, scale, W, (hipStream_t)stream),
                     "hils_sparse_attn_bwd");
 }
+
+extern "C" {
+
+hils_status hils_decode_step_paged(const void* q, const void* q_ret, const void* k_new, const void* v_new,
+                                   void* K_pages, void* V_pages, void* K_lm_pages, const int32_t* page_table,
+                                   int64_t n_pages, int64_t max_pages, const int64_t* n_ctx, int64_t n_ctx_max,
+                                   int landmark_free, void* o, int32_t* idx, float* w, int64_t B, int64_t H,
+                                   int64_t d, int64_t C, int64_t topk, float scale, hils_dtype dt, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  Dims D;
+  hils_status st;
+  if (C != 64) return fail(HILS_ERR_UNSUPPORTED, "chunk size C must be 64 (got %lld)", (long long)C);
+  if (max_pages < 1) return fail(HILS_ERR_INVALID_ARG, "max_pages must be >= 1 (got %lld)", (long long)max_pages);
+  if (n_pages < 1) return fail(HILS_ERR_INVALID_ARG, "n_pages must be >= 1 (got %lld)", (long long)n_pages);
+  const int64_t L_max = max_pages * C;
+  if ((st = check_dims(B, H, L_max, d, C, topk, true, &D)) != HILS_OK) return st;
+  if ((st = check_dt(dt)) != HILS_OK) return st;
+  if (n_ctx_max < 0 || n_ctx_max >= L_max)
+    return fail(HILS_ERR_INVALID_ARG, "n_ctx_max (%lld) must be in [0, max_pages*C=%lld)", (long long)n_ctx_max,
+                (long long)L_max);
+  if (landmark_free != 0 && landmark_free != 1) return fail(HILS_ERR_INVALID_ARG, "landmark_free must be 0 or 1");
+  REQUIRE_PTR(q);
+  OPTIONAL_PTR(q_ret);
+  REQUIRE_PTR(k_new);
+  REQUIRE_PTR(v_new);
+  REQUIRE_PTR(K_pages);
+  REQUIRE_PTR(V_pages);
+  REQUIRE_PTR(K_lm_pages);
+  REQUIRE_PTR(page_table);
+  REQUIRE_PTR(n_ctx);
+  REQUIRE_PTR(o);
+  REQUIRE_PTR(idx);
+  REQUIRE_PTR(w);
+  if (!(scale > 0.f)) return fail(HILS_ERR_INVALID_ARG, "scale must be positive");
+  hils::DecodeBufs W;
+  const size_t need = carve_decode(nullptr, B * H, L_max, d, topk, &W);
+  if ((st = check_ws(ws, ws_bytes, need)) != HILS_OK) return st;
+  carve_decode(ws, B * H, L_max, d, topk, &W);
+  return hip_status(hils::launch_decode_paged(dt, (int)d, q, q_ret, k_new, v_new, K_pages, V_pages, K_lm_pages,
+                                              landmark_free != 0, page_table, (int)max_pages, n_pages, n_ctx,
+                                              n_ctx_max, (int)B, (int)H, o, idx, w, (int)topk, scale, W,
+                                              (hipStream_t)stream),
+                    "hils_decode_step_paged");
+}
+
+}  // extern "C"

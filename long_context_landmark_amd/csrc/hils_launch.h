@@ -62,6 +62,14 @@ struct DecodeBufs {
   uint64_t* lists;  // [BH][decode_max_slices()][decode_list_len()] best (score, chunk) keys of every slice
   float* part;      // [BH][decode_split()][d] weighted partial outputs of the attention workgroups
 };
+// cache addressing of a decode step: contiguous (pt == nullptr) or paged (see launch_decode_paged)
+struct DecAddr {
+  const int32_t* pt;    // page table [B][max_pages]: pool page of each chunk of each sequence
+  const int64_t* npos;  // position of each sequence [B]
+  int max_pages;
+  int H;
+  int64_t pages;  // pages in the pool
+};
 int decode_split();
 int decode_slices(int64_t n_ctx);
 int decode_max_slices();
@@ -92,6 +100,12 @@ hipError_t launch_lf_bwd(int dt, int d, const void* Qs, const void* K, const flo
 hipError_t launch_decode(int dt, int d, const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc,
                          void* Vc, const void* Klm, bool lf, int64_t n, int64_t Lmax, int64_t Nmax, void* o,
                          int32_t* idx, float* w, int BH, int k, float scale, const DecodeBufs& ws, hipStream_t st);
+// decode step of B sequences at their own positions n_ctx[b] (device, <= n_max) over paged caches: page p of
+// the pools holds one chunk of 64 rows per head (Kp, Vp: [pages][H][64][d]; Klm_p: [pages][H][d])
+hipError_t launch_decode_paged(int dt, int d, const void* q, const void* qr, const void* k_new, const void* v_new,
+                               void* Kp, void* Vp, void* Klm_p, bool lf, const int32_t* page_table, int max_pages,
+                               int64_t pages, const int64_t* n_ctx, int64_t n_max, int B, int H, void* o,
+                               int32_t* idx, float* w, int k, float scale, const DecodeBufs& ws, hipStream_t st);
 // landmark-free chunk keys: rows 0..nchunks-1 of Klm ([BH][Nlm][d]) = means of the key rows of each chunk
 // (K: [BH][Lk][d])
 hipError_t launch_chunk_means(int dt, int d, const void* K, void* Klm, int BH, int64_t Lk, int64_t Nlm, int nchunks,

@@ -44,6 +44,8 @@ _lib.hils_chunk_means.argtypes = [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, 
 _lib.hils_sparse_attn_fwd_lf.argtypes = _lib.hils_sparse_attn_fwd_rq.argtypes
 _lib.hils_decode_step_lf.argtypes = _lib.hils_decode_step_rq.argtypes
 _lib.hils_sparse_attn_bwd_lf.argtypes = _lib.hils_sparse_attn_bwd_rq.argtypes
+_lib.hils_decode_step_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _int, _vp, _vp,
+                                        _vp, _i64, _i64, _i64, _i64, _i64, _f, _int, _vp, _sz, _vp]
 _lib.hils_profile_enable.argtypes = [_int]
 _lib.hils_profile_enable.restype = None
 _lib.hils_profile_read.argtypes = [ctypes.c_char_p, _int, ctypes.POINTER(ctypes.c_double),
@@ -326,3 +328,30 @@ def sparse_attn_bwd_lf(Q, K, V, K_lm, dO, idx, w, lse, k, C=64, scale=None, ws=N
     if Q_ret is None:
         return dQ, dK, dV, dKlm
     return dQ, dQr, dK, dV, dKlm
+
+
+def decode_step_paged(q, k_new, v_new, K_pages, V_pages, K_lm_pages, page_table, n_ctx, n_ctx_max, k, C=64,
+                      scale=None, ws=None, out=None, idx=None, w=None, q_ret=None, landmark_free=False):
+    """One decode step of B sequences at their own positions n_ctx[b] (int64 device tensor [B]; n_ctx_max >= all
+    of them) over page pools K_pages / V_pages [P,H,64,d] and K_lm_pages [P,H,d], page_table int32 [B,max_pages]
+    (device).  Returns (o, idx, w); the pools are updated in place."""
+    _contig(q, k_new, v_new, K_pages, V_pages, K_lm_pages, page_table, n_ctx, q_ret)
+    _like(q_ret, q, "q_ret")
+    B, H, d = q.shape
+    P = K_pages.shape[0]
+    if K_pages.shape != (P, H, C, d) or V_pages.shape != K_pages.shape or K_lm_pages.shape != (P, H, d):
+        raise ValueError("pools must be [P,H,C,d] (keys, values) and [P,H,d] (landmarks)")
+    if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be int32 [B,max_pages]")
+    if n_ctx.dtype != torch.int64 or tuple(n_ctx.shape) != (B,):
+        raise ValueError("n_ctx must be int64 [B]")
+    max_pages = page_table.shape[1]
+    o = out if out is not None else torch.empty_like(q)
+    idx = idx if idx is not None else torch.empty((B, H, k + 1), dtype=torch.int32, device=q.device)
+    w = w if w is not None else torch.empty((B, H, k + 1), dtype=torch.float32, device=q.device)
+    wsb, n = _workspace(OP_DECODE, B, H, max_pages * C, d, C, k, q.device, ws)
+    _check(_lib.hils_decode_step_paged(_p(q), _p(q_ret), _p(k_new), _p(v_new), _p(K_pages), _p(V_pages),
+                                       _p(K_lm_pages), _p(page_table), P, max_pages, _p(n_ctx), int(n_ctx_max),
+                                       1 if landmark_free else 0, _p(o), _p(idx), _p(w), B, H, d, C, k,
+                                       _scale(d, scale), _dt(q), _p(wsb), n, _stream()))
+    return o, idx, w

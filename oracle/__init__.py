@@ -309,3 +309,34 @@ def bwd_lf(Q, K, V, dO, idx, C, k, scale=None, nthreads=0, Q_ret=None):
     if Qr is not None:
         out["dQ_ret"] = dQr
     return out
+
+
+def decode_paged(q, k_new, v_new, Kp, Vp, Klm_p, page_table, n_ctx, C, k, scale=None, nthreads=0, q_ret=None,
+                 landmark_free=False):
+    """One decode step of B sequences at positions n_ctx[b] over page pools Kp, Vp [P,H,C,d], Klm_p [P,H,d]
+    (host arrays, updated in place) with page_table [B,max_pages].  Paging only moves rows: each sequence's
+    chunks 0..n_ctx[b]//C are gathered into contiguous caches, ``decode`` runs there, and the rows it writes
+    go back to their pages.  Returns idx / sel / w / lse [B,H,k+1] and o [B,H,d]."""
+    B, H, d = q.shape
+    maxp = page_table.shape[1]
+    Lmax = maxp * C
+    outs = []
+    for b in range(B):
+        n = int(n_ctx[b])
+        c = n // C
+        pages = [int(page_table[b, j]) for j in range(c + 1)]
+        Kc = np.zeros((1, H, Lmax, d), Kp.dtype)
+        Vc = np.zeros_like(Kc)
+        Klm = np.zeros((1, H, maxp, d), Klm_p.dtype)
+        for j, p in enumerate(pages):
+            Kc[0, :, j * C:(j + 1) * C] = Kp[p]
+            Vc[0, :, j * C:(j + 1) * C] = Vp[p]
+            Klm[0, :, j] = Klm_p[p]
+        r = decode(q[b:b + 1], k_new[b:b + 1], v_new[b:b + 1], Kc, Vc, Klm, n, C, k, scale=scale, nthreads=nthreads,
+                   q_ret=None if q_ret is None else q_ret[b:b + 1], landmark_free=landmark_free)
+        Kp[pages[c], :, n - c * C] = Kc[0, :, n]
+        Vp[pages[c], :, n - c * C] = Vc[0, :, n]
+        if landmark_free:
+            Klm_p[pages[c]] = Klm[0, :, c]
+        outs.append(r)
+    return {key: np.concatenate([r[key] for r in outs]) for key in ("idx", "sel", "w", "lse", "o")}

@@ -153,3 +153,18 @@ def test_landmark_free_backward_validates(lib, hils):
                                        None) == INVALID
     assert lib.hils_sparse_attn_bwd_lf(FAKE, None, *([FAKE] * 8), None, *([FAKE] * 3), 1, 2, 1024, 128, 64, 4,
                                        0.125, 1, FAKE, nb, None) == UNSUPPORTED
+
+
+def test_paged_decode_validates(lib, hils):
+    nd = hils.workspace_size(hils.OP_DECODE, 2, 2, 64 * 10, 64, 64, 4)
+    head = [FAKE] * 8
+    # n_ctx_max beyond the table, a zero-page pool, and a bad landmark_free flag
+    assert lib.hils_decode_step_paged(*head, 5, 10, FAKE, 640, 0, FAKE, FAKE, FAKE, 2, 2, 64, 64, 4, 0.125, 0,
+                                      FAKE, nd, None) == INVALID
+    assert "n_ctx_max" in lib.hils_last_error().decode()
+    assert lib.hils_decode_step_paged(*head, 0, 10, FAKE, 100, 0, FAKE, FAKE, FAKE, 2, 2, 64, 64, 4, 0.125, 0,
+                                      FAKE, nd, None) == INVALID
+    assert lib.hils_decode_step_paged(*head, 5, 10, FAKE, 100, 2, FAKE, FAKE, FAKE, 2, 2, 64, 64, 4, 0.125, 0,
+                                      FAKE, nd, None) == INVALID
+    assert lib.hils_decode_step_paged(*head, 5, 10, FAKE, 100, 0, FAKE, FAKE, FAKE, 2, 2, 64, 64, 4, 0.125, 0,
+                                      FAKE, nd - 16, None) == WORKSPACE

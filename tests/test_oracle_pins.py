@@ -596,3 +596,72 @@ def test_landmark_free_central_differences(oracle_mod, qret):
             assert abs(fd - an) <= 2e-4 * max(1.0, abs(an)), (name, pos, fd, an)
     # the past chunks' mean gradient is returned beside dK (which already holds it)
     assert np.abs(g["dKlm"]).max() > 0
+
+
+# --------------------------------------------------------------------------- paged, batched decode
+
+
+def _paged_from_contiguous(Kc, Vc, Klm, nchunks, rng, spare=3):
+    """Page pools holding the first nchunks[b] chunks of every sequence, pages in a shuffled order."""
+    B, H, Lmax, d = Kc.shape
+    C = 64
+    total = int(sum(nchunks)) + spare
+    order = rng.permutation(total)
+    maxp = Lmax // C
+    table = np.zeros((B, maxp), np.int32)
+    Kp = np.zeros((total, H, C, d), Kc.dtype)
+    Vp = np.zeros_like(Kp)
+    Lp = np.zeros((total, H, d), Klm.dtype)
+    nxt = 0
+    for b in range(B):
+        for j in range(nchunks[b]):
+            p = int(order[nxt])
+            nxt += 1
+            table[b, j] = p
+            Kp[p] = Kc[b, :, j * C:(j + 1) * C]
+            Vp[p] = Vc[b, :, j * C:(j + 1) * C]
+            Lp[p] = Klm[b, :, j]
+    return Kp, Vp, Lp, table
+
+
+@pytest.mark.parametrize("lf", [False, True])
+def test_paged_decode_equals_contiguous_per_sequence(oracle_mod, lf):
+    """Ragged positions, shuffled pages: every sequence's steps equal its own contiguous decode."""
+    B, H, d, C, k = 3, 2, 16, 64, 3
+    ctxs = [64 * 5 + 10, 64 * 2 + 60, 7]
+    steps = 70
+    rng = np.random.default_rng(9)
+    xs = [synth.decode_inputs(1, H, d, ctx, steps, C=C, seed=50 + b, dtype="bf16", with_qret=True)
+          for b, ctx in enumerate(ctxs)]
+    Lmax = max(ctxs) + steps
+    Lmax = (Lmax + C - 1) // C * C
+    Kc = np.zeros((B, H, Lmax, d), np.uint16)
+    Vc = np.zeros_like(Kc)
+    Klm = np.zeros((B, H, Lmax // C, d), np.uint16)
+    for b, x in enumerate(xs):
+        Kc[b, :, :x["K_cache"].shape[2]] = x["K_cache"][0]
+        Vc[b, :, :x["V_cache"].shape[2]] = x["V_cache"][0]
+        Klm[b, :, :x["Klm"].shape[2]] = x["Klm"][0]
+        if lf:
+            oracle_mod.chunk_means(Kc[b:b + 1], C, nchunks=ctxs[b] // C, Klm=Klm[b:b + 1])
+    nchunks = [(ctx + steps - 1) // C + 1 for ctx in ctxs]
+    Kp, Vp, Lp, table = _paged_from_contiguous(Kc, Vc, Klm, nchunks, rng)
+    conts = [(Kc[b:b + 1].copy(), Vc[b:b + 1].copy(), Klm[b:b + 1].copy()) for b in range(B)]
+    for s in range(steps):
+        pos = np.array([ctx + s for ctx in ctxs], np.int64)
+        q = np.stack([x["q"][s][0] for x in xs])
+        qr = np.stack([x["q_ret"][s][0] for x in xs])
+        kn = np.stack([x["k_new"][s][0] for x in xs])
+        vn = np.stack([x["v_new"][s][0] for x in xs])
+        got = oracle_mod.decode_paged(q, kn, vn, Kp, Vp, Lp, table, pos, C, k, q_ret=qr, landmark_free=lf)
+        for b in range(B):
+            Kb, Vb, Lb = conts[b]
+            ref = oracle_mod.decode(q[b:b + 1], kn[b:b + 1], vn[b:b + 1], Kb, Vb, Lb, int(pos[b]), C, k,
+                                    q_ret=qr[b:b + 1], landmark_free=lf)
+            for key in ("idx", "w", "o"):
+                np.testing.assert_array_equal(got[key][b], ref[key][0])
+    # the pools hold what the contiguous caches hold
+    for b in range(B):
+        for j in range(nchunks[b]):
+            np.testing.assert_array_equal(Kp[table[b, j]], conts[b][0][0, :, j * C:(j + 1) * C])
+            np.testing.assert_array_equal(Lp[table[b, j]], conts[b][2][0, :, j])
