@@ -417,6 +417,64 @@ def bench_decode(hils, synth, name, replicas, warmup, lf=False):
     return res
 
 
+def bench_decode_paged(hils, synth, name, warmup):
+    """Batched decode of ragged sequences over a paged cache: one step advances every sequence by one token."""
+    import torch
+
+    w = synth.WORKLOADS[name]
+    x = synth.torch_paged_decode_inputs(w)
+    B, H, d = w.B, w.H, w.d
+    maxp = x["page_table"].shape[1]
+    ws = torch.empty(hils.workspace_size(hils.OP_DECODE, B, H, maxp * w.C, d, w.C, w.k), dtype=torch.uint8,
+                     device="cuda:0")
+    o = torch.empty((B, H, d), dtype=torch.bfloat16, device="cuda:0")
+    idx = torch.empty((B, H, w.k + 1), dtype=torch.int32, device="cuda:0")
+    wt = torch.empty((B, H, w.k + 1), dtype=torch.float32, device="cuda:0")
+
+    def step(s):
+        hils.decode_step_paged(x["q"][s], x["k_new"][s], x["v_new"][s], x["K_pages"], x["V_pages"], x["K_lm_pages"],
+                               x["page_table"], x["pos"][s], x["pos_max"][s], w.k, ws=ws, out=o, idx=idx, w=wt)
+
+    for s in range(warmup):
+        step(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s in range(w.steps):
+            step(s)
+    graph.replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    graph.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    del graph
+    us = e0.elapsed_time(e1) * 1e3 / w.steps
+    hils.profile_enable(True)
+    for s in range(8):
+        step(s)
+    torch.cuda.synchronize()
+    kt = hils.profile_read()
+    hils.profile_enable(False)
+    # landmark rows read per step (every sequence scans its chunks) and the kept chunks' keys and values
+    lm_bytes = sum(c // w.C for c in x["ctx"]) * H * d * 2
+    kv_bytes = B * H * (w.k + 1) * w.C * d * 2 * 2
+    res = {
+        "us_per_step": us,
+        "tokens_per_s": B / (us * 1e-6),
+        "timing": "every step captured in one HIP graph, replayed once",
+        "hbm_gbs": (lm_bytes + kv_bytes) / (us * 1e-6) / 1e9,
+        "kernel_us": {n: round(t / c * 1e3, 3) for n, (t, c) in kt.items()},
+        "config": {"workload": name, "B": B, "H": H, "d": d, "contexts": [min(x["ctx"]), max(x["ctx"])],
+                   "steps": w.steps, "k": w.k, "pages": int(x["K_pages"].shape[0]), "cache": "paged, page = chunk"},
+    }
+    del x, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(synth, name):
     """The oracle (plain C, double precision) on the host cores, on the full 8K workload."""
     import oracle
@@ -477,6 +535,8 @@ def main():
         name = args.only[:-len("_retrieval")] if rq else args.only[:-len("_landmark_free")] if lf else args.only
         if name.startswith("prefill"):
             res = bench_prefill(hils, synth, name, args.steps, args.warmup, rq=rq, lf=lf)
+        elif name.startswith("decode_paged"):
+            res = bench_decode_paged(hils, synth, name, args.warmup)
         elif name.startswith("decode"):
             res = bench_decode(hils, synth, name, args.decode_replicas, args.warmup, lf=lf)
         elif name.startswith("train"):
@@ -521,6 +581,10 @@ def main():
         extra["train_8k_landmark_free"] = bench_train(hils, synth, "train_8k", max(3, min(args.steps, 20)), 2, lf=True)
         log(f"[bench] prefill_8k_landmark_free {extra['prefill_8k_landmark_free']['ms_per_step']*1e3:.1f} us/step, "
             f"decode_512k_landmark_free {extra['decode_512k_landmark_free']['us_per_token']:.2f} us/token")
+    if "decode_paged_b16" not in skip:
+        log("[bench] decode_paged_b16 (16 ragged sequences, paged cache)")
+        extra["decode_paged_b16"] = bench_decode_paged(hils, synth, "decode_paged_b16", 4)
+        log(f"[bench] decode_paged_b16 {extra['decode_paged_b16']['us_per_step']:.2f} us/step")
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")

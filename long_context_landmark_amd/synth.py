@@ -193,6 +193,10 @@ WORKLOADS = {
                              gen={"klm": "chunkmean", "klm_noise": 0.1, "qkv_std": 1.0 / math.sqrt(2.0)}),
     "train_8k": Workload("train_8k", "train", 4, 16, 64, 8192, 8, seed=1005,
                          gen={"klm": "iid", "with_dO": True}),
+    # serving shape: 16 sequences with contexts spread over 16K..128K tokens (L = the longest), pages of one
+    # chunk in a shuffled pool
+    "decode_paged_b16": Workload("decode_paged_b16", "decode", 16, 16, 64, 131072, 16, seed=1006, steps=64,
+                                 gen={"ctx_lo": 16384}),
 }
 
 
@@ -304,3 +308,33 @@ def torch_decode_inputs(w: Workload, replicas=1, device="cuda:0", seed=None):
     v_new = torch.randn((steps, B, H, d), generator=g, device=device).to(dt)
     return {"replicas": reps, "q": q.to(dt).contiguous(), "k_new": k_new.contiguous(), "v_new": v_new.contiguous(),
             "ctx": ctx}
+
+
+def torch_paged_decode_inputs(w: Workload, device="cuda:0", seed=None):
+    """Paged decode workload on the device: contexts evenly spread over [ctx_lo, L] (ragged), every chunk a
+    pool page in shuffled order (spare pages for the steps), per-step positions, q, k_new and v_new."""
+    import torch
+
+    g = _torch_gen(w.seed if seed is None else seed, device)
+    B, H, d, C, steps = w.B, w.H, w.d, w.C, w.steps
+    lo = int(w.gen.get("ctx_lo", w.L // 2))
+    ctx = [lo + (w.L - lo) * b // max(1, B - 1) - (b * 37) % C for b in range(B)]
+    nch = [(c + steps - 1) // C + 1 for c in ctx]
+    maxp = max(nch)
+    P = sum(nch)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    order = torch.randperm(P, generator=g, device=device).to(torch.int32)
+    table = torch.zeros((B, maxp), dtype=torch.int32, device=device)
+    off = 0
+    for b in range(B):
+        table[b, :nch[b]] = order[off:off + nch[b]]
+        off += nch[b]
+    Kp = torch.randn((P, H, C, d), generator=g, device=device).to(dt)
+    Vp = torch.randn((P, H, C, d), generator=g, device=device).to(dt)
+    Lp = torch.randn((P, H, d), generator=g, device=device).to(dt)
+    pos = torch.tensor([[c + s for c in ctx] for s in range(steps)], dtype=torch.int64, device=device)
+    q = torch.randn((steps, B, H, d), generator=g, device=device).to(dt)
+    k_new = torch.randn((steps, B, H, d), generator=g, device=device).to(dt)
+    v_new = torch.randn((steps, B, H, d), generator=g, device=device).to(dt)
+    return {"K_pages": Kp, "V_pages": Vp, "K_lm_pages": Lp, "page_table": table, "pos": pos,
+            "pos_max": [max(ctx) + s for s in range(steps)], "ctx": ctx, "q": q, "k_new": k_new, "v_new": v_new}
