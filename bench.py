@@ -48,9 +48,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: (kernel, FETCH_SIZE KiB, WRITE_SIZE KiB, source digest)
-    "prefill_8k": ("chunk_attn_fwd", 28621.9, 130576.2, "79664decdcc7b0e9"),
-    "prefill_128k": ("chunk_attn_fwd", 8509302.0, 17021942.0, "79664decdcc7b0e9"),
-    "train_8k": ("chunk_bwd", 237992.0, 902533.8, "2a8888f1bc2af317"),
+    "prefill_8k": ("chunk_attn_fwd", 28621.2, 130575.6, "61955e7f109bb0b3"),
+    "prefill_128k": ("chunk_attn_fwd", 8510411.9, 17017989.0, "61955e7f109bb0b3"),
+    "train_8k": ("chunk_bwd", 238081.9, 902126.3, "d47ff5144bc2e4ed"),
 }
 
 
