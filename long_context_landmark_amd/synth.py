@@ -338,3 +338,11 @@ def torch_paged_decode_inputs(w: Workload, device="cuda:0", seed=None):
     v_new = torch.randn((steps, B, H, d), generator=g, device=device).to(dt)
     return {"K_pages": Kp, "V_pages": Vp, "K_lm_pages": Lp, "page_table": table, "pos": pos,
             "pos_max": [max(ctx) + s for s in range(steps)], "ctx": ctx, "q": q, "k_new": k_new, "v_new": v_new}
+
+
+def first_last_landmarks(K: np.ndarray, C: int = 64) -> np.ndarray:
+    """Two landmarks per chunk, the keys of its first and last token: [B,H,N,2,d] from K [B,H,L,d]
+    (a copy of rows, same element type)."""
+    B, H, L, d = K.shape
+    Kc = K.reshape(B, H, L // C, C, d)
+    return np.ascontiguousarray(np.stack([Kc[:, :, :, 0], Kc[:, :, :, C - 1]], axis=3))

@@ -82,6 +82,12 @@ def _load():
     lib.oracle_bwd_lf.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, ip, vp, vp, vp, vp,
                                   vp, ip]
     lib.oracle_bwd_lf.restype = ip
+    lib.oracle_fwd_ml.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, dbl, ip, vp, i64, ip,
+                                  vp, vp, vp, vp, vp, ip]
+    lib.oracle_fwd_ml.restype = ip
+    lib.oracle_bwd_ml.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, i64, i64, i64, i64, i64, i64, dbl, ip, vp, vp,
+                                  vp, vp, vp, ip]
+    lib.oracle_bwd_ml.restype = ip
     _lib = lib
     return lib
 
@@ -340,3 +346,53 @@ def decode_paged(q, k_new, v_new, Kp, Vp, Klm_p, page_table, n_ctx, C, k, scale=
             Klm_p[pages[c]] = Klm[0, :, c]
         outs.append(r)
     return {key: np.concatenate([r[key] for r in outs]) for key in ("idx", "sel", "w", "lse", "o")}
+
+
+def fwd_ml(Q, K, V, Klm, C, k, scale=None, rows=None, idx=None, nthreads=0, Q_ret=None):
+    """Forward with m landmarks per chunk (Klm [B,H,N,m,d]): the chunk score is the log-sum-exp of the
+    chunk's landmark scores.  Returns what ``fwd`` returns."""
+    Q, K, V, Klm = _c(Q), _c(K), _c(V), _c(Klm)
+    Qr = _c(Q_ret) if Q_ret is not None else None
+    B, H, L, d = Q.shape
+    N, m = Klm.shape[2], Klm.shape[3]
+    if N != (L + C - 1) // C or Klm.shape[4] != d:
+        raise ValueError("Klm must be [B,H,N,m,d]")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    k1 = k + 1
+    if rows is not None:
+        rows = _c(np.asarray(rows, np.int64))
+        lead = (rows.shape[0],)
+    else:
+        lead = (B, H, L)
+    use_idx = idx is not None
+    idx_out = _c(np.array(idx, np.int32, copy=True)).reshape(lead + (k1,)) if use_idx else np.empty(lead + (k1,), np.int32)
+    sel, w, lse = (np.empty(lead + (k1,), np.float64) for _ in range(3))
+    O = np.empty(lead + (d,), np.float64)
+    used = _load().oracle_fwd_ml(_p(Q), _p(Qr), _p(K), _p(V), _p(Klm), m, B, H, L, d, C, k, scale, _dt(Q, K, V, Klm),
+                                 _p(rows), 0 if rows is None else rows.shape[0], int(use_idx),
+                                 _p(idx_out), _p(sel), _p(w), _p(lse), _p(O), nthreads)
+    if used < 0:
+        raise ValueError("unsupported landmark count")
+    return {"idx": idx_out, "sel": sel, "w": w, "lse": lse, "O": O, "threads": used}
+
+
+def bwd_ml(Q, K, V, Klm, dO, idx, C, k, scale=None, nthreads=0, Q_ret=None):
+    """Backward of ``fwd_ml`` with the selection fixed by idx: dQ, dK, dV [B,H,L,d], dKlm [B,H,N,m,d] (float64),
+    and dQ_ret with ``Q_ret``."""
+    Q, K, V, Klm, dO = _c(Q), _c(K), _c(V), _c(Klm), _c(dO)
+    Qr = _c(Q_ret) if Q_ret is not None else None
+    B, H, L, d = Q.shape
+    N, m = Klm.shape[2], Klm.shape[3]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    idx = _c(np.asarray(idx, np.int32))
+    dQ, dK, dV = (np.empty((B, H, L, d), np.float64) for _ in range(3))
+    dKlm = np.empty((B, H, N, m, d), np.float64)
+    dQr = np.empty((B, H, L, d), np.float64) if Qr is not None else None
+    used = _load().oracle_bwd_ml(_p(Q), _p(Qr), _p(K), _p(V), _p(Klm), m, _p(dO), _p(idx), B, H, L, d, C, k, scale,
+                                 _dt(Q, K, V, Klm, dO), _p(dQ), _p(dQr), _p(dK), _p(dV), _p(dKlm), nthreads)
+    if used < 0:
+        raise ValueError("unsupported landmark count")
+    out = {"dQ": dQ, "dK": dK, "dV": dV, "dKlm": dKlm, "threads": used}
+    if Qr is not None:
+        out["dQ_ret"] = dQr
+    return out

@@ -30,6 +30,13 @@
  *             query's own chunk only the keys up to the query are averaged,
  *             so nothing after the query enters its scores and a decode step
  *             equals the prefill row at the same position.
+ *   [HiLS-p1] "Method" > "Input & chunking" speaks of a few landmarks per
+ *             chunk (usually its first and last token) and "Key modules"
+ *             item 1 of a softmax over a chunk's landmark scores before the
+ *             chunk-level one.  Read, for m landmarks per chunk, as: the
+ *             chunk score is the log-sum-exp of its m landmark scores (the
+ *             normaliser of that inner softmax), rounded to fp32 once; with
+ *             m = 1 it is the plain score.
  * Points the pages leave open are fixed as follows (one landmark key per
  * chunk; scale 1/sqrt(d) on both softmax levels; top-k ties go to the lower
  * chunk index; the query's own chunk is always in the set, is not counted in
@@ -86,6 +93,7 @@ typedef struct {
   double scale;
   int dt;
   int lf;  /* landmark-free: the own chunk's landmark is the mean of its keys up to the query */
+  int64_t m;  /* landmarks per chunk (0 or 1: one); Klm is then [B,H,N,m,d] */
 } prob_t;
 
 #define MAX_D 256
@@ -140,6 +148,16 @@ static float chunk_score(const prob_t* P, const void* q, int64_t qrow, int64_t b
     double s = 0.0;
     for (int64_t e = 0; e < P->d; ++e) s += elem(qs, qrow * P->d + e, P->dt) * m[e];
     return (float)(P->scale * s);
+  }
+  if (P->m > 1) {
+    /* several landmarks: log-sum-exp of their scores */
+    double a[64], amax = -INFINITY, z = 0.0;
+    for (int64_t r = 0; r < P->m; ++r) {
+      a[r] = P->scale * dot_row(qs, qrow, P->Klm, (bh * P->Nlm + j) * P->m + r, P->d, P->dt);
+      if (a[r] > amax) amax = a[r];
+    }
+    for (int64_t r = 0; r < P->m; ++r) z += exp(a[r] - amax);
+    return (float)(amax + log(z));
   }
   return (float)(P->scale * dot_row(qs, qrow, P->Klm, bh * P->Nlm + j, P->d, P->dt));
 }
@@ -414,17 +432,17 @@ int oracle_decode_lf(const void* q, const void* qr, const void* k_new, const voi
  * dKlm_j += scale ds_j qr_t, and dQ keeps the in-chunk terms only.
  */
 static int bwd_common(const void* Q, const void* Qr, const void* K, const void* V, const void* Klm, int lf,
-                      const void* dO, const int32_t* idx_in, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
-                      int64_t k, double scale, int dt, double* dQ, double* dQr, double* dK, double* dV,
+                      int64_t m, const void* dO, const int32_t* idx_in, int64_t B, int64_t H, int64_t L, int64_t d,
+                      int64_t C, int64_t k, double scale, int dt, double* dQ, double* dQr, double* dK, double* dV,
                       double* dKlm, int nthreads) {
   int64_t N = (L + C - 1) / C;
-  prob_t P = {Q, K, V, Klm, Qr, B, H, L, d, C, k, N, L, N, scale, dt, lf};
+  prob_t P = {Q, K, V, Klm, Qr, B, H, L, d, C, k, N, L, N, scale, dt, lf, m};
   int used = set_threads(nthreads);
   int64_t k1 = k + 1;
   memset(dQ, 0, sizeof(double) * (size_t)(B * H * L * d));
   memset(dK, 0, sizeof(double) * (size_t)(B * H * L * d));
   memset(dV, 0, sizeof(double) * (size_t)(B * H * L * d));
-  memset(dKlm, 0, sizeof(double) * (size_t)(B * H * N * d));
+  memset(dKlm, 0, sizeof(double) * (size_t)(B * H * N * (m > 1 ? m : 1) * d));
   if (dQr) memset(dQr, 0, sizeof(double) * (size_t)(B * H * L * d));
   double* dS = dQr ? dQr : dQ;  /* where the score gradients go */
 #pragma omp parallel for schedule(dynamic, 1)
@@ -472,6 +490,22 @@ static int bwd_common(const void* Q, const void* Qr, const void* K, const void* 
           for (int64_t e = 0; e < d; ++e) dS[row * d + e] += scale * ds * m[e];
           for (int64_t i = j * C; i <= t; ++i)
             for (int64_t e = 0; e < d; ++e) dK[(bh * L + i) * d + e] += scale * ds * qrv[e] / (double)cnt;
+        } else if (P.m > 1) {
+          /* chunk score = log-sum-exp of its landmark scores: landmark r takes the share p_r */
+          double a[64], amax = -INFINITY, z = 0.0;
+          for (int64_t u = 0; u < P.m; ++u) {
+            a[u] = scale * dot_row(Qr ? Qr : Q, row, Klm, (bh * N + j) * P.m + u, d, dt);
+            if (a[u] > amax) amax = a[u];
+          }
+          for (int64_t u = 0; u < P.m; ++u) z += exp(a[u] - amax);
+          for (int64_t u = 0; u < P.m; ++u) {
+            double pu = exp(a[u] - amax) / z;
+            int64_t lr = (bh * N + j) * P.m + u;
+            for (int64_t e = 0; e < d; ++e) {
+              dS[row * d + e] += scale * ds * pu * elem(Klm, lr * d + e, dt);
+              dKlm[lr * d + e] += scale * ds * pu * qrv[e];
+            }
+          }
         } else {
           for (int64_t e = 0; e < d; ++e) {
             dS[row * d + e] += scale * ds * elem(Klm, (bh * N + j) * d + e, dt);
@@ -509,7 +543,8 @@ int oracle_bwd(const void* Q, const void* Qr, const void* K, const void* V, cons
                const int32_t* idx_in, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
                int64_t k, double scale, int dt, double* dQ, double* dQr, double* dK, double* dV, double* dKlm,
                int nthreads) {
-  return bwd_common(Q, Qr, K, V, Klm, 0, dO, idx_in, B, H, L, d, C, k, scale, dt, dQ, dQr, dK, dV, dKlm, nthreads);
+  return bwd_common(Q, Qr, K, V, Klm, 0, 1, dO, idx_in, B, H, L, d, C, k, scale, dt, dQ, dQr, dK, dV, dKlm,
+                    nthreads);
 }
 
 /*
@@ -525,8 +560,33 @@ int oracle_bwd_lf(const void* Q, const void* Qr, const void* K, const void* V, c
   int64_t N = L / C;
   void* Klm = malloc((size_t)(B * H * N * d) * (dt == DT_F32 ? 4 : 2));
   oracle_chunk_means(K, L, Klm, N, B, H, N, d, C, dt, nthreads);
-  int used = bwd_common(Q, Qr, K, V, Klm, 1, dO, idx_in, B, H, L, d, C, k, scale, dt, dQ, dQr, dK, dV, dKlm,
+  int used = bwd_common(Q, Qr, K, V, Klm, 1, 1, dO, idx_in, B, H, L, d, C, k, scale, dt, dQ, dQr, dK, dV, dKlm,
                         nthreads);
   free(Klm);
   return used;
+}
+
+/*
+ * Forward and backward with m landmarks per chunk (Klm [B,H,N,m,d], 1 <= m <= 64): the chunk score
+ * is the log-sum-exp of the chunk's landmark scores; dKlm is [B,H,N,m,d].
+ */
+int oracle_fwd_ml(const void* Q, const void* Qr, const void* K, const void* V, const void* Klm, int64_t m,
+                  int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t k, double scale,
+                  int dt, const int64_t* rows, int64_t nrows, int use_idx,
+                  int32_t* idx, double* sel, double* w, double* lse, double* O, int nthreads) {
+  if (m < 1 || m > 64) return -1;
+  int64_t N = (L + C - 1) / C;
+  prob_t P = {Q, K, V, Klm, Qr, B, H, L, d, C, k, N, L, N, scale, dt, 0, m};
+  int used = set_threads(nthreads);
+  fwd_rows(&P, rows, nrows, use_idx, NULL, idx, sel, w, lse, O);
+  return used;
+}
+
+int oracle_bwd_ml(const void* Q, const void* Qr, const void* K, const void* V, const void* Klm, int64_t m,
+                  const void* dO, const int32_t* idx_in, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
+                  int64_t k, double scale, int dt, double* dQ, double* dQr, double* dK, double* dV, double* dKlm,
+                  int nthreads) {
+  if (m < 1 || m > 64) return -1;
+  return bwd_common(Q, Qr, K, V, Klm, 0, m, dO, idx_in, B, H, L, d, C, k, scale, dt, dQ, dQr, dK, dV, dKlm,
+                    nthreads);
 }

@@ -665,3 +665,76 @@ def test_paged_decode_equals_contiguous_per_sequence(oracle_mod, lf):
         for j in range(nchunks[b]):
             np.testing.assert_array_equal(Kp[table[b, j]], conts[b][0][0, :, j * C:(j + 1) * C])
             np.testing.assert_array_equal(Lp[table[b, j]], conts[b][2][0, :, j])
+
+
+# --------------------------------------------------------------------------- several landmarks per chunk
+# Reading of "a few landmarks per chunk" with the softmax over a chunk's landmark scores (ai-feeds summary,
+# "Method" > "Input & chunking" and "Key modules" item 1): the chunk score is the log-sum-exp of them.
+
+
+def test_one_landmark_per_chunk_is_the_plain_operator(oracle_mod):
+    B, H, L, d, C, k = 1, 2, 1024, 16, 64, 4
+    x = rand_inputs(B, H, L, d, C=C, seed=60, dtype="bf16")
+    a = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], C, k)
+    b = oracle_mod.fwd_ml(x["Q"], x["K"], x["V"], np.ascontiguousarray(x["Klm"][:, :, :, None, :]), C, k)
+    for key in ("idx", "sel", "w", "lse", "O"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_duplicated_landmarks_shift_every_score_by_log2(oracle_mod):
+    B, H, L, d, C, k = 1, 2, 1024, 16, 64, 4
+    x = rand_inputs(B, H, L, d, C=C, seed=61, dtype="bf16")
+    a = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], C, k)
+    two = np.ascontiguousarray(np.stack([x["Klm"], x["Klm"]], axis=3))
+    b = oracle_mod.fwd_ml(x["Q"], x["K"], x["V"], two, C, k)
+    np.testing.assert_array_equal(a["idx"], b["idx"])
+    ok = a["idx"] >= 0
+    np.testing.assert_allclose(b["sel"][ok], a["sel"][ok] + math.log(2.0), rtol=0, atol=2e-6)
+    np.testing.assert_allclose(b["w"], a["w"], rtol=0, atol=2e-6)
+    np.testing.assert_allclose(b["O"], a["O"], rtol=0, atol=2e-5)
+
+
+def test_first_last_landmark_scores_are_logaddexp(oracle_mod):
+    B, H, L, d, C, k = 1, 1, 1024, 16, 64, 3
+    x = rand_inputs(B, H, L, d, C=C, seed=62, dtype="bf16")
+    lm = synth.first_last_landmarks(x["K"], C)
+    r = oracle_mod.fwd_ml(x["Q"], x["K"], x["V"], lm, C, k)
+    q, l2 = f64(x["Q"])[0, 0], f64(lm)[0, 0]
+    a = np.einsum("td,jrd->tjr", q, l2) / math.sqrt(d)
+    S = np.logaddexp(a[..., 0], a[..., 1]).astype(np.float32)
+    for t in range(0, L, 3):
+        c = t // C
+        m = min(k, c)
+        order = np.lexsort((np.arange(c), -S[t, :c]))[:m]
+        got = r["idx"][0, 0, t]
+        # exact ties aside, the selection is the lexsort of the fp32 scores
+        np.testing.assert_array_equal(got[:m], order)
+        np.testing.assert_allclose(r["sel"][0, 0, t, :m], S[t, order], rtol=1e-6, atol=1e-6)
+        assert abs(r["sel"][0, 0, t, k] - S[t, c]) <= 1e-6 * max(1.0, abs(S[t, c]))
+
+
+def test_several_landmarks_central_differences(oracle_mod):
+    B, H, L, d, C, k = 1, 1, 256, 8, 64, 2
+    x = rand_inputs(B, H, L, d, C=C, seed=63, dtype="f32", with_dO=True)
+    rng = np.random.default_rng(3)
+    lm = rng.standard_normal((B, H, L // C, 3, d), dtype=np.float32)
+    names = {"Q": "dQ", "K": "dK", "V": "dV", "Klm": "dKlm"}
+    inp = {"Q": x["Q"], "K": x["K"], "V": x["V"], "Klm": lm}
+    G = x["dO"]
+    idx = oracle_mod.fwd_ml(inp["Q"], inp["K"], inp["V"], lm, C, k)["idx"]
+    g = oracle_mod.bwd_ml(inp["Q"], inp["K"], inp["V"], lm, G, idx, C, k)
+    h = 2.0 ** -10
+    for name, gname in names.items():
+        for _ in range(12):
+            pos = tuple(int(rng.integers(0, s)) for s in inp[name].shape)
+            vals = []
+            for sgn in (1, -1):
+                p = dict(inp)
+                a = inp[name].copy()
+                a[pos] = np.float32(a[pos] + sgn * h)
+                p[name] = a
+                O = oracle_mod.fwd_ml(p["Q"], p["K"], p["V"], p["Klm"], C, k, idx=idx)["O"]
+                vals.append(float(np.sum(O * G.astype(np.float64))))
+            fd = (vals[0] - vals[1]) / (2 * h)
+            an = g[gname][pos]
+            assert abs(fd - an) <= 2e-4 * max(1.0, abs(an)), (name, pos, fd, an)
