@@ -71,7 +71,8 @@ enum {
   HILS_OP_TOPK = 1,
   HILS_OP_FWD = 2,
   HILS_OP_DECODE = 3,
-  HILS_OP_BWD = 4
+  HILS_OP_BWD = 4,
+  HILS_OP_FWD_ML = 5
 };
 
 /* Message of the last non-OK status returned to the calling thread ("" if none). */
@@ -244,6 +245,23 @@ hils_status hils_decode_step_lf(const void* q, const void* q_ret, const void* k_
                                 void* K_cache, void* V_cache, void* K_lm_cache, int64_t n_ctx, int64_t L_max,
                                 void* o, int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C,
                                 int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Several landmarks per chunk (ai-feeds summary, "Method" > "Input &
+ * chunking": a few landmarks per chunk, usually its first and last token;
+ * "Key modules" item 1: a softmax over a chunk's landmark scores before the
+ * chunk-level one).  K_lm is [B][H][N][m][d] (dt), 1 <= m <= 16; the chunk
+ * score is the log-sum-exp of its m landmark scores, for the past chunks and
+ * the own chunk alike; with m = 1 it is the plain score.  Otherwise as
+ * hils_sparse_attn_fwd_rq (Q_ret may be null).  The causal chunk scores are
+ * materialised in the workspace: hils_workspace_size(HILS_OP_FWD_ML, ...)
+ * bytes, B*H*L*N*4 more than HILS_OP_FWD.
+ */
+hils_status hils_sparse_attn_fwd_ml(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm,
+                                    int64_t m, int32_t* idx, float* sel_score, int select, void* O, float* w_out,
+                                    float* lse_out, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
+                                    int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
+                                    void* stream);
 
 /*
  * Batched decode over a paged cache (serving shapes: B sequences at their own

@@ -16,7 +16,7 @@ LIB = os.path.join(PKG, "libhils.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["hils_api.cpp", "profile.cpp", "scores_topk.hip", "route.hip", "attn_fwd.hip", "decode.hip", "attn_bwd.hip",
-           "landmark_free.hip"]
+           "landmark_free.hip", "multi_landmark.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -107,6 +107,8 @@ size_t carve_route(Carver& cv, const Dims& D, hils::RouteBufs& rb, int ppi) {
   return cv.off;
 }
 
+size_t ml_scores_bytes(const Dims& D) { return (size_t)D.B * D.H * D.L * D.N * sizeof(float); }
+
 size_t carve_fwd(void* base, const Dims& D, FwdWs* ws) {
   Carver cv(base);
   const int64_t BH = D.B * D.H;
@@ -153,9 +155,9 @@ hils_status check_ws(void* ws, size_t ws_bytes, size_t need) {
 }  // namespace
 
 static hils_status fwd_impl(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm, bool lf,
-                            int32_t* idx, float* sel_score, int select, void* O, float* w_out, float* lse_out,
-                            int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk, float scale,
-                            hils_dtype dt, void* ws, size_t ws_bytes, void* stream);
+                            int64_t mlm, int32_t* idx, float* sel_score, int select, void* O, float* w_out,
+                            float* lse_out, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk,
+                            float scale, hils_dtype dt, void* ws, size_t ws_bytes, void* stream);
 static hils_status decode_impl(const void* q, const void* q_ret, const void* k_new, const void* v_new, void* K_cache,
                                void* V_cache, const void* K_lm_cache, bool lf, int64_t n_ctx, int64_t L_max, void* o,
                                int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C, int64_t topk,
@@ -185,6 +187,11 @@ size_t hils_workspace_size(int op, int64_t B, int64_t H, int64_t L, int64_t d, i
       if (check_dims(B, H, L, d, C, topk, true, &D) != HILS_OK) return 0;
       FwdWs ws;
       return carve_fwd(nullptr, D, &ws);
+    }
+    case HILS_OP_FWD_ML: {
+      if (check_dims(B, H, L, d, C, topk, true, &D) != HILS_OK) return 0;
+      FwdWs ws;
+      return align_up(carve_fwd(nullptr, D, &ws)) + ml_scores_bytes(D);
     }
     case HILS_OP_BWD: {
       if (check_dims(B, H, L, d, C, topk, true, &D) != HILS_OK) return 0;
@@ -251,8 +258,8 @@ hils_status hils_sparse_attn_fwd_rq(const void* Q, const void* Q_ret, const void
                                     float* lse_out, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
                                     int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
                                     void* stream) {
-  return fwd_impl(Q, Q_ret, K, V, K_lm, false, idx, sel_score, select, O, w_out, lse_out, B, H, L, d, C, topk, scale,
-                  dt, ws, ws_bytes, stream);
+  return fwd_impl(Q, Q_ret, K, V, K_lm, false, 0, idx, sel_score, select, O, w_out, lse_out, B, H, L, d, C, topk,
+                  scale, dt, ws, ws_bytes, stream);
 }
 
 hils_status hils_sparse_attn_fwd_lf(const void* Q, const void* Q_ret, const void* K, const void* V, void* K_lm_out,
@@ -260,7 +267,18 @@ hils_status hils_sparse_attn_fwd_lf(const void* Q, const void* Q_ret, const void
                                     float* lse_out, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
                                     int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
                                     void* stream) {
-  return fwd_impl(Q, Q_ret, K, V, K_lm_out, true, idx, sel_score, select, O, w_out, lse_out, B, H, L, d, C, topk,
+  return fwd_impl(Q, Q_ret, K, V, K_lm_out, true, 0, idx, sel_score, select, O, w_out, lse_out, B, H, L, d, C, topk,
+                  scale, dt, ws, ws_bytes, stream);
+}
+
+hils_status hils_sparse_attn_fwd_ml(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm,
+                                    int64_t m, int32_t* idx, float* sel_score, int select, void* O, float* w_out,
+                                    float* lse_out, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C,
+                                    int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  if (m < 1 || m > 16) return fail(HILS_ERR_UNSUPPORTED, "landmarks per chunk must be in [1, 16] (got %lld)",
+                                   (long long)m);
+  return fwd_impl(Q, Q_ret, K, V, K_lm, false, m, idx, sel_score, select, O, w_out, lse_out, B, H, L, d, C, topk,
                   scale, dt, ws, ws_bytes, stream);
 }
 
@@ -283,9 +301,9 @@ hils_status hils_chunk_means(const void* K, void* K_lm, int64_t B, int64_t H, in
 }  // extern "C"
 
 static hils_status fwd_impl(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm, bool lf,
-                            int32_t* idx, float* sel_score, int select, void* O, float* w_out, float* lse_out,
-                            int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk, float scale,
-                            hils_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+                            int64_t mlm, int32_t* idx, float* sel_score, int select, void* O, float* w_out,
+                            float* lse_out, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk,
+                            float scale, hils_dtype dt, void* ws, size_t ws_bytes, void* stream) {
   Dims D;
   hils_status st;
   if ((st = check_dims(B, H, L, d, C, topk, true, &D)) != HILS_OK) return st;
@@ -303,9 +321,12 @@ static hils_status fwd_impl(const void* Q, const void* Q_ret, const void* K, con
   if (select != 0 && select != 1) return fail(HILS_ERR_INVALID_ARG, "select must be 0 or 1");
   if (!(scale > 0.f)) return fail(HILS_ERR_INVALID_ARG, "scale must be positive");
   FwdWs W;
-  const size_t need = carve_fwd(nullptr, D, &W);
+  const size_t need0 = carve_fwd(nullptr, D, &W);
+  // several landmarks per chunk: the causal chunk scores are materialised after the plain workspace
+  const size_t need = mlm > 0 ? align_up(need0) + ml_scores_bytes(D) : need0;
   if ((st = check_ws(ws, ws_bytes, need)) != HILS_OK) return st;
   carve_fwd(ws, D, &W);
+  float* S_ml = mlm > 0 ? reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(need0)) : nullptr;
   const int BH = (int)(B * H), iL = (int)L, iN = (int)D.N, ik = (int)topk, id = (int)d;
   hipStream_t s = (hipStream_t)stream;
   float* w = w_out ? w_out : W.w_tmp;
@@ -315,7 +336,10 @@ static hils_status fwd_impl(const void* Q, const void* Q_ret, const void* K, con
   // landmark-free chunks: the landmarks are the chunks' key means, formed here
   if (lf && (e = hils::launch_chunk_means(dt, id, K, (void*)K_lm, BH, L, D.N, iN, s)) != hipSuccess)
     return hip_status(e, "hils_sparse_attn_fwd: chunk means");
-  if (select) e = hils::launch_topk(dt, id, Qs, K_lm, W.klm_frag, idx, sel_score, w, BH, iL, iN, ik, scale, s);
+  if (mlm > 0)
+    e = hils::launch_ml_selection(dt, id, Qs, K_lm, (int)mlm, S_ml, idx, sel_score, w, BH, iL, iN, ik, select, scale,
+                                  s);
+  else if (select) e = hils::launch_topk(dt, id, Qs, K_lm, W.klm_frag, idx, sel_score, w, BH, iL, iN, ik, scale, s);
   else e = hils::launch_fixed_selection(dt, id, Qs, K_lm, idx, sel_score, w, BH, iL, iN, ik, scale, s);
   if (e != hipSuccess) return hip_status(e, "hils_sparse_attn_fwd: selection");
   // ... and the own chunk is scored by the mean of its keys up to the query

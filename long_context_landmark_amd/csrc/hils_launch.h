@@ -106,6 +106,11 @@ hipError_t launch_decode_paged(int dt, int d, const void* q, const void* qr, con
                                void* Kp, void* Vp, void* Klm_p, bool lf, const int32_t* page_table, int max_pages,
                                int64_t pages, const int64_t* n_ctx, int64_t n_max, int B, int H, void* o,
                                int32_t* idx, float* w, int k, float scale, const DecodeBufs& ws, hipStream_t st);
+// several landmarks per chunk (Klm [BH][N][m][d]): causal chunk scores (log-sum-exp over a chunk's landmarks)
+// into S [BH][L][N], then the selection (select = 1) or the scores of the caller's idx, and the weights
+hipError_t launch_ml_selection(int dt, int d, const void* Qs, const void* Klm, int m, float* S, int32_t* idx,
+                               float* sel, float* w, int BH, int L, int N, int k, int select, float scale,
+                               hipStream_t st);
 // landmark-free chunk keys: rows 0..nchunks-1 of Klm ([BH][Nlm][d]) = means of the key rows of each chunk
 // (K: [BH][Lk][d])
 hipError_t launch_chunk_means(int dt, int d, const void* K, void* Klm, int BH, int64_t Lk, int64_t Nlm, int nchunks,

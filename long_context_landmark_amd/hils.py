@@ -44,6 +44,7 @@ _lib.hils_chunk_means.argtypes = [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, 
 _lib.hils_sparse_attn_fwd_lf.argtypes = _lib.hils_sparse_attn_fwd_rq.argtypes
 _lib.hils_decode_step_lf.argtypes = _lib.hils_decode_step_rq.argtypes
 _lib.hils_sparse_attn_bwd_lf.argtypes = _lib.hils_sparse_attn_bwd_rq.argtypes
+_lib.hils_sparse_attn_fwd_ml.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64] + _lib.hils_sparse_attn_fwd.argtypes[4:]
 _lib.hils_decode_step_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _int, _vp, _vp,
                                         _vp, _i64, _i64, _i64, _i64, _i64, _f, _int, _vp, _sz, _vp]
 _lib.hils_profile_enable.argtypes = [_int]
@@ -55,7 +56,7 @@ for _fn in ("hils_landmark_scores", "hils_topk_select", "hils_sparse_attn_fwd", 
             "hils_sparse_attn_bwd"):
     getattr(_lib, _fn).restype = _int
 
-OP_SCORES, OP_TOPK, OP_FWD, OP_DECODE, OP_BWD = range(5)
+OP_SCORES, OP_TOPK, OP_FWD, OP_DECODE, OP_BWD, OP_FWD_ML = range(6)
 BF16, FP32 = 0, 1
 
 EXPORTS = ("hils_last_error", "hils_version", "hils_workspace_size", "hils_landmark_scores", "hils_topk_select",
@@ -355,3 +356,34 @@ def decode_step_paged(q, k_new, v_new, K_pages, V_pages, K_lm_pages, page_table,
                                        1 if landmark_free else 0, _p(o), _p(idx), _p(w), B, H, d, C, k,
                                        _scale(d, scale), _dt(q), _p(wsb), n, _stream()))
     return o, idx, w
+
+
+def sparse_attn_fwd_ml(Q, K, V, K_lm, k, C=64, scale=None, idx=None, save_for_backward=False, ws=None, out=None,
+                       Q_ret=None):
+    """Forward with several landmarks per chunk: K_lm [B,H,N,m,d]; the chunk score is the log-sum-exp of the
+    chunk's landmark scores.  Returns (O, idx, sel_score, w, lse) like ``sparse_attn_fwd``."""
+    _contig(Q, K, V, K_lm, idx, Q_ret)
+    _like(Q_ret, Q, "Q_ret")
+    B, H, L, d = Q.shape
+    if K_lm.dim() != 5 or K_lm.shape[:3] != (B, H, L // C) or K_lm.shape[4] != d or K_lm.dtype != Q.dtype:
+        raise ValueError("K_lm must be [B,H,L/C,m,d] of Q's dtype")
+    m = K_lm.shape[3]
+    for t in (K, V):
+        if t.shape != Q.shape or t.dtype != Q.dtype:
+            raise ValueError("Q, K, V must share shape and dtype")
+    select = 1
+    if idx is None:
+        idx = torch.empty((B, H, L, k + 1), dtype=torch.int32, device=Q.device)
+    else:
+        select = 0
+        if idx.shape != (B, H, L, k + 1) or idx.dtype != torch.int32:
+            raise ValueError("idx must be int32 [B,H,L,k+1]")
+    sel = torch.empty((B, H, L, k + 1), dtype=torch.float32, device=Q.device)
+    w = torch.empty_like(sel) if save_for_backward else None
+    lse = torch.empty_like(sel) if save_for_backward else None
+    O = out if out is not None else torch.empty_like(Q)
+    wsb, n = _workspace(OP_FWD_ML, B, H, L, d, C, k, Q.device, ws)
+    _check(_lib.hils_sparse_attn_fwd_ml(_p(Q), _p(Q_ret), _p(K), _p(V), _p(K_lm), m, _p(idx), _p(sel), select, _p(O),
+                                        _p(w), _p(lse), B, H, L, d, C, k, _scale(d, scale), _dt(Q), _p(wsb), n,
+                                        _stream()))
+    return O, idx, sel, w, lse

@@ -168,3 +168,17 @@ def test_paged_decode_validates(lib, hils):
                                       FAKE, nd, None) == INVALID
     assert lib.hils_decode_step_paged(*head, 5, 10, FAKE, 100, 0, FAKE, FAKE, FAKE, 2, 2, 64, 64, 4, 0.125, 0,
                                       FAKE, nd - 16, None) == WORKSPACE
+
+
+def test_multi_landmark_forward_validates(lib, hils):
+    need = hils.workspace_size(hils.OP_FWD_ML, 1, 2, 1024, 64, 64, 4)
+    # the plain forward's workspace (aligned) plus the causal chunk scores, B*H*L*N fp32
+    base = hils.workspace_size(hils.OP_FWD, 1, 2, 1024, 64, 64, 4)
+    assert base + 2 * 1024 * 16 * 4 <= need < base + 2 * 1024 * 16 * 4 + 256
+    tail = [1, FAKE, None, None, 1, 2, 1024, 64, 64, 4, 0.125, 0]
+    assert lib.hils_sparse_attn_fwd_ml(FAKE, None, FAKE, FAKE, FAKE, 0, FAKE, FAKE, *tail, FAKE, need,
+                                       None) == UNSUPPORTED
+    assert lib.hils_sparse_attn_fwd_ml(FAKE, None, FAKE, FAKE, FAKE, 17, FAKE, FAKE, *tail, FAKE, need,
+                                       None) == UNSUPPORTED
+    assert lib.hils_sparse_attn_fwd_ml(FAKE, None, FAKE, FAKE, FAKE, 2, FAKE, FAKE, *tail, FAKE, need - 16,
+                                       None) == WORKSPACE

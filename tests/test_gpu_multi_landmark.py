@@ -1,0 +1,110 @@
+"""Parity of the several-landmarks-per-chunk forward with the CPU oracle.
+
+A chunk's score is the log-sum-exp of its landmark scores (the HiLS summary page, "Method" >
+"Input & chunking" and "Key modules" item 1).  Landmarks: the keys of each chunk's first and last
+token, or random rows.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_landmark_amd import synth
+from gpu_util import GAP, assert_close, dev, f32, say, to_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _landmarks(x, kind, m, seed):
+    if kind == "firstlast":
+        return synth.first_last_landmarks(x["K"], 64)
+    B, H, L, d = x["K"].shape
+    lm = np.random.default_rng(seed).standard_normal((B, H, L // 64, m, d), dtype=np.float32)
+    return synth.f32_to_bf16_bits(lm) if x["K"].dtype == np.uint16 else lm
+
+
+def _check_sets(gi, ri, Qs, lm, k):
+    """Index sets equal, or differing only where the oracle's chunk scores are within GAP of the m-th best."""
+    B, H, L, _ = gi.shape
+    d = Qs.shape[-1]
+    g, r = gi.reshape(-1, k + 1), ri.reshape(-1, k + 1)
+    t_of = np.arange(g.shape[0]) % L
+    np.testing.assert_array_equal(g[:, k], t_of // 64)
+    bad = []
+    for row in range(g.shape[0]):
+        c = t_of[row] // 64
+        m = min(k, c)
+        assert np.all(g[row, m:k] == -1)
+        a, b = set(g[row, :m].tolist()), set(r[row, :m].tolist())
+        if a == b:
+            continue
+        bh = row // L
+        q = synth.as_f32(Qs.reshape(-1, L, d)[bh, t_of[row]]).astype(np.float64)
+        lmf = synth.as_f32(lm.reshape(B * H, lm.shape[2], lm.shape[3], d)[bh, :c]).astype(np.float64)
+        a_r = lmf @ q / math.sqrt(d)
+        sc = np.log(np.exp(a_r - a_r.max(1, keepdims=True)).sum(1)) + a_r.max(1)
+        sc = sc.astype(np.float32)
+        mth = np.sort(sc)[::-1][m - 1]
+        for j in a ^ b:
+            assert abs(float(sc[j]) - float(mth)) < GAP, (row, j)
+        bad.append(row)
+    say(f"  selection: {len(bad)} of {g.shape[0]} rows differ on near ties")
+    return np.asarray(bad, np.int64)
+
+
+@pytest.mark.parametrize("dtype,B,H,L,d,k,kind,m", [
+    ("bf16", 1, 2, 2112, 64, 8, "firstlast", 2),
+    ("bf16", 1, 2, 1024, 128, 16, "firstlast", 2),
+    ("f32", 1, 2, 1024, 64, 4, "firstlast", 2),
+    ("bf16", 1, 2, 2048, 64, 8, "random", 3),
+])
+def test_fwd_multi_landmark(hils, gpu, dtype, B, H, L, d, k, kind, m):
+    say(f"fwd several landmarks dtype={dtype} B={B} H={H} L={L} d={d} k={k} landmarks={kind}x{m}")
+    x = synth.prefill_inputs(B, H, L, d, C=64, seed=800 + L + d + m, dtype=dtype)
+    lm = _landmarks(x, kind, m, seed=801 + L)
+    t = to_inputs(x, ("Q", "K", "V"))
+    O, idx, sel, w, lse = hils.sparse_attn_fwd_ml(t["Q"], t["K"], t["V"], dev(lm), k, save_for_backward=True)
+    torch.cuda.synchronize()
+    ref = oracle.fwd_ml(x["Q"], x["K"], x["V"], lm, 64, k)
+    gi = idx.cpu().numpy()
+    bad = _check_sets(gi, ref["idx"], x["Q"], lm, k)
+    ro = ref["O"].reshape(-1, d).copy()
+    rw = ref["w"].reshape(-1, k + 1).copy()
+    ri = ref["idx"].reshape(-1, k + 1).copy()
+    if len(bad):
+        fix = oracle.fwd_ml(x["Q"], x["K"], x["V"], lm, 64, k, rows=bad, idx=gi.reshape(-1, k + 1)[bad])
+        ro[bad], rw[bad], ri[bad] = fix["O"], fix["w"], fix["idx"]
+    tol = (5e-3, 3e-3) if dtype == "f32" else (2e-2, 1e-2)
+    assert_close(f32(O).reshape(-1, d), ro, "O", *tol)
+    gw, gx = f32(w).reshape(-1, k + 1), gi.reshape(-1, k + 1)
+    for r in range(0, gx.shape[0], 5):
+        gm = {int(j): gw[r, s] for s, j in enumerate(gx[r]) if j >= 0}
+        om = {int(j): rw[r, s] for s, j in enumerate(ri[r]) if j >= 0}
+        assert gm.keys() == om.keys()
+        for j in gm:
+            assert abs(gm[j] - om[j]) < 2e-5, (r, j, gm[j], om[j])
+    # own-chunk scores
+    own = f32(sel).reshape(-1, k + 1)[:, k]
+    assert np.abs(own - ref["sel"].reshape(-1, k + 1)[:, k]).max() < 1e-4
+
+
+def test_fwd_multi_landmark_fixed_selection(hils, gpu):
+    B, H, L, d, k = 1, 2, 1024, 64, 4
+    x = synth.prefill_inputs(B, H, L, d, C=64, seed=810, dtype="bf16")
+    lm = synth.first_last_landmarks(x["K"], 64)
+    ref = oracle.fwd_ml(x["Q"], x["K"], x["V"], lm, 64, k)
+    idx = ref["idx"].copy()
+    rng = np.random.default_rng(1)
+    for bh in range(B * H):
+        for tt in range(L):
+            c = tt // 64
+            if c > k:
+                idx[0, bh, tt, :k] = np.sort(rng.choice(c, size=k, replace=False))
+    t = to_inputs(x, ("Q", "K", "V"))
+    O, _, sel, w, lse = hils.sparse_attn_fwd_ml(t["Q"], t["K"], t["V"], dev(lm), k, idx=torch.from_numpy(idx).to(gpu),
+                                                save_for_backward=True)
+    want = oracle.fwd_ml(x["Q"], x["K"], x["V"], lm, 64, k, idx=idx)
+    assert_close(f32(O), want["O"], "O (fixed selection)")
+    assert_close(f32(w), want["w"], "w (fixed selection)", 1e-5, 1e-5)
