@@ -264,6 +264,20 @@ hils_status hils_sparse_attn_fwd_ml(const void* Q, const void* Q_ret, const void
                                     void* stream);
 
 /*
+ * Backward of hils_sparse_attn_fwd_ml (selection held fixed), 1 <= m <= 4:
+ * as hils_sparse_attn_bwd_rq with the same K_lm [B][H][N][m][d]; landmark u
+ * of a kept chunk takes the share p_u = softmax_u of the chunk's landmark
+ * scores of its score gradient, so dK_lm is [B][H][N][m][d] float and dQ (or
+ * dQ_ret) gets scale * ds * sum_u p_u K_lm[j][u].  fp32 inputs: d = 64 only.
+ * Workspace: hils_workspace_size(HILS_OP_BWD, ...).
+ */
+hils_status hils_sparse_attn_bwd_ml(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm,
+                                    int64_t m, const void* dO, const int32_t* idx, const float* w, const float* lse,
+                                    float* dQ, float* dQ_ret, float* dK, float* dV, float* dK_lm, int64_t B,
+                                    int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk, float scale,
+                                    hils_dtype dt, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Batched decode over a paged cache (serving shapes: B sequences at their own
  * positions, pages of one chunk).  The same step as hils_decode_step_rq /
  * hils_decode_step_lf (ai-feeds summary "Limitations": the per-step landmark

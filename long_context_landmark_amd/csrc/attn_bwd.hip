@@ -333,7 +333,7 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* __restri
                                                         const int32_t* __restrict__ idx, const float* __restrict__ w,
                                                         const T* __restrict__ Klm, float* __restrict__ ds_out,
                                                         float* __restrict__ dQ, float* __restrict__ dQr, int64_t rows,
-                                                        int L, int N, int k, float scale, int lf) {
+                                                        int L, int N, int k, float scale, int skip) {
   constexpr int V8 = D / 8;                    // threads per row
   constexpr int LW = 2 * Elem<T>::bytes;       // 32-bit words of eight landmark elements
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -375,7 +375,8 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* __restri
   }
   // RQ: the landmark scores came from separate retrieval queries, whose gradient (the
   // ds * Klm terms) goes to dQr; dQ then keeps the in-chunk attention terms only.
-  // lf (landmark-free chunks): the own slot's landmark is not a K_lm row; lf_bwd adds its term
+  // skip = 1 (landmark-free chunks): the own slot's landmark is not a K_lm row, lf_bwd adds its term;
+  // skip = 2 (several landmarks per chunk): no slot's is, ml_dq adds them
   float acc[8], accr[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = accr[e] = 0.f;
@@ -384,7 +385,7 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* __restri
     if (!ok[r]) continue;
     const float ds = wr[r] * (dr[r] - Dsum);
     if (c8 == 0) ds_out[row * k1 + r] = ds;
-    const float sds = (lf && r == k) ? 0.f : scale * ds;
+    const float sds = (skip == 2 || (skip == 1 && r == k)) ? 0.f : scale * ds;
     _Float16 h[8];
     __builtin_memcpy(h, &raw[r], 16);
     T lm[8];
@@ -471,7 +472,7 @@ __global__ __launch_bounds__(256) void klm_bwd_kernel(const T* __restrict__ Q, c
 }
 
 template <typename T, int D>
-static hipError_t bwd_t(const void* Q, const void* Qr, const void* K, const void* V, const void* Klm, bool lf,
+static hipError_t bwd_t(const void* Q, const void* Qr, const void* K, const void* V, const void* Klm, bool lf, int mlm,
                         const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ, float* dQr,
                         float* dK, float* dV, float* dKlm, int BH, int L, int N, int k, float scale,
                         const BwdBufs& ws, hipStream_t st) {
@@ -483,19 +484,27 @@ static hipError_t bwd_t(const void* Q, const void* Qr, const void* K, const void
               ws.trash, ws.trash_f, dK, dV, L, N, k, scale);
   const dim3 rgrid((unsigned)((rows * (D / 8) + 255) / 256));
   const bool rq = Qr != nullptr;
+  const int skip = mlm > 0 ? 2 : (lf ? 1 : 0);
   if (k <= 8 && !rq)
     HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 9, false>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx,
-                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, (int)lf);
+                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, skip);
   else if (!rq)
     HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 17, false>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx,
-                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, (int)lf);
+                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, skip);
   else if (k <= 8)
     HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 9, true>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx,
-                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, (int)lf);
+                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, skip);
   else
     HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 17, true>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx,
-                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, (int)lf);
+                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, skip);
   // dKlm_j sums ds_tj times the query that scored the landmark
+  if (mlm > 0) {
+    // several landmarks per chunk: the score paths through every landmark's share
+    hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return e2;
+    return launch_ml_bwd(Elem<T>::bytes == 2 ? 0 : 1, D, rq ? Qr : Q, Klm, mlm, idx, ws.ds, ws.rb.chunk_off,
+                         ws.rb.pairs, rq ? dQr : dQ, dKlm, BH, L, N, k, scale, st);
+  }
   HILS_LAUNCH("klm_bwd", (klm_bwd_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)(rq ? Qr : Q), ws.ds,
               ws.rb.chunk_off, ws.rb.pairs, dKlm, L, N, k, scale, (int)lf);
   if (lf) {
@@ -508,18 +517,18 @@ static hipError_t bwd_t(const void* Q, const void* Qr, const void* K, const void
 }
 
 hipError_t launch_bwd(int dt, int d, const void* Q, const void* Qr, const void* K, const void* V, const void* Klm,
-                      bool lf, const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
+                      bool lf, int mlm, const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
                       float* dQr, float* dK, float* dV, float* dKlm, int BH, int L, int N, int k, float scale,
                       const BwdBufs& ws, hipStream_t st) {
   if ((Qr == nullptr) != (dQr == nullptr)) return hipErrorInvalidValue;
   if (dt == 0)
-    return d == 64 ? bwd_t<bf16_t, 64>(Q, Qr, K, V, Klm, lf, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k,
+    return d == 64 ? bwd_t<bf16_t, 64>(Q, Qr, K, V, Klm, lf, mlm, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k,
                                        scale, ws, st)
-                   : bwd_t<bf16_t, 128>(Q, Qr, K, V, Klm, lf, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k,
+                   : bwd_t<bf16_t, 128>(Q, Qr, K, V, Klm, lf, mlm, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k,
                                         scale, ws, st);
   // fp32 inputs: head dim 64 only (the fp32 LDS tiles of d = 128 exceed a workgroup's LDS)
   if (d != 64) return hipErrorInvalidValue;
-  return bwd_t<float, 64>(Q, Qr, K, V, Klm, lf, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k, scale, ws, st);
+  return bwd_t<float, 64>(Q, Qr, K, V, Klm, lf, mlm, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k, scale, ws, st);
 }
 
 }  // namespace hils

@@ -163,7 +163,7 @@ static hils_status decode_impl(const void* q, const void* q_ret, const void* k_n
                                int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C, int64_t topk,
                                float scale, hils_dtype dt, void* ws, size_t ws_bytes, void* stream);
 static hils_status bwd_impl(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm, bool lf,
-                            const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
+                            int64_t mlm, const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
                             float* dQ_ret, float* dK, float* dV, float* dK_lm, int64_t B, int64_t H, int64_t L,
                             int64_t d, int64_t C, int64_t topk, float scale, hils_dtype dt, void* ws,
                             size_t ws_bytes, void* stream);
@@ -435,7 +435,7 @@ hils_status hils_sparse_attn_bwd_rq(const void* Q, const void* Q_ret, const void
                                     float* dQ_ret, float* dK, float* dV, float* dK_lm, int64_t B, int64_t H,
                                     int64_t L, int64_t d, int64_t C, int64_t topk, float scale, hils_dtype dt,
                                     void* ws, size_t ws_bytes, void* stream) {
-  return bwd_impl(Q, Q_ret, K, V, K_lm, false, dO, idx, w, lse, dQ, dQ_ret, dK, dV, dK_lm, B, H, L, d, C, topk, scale,
+  return bwd_impl(Q, Q_ret, K, V, K_lm, false, 0, dO, idx, w, lse, dQ, dQ_ret, dK, dV, dK_lm, B, H, L, d, C, topk, scale,
                   dt, ws, ws_bytes, stream);
 }
 
@@ -444,14 +444,25 @@ hils_status hils_sparse_attn_bwd_lf(const void* Q, const void* Q_ret, const void
                                     float* dQ_ret, float* dK, float* dV, float* dK_lm, int64_t B, int64_t H,
                                     int64_t L, int64_t d, int64_t C, int64_t topk, float scale, hils_dtype dt,
                                     void* ws, size_t ws_bytes, void* stream) {
-  return bwd_impl(Q, Q_ret, K, V, K_lm, true, dO, idx, w, lse, dQ, dQ_ret, dK, dV, dK_lm, B, H, L, d, C, topk, scale,
-                  dt, ws, ws_bytes, stream);
+  return bwd_impl(Q, Q_ret, K, V, K_lm, true, 0, dO, idx, w, lse, dQ, dQ_ret, dK, dV, dK_lm, B, H, L, d, C, topk,
+                  scale, dt, ws, ws_bytes, stream);
+}
+
+hils_status hils_sparse_attn_bwd_ml(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm,
+                                    int64_t m, const void* dO, const int32_t* idx, const float* w, const float* lse,
+                                    float* dQ, float* dQ_ret, float* dK, float* dV, float* dK_lm, int64_t B,
+                                    int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk, float scale,
+                                    hils_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+  if (m < 1 || m > 4)
+    return fail(HILS_ERR_UNSUPPORTED, "backward: landmarks per chunk must be in [1, 4] (got %lld)", (long long)m);
+  return bwd_impl(Q, Q_ret, K, V, K_lm, false, m, dO, idx, w, lse, dQ, dQ_ret, dK, dV, dK_lm, B, H, L, d, C, topk,
+                  scale, dt, ws, ws_bytes, stream);
 }
 
 }  // extern "C"
 
 static hils_status bwd_impl(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm, bool lf,
-                            const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
+                            int64_t mlm, const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
                             float* dQ_ret, float* dK, float* dV, float* dK_lm, int64_t B, int64_t H, int64_t L,
                             int64_t d, int64_t C, int64_t topk, float scale, hils_dtype dt, void* ws,
                             size_t ws_bytes, void* stream) {
@@ -481,7 +492,7 @@ static hils_status bwd_impl(const void* Q, const void* Q_ret, const void* K, con
   const size_t need = carve_bwd(nullptr, D, &W);
   if ((st = check_ws(ws, ws_bytes, need)) != HILS_OK) return st;
   carve_bwd(ws, D, &W);
-  return hip_status(hils::launch_bwd(dt, (int)d, Q, Q_ret, K, V, K_lm, lf, dO, idx, w, lse, dQ, dQ_ret, dK, dV, dK_lm,
+  return hip_status(hils::launch_bwd(dt, (int)d, Q, Q_ret, K, V, K_lm, lf, (int)mlm, dO, idx, w, lse, dQ, dQ_ret, dK, dV, dK_lm,
                                      (int)(B * H), (int)L, (int)D.N, (int)topk, scale, W, (hipStream_t)stream),
                     "hils_sparse_attn_bwd");
 }

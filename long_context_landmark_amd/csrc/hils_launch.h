@@ -88,7 +88,7 @@ struct BwdBufs {
 // lf: landmark-free chunks (Klm holds the key means); the score gradients are carried into dK as well,
 // and dKlm receives the past chunks' mean gradient
 hipError_t launch_bwd(int dt, int d, const void* Q, const void* Qr, const void* K, const void* V, const void* Klm,
-                      bool lf, const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
+                      bool lf, int mlm, const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
                       float* dQr, float* dK, float* dV, float* dKlm, int BH, int L, int N, int k, float scale,
                       const BwdBufs& ws, hipStream_t st);
 // landmark-free backward tail, per (chunk, head): the own slot's ds against the causal means into dQs, and
@@ -111,6 +111,11 @@ hipError_t launch_decode_paged(int dt, int d, const void* q, const void* qr, con
 hipError_t launch_ml_selection(int dt, int d, const void* Qs, const void* Klm, int m, float* S, int32_t* idx,
                                float* sel, float* w, int BH, int L, int N, int k, int select, float scale,
                                hipStream_t st);
+// backward tail of several landmarks per chunk (1 <= m <= 4; fp32: d = 64): dKlm [BH][N][m][d] over each
+// chunk's pairs, and every slot's score term into dQs
+hipError_t launch_ml_bwd(int dt, int d, const void* Qs, const void* Klm, int m, const int32_t* idx, const float* ds,
+                         const int* chunk_off, const int* pairs, float* dQs, float* dKlm, int BH, int L, int N, int k,
+                         float scale, hipStream_t st);
 // landmark-free chunk keys: rows 0..nchunks-1 of Klm ([BH][Nlm][d]) = means of the key rows of each chunk
 // (K: [BH][Lk][d])
 hipError_t launch_chunk_means(int dt, int d, const void* K, void* Klm, int BH, int64_t Lk, int64_t Nlm, int nchunks,

@@ -164,3 +164,204 @@ hipError_t launch_ml_selection(int dt, int d, const void* Qs, const void* Klm, i
 }
 
 }  // namespace hils
+
+namespace hils {
+
+// Backward of the log-sum-exp chunk scores.  For a pair (query t, kept chunk j) with score gradient
+// ds (from dq_reduce) and landmark shares p_u = softmax_u(scale qs_t . Klm_j,u):
+//   ml_klm_bwd  one workgroup per (chunk, head), the chunk's pairs in routing order (its own queries
+//               first): dKlm_j,u = scale * sum ds p_u qs_t.  Four lanes per pair split the head
+//               dimension; the chunk's landmark rows sit in LDS.  Deterministic, no atomics.
+//   ml_dq       one group of D/8 lanes per query row: dQs_t += scale * sum over slots of
+//               ds sum_u p_u Klm_j,u (read, added to and written).
+template <typename T, int D, int MM>
+__global__ __launch_bounds__(256) void ml_klm_bwd_kernel(const T* __restrict__ Qs, const T* __restrict__ Klm,
+                                                         const float* __restrict__ ds,
+                                                         const int* __restrict__ chunk_off,
+                                                         const int* __restrict__ pairs, float* __restrict__ dKlm,
+                                                         int L, int N, int k, int m, float scale) {
+  constexpr int QD = D / 4;
+  constexpr int EPP = 16 / Elem<T>::bytes;
+  __shared__ float lmv[MM][D];
+  __shared__ float red[64][D + 1];
+  const int j = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int p = tid >> 2, qt = tid & 3;
+  const int k1 = k + 1;
+  for (int i = tid; i < m * D; i += 256)
+    lmv[i / D][i % D] = Elem<T>::to_f32(Klm, ((int64_t)bh * N + j) * m * D + i);
+  __syncthreads();
+  const int* co = chunk_off + (int64_t)bh * (N + 1);
+  const int p_begin = co[j], p_end = co[j + 1];
+  const int* pl = pairs + (int64_t)bh * L * k;
+  const int ntiles = 1 + (p_end - p_begin + 63) / 64;
+  float acc[MM][QD];
+#pragma unroll
+  for (int u = 0; u < MM; ++u)
+#pragma unroll
+    for (int e = 0; e < QD; ++e) acc[u][e] = 0.f;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    int t, slot;
+    bool valid = true;
+    if (tile == 0) {
+      t = j * 64 + p;
+      slot = k;
+    } else {
+      const int pp = p_begin + (tile - 1) * 64 + p;
+      valid = pp < p_end;
+      const int pe = valid ? pl[pp] : 0;
+      t = pe >> 5;
+      slot = pe & 31;
+    }
+    // all four lanes of a pair take the same branch, so the shuffles below stay within valid pairs
+    if (!valid) continue;
+    const int64_t row = (int64_t)bh * L + t;
+    const float dsv = ds[row * k1 + slot];
+    float qv[QD];
+    const T* qp = Qs + row * D + qt * QD;
+#pragma unroll
+    for (int u = 0; u < QD / EPP; ++u) {
+      const int4 raw = *reinterpret_cast<const int4*>(qp + u * EPP);
+      T vals[EPP];
+      __builtin_memcpy(vals, &raw, 16);
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) qv[u * EPP + e] = Elem<T>::to_f32(vals, e);
+    }
+    float a[MM], amax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < MM; ++u) {
+      float dot = 0.f;
+      if (u < m) {
+#pragma unroll
+        for (int e = 0; e < QD; ++e) dot += qv[e] * lmv[u][qt * QD + e];
+      }
+      dot += lane_xor(dot, 1);
+      dot += lane_xor(dot, 2);
+      a[u] = scale * dot;
+      if (u < m) amax = fmaxf(amax, a[u]);
+    }
+    float z = 0.f;
+#pragma unroll
+    for (int u = 0; u < MM; ++u) z += u < m ? __expf(a[u] - amax) : 0.f;
+    const float g = dsv / z;
+#pragma unroll
+    for (int u = 0; u < MM; ++u) {
+      const float c = u < m ? g * __expf(a[u] - amax) : 0.f;
+#pragma unroll
+      for (int e = 0; e < QD; ++e) acc[u][e] += c * qv[e];
+    }
+  }
+  for (int u = 0; u < m && u < MM; ++u) {
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < QD; ++e) red[p][qt * QD + e] = acc[u][e];
+    __syncthreads();
+    if (tid < D) {
+      float s = 0.f;
+      for (int q = 0; q < 64; ++q) s += red[q][tid];
+      dKlm[(((int64_t)bh * N + j) * m + u) * D + tid] = scale * s;
+    }
+  }
+}
+
+template <typename T, int D, int MM>
+__global__ __launch_bounds__(256) void ml_dq_kernel(const T* __restrict__ Qs, const T* __restrict__ Klm,
+                                                    const int32_t* __restrict__ idx, const float* __restrict__ ds,
+                                                    float* __restrict__ dQs, int64_t rows, int L, int N, int k, int m,
+                                                    float scale) {
+  constexpr int V8 = D / 8;  // lanes per row, eight elements each
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / V8;
+  const int c8 = (int)(gid % V8);
+  // rows are whole lane groups (V8 divides 64), so every lane of a group is live or none is
+  if (row >= rows) return;
+  const int64_t bh = row / L;
+  const int k1 = k + 1;
+  float qv[8];
+  {
+    T vals[8];
+    if (Elem<T>::bytes == 2) {
+      const int4 raw = *reinterpret_cast<const int4*>(Qs + row * D + 8 * c8);
+      __builtin_memcpy(vals, &raw, 16);
+    } else {
+      const int4 r0 = *reinterpret_cast<const int4*>(Qs + row * D + 8 * c8);
+      const int4 r1 = *reinterpret_cast<const int4*>(Qs + row * D + 8 * c8 + 4);
+      __builtin_memcpy(vals, &r0, 16);
+      __builtin_memcpy(reinterpret_cast<char*>(vals) + 16, &r1, 16);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[e] = Elem<T>::to_f32(vals, e);
+  }
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int r = 0; r < k1; ++r) {
+    const int j = idx[row * k1 + r];
+    if (j < 0 || j >= N) continue;  // the same for every lane of the row
+    const float dsv = ds[row * k1 + r];
+    float lv[MM][8], a[MM], amax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < MM; ++u) {
+      float dot = 0.f;
+      if (u < m) {
+        const T* lp = Klm + ((bh * N + j) * m + u) * D + 8 * c8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          lv[u][e] = Elem<T>::to_f32(lp, e);
+          dot += qv[e] * lv[u][e];
+        }
+      }
+#pragma unroll
+      for (int msk = 1; msk < V8; msk <<= 1) dot += lane_xor(dot, msk);
+      a[u] = scale * dot;
+      if (u < m) amax = fmaxf(amax, a[u]);
+    }
+    float z = 0.f;
+#pragma unroll
+    for (int u = 0; u < MM; ++u) z += u < m ? __expf(a[u] - amax) : 0.f;
+    const float g = scale * dsv / z;
+#pragma unroll
+    for (int u = 0; u < MM; ++u) {
+      if (u >= m) continue;
+      const float cu = g * __expf(a[u] - amax);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += cu * lv[u][e];
+    }
+  }
+  float4* out = reinterpret_cast<float4*>(dQs + row * D + 8 * c8);
+  float4 o0 = out[0], o1 = out[1];
+  o0.x += acc[0];
+  o0.y += acc[1];
+  o0.z += acc[2];
+  o0.w += acc[3];
+  o1.x += acc[4];
+  o1.y += acc[5];
+  o1.z += acc[6];
+  o1.w += acc[7];
+  out[0] = o0;
+  out[1] = o1;
+}
+
+template <typename T, int D>
+static hipError_t ml_bwd_t(const void* Qs, const void* Klm, int m, const int32_t* idx, const float* ds,
+                           const int* chunk_off, const int* pairs, float* dQs, float* dKlm, int BH, int L, int N,
+                           int k, float scale, hipStream_t st) {
+  HILS_LAUNCH("ml_klm_bwd", (ml_klm_bwd_kernel<T, D, 4>), dim3(N, BH), dim3(256), 0, st, (const T*)Qs,
+              (const T*)Klm, ds, chunk_off, pairs, dKlm, L, N, k, m, scale);
+  const int64_t rows = (int64_t)BH * L;
+  HILS_LAUNCH("ml_dq", (ml_dq_kernel<T, D, 4>), dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, st,
+              (const T*)Qs, (const T*)Klm, idx, ds, dQs, rows, L, N, k, m, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_ml_bwd(int dt, int d, const void* Qs, const void* Klm, int m, const int32_t* idx, const float* ds,
+                         const int* chunk_off, const int* pairs, float* dQs, float* dKlm, int BH, int L, int N, int k,
+                         float scale, hipStream_t st) {
+  if (m < 1 || m > 4) return hipErrorInvalidValue;
+  if (dt == 0)
+    return d == 64 ? ml_bwd_t<bf16_t, 64>(Qs, Klm, m, idx, ds, chunk_off, pairs, dQs, dKlm, BH, L, N, k, scale, st)
+                   : ml_bwd_t<bf16_t, 128>(Qs, Klm, m, idx, ds, chunk_off, pairs, dQs, dKlm, BH, L, N, k, scale, st);
+  if (d != 64) return hipErrorInvalidValue;
+  return ml_bwd_t<float, 64>(Qs, Klm, m, idx, ds, chunk_off, pairs, dQs, dKlm, BH, L, N, k, scale, st);
+}
+
+}  // namespace hils

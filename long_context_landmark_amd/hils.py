@@ -45,6 +45,7 @@ _lib.hils_sparse_attn_fwd_lf.argtypes = _lib.hils_sparse_attn_fwd_rq.argtypes
 _lib.hils_decode_step_lf.argtypes = _lib.hils_decode_step_rq.argtypes
 _lib.hils_sparse_attn_bwd_lf.argtypes = _lib.hils_sparse_attn_bwd_rq.argtypes
 _lib.hils_sparse_attn_fwd_ml.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64] + _lib.hils_sparse_attn_fwd.argtypes[4:]
+_lib.hils_sparse_attn_bwd_ml.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64] + _lib.hils_sparse_attn_bwd_rq.argtypes[5:]
 _lib.hils_decode_step_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _int, _vp, _vp,
                                         _vp, _i64, _i64, _i64, _i64, _i64, _f, _int, _vp, _sz, _vp]
 _lib.hils_profile_enable.argtypes = [_int]
@@ -387,3 +388,23 @@ def sparse_attn_fwd_ml(Q, K, V, K_lm, k, C=64, scale=None, idx=None, save_for_ba
                                         _p(w), _p(lse), B, H, L, d, C, k, _scale(d, scale), _dt(Q), _p(wsb), n,
                                         _stream()))
     return O, idx, sel, w, lse
+
+
+def sparse_attn_bwd_ml(Q, K, V, K_lm, dO, idx, w, lse, k, C=64, scale=None, ws=None, Q_ret=None):
+    """Backward of ``sparse_attn_fwd_ml`` (K_lm [B,H,N,m,d], m <= 4), selection held fixed.  Returns
+    (dQ, dK, dV, dK_lm) or, with ``Q_ret``, (dQ, dQ_ret, dK, dV, dK_lm); dK_lm is [B,H,N,m,d]."""
+    _contig(Q, K, V, K_lm, dO, idx, w, lse, Q_ret)
+    _like(Q_ret, Q, "Q_ret")
+    B, H, L, d = Q.shape
+    m = K_lm.shape[3]
+    f32 = dict(dtype=torch.float32, device=Q.device)
+    dQ, dK, dV = (torch.empty((B, H, L, d), **f32) for _ in range(3))
+    dKlm = torch.empty((B, H, L // C, m, d), **f32)
+    dQr = torch.empty((B, H, L, d), **f32) if Q_ret is not None else None
+    wsb, n = _workspace(OP_BWD, B, H, L, d, C, k, Q.device, ws)
+    _check(_lib.hils_sparse_attn_bwd_ml(_p(Q), _p(Q_ret), _p(K), _p(V), _p(K_lm), m, _p(dO), _p(idx), _p(w), _p(lse),
+                                        _p(dQ), _p(dQr), _p(dK), _p(dV), _p(dKlm), B, H, L, d, C, k, _scale(d, scale),
+                                        _dt(Q), _p(wsb), n, _stream()))
+    if Q_ret is None:
+        return dQ, dK, dV, dKlm
+    return dQ, dQr, dK, dV, dKlm

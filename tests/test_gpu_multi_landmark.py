@@ -108,3 +108,27 @@ def test_fwd_multi_landmark_fixed_selection(hils, gpu):
     want = oracle.fwd_ml(x["Q"], x["K"], x["V"], lm, 64, k, idx=idx)
     assert_close(f32(O), want["O"], "O (fixed selection)")
     assert_close(f32(w), want["w"], "w (fixed selection)", 1e-5, 1e-5)
+
+
+@pytest.mark.parametrize("dtype,B,H,L,d,k,kind,m,rq", [
+    ("bf16", 1, 2, 2112, 64, 8, "firstlast", 2, False),
+    ("bf16", 1, 2, 1024, 128, 16, "firstlast", 2, False),
+    ("f32", 1, 2, 1024, 64, 4, "firstlast", 2, False),
+    ("bf16", 1, 2, 2048, 64, 8, "random", 3, True),
+])
+def test_bwd_multi_landmark(hils, gpu, dtype, B, H, L, d, k, kind, m, rq):
+    say(f"bwd several landmarks dtype={dtype} B={B} H={H} L={L} d={d} k={k} landmarks={kind}x{m} retrieval={rq}")
+    x = synth.prefill_inputs(B, H, L, d, C=64, seed=820 + L + d + m, dtype=dtype, with_dO=True, with_qret=rq)
+    lm = _landmarks(x, kind, m, seed=821 + L)
+    t = to_inputs(x, ("Q", "K", "V", "dO") + (("Q_ret",) if rq else ()))
+    lm_g = dev(lm)
+    O, idx, sel, w, lse = hils.sparse_attn_fwd_ml(t["Q"], t["K"], t["V"], lm_g, k, save_for_backward=True,
+                                                  Q_ret=t.get("Q_ret"))
+    grads = hils.sparse_attn_bwd_ml(t["Q"], t["K"], t["V"], lm_g, t["dO"], idx, w, lse, k, Q_ret=t.get("Q_ret"))
+    torch.cuda.synchronize()
+    ref = oracle.bwd_ml(x["Q"], x["K"], x["V"], lm, x["dO"], idx.cpu().numpy(), 64, k,
+                        Q_ret=x["Q_ret"] if rq else None)
+    names = ("dQ", "dQ_ret", "dK", "dV", "dKlm") if rq else ("dQ", "dK", "dV", "dKlm")
+    tol = (5e-3, 3e-3) if dtype == "f32" else (2e-2, 1e-2)
+    for name, got in zip(names, grads):
+        assert_close(f32(got), ref[name], name, *tol)
