@@ -100,6 +100,10 @@ def prefill_work(B, H, L, d, k, C=64):
             # landmark-free chunks only
             "chunk_mean": ("hbm", 0, BH * (L * d * 2 + N * d * 2)),
             "lf_own": ("hbm", BH * L * 2 * d, BH * L * (2 * d * 2 + k1 * 12)),
+            # two landmarks per chunk only: causal (query, chunk, landmark) dot products on the VALU, the
+            # chunk scores written once and read back by the selection
+            "ml_scores": ("valu", BH * C * (N * (N + 1) // 2) * 2 * 2 * d, BH * (L * d * 2 + C * (N * (N + 1) // 2) * 4)),
+            "ml_select": ("hbm", 0, BH * (C * (N * (N + 1) // 2) * 4 + L * k1 * 12)),
         },
     }
 
@@ -130,6 +134,9 @@ def train_work(B, H, L, d, k, C=64):
     kern["klm_bwd"] = ("hbm", 0, pairs_all * (2 * d + 8) + BH * N * d * 4)
     # landmark-free chunks only: q and k read, dQ and dK read and written, per row
     kern["lf_bwd"] = ("hbm", 0, BH * L * (2 * d * 2 + 4 + 4 * d * 4) + BH * N * d * 4)
+    # two landmarks per chunk only: per pair q and two landmark rows read, dKlm and dQ written
+    kern["ml_klm_bwd"] = ("hbm", 0, pairs_all * (2 * d + 4) + BH * N * 2 * d * (2 + 4))
+    kern["ml_dq"] = ("hbm", 0, BH * L * (2 * d + (k + 1) * (8 + 2 * 2 * d) + 2 * 4 * d))
     return {"flops": fw["flops"] + f_bwd, "bytes": fw["bytes"] + b_bwd, "kernels": kern}
 
 
@@ -145,6 +152,9 @@ def roofline(kernels_ms, work, launches_per_step, workload=None):
     if bound == "mfma":
         achieved = flops / per / (per_launch_ms * 1e-3) / 1e12
         peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+    elif bound == "valu":
+        achieved = flops / per / (per_launch_ms * 1e-3) / 1e12
+        peak, unit = PEAK_FP32_TFLOPS, "TFLOP/s"
     else:
         achieved = nbytes / per / (per_launch_ms * 1e-3) / 1e9
         peak, unit = PEAK_HBM_GBS, "GB/s"
@@ -214,7 +224,7 @@ def kernel_times(hils, fn, steps):
 # ----------------------------------------------------------------------------- workloads
 
 
-def bench_prefill(hils, synth, name, steps, warmup, rq=False, lf=False):
+def bench_prefill(hils, synth, name, steps, warmup, rq=False, lf=False, ml=False):
     """rq: separate retrieval queries score the landmarks (low-rank query calibration).
     lf: landmark-free chunks, the landmarks formed inside the step as the chunks' key means."""
     import torch
@@ -222,12 +232,16 @@ def bench_prefill(hils, synth, name, steps, warmup, rq=False, lf=False):
     w = synth.WORKLOADS[name]
     x = synth.torch_prefill_inputs(w, with_qret=rq)
     klm_out = torch.empty_like(x["Klm"]) if lf else None
-    ws = torch.empty(hils.workspace_size(hils.OP_FWD, w.B, w.H, w.L, w.d, w.C, w.k), dtype=torch.uint8,
+    # several landmarks per chunk: the keys of each chunk's first and last token
+    klm_ml = torch.stack([x["K"][:, :, ::w.C], x["K"][:, :, w.C - 1::w.C]], dim=3).contiguous() if ml else None
+    ws = torch.empty(hils.workspace_size(hils.OP_FWD_ML if ml else hils.OP_FWD, w.B, w.H, w.L, w.d, w.C, w.k), dtype=torch.uint8,
                      device="cuda:0")
     O = torch.empty_like(x["Q"])
 
     def step():
-        if lf:
+        if ml:
+            hils.sparse_attn_fwd_ml(x["Q"], x["K"], x["V"], klm_ml, w.k, ws=ws, out=O, Q_ret=x.get("Q_ret"))
+        elif lf:
             hils.sparse_attn_fwd_lf(x["Q"], x["K"], x["V"], w.k, ws=ws, out=O, Q_ret=x.get("Q_ret"), K_lm=klm_out)
         else:
             hils.sparse_attn_fwd(x["Q"], x["K"], x["V"], x["Klm"], w.k, ws=ws, out=O, Q_ret=x.get("Q_ret"))
@@ -239,7 +253,7 @@ def bench_prefill(hils, synth, name, steps, warmup, rq=False, lf=False):
     work = prefill_work(w.B, w.H, w.L, w.d, w.k, w.C)
     nsteps = max(1, min(steps, 10))
     per_kernel = {n: round(t / c * 1e3, 3) for n, (t, c) in kt.items()}
-    rl = roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()}, None if rq or lf else name)
+    rl = roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()}, None if rq or lf or ml else name)
     res = {
         "tokens_per_s": w.B * w.L / (ms * 1e-3),
         "ms_per_step": ms,
@@ -253,14 +267,15 @@ def bench_prefill(hils, synth, name, steps, warmup, rq=False, lf=False):
         "kernel_us": per_kernel,
         "roofline": rl,
         "config": {"workload": name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "C": w.C, "k": w.k,
-                   **({"retrieval_query": True} if rq else {}), **({"landmark_free": True} if lf else {})},
+                   **({"retrieval_query": True} if rq else {}), **({"landmark_free": True} if lf else {}),
+                   **({"landmarks_per_chunk": 2} if ml else {})},
     }
     del x, ws, O
     torch.cuda.empty_cache()
     return res
 
 
-def bench_train(hils, synth, name, steps, warmup, rq=False, lf=False):
+def bench_train(hils, synth, name, steps, warmup, rq=False, lf=False, ml=False):
     import torch
 
     w = synth.WORKLOADS[name]
@@ -279,6 +294,11 @@ def bench_train(hils, synth, name, steps, warmup, rq=False, lf=False):
     grads = [torch.empty((B, H, L, d), **f32) for _ in range(3)] + [torch.empty((B, H, L // w.C, d), **f32)]
     dQr = torch.empty((B, H, L, d), **f32) if rq else None
     klm_lf = torch.empty_like(x["Klm"]) if lf else None
+    klm_ml = torch.stack([x["K"][:, :, ::w.C], x["K"][:, :, w.C - 1::w.C]], dim=3).contiguous() if ml else None
+    dklm_ml = torch.empty((B, H, L // w.C, 2, d), **f32) if ml else None
+    if ml:
+        wsf = torch.empty(hils.workspace_size(hils.OP_FWD_ML, w.B, w.H, w.L, w.d, w.C, w.k), dtype=torch.uint8,
+                          device="cuda:0")
     import ctypes
 
     lib = hils._lib
@@ -287,6 +307,15 @@ def bench_train(hils, synth, name, steps, warmup, rq=False, lf=False):
     def step():
         s_ = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         scale = 1.0 / math.sqrt(d)
+        if ml:
+            hils._check(lib.hils_sparse_attn_fwd_ml(P(x["Q"]), None, P(x["K"]), P(x["V"]), P(klm_ml), 2, P(idx), P(sel),
+                                                    1, P(O), P(wt), P(lse), B, H, L, d, w.C, w.k, scale, 0, P(wsf),
+                                                    wsf.numel(), s_))
+            hils._check(lib.hils_sparse_attn_bwd_ml(P(x["Q"]), None, P(x["K"]), P(x["V"]), P(klm_ml), 2, P(x["dO"]),
+                                                    P(idx), P(wt), P(lse), P(grads[0]), None, P(grads[1]),
+                                                    P(grads[2]), P(dklm_ml), B, H, L, d, w.C, w.k, scale, 0, P(wsb),
+                                                    wsb.numel(), s_))
+            return
         if lf:
             qr = P(x["Q_ret"]) if rq else None
             hils._check(lib.hils_sparse_attn_fwd_lf(P(x["Q"]), qr, P(x["K"]), P(x["V"]), P(klm_lf), P(idx), P(sel), 1,
@@ -328,10 +357,11 @@ def bench_train(hils, synth, name, steps, warmup, rq=False, lf=False):
         "tflops": work["flops"] / (ms * 1e-3) / 1e12,
         "algorithmic_gflop": work["flops"] / 1e9,
         "kernel_us": {n: round(t / c * 1e3, 3) for n, (t, c) in kt.items()},
-        "roofline": roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()}, None if rq or lf else name),
+        "roofline": roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()},
+                             None if rq or lf or ml else name),
         "config": {"workload": name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "C": w.C, "k": w.k,
                    "step": "forward + backward", **({"retrieval_query": True} if rq else {}),
-                   **({"landmark_free": True} if lf else {})},
+                   **({"landmark_free": True} if lf else {}), **({"landmarks_per_chunk": 2} if ml else {})},
     }
     del x, wsf, wsb
     torch.cuda.empty_cache()
@@ -501,7 +531,9 @@ def main():
     ap.add_argument("--only", default="", help="run only this workload (prefill_8k, prefill_128k, decode_512k, "
                                                "train_8k; a _retrieval suffix on a prefill or train workload "
                                                "adds separate retrieval queries, a _landmark_free suffix on a "
-                                               "prefill, decode or train workload uses key-mean landmarks) and print "
+                                               "prefill, decode or train workload uses key-mean landmarks, a "
+                                               "_two_landmarks suffix on a prefill or train workload uses the "
+                                               "first and last token of each chunk as landmarks) and print "
                                                "its result object; for profiling runs")
     ap.add_argument("--decode-replicas", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -532,15 +564,19 @@ def main():
             return
         rq = args.only.endswith("_retrieval")
         lf = args.only.endswith("_landmark_free")
-        name = args.only[:-len("_retrieval")] if rq else args.only[:-len("_landmark_free")] if lf else args.only
+        ml = args.only.endswith("_two_landmarks")
+        name = args.only
+        for suffix in ("_retrieval", "_landmark_free", "_two_landmarks"):
+            if name.endswith(suffix):
+                name = name[:-len(suffix)]
         if name.startswith("prefill"):
-            res = bench_prefill(hils, synth, name, args.steps, args.warmup, rq=rq, lf=lf)
+            res = bench_prefill(hils, synth, name, args.steps, args.warmup, rq=rq, lf=lf, ml=ml)
         elif name.startswith("decode_paged"):
             res = bench_decode_paged(hils, synth, name, args.warmup)
         elif name.startswith("decode"):
             res = bench_decode(hils, synth, name, args.decode_replicas, args.warmup, lf=lf)
         elif name.startswith("train"):
-            res = bench_train(hils, synth, name, args.steps, args.warmup, rq=rq, lf=lf)
+            res = bench_train(hils, synth, name, args.steps, args.warmup, rq=rq, lf=lf, ml=ml)
         else:
             raise SystemExit(f"unknown workload {args.only}")
         print(json.dumps({"workload": args.only, **res}), flush=True)
@@ -581,6 +617,14 @@ def main():
         extra["train_8k_landmark_free"] = bench_train(hils, synth, "train_8k", max(3, min(args.steps, 20)), 2, lf=True)
         log(f"[bench] prefill_8k_landmark_free {extra['prefill_8k_landmark_free']['ms_per_step']*1e3:.1f} us/step, "
             f"decode_512k_landmark_free {extra['decode_512k_landmark_free']['us_per_token']:.2f} us/token")
+    if "two_landmarks" not in skip:
+        # two landmarks per chunk (the keys of its first and last token), log-sum-exp chunk scores
+        log("[bench] prefill_8k and train_8k with two landmarks per chunk")
+        extra["prefill_8k_two_landmarks"] = bench_prefill(hils, synth, "prefill_8k", max(3, min(args.steps, 20)), 2,
+                                                          ml=True)
+        extra["train_8k_two_landmarks"] = bench_train(hils, synth, "train_8k", max(3, min(args.steps, 20)), 2, ml=True)
+        log(f"[bench] prefill_8k_two_landmarks {extra['prefill_8k_two_landmarks']['ms_per_step']*1e3:.1f} us/step, "
+            f"train_8k_two_landmarks {extra['train_8k_two_landmarks']['ms_per_step']*1e3:.1f} us/step")
     if "decode_paged_b16" not in skip:
         log("[bench] decode_paged_b16 (16 ragged sequences, paged cache)")
         extra["decode_paged_b16"] = bench_decode_paged(hils, synth, "decode_paged_b16", 4)

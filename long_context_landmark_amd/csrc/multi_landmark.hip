@@ -5,11 +5,12 @@
 //
 //   ml_scores   one workgroup per (query chunk, head): the 64 queries staged as fp32 in LDS; for
 //               every tile of 64 chunks up to the query chunk and every landmark, the landmark
-//               rows staged and the 64 x 64 dot products formed on the VALU (lane = query, wave =
-//               16 chunks, so landmark reads are LDS broadcasts), folded into a running
+//               rows staged and the 64 x 64 dot products formed on the VALU (each thread a block of
+//               4 queries x 4 chunks: eight LDS reads per sixteen products), folded into a running
 //               log-sum-exp per (query, chunk).  Writes the causal chunk scores S [BH][L][N] (fp32).
 //   ml_select   one wave per query row: the m = min(k, c) best past chunks by (score desc, index
-//               asc) in k rounds of a wave maximum over 64-bit keys, the own chunk's score, and
+//               asc) in k rounds of a wave maximum over 64-bit keys (held in registers when the
+//               row has at most 512 chunks), the own chunk's score, and
 //               the fusion weights; or, for a caller-given selection, its scores and weights.
 // The selection outputs then feed the routing and chunk-attention kernels of the plain forward.
 #include "hils_device.h"
@@ -25,7 +26,7 @@ __global__ __launch_bounds__(256) void ml_scores_kernel(const T* __restrict__ Qs
   constexpr int RPR = 256 / PIECES;
   constexpr int KS = D + 1;
   const int qc = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const int q = tid & 63, jg = tid >> 6;  // lane: query; wave: 16 chunks of the tile
+  const int qg = tid & 15, jg = tid >> 4;  // this thread's block: queries 4qg..4qg+3, tile chunks 4jg..4jg+3
   const int64_t row0 = (int64_t)bh * L + (int64_t)qc * 64;
   __shared__ float qs[64 * KS];
   __shared__ float lm[64 * KS];
@@ -54,13 +55,19 @@ __global__ __launch_bounds__(256) void ml_scores_kernel(const T* __restrict__ Qs
         for (int e = 0; e < EPP; ++e) lm[jj * KS + piece * EPP + e] = Elem<T>::to_f32(vals, e);
       }
       __syncthreads();
-      float acc[16];
+      float acc[16];  // [query a][chunk b] at 4a + b
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[i] = 0.f;
       for (int e = 0; e < D; ++e) {
-        const float qv = qs[q * KS + e];
+        float qv[4], lv[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] += qv * lm[(jg * 16 + i) * KS + e];
+        for (int a = 0; a < 4; ++a) qv[a] = qs[(4 * qg + a) * KS + e];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) lv[b] = lm[(4 * jg + b) * KS + e];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) acc[4 * a + b] += qv[a] * lv[b];
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -76,15 +83,21 @@ __global__ __launch_bounds__(256) void ml_scores_kernel(const T* __restrict__ Qs
         }
       }
     }
-    float* srow = S + (row0 + q) * N;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int j = j0 + jg * 16 + i;
-      if (j <= qc) srow[j] = m == 1 ? mx[i] : mx[i] + __logf(z[i]);
+    for (int a = 0; a < 4; ++a) {
+      float* srow = S + (row0 + 4 * qg + a) * N;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int j = j0 + 4 * jg + b;
+        if (j <= qc) srow[j] = m == 1 ? mx[4 * a + b] : mx[4 * a + b] + __logf(z[4 * a + b]);
+      }
     }
   }
 }
 
+// VPL > 0: every candidate of a row fits in VPL keys per lane (c <= 64 VPL), which are loaded once; VPL = 0:
+// the row is re-read from memory in every round
+template <int VPL>
 __global__ __launch_bounds__(256) void ml_select_kernel(const float* __restrict__ S, int32_t* __restrict__ idx,
                                                         float* __restrict__ sel, float* __restrict__ w, int64_t rows,
                                                         int L, int N, int k, int select) {
@@ -101,12 +114,24 @@ __global__ __launch_bounds__(256) void ml_select_kernel(const float* __restrict_
   int ix = -1;
   float sv = -INFINITY;
   if (select) {
+    uint64_t keys[VPL > 0 ? VPL : 1];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int j = lane + 64 * i;
+      keys[i] = j < c ? make_key(srow[j], j) : 0ull;
+    }
     uint64_t prev = ~0ull;
     for (int r = 0; r < m; ++r) {
       uint64_t best = 0ull;
-      for (int j = lane; j < c; j += 64) {
-        const uint64_t key = make_key(srow[j], j);
-        if (key < prev && key > best) best = key;
+      if (VPL > 0) {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+          if (keys[i] < prev && keys[i] > best) best = keys[i];
+      } else {
+        for (int j = lane; j < c; j += 64) {
+          const uint64_t key = make_key(srow[j], j);
+          if (key < prev && key > best) best = key;
+        }
       }
 #pragma unroll
       for (int msk = 1; msk < 64; msk <<= 1) {
@@ -158,8 +183,13 @@ hipError_t launch_ml_selection(int dt, int d, const void* Qs, const void* Klm, i
                 : ml_scores_t<float, 128>(Qs, Klm, S, BH, L, N, m, scale, st);
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)BH * L;
-  HILS_LAUNCH("ml_select", ml_select_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, S, idx, sel, w,
-              rows, L, N, k, select);
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (N <= 128)
+    HILS_LAUNCH("ml_select", ml_select_kernel<2>, grid, dim3(256), 0, st, S, idx, sel, w, rows, L, N, k, select);
+  else if (N <= 512)
+    HILS_LAUNCH("ml_select", ml_select_kernel<8>, grid, dim3(256), 0, st, S, idx, sel, w, rows, L, N, k, select);
+  else
+    HILS_LAUNCH("ml_select", ml_select_kernel<0>, grid, dim3(256), 0, st, S, idx, sel, w, rows, L, N, k, select);
   return hipGetLastError();
 }
 
@@ -250,7 +280,9 @@ __global__ __launch_bounds__(256) void ml_klm_bwd_kernel(const T* __restrict__ Q
       for (int e = 0; e < QD; ++e) acc[u][e] += c * qv[e];
     }
   }
-  for (int u = 0; u < m && u < MM; ++u) {
+#pragma unroll
+  for (int u = 0; u < MM; ++u) {
+    if (u >= m) break;  // uniform over the workgroup
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < QD; ++e) red[p][qt * QD + e] = acc[u][e];
@@ -341,16 +373,25 @@ __global__ __launch_bounds__(256) void ml_dq_kernel(const T* __restrict__ Qs, co
   out[1] = o1;
 }
 
+template <typename T, int D, int MM>
+static hipError_t ml_bwd_mm(const void* Qs, const void* Klm, int m, const int32_t* idx, const float* ds,
+                            const int* chunk_off, const int* pairs, float* dQs, float* dKlm, int BH, int L, int N,
+                            int k, float scale, hipStream_t st) {
+  HILS_LAUNCH("ml_klm_bwd", (ml_klm_bwd_kernel<T, D, MM>), dim3(N, BH), dim3(256), 0, st, (const T*)Qs,
+              (const T*)Klm, ds, chunk_off, pairs, dKlm, L, N, k, m, scale);
+  const int64_t rows = (int64_t)BH * L;
+  HILS_LAUNCH("ml_dq", (ml_dq_kernel<T, D, MM>), dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, st,
+              (const T*)Qs, (const T*)Klm, idx, ds, dQs, rows, L, N, k, m, scale);
+  return hipGetLastError();
+}
+
+// the landmark count rounded up to 2 or 4 sizes the per-lane accumulators
 template <typename T, int D>
 static hipError_t ml_bwd_t(const void* Qs, const void* Klm, int m, const int32_t* idx, const float* ds,
                            const int* chunk_off, const int* pairs, float* dQs, float* dKlm, int BH, int L, int N,
                            int k, float scale, hipStream_t st) {
-  HILS_LAUNCH("ml_klm_bwd", (ml_klm_bwd_kernel<T, D, 4>), dim3(N, BH), dim3(256), 0, st, (const T*)Qs,
-              (const T*)Klm, ds, chunk_off, pairs, dKlm, L, N, k, m, scale);
-  const int64_t rows = (int64_t)BH * L;
-  HILS_LAUNCH("ml_dq", (ml_dq_kernel<T, D, 4>), dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, st,
-              (const T*)Qs, (const T*)Klm, idx, ds, dQs, rows, L, N, k, m, scale);
-  return hipGetLastError();
+  return m <= 2 ? ml_bwd_mm<T, D, 2>(Qs, Klm, m, idx, ds, chunk_off, pairs, dQs, dKlm, BH, L, N, k, scale, st)
+                : ml_bwd_mm<T, D, 4>(Qs, Klm, m, idx, ds, chunk_off, pairs, dQs, dKlm, BH, L, N, k, scale, st);
 }
 
 hipError_t launch_ml_bwd(int dt, int d, const void* Qs, const void* Klm, int m, const int32_t* idx, const float* ds,
