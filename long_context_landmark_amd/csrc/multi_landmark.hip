@@ -9,8 +9,9 @@
 //               4 queries x 4 chunks: eight LDS reads per sixteen products), folded into a running
 //               log-sum-exp per (query, chunk).  Writes the causal chunk scores S [BH][L][N] (fp32).
 //   ml_select   one wave per query row: the m = min(k, c) best past chunks by (score desc, index
-//               asc) in k rounds of a wave maximum over 64-bit keys (held in registers when the
-//               row has at most 512 chunks), the own chunk's score, and
+//               asc) in k rounds of a group maximum over 64-bit keys (16 lanes per row when the
+//               row has at most 128 chunks and k < 16, else a wave; keys held in registers up to
+//               512 chunks), the own chunk's score, and
 //               the fusion weights; or, for a caller-given selection, its scores and weights.
 // The selection outputs then feed the routing and chunk-attention kernels of the plain forward.
 #include "hils_device.h"
@@ -95,71 +96,78 @@ __global__ __launch_bounds__(256) void ml_scores_kernel(const T* __restrict__ Qs
   }
 }
 
-// VPL > 0: every candidate of a row fits in VPL keys per lane (c <= 64 VPL), which are loaded once; VPL = 0:
-// the row is re-read from memory in every round
-template <int VPL>
+// G lanes per query row (64 / G rows per wave).  VPL > 0: every candidate of a row fits in VPL keys per
+// lane (c <= G VPL), loaded once; VPL = 0: the row is re-read from memory in every round.  Lane gl of a
+// row's group ends up holding slot gl (gl < k) and, if gl == k, the own chunk; G > k is required.
+template <int VPL, int G>
 __global__ __launch_bounds__(256) void ml_select_kernel(const float* __restrict__ S, int32_t* __restrict__ idx,
                                                         float* __restrict__ sel, float* __restrict__ w, int64_t rows,
                                                         int L, int N, int k, int select) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int t = (int)(row % L);
+  const int lane = threadIdx.x & 63, gl = lane % G;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / G) + lane / G;
+  // rows past the end compute alongside (every lane takes part in the group shuffles) and write nothing
+  const bool live = row < rows;
+  const int64_t rr = live ? row : rows - 1;
+  const int t = (int)(rr % L);
   const int c = t / 64;
   const int m = min(k, c);
   const int k1 = k + 1;
-  const float* srow = S + row * N;
-  const int64_t base = row * k1;
-  // this lane's slot: a kept past chunk (lane < k) or the own chunk (lane == k)
+  const float* srow = S + rr * N;
+  const int64_t base = rr * k1;
   int ix = -1;
   float sv = -INFINITY;
   if (select) {
     uint64_t keys[VPL > 0 ? VPL : 1];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-      const int j = lane + 64 * i;
+      const int j = gl + G * i;
       keys[i] = j < c ? make_key(srow[j], j) : 0ull;
     }
     uint64_t prev = ~0ull;
-    for (int r = 0; r < m; ++r) {
+    // m differs between the rows of a wave: every group runs k rounds, extra ones find nothing new
+    for (int r = 0; r < k; ++r) {
       uint64_t best = 0ull;
       if (VPL > 0) {
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
           if (keys[i] < prev && keys[i] > best) best = keys[i];
       } else {
-        for (int j = lane; j < c; j += 64) {
+        for (int j = gl; j < c; j += G) {
           const uint64_t key = make_key(srow[j], j);
           if (key < prev && key > best) best = key;
         }
       }
 #pragma unroll
-      for (int msk = 1; msk < 64; msk <<= 1) {
+      for (int msk = 1; msk < G; msk <<= 1) {
         const uint64_t o = shfl_xor_u64(best, msk);
         best = o > best ? o : best;
       }
-      if (lane == r) {
+      if (gl == r && r < m) {
         ix = key_index(best);
         sv = key_score(best);
       }
       prev = best;
     }
-  } else if (lane < k) {
-    ix = idx[base + lane];
+  } else if (gl < k) {
+    ix = idx[base + gl];
     if (ix >= 0) sv = srow[ix];
   }
-  if (lane == k) {
+  if (gl == k) {
     ix = c;
     sv = srow[c];
   }
-  const bool used = lane <= k && ix >= 0;
-  const float smax = wave_max(used ? sv : -INFINITY);
+  const bool used = gl <= k && ix >= 0;
+  float smax = used ? sv : -INFINITY;
+#pragma unroll
+  for (int msk = 1; msk < G; msk <<= 1) smax = fmaxf(smax, lane_xor(smax, msk));
   const float ev = used ? __expf(sv - smax) : 0.f;
-  const float den = wave_sum(ev);
-  if (lane <= k) {
-    if (select) idx[base + lane] = ix;
-    sel[base + lane] = used ? sv : -INFINITY;
-    if (w) w[base + lane] = ev / den;
+  float den = ev;
+#pragma unroll
+  for (int msk = 1; msk < G; msk <<= 1) den += lane_xor(den, msk);
+  if (live && gl <= k) {
+    if (select) idx[base + gl] = ix;
+    sel[base + gl] = used ? sv : -INFINITY;
+    if (w) w[base + gl] = ev / den;
   }
 }
 
@@ -183,13 +191,20 @@ hipError_t launch_ml_selection(int dt, int d, const void* Qs, const void* Klm, i
                 : ml_scores_t<float, 128>(Qs, Klm, S, BH, L, N, m, scale, st);
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)BH * L;
-  const dim3 grid((unsigned)((rows + 3) / 4));
-  if (N <= 128)
-    HILS_LAUNCH("ml_select", ml_select_kernel<2>, grid, dim3(256), 0, st, S, idx, sel, w, rows, L, N, k, select);
-  else if (N <= 512)
-    HILS_LAUNCH("ml_select", ml_select_kernel<8>, grid, dim3(256), 0, st, S, idx, sel, w, rows, L, N, k, select);
-  else
-    HILS_LAUNCH("ml_select", ml_select_kernel<0>, grid, dim3(256), 0, st, S, idx, sel, w, rows, L, N, k, select);
+  if (N <= 128 && k < 16) {
+    // 16 lanes per row, eight keys each: four rows share a wave and its shuffles
+    const dim3 grid((unsigned)((rows + 15) / 16));
+    HILS_LAUNCH("ml_select", (ml_select_kernel<8, 16>), grid, dim3(256), 0, st, S, idx, sel, w, rows, L, N, k,
+                select);
+  } else {
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    if (N <= 512)
+      HILS_LAUNCH("ml_select", (ml_select_kernel<8, 64>), grid, dim3(256), 0, st, S, idx, sel, w, rows, L, N, k,
+                  select);
+    else
+      HILS_LAUNCH("ml_select", (ml_select_kernel<0, 64>), grid, dim3(256), 0, st, S, idx, sel, w, rows, L, N, k,
+                  select);
+  }
   return hipGetLastError();
 }
 
