@@ -48,9 +48,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: (kernel, FETCH_SIZE KiB, WRITE_SIZE KiB, source digest)
-    "prefill_8k": ("chunk_attn_fwd", 28621.2, 130575.6, "61955e7f109bb0b3"),
-    "prefill_128k": ("chunk_attn_fwd", 8510411.9, 17017989.0, "61955e7f109bb0b3"),
-    "train_8k": ("chunk_bwd", 238081.9, 902126.3, "d47ff5144bc2e4ed"),
+    "prefill_8k": ("chunk_attn_fwd", 28618.8, 130579.2, "ad203af3dc9d86c0"),
+    "prefill_128k": ("chunk_attn_fwd", 8509578.3, 17019386.8, "ad203af3dc9d86c0"),
+    "train_8k": ("chunk_bwd", 238209.6, 901965.7, "860ab69a12813d2f"),
 }
 
 
