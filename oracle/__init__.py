@@ -85,6 +85,8 @@ def _load():
     lib.oracle_fwd_ml.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, dbl, ip, vp, i64, ip,
                                   vp, vp, vp, vp, vp, ip]
     lib.oracle_fwd_ml.restype = ip
+    lib.oracle_decode_ml.argtypes = lib.oracle_decode.argtypes[:7] + [i64] + lib.oracle_decode.argtypes[7:]
+    lib.oracle_decode_ml.restype = ip
     lib.oracle_bwd_ml.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, i64, i64, i64, i64, i64, i64, dbl, ip, vp, vp,
                                   vp, vp, vp, ip]
     lib.oracle_bwd_ml.restype = ip
@@ -253,9 +255,17 @@ def decode(q, k_new, v_new, Kc, Vc, Klm, n, C, k, scale=None, nthreads=0, q_ret=
     w = np.empty((B, H, k1), np.float64)
     lse = np.empty((B, H, k1), np.float64)
     o = np.empty((B, H, d), np.float64)
-    fn = _load().oracle_decode_lf if landmark_free else _load().oracle_decode
-    used = fn(_p(q), _p(qr), _p(k_new), _p(v_new), _p(Kc), _p(Vc), _p(Klm), n, Lmax, Nmax, B, H, d, C, k, scale,
-              _dt(q, k_new, v_new, Kc, Vc, Klm), _p(idx), _p(sel), _p(w), _p(lse), _p(o), nthreads)
+    tail = (n, Lmax, Nmax, B, H, d, C, k, scale, _dt(q, k_new, v_new, Kc, Vc, Klm), _p(idx), _p(sel), _p(w), _p(lse),
+            _p(o), nthreads)
+    head = (_p(q), _p(qr), _p(k_new), _p(v_new), _p(Kc), _p(Vc), _p(Klm))
+    if Klm.ndim == 5:
+        # several landmarks per chunk: Klm [B,H,Nmax,m,d]
+        if landmark_free:
+            raise ValueError("landmark-free decode takes one landmark per chunk")
+        used = _load().oracle_decode_ml(*head, Klm.shape[3], *tail)
+    else:
+        fn = _load().oracle_decode_lf if landmark_free else _load().oracle_decode
+        used = fn(*head, *tail)
     if used < 0:
         raise ValueError("unsupported shape")
     return {"idx": idx, "sel": sel, "w": w, "lse": lse, "o": o, "threads": used}

@@ -365,7 +365,7 @@ int oracle_fwd_lf(const void* Q, const void* Qr, const void* K, const void* V, v
  * Caches are [B,H,Lmax,d]; Klm is [B,H,Nmax,d].
  */
 static int decode_common(const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc, void* Vc,
-                         void* Klm, int lf, int64_t n, int64_t Lmax, int64_t Nmax, int64_t B, int64_t H,
+                         void* Klm, int lf, int64_t mlm, int64_t n, int64_t Lmax, int64_t Nmax, int64_t B, int64_t H,
                          int64_t d, int64_t C, int64_t k, double scale, int dt, int32_t* idx,
                          double* sel, double* w, double* lse, double* o, int nthreads) {
   int64_t esz = dt == DT_F32 ? 4 : 2;
@@ -382,7 +382,7 @@ static int decode_common(const void* q, const void* qr, const void* k_new, const
       for (int64_t e = 0; e < d; ++e) store_dt(Klm, (bh * Nmax + c) * d + e, m[e], dt);
     }
   }
-  prob_t P = {q, Kc, Vc, Klm, qr, B, H, n + 1, d, C, k, Nmax, Lmax, Nmax, scale, dt, lf};
+  prob_t P = {q, Kc, Vc, Klm, qr, B, H, n + 1, d, C, k, Nmax, Lmax, Nmax, scale, dt, lf, mlm};
   int used = set_threads(nthreads);
   int64_t k1 = k + 1;
 #pragma omp parallel for schedule(static)
@@ -396,7 +396,7 @@ int oracle_decode(const void* q, const void* qr, const void* k_new, const void* 
                   const void* Klm, int64_t n, int64_t Lmax, int64_t Nmax, int64_t B, int64_t H,
                   int64_t d, int64_t C, int64_t k, double scale, int dt, int32_t* idx,
                   double* sel, double* w, double* lse, double* o, int nthreads) {
-  return decode_common(q, qr, k_new, v_new, Kc, Vc, (void*)Klm, 0, n, Lmax, Nmax, B, H, d, C, k, scale, dt, idx,
+  return decode_common(q, qr, k_new, v_new, Kc, Vc, (void*)Klm, 0, 1, n, Lmax, Nmax, B, H, d, C, k, scale, dt, idx,
                        sel, w, lse, o, nthreads);
 }
 
@@ -411,7 +411,7 @@ int oracle_decode_lf(const void* q, const void* qr, const void* k_new, const voi
                      int64_t d, int64_t C, int64_t k, double scale, int dt, int32_t* idx,
                      double* sel, double* w, double* lse, double* o, int nthreads) {
   if (d > MAX_D) return -1;
-  return decode_common(q, qr, k_new, v_new, Kc, Vc, Klm, 1, n, Lmax, Nmax, B, H, d, C, k, scale, dt, idx, sel, w,
+  return decode_common(q, qr, k_new, v_new, Kc, Vc, Klm, 1, 1, n, Lmax, Nmax, B, H, d, C, k, scale, dt, idx, sel, w,
                        lse, o, nthreads);
 }
 
@@ -589,4 +589,14 @@ int oracle_bwd_ml(const void* Q, const void* Qr, const void* K, const void* V, c
   if (m < 1 || m > 64) return -1;
   return bwd_common(Q, Qr, K, V, Klm, 0, m, dO, idx_in, B, H, L, d, C, k, scale, dt, dQ, dQr, dK, dV, dKlm,
                     nthreads);
+}
+
+/* Decode step with m landmarks per chunk (Klm [B,H,Nmax,m,d]): scores as in oracle_fwd_ml. */
+int oracle_decode_ml(const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc, void* Vc,
+                     const void* Klm, int64_t m, int64_t n, int64_t Lmax, int64_t Nmax, int64_t B, int64_t H,
+                     int64_t d, int64_t C, int64_t k, double scale, int dt, int32_t* idx,
+                     double* sel, double* w, double* lse, double* o, int nthreads) {
+  if (m < 1 || m > 64) return -1;
+  return decode_common(q, qr, k_new, v_new, Kc, Vc, (void*)Klm, 0, m, n, Lmax, Nmax, B, H, d, C, k, scale, dt, idx,
+                       sel, w, lse, o, nthreads);
 }

@@ -738,3 +738,29 @@ def test_several_landmarks_central_differences(oracle_mod):
             fd = (vals[0] - vals[1]) / (2 * h)
             an = g[gname][pos]
             assert abs(fd - an) <= 2e-4 * max(1.0, abs(an)), (name, pos, fd, an)
+
+
+def test_several_landmarks_decode_matches_prefill_rows(oracle_mod):
+    B, H, d, C, k, m = 1, 2, 16, 64, 3, 2
+    ctx, steps = 64 * 3 + 20, 60
+    x = synth.decode_inputs(B, H, d, ctx, steps, C=C, seed=64, dtype="bf16")
+    Nmax = x["Klm"].shape[2]
+    rng = np.random.default_rng(4)
+    lm = synth.f32_to_bf16_bits(rng.standard_normal((B, H, Nmax, m, d), dtype=np.float32))
+    Kc, Vc = x["K_cache"].copy(), x["V_cache"].copy()
+    outs = [oracle_mod.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc, Vc, lm, ctx + s, C, k)
+            for s in range(steps)]
+    L = ctx + steps
+    L_pad = ((L + C - 1) // C) * C
+    Q = np.zeros((B, H, L_pad, d), np.uint16)
+    for s in range(steps):
+        Q[:, :, ctx + s] = x["q"][s]
+    K = np.zeros_like(Q)
+    V = np.zeros_like(Q)
+    K[:, :, :L] = Kc[:, :, :L]
+    V[:, :, :L] = Vc[:, :, :L]
+    rows = np.array([bh * L_pad + ctx + s for s in range(steps) for bh in range(B * H)])
+    ref = oracle_mod.fwd_ml(Q, K, V, np.ascontiguousarray(lm[:, :, :L_pad // C]), C, k, rows=rows)
+    for i, (s, bh) in enumerate((s, bh) for s in range(steps) for bh in range(B * H)):
+        np.testing.assert_array_equal(outs[s]["idx"].reshape(-1, k + 1)[bh], ref["idx"][i])
+        np.testing.assert_array_equal(outs[s]["o"].reshape(-1, d)[bh], ref["O"][i])
