@@ -264,6 +264,17 @@ hils_status hils_sparse_attn_fwd_ml(const void* Q, const void* Q_ret, const void
                                     void* stream);
 
 /*
+ * Decode step with several landmarks per chunk: as hils_decode_step_rq
+ * (q_ret may be null) with K_lm_cache [B][H][N_max][m][d] (dt), 1 <= m <= 16;
+ * the caller writes the open chunk's m landmark rows before the step.
+ */
+hils_status hils_decode_step_ml(const void* q, const void* q_ret, const void* k_new, const void* v_new,
+                                void* K_cache, void* V_cache, const void* K_lm_cache, int64_t m, int64_t n_ctx,
+                                int64_t L_max, void* o, int32_t* idx, float* w, int64_t B, int64_t H, int64_t d,
+                                int64_t C, int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/*
  * Backward of hils_sparse_attn_fwd_ml (selection held fixed), 1 <= m <= 4:
  * as hils_sparse_attn_bwd_rq with the same K_lm [B][H][N][m][d]; landmark u
  * of a kept chunk takes the share p_u = softmax_u of the chunk's landmark

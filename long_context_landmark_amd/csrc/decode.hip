@@ -94,13 +94,13 @@ __device__ __forceinline__ int wave_excl_prefix_small(int v, int& total) {
 // element type; the scan reads only rows of earlier chunks, decode_attend reads this one.  With LF
 // the grid has one workgroup more than there are slices, and that last one appends (so the slices
 // do not wait for the mean).
-template <typename T, int D, bool LF, bool PG>
+template <typename T, int D, bool LF, bool PG, bool ML>
 __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ q, const T* __restrict__ k_new,
                                                           const T* __restrict__ v_new, T* __restrict__ Kc,
                                                           T* __restrict__ Vc, const T* __restrict__ Klm,
                                                           T* __restrict__ Klm_w, uint64_t* __restrict__ lists,
                                                           int64_t n_in, int64_t Lmax, int64_t Nmax, float scale,
-                                                          DecAddr A) {
+                                                          DecAddr A, int mlm) {
   constexpr int EPP = 16 / Elem<T>::bytes;  // elements per 16-byte piece
   constexpr int PIECES = D / EPP;           // pieces per row
   constexpr int RPR = 256 / PIECES;         // rows per round
@@ -143,26 +143,44 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const T* __restrict__ 
   float qv[EPP];
 #pragma unroll
   for (int e = 0; e < EPP; ++e) qv[e] = Elem<T>::to_f32(q, (int64_t)bh * D + piece * EPP + e);
-  const T* base = Klm + (int64_t)bh * Nmax * D + piece * EPP;
-  int4 raw[ROUNDS];
+  // ML: mlm landmarks per chunk (rows lm*mlm + u), the chunk score is the log-sum-exp of their scores;
+  // otherwise one landmark row per chunk
+  const int nlm = ML ? mlm : 1;
+  float mx[ROUNDS], zz[ROUNDS];
+  for (int u = 0; u < nlm; ++u) {
+    int4 raw[ROUNDS];
 #pragma unroll
-  for (int round = 0; round < ROUNDS; ++round) {
-    const int j = j0 + round * RPR + rr;
-    const T* rp = PG ? Klm + dec_lm_row<PG>(A, bh, j, Nmax) * D + piece * EPP : base + (int64_t)j * D;
-    raw[round] = j < c ? *reinterpret_cast<const int4*>(rp) : make_int4(0, 0, 0, 0);
+    for (int round = 0; round < ROUNDS; ++round) {
+      const int j = j0 + round * RPR + rr;
+      const int64_t lr = PG ? dec_lm_row<PG>(A, bh, j, Nmax) : (int64_t)bh * Nmax + j;
+      const T* rp = Klm + (lr * nlm + u) * D + piece * EPP;
+      raw[round] = j < c ? *reinterpret_cast<const int4*>(rp) : make_int4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int round = 0; round < ROUNDS; ++round) {
+      T vals[EPP];
+      __builtin_memcpy(vals, &raw[round], 16);
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) dot += qv[e] * Elem<T>::to_f32(vals, e);
+#pragma unroll
+      for (int m = 1; m < PIECES; m <<= 1) dot += lane_xor(dot, m);
+      const float a = scale * dot;
+      if (u == 0) {
+        mx[round] = a;
+        zz[round] = 1.f;
+      } else if (a > mx[round]) {
+        zz[round] = zz[round] * __expf(mx[round] - a) + 1.f;
+        mx[round] = a;
+      } else {
+        zz[round] += __expf(a - mx[round]);
+      }
+    }
   }
   __shared__ __align__(16) float sc[DEC_ROWS];
 #pragma unroll
-  for (int round = 0; round < ROUNDS; ++round) {
-    T vals[EPP];
-    __builtin_memcpy(vals, &raw[round], 16);
-    float dot = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPP; ++e) dot += qv[e] * Elem<T>::to_f32(vals, e);
-#pragma unroll
-    for (int m = 1; m < PIECES; m <<= 1) dot += lane_xor(dot, m);
-    if (piece == 0) sc[round * RPR + rr] = scale * dot;
-  }
+  for (int round = 0; round < ROUNDS; ++round)
+    if (piece == 0) sc[round * RPR + rr] = ML ? mx[round] + __logf(zz[round]) : mx[round];
   __syncthreads();
   if (tid >= 64) return;
   // The slice's DEC_LIST best keys, by one wave.  Lane l holds scores 4l..4l+3.  The
@@ -383,7 +401,7 @@ __global__ __launch_bounds__(64 * DEC_NWV) void decode_attend_kernel(const T* __
                                                             const uint64_t* __restrict__ lists,
                                                             float* __restrict__ part, int32_t* __restrict__ idx,
                                                             float* __restrict__ wout, int64_t n_in, int64_t Lmax,
-                                                            int64_t Nmax, int k, float scale, DecAddr A) {
+                                                            int64_t Nmax, int k, float scale, DecAddr A, int mlm) {
   constexpr int EPP = 16 / Elem<T>::bytes;
   constexpr int PIECES = D / EPP;
   const int sp = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -405,10 +423,24 @@ __global__ __launch_bounds__(64 * DEC_NWV) void decode_attend_kernel(const T* __
     // given) is formed meanwhile, then the selection and the weights
     MergeIn mi;
     if (m > 0) merge_load(lists + (int64_t)bh * DEC_MAX_SLICES * DEC_LIST, S, m, lane, mi);
-    float dot = 0.f;
-    for (int e = lane; e < D; e += 64)
-      dot += Elem<T>::to_f32(qr, (int64_t)bh * D + e) * Elem<T>::to_f32(Klm, dec_lm_row<PG>(A, bh, c, Nmax) * D + e);
-    const float s_own = scale * wave_sum(dot);
+    const int64_t own_lm = dec_lm_row<PG>(A, bh, c, Nmax) * mlm;
+    float s_own = 0.f, z_own = 0.f;
+    for (int u = 0; u < mlm; ++u) {
+      float dot = 0.f;
+      for (int e = lane; e < D; e += 64)
+        dot += Elem<T>::to_f32(qr, (int64_t)bh * D + e) * Elem<T>::to_f32(Klm, (own_lm + u) * D + e);
+      const float a = scale * wave_sum(dot);
+      if (u == 0) {
+        s_own = a;
+        z_own = 1.f;
+      } else if (a > s_own) {
+        z_own = z_own * __expf(s_own - a) + 1.f;
+        s_own = a;
+      } else {
+        z_own += __expf(a - s_own);
+      }
+    }
+    if (mlm > 1) s_own += __logf(z_own);
     if (m > 0) wave_merge_lists(mi, m, top, surv, lane);
     const bool used = lane < m || lane == 16;
     const float sv = lane < m ? key_score(top[lane]) : (lane == 16 ? s_own : -INFINITY);
@@ -457,41 +489,47 @@ int decode_split() { return DEC_SPLIT; }
 
 template <typename T, int D, bool PG>
 static hipError_t decode_t(const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc, void* Vc,
-                           const void* Klm, bool lf, int64_t n, int64_t Lmax, int64_t Nmax, void* o, int32_t* idx,
-                           float* w, int BH, int k, float scale, const DecodeBufs& ws, const DecAddr& A,
+                           const void* Klm, bool lf, int mlm, int64_t n, int64_t Lmax, int64_t Nmax, void* o,
+                           int32_t* idx, float* w, int BH, int k, float scale, const DecodeBufs& ws, const DecAddr& A,
                            hipStream_t st) {
   // n: the position (contiguous caches) or the largest position of the batch (paged), which sizes the scan
   const int S = decode_slices(n);
   // the landmark scores use the retrieval query (the attention query when none is given)
   const T* qs = (const T*)(qr ? qr : q);
-  if (lf)
-    HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D, true, PG>), dim3(S + 1, BH), dim3(256), 0, st, qs,
+  if (mlm > 1)
+    HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D, false, PG, true>), dim3(S > 0 ? S : 1, BH), dim3(256), 0, st,
+                qs, (const T*)k_new, (const T*)v_new, (T*)Kc, (T*)Vc, (const T*)Klm, (T*)nullptr, ws.lists, n, Lmax,
+                Nmax, scale, A, mlm);
+  else if (lf)
+    HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D, true, PG, false>), dim3(S + 1, BH), dim3(256), 0, st, qs,
                 (const T*)k_new, (const T*)v_new, (T*)Kc, (T*)Vc, (const T*)Klm, (T*)Klm, ws.lists, n, Lmax, Nmax,
-                scale, A);
+                scale, A, mlm);
   else
-    HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D, false, PG>), dim3(S > 0 ? S : 1, BH), dim3(256), 0, st, qs,
+    HILS_LAUNCH("decode_scan", (decode_scan_kernel<T, D, false, PG, false>), dim3(S > 0 ? S : 1, BH), dim3(256), 0, st,
+                qs,
                 (const T*)k_new, (const T*)v_new, (T*)Kc, (T*)Vc, (const T*)Klm, (T*)nullptr, ws.lists, n, Lmax,
-                Nmax, scale, A);
+                Nmax, scale, A, mlm);
   HILS_LAUNCH("decode_attend", (decode_attend_kernel<T, D, PG>), dim3(DEC_SPLIT, BH), dim3(64 * DEC_NWV), 0, st,
               (const T*)q, qs, (const T*)Kc, (const T*)Vc, (const T*)Klm, ws.lists, ws.part, idx, w, n, Lmax, Nmax, k,
-              scale, A);
+              scale, A, mlm);
   HILS_LAUNCH("decode_fuse", (decode_fuse_kernel<T, D>), dim3(BH), dim3(64), 0, st, ws.part, (T*)o);
   return hipGetLastError();
 }
 
 template <bool PG>
 static hipError_t decode_dispatch(int dt, int d, const void* q, const void* qr, const void* k_new, const void* v_new,
-                                  void* Kc, void* Vc, const void* Klm, bool lf, int64_t n, int64_t Lmax, int64_t Nmax,
+                                  void* Kc, void* Vc, const void* Klm, bool lf, int mlm, int64_t n, int64_t Lmax,
+                                  int64_t Nmax,
                                   void* o, int32_t* idx, float* w, int BH, int k, float scale, const DecodeBufs& ws,
                                   const DecAddr& A, hipStream_t st) {
   if (dt == 0)
-    return d == 64 ? decode_t<bf16_t, 64, PG>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, n, Lmax, Nmax, o, idx, w, BH, k,
+    return d == 64 ? decode_t<bf16_t, 64, PG>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, mlm, n, Lmax, Nmax, o, idx, w, BH, k,
                                               scale, ws, A, st)
-                   : decode_t<bf16_t, 128, PG>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, n, Lmax, Nmax, o, idx, w, BH, k,
+                   : decode_t<bf16_t, 128, PG>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, mlm, n, Lmax, Nmax, o, idx, w, BH, k,
                                                scale, ws, A, st);
-  return d == 64 ? decode_t<float, 64, PG>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, n, Lmax, Nmax, o, idx, w, BH, k,
+  return d == 64 ? decode_t<float, 64, PG>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, mlm, n, Lmax, Nmax, o, idx, w, BH, k,
                                            scale, ws, A, st)
-                 : decode_t<float, 128, PG>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, n, Lmax, Nmax, o, idx, w, BH, k,
+                 : decode_t<float, 128, PG>(q, qr, k_new, v_new, Kc, Vc, Klm, lf, mlm, n, Lmax, Nmax, o, idx, w, BH, k,
                                             scale, ws, A, st);
 }
 
@@ -500,16 +538,16 @@ hipError_t launch_decode_paged(int dt, int d, const void* q, const void* qr, con
                                int64_t pages, const int64_t* n_ctx, int64_t n_max, int B, int H, void* o,
                                int32_t* idx, float* w, int k, float scale, const DecodeBufs& ws, hipStream_t st) {
   const DecAddr A{page_table, n_ctx, max_pages, H, pages};
-  return decode_dispatch<true>(dt, d, q, qr, k_new, v_new, Kp, Vp, Klm_p, lf, n_max, 0, 0, o, idx, w, B * H, k,
+  return decode_dispatch<true>(dt, d, q, qr, k_new, v_new, Kp, Vp, Klm_p, lf, 1, n_max, 0, 0, o, idx, w, B * H, k,
                                scale, ws, A, st);
 }
 
 hipError_t launch_decode(int dt, int d, const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc,
-                         void* Vc, const void* Klm, bool lf, int64_t n, int64_t Lmax, int64_t Nmax, void* o,
+                         void* Vc, const void* Klm, bool lf, int mlm, int64_t n, int64_t Lmax, int64_t Nmax, void* o,
                          int32_t* idx, float* w, int BH, int k, float scale, const DecodeBufs& ws, hipStream_t st) {
   const DecAddr A{nullptr, nullptr, 0, 1, 0};
-  return decode_dispatch<false>(dt, d, q, qr, k_new, v_new, Kc, Vc, Klm, lf, n, Lmax, Nmax, o, idx, w, BH, k, scale,
-                                ws, A, st);
+  return decode_dispatch<false>(dt, d, q, qr, k_new, v_new, Kc, Vc, Klm, lf, mlm, n, Lmax, Nmax, o, idx, w, BH, k,
+                                scale, ws, A, st);
 }
 
 }  // namespace hils

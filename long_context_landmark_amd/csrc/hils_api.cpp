@@ -159,7 +159,7 @@ static hils_status fwd_impl(const void* Q, const void* Q_ret, const void* K, con
                             float* lse_out, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk,
                             float scale, hils_dtype dt, void* ws, size_t ws_bytes, void* stream);
 static hils_status decode_impl(const void* q, const void* q_ret, const void* k_new, const void* v_new, void* K_cache,
-                               void* V_cache, const void* K_lm_cache, bool lf, int64_t n_ctx, int64_t L_max, void* o,
+                               void* V_cache, const void* K_lm_cache, bool lf, int64_t mlm, int64_t n_ctx, int64_t L_max, void* o,
                                int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C, int64_t topk,
                                float scale, hils_dtype dt, void* ws, size_t ws_bytes, void* stream);
 static hils_status bwd_impl(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm, bool lf,
@@ -371,7 +371,7 @@ hils_status hils_decode_step_rq(const void* q, const void* q_ret, const void* k_
                                 void* o, int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C,
                                 int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
                                 void* stream) {
-  return decode_impl(q, q_ret, k_new, v_new, K_cache, V_cache, K_lm_cache, false, n_ctx, L_max, o, idx, w, B, H, d,
+  return decode_impl(q, q_ret, k_new, v_new, K_cache, V_cache, K_lm_cache, false, 1, n_ctx, L_max, o, idx, w, B, H, d,
                      C, topk, scale, dt, ws, ws_bytes, stream);
 }
 
@@ -380,14 +380,25 @@ hils_status hils_decode_step_lf(const void* q, const void* q_ret, const void* k_
                                 void* o, int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C,
                                 int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
                                 void* stream) {
-  return decode_impl(q, q_ret, k_new, v_new, K_cache, V_cache, K_lm_cache, true, n_ctx, L_max, o, idx, w, B, H, d,
+  return decode_impl(q, q_ret, k_new, v_new, K_cache, V_cache, K_lm_cache, true, 1, n_ctx, L_max, o, idx, w, B, H, d,
                      C, topk, scale, dt, ws, ws_bytes, stream);
+}
+
+hils_status hils_decode_step_ml(const void* q, const void* q_ret, const void* k_new, const void* v_new,
+                                void* K_cache, void* V_cache, const void* K_lm_cache, int64_t m, int64_t n_ctx,
+                                int64_t L_max, void* o, int32_t* idx, float* w, int64_t B, int64_t H, int64_t d,
+                                int64_t C, int64_t topk, float scale, hils_dtype dt, void* ws, size_t ws_bytes,
+                                void* stream) {
+  if (m < 1 || m > 16) return fail(HILS_ERR_UNSUPPORTED, "landmarks per chunk must be in [1, 16] (got %lld)",
+                                   (long long)m);
+  return decode_impl(q, q_ret, k_new, v_new, K_cache, V_cache, K_lm_cache, false, m, n_ctx, L_max, o, idx, w, B, H,
+                     d, C, topk, scale, dt, ws, ws_bytes, stream);
 }
 
 }  // extern "C"
 
 static hils_status decode_impl(const void* q, const void* q_ret, const void* k_new, const void* v_new, void* K_cache,
-                               void* V_cache, const void* K_lm_cache, bool lf, int64_t n_ctx, int64_t L_max, void* o,
+                               void* V_cache, const void* K_lm_cache, bool lf, int64_t mlm, int64_t n_ctx, int64_t L_max, void* o,
                                int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C, int64_t topk,
                                float scale, hils_dtype dt, void* ws, size_t ws_bytes, void* stream) {
   Dims D;
@@ -414,7 +425,8 @@ static hils_status decode_impl(const void* q, const void* q_ret, const void* k_n
   const size_t need = carve_decode(nullptr, B * H, L_max, d, topk, &W);
   if ((st = check_ws(ws, ws_bytes, need)) != HILS_OK) return st;
   carve_decode(ws, B * H, L_max, d, topk, &W);
-  return hip_status(hils::launch_decode(dt, (int)d, q, q_ret, k_new, v_new, K_cache, V_cache, K_lm_cache, lf, n_ctx,
+  return hip_status(hils::launch_decode(dt, (int)d, q, q_ret, k_new, v_new, K_cache, V_cache, K_lm_cache, lf, (int)mlm,
+                                        n_ctx,
                                         L_max, Nmax, o, idx, w, (int)(B * H), (int)topk, scale, W,
                                         (hipStream_t)stream),
                     "hils_decode_step");

@@ -97,8 +97,9 @@ hipError_t launch_lf_bwd(int dt, int d, const void* Qs, const void* K, const flo
                          float* dK, int BH, int L, int N, int k, float scale, hipStream_t st);
 // qr: retrieval query for the landmark scores (null: q).  lf: landmark-free chunks, the step writes
 // the open chunk's landmark row (the mean of its keys so far) before it is read
+// mlm: landmarks per chunk (Klm [BH][Nmax][mlm][d]; the chunk score is the log-sum-exp of theirs)
 hipError_t launch_decode(int dt, int d, const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc,
-                         void* Vc, const void* Klm, bool lf, int64_t n, int64_t Lmax, int64_t Nmax, void* o,
+                         void* Vc, const void* Klm, bool lf, int mlm, int64_t n, int64_t Lmax, int64_t Nmax, void* o,
                          int32_t* idx, float* w, int BH, int k, float scale, const DecodeBufs& ws, hipStream_t st);
 // decode step of B sequences at their own positions n_ctx[b] (device, <= n_max) over paged caches: page p of
 // the pools holds one chunk of 64 rows per head (Kp, Vp: [pages][H][64][d]; Klm_p: [pages][H][d])

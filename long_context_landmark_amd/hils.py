@@ -43,6 +43,7 @@ _lib.hils_sparse_attn_bwd_rq.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
 _lib.hils_chunk_means.argtypes = [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _int, _vp]
 _lib.hils_sparse_attn_fwd_lf.argtypes = _lib.hils_sparse_attn_fwd_rq.argtypes
 _lib.hils_decode_step_lf.argtypes = _lib.hils_decode_step_rq.argtypes
+_lib.hils_decode_step_ml.argtypes = _lib.hils_decode_step_rq.argtypes[:7] + [_i64] + _lib.hils_decode_step_rq.argtypes[7:]
 _lib.hils_sparse_attn_bwd_lf.argtypes = _lib.hils_sparse_attn_bwd_rq.argtypes
 _lib.hils_sparse_attn_fwd_ml.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64] + _lib.hils_sparse_attn_fwd.argtypes[4:]
 _lib.hils_sparse_attn_bwd_ml.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64] + _lib.hils_sparse_attn_bwd_rq.argtypes[5:]
@@ -271,7 +272,13 @@ def decode_step(q, k_new, v_new, K_cache, V_cache, K_lm_cache, n_ctx, k, C=64, s
     wsb, n = _workspace(OP_DECODE, B, H, L_max, d, C, k, q.device, ws)
     args = (_p(k_new), _p(v_new), _p(K_cache), _p(V_cache), _p(K_lm_cache), n_ctx, L_max, _p(o), _p(idx), _p(w), B,
             H, d, C, k, _scale(d, scale), _dt(q), _p(wsb), n, _stream())
-    if landmark_free:
+    if K_lm_cache.dim() == 5:
+        # several landmarks per chunk: K_lm_cache [B,H,N_max,m,d]
+        if landmark_free:
+            raise ValueError("landmark-free decode takes one landmark per chunk")
+        a = list(args)
+        _check(_lib.hils_decode_step_ml(_p(q), _p(q_ret), *a[:5], K_lm_cache.shape[3], *a[5:]))
+    elif landmark_free:
         _check(_lib.hils_decode_step_lf(_p(q), _p(q_ret), *args))
     elif q_ret is None:
         _check(_lib.hils_decode_step(_p(q), *args))

@@ -182,3 +182,10 @@ def test_multi_landmark_forward_validates(lib, hils):
                                        None) == UNSUPPORTED
     assert lib.hils_sparse_attn_fwd_ml(FAKE, None, FAKE, FAKE, FAKE, 2, FAKE, FAKE, *tail, FAKE, need - 16,
                                        None) == WORKSPACE
+
+
+def test_multi_landmark_decode_validates(lib, hils):
+    nd = hils.workspace_size(hils.OP_DECODE, 1, 2, 1024, 64, 64, 4)
+    for m in (0, 17):
+        assert lib.hils_decode_step_ml(FAKE, None, *([FAKE] * 5), m, 100, 1024, FAKE, FAKE, FAKE, 1, 2, 64, 64, 4,
+                                       0.125, 0, FAKE, nd, None) == UNSUPPORTED

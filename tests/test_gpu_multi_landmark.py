@@ -132,3 +132,53 @@ def test_bwd_multi_landmark(hils, gpu, dtype, B, H, L, d, k, kind, m, rq):
     tol = (5e-3, 3e-3) if dtype == "f32" else (2e-2, 1e-2)
     for name, got in zip(names, grads):
         assert_close(f32(got), ref[name], name, *tol)
+
+
+@pytest.mark.parametrize("dtype,H,d,ctx,steps,k,m", [
+    ("bf16", 2, 64, 64 * 40 + 10, 70, 4, 2),   # crosses a chunk boundary
+    ("bf16", 2, 128, 64 * 300 + 62, 3, 16, 3),  # several scan slices
+    ("f32", 2, 64, 64 * 20, 20, 4, 2),
+])
+def test_decode_multi_landmark(hils, gpu, dtype, H, d, ctx, steps, k, m):
+    B = 1
+    say(f"decode several landmarks dtype={dtype} H={H} d={d} ctx={ctx} steps={steps} k={k} m={m}")
+    x = synth.decode_inputs(B, H, d, ctx, steps, C=64, seed=830 + ctx + d, dtype=dtype)
+    Nmax = x["Klm"].shape[2]
+    lm = np.random.default_rng(831).standard_normal((B, H, Nmax, m, d), dtype=np.float32)
+    lm = synth.f32_to_bf16_bits(lm) if dtype == "bf16" else lm
+    Lmax = x["K_cache"].shape[2]
+    Kc_g, Vc_g, lm_g = dev(x["K_cache"]), dev(x["V_cache"]), dev(lm)
+    Kc_h, Vc_h = x["K_cache"].copy(), x["V_cache"].copy()
+    ws = torch.empty(hils.workspace_size(hils.OP_DECODE, B, H, Lmax, d, 64, k), dtype=torch.uint8, device=gpu)
+    tol = (5e-3, 3e-3) if dtype == "f32" else (2e-2, 1e-2)
+    lmf = synth.as_f32(lm).astype(np.float64)[0]
+    for s in range(steps):
+        n = ctx + s
+        o, idx, w = hils.decode_step(dev(x["q"][s]), dev(x["k_new"][s]), dev(x["v_new"][s]), Kc_g, Vc_g, lm_g, n, k,
+                                     ws=ws)
+        ref = oracle.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc_h, Vc_h, lm, n, 64, k)
+        torch.cuda.synchronize()
+        c = n // 64
+        mm = min(k, c)
+        gi, ri = idx.cpu().numpy().reshape(H, k + 1), ref["idx"].reshape(H, k + 1)
+        go, ro = f32(o).reshape(H, d), ref["o"].reshape(H, d)
+        gw, rw = f32(w).reshape(H, k + 1), ref["w"].reshape(H, k + 1)
+        keep = []
+        for h in range(H):
+            assert gi[h, k] == c and np.all(gi[h, mm:k] == -1)
+            a, b = set(gi[h, :mm].tolist()), set(ri[h, :mm].tolist())
+            if a != b:
+                q = synth.as_f32(x["q"][s][0, h]).astype(np.float64)
+                sc_r = lmf[h, :c] @ q / np.sqrt(d)
+                sc = (np.log(np.exp(sc_r - sc_r.max(1, keepdims=True)).sum(1)) + sc_r.max(1)).astype(np.float32)
+                mth = np.sort(sc)[::-1][mm - 1]
+                for j in a ^ b:
+                    assert abs(float(sc[j]) - float(mth)) < GAP, (s, h, j)
+                continue
+            keep.append(h)
+            gm = {int(j): gw[h, r] for r, j in enumerate(gi[h]) if j >= 0}
+            om = {int(j): rw[h, r] for r, j in enumerate(ri[h]) if j >= 0}
+            assert gm.keys() == om.keys()
+            for j in gm:
+                assert abs(gm[j] - om[j]) < 2e-5
+        assert_close(go[keep], ro[keep], f"o step {s}", *tol)
