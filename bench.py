@@ -368,7 +368,7 @@ def bench_train(hils, synth, name, steps, warmup, rq=False, lf=False, ml=False):
     return res
 
 
-def bench_decode(hils, synth, name, replicas, warmup, lf=False):
+def bench_decode(hils, synth, name, replicas, warmup, lf=False, ml=False):
     """lf: landmark-free chunks; each replica's landmark rows start as its chunks' key means and the step
     maintains the open chunk's row."""
     import torch
@@ -379,6 +379,13 @@ def bench_decode(hils, synth, name, replicas, warmup, lf=False):
     if lf:
         for r in reps:
             hils.chunk_means(r["K_cache"], w.C, n_chunks=w.L // w.C, K_lm=r["Klm"])
+    if ml:
+        # two landmarks per chunk: the given row and a second N(0,1) row
+        g = torch.Generator(device="cuda:0")
+        g.manual_seed(w.seed + 7)
+        for r in reps:
+            extra_lm = torch.randn(r["Klm"].shape, generator=g, device="cuda:0").to(r["Klm"].dtype)
+            r["Klm"] = torch.stack([r["Klm"], extra_lm], dim=3).contiguous()
     B, H, d = w.B, w.H, w.d
     Lmax = w.L + w.steps
     ws = torch.empty(hils.workspace_size(hils.OP_DECODE, B, H, Lmax, d, w.C, w.k), dtype=torch.uint8,
@@ -437,10 +444,10 @@ def bench_decode(hils, synth, name, replicas, warmup, lf=False):
         "calls": calls,
         "wall_s": wall,
         "kernel_us": {n: round(t / c * 1e3, 3) for n, (t, c) in kt.items()},
-        "roofline": roofline(kt, work, {n: 1 for n in kt}, None if lf else name),
+        "roofline": roofline(kt, work, {n: 1 for n in kt}, None if lf or ml else name),
         "config": {"workload": name, "B": B, "H": H, "d": d, "context": w.L, "steps": w.steps, "k": w.k,
                    "replicas": len(reps), "protocol": "cold" if len(reps) > 1 else "warm",
-                   **({"landmark_free": True} if lf else {})},
+                   **({"landmark_free": True} if lf else {}), **({"landmarks_per_chunk": 2} if ml else {})},
     }
     del x, reps, ws
     torch.cuda.empty_cache()
@@ -532,8 +539,9 @@ def main():
                                                "train_8k; a _retrieval suffix on a prefill or train workload "
                                                "adds separate retrieval queries, a _landmark_free suffix on a "
                                                "prefill, decode or train workload uses key-mean landmarks, a "
-                                               "_two_landmarks suffix on a prefill or train workload uses the "
-                                               "first and last token of each chunk as landmarks) and print "
+                                               "_two_landmarks suffix on a prefill, train or decode workload uses "
+                                               "two landmarks per chunk (prefill and train: the "
+                                               "first and last token of each chunk) and print "
                                                "its result object; for profiling runs")
     ap.add_argument("--decode-replicas", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -574,7 +582,7 @@ def main():
         elif name.startswith("decode_paged"):
             res = bench_decode_paged(hils, synth, name, args.warmup)
         elif name.startswith("decode"):
-            res = bench_decode(hils, synth, name, args.decode_replicas, args.warmup, lf=lf)
+            res = bench_decode(hils, synth, name, args.decode_replicas, args.warmup, lf=lf, ml=ml)
         elif name.startswith("train"):
             res = bench_train(hils, synth, name, args.steps, args.warmup, rq=rq, lf=lf, ml=ml)
         else:
@@ -623,6 +631,7 @@ def main():
         extra["prefill_8k_two_landmarks"] = bench_prefill(hils, synth, "prefill_8k", max(3, min(args.steps, 20)), 2,
                                                           ml=True)
         extra["train_8k_two_landmarks"] = bench_train(hils, synth, "train_8k", max(3, min(args.steps, 20)), 2, ml=True)
+        extra["decode_512k_two_landmarks"] = bench_decode(hils, synth, "decode_512k", args.decode_replicas, 4, ml=True)
         log(f"[bench] prefill_8k_two_landmarks {extra['prefill_8k_two_landmarks']['ms_per_step']*1e3:.1f} us/step, "
             f"train_8k_two_landmarks {extra['train_8k_two_landmarks']['ms_per_step']*1e3:.1f} us/step")
     if "decode_paged_b16" not in skip:
