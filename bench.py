@@ -100,9 +100,9 @@ def prefill_work(B, H, L, d, k, C=64):
             # landmark-free chunks only
             "chunk_mean": ("hbm", 0, BH * (L * d * 2 + N * d * 2)),
             "lf_own": ("hbm", BH * L * 2 * d, BH * L * (2 * d * 2 + k1 * 12)),
-            # two landmarks per chunk only: causal (query, chunk, landmark) dot products on the VALU, the
+            # two landmarks per chunk only: causal (query, chunk, landmark) dot products on MFMA, the
             # chunk scores written once and read back by the selection
-            "ml_scores": ("valu", BH * C * (N * (N + 1) // 2) * 2 * 2 * d, BH * (L * d * 2 + C * (N * (N + 1) // 2) * 4)),
+            "ml_scores": ("mfma", BH * C * (N * (N + 1) // 2) * 2 * 2 * d, BH * (L * d * 2 + C * (N * (N + 1) // 2) * 4)),
             "ml_select": ("hbm", 0, BH * (C * (N * (N + 1) // 2) * 4 + L * k1 * 12)),
         },
     }

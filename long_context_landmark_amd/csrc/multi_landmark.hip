@@ -3,11 +3,11 @@
 // softmax over a chunk's landmark scores before the chunk-level one.  Read as: the chunk score is
 // the log-sum-exp of the chunk's m landmark scores.  K_lm is [B][H][N][m][d].
 //
-//   ml_scores   one workgroup per (query chunk, head): the 64 queries staged as fp32 in LDS; for
-//               every tile of 64 chunks up to the query chunk and every landmark, the landmark
-//               rows staged and the 64 x 64 dot products formed on the VALU (each thread a block of
-//               4 queries x 4 chunks: eight LDS reads per sixteen products), folded into a running
-//               log-sum-exp per (query, chunk).  Writes the causal chunk scores S [BH][L][N] (fp32).
+//   ml_scores   one workgroup per (64 queries, 64 chunks, head) tile on or below the causal
+//               diagonal: for every landmark the 64 x 64 score tile on MFMA (16x16x32 bf16 or
+//               16x16x4 fp32; each wave 16 chunks x 64 queries, operands straight from HBM), folded
+//               into a running log-sum-exp per (query, chunk) in registers.  Writes the causal chunk
+//               scores S [BH][L][N] (fp32).
 //   ml_select   one wave per query row: the m = min(k, c) best past chunks by (score desc, index
 //               asc) in k rounds of a group maximum over 64-bit keys (16 lanes per row when the
 //               row has at most 128 chunks and k < 16, else a wave; keys held in registers up to
@@ -22,76 +22,52 @@ namespace hils {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void ml_scores_kernel(const T* __restrict__ Qs, const T* __restrict__ Klm,
                                                         float* __restrict__ S, int L, int N, int m, float scale) {
-  constexpr int EPP = 16 / Elem<T>::bytes;
-  constexpr int PIECES = D / EPP;
-  constexpr int RPR = 256 / PIECES;
-  constexpr int KS = D + 1;
-  const int qc = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const int qg = tid & 15, jg = tid >> 4;  // this thread's block: queries 4qg..4qg+3, tile chunks 4jg..4jg+3
-  const int64_t row0 = (int64_t)bh * L + (int64_t)qc * 64;
-  __shared__ float qs[64 * KS];
-  __shared__ float lm[64 * KS];
-  const int piece = tid % PIECES, rr = tid / PIECES;
+  const int bh = blockIdx.z;
+  const int t0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
+  if (j0 > t0 / 64) return;  // no causal chunk in this tile
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
+  const T* Qb = Qs + (int64_t)bh * L * D;
+  const int jrow = j0 + 16 * w + r16;
+  float mx[4][4], z[4][4];
+  for (int u = 0; u < m; ++u) {
+    f32x4_t acc[4];
 #pragma unroll
-  for (int r0 = 0; r0 < 64; r0 += RPR) {
-    const int r = r0 + rr;
-    const int4 raw = *reinterpret_cast<const int4*>(Qs + (row0 + r) * D + piece * EPP);
-    T vals[EPP];
-    __builtin_memcpy(vals, &raw, 16);
+    for (int qb = 0; qb < 4; ++qb) acc[qb] = zero4();
 #pragma unroll
-    for (int e = 0; e < EPP; ++e) qs[r * KS + piece * EPP + e] = Elem<T>::to_f32(vals, e);
-  }
-  for (int j0 = 0; j0 <= qc; j0 += 64) {
-    float mx[16], z[16];
-    for (int u = 0; u < m; ++u) {
-      __syncthreads();  // the previous landmark tile is consumed
+    for (int ks = 0; ks < D / 32; ++ks) {
+      Frag<T> a;
+      if (jrow < N) a.load(Klm + (((int64_t)bh * N + jrow) * m + u) * D + ks * 32 + 8 * g);
+      else a.zero();
 #pragma unroll
-      for (int r0 = 0; r0 < 64; r0 += RPR) {
-        const int jj = r0 + rr, j = j0 + jj;
-        int4 raw = make_int4(0, 0, 0, 0);
-        if (j <= qc) raw = *reinterpret_cast<const int4*>(Klm + (((int64_t)bh * N + j) * m + u) * D + piece * EPP);
-        T vals[EPP];
-        __builtin_memcpy(vals, &raw, 16);
-#pragma unroll
-        for (int e = 0; e < EPP; ++e) lm[jj * KS + piece * EPP + e] = Elem<T>::to_f32(vals, e);
-      }
-      __syncthreads();
-      float acc[16];  // [query a][chunk b] at 4a + b
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-      for (int e = 0; e < D; ++e) {
-        float qv[4], lv[4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) qv[a] = qs[(4 * qg + a) * KS + e];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) lv[b] = lm[(4 * jg + b) * KS + e];
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int b = 0; b < 4; ++b) acc[4 * a + b] += qv[a] * lv[b];
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float a = scale * acc[i];
-        if (u == 0) {
-          mx[i] = a;
-          z[i] = 1.f;
-        } else if (a > mx[i]) {
-          z[i] = z[i] * __expf(mx[i] - a) + 1.f;
-          mx[i] = a;
-        } else {
-          z[i] += __expf(a - mx[i]);
-        }
+      for (int qb = 0; qb < 4; ++qb) {
+        Frag<T> b;
+        b.load(Qb + (int64_t)(t0 + 16 * qb + r16) * D + ks * 32 + 8 * g);
+        mma(acc[qb], a, b);
       }
     }
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      float* srow = S + (row0 + 4 * qg + a) * N;
+    for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int j = j0 + 4 * jg + b;
-        if (j <= qc) srow[j] = m == 1 ? mx[4 * a + b] : mx[4 * a + b] + __logf(z[4 * a + b]);
+      for (int i = 0; i < 4; ++i) {
+        const float a = scale * acc[qb][i];
+        if (u == 0) {
+          mx[qb][i] = a;
+          z[qb][i] = 1.f;
+        } else if (a > mx[qb][i]) {
+          z[qb][i] = z[qb][i] * __expf(mx[qb][i] - a) + 1.f;
+          mx[qb][i] = a;
+        } else {
+          z[qb][i] += __expf(a - mx[qb][i]);
+        }
       }
+  }
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb) {
+    const int t = t0 + 16 * qb + r16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + 16 * w + 4 * g + i;
+      if (j < N && j <= t / 64) S[((int64_t)bh * L + t) * N + j] = m == 1 ? mx[qb][i] : mx[qb][i] + __logf(z[qb][i]);
     }
   }
 }
@@ -174,8 +150,8 @@ __global__ __launch_bounds__(256) void ml_select_kernel(const float* __restrict_
 template <typename T, int D>
 static hipError_t ml_scores_t(const void* Qs, const void* Klm, float* S, int BH, int L, int N, int m, float scale,
                               hipStream_t st) {
-  HILS_LAUNCH("ml_scores", (ml_scores_kernel<T, D>), dim3(L / 64, BH), dim3(256), 0, st, (const T*)Qs,
-              (const T*)Klm, S, L, N, m, scale);
+  HILS_LAUNCH("ml_scores", (ml_scores_kernel<T, D>), dim3(L / 64, (N + 63) / 64, BH), dim3(256), 0, st,
+              (const T*)Qs, (const T*)Klm, S, L, N, m, scale);
   return hipGetLastError();
 }
 
