@@ -13,13 +13,15 @@
 // them).  decode_scan streams them with 16-byte coalesced loads over many
 // workgroups; each workgroup scores 256 chunks and writes only its 16 best
 // (score, chunk) keys, sorted.  The top-m of the context is the top-m of the
-// union of these lists, since m <= 16.  decode_attend runs one 1024-thread
-// workgroup per head: wave 0 merges the lists (the m-th largest of a few list
-// heads bounds the answer from below; the keys above the bound are compacted
-// with ballots and sorted exactly) while wave 15 already attends to the open
-// chunk, which needs no selection.  The kept chunks are then split over the 16
-// wavefronts (split-K), each reading its chunk's keys and values with 16-byte
-// loads, and the per-chunk outputs are fused with the retrieval weights in LDS.
+// union of these lists, since m <= 16.  decode_attend runs DEC_SPLIT = 8
+// workgroups of two wavefronts per head: wave 0 of every workgroup merges the
+// lists (the m-th largest of a few list heads bounds the answer from below; the
+// keys above the bound are compacted with ballots and sorted exactly) and forms
+// the fusion weights, while the second wave of workgroup 0 already attends to
+// the open chunk, which needs no selection.  The kept chunks are then split over
+// the 16 wavefronts of the eight workgroups (split-K), each reading its chunk's
+// keys and values with 16-byte loads; every workgroup writes its weighted
+// partial sum, and decode_fuse adds the eight partials of a head in order.
 #include "hils_device.h"
 #include "hils_launch.h"
 

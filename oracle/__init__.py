@@ -11,6 +11,8 @@ marshals numpy arrays through ctypes.  Inputs are either ``float32`` arrays or
 
 Parity status of each function (what pins it is in ``tests/test_oracle_*.py``):
   landmark_scores  pinned (numpy einsum in fp64)
+  landmark_scores_rows  pinned (rows of the einsum scores in the order listed, and equal
+                   to the same rows of landmark_scores)
   fwd (selection)  pinned (numpy lexsort, subset brute force, exact ties)
   fwd (attention)  pinned (dense causal attention via the chunk-LSE identity,
                    single-chunk reduction, equal-score mean, invariances)
@@ -21,6 +23,13 @@ Parity status of each function (what pins it is in ``tests/test_oracle_*.py``):
   landmark-free    pinned (key means against numpy; rows ending a chunk equal the plain
                    operator on numpy means; own score of a chunk's first row is the scaled
                    q.k; own score against numpy prefix means; decode steps equal prefill rows)
+  fwd_ml, bwd_ml   pinned (one landmark per chunk is the plain operator bit for bit;
+  (several         duplicated landmarks shift every score by log 2 and change nothing
+   landmarks)      else; first/last-token landmark scores against numpy logaddexp and their
+                   lexsort; central differences of dQ, dK, dV and dKlm; decode steps with
+                   several landmarks equal prefill rows)
+  decode_paged     pinned (equal to per-sequence contiguous decode steps over the gathered
+                   pages, pages shuffled; with and without landmark-free chunks)
 """
 from __future__ import annotations
 
@@ -67,7 +76,7 @@ def _load():
                                vp, vp, vp, vp, vp, ip]
     lib.oracle_fwd.restype = ip
     lib.oracle_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, dbl,
-                                  ip, vp, vp, vp, vp, vp, ip]
+                                  ip, vp, vp, vp, vp, vp, ip, ip]
     lib.oracle_decode.restype = ip
     lib.oracle_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, dbl, ip, vp, vp,
                                vp, vp, vp, ip]
@@ -225,7 +234,8 @@ def fwd_lf(Q, K, V, C, k, scale=None, rows=None, idx=None, nthreads=0, Q_ret=Non
     return {"idx": idx_out, "sel": sel, "w": w, "lse": lse, "O": O, "Klm": Klm, "threads": used}
 
 
-def decode(q, k_new, v_new, Kc, Vc, Klm, n, C, k, scale=None, nthreads=0, q_ret=None, landmark_free=False):
+def decode(q, k_new, v_new, Kc, Vc, Klm, n, C, k, scale=None, nthreads=0, q_ret=None, landmark_free=False,
+           idx=None):
     """One decode step at position n for every (b,h).
 
     Writes k_new / v_new into row n of ``Kc`` / ``Vc`` in place (these are the
@@ -233,6 +243,8 @@ def decode(q, k_new, v_new, Kc, Vc, Klm, n, C, k, scale=None, nthreads=0, q_ret=
     and o [B,H,d].  ``q_ret`` (like q): retrieval queries for the landmark scores.
     ``landmark_free``: landmark row n//C of ``Klm`` (updated in place) becomes the mean of the open
     chunk's keys so far; earlier rows are read as given (the key means of their chunks).
+    ``idx`` [B,H,k+1] (optional): the selection held fixed; the step scores, weights and attends to
+    these chunks (slots with -1 unused) instead of selecting its own, as ``fwd`` does with ``idx``.
     """
     q, k_new, v_new = _c(q), _c(k_new), _c(v_new)
     if landmark_free and not Klm.flags.c_contiguous:
@@ -250,13 +262,14 @@ def decode(q, k_new, v_new, Kc, Vc, Klm, n, C, k, scale=None, nthreads=0, q_ret=
         raise ValueError("n out of range")
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     k1 = k + 1
-    idx = np.empty((B, H, k1), np.int32)
+    use_idx = idx is not None
+    idx = _c(np.array(idx, np.int32, copy=True)).reshape(B, H, k1) if use_idx else np.empty((B, H, k1), np.int32)
     sel = np.empty((B, H, k1), np.float64)
     w = np.empty((B, H, k1), np.float64)
     lse = np.empty((B, H, k1), np.float64)
     o = np.empty((B, H, d), np.float64)
     tail = (n, Lmax, Nmax, B, H, d, C, k, scale, _dt(q, k_new, v_new, Kc, Vc, Klm), _p(idx), _p(sel), _p(w), _p(lse),
-            _p(o), nthreads)
+            _p(o), nthreads, int(use_idx))
     head = (_p(q), _p(qr), _p(k_new), _p(v_new), _p(Kc), _p(Vc), _p(Klm))
     if Klm.ndim == 5:
         # several landmarks per chunk: Klm [B,H,Nmax,m,d]
@@ -328,11 +341,12 @@ def bwd_lf(Q, K, V, dO, idx, C, k, scale=None, nthreads=0, Q_ret=None):
 
 
 def decode_paged(q, k_new, v_new, Kp, Vp, Klm_p, page_table, n_ctx, C, k, scale=None, nthreads=0, q_ret=None,
-                 landmark_free=False):
+                 landmark_free=False, idx=None):
     """One decode step of B sequences at positions n_ctx[b] over page pools Kp, Vp [P,H,C,d], Klm_p [P,H,d]
-    (host arrays, updated in place) with page_table [B,max_pages].  Paging only moves rows: each sequence's
-    chunks 0..n_ctx[b]//C are gathered into contiguous caches, ``decode`` runs there, and the rows it writes
-    go back to their pages.  Returns idx / sel / w / lse [B,H,k+1] and o [B,H,d]."""
+    (or [P,H,m,d]: m landmarks per chunk) (host arrays, updated in place) with page_table [B,max_pages].
+    Paging only moves rows: each sequence's chunks 0..n_ctx[b]//C are gathered into contiguous caches,
+    ``decode`` runs there, and the rows it writes go back to their pages.  ``idx`` [B,H,k+1] (optional):
+    the selection held fixed.  Returns idx / sel / w / lse [B,H,k+1] and o [B,H,d]."""
     B, H, d = q.shape
     maxp = page_table.shape[1]
     Lmax = maxp * C
@@ -343,13 +357,14 @@ def decode_paged(q, k_new, v_new, Kp, Vp, Klm_p, page_table, n_ctx, C, k, scale=
         pages = [int(page_table[b, j]) for j in range(c + 1)]
         Kc = np.zeros((1, H, Lmax, d), Kp.dtype)
         Vc = np.zeros_like(Kc)
-        Klm = np.zeros((1, H, maxp, d), Klm_p.dtype)
+        Klm = np.zeros((1, H, maxp) + Klm_p.shape[2:], Klm_p.dtype)
         for j, p in enumerate(pages):
             Kc[0, :, j * C:(j + 1) * C] = Kp[p]
             Vc[0, :, j * C:(j + 1) * C] = Vp[p]
             Klm[0, :, j] = Klm_p[p]
         r = decode(q[b:b + 1], k_new[b:b + 1], v_new[b:b + 1], Kc, Vc, Klm, n, C, k, scale=scale, nthreads=nthreads,
-                   q_ret=None if q_ret is None else q_ret[b:b + 1], landmark_free=landmark_free)
+                   q_ret=None if q_ret is None else q_ret[b:b + 1], landmark_free=landmark_free,
+                   idx=None if idx is None else idx[b:b + 1])
         Kp[pages[c], :, n - c * C] = Kc[0, :, n]
         Vp[pages[c], :, n - c * C] = Vc[0, :, n]
         if landmark_free:

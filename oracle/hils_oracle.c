@@ -363,11 +363,13 @@ int oracle_fwd_lf(const void* Q, const void* Qr, const void* K, const void* V, v
  * t = n over keys 0..n and landmark rows 0..n/C.  The landmark row of the
  * open chunk n/C is read as the caller supplied it.
  * Caches are [B,H,Lmax,d]; Klm is [B,H,Nmax,d].
+ * use_idx: idx holds a given selection on entry (as in oracle_fwd); the step
+ * then scores and attends to those chunks instead of selecting its own.
  */
 static int decode_common(const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc, void* Vc,
                          void* Klm, int lf, int64_t mlm, int64_t n, int64_t Lmax, int64_t Nmax, int64_t B, int64_t H,
                          int64_t d, int64_t C, int64_t k, double scale, int dt, int32_t* idx,
-                         double* sel, double* w, double* lse, double* o, int nthreads) {
+                         double* sel, double* w, double* lse, double* o, int nthreads, int use_idx) {
   int64_t esz = dt == DT_F32 ? 4 : 2;
   for (int64_t bh = 0; bh < B * H; ++bh) {
     memcpy((char*)Kc + ((bh * Lmax + n) * d) * esz, (const char*)k_new + bh * d * esz, (size_t)(d * esz));
@@ -387,7 +389,7 @@ static int decode_common(const void* q, const void* qr, const void* k_new, const
   int64_t k1 = k + 1;
 #pragma omp parallel for schedule(static)
   for (int64_t bh = 0; bh < B * H; ++bh)
-    row_forward(&P, q, bh, bh, n, 0, NULL, idx + bh * k1, sel + bh * k1, w + bh * k1,
+    row_forward(&P, q, bh, bh, n, use_idx, NULL, idx + bh * k1, sel + bh * k1, w + bh * k1,
                 lse + bh * k1, o + bh * d);
   return used;
 }
@@ -395,9 +397,9 @@ static int decode_common(const void* q, const void* qr, const void* k_new, const
 int oracle_decode(const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc, void* Vc,
                   const void* Klm, int64_t n, int64_t Lmax, int64_t Nmax, int64_t B, int64_t H,
                   int64_t d, int64_t C, int64_t k, double scale, int dt, int32_t* idx,
-                  double* sel, double* w, double* lse, double* o, int nthreads) {
+                  double* sel, double* w, double* lse, double* o, int nthreads, int use_idx) {
   return decode_common(q, qr, k_new, v_new, Kc, Vc, (void*)Klm, 0, 1, n, Lmax, Nmax, B, H, d, C, k, scale, dt, idx,
-                       sel, w, lse, o, nthreads);
+                       sel, w, lse, o, nthreads, use_idx);
 }
 
 /*
@@ -409,10 +411,10 @@ int oracle_decode(const void* q, const void* qr, const void* k_new, const void* 
 int oracle_decode_lf(const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc, void* Vc,
                      void* Klm, int64_t n, int64_t Lmax, int64_t Nmax, int64_t B, int64_t H,
                      int64_t d, int64_t C, int64_t k, double scale, int dt, int32_t* idx,
-                     double* sel, double* w, double* lse, double* o, int nthreads) {
+                     double* sel, double* w, double* lse, double* o, int nthreads, int use_idx) {
   if (d > MAX_D) return -1;
   return decode_common(q, qr, k_new, v_new, Kc, Vc, Klm, 1, 1, n, Lmax, Nmax, B, H, d, C, k, scale, dt, idx, sel, w,
-                       lse, o, nthreads);
+                       lse, o, nthreads, use_idx);
 }
 
 /*
@@ -595,8 +597,8 @@ int oracle_bwd_ml(const void* Q, const void* Qr, const void* K, const void* V, c
 int oracle_decode_ml(const void* q, const void* qr, const void* k_new, const void* v_new, void* Kc, void* Vc,
                      const void* Klm, int64_t m, int64_t n, int64_t Lmax, int64_t Nmax, int64_t B, int64_t H,
                      int64_t d, int64_t C, int64_t k, double scale, int dt, int32_t* idx,
-                     double* sel, double* w, double* lse, double* o, int nthreads) {
+                     double* sel, double* w, double* lse, double* o, int nthreads, int use_idx) {
   if (m < 1 || m > 64) return -1;
   return decode_common(q, qr, k_new, v_new, Kc, Vc, (void*)Klm, 0, m, n, Lmax, Nmax, B, H, d, C, k, scale, dt, idx,
-                       sel, w, lse, o, nthreads);
+                       sel, w, lse, o, nthreads, use_idx);
 }

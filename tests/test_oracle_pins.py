@@ -79,6 +79,26 @@ def test_scores_bf16_inputs_exact(oracle_mod):
     np.testing.assert_array_equal(S[ok], ref[ok].astype(np.float32).astype(np.float64))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_score_rows_match_einsum_rows(oracle_mod, dtype):
+    """The row-subset scorer (used by the selection gap rule of the GPU tests) returns, for each listed
+    flattened row (b*H + h)*L + t, that row of the einsum scores with the causal mask, in the order listed:
+    rows of several heads, a repeated row, unsorted order, the first and last row of a chunk."""
+    B, H, L, d, C = 2, 3, 320, 32, 64
+    x = rand_inputs(B, H, L, d, C=C, seed=21, dtype=dtype)
+    ref = np.einsum("bhtd,bhjd->bhtj", f64(x["Q"]), f64(x["Klm"])) / math.sqrt(d)
+    ref = ref.astype(np.float32).astype(np.float64).reshape(B * H * L, L // C)
+    rows = np.array([5 * L + 319, 0, 63, 64, 2 * L + 200, 3 * L + 127, 2 * L + 200, L + 1, 4 * L + 256], np.int64)
+    S = oracle_mod.landmark_scores_rows(x["Q"], x["Klm"], C, rows)
+    assert S.shape == (rows.size, L // C)
+    for i, r in enumerate(rows):
+        c = int(r % L) // C
+        np.testing.assert_allclose(S[i, :c + 1], ref[r, :c + 1], rtol=1e-6, atol=1e-7)
+        assert np.all(np.isneginf(S[i, c + 1:]))
+        # and the full-matrix scorer agrees bit for bit on that row
+        np.testing.assert_array_equal(S[i], oracle_mod.landmark_scores(x["Q"], x["Klm"], C).reshape(B * H * L, -1)[r])
+
+
 # --------------------------------------------------------------------------- selection
 
 
@@ -309,6 +329,54 @@ def test_decode_matches_prefill_rows(oracle_mod, qret):
         np.testing.assert_array_equal(outs[s]["o"].reshape(-1, d)[bh], ref["O"][i])
     # the appended rows are the step inputs
     np.testing.assert_array_equal(Kc[:, :, ctx:L], np.moveaxis(x["k_new"], 0, 2))
+
+
+@pytest.mark.parametrize("lf", [False, True])
+def test_decode_fixed_selection_matches_prefill_rows(oracle_mod, lf):
+    """A decode step with its selection held fixed equals the prefill row with that selection held fixed
+    (the fixed-selection forward is pinned above); given its own selection it is the free step exactly."""
+    B, H, d, C, k = 1, 2, 16, 64, 3
+    ctx, steps = 64 * 7 + 20, 50
+    x = synth.decode_inputs(B, H, d, ctx, steps, C=C, seed=16, dtype="bf16")
+    Kc, Vc = x["K_cache"].copy(), x["V_cache"].copy()
+    Klm = x["Klm"].copy()
+    if lf:
+        oracle_mod.chunk_means(Kc, C, nchunks=ctx // C, Klm=Klm)
+    rng = np.random.default_rng(3)
+    fixed, outs = [], []
+    for s in range(steps):
+        n = ctx + s
+        c = n // C
+        free = oracle_mod.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc, Vc, Klm, n, C, k, landmark_free=lf)
+        again = oracle_mod.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc, Vc, Klm, n, C, k, landmark_free=lf,
+                                  idx=free["idx"])
+        for key in ("idx", "sel", "w", "lse", "o"):
+            np.testing.assert_array_equal(again[key], free[key])
+        sel = free["idx"].copy()
+        for h in range(H):
+            sel[0, h, :k] = np.sort(rng.choice(c, size=k, replace=False))
+        fixed.append(sel)
+        outs.append(oracle_mod.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc, Vc, Klm, n, C, k,
+                                      landmark_free=lf, idx=sel))
+    L = ctx + steps
+    L_pad = ((L + C - 1) // C) * C
+    Q = np.zeros((B, H, L_pad, d), np.uint16)
+    for s in range(steps):
+        Q[:, :, ctx + s] = x["q"][s]
+    K = np.zeros_like(Q)
+    V = np.zeros_like(Q)
+    K[:, :, :L] = Kc[:, :, :L]
+    V[:, :, :L] = Vc[:, :, :L]
+    rows = np.array([bh * L_pad + ctx + s for s in range(steps) for bh in range(B * H)])
+    idx = np.stack([fixed[s].reshape(-1, k + 1)[bh] for s in range(steps) for bh in range(B * H)])
+    if lf:
+        ref = oracle_mod.fwd_lf(Q, K, V, C, k, rows=rows, idx=idx)
+    else:
+        ref = oracle_mod.fwd(Q, K, V, x["Klm"][:, :, :L_pad // C], C, k, rows=rows, idx=idx)
+    for i, (s, bh) in enumerate((s, bh) for s in range(steps) for bh in range(B * H)):
+        np.testing.assert_array_equal(outs[s]["idx"].reshape(-1, k + 1)[bh], ref["idx"][i])
+        np.testing.assert_array_equal(outs[s]["w"].reshape(-1, k + 1)[bh], ref["w"][i])
+        np.testing.assert_array_equal(outs[s]["o"].reshape(-1, d)[bh], ref["O"][i])
 
 
 def test_decode_in_first_chunk_is_dense(oracle_mod):
@@ -611,7 +679,7 @@ def _paged_from_contiguous(Kc, Vc, Klm, nchunks, rng, spare=3):
     table = np.zeros((B, maxp), np.int32)
     Kp = np.zeros((total, H, C, d), Kc.dtype)
     Vp = np.zeros_like(Kp)
-    Lp = np.zeros((total, H, d), Klm.dtype)
+    Lp = np.zeros((total, H) + Klm.shape[3:], Klm.dtype)
     nxt = 0
     for b in range(B):
         for j in range(nchunks[b]):
@@ -624,9 +692,10 @@ def _paged_from_contiguous(Kc, Vc, Klm, nchunks, rng, spare=3):
     return Kp, Vp, Lp, table
 
 
-@pytest.mark.parametrize("lf", [False, True])
-def test_paged_decode_equals_contiguous_per_sequence(oracle_mod, lf):
-    """Ragged positions, shuffled pages: every sequence's steps equal its own contiguous decode."""
+@pytest.mark.parametrize("lf,m", [(False, 1), (True, 1), (False, 2)])
+def test_paged_decode_equals_contiguous_per_sequence(oracle_mod, lf, m):
+    """Ragged positions, shuffled pages: every sequence's steps equal its own contiguous decode (one landmark
+    per chunk, landmark-free chunks, two landmarks per chunk); so do steps with a selection held fixed."""
     B, H, d, C, k = 3, 2, 16, 64, 3
     ctxs = [64 * 5 + 10, 64 * 2 + 60, 7]
     steps = 70
@@ -637,11 +706,15 @@ def test_paged_decode_equals_contiguous_per_sequence(oracle_mod, lf):
     Lmax = (Lmax + C - 1) // C * C
     Kc = np.zeros((B, H, Lmax, d), np.uint16)
     Vc = np.zeros_like(Kc)
-    Klm = np.zeros((B, H, Lmax // C, d), np.uint16)
+    Klm = np.zeros((B, H, Lmax // C) + ((m, d) if m > 1 else (d,)), np.uint16)
     for b, x in enumerate(xs):
         Kc[b, :, :x["K_cache"].shape[2]] = x["K_cache"][0]
         Vc[b, :, :x["V_cache"].shape[2]] = x["V_cache"][0]
-        Klm[b, :, :x["Klm"].shape[2]] = x["Klm"][0]
+        if m > 1:
+            extra = synth.f32_to_bf16_bits(rng.standard_normal(x["Klm"].shape[1:3] + (m - 1, d), dtype=np.float32))
+            Klm[b, :, :x["Klm"].shape[2]] = np.concatenate([x["Klm"][0][:, :, None], extra], axis=2)
+        else:
+            Klm[b, :, :x["Klm"].shape[2]] = x["Klm"][0]
         if lf:
             oracle_mod.chunk_means(Kc[b:b + 1], C, nchunks=ctxs[b] // C, Klm=Klm[b:b + 1])
     nchunks = [(ctx + steps - 1) // C + 1 for ctx in ctxs]
@@ -654,12 +727,26 @@ def test_paged_decode_equals_contiguous_per_sequence(oracle_mod, lf):
         kn = np.stack([x["k_new"][s][0] for x in xs])
         vn = np.stack([x["v_new"][s][0] for x in xs])
         got = oracle_mod.decode_paged(q, kn, vn, Kp, Vp, Lp, table, pos, C, k, q_ret=qr, landmark_free=lf)
+        # a selection held fixed: every past slot moved to another past chunk where one exists
+        fixed = got["idx"].copy()
+        for b in range(B):
+            c = int(pos[b]) // C
+            for h in range(H):
+                mm = min(k, c)
+                if c > mm:
+                    fixed[b, h, :mm] = np.sort(rng.choice(c, size=mm, replace=False))
+        got_f = oracle_mod.decode_paged(q, kn, vn, Kp, Vp, Lp, table, pos, C, k, q_ret=qr, landmark_free=lf,
+                                        idx=fixed)
         for b in range(B):
             Kb, Vb, Lb = conts[b]
             ref = oracle_mod.decode(q[b:b + 1], kn[b:b + 1], vn[b:b + 1], Kb, Vb, Lb, int(pos[b]), C, k,
                                     q_ret=qr[b:b + 1], landmark_free=lf)
             for key in ("idx", "w", "o"):
                 np.testing.assert_array_equal(got[key][b], ref[key][0])
+            ref_f = oracle_mod.decode(q[b:b + 1], kn[b:b + 1], vn[b:b + 1], Kb, Vb, Lb, int(pos[b]), C, k,
+                                      q_ret=qr[b:b + 1], landmark_free=lf, idx=fixed[b:b + 1])
+            for key in ("idx", "w", "o"):
+                np.testing.assert_array_equal(got_f[key][b], ref_f[key][0])
     # the pools hold what the contiguous caches hold
     for b in range(B):
         for j in range(nchunks[b]):
