@@ -97,3 +97,37 @@ def check_selection(gpu_idx, ora_idx, Q, Klm, C, k, rows=None):
 
 def to_inputs(x, names=("Q", "K", "V", "Klm")):
     return {n: dev(x[n]) for n in names}
+
+
+def check_decode_step(tag, gi, gw, go, ref, rerun, own, past_scores, k, tol=(MAX_ABS, REL_L2), w_tol=2e-5):
+    """One decode step of R rows (flattened (b, h)) against the oracle.
+
+    gi [R, k+1], gw [R, k+1], go [R, d]: the GPU's selection, weights and output.  ``ref``: the oracle's free
+    step (idx [.., k+1]).  ``own[r]``: the open chunk of row r.  ``past_scores(r)``: the oracle-precision fp32
+    scores of row r's past chunks 0..own[r]-1.  Selection: the own slot and the -1 padding are exact, and the
+    past-chunk sets are equal or differ only in chunks whose score lies within GAP of the m-th best.
+    Outputs: o and w of every row against the oracle step with the GPU's selection held fixed
+    (``rerun(gi)``), so rows that differ on a near tie are checked too.  Returns the number of such rows."""
+    R = gi.shape[0]
+    ri = np.asarray(ref["idx"]).reshape(R, k + 1)
+    differ = 0
+    for r in range(R):
+        c = int(own[r])
+        m = min(k, c)
+        assert gi[r, k] == c and np.all(gi[r, m:k] == -1), (tag, r, gi[r])
+        a, b = set(gi[r, :m].tolist()), set(ri[r, :m].tolist())
+        assert len(a) == m, (tag, r, gi[r])
+        if a != b:
+            sc = np.asarray(past_scores(r), np.float32)
+            mth = np.sort(sc)[::-1][m - 1]
+            for j in a ^ b:
+                gap = abs(float(sc[j]) - float(mth))
+                assert gap < GAP, (tag, r, j, gap)
+            differ += 1
+    fixed = rerun(gi)
+    assert_close(go, np.asarray(fixed["o"]).reshape(go.shape), f"o {tag}", *tol)
+    fw = np.asarray(fixed["w"]).reshape(R, k + 1)
+    np.testing.assert_array_equal(np.asarray(fixed["idx"]).reshape(R, k + 1), gi)
+    werr = float(np.max(np.abs(gw - fw)))
+    assert werr < w_tol, (tag, werr)
+    return differ

@@ -5,37 +5,25 @@ import torch
 
 import oracle
 from long_context_landmark_amd import synth
-from gpu_util import GAP, assert_close, dev, f32, host, say
+from gpu_util import GAP, assert_close, check_decode_step, dev, f32, host, say
 
 pytestmark = pytest.mark.gpu
 
 
-def _check_step(s, n, g_idx, g_w, g_o, ref, Klm_h, q_h, k, d, C=64, tol=(2e-2, 1e-2)):
-    """Selection by the gap rule, then o and w against the oracle (with the GPU selection where sets differ)."""
-    B, H = g_idx.shape[:2]
-    c = n // C
-    m = min(k, c)
-    gi = g_idx.reshape(-1, k + 1)
-    oi = ref["idx"].reshape(-1, k + 1)
-    assert np.all(gi[:, k] == c)
-    assert np.all(gi[:, m:k] == -1)
-    differ = []
-    for bh in range(B * H):
-        a, b = set(gi[bh, :m].tolist()), set(oi[bh, :m].tolist())
-        if a != b:
-            qrow = q_h.reshape(B * H, d)[bh].astype(np.float64) if q_h.dtype != np.uint16 else \
-                synth.bf16_bits_to_f32(q_h.reshape(B * H, d)[bh]).astype(np.float64)
-            lm = Klm_h.reshape(B * H, -1, d)[bh]
-            lmf = synth.bf16_bits_to_f32(lm) if lm.dtype == np.uint16 else lm
-            sc = (lmf[:c].astype(np.float64) @ qrow / np.sqrt(d)).astype(np.float32)
-            mth = np.sort(sc)[::-1][m - 1]
-            for j in a ^ b:
-                assert abs(float(sc[j]) - float(mth)) < GAP, (s, bh, j)
-            differ.append(bh)
-    return differ
+def past_scores_fn(q_h, Klm_h, c, d, scale=None):
+    """fp32 scores of row r's past chunks 0..c-1 (double-precision dot products rounded once, as the oracle
+    rounds them); q_h [R, d] and Klm_h [R, N, d] in the generated representation."""
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    q64 = synth.as_f32(q_h).astype(np.float64)
+
+    def f(r):
+        lm = synth.as_f32(Klm_h[r, :c]).astype(np.float64)
+        return (lm @ q64[r] * scale).astype(np.float32)
+
+    return f
 
 
-def _run_decode(hils, x, k, steps, check_every=1, tol=(2e-2, 1e-2)):
+def _run_decode(hils, x, k, steps, tol=(2e-2, 1e-2)):
     B, H, Lmax, d = x["K_cache"].shape
     ctx = x["ctx"]
     Kc_g, Vc_g, Klm_g = dev(x["K_cache"]), dev(x["V_cache"]), dev(x["Klm"])
@@ -45,49 +33,21 @@ def _run_decode(hils, x, k, steps, check_every=1, tol=(2e-2, 1e-2)):
     # optional retrieval queries: they score the landmarks, q keeps the attention
     rq = "q_ret" in x
     qr_all = dev(x["q_ret"]) if rq else None
+    Klm_r = x["Klm"].reshape(B * H, -1, d)
     n_differ = 0
     for s in range(steps):
         n = ctx + s
         o, idx, w = hils.decode_step(q_all[s], k_all[s], v_all[s], Kc_g, Vc_g, Klm_g, n, k, ws=ws,
                                      q_ret=qr_all[s] if rq else None)
-        ref = oracle.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc_h, Vc_h, x["Klm"], n, 64, k,
-                            q_ret=x["q_ret"][s] if rq else None)
-        if s % check_every and s != steps - 1:
-            continue
+        step = lambda sel=None: oracle.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc_h, Vc_h, x["Klm"], n, 64,
+                                              k, q_ret=x["q_ret"][s] if rq else None,
+                                              idx=None if sel is None else sel.reshape(B, H, k + 1))
+        ref = step()
         torch.cuda.synchronize()
-        gi = idx.cpu().numpy()
-        differ = _check_step(s, n, gi, f32(w), f32(o), ref, x["Klm"], x["q_ret" if rq else "q"][s], k, d)
-        ro = ref["o"].reshape(B * H, d).copy()
-        rw = ref["w"].reshape(B * H, k + 1).copy()
-        for bh in differ:
-            n_differ += 1
-            b, h = divmod(bh, H)
-            # oracle forward of this single row with the GPU's selection
-            L = ((n // 64) + 1) * 64
-            Qp = np.zeros((1, 1, L, d), x["q"].dtype)
-            Qp[0, 0, n] = x["q"][s][b, h]
-            Qr = None
-            if rq:
-                Qr = np.zeros_like(Qp)
-                Qr[0, 0, n] = x["q_ret"][s][b, h]
-            Kp = np.ascontiguousarray(Kc_h[b:b + 1, h:h + 1, :L])
-            Vp = np.ascontiguousarray(Vc_h[b:b + 1, h:h + 1, :L])
-            Lp = np.ascontiguousarray(x["Klm"][b:b + 1, h:h + 1, :L // 64])
-            fx = oracle.fwd(Qp, Kp, Vp, Lp, 64, k, rows=[n], idx=gi.reshape(B * H, k + 1)[bh:bh + 1], Q_ret=Qr)
-            ro[bh] = fx["O"][0]
-            rw[bh] = fx["w"][0]
-        assert_close(f32(o).reshape(B * H, d), ro, f"o step {s}", *tol)
-        # weights compared per chunk index
-        gw = f32(w).reshape(B * H, k + 1)
-        gidx = gi.reshape(B * H, k + 1)
-        for bh in range(B * H):
-            if bh in differ:
-                continue
-            gm = {int(j): gw[bh, r] for r, j in enumerate(gidx[bh]) if j >= 0}
-            om = {int(j): rw[bh, r] for r, j in enumerate(ref["idx"].reshape(B * H, k + 1)[bh]) if j >= 0}
-            assert gm.keys() == om.keys()
-            for j in gm:
-                assert abs(gm[j] - om[j]) < 1e-5
+        gi = idx.cpu().numpy().reshape(B * H, k + 1)
+        qs = x["q_ret" if rq else "q"][s].reshape(B * H, d)
+        n_differ += check_decode_step(f"step {s}", gi, f32(w).reshape(B * H, k + 1), f32(o).reshape(B * H, d), ref,
+                                      step, [n // 64] * (B * H), past_scores_fn(qs, Klm_r, n // 64, d), k, tol)
     # the caches were appended identically
     np.testing.assert_array_equal(host(Kc_g), Kc_h)
     np.testing.assert_array_equal(host(Vc_g), Vc_h)
@@ -123,30 +83,47 @@ def test_decode_steps_retrieval_query(hils, gpu, dtype, B, H, d, ctx, steps, k):
 
 
 def test_decode_equals_prefill_rows(hils, gpu):
-    """A decode step at position n gives the prefill output of row n on the same tensors."""
-    B, H, d, k = 1, 2, 64, 8
+    """A decode step at position n gives the prefill output of row n on the same tensors: equal past-chunk
+    sets (or sets that differ only on near ties of the oracle's scores) and, where the sets are equal, equal
+    outputs within the parity bar."""
+    B, H, d, k = 1, 4, 64, 8
     L = 64 * 50
     x = synth.prefill_inputs(B, H, L, d, C=64, seed=77, dtype="bf16", klm="chunkmean")
     Q, K, V, Klm = (dev(x[n]) for n in ("Q", "K", "V", "Klm"))
     O, idx, _, _, _ = hils.sparse_attn_fwd(Q, K, V, Klm, k)
     ws = torch.empty(hils.workspace_size(hils.OP_DECODE, B, H, L, d, 64, k), dtype=torch.uint8, device="cuda:0")
     Kc, Vc = K.clone(), V.clone()
-    for n in (0, 1, 63, 64, 100, 640, L - 1):
+    differ = 0
+    for n in (0, 1, 63, 64, 100, 640, 1000, 2047, 2048, L - 65, L - 1):
         o, di, dw = hils.decode_step(Q[:, :, n].contiguous(), K[:, :, n].contiguous(), V[:, :, n].contiguous(), Kc, Vc,
                                      Klm, n, k, ws=ws)
         torch.cuda.synchronize()
-        a = np.sort(idx[:, :, n].cpu().numpy(), -1)
-        b = np.sort(di.cpu().numpy(), -1)
-        same = np.all(a == b, -1).reshape(-1)
-        assert same.mean() >= 0.5
+        c = n // 64
+        m = min(k, c)
+        a = idx[:, :, n].cpu().numpy().reshape(B * H, k + 1)
+        b = di.cpu().numpy().reshape(B * H, k + 1)
+        assert np.all(a[:, k] == c) and np.all(b[:, k] == c)
+        rows = np.arange(B * H) * L + n
         go, po = f32(o).reshape(-1, d), f32(O[:, :, n]).reshape(-1, d)
-        assert np.max(np.abs(go[same] - po[same])) < 2e-2
+        for r in range(B * H):
+            sa, sb = set(a[r, :m].tolist()), set(b[r, :m].tolist())
+            assert len(sa) == m and len(sb) == m
+            if sa != sb:
+                S = oracle.landmark_scores_rows(x["Q"], x["Klm"], 64, rows[r:r + 1])[0, :c].astype(np.float32)
+                mth = np.sort(S)[::-1][m - 1]
+                for j in sa ^ sb:
+                    assert abs(float(S[j]) - float(mth)) < GAP, (n, r, j)
+                differ += 1
+            else:
+                assert np.max(np.abs(go[r] - po[r])) < 2e-2, (n, r)
+    say(f"  rows whose decode and prefill sets differ on near ties: {differ}")
 
 
 @pytest.mark.timeout(600)
 def test_workload_decode_512k(hils, gpu):
     """The 512K decode workload (B=1 H=16 d=64, 524288 cached tokens, k=16, one needle chunk per head):
-    256 appended steps, each checked against the oracle; every step keeps the needle chunk."""
+    256 appended steps, every step checked against the oracle (selection by the gap rule, o and w with the
+    GPU's selection held fixed, max-abs and rel-L2); every step keeps the needle chunk."""
     w = synth.WORKLOADS["decode_512k"]
     say(f"workload {w.name}: generating")
     x = synth.workload_inputs(w)
@@ -156,21 +133,29 @@ def test_workload_decode_512k(hils, gpu):
     Kc_h, Vc_h = x["K_cache"], x["V_cache"]
     ws = torch.empty(hils.workspace_size(hils.OP_DECODE, B, H, Lmax, d, 64, w.k), dtype=torch.uint8, device="cuda:0")
     q_all, k_all, v_all = dev(x["q"]), dev(x["k_new"]), dev(x["v_new"])
+    Klm_r = x["Klm"].reshape(B * H, -1, d)
     differ_total = 0
     for s in range(w.steps):
         n = w.L + s
         o, idx, wt = hils.decode_step(q_all[s], k_all[s], v_all[s], Kc_g, Vc_g, Klm_g, n, w.k, ws=ws)
-        ref = oracle.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc_h, Vc_h, x["Klm"], n, 64, w.k)
-        gi = idx.cpu().numpy()
-        differ = _check_step(s, n, gi, f32(wt), f32(o), ref, x["Klm"], x["q"][s], w.k, d)
-        differ_total += len(differ)
-        keep = np.ones(B * H, bool)
-        keep[differ] = False
-        assert_close(f32(o).reshape(B * H, d)[keep], ref["o"].reshape(B * H, d)[keep], f"o step {s}") if s % 32 == 0 \
-            else None
-        go = f32(o).reshape(B * H, d)[keep]
-        ma = np.max(np.abs(go - ref["o"].reshape(B * H, d)[keep]))
-        assert ma < 2e-2, (s, ma)
+        step = lambda sel=None: oracle.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc_h, Vc_h, x["Klm"], n, 64,
+                                              w.k, idx=None if sel is None else sel.reshape(B, H, w.k + 1))
+        ref = step()
+        gi = idx.cpu().numpy().reshape(B * H, w.k + 1)
+        differ_total += check_decode_step(f"step {s}", gi, f32(wt).reshape(B * H, w.k + 1),
+                                          f32(o).reshape(B * H, d), ref, step, [n // 64] * (B * H),
+                                          past_scores_fn(x["q"][s].reshape(B * H, d), Klm_r, n // 64, d), w.k)
         for h in range(H):
-            assert int(x["needle_chunk"][0, h]) in gi[0, h, :w.k].tolist(), (s, h)
+            assert int(x["needle_chunk"][0, h]) in gi[h, :w.k].tolist(), (s, h)
     say(f"  rows with near-tie selection differences over all steps: {differ_total}")
+
+
+@pytest.mark.parametrize("ctx,d,k", [
+    (64 * 9000 + 17, 64, 16),    # 36 scan slices: lists beyond the 32nd lane of the merge
+    (64 * 16383 + 40, 64, 8),    # 64 scan slices: the library's largest context
+])
+def test_decode_many_slices(hils, gpu, ctx, d, k):
+    """Contexts above 512K tokens, up to the 16384-chunk limit: more than 32 slice lists per head."""
+    say(f"decode many slices ctx={ctx} d={d} k={k} slices={(ctx // 64 + 255) // 256}")
+    x = synth.decode_inputs(1, 2, d, ctx, 3, C=64, seed=ctx % 1000, dtype="bf16")
+    _run_decode(hils, x, k, 3)

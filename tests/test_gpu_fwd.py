@@ -205,3 +205,29 @@ def test_workload_prefill_128k_sampled(hils, gpu):
         ro[bad] = oracle.fwd(Qh, Kh, Vh, Lh, 64, w.k, rows=rows[bad], idx=gi[bad])["O"]
     go = f32(O[:, heads]).reshape(-1, w.d)[rows]
     assert_close(go, ro, "O (sampled)")
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("N,d,k", [(2304, 64, 8), (4100, 128, 16)])
+def test_fwd_beyond_2048_chunks_sampled(hils, gpu, N, d, k):
+    """More than 2048 chunks per sequence (the routing's one-wavefront scatter, long top-k candidate lists):
+    sampled rows including chunk boundaries against the oracle, and two runs bitwise equal."""
+    B, H, L = 1, 1, 64 * N
+    say(f"long prefill B={B} H={H} L={L} d={d} k={k} (N={N})")
+    x = _inputs(B, H, L, d, k, seed=N + d, klm="chunkmean")
+    t = to_inputs(x)
+    outs = [hils.sparse_attn_fwd(t["Q"], t["K"], t["V"], t["Klm"], k, save_for_backward=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+    O, idx = outs[0][0], outs[0][1]
+    rng = np.random.default_rng(N)
+    rows = np.unique(np.concatenate([rng.integers(0, L, 1500), np.arange(63, L, 64 * 101), [0, 64, 65, L - 64, L - 1],
+                                     np.arange(2048 * 64, L, 64 * 37)]))
+    ref = oracle.fwd(x["Q"], x["K"], x["V"], x["Klm"], 64, k, rows=rows)
+    gi = idx.cpu().numpy().reshape(-1, k + 1)[rows]
+    bad = check_selection(gi, ref["idx"], x["Q"], x["Klm"], 64, k, rows=rows)
+    ro = ref["O"].copy()
+    if len(bad):
+        ro[bad] = oracle.fwd(x["Q"], x["K"], x["V"], x["Klm"], 64, k, rows=rows[bad], idx=gi[bad])["O"]
+    assert_close(f32(O).reshape(-1, d)[rows], ro, "O (sampled)")

@@ -10,8 +10,8 @@ import torch
 
 import oracle
 from long_context_landmark_amd import synth
-from gpu_util import assert_close, check_selection, dev, f32, host, say, to_inputs
-from test_gpu_decode import _check_step
+from gpu_util import assert_close, check_decode_step, check_selection, dev, f32, host, say, to_inputs
+from test_gpu_decode import past_scores_fn
 
 pytestmark = pytest.mark.gpu
 
@@ -109,21 +109,15 @@ def test_decode_landmark_free(hils, gpu, dtype, B, H, d, ctx, steps, k, rq):
         n = ctx + s
         o, idx, w = hils.decode_step(q_all[s], k_all[s], v_all[s], Kc_g, Vc_g, Klm_g, n, k, ws=ws,
                                      q_ret=qr_all[s] if rq else None, landmark_free=True)
-        ref = oracle.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc_h, Vc_h, Klm_h, n, 64, k,
-                            q_ret=x["q_ret"][s] if rq else None, landmark_free=True)
+        step = lambda sel=None: oracle.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc_h, Vc_h, Klm_h, n, 64, k,
+                                              q_ret=x["q_ret"][s] if rq else None, landmark_free=True,
+                                              idx=None if sel is None else sel.reshape(B, H, k + 1))
+        ref = step()
         torch.cuda.synchronize()
-        gi = idx.cpu().numpy()
-        differ = _check_step(s, n, gi, f32(w), f32(o), ref, Klm_h, x["q_ret" if rq else "q"][s], k, d)
-        keep = [bh for bh in range(B * H) if bh not in differ]
-        assert_close(f32(o).reshape(B * H, d)[keep], ref["o"].reshape(B * H, d)[keep], f"o step {s}", *tol)
-        gw, rw = f32(w).reshape(B * H, k + 1), ref["w"].reshape(B * H, k + 1)
-        gx, rx = gi.reshape(B * H, k + 1), ref["idx"].reshape(B * H, k + 1)
-        for bh in keep:
-            gm = {int(j): gw[bh, r] for r, j in enumerate(gx[bh]) if j >= 0}
-            om = {int(j): rw[bh, r] for r, j in enumerate(rx[bh]) if j >= 0}
-            assert gm.keys() == om.keys()
-            for j in gm:
-                assert abs(gm[j] - om[j]) < 2e-5
+        gi = idx.cpu().numpy().reshape(B * H, k + 1)
+        qs = x["q_ret" if rq else "q"][s].reshape(B * H, d)
+        check_decode_step(f"step {s}", gi, f32(w).reshape(B * H, k + 1), f32(o).reshape(B * H, d), ref, step,
+                          [n // 64] * (B * H), past_scores_fn(qs, Klm_h.reshape(B * H, -1, d), n // 64, d), k, tol)
     np.testing.assert_array_equal(host(Kc_g), Kc_h)
     # the landmark rows the steps maintained
     last = (ctx + steps - 1) // 64

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from long_context_landmark_amd import synth
-from gpu_util import GAP, assert_close, dev, f32, say, to_inputs
+from gpu_util import GAP, assert_close, check_decode_step, dev, f32, say, to_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -156,29 +156,16 @@ def test_decode_multi_landmark(hils, gpu, dtype, H, d, ctx, steps, k, m):
         n = ctx + s
         o, idx, w = hils.decode_step(dev(x["q"][s]), dev(x["k_new"][s]), dev(x["v_new"][s]), Kc_g, Vc_g, lm_g, n, k,
                                      ws=ws)
-        ref = oracle.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc_h, Vc_h, lm, n, 64, k)
+        step = lambda sel=None: oracle.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc_h, Vc_h, lm, n, 64, k,
+                                              idx=None if sel is None else sel.reshape(B, H, k + 1))
+        ref = step()
         torch.cuda.synchronize()
         c = n // 64
-        mm = min(k, c)
-        gi, ri = idx.cpu().numpy().reshape(H, k + 1), ref["idx"].reshape(H, k + 1)
-        go, ro = f32(o).reshape(H, d), ref["o"].reshape(H, d)
-        gw, rw = f32(w).reshape(H, k + 1), ref["w"].reshape(H, k + 1)
-        keep = []
-        for h in range(H):
-            assert gi[h, k] == c and np.all(gi[h, mm:k] == -1)
-            a, b = set(gi[h, :mm].tolist()), set(ri[h, :mm].tolist())
-            if a != b:
-                q = synth.as_f32(x["q"][s][0, h]).astype(np.float64)
-                sc_r = lmf[h, :c] @ q / np.sqrt(d)
-                sc = (np.log(np.exp(sc_r - sc_r.max(1, keepdims=True)).sum(1)) + sc_r.max(1)).astype(np.float32)
-                mth = np.sort(sc)[::-1][mm - 1]
-                for j in a ^ b:
-                    assert abs(float(sc[j]) - float(mth)) < GAP, (s, h, j)
-                continue
-            keep.append(h)
-            gm = {int(j): gw[h, r] for r, j in enumerate(gi[h]) if j >= 0}
-            om = {int(j): rw[h, r] for r, j in enumerate(ri[h]) if j >= 0}
-            assert gm.keys() == om.keys()
-            for j in gm:
-                assert abs(gm[j] - om[j]) < 2e-5
-        assert_close(go[keep], ro[keep], f"o step {s}", *tol)
+
+        def past(h, s=s, c=c):
+            q = synth.as_f32(x["q"][s][0, h]).astype(np.float64)
+            sc_r = lmf[h, :c] @ q / np.sqrt(d)
+            return (np.log(np.exp(sc_r - sc_r.max(1, keepdims=True)).sum(1)) + sc_r.max(1)).astype(np.float32)
+
+        check_decode_step(f"step {s}", idx.cpu().numpy().reshape(H, k + 1), f32(w).reshape(H, k + 1),
+                          f32(o).reshape(H, d), ref, step, [c] * H, past, k, tol)

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from long_context_landmark_amd import synth
-from gpu_util import GAP, assert_close, dev, f32, host, say
+from gpu_util import assert_close, check_decode_step, dev, f32, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -71,37 +71,23 @@ def test_decode_paged(hils, gpu, dtype, H, d, ctxs, steps, k, lf, rq):
         o, idx, w = hils.decode_step_paged(dev(q), dev(kn), dev(vn), Kp_g, Vp_g, Lp_g, table_g,
                                            torch.from_numpy(pos).to(gpu), int(pos.max()), k,
                                            q_ret=dev(qr) if rq else None, landmark_free=lf, ws=ws)
-        ref = oracle.decode_paged(q, kn, vn, Kp, Vp, Lp, table, pos, 64, k, q_ret=qr, landmark_free=lf)
+        step = lambda sel=None: oracle.decode_paged(q, kn, vn, Kp, Vp, Lp, table, pos, 64, k, q_ret=qr,
+                                                    landmark_free=lf,
+                                                    idx=None if sel is None else sel.reshape(B, H, k + 1))
+        ref = step()
         torch.cuda.synchronize()
-        gi = idx.cpu().numpy().reshape(B * H, k + 1)
-        ri = ref["idx"].reshape(B * H, k + 1)
-        go, ro = f32(o).reshape(B * H, d), ref["o"].reshape(B * H, d)
-        gw, rw = f32(w).reshape(B * H, k + 1), ref["w"].reshape(B * H, k + 1)
-        keep = []
-        for bh in range(B * H):
+        own = [int(pos[bh // H]) // 64 for bh in range(B * H)]
+
+        def past(bh, q=q, qr=qr, own=own):
             b, h = divmod(bh, H)
-            c = int(pos[b]) // 64
-            m = min(k, c)
-            assert gi[bh, k] == c and np.all(gi[bh, m:k] == -1)
-            gs, rs = set(gi[bh, :m].tolist()), set(ri[bh, :m].tolist())
-            if gs != rs:
-                # allowed only on a near tie of the oracle's scores
-                qs = (qr if rq else q)[b, h]
-                qf = synth.as_f32(qs).astype(np.float64)
-                lm = synth.as_f32(np.stack([Lp[table[b, j], h] for j in range(c)])).astype(np.float64)
-                sc = (lm @ qf / np.sqrt(d)).astype(np.float32)
-                mth = np.sort(sc)[::-1][m - 1]
-                for j in gs ^ rs:
-                    assert abs(float(sc[j]) - float(mth)) < GAP, (s, bh, j)
-                near += 1
-                continue
-            keep.append(bh)
-            gm = {int(j): gw[bh, r] for r, j in enumerate(gi[bh]) if j >= 0}
-            om = {int(j): rw[bh, r] for r, j in enumerate(ri[bh]) if j >= 0}
-            assert gm.keys() == om.keys()
-            for j in gm:
-                assert abs(gm[j] - om[j]) < 2e-5
-        assert_close(go[keep], ro[keep], f"o step {s}", *tol)
+            c = own[bh]
+            qf = synth.as_f32((qr if rq else q)[b, h]).astype(np.float64)
+            lm = synth.as_f32(np.stack([Lp[table[b, j], h] for j in range(c)])).astype(np.float64)
+            return (lm @ qf / np.sqrt(d)).astype(np.float32)
+
+        near += check_decode_step(f"step {s}", idx.cpu().numpy().reshape(B * H, k + 1),
+                                  f32(w).reshape(B * H, k + 1), f32(o).reshape(B * H, d), ref, step, own, past, k,
+                                  tol)
     say(f"  rows with near-tie selection differences: {near}")
     np.testing.assert_array_equal(host(Kp_g), Kp)
     np.testing.assert_array_equal(host(Vp_g), Vp)
