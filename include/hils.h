@@ -319,6 +319,28 @@ hils_status hils_decode_step_paged(const void* q, const void* q_ret, const void*
                                    size_t ws_bytes, void* stream);
 
 /*
+ * Decode step that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and kernels as
+ * hils_decode_step without ws / ws_bytes: the step's scratch (per-slice
+ * candidate lists and split-K partial outputs, HILS_DECODE_NOALLOC_SCRATCH_BYTES
+ * bytes) is a fixed device array of the library, one per GPU, held until the
+ * process ends.  Its device address is looked up on the first call on each
+ * device (call it once outside graph capture).  B*H is limited to what the
+ * array holds (682 at d = 128, 819 at d = 64); larger batches return
+ * HILS_ERR_UNSUPPORTED before any HIP call.  Nothing in the array must start
+ * at zero; every call rewrites what it reads.  Every call on one GPU shares
+ * that GPU's array, which keeps the last call's contents: calls that overlap
+ * on one GPU (concurrent streams, or host threads) race and must be
+ * serialised by the caller.  Never calls hipMalloc or hipFree.
+ */
+#define HILS_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+hils_status hils_decode_step_noalloc(const void* q, const void* k_new, const void* v_new, void* K_cache,
+                                     void* V_cache, const void* K_lm_cache, int64_t n_ctx, int64_t L_max, void* o,
+                                     int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C,
+                                     int64_t topk, float scale, hils_dtype dt, void* stream);
+
+/*
  * Optional per-kernel timing, for measurement only (off by default; not a
  * step of the method).  While enabled, every kernel an entry point launches is
  * bracketed by a pair of HIP events recorded on the caller's stream, which

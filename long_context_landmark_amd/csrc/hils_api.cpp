@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "hils_launch.h"
 
@@ -161,7 +162,8 @@ static hils_status fwd_impl(const void* Q, const void* Q_ret, const void* K, con
 static hils_status decode_impl(const void* q, const void* q_ret, const void* k_new, const void* v_new, void* K_cache,
                                void* V_cache, const void* K_lm_cache, bool lf, int64_t mlm, int64_t n_ctx, int64_t L_max, void* o,
                                int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C, int64_t topk,
-                               float scale, hils_dtype dt, void* ws, size_t ws_bytes, void* stream);
+                               float scale, hils_dtype dt, void* ws, size_t ws_bytes, void* stream,
+                               bool validate_only = false);
 static hils_status bwd_impl(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm, bool lf,
                             int64_t mlm, const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
                             float* dQ_ret, float* dK, float* dV, float* dK_lm, int64_t B, int64_t H, int64_t L,
@@ -400,7 +402,8 @@ hils_status hils_decode_step_ml(const void* q, const void* q_ret, const void* k_
 static hils_status decode_impl(const void* q, const void* q_ret, const void* k_new, const void* v_new, void* K_cache,
                                void* V_cache, const void* K_lm_cache, bool lf, int64_t mlm, int64_t n_ctx, int64_t L_max, void* o,
                                int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C, int64_t topk,
-                               float scale, hils_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+                               float scale, hils_dtype dt, void* ws, size_t ws_bytes, void* stream,
+                               bool validate_only) {
   Dims D;
   hils_status st;
   if (L_max < 1) return fail(HILS_ERR_INVALID_ARG, "L_max must be >= 1 (got %lld)", (long long)L_max);
@@ -421,6 +424,7 @@ static hils_status decode_impl(const void* q, const void* q_ret, const void* k_n
   REQUIRE_PTR(idx);
   REQUIRE_PTR(w);
   if (!(scale > 0.f)) return fail(HILS_ERR_INVALID_ARG, "scale must be positive");
+  if (validate_only) return HILS_OK;
   hils::DecodeBufs W;
   const size_t need = carve_decode(nullptr, B * H, L_max, d, topk, &W);
   if ((st = check_ws(ws, ws_bytes, need)) != HILS_OK) return st;
@@ -551,6 +555,70 @@ hils_status hils_decode_step_paged(const void* q, const void* q_ret, const void*
                                               n_ctx_max, (int)B, (int)H, o, idx, w, (int)topk, scale, W,
                                               (hipStream_t)stream),
                     "hils_decode_step_paged");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// Decode step without a caller workspace: the step's scratch (the per-slice candidate lists and
+// the split-K partial outputs) lives in a file-scope device array of fixed size, one copy per GPU,
+// held until the process ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: its device address is looked up once per device (with that device current) and only
+// that address is ever handed to kernels.
+namespace {
+constexpr size_t NOALLOC_SCRATCH_BYTES = HILS_DECODE_NOALLOC_SCRATCH_BYTES;
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[NOALLOC_MAX_DEVICES] = {};
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+// Device address of this device's scratch array (looked up on the first call on the device).
+static hils_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hils_decode_step_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+    return fail(HILS_ERR_UNSUPPORTED, "hils_decode_step_noalloc: device ordinal %d above %d", dev,
+                NOALLOC_MAX_DEVICES - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hils_decode_step_noalloc: hipGetSymbolAddress");
+    if (!ptr || ((uintptr_t)ptr & 255u))
+      return fail(HILS_ERR_HIP, "hils_decode_step_noalloc: scratch array has no usable device address");
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return HILS_OK;
+}
+
+extern "C" {
+
+hils_status hils_decode_step_noalloc(const void* q, const void* k_new, const void* v_new, void* K_cache,
+                                     void* V_cache, const void* K_lm_cache, int64_t n_ctx, int64_t L_max, void* o,
+                                     int32_t* idx, float* w, int64_t B, int64_t H, int64_t d, int64_t C,
+                                     int64_t topk, float scale, hils_dtype dt, void* stream) {
+  // the workspace the plain step would need must fit the scratch array; checked before any HIP call
+  if (B >= 1 && H >= 1 && B * H <= (int64_t(1) << 30) && (d == 64 || d == 128)) {
+    hils::DecodeBufs W;
+    const size_t need = carve_decode(nullptr, B * H, L_max, d, topk, &W);
+    if (need > NOALLOC_SCRATCH_BYTES)
+      return fail(HILS_ERR_UNSUPPORTED,
+                  "hils_decode_step_noalloc: B*H = %lld needs %zu bytes of scratch, above the fixed %zu bytes; "
+                  "use hils_decode_step with a workspace",
+                  (long long)(B * H), need, NOALLOC_SCRATCH_BYTES);
+  }
+  // argument checks of the plain step (null workspace pointers: it would reject a real workspace need)
+  hils_status st = decode_impl(q, nullptr, k_new, v_new, K_cache, V_cache, K_lm_cache, false, 1, n_ctx, L_max, o,
+                               idx, w, B, H, d, C, topk, scale, dt, nullptr, 0, nullptr, /*validate_only=*/true);
+  if (st != HILS_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != HILS_OK) return st;
+  return decode_impl(q, nullptr, k_new, v_new, K_cache, V_cache, K_lm_cache, false, 1, n_ctx, L_max, o, idx, w, B, H,
+                     d, C, topk, scale, dt, ws, NOALLOC_SCRATCH_BYTES, stream, false);
 }
 
 }  // extern "C"

@@ -49,6 +49,7 @@ _lib.hils_sparse_attn_fwd_ml.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64] + _lib.h
 _lib.hils_sparse_attn_bwd_ml.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64] + _lib.hils_sparse_attn_bwd_rq.argtypes[5:]
 _lib.hils_decode_step_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _int, _vp, _vp,
                                         _vp, _i64, _i64, _i64, _i64, _i64, _f, _int, _vp, _sz, _vp]
+_lib.hils_decode_step_noalloc.argtypes = _lib.hils_decode_step.argtypes[:-3] + [_vp]
 _lib.hils_profile_enable.argtypes = [_int]
 _lib.hils_profile_enable.restype = None
 _lib.hils_profile_read.argtypes = [ctypes.c_char_p, _int, ctypes.POINTER(ctypes.c_double),
@@ -284,6 +285,22 @@ def decode_step(q, k_new, v_new, K_cache, V_cache, K_lm_cache, n_ctx, k, C=64, s
         _check(_lib.hils_decode_step(_p(q), *args))
     else:
         _check(_lib.hils_decode_step_rq(_p(q), _p(q_ret), *args))
+    return o, idx, w
+
+
+def decode_step_noalloc(q, k_new, v_new, K_cache, V_cache, K_lm_cache, n_ctx, k, C=64, scale=None, out=None,
+                        idx=None, w=None):
+    """As ``decode_step`` (one landmark per chunk, no retrieval query), without a workspace: the library's
+    fixed per-device scratch array holds the step's temporaries (calls on one GPU must not overlap)."""
+    _contig(q, k_new, v_new, K_cache, V_cache, K_lm_cache)
+    B, H, d = q.shape
+    L_max = K_cache.shape[2]
+    o = out if out is not None else torch.empty_like(q)
+    idx = idx if idx is not None else torch.empty((B, H, k + 1), dtype=torch.int32, device=q.device)
+    w = w if w is not None else torch.empty((B, H, k + 1), dtype=torch.float32, device=q.device)
+    _check(_lib.hils_decode_step_noalloc(_p(q), _p(k_new), _p(v_new), _p(K_cache), _p(V_cache), _p(K_lm_cache),
+                                         n_ctx, L_max, _p(o), _p(idx), _p(w), B, H, d, C, k, _scale(d, scale),
+                                         _dt(q), _stream()))
     return o, idx, w
 
 

@@ -189,3 +189,17 @@ def test_multi_landmark_decode_validates(lib, hils):
     for m in (0, 17):
         assert lib.hils_decode_step_ml(FAKE, None, *([FAKE] * 5), m, 100, 1024, FAKE, FAKE, FAKE, 1, 2, 64, 64, 4,
                                        0.125, 0, FAKE, nd, None) == UNSUPPORTED
+
+
+def test_noalloc_decode_validation(lib):
+    """The no-allocation decode step rejects, before any HIP call, batches whose scratch exceeds the fixed
+    array and the argument errors of the workspace step."""
+    args = [FAKE] * 6 + [100, 1024] + [FAKE] * 3
+    assert lib.hils_decode_step_noalloc(*args, 1, 700, 128, 64, 8, ctypes.c_float(0.125), 0, None) == UNSUPPORTED
+    assert "scratch" in lib.hils_last_error().decode()
+    assert lib.hils_decode_step_noalloc(*args, 1, 2, 96, 64, 8, ctypes.c_float(0.125), 0, None) == UNSUPPORTED
+    assert lib.hils_decode_step_noalloc(*[FAKE] * 6, 2000, 1024, *[FAKE] * 3, 1, 2, 64, 64, 8,
+                                        ctypes.c_float(0.125), 0, None) == INVALID
+    assert "n_ctx" in lib.hils_last_error().decode()
+    assert lib.hils_decode_step_noalloc(*[FAKE] * 5, None, 100, 1024, *[FAKE] * 3, 1, 2, 64, 64, 8,
+                                        ctypes.c_float(0.125), 0, None) == INVALID
