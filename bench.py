@@ -74,6 +74,12 @@ def measured_traffic(workload, kernel):
 
 
 # ----------------------------------------------------------------------------- algorithmic work
+# Per kernel: (bound, algorithmic FLOPs, algorithmic bytes, design bytes).  "Algorithmic" is the method's own
+# work: the landmark dot products (2d per causal (query, chunk) score), the attention inside each kept chunk
+# (4 C d per (query, kept chunk) pair; causal for the own chunk) and reading Q, K, V, landmarks and writing O
+# once.  "Design bytes" is this implementation's traffic model of the kernel (per-pair query gathers and
+# partial-output round trips of the chunk-major schedule), reported beside the measured counter bytes; it is
+# never used as achieved work.  Contractions are priced against bf16 MFMA, the rest against HBM.
 
 
 def prefill_work(B, H, L, d, k, C=64):
@@ -90,20 +96,22 @@ def prefill_work(B, H, L, d, k, C=64):
         "flops": f_topk + f_chunk + f_own,
         "bytes": io,
         "kernels": {
-            # name: (bound, algorithmic flops, algorithmic bytes)
-            "topk_select": ("mfma", f_topk, BH * (L * d * 2 + N * d * 2 + L * k1 * 12)),
-            "chunk_attn_fwd": ("hbm", f_chunk, pairs * (2 * d + 2 * d + 8) + BH * N * C * d * 4),
-            "own_combine": ("hbm", f_own, BH * L * (3 * d * 2 + d * 2 + k1 * 8) + pairs * 2 * d),
-            "route_count": ("hbm", 0, BH * L * k * 4),
-            "route_scan": ("hbm", 0, BH * 2 * N * 4 * max(1, L // 1024)),
-            "route_scatter": ("hbm", 0, BH * L * k * 8),
+            # name: (bound, algorithmic flops, algorithmic bytes, design bytes)
+            "topk_select": ("mfma", f_topk, BH * (L * d * 2 + N * d * 2), BH * (L * d * 2 + N * d * 2 + L * k1 * 12)),
+            "chunk_attn_fwd": ("mfma", f_chunk, BH * L * d * 2 * 2,
+                               pairs * (2 * d + 2 * d + 8) + BH * N * C * d * 4),
+            "own_combine": ("hbm", f_own, BH * L * 4 * d * 2, BH * L * (3 * d * 2 + d * 2 + k1 * 8) + pairs * 2 * d),
+            "route_count": ("hbm", 0, BH * L * k * 4, BH * L * k * 4),
+            "route_scan": ("hbm", 0, BH * 2 * N * 4 * max(1, L // 1024), BH * 2 * N * 4 * max(1, L // 1024)),
+            "route_scatter": ("hbm", 0, BH * L * k * 8, BH * L * k * 8),
             # landmark-free chunks only
-            "chunk_mean": ("hbm", 0, BH * (L * d * 2 + N * d * 2)),
-            "lf_own": ("hbm", BH * L * 2 * d, BH * L * (2 * d * 2 + k1 * 12)),
+            "chunk_mean": ("hbm", 0, BH * (L * d * 2 + N * d * 2), BH * (L * d * 2 + N * d * 2)),
+            "lf_own": ("hbm", BH * L * 2 * d, BH * L * 2 * d * 2, BH * L * (2 * d * 2 + k1 * 12)),
             # two landmarks per chunk only: causal (query, chunk, landmark) dot products on MFMA, the
             # chunk scores written once and read back by the selection
-            "ml_scores": ("mfma", BH * C * (N * (N + 1) // 2) * 2 * 2 * d, BH * (L * d * 2 + C * (N * (N + 1) // 2) * 4)),
-            "ml_select": ("hbm", 0, BH * (C * (N * (N + 1) // 2) * 4 + L * k1 * 12)),
+            "ml_scores": ("mfma", BH * C * (N * (N + 1) // 2) * 2 * 2 * d, BH * (L * d * 2 + N * 2 * d * 2),
+                          BH * (L * d * 2 + C * (N * (N + 1) // 2) * 4)),
+            "ml_select": ("hbm", 0, BH * L * k1 * 12, BH * (C * (N * (N + 1) // 2) * 4 + L * k1 * 12)),
         },
     }
 
@@ -118,7 +126,8 @@ def decode_work(B, H, d, n, k, C=64):
     return {
         "bytes": b_scan + b_attn + BH * d * 2 * 5,
         "flops": BH * (2 * d * (c + 1) + 4 * d * (m * C + own)),
-        "kernels": {"decode_scan": ("hbm", BH * 2 * d * c, b_scan), "decode_attend": ("hbm", 0, b_attn)},
+        "kernels": {"decode_scan": ("hbm", BH * 2 * d * c, b_scan, b_scan),
+                    "decode_attend": ("hbm", BH * 4 * d * (m * C + own), b_attn, b_attn + BH * 64 * 16 * 8)},
     }
 
 
@@ -127,40 +136,56 @@ def train_work(B, H, L, d, k, C=64):
     BH, N = B * H, L // C
     pairs_all = fw["pairs"] + BH * L
     f_bwd = (fw["pairs"] * 10 * C * d) + BH * N * 10 * d * (C * (C + 1) // 2)
-    b_bwd = pairs_all * (2 * d * 2 + 4 * d + 12) + BH * L * (3 * d * 2 + 4 * d * 4) + BH * N * C * d * 2 * 2
+    b_bwd = BH * L * (4 * d * 2 + 3 * d * 4) + BH * N * d * (2 + 4)  # Q, K, V, dO read; dQ, dK, dV, dKlm written
     kern = dict(fw["kernels"])
-    kern["chunk_bwd"] = ("hbm", f_bwd, pairs_all * (2 * d * 2 + 4 * d + 12) + BH * N * C * d * (2 * 2 + 4 * 2))
-    kern["dq_reduce"] = ("hbm", 0, pairs_all * (4 * d + 2 * d + 12) + BH * L * d * 4)
-    kern["klm_bwd"] = ("hbm", 0, pairs_all * (2 * d + 8) + BH * N * d * 4)
+    kern["chunk_bwd"] = ("mfma", f_bwd, BH * L * (4 * d * 2 + 2 * d * 4),
+                         pairs_all * (2 * d * 2 + 4 * d + 12) + BH * N * C * d * (2 * 2 + 4 * 2))
+    kern["dq_reduce"] = ("hbm", 0, BH * L * d * 4, pairs_all * (4 * d + 2 * d + 12) + BH * L * d * 4)
+    kern["klm_bwd"] = ("hbm", 0, BH * N * d * 4, pairs_all * (2 * d + 8) + BH * N * d * 4)
     # landmark-free chunks only: q and k read, dQ and dK read and written, per row
-    kern["lf_bwd"] = ("hbm", 0, BH * L * (2 * d * 2 + 4 + 4 * d * 4) + BH * N * d * 4)
+    kern["lf_bwd"] = ("hbm", 0, BH * L * 2 * d * 2, BH * L * (2 * d * 2 + 4 + 4 * d * 4) + BH * N * d * 4)
     # two landmarks per chunk only: per pair q and two landmark rows read, dKlm and dQ written
-    kern["ml_klm_bwd"] = ("hbm", 0, pairs_all * (2 * d + 4) + BH * N * 2 * d * (2 + 4))
-    kern["ml_dq"] = ("hbm", 0, BH * L * (2 * d + (k + 1) * (8 + 2 * 2 * d) + 2 * 4 * d))
+    kern["ml_klm_bwd"] = ("hbm", 0, BH * N * 2 * d * 4, pairs_all * (2 * d + 4) + BH * N * 2 * d * (2 + 4))
+    kern["ml_dq"] = ("hbm", 0, BH * L * d * 4, BH * L * (2 * d + (k + 1) * (8 + 2 * 2 * d) + 2 * 4 * d))
     return {"flops": fw["flops"] + f_bwd, "bytes": fw["bytes"] + b_bwd, "kernels": kern}
 
 
 def roofline(kernels_ms, work, launches_per_step, workload=None):
-    """Roofline of the kernel with the largest time per step."""
+    """Roofline of the kernel with the largest time per step.
+
+    achieved = the kernel's algorithmic FLOPs (contractions, against bf16 MFMA) or bytes (against HBM) per
+    launch over its average launch time from HIP events on the launching stream; traffic = HBM bytes per
+    launch from the recorded FETCH_SIZE / WRITE_SIZE counters (null once the kernel's sources changed), and
+    hbm_measured their rate over the same launch time."""
     if not kernels_ms:
         return None
     name = max(kernels_ms, key=lambda n: kernels_ms[n][0])
     total_ms, calls = kernels_ms[name]
     per_launch_ms = total_ms / max(1, calls)
-    bound, flops, nbytes = work["kernels"].get(name, ("hbm", 0, 0))
+    bound, flops, nbytes, design = work["kernels"].get(name, ("hbm", 0, 0, 0))
     per = max(1, launches_per_step.get(name, 1))
     if bound == "mfma":
         achieved = flops / per / (per_launch_ms * 1e-3) / 1e12
         peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
-    elif bound == "valu":
-        achieved = flops / per / (per_launch_ms * 1e-3) / 1e12
-        peak, unit = PEAK_FP32_TFLOPS, "TFLOP/s"
     else:
         achieved = nbytes / per / (per_launch_ms * 1e-3) / 1e9
         peak, unit = PEAK_HBM_GBS, "GB/s"
-    return {"kernel": name, "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 5), "traffic": measured_traffic(workload, name),
-            "avg_launch_us": round(per_launch_ms * 1e3, 3)}
+    traffic = measured_traffic(workload, name)
+    out = {"kernel": name, "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+           "frac": round(achieved / peak, 5), "traffic": traffic, "avg_launch_us": round(per_launch_ms * 1e3, 3),
+           "design_bytes": int(design / per)}
+    if traffic:
+        gbs = traffic / (per_launch_ms * 1e-3) / 1e9
+        out["hbm_measured"] = {"GB/s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
+
+
+def step_fractions(work, ms):
+    """Whole-step algorithmic rates against both roofs."""
+    tf = work["flops"] / (ms * 1e-3) / 1e12
+    gbs = work["bytes"] / (ms * 1e-3) / 1e9
+    return {"tflops": round(tf, 2), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4), "hbm_gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 # ----------------------------------------------------------------------------- timing
@@ -260,9 +285,9 @@ def bench_prefill(hils, synth, name, steps, warmup, rq=False, lf=False, ml=False
         "ms_per_step_eager": ms_eager,
         "timing": "HIP graph of one step, replayed",
         "wall_s": wall,
-        "tflops": work["flops"] / (ms * 1e-3) / 1e12,
-        "mfma_frac": work["flops"] / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "step_roofline": step_fractions(work, ms),
         "algorithmic_gflop": work["flops"] / 1e9,
+        "algorithmic_mb": work["bytes"] / 1e6,
         "pairs": work["pairs"],
         "kernel_us": per_kernel,
         "roofline": rl,
@@ -354,8 +379,9 @@ def bench_train(hils, synth, name, steps, warmup, rq=False, lf=False, ml=False):
         "ms_per_step_eager": ms_eager,
         "timing": "HIP graph of one step, replayed",
         "wall_s": wall,
-        "tflops": work["flops"] / (ms * 1e-3) / 1e12,
+        "step_roofline": step_fractions(work, ms),
         "algorithmic_gflop": work["flops"] / 1e9,
+        "algorithmic_mb": work["bytes"] / 1e6,
         "kernel_us": {n: round(t / c * 1e3, 3) for n, (t, c) in kt.items()},
         "roofline": roofline(kt, work, {n: c // nsteps for n, (t, c) in kt.items()},
                              None if rq or lf or ml else name),
@@ -368,9 +394,11 @@ def bench_train(hils, synth, name, steps, warmup, rq=False, lf=False, ml=False):
     return res
 
 
-def bench_decode(hils, synth, name, replicas, warmup, lf=False, ml=False):
+def bench_decode(hils, synth, name, replicas, warmup, lf=False, ml=False, eager_steps=0):
     """lf: landmark-free chunks; each replica's landmark rows start as its chunks' key means and the step
-    maintains the open chunk's row."""
+    maintains the open chunk's row.  eager_steps > 0: run only that many steps of every replica, launched
+    one by one without a HIP graph (for counter collection, whose per-dispatch bookkeeping does not cope
+    with a graph of thousands of kernel nodes), and return the wall time per token."""
     import torch
 
     w = synth.WORKLOADS[name]
@@ -402,6 +430,18 @@ def bench_decode(hils, synth, name, replicas, warmup, lf=False, ml=False):
     for s in range(warmup):
         token(s)
     torch.cuda.synchronize()
+    if eager_steps:
+        t0 = time.perf_counter()
+        for s in range(eager_steps):
+            token(s)
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / (eager_steps * len(reps))
+        del x, reps, ws
+        torch.cuda.empty_cache()
+        return {"us_per_token_eager": us, "timing": f"{eager_steps} steps per replica, launched eagerly",
+                "config": {"workload": name, "B": B, "H": H, "d": d, "context": w.L, "steps": eager_steps,
+                           "k": w.k, "replicas": replicas, **({"landmark_free": True} if lf else {}),
+                           **({"landmarks_per_chunk": 2} if ml else {})}}
     # eager pass (host launch overhead included), then the whole run captured once and replayed
     t0 = time.perf_counter()
     for s in range(w.steps):
@@ -512,13 +552,17 @@ def bench_decode_paged(hils, synth, name, warmup):
     return res
 
 
+def _threads():
+    return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(synth, name):
     """The oracle (plain C, double precision) on the host cores, on the full 8K workload."""
     import oracle
 
     w = synth.WORKLOADS[name]
     x = synth.workload_inputs(w)
-    nthreads = len(os.sched_getaffinity(0))
+    nthreads = _threads()
     # the full forward, repeated until about ten seconds of host work have run (at most 40 passes)
     reps, dt = 0, 0.0
     while reps < 40 and (reps == 0 or dt < 10.0):
@@ -528,6 +572,97 @@ def cpu_baseline(synth, name):
         reps += 1
     return {"value": reps * w.B * w.L / dt, "unit": "tokens/s", "cores": int(r["threads"]), "kind": "oracle",
             "sample": f"full {name} forward (B={w.B} H={w.H} L={w.L} d={w.d} k={w.k}) x {reps}, {dt:.1f} s"}
+
+
+def cpu_baseline_prefill_heads(synth, name, heads):
+    """The oracle's forward on ``heads`` of the workload's H heads (same shapes per head), scaled to all
+    heads: the work is exactly linear in the head count."""
+    import oracle
+
+    w = synth.WORKLOADS[name]
+    x = synth.workload_inputs(w, H=heads)
+    t0 = time.perf_counter()
+    r = oracle.fwd(x["Q"], x["K"], x["V"], x["Klm"], w.C, w.k, nthreads=_threads())
+    dt = time.perf_counter() - t0
+    scale = w.H / heads
+    return {"value": w.B * w.L / (dt * scale), "unit": "tokens/s", "cores": int(r["threads"]), "kind": "oracle",
+            "sample": f"{name} forward on {heads} of {w.H} heads (B={w.B} L={w.L} d={w.d} k={w.k}), {dt:.1f} s, "
+                      f"scaled x{scale:g} to all heads"}
+
+
+def cpu_baseline_decode(synth, name, heads, steps):
+    """The oracle's decode steps on ``heads`` of the workload's heads at its context, scaled to all heads."""
+    import oracle
+
+    w = synth.WORKLOADS[name]
+    x = synth.workload_inputs(w, H=heads, steps=steps)
+    Kc, Vc = x["K_cache"], x["V_cache"]
+    nthreads = _threads()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        r = oracle.decode(x["q"][s], x["k_new"][s], x["v_new"][s], Kc, Vc, x["Klm"], w.L + s, w.C, w.k,
+                          nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    scale = w.H / heads
+    return {"value": dt / steps * scale * 1e6, "unit": "us/token", "cores": int(r["threads"]), "kind": "oracle",
+            "sample": f"{name}: {steps} decode steps on {heads} of {w.H} heads at context {w.L} (d={w.d} k={w.k}), "
+                      f"{dt:.1f} s, scaled x{scale:g} to all heads"}
+
+
+def cpu_baseline_train(synth, name, batch):
+    """The oracle's forward and backward (selection from its forward) on ``batch`` of the workload's B
+    sequences, scaled to the whole batch."""
+    import oracle
+
+    w = synth.WORKLOADS[name]
+    x = synth.workload_inputs(w, B=batch, with_dO=True)
+    nthreads = _threads()
+    t0 = time.perf_counter()
+    f = oracle.fwd(x["Q"], x["K"], x["V"], x["Klm"], w.C, w.k, nthreads=nthreads)
+    oracle.bwd(x["Q"], x["K"], x["V"], x["Klm"], x["dO"], f["idx"], w.C, w.k, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    scale = w.B / batch
+    return {"value": w.B * w.L / (dt * scale), "unit": "tokens/s", "cores": int(f["threads"]), "kind": "oracle",
+            "sample": f"{name} forward + backward on {batch} of {w.B} sequences (H={w.H} L={w.L} d={w.d} k={w.k}), "
+                      f"{dt:.1f} s, scaled x{scale:g} to the whole batch"}
+
+
+def measured_peaks():
+    """Rates the box reaches with library kernels: a 1 GiB device copy (HBM read + write) and a bf16
+    8192^3 matrix product (hipBLASLt on MFMA).  Context for the spec peaks the rooflines use."""
+    import torch
+
+    out = {}
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    out["hbm_copy_GBs"] = round(2 * nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del src, dst
+    n = 8192
+    a = torch.randn((n, n), device="cuda:0", dtype=torch.bfloat16)
+    b = torch.randn((n, n), device="cuda:0", dtype=torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    out["bf16_gemm_TFLOPs"] = round(2 * n ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    del a, b, c
+    torch.cuda.empty_cache()
+    out["note"] = "1 GiB device copy (read + write bytes) and a bf16 8192^3 torch matmul, 10 runs each"
+    return out
 
 
 # ----------------------------------------------------------------------------- main
@@ -548,6 +683,8 @@ def main():
                                                "first and last token of each chunk) and print "
                                                "its result object; for profiling runs")
     ap.add_argument("--decode-replicas", type=int, default=32)
+    ap.add_argument("--decode-eager-steps", type=int, default=0,
+                    help="with --only decode_*: run this many steps per replica without a HIP graph (counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -586,7 +723,8 @@ def main():
         elif name.startswith("decode_paged"):
             res = bench_decode_paged(hils, synth, name, args.warmup)
         elif name.startswith("decode"):
-            res = bench_decode(hils, synth, name, args.decode_replicas, args.warmup, lf=lf, ml=ml)
+            res = bench_decode(hils, synth, name, args.decode_replicas, args.warmup, lf=lf, ml=ml,
+                               eager_steps=args.decode_eager_steps)
         elif name.startswith("train"):
             res = bench_train(hils, synth, name, args.steps, args.warmup, rq=rq, lf=lf, ml=ml)
         else:
@@ -642,10 +780,21 @@ def main():
         log("[bench] decode_paged_b16 (16 ragged sequences, paged cache)")
         extra["decode_paged_b16"] = bench_decode_paged(hils, synth, "decode_paged_b16", 4)
         log(f"[bench] decode_paged_b16 {extra['decode_paged_b16']['us_per_step']:.2f} us/step")
+    log("[bench] measured peaks (library copy and matmul)")
+    peaks = measured_peaks()
     cpu = None
     if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle)")
+        log("[bench] cpu baseline (oracle): prefill_8k")
         cpu = cpu_baseline(synth, "prefill_8k")
+        if "prefill_128k" in extra:
+            log("[bench] cpu baseline (oracle): prefill_128k, 2 heads")
+            extra["prefill_128k"]["cpu_baseline"] = cpu_baseline_prefill_heads(synth, "prefill_128k", 2)
+        if "decode_512k" in extra:
+            log("[bench] cpu baseline (oracle): decode_512k, 4 heads, 16 steps")
+            extra["decode_512k"]["cpu_baseline"] = cpu_baseline_decode(synth, "decode_512k", 4, 16)
+        if "train_8k" in extra:
+            log("[bench] cpu baseline (oracle): train_8k, 1 sequence")
+            extra["train_8k"]["cpu_baseline"] = cpu_baseline_train(synth, "train_8k", 1)
     line = {
         "metric": METRIC,
         "value": round(head["tokens_per_s"], 1),
@@ -662,6 +811,7 @@ def main():
         "config": head["config"],
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
+        "measured_peaks": peaks,
         "detail": {"prefill_8k": {k: v for k, v in head.items() if k not in ("roofline", "config")}},
         "workloads": extra,
     }
