@@ -82,10 +82,18 @@ const char* hils_last_error(void);
 int hils_version(void);
 
 /*
+ * OR into the operation code of hils_workspace_size when the call's inputs
+ * are HILS_FP32: the forward's per-pair chunk outputs and the backward's
+ * per-pair dQ parts are then kept in fp32 (bf16 for 16-bit inputs), so
+ * HILS_OP_FWD, HILS_OP_FWD_ML and HILS_OP_BWD need more workspace.
+ */
+#define HILS_WS_FP32 256
+
+/*
  * Bytes of workspace the operation needs for these sizes (0 if none; a
  * null workspace pointer is then accepted).  For HILS_OP_DECODE pass the
- * cache capacity L_max as L.  Returns 0 and sets hils_last_error for
- * invalid sizes.
+ * cache capacity L_max as L.  op may carry HILS_WS_FP32 (see above).
+ * Returns 0 and sets hils_last_error for invalid sizes.
  */
 size_t hils_workspace_size(int op, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk);
 
@@ -296,7 +304,12 @@ hils_status hils_sparse_attn_bwd_ml(const void* Q, const void* Q_ret, const void
  * n_ctx[b], with the caches held in page pools:
  *   K_pages, V_pages : [n_pages][H][64][d] (dt); page p holds, for every head,
  *                      the 64 key / value rows of one chunk
- *   K_lm_pages       : [n_pages][H][d] (dt); the landmark row of that chunk
+ *   K_lm_pages       : [n_pages][H][m][d] (dt); the m landmark rows of that
+ *                      chunk (m = 1: one landmark; m > 1: several landmarks,
+ *                      the chunk score is the log-sum-exp of their scores as
+ *                      in hils_decode_step_ml)
+ *   m                : landmarks per chunk, 1 <= m <= 16 (m > 1 needs
+ *                      landmark_free = 0)
  *   page_table       : [B][max_pages] int32 (device): pool page of chunk j of
  *                      sequence b, for every chunk 0 .. n_ctx[b]/64
  *   n_ctx            : [B] int64 (device): each sequence's position; the new
@@ -312,7 +325,7 @@ hils_status hils_sparse_attn_bwd_ml(const void* Q, const void* Q_ret, const void
  * hils_workspace_size(HILS_OP_DECODE, B, H, max_pages*64, d, C, topk).
  */
 hils_status hils_decode_step_paged(const void* q, const void* q_ret, const void* k_new, const void* v_new,
-                                   void* K_pages, void* V_pages, void* K_lm_pages, const int32_t* page_table,
+                                   void* K_pages, void* V_pages, void* K_lm_pages, int64_t m, const int32_t* page_table,
                                    int64_t n_pages, int64_t max_pages, const int64_t* n_ctx, int64_t n_ctx_max,
                                    int landmark_free, void* o, int32_t* idx, float* w, int64_t B, int64_t H,
                                    int64_t d, int64_t C, int64_t topk, float scale, hils_dtype dt, void* ws,

@@ -91,8 +91,10 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
                                                         const T* __restrict__ dO, const float* __restrict__ w,
                                                         const float* __restrict__ lse,
                                                         const int* __restrict__ chunk_off,
-                                                        const int* __restrict__ pairs, uint16_t* __restrict__ dq_part,
-                                                        float* __restrict__ Dpart, uint16_t* __restrict__ trash,
+                                                        const int* __restrict__ pairs,
+                                                        typename PartialOf<T>::type* __restrict__ dq_part,
+                                                        float* __restrict__ Dpart,
+                                                        typename PartialOf<T>::type* __restrict__ trash,
                                                         float* __restrict__ trash_f, float* __restrict__ dK,
                                                         float* __restrict__ dV, int L, int N, int k, float scale) {
   using S = BwdLds<T, D>;
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
         for (int e = 0; e < 8; ++e) v8[e] = dp[2 * h + e / 4][e % 4];
         daf[h].set(v8);
       }
-      uint16_t* dst = valid ? dq_part + (row * k1 + in.slot) * D : trash;
+      typename PartialOf<T>::type* dst = valid ? dq_part + (row * k1 + in.slot) * D : trash;
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
         f32x4_t dq = zero4();
@@ -230,10 +232,13 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
           a.load4x2(rowp, rowp + 16);
           mma(dq, a, daf[h]);
         }
-        u16x4_t h4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) h4[i] = __builtin_bit_cast(uint16_t, (_Float16)(scale * dq[i]));
-        *reinterpret_cast<u16x4_t*>(dst + 16 * db + 4 * g) = h4;
+        // bf16 parts keep fp32's exponent range (no overflow whatever the scale of dQ); fp32 inputs keep fp32
+        if constexpr (sizeof(typename PartialOf<T>::type) == 2) {
+          *reinterpret_cast<uint2*>(dst + 16 * db + 4 * g) =
+              make_uint2(pack_bf16x2(scale * dq[0], scale * dq[1]), pack_bf16x2(scale * dq[2], scale * dq[3]));
+        } else {
+          *reinterpret_cast<f32x4_t*>(dst + 16 * db + 4 * g) = scale * dq;
+        }
       }
     }
     __syncthreads();  // previous tile's readers of the staged buffers are done
@@ -328,7 +333,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
 // and dropped slots read a valid address and are not used): two memory round trips per
 // thread, the landmark rows once the indices are in.
 template <typename T, int D, int K1M, bool RQ>
-__global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* __restrict__ dq_part,
+__global__ __launch_bounds__(256) void dq_reduce_kernel(const typename PartialOf<T>::type* __restrict__ dq_part,
                                                         const float* __restrict__ Dpart,
                                                         const int32_t* __restrict__ idx, const float* __restrict__ w,
                                                         const T* __restrict__ Klm, float* __restrict__ ds_out,
@@ -342,16 +347,19 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* __restri
   if (row >= rows) return;
   const int k1 = k + 1;
   const int64_t bh = row / L;
+  constexpr int VPP = (int)sizeof(typename PartialOf<T>::type) / 2;  // 16-byte loads per eight elements
   int jr[K1M];
   float wr[K1M], dr[K1M];
-  uint4 raw[K1M];
+  uint4 raw[K1M][VPP];
 #pragma unroll
   for (int r = 0; r < K1M; ++r) {
     const int64_t e = row * k1 + (r < k1 ? r : 0);
     jr[r] = idx[e];
     wr[r] = w[e];
     dr[r] = Dpart[e];
-    raw[r] = *reinterpret_cast<const uint4*>(dq_part + e * D + 8 * c8);
+    const uint4* src = reinterpret_cast<const uint4*>(dq_part + e * D + 8 * c8);
+#pragma unroll
+    for (int h = 0; h < VPP; ++h) raw[r][h] = src[h];
   }
   bool ok[K1M];
   float Dsum = 0.f;
@@ -386,17 +394,26 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const uint16_t* __restri
     const float ds = wr[r] * (dr[r] - Dsum);
     if (c8 == 0) ds_out[row * k1 + r] = ds;
     const float sds = (skip == 2 || (skip == 1 && r == k)) ? 0.f : scale * ds;
-    _Float16 h[8];
-    __builtin_memcpy(h, &raw[r], 16);
+    float h[8];
+    if constexpr (VPP == 1) {
+      const uint32_t wds[4] = {raw[r][0].x, raw[r][0].y, raw[r][0].z, raw[r][0].w};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        h[2 * x] = __uint_as_float(wds[x] << 16);
+        h[2 * x + 1] = __uint_as_float(wds[x] & 0xFFFF0000u);
+      }
+    } else {
+      __builtin_memcpy(h, raw[r], 32);
+    }
     T lm[8];
     __builtin_memcpy(lm, lw[r], 8 * sizeof(T));
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if (RQ) {
-        acc[e] += (float)h[e];
+        acc[e] += h[e];
         accr[e] += sds * Elem<T>::to_f32(lm, e);
       } else {
-        acc[e] += (float)h[e] + sds * Elem<T>::to_f32(lm, e);
+        acc[e] += h[e] + sds * Elem<T>::to_f32(lm, e);
       }
     }
   }
@@ -476,26 +493,27 @@ static hipError_t bwd_t(const void* Q, const void* Qr, const void* K, const void
                         const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ, float* dQr,
                         float* dK, float* dV, float* dKlm, int BH, int L, int N, int k, float scale,
                         const BwdBufs& ws, hipStream_t st) {
+  using PT = typename PartialOf<T>::type;
   const int64_t rows = (int64_t)BH * L;
   hipError_t e = launch_route(idx, ws.rb, BH, L, N, k, st);
   if (e != hipSuccess) return e;
   HILS_LAUNCH("chunk_bwd", (chunk_bwd_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)Q, (const T*)K,
-              (const T*)V, (const T*)Klm, (const T*)dO, w, lse, ws.rb.chunk_off, ws.rb.pairs, ws.dq_part, ws.Dpart,
-              ws.trash, ws.trash_f, dK, dV, L, N, k, scale);
+              (const T*)V, (const T*)Klm, (const T*)dO, w, lse, ws.rb.chunk_off, ws.rb.pairs, (PT*)ws.dq_part, ws.Dpart,
+              (PT*)ws.trash, ws.trash_f, dK, dV, L, N, k, scale);
   const dim3 rgrid((unsigned)((rows * (D / 8) + 255) / 256));
   const bool rq = Qr != nullptr;
   const int skip = mlm > 0 ? 2 : (lf ? 1 : 0);
   if (k <= 8 && !rq)
-    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 9, false>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx,
+    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 9, false>), rgrid, dim3(256), 0, st, (const PT*)ws.dq_part, ws.Dpart, idx,
                 w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, skip);
   else if (!rq)
-    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 17, false>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx,
+    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 17, false>), rgrid, dim3(256), 0, st, (const PT*)ws.dq_part, ws.Dpart, idx,
                 w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, skip);
   else if (k <= 8)
-    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 9, true>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx,
+    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 9, true>), rgrid, dim3(256), 0, st, (const PT*)ws.dq_part, ws.Dpart, idx,
                 w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, skip);
   else
-    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 17, true>), rgrid, dim3(256), 0, st, ws.dq_part, ws.Dpart, idx,
+    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 17, true>), rgrid, dim3(256), 0, st, (const PT*)ws.dq_part, ws.Dpart, idx,
                 w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, skip);
   // dKlm_j sums ds_tj times the query that scored the landmark
   if (mlm > 0) {

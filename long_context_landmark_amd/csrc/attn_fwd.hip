@@ -197,9 +197,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 3) : 1) void c
                                                              const T* __restrict__ V, const int4* __restrict__ items,
                                                              const int* __restrict__ n_items,
                                                              const int* __restrict__ pairs, float* __restrict__ lse_pair,
-                                                             uint16_t* __restrict__ partial, uint16_t* __restrict__ trash,
+                                                             typename PartialOf<T>::type* __restrict__ partial,
+                                                             typename PartialOf<T>::type* __restrict__ trash,
                                                              float* __restrict__ trash_lse, int L, int N, int k,
                                                              int max_items, float scale, int spread) {
+  using PT = typename PartialOf<T>::type;
+  constexpr bool P16 = sizeof(PT) == 2;
   // A head whose query rows fit in one XCD's L2 keeps all its items on that XCD (the rows
   // gathered by its items are then read from HBM once).  Larger heads are spread over all
   // XCDs, head after head, so the query rows of the few heads in flight stay in the
@@ -250,9 +253,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 3) : 1) void c
   // lane, 1 KiB a store).  Rows of absent pairs go to a scratch row: every lane stores, so
   // the waits on the loads of the next tiles can count the stores.
   constexpr bool ROWS = frags_in_regs<T, D>() > 0;
-  constexpr int RSB = D + 8;  // row stride of the turnaround buffer (bf16 elements)
-  uint16_t* rowbuf = reinterpret_cast<uint16_t*>(&s) + w_ * 16 * RSB;
-  static_assert(!ROWS || 4 * 16 * RSB * 2 <= 64 * ChunkLds<T, D>::KS * (int)sizeof(T),
+  constexpr int EPV = 16 / (int)sizeof(PT);         // partial elements per 16-byte piece
+  constexpr int RSB = D + (P16 ? 8 : 4);             // row stride of the turnaround buffer (elements)
+  PT* rowbuf = reinterpret_cast<PT*>(&s) + w_ * 16 * RSB;
+  static_assert(!ROWS || 4 * 16 * RSB * (int)sizeof(PT) <= 64 * ChunkLds<T, D>::KS * (int)sizeof(T),
                 "turnaround buffer fits the K staging area");
   auto tile = [&](const Frag<T>(&qf)[D / 32], int pe, int base) {
     Frag<T> qx[D / 32];
@@ -267,28 +271,36 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 3) : 1) void c
     const bool ok = pe >= 0;
     const int64_t prow = (int64_t)bh * L * k + base + 16 * w_ + r16;
     if constexpr (ROWS) {
-      constexpr int PPR = D / 8, RPI = 64 / PPR;  // 16-byte pieces per row, rows per store
+      constexpr int PPR = D / EPV, RPI = 64 / PPR;  // 16-byte pieces per row, rows per store
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db)
-        *reinterpret_cast<uint2*>(rowbuf + r16 * RSB + 16 * db + 4 * g) =
-            make_uint2(pack_bf16x2(o[db][0], o[db][1]), pack_bf16x2(o[db][2], o[db][3]));
+      for (int db = 0; db < D / 16; ++db) {
+        if constexpr (P16)
+          *reinterpret_cast<uint2*>(rowbuf + r16 * RSB + 16 * db + 4 * g) =
+              make_uint2(pack_bf16x2(o[db][0], o[db][1]), pack_bf16x2(o[db][2], o[db][3]));
+        else
+          *reinterpret_cast<f32x4_t*>(rowbuf + r16 * RSB + 16 * db + 4 * g) = o[db];
+      }
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int it = 0; it < 16 / RPI; ++it) {
         const int row = it * RPI + lane / PPR, pc = lane % PPR;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(rowbuf + row * RSB + 8 * pc);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(rowbuf + row * RSB + EPV * pc);
         const int pidx = base + 16 * w_ + row;
-        uint16_t* dst = pidx < p1 ? partial + ((int64_t)bh * L * k + pidx) * D : trash;
-        if constexpr (STREAM_OUT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst + 8 * pc));
-        else *reinterpret_cast<u32x4_t*>(dst + 8 * pc) = v;
+        PT* dst = pidx < p1 ? partial + ((int64_t)bh * L * k + pidx) * D : trash;
+        if constexpr (STREAM_OUT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst + EPV * pc));
+        else *reinterpret_cast<u32x4_t*>(dst + EPV * pc) = v;
       }
       __builtin_amdgcn_wave_barrier();
     } else {
-      uint16_t* dst = ok ? partial + prow * D : trash;
+      PT* dst = ok ? partial + prow * D : trash;
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
-        const uint2 v2 = make_uint2(pack_bf16x2(o[db][0], o[db][1]), pack_bf16x2(o[db][2], o[db][3]));
-        *reinterpret_cast<uint2*>(dst + 16 * db + 4 * g) = v2;
+        if constexpr (P16) {
+          const uint2 v2 = make_uint2(pack_bf16x2(o[db][0], o[db][1]), pack_bf16x2(o[db][2], o[db][3]));
+          *reinterpret_cast<uint2*>(dst + 16 * db + 4 * g) = v2;
+        } else {
+          *reinterpret_cast<f32x4_t*>(dst + 16 * db + 4 * g) = o[db];
+        }
       }
     }
     // the four lane groups hold the same row statistics
@@ -332,9 +344,11 @@ template <typename T, int D>
 __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 5 : 3) : 1) void own_combine_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                           const T* __restrict__ V, const int* __restrict__ pos_of,
                                                           const float* __restrict__ w,
-                                                          const uint16_t* __restrict__ partial,
+                                                          const typename PartialOf<T>::type* __restrict__ partial,
                                                           const float* __restrict__ lse_pair, T* __restrict__ O,
                                                           float* __restrict__ lse, int L, int N, int k, float scale) {
+  using PT = typename PartialOf<T>::type;
+  constexpr int VPP = (int)sizeof(PT) / 2;  // 16-byte loads per 8-element piece
   constexpr int RS = D + 4;         // row stride of the output rows in LDS (floats)
   constexpr int PPR = D / 8;        // 8-element pieces per row
   constexpr int NI = 64 * PPR / 256;  // pieces per thread
@@ -393,12 +407,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 5 : 3) : 1) void o
   }
   // partial pieces of SB slots for every owned piece are in flight together; a slot whose
   // position is -1 reads row 0 of the head's list and is dropped
-  constexpr int SB = NI == 2 ? 8 : 4;
+  constexpr int SB = (NI == 2 ? 8 : 4) / VPP;
   const int m = min(k, 16);
 #pragma unroll
   for (int r0 = 0; r0 < 16; r0 += SB) {
     if (r0 >= m) break;
-    u32x4_t v[NI][SB];
+    u32x4_t v[NI][SB][VPP];
     bool kept[NI][SB];
     float wt[NI][SB];
 #pragma unroll
@@ -409,19 +423,28 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 5 : 3) : 1) void o
         const int p = pos_s[q][r0 + sb];
         kept[it][sb] = p >= 0;
         wt[it][sb] = w_s[q][r0 + sb];
-        v[it][sb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(partial + (pbase + max(p, 0)) * D + 8 * pc));
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(partial + (pbase + max(p, 0)) * D + 8 * pc);
+#pragma unroll
+        for (int h = 0; h < VPP; ++h) v[it][sb][h] = __builtin_nontemporal_load(src + h);
       }
     }
 #pragma unroll
     for (int it = 0; it < NI; ++it)
 #pragma unroll
       for (int sb = 0; sb < SB; ++sb) {
-        const uint32_t wds[4] = {v[it][sb][0], v[it][sb][1], v[it][sb][2], v[it][sb][3]};
+        float pv[8];
+        if constexpr (VPP == 1) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          acc[it][2 * x] += kept[it][sb] ? wt[it][sb] * __uint_as_float(wds[x] << 16) : 0.f;
-          acc[it][2 * x + 1] += kept[it][sb] ? wt[it][sb] * __uint_as_float(wds[x] & 0xFFFF0000u) : 0.f;
+          for (int x = 0; x < 4; ++x) {
+            pv[2 * x] = __uint_as_float(v[it][sb][0][x] << 16);
+            pv[2 * x + 1] = __uint_as_float(v[it][sb][0][x] & 0xFFFF0000u);
+          }
+        } else {
+#pragma unroll
+          for (int x = 0; x < 8; ++x) pv[x] = __uint_as_float(v[it][sb][x / 4][x % 4]);
         }
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[it][x] += kept[it][sb] ? wt[it][sb] * pv[x] : 0.f;
       }
   }
 #pragma unroll
@@ -472,10 +495,14 @@ __global__ __launch_bounds__(256) void fixed_selection_kernel(const T* __restric
 }
 
 template <typename T, int D>
-static hipError_t chunk_attn_t(const void* Q, const void* K, const void* V, const RouteBufs& rb, float* lse, uint16_t* partial, uint16_t* trash, float* trash_lse, int BH, int L, int N,
-                               int k, float scale, hipStream_t st) {
+static hipError_t chunk_attn_t(const void* Q, const void* K, const void* V, const RouteBufs& rb, float* lse,
+                               void* partial_v, void* trash_v, float* trash_lse, int BH, int L, int N, int k,
+                               float scale, hipStream_t st) {
+  using PT = typename PartialOf<T>::type;
+  PT* partial = (PT*)partial_v;
+  PT* trash = (PT*)trash_v;
   const int spread = (int64_t)L * D * sizeof(T) > L2_BYTES_PER_XCD;
-  if ((int64_t)BH * L * k * D * 2 > MALL_BYTES)
+  if ((int64_t)BH * L * k * D * (int64_t)sizeof(PT) > MALL_BYTES)
     HILS_LAUNCH("chunk_attn_fwd", (chunk_attn_fwd_kernel<T, D, true>), dim3(rb.max_items, BH), dim3(256), 0, st,
                 (const T*)Q, (const T*)K, (const T*)V, rb.items, rb.n_items, rb.pairs, lse, partial,
                 trash, trash_lse, L, N, k, rb.max_items, scale, spread);
@@ -488,15 +515,16 @@ static hipError_t chunk_attn_t(const void* Q, const void* K, const void* V, cons
 
 template <typename T, int D>
 static hipError_t own_combine_t(const void* Q, const void* K, const void* V, const int* pos_of, const float* w,
-                                const uint16_t* partial, const float* lse_pair, void* O, float* lse, int BH, int L,
+                                const void* partial, const float* lse_pair, void* O, float* lse, int BH, int L,
                                 int N, int k, float scale, hipStream_t st) {
   HILS_LAUNCH("own_combine", (own_combine_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)Q, (const T*)K,
-              (const T*)V, pos_of, w, partial, lse_pair, (T*)O, lse, L, N, k, scale);
+              (const T*)V, pos_of, w, (const typename PartialOf<T>::type*)partial, lse_pair, (T*)O, lse, L, N, k,
+              scale);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_attn_fwd(int dt, int d, const void* Q, const void* K, const void* V, const RouteBufs& rb,
-                                 float* lse, uint16_t* partial, uint16_t* trash, float* trash_lse,
+                                 float* lse, void* partial, void* trash, float* trash_lse,
                                  int BH, int L, int N, int k, float scale, hipStream_t st) {
   if (dt == 0)
     return d == 64 ? chunk_attn_t<bf16_t, 64>(Q, K, V, rb, lse, partial, trash, trash_lse, BH, L, N, k, scale, st)
@@ -506,7 +534,7 @@ hipError_t launch_chunk_attn_fwd(int dt, int d, const void* Q, const void* K, co
 }
 
 hipError_t launch_own_combine(int dt, int d, const void* Q, const void* K, const void* V, const int* pos_of,
-                              const float* w, const uint16_t* partial, const float* lse_pair, void* O, float* lse,
+                              const float* w, const void* partial, const float* lse_pair, void* O, float* lse,
                               int BH, int L, int N, int k, float scale, hipStream_t st) {
   if (dt == 0)
     return d == 64 ? own_combine_t<bf16_t, 64>(Q, K, V, pos_of, w, partial, lse_pair, O, lse, BH, L, N, k, scale, st)

@@ -536,11 +536,11 @@ static hipError_t decode_dispatch(int dt, int d, const void* q, const void* qr, 
 }
 
 hipError_t launch_decode_paged(int dt, int d, const void* q, const void* qr, const void* k_new, const void* v_new,
-                               void* Kp, void* Vp, void* Klm_p, bool lf, const int32_t* page_table, int max_pages,
+                               void* Kp, void* Vp, void* Klm_p, bool lf, int mlm, const int32_t* page_table, int max_pages,
                                int64_t pages, const int64_t* n_ctx, int64_t n_max, int B, int H, void* o,
                                int32_t* idx, float* w, int k, float scale, const DecodeBufs& ws, hipStream_t st) {
   const DecAddr A{page_table, n_ctx, max_pages, H, pages};
-  return decode_dispatch<true>(dt, d, q, qr, k_new, v_new, Kp, Vp, Klm_p, lf, 1, n_max, 0, 0, o, idx, w, B * H, k,
+  return decode_dispatch<true>(dt, d, q, qr, k_new, v_new, Kp, Vp, Klm_p, lf, mlm, n_max, 0, 0, o, idx, w, B * H, k,
                                scale, ws, A, st);
 }
 

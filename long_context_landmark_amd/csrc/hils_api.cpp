@@ -85,8 +85,8 @@ struct Carver {
 
 struct FwdWs {
   hils::RouteBufs rb;
-  uint16_t* partial;
-  uint16_t* trash;   // d elements: stores of absent pairs in the chunk-major kernel
+  void* partial;     // [BH][L*k][d] chunk outputs: bf16, or fp32 for fp32 inputs
+  void* trash;       // d elements: stores of absent pairs in the chunk-major kernel
   float* trash_lse;
   float* lse_pair;  // [BH][L*k] chunk log-partition of every pair, in list order
   float* w_tmp;
@@ -110,28 +110,29 @@ size_t carve_route(Carver& cv, const Dims& D, hils::RouteBufs& rb, int ppi) {
 
 size_t ml_scores_bytes(const Dims& D) { return (size_t)D.B * D.H * D.L * D.N * sizeof(float); }
 
-size_t carve_fwd(void* base, const Dims& D, FwdWs* ws) {
+// esz: bytes per element of the per-pair intermediate rows (2: 16-bit inputs, 4: fp32 inputs)
+size_t carve_fwd(void* base, const Dims& D, FwdWs* ws, int esz) {
   Carver cv(base);
   const int64_t BH = D.B * D.H;
   carve_route(cv, D, ws->rb, hils::fwd_pairs_per_item((int)D.N));
   ws->rb.pos_of = cv.take<int>((size_t)BH * D.L * D.k);
-  ws->partial = cv.take<uint16_t>((size_t)BH * D.L * D.k * D.d);
+  ws->partial = cv.take<uint8_t>((size_t)BH * D.L * D.k * D.d * esz);
   ws->lse_pair = cv.take<float>((size_t)BH * D.L * D.k);
   ws->w_tmp = cv.take<float>((size_t)BH * D.L * (D.k + 1));
-  ws->trash = cv.take<uint16_t>((size_t)D.d);
+  ws->trash = cv.take<float>((size_t)D.d);
   ws->trash_lse = cv.take<float>(64);
   ws->klm_frag = cv.take<uint8_t>(hils::topk_workspace_bytes((int)BH, (int)D.N, (int)D.d));
   return cv.off;
 }
 
-size_t carve_bwd(void* base, const Dims& D, hils::BwdBufs* ws) {
+size_t carve_bwd(void* base, const Dims& D, hils::BwdBufs* ws, int esz) {
   Carver cv(base);
   const int64_t BH = D.B * D.H;
   carve_route(cv, D, ws->rb, hils::fwd_pairs_per_item((int)D.N));
-  ws->dq_part = cv.take<uint16_t>((size_t)BH * D.L * (D.k + 1) * D.d);
+  ws->dq_part = cv.take<uint8_t>((size_t)BH * D.L * (D.k + 1) * D.d * esz);
   ws->Dpart = cv.take<float>((size_t)BH * D.L * (D.k + 1));
   ws->ds = cv.take<float>((size_t)BH * D.L * (D.k + 1));
-  ws->trash = cv.take<uint16_t>((size_t)D.d);
+  ws->trash = cv.take<float>((size_t)D.d);
   ws->trash_f = cv.take<float>(64);
   return cv.off;
 }
@@ -179,6 +180,8 @@ int hils_version(void) { return 10000; }
 size_t hils_workspace_size(int op, int64_t B, int64_t H, int64_t L, int64_t d, int64_t C, int64_t topk) {
   Dims D;
   g_err[0] = 0;
+  const int esz = (op & HILS_WS_FP32) ? 4 : 2;
+  op &= ~HILS_WS_FP32;
   switch (op) {
     case HILS_OP_SCORES:
       return 0;
@@ -188,17 +191,17 @@ size_t hils_workspace_size(int op, int64_t B, int64_t H, int64_t L, int64_t d, i
     case HILS_OP_FWD: {
       if (check_dims(B, H, L, d, C, topk, true, &D) != HILS_OK) return 0;
       FwdWs ws;
-      return carve_fwd(nullptr, D, &ws);
+      return carve_fwd(nullptr, D, &ws, esz);
     }
     case HILS_OP_FWD_ML: {
       if (check_dims(B, H, L, d, C, topk, true, &D) != HILS_OK) return 0;
       FwdWs ws;
-      return align_up(carve_fwd(nullptr, D, &ws)) + ml_scores_bytes(D);
+      return align_up(carve_fwd(nullptr, D, &ws, esz)) + ml_scores_bytes(D);
     }
     case HILS_OP_BWD: {
       if (check_dims(B, H, L, d, C, topk, true, &D) != HILS_OK) return 0;
       hils::BwdBufs ws;
-      return carve_bwd(nullptr, D, &ws);
+      return carve_bwd(nullptr, D, &ws, esz);
     }
     case HILS_OP_DECODE: {
       if (check_dims(B, H, ((L + C - 1) / (C > 0 ? C : 1)) * (C > 0 ? C : 1), d, C, topk, true, &D) != HILS_OK)
@@ -323,11 +326,12 @@ static hils_status fwd_impl(const void* Q, const void* Q_ret, const void* K, con
   if (select != 0 && select != 1) return fail(HILS_ERR_INVALID_ARG, "select must be 0 or 1");
   if (!(scale > 0.f)) return fail(HILS_ERR_INVALID_ARG, "scale must be positive");
   FwdWs W;
-  const size_t need0 = carve_fwd(nullptr, D, &W);
+  const int esz = dt == HILS_FP32 ? 4 : 2;
+  const size_t need0 = carve_fwd(nullptr, D, &W, esz);
   // several landmarks per chunk: the causal chunk scores are materialised after the plain workspace
   const size_t need = mlm > 0 ? align_up(need0) + ml_scores_bytes(D) : need0;
   if ((st = check_ws(ws, ws_bytes, need)) != HILS_OK) return st;
-  carve_fwd(ws, D, &W);
+  carve_fwd(ws, D, &W, esz);
   float* S_ml = mlm > 0 ? reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(need0)) : nullptr;
   const int BH = (int)(B * H), iL = (int)L, iN = (int)D.N, ik = (int)topk, id = (int)d;
   hipStream_t s = (hipStream_t)stream;
@@ -505,9 +509,10 @@ static hils_status bwd_impl(const void* Q, const void* Q_ret, const void* K, con
   REQUIRE_PTR(dK_lm);
   if (!(scale > 0.f)) return fail(HILS_ERR_INVALID_ARG, "scale must be positive");
   hils::BwdBufs W;
-  const size_t need = carve_bwd(nullptr, D, &W);
+  const int esz = dt == HILS_FP32 ? 4 : 2;
+  const size_t need = carve_bwd(nullptr, D, &W, esz);
   if ((st = check_ws(ws, ws_bytes, need)) != HILS_OK) return st;
-  carve_bwd(ws, D, &W);
+  carve_bwd(ws, D, &W, esz);
   return hip_status(hils::launch_bwd(dt, (int)d, Q, Q_ret, K, V, K_lm, lf, (int)mlm, dO, idx, w, lse, dQ, dQ_ret, dK, dV, dK_lm,
                                      (int)(B * H), (int)L, (int)D.N, (int)topk, scale, W, (hipStream_t)stream),
                     "hils_sparse_attn_bwd");
@@ -516,7 +521,7 @@ static hils_status bwd_impl(const void* Q, const void* Q_ret, const void* K, con
 extern "C" {
 
 hils_status hils_decode_step_paged(const void* q, const void* q_ret, const void* k_new, const void* v_new,
-                                   void* K_pages, void* V_pages, void* K_lm_pages, const int32_t* page_table,
+                                   void* K_pages, void* V_pages, void* K_lm_pages, int64_t m, const int32_t* page_table,
                                    int64_t n_pages, int64_t max_pages, const int64_t* n_ctx, int64_t n_ctx_max,
                                    int landmark_free, void* o, int32_t* idx, float* w, int64_t B, int64_t H,
                                    int64_t d, int64_t C, int64_t topk, float scale, hils_dtype dt, void* ws,
@@ -533,6 +538,9 @@ hils_status hils_decode_step_paged(const void* q, const void* q_ret, const void*
     return fail(HILS_ERR_INVALID_ARG, "n_ctx_max (%lld) must be in [0, max_pages*C=%lld)", (long long)n_ctx_max,
                 (long long)L_max);
   if (landmark_free != 0 && landmark_free != 1) return fail(HILS_ERR_INVALID_ARG, "landmark_free must be 0 or 1");
+  if (m < 1 || m > 16) return fail(HILS_ERR_UNSUPPORTED, "landmarks per chunk must be in [1, 16] (got %lld)",
+                                   (long long)m);
+  if (m > 1 && landmark_free) return fail(HILS_ERR_INVALID_ARG, "landmark-free chunks take one landmark per chunk");
   REQUIRE_PTR(q);
   OPTIONAL_PTR(q_ret);
   REQUIRE_PTR(k_new);
@@ -551,7 +559,7 @@ hils_status hils_decode_step_paged(const void* q, const void* q_ret, const void*
   if ((st = check_ws(ws, ws_bytes, need)) != HILS_OK) return st;
   carve_decode(ws, B * H, L_max, d, topk, &W);
   return hip_status(hils::launch_decode_paged(dt, (int)d, q, q_ret, k_new, v_new, K_pages, V_pages, K_lm_pages,
-                                              landmark_free != 0, page_table, (int)max_pages, n_pages, n_ctx,
+                                              landmark_free != 0, (int)m, page_table, (int)max_pages, n_pages, n_ctx,
                                               n_ctx_max, (int)B, (int)H, o, idx, w, (int)topk, scale, W,
                                               (hipStream_t)stream),
                     "hils_decode_step_paged");

@@ -45,6 +45,11 @@ template <> struct Elem<float> {
   __device__ static void store(float* p, int64_t i, float v) { p[i] = v; }
 };
 
+// Storage type of per-pair intermediate rows (chunk outputs, in-chunk dQ parts): bf16 bits for 16-bit
+// inputs, fp32 for fp32 inputs (their intermediates keep the inputs' precision).
+template <typename T> struct PartialOf { using type = uint16_t; };
+template <> struct PartialOf<float> { using type = float; };
+
 // Eight consecutive k-elements of one row, as one MFMA operand fragment.
 template <typename T> struct Frag;
 template <> struct Frag<bf16_t> {

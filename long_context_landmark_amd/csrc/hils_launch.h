@@ -44,16 +44,17 @@ int route_max_items(int L, int N, int k, int pairs_per_item);
 hipError_t launch_route(const int32_t* idx, const RouteBufs& rb, int BH, int L, int N, int k, hipStream_t st);
 
 // Writes, for every pair at position p of the routing lists, the chunk output (softmax
-// attention of the query over the chunk, not yet weighted) partial[bh][p][d] (bf16) and the chunk log-partition lse_pair[bh][p]: consecutive pairs of a
+// attention of the query over the chunk, not yet weighted) partial[bh][p][d] (bf16 for 16-bit
+// inputs, fp32 for fp32 inputs) and the chunk log-partition lse_pair[bh][p]: consecutive pairs of a
 // work item land in consecutive rows.  trash (d elements) and trash_lse (one float) receive
 // the stores of absent pairs.
 hipError_t launch_chunk_attn_fwd(int dt, int d, const void* Q, const void* K, const void* V, const RouteBufs& rb,
-                                 float* lse_pair, uint16_t* partial, uint16_t* trash, float* trash_lse,
+                                 float* lse_pair, void* partial, void* trash, float* trash_lse,
                                  int BH, int L, int N, int k, float scale, hipStream_t st);
 // partial and lse_pair are indexed by pair position (chunk-major, as chunk_attn_fwd writes
 // them); pos_of maps (query, slot) to that position
 hipError_t launch_own_combine(int dt, int d, const void* Q, const void* K, const void* V, const int* pos_of,
-                              const float* w, const uint16_t* partial, const float* lse_pair, void* O, float* lse,
+                              const float* w, const void* partial, const float* lse_pair, void* O, float* lse,
                               int BH, int L, int N, int k, float scale, hipStream_t st);
 // pairs per chunk-major work item: short sequences favour balance, long ones fewer K/V re-reads
 inline int fwd_pairs_per_item(int N) { return N <= 1024 ? 512 : 1024; }
@@ -77,10 +78,11 @@ int decode_list_len();
 
 struct BwdBufs {
   RouteBufs rb;
-  uint16_t* dq_part;  // [BH][L][k+1][d] fp16 in-chunk dQ contribution of every (query, slot)
+  void* dq_part;    // [BH][L][k+1][d] in-chunk dQ contribution of every (query, slot): bf16 for 16-bit
+                    // inputs, fp32 for fp32 inputs
   float* Dpart;    // [BH][L][k+1]    D_j = dO_t . o_tj of every (query, slot)
   float* ds;       // [BH][L][k+1]    fusion-score gradient of every (query, slot)
-  uint16_t* trash; // d elements: stores of lanes without a pair
+  void* trash;     // d elements: stores of lanes without a pair
   float* trash_f;  // one float, likewise
 };
 // Qr / dQr: retrieval queries that scored the landmarks and their gradient (both null: Q scored them,
@@ -102,9 +104,9 @@ hipError_t launch_decode(int dt, int d, const void* q, const void* qr, const voi
                          void* Vc, const void* Klm, bool lf, int mlm, int64_t n, int64_t Lmax, int64_t Nmax, void* o,
                          int32_t* idx, float* w, int BH, int k, float scale, const DecodeBufs& ws, hipStream_t st);
 // decode step of B sequences at their own positions n_ctx[b] (device, <= n_max) over paged caches: page p of
-// the pools holds one chunk of 64 rows per head (Kp, Vp: [pages][H][64][d]; Klm_p: [pages][H][d])
+// the pools holds one chunk of 64 rows per head (Kp, Vp: [pages][H][64][d]; Klm_p: [pages][H][mlm][d])
 hipError_t launch_decode_paged(int dt, int d, const void* q, const void* qr, const void* k_new, const void* v_new,
-                               void* Kp, void* Vp, void* Klm_p, bool lf, const int32_t* page_table, int max_pages,
+                               void* Kp, void* Vp, void* Klm_p, bool lf, int mlm, const int32_t* page_table, int max_pages,
                                int64_t pages, const int64_t* n_ctx, int64_t n_max, int B, int H, void* o,
                                int32_t* idx, float* w, int k, float scale, const DecodeBufs& ws, hipStream_t st);
 // several landmarks per chunk (Klm [BH][N][m][d]): causal chunk scores (log-sum-exp over a chunk's landmarks)

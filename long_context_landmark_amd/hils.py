@@ -47,7 +47,7 @@ _lib.hils_decode_step_ml.argtypes = _lib.hils_decode_step_rq.argtypes[:7] + [_i6
 _lib.hils_sparse_attn_bwd_lf.argtypes = _lib.hils_sparse_attn_bwd_rq.argtypes
 _lib.hils_sparse_attn_fwd_ml.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64] + _lib.hils_sparse_attn_fwd.argtypes[4:]
 _lib.hils_sparse_attn_bwd_ml.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64] + _lib.hils_sparse_attn_bwd_rq.argtypes[5:]
-_lib.hils_decode_step_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _int, _vp, _vp,
+_lib.hils_decode_step_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _int, _vp, _vp,
                                         _vp, _i64, _i64, _i64, _i64, _i64, _f, _int, _vp, _sz, _vp]
 _lib.hils_decode_step_noalloc.argtypes = _lib.hils_decode_step.argtypes[:-3] + [_vp]
 _lib.hils_profile_enable.argtypes = [_int]
@@ -60,6 +60,7 @@ for _fn in ("hils_landmark_scores", "hils_topk_select", "hils_sparse_attn_fwd", 
     getattr(_lib, _fn).restype = _int
 
 OP_SCORES, OP_TOPK, OP_FWD, OP_DECODE, OP_BWD, OP_FWD_ML = range(6)
+WS_FP32 = 256  # OR into an operation code for fp32 inputs
 BF16, FP32 = 0, 1
 
 EXPORTS = ("hils_last_error", "hils_version", "hils_workspace_size", "hils_landmark_scores", "hils_topk_select",
@@ -129,8 +130,9 @@ def workspace_size(op: int, B, H, L, d, C, k) -> int:
     return n
 
 
-def _workspace(op, B, H, L, d, C, k, device, ws=None):
-    n = workspace_size(op, B, H, L, d, C, k)
+def _workspace(op, B, H, L, d, C, k, device, ws=None, dtype=None):
+    """dtype: the inputs' torch dtype; fp32 inputs keep fp32 per-pair intermediates (a larger workspace)."""
+    n = workspace_size(op | (WS_FP32 if dtype == torch.float32 else 0), B, H, L, d, C, k)
     if n == 0:
         return None, 0
     if ws is not None:
@@ -200,7 +202,7 @@ def sparse_attn_fwd(Q, K, V, K_lm, k, C=64, scale=None, idx=None, save_for_backw
     w = torch.empty_like(sel) if save_for_backward else None
     lse = torch.empty_like(sel) if save_for_backward else None
     O = out if out is not None else torch.empty_like(Q)
-    wsb, n = _workspace(OP_FWD, B, H, L, d, C, k, Q.device, ws)
+    wsb, n = _workspace(OP_FWD, B, H, L, d, C, k, Q.device, ws, Q.dtype)
     args = (_p(K), _p(V), _p(K_lm), _p(idx), _p(sel), select, _p(O), _p(w), _p(lse), B, H, L, d, C, k,
             _scale(d, scale), _dt(Q), _p(wsb), n, _stream())
     if Q_ret is None:
@@ -250,7 +252,7 @@ def sparse_attn_fwd_lf(Q, K, V, k, C=64, scale=None, idx=None, save_for_backward
     w = torch.empty_like(sel) if save_for_backward else None
     lse = torch.empty_like(sel) if save_for_backward else None
     O = out if out is not None else torch.empty_like(Q)
-    wsb, n = _workspace(OP_FWD, B, H, L, d, C, k, Q.device, ws)
+    wsb, n = _workspace(OP_FWD, B, H, L, d, C, k, Q.device, ws, Q.dtype)
     _check(_lib.hils_sparse_attn_fwd_lf(_p(Q), _p(Q_ret), _p(K), _p(V), _p(K_lm), _p(idx), _p(sel), select, _p(O),
                                         _p(w), _p(lse), B, H, L, d, C, k, _scale(d, scale), _dt(Q), _p(wsb), n,
                                         _stream()))
@@ -326,7 +328,7 @@ def sparse_attn_bwd(Q, K, V, K_lm, dO, idx, w, lse, k, C=64, scale=None, ws=None
         dKlm = torch.empty((B, H, L // C, d), **f32)
         if Q_ret is not None:
             dQr = torch.empty((B, H, L, d), **f32)
-    wsb, n = _workspace(OP_BWD, B, H, L, d, C, k, Q.device, ws)
+    wsb, n = _workspace(OP_BWD, B, H, L, d, C, k, Q.device, ws, Q.dtype)
     tail = (_p(dK), _p(dV), _p(dKlm), B, H, L, d, C, k, _scale(d, scale), _dt(Q), _p(wsb), n, _stream())
     head = (_p(K), _p(V), _p(K_lm), _p(dO), _p(idx), _p(w), _p(lse))
     if Q_ret is None:
@@ -347,7 +349,7 @@ def sparse_attn_bwd_lf(Q, K, V, K_lm, dO, idx, w, lse, k, C=64, scale=None, ws=N
     dQ, dK, dV = (torch.empty((B, H, L, d), **f32) for _ in range(3))
     dKlm = torch.empty((B, H, L // C, d), **f32)
     dQr = torch.empty((B, H, L, d), **f32) if Q_ret is not None else None
-    wsb, n = _workspace(OP_BWD, B, H, L, d, C, k, Q.device, ws)
+    wsb, n = _workspace(OP_BWD, B, H, L, d, C, k, Q.device, ws, Q.dtype)
     _check(_lib.hils_sparse_attn_bwd_lf(_p(Q), _p(Q_ret), _p(K), _p(V), _p(K_lm), _p(dO), _p(idx), _p(w), _p(lse),
                                         _p(dQ), _p(dQr), _p(dK), _p(dV), _p(dKlm), B, H, L, d, C, k, _scale(d, scale),
                                         _dt(Q), _p(wsb), n, _stream()))
@@ -359,14 +361,17 @@ def sparse_attn_bwd_lf(Q, K, V, K_lm, dO, idx, w, lse, k, C=64, scale=None, ws=N
 def decode_step_paged(q, k_new, v_new, K_pages, V_pages, K_lm_pages, page_table, n_ctx, n_ctx_max, k, C=64,
                       scale=None, ws=None, out=None, idx=None, w=None, q_ret=None, landmark_free=False):
     """One decode step of B sequences at their own positions n_ctx[b] (int64 device tensor [B]; n_ctx_max >= all
-    of them) over page pools K_pages / V_pages [P,H,64,d] and K_lm_pages [P,H,d], page_table int32 [B,max_pages]
-    (device).  Returns (o, idx, w); the pools are updated in place."""
+    of them) over page pools K_pages / V_pages [P,H,64,d] and K_lm_pages [P,H,d] (or [P,H,m,d]: m landmarks per
+    chunk, log-sum-exp chunk scores), page_table int32 [B,max_pages] (device).  Returns (o, idx, w); the pools are
+    updated in place."""
     _contig(q, k_new, v_new, K_pages, V_pages, K_lm_pages, page_table, n_ctx, q_ret)
     _like(q_ret, q, "q_ret")
     B, H, d = q.shape
     P = K_pages.shape[0]
-    if K_pages.shape != (P, H, C, d) or V_pages.shape != K_pages.shape or K_lm_pages.shape != (P, H, d):
-        raise ValueError("pools must be [P,H,C,d] (keys, values) and [P,H,d] (landmarks)")
+    m = K_lm_pages.shape[2] if K_lm_pages.dim() == 4 else 1
+    lm_shape = (P, H, m, d) if K_lm_pages.dim() == 4 else (P, H, d)
+    if K_pages.shape != (P, H, C, d) or V_pages.shape != K_pages.shape or K_lm_pages.shape != lm_shape:
+        raise ValueError("pools must be [P,H,C,d] (keys, values) and [P,H,d] or [P,H,m,d] (landmarks)")
     if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.shape[0] != B:
         raise ValueError("page_table must be int32 [B,max_pages]")
     if n_ctx.dtype != torch.int64 or tuple(n_ctx.shape) != (B,):
@@ -377,7 +382,7 @@ def decode_step_paged(q, k_new, v_new, K_pages, V_pages, K_lm_pages, page_table,
     w = w if w is not None else torch.empty((B, H, k + 1), dtype=torch.float32, device=q.device)
     wsb, n = _workspace(OP_DECODE, B, H, max_pages * C, d, C, k, q.device, ws)
     _check(_lib.hils_decode_step_paged(_p(q), _p(q_ret), _p(k_new), _p(v_new), _p(K_pages), _p(V_pages),
-                                       _p(K_lm_pages), _p(page_table), P, max_pages, _p(n_ctx), int(n_ctx_max),
+                                       _p(K_lm_pages), m, _p(page_table), P, max_pages, _p(n_ctx), int(n_ctx_max),
                                        1 if landmark_free else 0, _p(o), _p(idx), _p(w), B, H, d, C, k,
                                        _scale(d, scale), _dt(q), _p(wsb), n, _stream()))
     return o, idx, w
@@ -407,7 +412,7 @@ def sparse_attn_fwd_ml(Q, K, V, K_lm, k, C=64, scale=None, idx=None, save_for_ba
     w = torch.empty_like(sel) if save_for_backward else None
     lse = torch.empty_like(sel) if save_for_backward else None
     O = out if out is not None else torch.empty_like(Q)
-    wsb, n = _workspace(OP_FWD_ML, B, H, L, d, C, k, Q.device, ws)
+    wsb, n = _workspace(OP_FWD_ML, B, H, L, d, C, k, Q.device, ws, Q.dtype)
     _check(_lib.hils_sparse_attn_fwd_ml(_p(Q), _p(Q_ret), _p(K), _p(V), _p(K_lm), m, _p(idx), _p(sel), select, _p(O),
                                         _p(w), _p(lse), B, H, L, d, C, k, _scale(d, scale), _dt(Q), _p(wsb), n,
                                         _stream()))
@@ -425,7 +430,7 @@ def sparse_attn_bwd_ml(Q, K, V, K_lm, dO, idx, w, lse, k, C=64, scale=None, ws=N
     dQ, dK, dV = (torch.empty((B, H, L, d), **f32) for _ in range(3))
     dKlm = torch.empty((B, H, L // C, m, d), **f32)
     dQr = torch.empty((B, H, L, d), **f32) if Q_ret is not None else None
-    wsb, n = _workspace(OP_BWD, B, H, L, d, C, k, Q.device, ws)
+    wsb, n = _workspace(OP_BWD, B, H, L, d, C, k, Q.device, ws, Q.dtype)
     _check(_lib.hils_sparse_attn_bwd_ml(_p(Q), _p(Q_ret), _p(K), _p(V), _p(K_lm), m, _p(dO), _p(idx), _p(w), _p(lse),
                                         _p(dQ), _p(dQr), _p(dK), _p(dV), _p(dKlm), B, H, L, d, C, k, _scale(d, scale),
                                         _dt(Q), _p(wsb), n, _stream()))

@@ -157,7 +157,7 @@ def test_landmark_free_backward_validates(lib, hils):
 
 def test_paged_decode_validates(lib, hils):
     nd = hils.workspace_size(hils.OP_DECODE, 2, 2, 64 * 10, 64, 64, 4)
-    head = [FAKE] * 8
+    head = [FAKE] * 7 + [1, FAKE]  # ..., K_lm_pages, m = 1 landmark per chunk, page_table
     # n_ctx_max beyond the table, a zero-page pool, and a bad landmark_free flag
     assert lib.hils_decode_step_paged(*head, 5, 10, FAKE, 640, 0, FAKE, FAKE, FAKE, 2, 2, 64, 64, 4, 0.125, 0,
                                       FAKE, nd, None) == INVALID
@@ -168,6 +168,11 @@ def test_paged_decode_validates(lib, hils):
                                       FAKE, nd, None) == INVALID
     assert lib.hils_decode_step_paged(*head, 5, 10, FAKE, 100, 0, FAKE, FAKE, FAKE, 2, 2, 64, 64, 4, 0.125, 0,
                                       FAKE, nd - 16, None) == WORKSPACE
+    # landmarks per chunk: 1..16, and one only with landmark-free chunks
+    for m, lf, status in ((0, 0, UNSUPPORTED), (17, 0, UNSUPPORTED), (2, 1, INVALID)):
+        assert lib.hils_decode_step_paged(*([FAKE] * 7), m, FAKE, 5, 10, FAKE, 100, lf, FAKE, FAKE, FAKE, 2, 2, 64,
+                                          64, 4, 0.125, 0, FAKE, nd, None) == status
+        assert "landmark" in lib.hils_last_error().decode()
 
 
 def test_multi_landmark_forward_validates(lib, hils):

@@ -5,7 +5,7 @@ import torch
 
 import oracle
 from long_context_landmark_amd import synth
-from gpu_util import assert_close, dev, f32, say
+from gpu_util import assert_close, dev, f32, say, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -30,9 +30,9 @@ def test_bwd_parity(hils, gpu, dtype, B, H, L, d, k):
     x = synth.prefill_inputs(B, H, L, d, C=64, seed=300 + L + d, dtype=dtype, with_dO=True)
     O, idx, (dQ, dK, dV, dKlm) = _fwd_bwd(hils, x, k)
     ref = oracle.bwd(x["Q"], x["K"], x["V"], x["Klm"], x["dO"], idx.cpu().numpy(), 64, k)
-    tol = (5e-3, 3e-3) if dtype == "f32" else (2e-2, 1e-2)
+    bar = tol(dtype)
     for name, got in (("dQ", dQ), ("dK", dK), ("dV", dV), ("dKlm", dKlm)):
-        assert_close(f32(got), ref[name], name, *tol)
+        assert_close(f32(got), ref[name], name, *bar)
 
 
 def test_bwd_closed_forms_on_gpu(hils, gpu):

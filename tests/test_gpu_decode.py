@@ -5,7 +5,7 @@ import torch
 
 import oracle
 from long_context_landmark_amd import synth
-from gpu_util import GAP, assert_close, check_decode_step, dev, f32, host, say
+from gpu_util import GAP, assert_close, check_decode_step, dev, f32, host, say, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -65,8 +65,8 @@ def _run_decode(hils, x, k, steps, tol=(2e-2, 1e-2)):
 def test_decode_steps(hils, gpu, dtype, B, H, d, ctx, steps, k):
     say(f"decode dtype={dtype} B={B} H={H} d={d} ctx={ctx} steps={steps} k={k}")
     x = synth.decode_inputs(B, H, d, ctx, steps, C=64, seed=ctx + d, dtype=dtype)
-    tol = (5e-3, 3e-3) if dtype == "f32" else (2e-2, 1e-2)
-    _run_decode(hils, x, k, steps, tol=tol)
+    bar = tol(dtype)
+    _run_decode(hils, x, k, steps, tol=bar)
 
 
 @pytest.mark.parametrize("dtype,B,H,d,ctx,steps,k", [
@@ -78,8 +78,8 @@ def test_decode_steps_retrieval_query(hils, gpu, dtype, B, H, d, ctx, steps, k):
     """Decode with a separate retrieval query scoring the landmarks."""
     say(f"decode retrieval query dtype={dtype} B={B} H={H} d={d} ctx={ctx} steps={steps} k={k}")
     x = synth.decode_inputs(B, H, d, ctx, steps, C=64, seed=ctx + d + 7, dtype=dtype, with_qret=True)
-    tol = (5e-3, 3e-3) if dtype == "f32" else (2e-2, 1e-2)
-    _run_decode(hils, x, k, steps, tol=tol)
+    bar = tol(dtype)
+    _run_decode(hils, x, k, steps, tol=bar)
 
 
 def test_decode_equals_prefill_rows(hils, gpu):

@@ -10,14 +10,14 @@ import torch
 
 import oracle
 from long_context_landmark_amd import synth
-from gpu_util import assert_close, check_decode_step, check_selection, dev, f32, host, say, to_inputs
+from gpu_util import assert_close, check_decode_step, check_selection, dev, f32, host, say, to_inputs, tol
 from test_gpu_decode import past_scores_fn
 
 pytestmark = pytest.mark.gpu
 
 
 def _tol(dtype):
-    return (5e-3, 3e-3) if dtype == "f32" else (2e-2, 1e-2)
+    return tol(dtype)
 
 
 def _means_close(got, ref, dtype, what):

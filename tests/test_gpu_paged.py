@@ -9,12 +9,12 @@ import torch
 
 import oracle
 from long_context_landmark_amd import synth
-from gpu_util import assert_close, check_decode_step, dev, f32, host, say
+from gpu_util import assert_close, check_decode_step, dev, f32, host, say, tol
 
 pytestmark = pytest.mark.gpu
 
 
-def _build(B, H, d, ctxs, steps, dtype, lf, rq, seed):
+def _build(B, H, d, ctxs, steps, dtype, lf, rq, seed, m=1):
     C = 64
     rng = np.random.default_rng(seed)
     xs = [synth.decode_inputs(1, H, d, ctx, steps, C=C, seed=seed + b, dtype=dtype, with_qret=rq)
@@ -27,10 +27,15 @@ def _build(B, H, d, ctxs, steps, dtype, lf, rq, seed):
     etype = xs[0]["K_cache"].dtype
     Kp = np.zeros((total, H, C, d), etype)
     Vp = np.zeros_like(Kp)
-    Lp = np.zeros((total, H, d), etype)
+    Lp = np.zeros((total, H) + ((m, d) if m > 1 else (d,)), etype)
     nxt = 0
     for b, x in enumerate(xs):
         Klm_b = x["Klm"].copy()
+        if m > 1:
+            # several landmarks per chunk: the given row and m - 1 further N(0,1) rows
+            extra = rng.standard_normal(Klm_b.shape[:3] + (m - 1, d), dtype=np.float32)
+            extra = synth.f32_to_bf16_bits(extra) if dtype == "bf16" else extra
+            Klm_b = np.concatenate([Klm_b[:, :, :, None], extra], axis=3)
         if lf:
             Klm_b[:] = 0
             oracle.chunk_means(x["K_cache"], C, nchunks=ctxs[b] // C, Klm=Klm_b)
@@ -46,21 +51,25 @@ def _build(B, H, d, ctxs, steps, dtype, lf, rq, seed):
     return xs, Kp, Vp, Lp, table
 
 
-@pytest.mark.parametrize("dtype,H,d,ctxs,steps,k,lf,rq", [
-    ("bf16", 2, 64, [64 * 40 + 10, 64 * 7 + 60, 3], 70, 4, False, False),
-    ("bf16", 2, 128, [64 * 300 + 62, 64 * 2, 64 * 17 + 33], 4, 16, False, True),
-    ("bf16", 2, 64, [64 * 25 + 50, 64 * 9 + 1], 30, 8, True, True),
-    ("f32", 1, 64, [64 * 20, 64 * 3 + 63], 20, 4, True, False),
+@pytest.mark.parametrize("dtype,H,d,ctxs,steps,k,lf,rq,m", [
+    ("bf16", 2, 64, [64 * 40 + 10, 64 * 7 + 60, 3], 70, 4, False, False, 1),
+    ("bf16", 2, 128, [64 * 300 + 62, 64 * 2, 64 * 17 + 33], 4, 16, False, True, 1),
+    ("bf16", 2, 64, [64 * 25 + 50, 64 * 9 + 1], 30, 8, True, True, 1),
+    ("f32", 1, 64, [64 * 20, 64 * 3 + 63], 20, 4, True, False, 1),
+    # several landmarks per page: log-sum-exp chunk scores
+    ("bf16", 2, 64, [64 * 40 + 10, 64 * 7 + 60, 3], 70, 4, False, False, 2),
+    ("bf16", 2, 128, [64 * 300 + 62, 64 * 17 + 33], 4, 16, False, True, 3),
+    ("f32", 1, 64, [64 * 20, 64 * 3 + 63], 20, 4, False, False, 2),
 ])
-def test_decode_paged(hils, gpu, dtype, H, d, ctxs, steps, k, lf, rq):
+def test_decode_paged(hils, gpu, dtype, H, d, ctxs, steps, k, lf, rq, m):
     B = len(ctxs)
-    say(f"paged decode dtype={dtype} B={B} H={H} d={d} ctx={ctxs} steps={steps} k={k} lf={lf} retrieval={rq}")
-    xs, Kp, Vp, Lp, table = _build(B, H, d, ctxs, steps, dtype, lf, rq, seed=700 + d + steps)
+    say(f"paged decode dtype={dtype} B={B} H={H} d={d} ctx={ctxs} steps={steps} k={k} lf={lf} retrieval={rq} m={m}")
+    xs, Kp, Vp, Lp, table = _build(B, H, d, ctxs, steps, dtype, lf, rq, seed=700 + d + steps + m, m=m)
     Kp_g, Vp_g, Lp_g = dev(Kp), dev(Vp), dev(Lp)
     table_g = torch.from_numpy(table).to(gpu)
     maxp = table.shape[1]
     ws = torch.empty(hils.workspace_size(hils.OP_DECODE, B, H, maxp * 64, d, 64, k), dtype=torch.uint8, device=gpu)
-    tol = (5e-3, 3e-3) if dtype == "f32" else (2e-2, 1e-2)
+    bar = tol(dtype)
     near = 0
     for s in range(steps):
         pos = np.array([ctx + s for ctx in ctxs], np.int64)
@@ -83,11 +92,14 @@ def test_decode_paged(hils, gpu, dtype, H, d, ctxs, steps, k, lf, rq):
             c = own[bh]
             qf = synth.as_f32((qr if rq else q)[b, h]).astype(np.float64)
             lm = synth.as_f32(np.stack([Lp[table[b, j], h] for j in range(c)])).astype(np.float64)
-            return (lm @ qf / np.sqrt(d)).astype(np.float32)
+            sc = lm @ qf / np.sqrt(d)
+            if m > 1:  # log-sum-exp over the chunk's landmarks
+                sc = np.log(np.exp(sc - sc.max(1, keepdims=True)).sum(1)) + sc.max(1)
+            return sc.astype(np.float32)
 
         near += check_decode_step(f"step {s}", idx.cpu().numpy().reshape(B * H, k + 1),
                                   f32(w).reshape(B * H, k + 1), f32(o).reshape(B * H, d), ref, step, own, past, k,
-                                  tol)
+                                  bar)
     say(f"  rows with near-tie selection differences: {near}")
     np.testing.assert_array_equal(host(Kp_g), Kp)
     np.testing.assert_array_equal(host(Vp_g), Vp)

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from long_context_landmark_amd import synth
-from gpu_util import assert_close, check_selection, dev, f32, say, to_inputs
+from gpu_util import assert_close, check_selection, dev, f32, say, to_inputs, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -22,7 +22,7 @@ CASES = [
 
 
 def _tol(dtype):
-    return (5e-3, 3e-3) if dtype == "f32" else (2e-2, 1e-2)
+    return tol(dtype)
 
 
 @pytest.mark.parametrize("dtype,B,H,L,d,k", CASES)
