@@ -47,10 +47,11 @@ KERNEL_SOURCES = {
     "dq_reduce": "attn_bwd.hip", "klm_bwd": "attn_bwd.hip", "route_scatter": "route.hip",
 }
 MEASURED_TRAFFIC = {
-    # workload: (kernel, FETCH_SIZE KiB, WRITE_SIZE KiB, source digest)
-    "prefill_8k": ("chunk_attn_fwd", 28618.8, 130579.2, "60362ff8b0b62b97"),
-    "prefill_128k": ("chunk_attn_fwd", 8509578.3, 17019386.8, "60362ff8b0b62b97"),
-    "train_8k": ("chunk_bwd", 238209.6, 901965.7, "e41e7d56f1d29212"),
+    # workload: {kernel: (FETCH_SIZE KiB, WRITE_SIZE KiB, source digest)}
+    "prefill_8k": {"chunk_attn_fwd": (28610.9, 130576.7, "d738d5d7972bc681"), "topk_select": (8454.7, 15328.7, "686dc6a7ef55ace2"), "own_combine": (92229.6, 16384.0, "d738d5d7972bc681")},
+    "prefill_128k": {"chunk_attn_fwd": (8510089.2, 17019389.7, "d738d5d7972bc681"), "topk_select": (541200.8, 965867.7, "686dc6a7ef55ace2"), "own_combine": (10197157.1, 1048576.0, "d738d5d7972bc681")},
+    "train_8k": {"chunk_bwd": (238497.0, 902758.0, "8ec357276b6307ad"), "chunk_attn_fwd": (105706.3, 522486.2, "d738d5d7972bc681"), "dq_reduce": (326656.0, 149723.1, "8ec357276b6307ad")},
+    "decode_512k": {"decode_scan": (8264.2, 68.0, "fa936788aff386d3"), "decode_attend": (2434.6, 34.1, "fa936788aff386d3")},
 }
 
 
@@ -67,10 +68,10 @@ def kernel_source_digest(kernel):
 
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of the kernel from the recorded counters, or None."""
-    rec = MEASURED_TRAFFIC.get(workload)
-    if rec is None or rec[0] != kernel or kernel_source_digest(kernel) != rec[3]:
+    rec = MEASURED_TRAFFIC.get(workload, {}).get(kernel)
+    if rec is None or kernel_source_digest(kernel) != rec[2]:
         return None
-    return round((rec[1] * COUNTER_SCALE["FETCH_SIZE"] + rec[2] * COUNTER_SCALE["WRITE_SIZE"]) * 1024)
+    return round((rec[0] * COUNTER_SCALE["FETCH_SIZE"] + rec[1] * COUNTER_SCALE["WRITE_SIZE"]) * 1024)
 
 
 # ----------------------------------------------------------------------------- algorithmic work
@@ -790,8 +791,8 @@ def main():
             log("[bench] cpu baseline (oracle): prefill_128k, 2 heads")
             extra["prefill_128k"]["cpu_baseline"] = cpu_baseline_prefill_heads(synth, "prefill_128k", 2)
         if "decode_512k" in extra:
-            log("[bench] cpu baseline (oracle): decode_512k, 4 heads, 16 steps")
-            extra["decode_512k"]["cpu_baseline"] = cpu_baseline_decode(synth, "decode_512k", 4, 16)
+            log("[bench] cpu baseline (oracle): decode_512k, 4 heads, 64 steps")
+            extra["decode_512k"]["cpu_baseline"] = cpu_baseline_decode(synth, "decode_512k", 4, 64)
         if "train_8k" in extra:
             log("[bench] cpu baseline (oracle): train_8k, 1 sequence")
             extra["train_8k"]["cpu_baseline"] = cpu_baseline_train(synth, "train_8k", 1)
