@@ -481,9 +481,12 @@ def bench_decode(hils, synth, name, replicas, warmup, lf=False, ml=False, eager_
         "timing": "every step of every replica captured in one HIP graph, replayed once",
         "hbm_gbs": work["bytes"] / (us * 1e-6) / 1e9,
         "hbm_frac": work["bytes"] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+        "step_roofline": step_fractions(work, us * 1e-3),
         "bytes_per_token": work["bytes"],
         "calls": calls,
         "wall_s": wall,
+        # each kernel bracketed by HIP events on its stream: for kernels of a few microseconds the bracket adds
+        # the launch's dispatch latency, so these exceed the kernels' own durations (rocprofv3 gives those)
         "kernel_us": {n: round(t / c * 1e3, 3) for n, (t, c) in kt.items()},
         "roofline": roofline(kt, work, {n: 1 for n in kt}, None if lf or ml else name),
         "config": {"workload": name, "B": B, "H": H, "d": d, "context": w.L, "steps": w.steps, "k": w.k,
