@@ -61,6 +61,7 @@ def _run_decode(hils, x, k, steps, tol=(2e-2, 1e-2)):
     ("bf16", 1, 3, 64, 5, 64, 8),              # first chunk only, then c = 1
     ("f32", 1, 2, 64, 64 * 20, 20, 4),
     ("f32", 1, 1, 128, 64 * 150 + 7, 4, 16),
+    ("bf16", 1, 3, 64, 64 * 600 + 61, 5, 1),  # top-1: crosses into a fresh chunk, three scan slices
 ])
 def test_decode_steps(hils, gpu, dtype, B, H, d, ctx, steps, k):
     say(f"decode dtype={dtype} B={B} H={H} d={d} ctx={ctx} steps={steps} k={k}")

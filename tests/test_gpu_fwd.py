@@ -40,6 +40,10 @@ CASES = [
     ("f32", 1, 1, 2048, 128, 8, "iid"),
     ("bf16", 1, 2, 19200, 64, 16, "iid"),  # 300 chunks: the multi-tile two-sweep selection
     ("bf16", 1, 1, 12352, 128, 8, "chunkmean"),  # 193 chunks, d=128
+    ("bf16", 1, 2, 64 * 129, 64, 16, "iid"),  # 129 chunks: the largest short-list selection, m up to 16
+    ("bf16", 1, 2, 64 * 130, 64, 8, "chunkmean"),  # 130 chunks: the long-list selection with three tiles
+    ("bf16", 1, 3, 4096, 64, 1, "iid"),  # top-1, three heads (no XCD remap)
+    ("bf16", 3, 1, 2048, 128, 1, "chunkmean"),  # top-1 at d = 128, three sequences
 ]
 
 
