@@ -166,6 +166,11 @@ __device__ __forceinline__ uint64_t make_key(float s, int32_t j) {
 __device__ __forceinline__ int32_t key_index(uint64_t key) { return (int32_t)(0xFFFFFFFFu - (uint32_t)key); }
 __device__ __forceinline__ float key_score(uint64_t key) { return unordered_float((uint32_t)(key >> 32)); }
 
+// A compile-time integer passed as a value (selects an unrolled variant of a generic lambda).
+template <int N> struct IntC {
+  static constexpr int value = N;
+};
+
 template <typename K> __device__ __forceinline__ void cmpswap_desc(K& a, K& b) {
   K hi = a > b ? a : b;
   K lo = a > b ? b : a;

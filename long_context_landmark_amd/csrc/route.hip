@@ -82,13 +82,17 @@ template <int NW = 4> __device__ int block_excl_scan(int v, int* buf, int* total
   return before + incl - v;
 }
 
-__global__ __launch_bounds__(256) void route_scan_kernel(int* __restrict__ counts, int* __restrict__ chunk_off,
-                                                         int4* __restrict__ items, int* __restrict__ n_items, int N,
-                                                         int nseg, int ppi, int max_items) {
-  __shared__ int buf[256];
+// One 1024-thread workgroup per (b,h): a thread per chunk forms that chunk's per-segment offsets
+// (its column of the counts, read 32 segments at a time), then block scans give the chunk offsets
+// and the work items; long sequences take N / 1024 such rounds.
+constexpr int ROUTE_SCAN_T = 1024;
+__global__ __launch_bounds__(ROUTE_SCAN_T) void route_scan_kernel(int* __restrict__ counts, int* __restrict__ chunk_off,
+                                                                  int4* __restrict__ items, int* __restrict__ n_items,
+                                                                  int N, int nseg, int ppi, int max_items) {
+  __shared__ int buf[ROUTE_SCAN_T / 64];
   const int bh = blockIdx.x, tid = threadIdx.x;
   int carry_p = 0, carry_i = 0;
-  for (int base = 0; base < N; base += 256) {
+  for (int base = 0; base < N; base += ROUTE_SCAN_T) {
     const int j = base + tid;
     int tot = 0;
     if (j < N) {
@@ -105,8 +109,8 @@ __global__ __launch_bounds__(256) void route_scan_kernel(int* __restrict__ count
     }
     const int nit = (tot + ppi - 1) / ppi;
     int sum_p, sum_i;
-    const int ex_p = block_excl_scan(tot, buf, &sum_p);
-    const int ex_i = block_excl_scan(nit, buf, &sum_i);
+    const int ex_p = block_excl_scan<ROUTE_SCAN_T / 64>(tot, buf, &sum_p);
+    const int ex_i = block_excl_scan<ROUTE_SCAN_T / 64>(nit, buf, &sum_i);
     if (j < N) {
       const int off = carry_p + ex_p;
       chunk_off[(int64_t)bh * (N + 1) + j] = off;
@@ -462,7 +466,7 @@ hipError_t launch_route(const int32_t* idx, const RouteBufs& rb, int BH, int L, 
                   rb.seg_q, rb.pairs_per_item, rb.max_items);
     return hipGetLastError();
   }
-  HILS_LAUNCH("route_scan", route_scan_kernel, dim3(BH), dim3(256), 0, st, rb.counts, rb.chunk_off, rb.items, rb.n_items, N,
+  HILS_LAUNCH("route_scan", route_scan_kernel, dim3(BH), dim3(ROUTE_SCAN_T), 0, st, rb.counts, rb.chunk_off, rb.items, rb.n_items, N,
                      rb.nseg, rb.pairs_per_item, rb.max_items);
   if (N <= ROUTE_STAGED_MAX_N && rb.seg_q * k <= 16384) {
     // more than 64 KiB of dynamic LDS per workgroup is opted into once per device

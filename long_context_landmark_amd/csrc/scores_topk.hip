@@ -381,40 +381,47 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
       sweep([&](int tile, f32x4_t(&acc)[4]) { survive(tile, acc); });
     }
     __syncthreads();
-    // exact top-m among the survivors: 4 lanes per query, 16 slots each.  When every query
-    // of the wavefront has at most 16 (or 32) survivors, one (two) of its lanes hold them all
-    // and the merges between lanes that hold nothing are skipped.
+    // exact top-m among the survivors by rank: a key's rank is the number of the query's
+    // survivors above it (keys are distinct, so ranks are too).  The four lanes of a query take
+    // its slots in turn (slot part + 4 i) and compare each with every survivor of the query;
+    // each key of rank below m then goes to that row of the sorted list.  NO, the slots a lane
+    // holds, follows the largest survivor count of the wavefront, so the comparisons number
+    // about n * n / 4 per lane.
     {
       const int q = tid >> 2, part = tid & 3;
-      const int n = cnt_s[q];
+      const int cn = cnt_s[q];
+      const int n = min(cn, TK_CAP);
       int nmax = n;
 #pragma unroll
       for (int msk = 1; msk < 64; msk <<= 1) nmax = max(nmax, lane_xor(nmax, msk));
-      uint64_t v[16];
-      if (nmax <= 8) {
-        // at most 8 survivors per query (the common case for k <= 8): they sit in the first
-        // 8 slots of part 0; an 8-input network sorts them
+      uint64_t own[TK_CAP / 4];
+      int rk[TK_CAP / 4];
+      auto rank_slots = [&](auto no_c) {
+        constexpr int NO = decltype(no_c)::value;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (part == 0 && e < n) ? surv[q][e] : 0ull;
-        sort8_desc(v);
-#pragma unroll
-        for (int e = 8; e < 16; ++e) v[e] = 0ull;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int p = 16 * part + e;
-          v[e] = (p < n && p < TK_CAP) ? surv[q][p] : 0ull;
+        for (int i = 0; i < NO; ++i) {
+          const int p = part + 4 * i;
+          own[i] = p < n ? surv[q][p] : 0ull;
+          rk[i] = 0;
         }
-        sort16_desc(v);
-        if (nmax > 16) merge16_with_lane(v, 1);
-        if (nmax > 32) merge16_with_lane(v, 2);
-      }
-      __syncthreads();  // every survivor has been read: the sorted keys overwrite the buffer
-      if (part == 0) {
+        for (int e = 0; e < nmax; ++e) {
+          const uint64_t y = e < n ? surv[q][e] : 0ull;  // 0 is below every key
 #pragma unroll
-        for (int e = 0; e < 16; ++e) top_s[q][e] = v[e];
-        if (n > TK_CAP) atomicOr(&ovf_s, 1);
+          for (int i = 0; i < NO; ++i) rk[i] += y > own[i] ? 1 : 0;
+        }
+      };
+      const int no = nmax <= 8 ? 2 : (nmax <= 16 ? 4 : (nmax <= 32 ? 8 : TK_CAP / 4));  // wavefront-uniform
+      if (no == 2) rank_slots(IntC<2>{});
+      else if (no == 4) rank_slots(IntC<4>{});
+      else if (no == 8) rank_slots(IntC<8>{});
+      else rank_slots(IntC<TK_CAP / 4>{});
+      __syncthreads();  // every survivor has been read: the sorted keys overwrite the buffer
+#pragma unroll
+      for (int i = 0; i < TK_CAP / 4; ++i) {
+        const int p = part + 4 * i;
+        if (i < no && p < n && rk[i] < m) top_s[q][rk[i]] = own[i];
       }
+      if (part == 0 && cn > TK_CAP) atomicOr(&ovf_s, 1);
     }
     __syncthreads();
     if (ovf_s) {
