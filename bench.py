@@ -48,10 +48,10 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: {kernel: (FETCH_SIZE KiB, WRITE_SIZE KiB, source digest)}
-    "prefill_8k": {"chunk_attn_fwd": (28610.9, 130576.7, "d738d5d7972bc681"), "topk_select": (8454.7, 15328.7, "686dc6a7ef55ace2"), "own_combine": (92229.6, 16384.0, "d738d5d7972bc681")},
-    "prefill_128k": {"chunk_attn_fwd": (8510089.2, 17019389.7, "d738d5d7972bc681"), "topk_select": (541200.8, 965867.7, "686dc6a7ef55ace2"), "own_combine": (10197157.1, 1048576.0, "d738d5d7972bc681")},
-    "train_8k": {"chunk_bwd": (238497.0, 902758.0, "8ec357276b6307ad"), "chunk_attn_fwd": (105706.3, 522486.2, "d738d5d7972bc681"), "dq_reduce": (326656.0, 149723.1, "8ec357276b6307ad")},
-    "decode_512k": {"decode_scan": (8264.2, 68.0, "fa936788aff386d3"), "decode_attend": (2434.6, 34.1, "fa936788aff386d3")},
+    "prefill_8k": {"chunk_attn_fwd": (28596.6, 130578.3, "292684829ec4835a"), "topk_select": (8442.5, 13824.0, "26f18bf8fd748134"), "own_combine": (92229.9, 16384.0, "292684829ec4835a")},
+    "prefill_128k": {"chunk_attn_fwd": (8509413.1, 17018062.2, "292684829ec4835a"), "topk_select": (541259.3, 835622.3, "26f18bf8fd748134"), "own_combine": (10197156.4, 1048576.0, "292684829ec4835a")},
+    "train_8k": {"chunk_bwd": (238657.8, 903003.5, "9efa9c46f334b4d3"), "chunk_attn_fwd": (105706.4, 522511.8, "292684829ec4835a"), "dq_reduce": (326658.6, 149704.0, "9efa9c46f334b4d3")},
+    "decode_512k": {"decode_scan": (8264.2, 68.0, "8aa435acddc0f2e9"), "decode_attend": (2434.6, 34.1, "8aa435acddc0f2e9")},
 }
 
 
