@@ -369,8 +369,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
             x = b3 ? u1 : u0;
           }
           const int q = 16 * (e >> 2) + r16;
+          // the key is formed while the slot is fetched, and stored without a branch: a value
+          // past the slots goes to the row's padding entry (never read; the count records it)
+          const uint64_t key = make_key(scale * x, jb + (e & 3));
           const int p = atomicAdd(&cnt_s[q], 1);
-          if (p < TK_CAP) surv[q][p] = make_key(scale * x, jb + (e & 3));
+          surv[q][p < TK_CAP ? p : TK_CAP] = key;
         }
       }
     };
