@@ -170,8 +170,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
   const int ntile = (c + 63) / 64;
   // scores of chunks tile*64 + 16w + 4g + i (i = 0..3) for queries 16qb + r16; the landmark
   // fragments of the next tile are loaded while the current one is on the MFMA units
-  // rows past the candidates (j >= c) load row c-1 instead: their scores are never used, and
-  // unconditional loads let the compiler wait for exactly the tile it needs
+  // rows past chunk c load row c instead (row c itself gives the own-chunk score, the others
+  // are never used), and unconditional loads let the compiler wait for exactly the tile it needs
   // In the fragment-order copy every tile below ceil(c/64) is whole; its rows at or past c
   // (later chunks, or zero padding) are scored but never used.
   auto load_tile = [&](int tile, Frag<T>(&a)[D / 32]) {
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) a[ks].load(fp + ks * 64 * 8);
     } else {
-      const int jrow = min(tile * 64 + 16 * w + r16, c - 1);
+      const int jrow = min(tile * 64 + 16 * w + r16, c);
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) a[ks].load(Kb + (int64_t)jrow * D + ks * 32 + 8 * g);
     }
@@ -231,11 +231,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
     load_tile(tile_at(0), first_tile);
     if constexpr (SMALL) load_tile(min(1, ntile - 1), second_tile);
   }
-  // own-chunk scores from the query fragments already held (wave 0): lane (r16, g) takes
-  // the elements 8g.. of every 32-element step of query 16 qb + r16, the four lane groups
-  // then add their partial products
+  // own-chunk scores.  When chunk c lies in the last candidate tile (c not a multiple of 64) the
+  // first sweep's products hold them: the lane that holds (query, c) stores them.  Otherwise
+  // wave 0 forms them from the query fragments already held: lane (r16, g) takes the elements
+  // 8g.. of every 32-element step of query 16 qb + r16, the four lane groups then add their
+  // partial products.
   __shared__ float own_s[64];
-  if (w == 0) {
+  const bool own_in_tile = (c & 63) != 0;
+  if (!own_in_tile && w == 0) {
     Frag<T> lf[D / 32];
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) lf[ks].load(Kb + (int64_t)c * D + ks * 32 + 8 * g);
@@ -279,6 +282,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
           if (j < c) {
 #pragma unroll
             for (int qb = 0; qb < 4; ++qb) gm[qb][i] = fmaxf(gm[qb][i], acc[qb][i]);
+          } else if (j == c) {  // the last, partial tile holds the own chunk
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb) own_s[16 * qb + r16] = scale * acc[qb][i];
           }
         }
       }
