@@ -403,8 +403,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
       int nmax = n;
 #pragma unroll
       for (int msk = 1; msk < 64; msk <<= 1) nmax = max(nmax, lane_xor(nmax, msk));
+      // every entry is defined (rank TK_CAP: never kept), also those past the unrolled count
       uint64_t own[TK_CAP / 4];
       int rk[TK_CAP / 4];
+#pragma unroll
+      for (int i = 0; i < TK_CAP / 4; ++i) {
+        own[i] = 0ull;
+        rk[i] = TK_CAP;
+      }
       auto rank_slots = [&](auto no_c) {
         constexpr int NO = decltype(no_c)::value;
 #pragma unroll
