@@ -151,6 +151,23 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_kernel(const int32_t* _
   const int* so = segoff + ((int64_t)bh * nseg + seg) * N;
   const int* co = chunk_off + (int64_t)bh * (N + 1);
   __shared__ int so_s[FUSED ? ROUTE_FUSED_MAX_N : 1], co_s[FUSED ? ROUTE_FUSED_MAX_N : 1];
+  const int t0 = seg * seg_q, t1 = min(L, t0 + seg_q);
+  const int qpw = (seg_q + NW - 1) / NW;
+  const int tw0 = min(t1, t0 + wv * qpw), tw1 = min(t1, tw0 + qpw);
+  const int total = (tw1 - tw0) * k;
+  const int32_t* idx_w = idx + ((int64_t)bh * L + tw0) * (k + 1);
+  // short sequences: the wave's chunk ids (at most 256 queries x 16 slots per segment) are read
+  // once, for the histogram and the ranking, and requested before the counts so that the two
+  // memory round trips overlap
+  constexpr int UBF = FUSED ? 256 * 16 / (NW * 64) : 1;
+  int jr[UBF];
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int u = 0; u < UBF; ++u) {
+      const int f = u * 64 + lane;
+      jr[u] = f < total ? idx_w[(f / k) * (k + 1) + f % k] : -1;
+    }
+  }
   if constexpr (FUSED) {
     static_assert(64 * NW >= ROUTE_FUSED_MAX_N, "one thread per chunk");
     __shared__ int buf[NW];
@@ -188,23 +205,7 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_kernel(const int32_t* _
   }
   auto seg_off = [&](int j) { if constexpr (FUSED) return so_s[j]; else return so[j]; };
   auto chunk_start = [&](int j) { if constexpr (FUSED) return co_s[j]; else return co[j]; };
-  const int t0 = seg * seg_q, t1 = min(L, t0 + seg_q);
-  const int qpw = (seg_q + NW - 1) / NW;
-  const int tw0 = min(t1, t0 + wv * qpw), tw1 = min(t1, tw0 + qpw);
-  const int total = (tw1 - tw0) * k;
-  const int32_t* idx_w = idx + ((int64_t)bh * L + tw0) * (k + 1);
   int* cur = cur_all + wv * N;
-  // short sequences: the wave's chunk ids (at most 256 queries x 16 slots per segment) are read
-  // once, for the histogram and the ranking
-  constexpr int UBF = FUSED ? 256 * 16 / (NW * 64) : 1;
-  int jr[UBF];
-  if constexpr (FUSED) {
-#pragma unroll
-    for (int u = 0; u < UBF; ++u) {
-      const int f = u * 64 + lane;
-      jr[u] = f < total ? idx_w[(f / k) * (k + 1) + f % k] : -1;
-    }
-  }
   if constexpr (NW > 1) {
     for (int i = tid; i < NW * N; i += 64 * NW) cur_all[i] = 0;
     __syncthreads();

@@ -403,14 +403,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
       int nmax = n;
 #pragma unroll
       for (int msk = 1; msk < 64; msk <<= 1) nmax = max(nmax, lane_xor(nmax, msk));
-      // every entry is defined (rank TK_CAP: never kept), also those past the unrolled count
+      // entries 0 .. NO-1 are formed and read by the variant of the same NO
       uint64_t own[TK_CAP / 4];
       int rk[TK_CAP / 4];
-#pragma unroll
-      for (int i = 0; i < TK_CAP / 4; ++i) {
-        own[i] = 0ull;
-        rk[i] = TK_CAP;
-      }
       auto rank_slots = [&](auto no_c) {
         constexpr int NO = decltype(no_c)::value;
 #pragma unroll
@@ -425,17 +420,22 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
           for (int i = 0; i < NO; ++i) rk[i] += y > own[i] ? 1 : 0;
         }
       };
+      auto place_slots = [&](auto no_c) {
+        constexpr int NO = decltype(no_c)::value;
+#pragma unroll
+        for (int i = 0; i < NO; ++i)
+          if (part + 4 * i < n && rk[i] < m) top_s[q][rk[i]] = own[i];
+      };
       const int no = nmax <= 8 ? 2 : (nmax <= 16 ? 4 : (nmax <= 32 ? 8 : TK_CAP / 4));  // wavefront-uniform
       if (no == 2) rank_slots(IntC<2>{});
       else if (no == 4) rank_slots(IntC<4>{});
       else if (no == 8) rank_slots(IntC<8>{});
       else rank_slots(IntC<TK_CAP / 4>{});
       __syncthreads();  // every survivor has been read: the sorted keys overwrite the buffer
-#pragma unroll
-      for (int i = 0; i < TK_CAP / 4; ++i) {
-        const int p = part + 4 * i;
-        if (i < no && p < n && rk[i] < m) top_s[q][rk[i]] = own[i];
-      }
+      if (no == 2) place_slots(IntC<2>{});
+      else if (no == 4) place_slots(IntC<4>{});
+      else if (no == 8) place_slots(IntC<8>{});
+      else place_slots(IntC<TK_CAP / 4>{});
       if (part == 0 && cn > TK_CAP) atomicOr(&ovf_s, 1);
     }
     __syncthreads();
