@@ -303,8 +303,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? (D == 64 ? 4 : 3) : 1) void c
         }
       }
     }
-    // the four lane groups hold the same row statistics; only the backward reads them
-    if (lse_pair) *(ok ? lse_pair + prow : trash_lse) = mx + __logf(sum);
+    // the four lane groups hold the same row statistics
+    *(ok ? lse_pair + prow : trash_lse) = mx + __logf(sum);
   };
   Frag<T> q0[D / 32], q1[D / 32], q2[D / 32];
   int pe0 = pair_ok(p0) ? pair_raw(p0) : -1;

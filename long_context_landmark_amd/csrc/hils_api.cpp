@@ -353,9 +353,8 @@ static hils_status fwd_impl(const void* Q, const void* Q_ret, const void* K, con
     return hip_status(e, "hils_sparse_attn_fwd: own chunk landmarks");
   if ((e = hils::launch_route(idx, W.rb, BH, iL, iN, ik, s)) != hipSuccess)
     return hip_status(e, "hils_sparse_attn_fwd: routing");
-  // the per-pair log-partitions are kept only for the backward (lse requested)
-  if ((e = hils::launch_chunk_attn_fwd(dt, id, Q, K, V, W.rb, lse_out ? W.lse_pair : nullptr, W.partial, W.trash,
-                                       W.trash_lse, BH, iL, iN, ik, scale, s)) != hipSuccess)
+  if ((e = hils::launch_chunk_attn_fwd(dt, id, Q, K, V, W.rb, W.lse_pair, W.partial, W.trash, W.trash_lse, BH, iL,
+                                       iN, ik, scale, s)) != hipSuccess)
     return hip_status(e, "hils_sparse_attn_fwd: chunk attention");
   if ((e = hils::launch_own_combine(dt, id, Q, K, V, W.rb.pos_of, w, W.partial, W.lse_pair, O, lse_out, BH, iL, iN,
                                     ik, scale, s)) != hipSuccess)
