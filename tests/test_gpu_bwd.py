@@ -35,6 +35,19 @@ def test_bwd_parity(hils, gpu, dtype, B, H, L, d, k):
         assert_close(f32(got), ref[name], name, *bar)
 
 
+@pytest.mark.timeout(300)
+def test_bwd_beyond_2048_chunks(hils, gpu):
+    """More than 2048 chunks per sequence (the routing's one-wavefront scatter, long candidate lists):
+    every gradient against the oracle on the GPU's selection."""
+    B, H, L, d, k = 1, 1, 64 * 2304, 64, 4
+    say(f"long bwd B={B} H={H} L={L} d={d} k={k}")
+    x = synth.prefill_inputs(B, H, L, d, C=64, seed=2304, dtype="bf16", with_dO=True)
+    O, idx, (dQ, dK, dV, dKlm) = _fwd_bwd(hils, x, k)
+    ref = oracle.bwd(x["Q"], x["K"], x["V"], x["Klm"], x["dO"], idx.cpu().numpy(), 64, k)
+    for name, got in (("dQ", dQ), ("dK", dK), ("dV", dV), ("dKlm", dKlm)):
+        assert_close(f32(got), ref[name], name)
+
+
 def test_bwd_closed_forms_on_gpu(hils, gpu):
     """Sums fixed by the invariances of the operator hold for the GPU gradients."""
     B, H, L, d, k = 1, 2, 2048, 64, 8

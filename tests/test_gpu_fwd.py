@@ -212,7 +212,7 @@ def test_workload_prefill_128k_sampled(hils, gpu):
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("N,d,k", [(2304, 64, 8), (4100, 128, 16)])
+@pytest.mark.parametrize("N,d,k", [(2304, 64, 8), (4100, 128, 16), (16384, 64, 4)])  # 16384: the largest accepted
 def test_fwd_beyond_2048_chunks_sampled(hils, gpu, N, d, k):
     """More than 2048 chunks per sequence (the routing's one-wavefront scatter, long top-k candidate lists):
     sampled rows including chunk boundaries against the oracle, and two runs bitwise equal."""
