@@ -18,7 +18,7 @@
 // (chunk index mod 64).  The m-th largest of those maxima is a lower bound on
 // the m-th largest score (the maxima are m distinct candidates), so a second
 // sweep, which recomputes bit-identical scores, only has to keep candidates at
-// or above it.  The exact top-m is then sorted out of the few survivors.  A
+// or above it.  The exact top-m is then ranked out of the few survivors.  A
 // query with more survivors than fit in LDS (possible only with many exactly
 // tied scores) falls back to m exact arg-max sweeps.
 #include "hils_device.h"
@@ -120,7 +120,7 @@ __device__ __forceinline__ float least_raw_bound(float t, float s) {
   return a;
 }
 
-constexpr int TK_CAP = 64;  // survivor slots per query (16 per sorting lane)
+constexpr int TK_CAP = 64;  // survivor slots per query (16 per ranking lane)
 constexpr int TK_SMALL_N = 129;  // up to this many chunks a query chunk has at most two candidate tiles
 
 // One workgroup per (b,h, query chunk c): the 64 queries t = 64c .. 64c+63
