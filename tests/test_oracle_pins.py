@@ -851,3 +851,45 @@ def test_several_landmarks_decode_matches_prefill_rows(oracle_mod):
     for i, (s, bh) in enumerate((s, bh) for s in range(steps) for bh in range(B * H)):
         np.testing.assert_array_equal(outs[s]["idx"].reshape(-1, k + 1)[bh], ref["idx"][i])
         np.testing.assert_array_equal(outs[s]["o"].reshape(-1, d)[bh], ref["O"][i])
+
+
+# ---------------------------------------------------------------------------------------------
+# Worked example with a closed-form answer (tests/golden/fusion_ties_6chunks.json, written by
+# tests/golden/make_golden.py without the oracle): scores alpha_j / 8 with a tie, uniform attention
+# inside chunks whose value rows are constant, so each query chunk's selection, weights and output
+# follow from the operator's definition by hand.
+def _golden_expect(case, k):
+    sel = np.array([-np.inf if s is None else s for s in case["sel"]])
+    return np.array(case["idx"]), sel, np.array(case["w"]), np.array(case["o01"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_matches_golden_worked_example(oracle_mod, dtype):
+    import golden_cases
+
+    g = golden_cases.load("fusion_ties_6chunks.json")
+    x = golden_cases.fusion_ties_prefill(g, dtype)
+    r = oracle_mod.fwd(x["Q"], x["K"], x["V"], x["Klm"], g["C"], g["k"])
+    C = g["C"]
+    for case in g["per_query_chunk"]:
+        idx, sel, w, o01 = _golden_expect(case, g["k"])
+        rows = slice(case["c"] * C, (case["c"] + 1) * C)
+        assert (r["idx"][0, 0, rows] == idx).all(), case["c"]
+        np.testing.assert_allclose(r["sel"][0, 0, rows], np.broadcast_to(sel, (C, sel.size)), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(r["w"][0, 0, rows], np.broadcast_to(w, (C, w.size)), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(r["O"][0, 0, rows, :2], np.broadcast_to(o01, (C, 2)), rtol=0, atol=1e-12)
+        assert np.abs(r["O"][0, 0, rows, 2:]).max() == 0.0
+
+
+@pytest.mark.parametrize("n", [5, 64, 64 * 3 + 17, 64 * 4, 64 * 6 - 1])
+def test_decode_matches_golden_worked_example(oracle_mod, n):
+    import golden_cases
+
+    g = golden_cases.load("fusion_ties_6chunks.json")
+    x = golden_cases.fusion_ties_decode(g, n, "f32")
+    r = oracle_mod.decode(x["q"], x["k_new"], x["v_new"], x["Kc"], x["Vc"], x["Klm"], n, g["C"], g["k"])
+    idx, sel, w, o01 = _golden_expect(g["per_query_chunk"][n // g["C"]], g["k"])
+    assert (r["idx"][0, 0] == idx).all()
+    np.testing.assert_allclose(r["sel"][0, 0], sel, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["w"][0, 0], w, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["o"][0, 0, :2], o01, rtol=0, atol=1e-12)
