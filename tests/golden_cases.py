@@ -50,3 +50,15 @@ def fusion_ties_decode(g, n, dtype):
     q = x["Q"][:, :, n].copy()
     return {n_: _cast(a, dtype) for n_, a in (("q", q), ("k_new", k_new), ("v_new", v_new), ("Kc", Kc), ("Vc", Vc),
                                               ("Klm", Klm))}
+
+
+def fusion_ties_dO(g, dtype):
+    """Upstream gradient e_0 on every row, [1, 1, L, d]."""
+    dO = np.zeros((1, 1, g["C"] * g["N"], g["d"]), np.float32)
+    dO[..., 0] = 1.0
+    return _cast(dO, dtype)
+
+
+def fusion_ties_idx(g):
+    """The worked example's selection, [1, 1, L, k+1] int32 (every row of a query chunk the same)."""
+    return np.repeat(np.array([c["idx"] for c in g["per_query_chunk"]], np.int32), g["C"], axis=0)[None, None]

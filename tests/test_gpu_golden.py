@@ -54,3 +54,24 @@ def test_decode_golden_worked_example(hils, gpu, dtype, n):
     go = f32(o)[0, 0]
     assert np.abs(go[:2] - e_o).max() < tol(dtype)[0]
     assert np.abs(go[2:]).max() == 0.0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_golden_worked_example(hils, gpu, dtype):
+    g = golden_cases.load("fusion_ties_6chunks.json")
+    x = golden_cases.fusion_ties_prefill(g, dtype)
+    Q, K, V, Klm = (dev(x[n]) for n in ("Q", "K", "V", "Klm"))
+    dO = dev(golden_cases.fusion_ties_dO(g, dtype))
+    O, idx, sel, w, lse = hils.sparse_attn_fwd(Q, K, V, Klm, g["k"], save_for_backward=True)
+    dQ, dK, dV, dKlm = hils.sparse_attn_bwd(Q, K, V, Klm, dO, idx, w, lse, g["k"])
+    torch.cuda.synchronize()
+    assert (idx.cpu().numpy() == golden_cases.fusion_ties_idx(g)).all()
+    b = g["backward"]
+    bar = tol(dtype)[0]
+    for name, got, want in (("dQ", dQ, b["dQ0"]), ("dV", dV, b["dV0"]), ("dKlm", dKlm, b["dKlm0"])):
+        a = f32(got)[0, 0]
+        err = np.abs(a[:, 0] - np.asarray(want)).max()
+        say(f"golden {dtype} {name}: max_abs={err:.3e}")
+        assert err < bar, name
+        assert np.abs(a[:, 1:]).max() < bar, name
+    assert np.abs(f32(dK)).max() < bar

@@ -893,3 +893,20 @@ def test_decode_matches_golden_worked_example(oracle_mod, n):
     np.testing.assert_allclose(r["sel"][0, 0], sel, rtol=0, atol=1e-12)
     np.testing.assert_allclose(r["w"][0, 0], w, rtol=0, atol=1e-12)
     np.testing.assert_allclose(r["o"][0, 0, :2], o01, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_matches_golden_worked_example(oracle_mod, dtype):
+    import golden_cases
+
+    g = golden_cases.load("fusion_ties_6chunks.json")
+    x = golden_cases.fusion_ties_prefill(g, dtype)
+    gr = oracle_mod.bwd(x["Q"], x["K"], x["V"], x["Klm"], golden_cases.fusion_ties_dO(g, dtype),
+                        golden_cases.fusion_ties_idx(g), g["C"], g["k"])
+    b = g["backward"]
+    np.testing.assert_allclose(gr["dQ"][0, 0, :, 0], b["dQ0"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(gr["dV"][0, 0, :, 0], b["dV0"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(gr["dKlm"][0, 0, :, 0], b["dKlm0"], rtol=0, atol=1e-12)
+    assert np.abs(gr["dK"]).max() < 1e-12
+    for name in ("dQ", "dV", "dKlm"):
+        assert np.abs(gr[name][..., 1:]).max() < 1e-12
