@@ -451,31 +451,51 @@ __global__ __launch_bounds__(256) void klm_bwd_kernel(const T* __restrict__ Q, c
 #pragma unroll
   for (int e = 0; e < QD; ++e) acc[e] = 0.f;
   // tile 0 holds the chunk's own queries (their own slot), which do not score K_lm_j when chunks are
-  // landmark-free
-  for (int tile = lf ? 1 : 0; tile < ntiles; ++tile) {
-    int t, slot;
-    bool valid = true;
-    if (tile == 0) {
-      t = j * 64 + p;
-      slot = k;
-    } else {
-      const int pp = p_begin + (tile - 1) * 64 + p;
-      valid = pp < p_end;
-      const int pe = valid ? pl[pp] : 0;
-      t = pe >> 5;
-      slot = pe & 31;
+  // landmark-free.  TB tiles at a time: their pair entries are requested together, then their ds
+  // values and query rows, so that a batch costs two memory round trips instead of two per tile;
+  // the sums still run tile by tile in list order.  Lanes past the chunk's pairs read a valid row
+  // (entries at clamped list positions, the chunk's first query) and add nothing.
+  constexpr int TB = QD / EPP <= 2 ? 8 : 4;
+  const int64_t npl = (int64_t)L * k;
+  for (int tb = lf ? 1 : 0; tb < ntiles; tb += TB) {
+    int pe[TB];
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      const int64_t pp = (int64_t)p_begin + (int64_t)(tb + u - 1) * 64 + p;
+      pe[u] = pl[pp < 0 ? 0 : (pp < npl ? pp : npl - 1)];
     }
-    if (!valid) continue;
-    const int64_t row = (int64_t)bh * L + t;
-    const float dsv = ds[row * k1 + slot];
-    const T* qp = Q + row * D + qt * QD;
+    bool ok[TB];
+    float dsv[TB];
+    int4 raw[TB][QD / EPP];
 #pragma unroll
-    for (int u = 0; u < QD / EPP; ++u) {
-      const int4 raw = *reinterpret_cast<const int4*>(qp + u * EPP);
-      T vals[EPP];
-      __builtin_memcpy(vals, &raw, 16);
+    for (int u = 0; u < TB; ++u) {
+      const int tile = tb + u;
+      int t, slot;
+      if (tile == 0) {
+        t = j * 64 + p;
+        slot = k;
+        ok[u] = true;
+      } else {
+        ok[u] = tile < ntiles && p_begin + (tile - 1) * 64 + p < p_end;
+        t = ok[u] ? (pe[u] >> 5) : j * 64;
+        slot = ok[u] ? (pe[u] & 31) : 0;
+      }
+      const int64_t row = (int64_t)bh * L + t;
+      dsv[u] = ds[row * k1 + slot];
+      const T* qp = Q + row * D + qt * QD;
 #pragma unroll
-      for (int e = 0; e < EPP; ++e) acc[u * EPP + e] += dsv * Elem<T>::to_f32(vals, e);
+      for (int v = 0; v < QD / EPP; ++v) raw[u][v] = *reinterpret_cast<const int4*>(qp + v * EPP);
+    }
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      if (!ok[u]) continue;
+#pragma unroll
+      for (int v = 0; v < QD / EPP; ++v) {
+        T vals[EPP];
+        __builtin_memcpy(vals, &raw[u][v], 16);
+#pragma unroll
+        for (int e = 0; e < EPP; ++e) acc[v * EPP + e] += dsv[u] * Elem<T>::to_f32(vals, e);
+      }
     }
   }
 #pragma unroll
