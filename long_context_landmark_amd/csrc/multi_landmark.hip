@@ -220,55 +220,76 @@ __global__ __launch_bounds__(256) void ml_klm_bwd_kernel(const T* __restrict__ Q
   for (int u = 0; u < MM; ++u)
 #pragma unroll
     for (int e = 0; e < QD; ++e) acc[u][e] = 0.f;
-  for (int tile = 0; tile < ntiles; ++tile) {
-    int t, slot;
-    bool valid = true;
-    if (tile == 0) {
-      t = j * 64 + p;
-      slot = k;
-    } else {
-      const int pp = p_begin + (tile - 1) * 64 + p;
-      valid = pp < p_end;
-      const int pe = valid ? pl[pp] : 0;
-      t = pe >> 5;
-      slot = pe & 31;
+  // TB tiles at a time: their pair entries are requested together, then their ds values and query
+  // rows (two memory round trips a batch instead of two a tile); the sums still run tile by tile in
+  // list order.  Lanes past the chunk's pairs read a valid row and add nothing.
+  constexpr int TB = QD / EPP <= 2 ? 8 : 4;
+  const int64_t npl = (int64_t)L * k;
+  for (int tb = 0; tb < ntiles; tb += TB) {
+    int pe[TB];
+#pragma unroll
+    for (int v = 0; v < TB; ++v) {
+      const int64_t pp = (int64_t)p_begin + (int64_t)(tb + v - 1) * 64 + p;
+      pe[v] = pl[pp < 0 ? 0 : (pp < npl ? pp : npl - 1)];
     }
-    // all four lanes of a pair take the same branch, so the shuffles below stay within valid pairs
-    if (!valid) continue;
-    const int64_t row = (int64_t)bh * L + t;
-    const float dsv = ds[row * k1 + slot];
-    float qv[QD];
-    const T* qp = Qs + row * D + qt * QD;
+    bool ok[TB];
+    float dsb[TB];
+    int4 raw[TB][QD / EPP];
 #pragma unroll
-    for (int u = 0; u < QD / EPP; ++u) {
-      const int4 raw = *reinterpret_cast<const int4*>(qp + u * EPP);
-      T vals[EPP];
-      __builtin_memcpy(vals, &raw, 16);
-#pragma unroll
-      for (int e = 0; e < EPP; ++e) qv[u * EPP + e] = Elem<T>::to_f32(vals, e);
-    }
-    float a[MM], amax = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < MM; ++u) {
-      float dot = 0.f;
-      if (u < m) {
-#pragma unroll
-        for (int e = 0; e < QD; ++e) dot += qv[e] * lmv[u][qt * QD + e];
+    for (int v = 0; v < TB; ++v) {
+      const int tile = tb + v;
+      int t, slot;
+      if (tile == 0) {
+        t = j * 64 + p;
+        slot = k;
+        ok[v] = true;
+      } else {
+        ok[v] = tile < ntiles && p_begin + (tile - 1) * 64 + p < p_end;
+        t = ok[v] ? (pe[v] >> 5) : j * 64;
+        slot = ok[v] ? (pe[v] & 31) : 0;
       }
-      dot += lane_xor(dot, 1);
-      dot += lane_xor(dot, 2);
-      a[u] = scale * dot;
-      if (u < m) amax = fmaxf(amax, a[u]);
+      const int64_t row = (int64_t)bh * L + t;
+      dsb[v] = ds[row * k1 + slot];
+      const T* qp = Qs + row * D + qt * QD;
+#pragma unroll
+      for (int w = 0; w < QD / EPP; ++w) raw[v][w] = *reinterpret_cast<const int4*>(qp + w * EPP);
     }
-    float z = 0.f;
 #pragma unroll
-    for (int u = 0; u < MM; ++u) z += u < m ? __expf(a[u] - amax) : 0.f;
-    const float g = dsv / z;
+    for (int v = 0; v < TB; ++v) {
+      // all four lanes of a pair take the same branch, so the shuffles below stay within valid pairs
+      if (!ok[v]) continue;
+      const float dsv = dsb[v];
+      float qv[QD];
 #pragma unroll
-    for (int u = 0; u < MM; ++u) {
-      const float c = u < m ? g * __expf(a[u] - amax) : 0.f;
+      for (int w = 0; w < QD / EPP; ++w) {
+        T vals[EPP];
+        __builtin_memcpy(vals, &raw[v][w], 16);
 #pragma unroll
-      for (int e = 0; e < QD; ++e) acc[u][e] += c * qv[e];
+        for (int e = 0; e < EPP; ++e) qv[w * EPP + e] = Elem<T>::to_f32(vals, e);
+      }
+      float a[MM], amax = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < MM; ++u) {
+        float dot = 0.f;
+        if (u < m) {
+#pragma unroll
+          for (int e = 0; e < QD; ++e) dot += qv[e] * lmv[u][qt * QD + e];
+        }
+        dot += lane_xor(dot, 1);
+        dot += lane_xor(dot, 2);
+        a[u] = scale * dot;
+        if (u < m) amax = fmaxf(amax, a[u]);
+      }
+      float z = 0.f;
+#pragma unroll
+      for (int u = 0; u < MM; ++u) z += u < m ? __expf(a[u] - amax) : 0.f;
+      const float gsc = dsv / z;
+#pragma unroll
+      for (int u = 0; u < MM; ++u) {
+        const float cu = u < m ? gsc * __expf(a[u] - amax) : 0.f;
+#pragma unroll
+        for (int e = 0; e < QD; ++e) acc[u][e] += cu * qv[e];
+      }
     }
   }
 #pragma unroll
