@@ -48,9 +48,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: {kernel: (FETCH_SIZE KiB, WRITE_SIZE KiB, source digest)}
-    "prefill_8k": {"chunk_attn_fwd": (28595.7, 130575.3, "292684829ec4835a"), "topk_select": (8440.9, 13824.0, "73c31c6e77c56efc"), "own_combine": (92230.1, 16384.0, "292684829ec4835a")},
-    "prefill_128k": {"chunk_attn_fwd": (8509682.1, 17020345.4, "292684829ec4835a"), "topk_select": (533229.7, 835605.3, "73c31c6e77c56efc"), "own_combine": (10197156.3, 1048576.0, "292684829ec4835a")},
-    "train_8k": {"chunk_bwd": (238613.4, 903162.8, "9efa9c46f334b4d3"), "chunk_attn_fwd": (105706.7, 522505.9, "292684829ec4835a"), "dq_reduce": (326658.5, 149721.2, "9efa9c46f334b4d3")},
+    "prefill_8k": {"chunk_attn_fwd": (28610.5, 130572.1, "292684829ec4835a"), "topk_select": (8441.0, 13831.5, "73c31c6e77c56efc"), "own_combine": (92229.7, 16384.0, "292684829ec4835a")},
+    "prefill_128k": {"chunk_attn_fwd": (8508646.3, 17017997.8, "292684829ec4835a"), "topk_select": (533231.9, 835622.5, "73c31c6e77c56efc"), "own_combine": (10197156.5, 1048576.0, "292684829ec4835a")},
+    "train_8k": {"chunk_bwd": (238868.0, 904105.2, "3c3eeb4166e0c5e8"), "chunk_attn_fwd": (105706.1, 522480.8, "292684829ec4835a"), "dq_reduce": (326660.8, 149728.0, "3c3eeb4166e0c5e8")},
     "decode_512k": {"decode_scan": (8264.2, 68.0, "8aa435acddc0f2e9"), "decode_attend": (2434.6, 34.1, "8aa435acddc0f2e9")},
 }
 
