@@ -338,37 +338,63 @@ __global__ __launch_bounds__(256) void ml_dq_kernel(const T* __restrict__ Qs, co
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int r = 0; r < k1; ++r) {
-    const int j = idx[row * k1 + r];
-    if (j < 0 || j >= N) continue;  // the same for every lane of the row
-    const float dsv = ds[row * k1 + r];
-    float lv[MM][8], a[MM], amax = -INFINITY;
+  // SB slots at a time: their chunk indices are requested together, then their ds values and
+  // landmark rows (two memory round trips a batch instead of two a slot); the sums still run slot by
+  // slot.  Unused slots read chunk 0's rows and add nothing (the same for every lane of the row).
+  constexpr int NV = Elem<T>::bytes == 2 ? 1 : 2;  // 16-byte loads per eight elements
+  constexpr int SB = NV * MM <= 4 ? 4 : 2;
+  for (int r0 = 0; r0 < k1; r0 += SB) {
+    int jb[SB];
 #pragma unroll
-    for (int u = 0; u < MM; ++u) {
-      float dot = 0.f;
-      if (u < m) {
-        const T* lp = Klm + ((bh * N + j) * m + u) * D + 8 * c8;
+    for (int sb = 0; sb < SB; ++sb) jb[sb] = r0 + sb < k1 ? idx[row * k1 + r0 + sb] : -1;
+    bool ok[SB];
+    float dsb[SB];
+    int4 raw[SB][MM][NV];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          lv[u][e] = Elem<T>::to_f32(lp, e);
-          dot += qv[e] * lv[u][e];
-        }
+    for (int sb = 0; sb < SB; ++sb) {
+      ok[sb] = jb[sb] >= 0 && jb[sb] < N;
+      const int j = ok[sb] ? jb[sb] : 0;
+      dsb[sb] = ds[row * k1 + (r0 + sb < k1 ? r0 + sb : 0)];
+#pragma unroll
+      for (int u = 0; u < MM; ++u) {
+        const T* lp = Klm + ((bh * N + j) * m + (u < m ? u : 0)) * D + 8 * c8;
+#pragma unroll
+        for (int h = 0; h < NV; ++h) raw[sb][u][h] = *reinterpret_cast<const int4*>(lp + h * (8 / NV));
       }
-#pragma unroll
-      for (int msk = 1; msk < V8; msk <<= 1) dot += lane_xor(dot, msk);
-      a[u] = scale * dot;
-      if (u < m) amax = fmaxf(amax, a[u]);
     }
-    float z = 0.f;
 #pragma unroll
-    for (int u = 0; u < MM; ++u) z += u < m ? __expf(a[u] - amax) : 0.f;
-    const float g = scale * dsv / z;
+    for (int sb = 0; sb < SB; ++sb) {
+      if (!ok[sb]) continue;  // the same for every lane of the row
+      const float dsv = dsb[sb];
+      float lv[MM][8], a[MM], amax = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < MM; ++u) {
-      if (u >= m) continue;
-      const float cu = g * __expf(a[u] - amax);
+      for (int u = 0; u < MM; ++u) {
+        T vals[8];
+        __builtin_memcpy(vals, &raw[sb][u][0], 8 * sizeof(T));
+        float dot = 0.f;
+        if (u < m) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += cu * lv[u][e];
+          for (int e = 0; e < 8; ++e) {
+            lv[u][e] = Elem<T>::to_f32(vals, e);
+            dot += qv[e] * lv[u][e];
+          }
+        }
+#pragma unroll
+        for (int msk = 1; msk < V8; msk <<= 1) dot += lane_xor(dot, msk);
+        a[u] = scale * dot;
+        if (u < m) amax = fmaxf(amax, a[u]);
+      }
+      float z = 0.f;
+#pragma unroll
+      for (int u = 0; u < MM; ++u) z += u < m ? __expf(a[u] - amax) : 0.f;
+      const float g = scale * dsv / z;
+#pragma unroll
+      for (int u = 0; u < MM; ++u) {
+        if (u >= m) continue;
+        const float cu = g * __expf(a[u] - amax);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += cu * lv[u][e];
+      }
     }
   }
   float4* out = reinterpret_cast<float4*>(dQs + row * D + 8 * c8);
