@@ -158,6 +158,9 @@ static hipError_t ml_scores_t(const void* Qs, const void* Klm, float* S, int BH,
 hipError_t launch_ml_selection(int dt, int d, const void* Qs, const void* Klm, int m, float* S, int32_t* idx,
                                float* sel, float* w, int BH, int L, int N, int k, int select, float scale,
                                hipStream_t st) {
+  // with at most two landmark tiles per query chunk the selection kernel forms the log-sum-exp
+  // scores itself and no score matrix is written
+  if (select && topk_ml_fused(N)) return launch_topk_ml(dt, d, Qs, Klm, m, idx, sel, w, BH, L, N, k, scale, st);
   hipError_t e;
   if (dt == 0)
     e = d == 64 ? ml_scores_t<bf16_t, 64>(Qs, Klm, S, BH, L, N, m, scale, st)

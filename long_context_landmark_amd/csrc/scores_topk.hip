@@ -128,11 +128,15 @@ constexpr int TK_SMALL_N = 129;  // up to this many chunks a query chunk has at 
 // every 64-chunk landmark tile against all 64 queries.
 // SMALL: every query chunk has at most two landmark tiles of candidates (N <= 129 chunks);
 // the score tiles of sweep 1 are then kept in registers for sweep 2.
-template <typename T, int D, bool SMALL>
-__global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) : 1) void topk_select_kernel(const T* __restrict__ Q, const T* __restrict__ Klm,
+// ML (with SMALL): mlm landmarks per chunk (rows j * mlm + u); a chunk's score is the log-sum-exp of
+// its landmark scores, folded over the landmarks in order as the separate score kernel of the
+// several-landmark path does, so that the kept tiles hold finished scores instead of raw products.
+template <typename T, int D, bool SMALL, bool ML = false>
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : (ML && D == 128 ? 2 : 3)) : 1) void topk_select_kernel(const T* __restrict__ Q, const T* __restrict__ Klm,
                                                           const T* __restrict__ F, int32_t* __restrict__ idx,
                                                           float* __restrict__ sel, float* __restrict__ wout, int L,
-                                                          int N, int k, float scale) {
+                                                          int N, int k, float scale, int mlm) {
+  static_assert(!ML || SMALL, "several landmarks only with short candidate lists");
   const int nc = L / 64;
   int xi, bh;
   xcd_map(xi, bh);  // a head's landmark rows are re-read by all its query chunks: keep them in one L2
@@ -141,7 +145,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
   const int m = min(k, c);
   const int k1 = k + 1;
   const T* Qb = Q + ((int64_t)bh * L + (int64_t)c * 64) * D;
-  const T* Kb = Klm + (int64_t)bh * N * D;
+  const int lpc = ML ? mlm : 1;  // landmark rows per chunk
+  const T* Kb = Klm + (int64_t)bh * N * lpc * D;
+  // the score of a kept value: raw products are scaled here, several-landmark tiles hold scores
+  auto sc = [&](float x) { return ML ? x : scale * x; };
   // bf16 landmarks of long candidate lists are read from their fragment-order copy (one
   // 1 KiB run per fragment load); with at most two tiles the direct loads are kept
   constexpr bool FRAG = sizeof(T) == 2 && !SMALL;
@@ -174,15 +181,15 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
   // are never used), and unconditional loads let the compiler wait for exactly the tile it needs
   // In the fragment-order copy every tile below ceil(c/64) is whole; its rows at or past c
   // (later chunks, or zero padding) are scored but never used.
-  auto load_tile = [&](int tile, Frag<T>(&a)[D / 32]) {
+  auto load_tile = [&](int tile, Frag<T>(&a)[D / 32], int u = 0) {
     if constexpr (FRAG) {
       const T* fp = Fb + ((int64_t)(4 * tile + w) * (D / 32) * 64 + lane) * 8;
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) a[ks].load(fp + ks * 64 * 8);
     } else {
-      const int jrow = min(tile * 64 + 16 * w + r16, c);
+      const int64_t lrow = (int64_t)min(tile * 64 + 16 * w + r16, c) * lpc + u;
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) a[ks].load(Kb + (int64_t)jrow * D + ks * 32 + 8 * g);
+      for (int ks = 0; ks < D / 32; ++ks) a[ks].load(Kb + lrow * D + ks * 32 + 8 * g);
     }
   };
   // the four query blocks' products are independent: issuing them in turn keeps the
@@ -226,11 +233,18 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
   };
 
   // the first landmark tile and the own-chunk operands are requested before anything waits
-  Frag<T> first_tile[D / 32], second_tile[SMALL ? D / 32 : 1];
+  Frag<T> first_tile[D / 32], second_tile[SMALL && !ML ? D / 32 : 1];
   if (m > 0) {
     load_tile(tile_at(0), first_tile);
-    if constexpr (SMALL) load_tile(min(1, ntile - 1), second_tile);
+    if constexpr (SMALL && !ML) load_tile(min(1, ntile - 1), second_tile);
   }
+  // one landmark's score a folded into the running maximum mx and sum z = sum exp(score - mx)
+  // (from mx = -inf, z = 0): one exponential of the lesser minus the greater of a and mx
+  auto lse_fold = [](float a, float& mx, float& z) {
+    const float hi = fmaxf(mx, a), e = __expf(fminf(mx, a) - hi);
+    z = a > mx ? z * e + 1.f : z + e;
+    mx = hi;
+  };
   // own-chunk scores.  When chunk c lies in the last candidate tile (c not a multiple of 64) the
   // first sweep's products hold them: the lane that holds (query, c) stores them.  Otherwise
   // wave 0 forms them from the query fragments already held: lane (r16, g) takes the elements
@@ -238,7 +252,23 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
   // partial products.
   __shared__ float own_s[64];
   const bool own_in_tile = (c & 63) != 0;
-  if (!own_in_tile && w == 0) {
+  if (ML && !own_in_tile && w == 0) {
+    // several landmarks: wave 0 forms the own chunk's landmark scores on the MFMA units, from a
+    // tile whose rows all clamp to chunk c, and folds element 0 of each query block
+    float omx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, oz[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < mlm; ++u) {
+      Frag<T> lf[D / 32];
+      load_tile(c / 64, lf, u);
+      f32x4_t cc[4];
+      mma_tile(lf, cc);
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) lse_fold(scale * cc[qb][0], omx[qb], oz[qb]);
+    }
+    if (g == 0) {
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) own_s[16 * qb + r16] = mlm == 1 ? omx[qb] : omx[qb] + __logf(oz[qb]);
+    }
+  } else if (!ML && !own_in_tile && w == 0) {
     Frag<T> lf[D / 32];
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) lf[ks].load(Kb + (int64_t)c * D + ks * 32 + 8 * g);
@@ -284,12 +314,54 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
             for (int qb = 0; qb < 4; ++qb) gm[qb][i] = fmaxf(gm[qb][i], acc[qb][i]);
           } else if (j == c) {  // the last, partial tile holds the own chunk
 #pragma unroll
-            for (int qb = 0; qb < 4; ++qb) own_s[16 * qb + r16] = scale * acc[qb][i];
+            for (int qb = 0; qb < 4; ++qb) own_s[16 * qb + r16] = sc(acc[qb][i]);
           }
         }
       }
     };
-    if constexpr (SMALL) {
+    if constexpr (ML) {
+      // a tile's landmarks in order, folded into a running log-sum-exp that ends in its kept
+      // tile; the next landmark rows (or the next tile's first) are requested before the
+      // current products.  The second tile runs only when it holds candidates.
+      Frag<T> nxt[D / 32];
+      auto ml_tile = [&](int tl, f32x4_t(&keep)[4], bool more) {
+        float mx[4][4], z[4][4];
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            mx[qb][i] = -INFINITY;
+            z[qb][i] = 0.f;
+          }
+        for (int u = 0; u < mlm; ++u) {
+          const bool next = u + 1 < mlm || more;
+          if (u + 1 < mlm) load_tile(tl, nxt, u + 1);
+          else if (more) load_tile(tl + 1, nxt, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          // one query block at a time: its products are folded before the next block's are formed
+#pragma unroll
+          for (int qb = 0; qb < 4; ++qb) {
+            f32x4_t cc = zero4();
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) mma(cc, first_tile[ks], qf[qb][ks]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lse_fold(scale * cc[i], mx[qb][i], z[qb][i]);
+          }
+          if (next) {
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) first_tile[ks] = nxt[ks];
+          }
+        }
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) keep[qb][i] = mlm == 1 ? mx[qb][i] : mx[qb][i] + __logf(z[qb][i]);
+      };
+      ml_tile(0, keep0, ntile > 1);
+      if (ntile > 1) ml_tile(1, keep1, false);
+      group_max(0, keep0);
+      if (ntile > 1) group_max(1, keep1);
+    } else if constexpr (SMALL) {
       mma_tile(first_tile, keep0);
       mma_tile(second_tile, keep1);
       group_max(0, keep0);
@@ -300,7 +372,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) gmax_s[16 * qb + r16][16 * w + 4 * g + i] = scale * gm[qb][i];
+      for (int i = 0; i < 4; ++i) gmax_s[16 * qb + r16][16 * w + 4 * g + i] = sc(gm[qb][i]);
     __syncthreads();
     {
       const int q = tid >> 2, part = tid & 3;
@@ -347,7 +419,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
       for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          bits |= ((SMALL ? scale * acc[qb][i] : acc[qb][i]) >= a0[qb] && (whole || jb + i < c)) ? (1u << (4 * qb + i))
+          bits |= ((SMALL ? sc(acc[qb][i]) : acc[qb][i]) >= a0[qb] && (whole || jb + i < c)) ? (1u << (4 * qb + i))
                                                                                             : 0u;
       if (!__any(bits != 0)) return;
       // long lists: the wave parks its accumulators in LDS (four 16-byte stores a lane) and
@@ -377,7 +449,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
           const int q = 16 * (e >> 2) + r16;
           // the key is formed while the slot is fetched, and stored without a branch: a value
           // past the slots goes to the row's padding entry (never read; the count records it)
-          const uint64_t key = make_key(scale * x, jb + (e & 3));
+          const uint64_t key = make_key(sc(x), jb + (e & 3));
           const int p = atomicAdd(&cnt_s[q], 1);
           surv[q][p < TK_CAP ? p : TK_CAP] = key;
         }
@@ -452,7 +524,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
       for (int r = 0; r < m; ++r) {
         if (tid < 64) best_s[tid] = 0ull;
         __syncthreads();
-        sweep([&](int tile, f32x4_t(&acc)[4]) {
+        auto least_below = [&](int tile, const f32x4_t(&acc)[4]) {
 #pragma unroll
           for (int qb = 0; qb < 4; ++qb) {
             const int q = 16 * qb + r16;
@@ -463,13 +535,20 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : 3) 
             for (int i = 0; i < 4; ++i) {
               const int j = tile * 64 + 16 * w + 4 * g + i;
               if (j < c) {
-                const uint64_t key = make_key(scale * acc[qb][i], j);
+                const uint64_t key = make_key(sc(acc[qb][i]), j);
                 if (key < prev && key > best) best = key;
               }
             }
             if (best) atomicMax((unsigned long long*)&best_s[q], (unsigned long long)best);
           }
-        });
+        };
+        // several-landmark scores are not recomputed: the kept tiles hold them
+        if constexpr (ML) {
+          least_below(0, keep0);
+          if (ntile > 1) least_below(1, keep1);
+        } else {
+          sweep([&](int tile, f32x4_t(&acc)[4]) { least_below(tile, acc); });
+        }
         __syncthreads();
         if (tid < 64 && redo_s[tid]) {
           top_s[tid][r] = best_s[tid];
@@ -545,10 +624,19 @@ hipError_t launch_topk_t(const void* Q, const void* Klm, void* frag_ws, int32_t*
   dim3 grid(L / 64, BH);
   if (N <= TK_SMALL_N)
     HILS_LAUNCH("topk_select", (topk_select_kernel<T, D, true>), grid, dim3(256), 0, st, (const T*)Q, (const T*)Klm, F,
-                idx, sel, w, L, N, k, scale);
+                idx, sel, w, L, N, k, scale, 1);
   else
     HILS_LAUNCH("topk_select", (topk_select_kernel<T, D, false>), grid, dim3(256), 0, st, (const T*)Q, (const T*)Klm, F,
-                idx, sel, w, L, N, k, scale);
+                idx, sel, w, L, N, k, scale, 1);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_topk_ml_t(const void* Q, const void* Klm, int mlm, int32_t* idx, float* sel, float* w, int BH,
+                            int L, int N, int k, float scale, hipStream_t st) {
+  if (N > TK_SMALL_N) return hipErrorInvalidValue;
+  HILS_LAUNCH("topk_select_ml", (topk_select_kernel<T, D, true, true>), dim3(L / 64, BH), dim3(256), 0, st,
+              (const T*)Q, (const T*)Klm, (const T*)nullptr, idx, sel, w, L, N, k, scale, mlm);
   return hipGetLastError();
 }
 
@@ -558,6 +646,16 @@ hipError_t launch_landmark_scores(int dt, int d, const void* Q, const void* Klm,
                               : launch_landmark_scores_t<bf16_t, 128>(Q, Klm, S, BH, L, N, scale, st);
   return d == 64 ? launch_landmark_scores_t<float, 64>(Q, Klm, S, BH, L, N, scale, st)
                  : launch_landmark_scores_t<float, 128>(Q, Klm, S, BH, L, N, scale, st);
+}
+
+bool topk_ml_fused(int N) { return N <= TK_SMALL_N; }
+
+hipError_t launch_topk_ml(int dt, int d, const void* Q, const void* Klm, int mlm, int32_t* idx, float* sel, float* w,
+                          int BH, int L, int N, int k, float scale, hipStream_t st) {
+  if (dt == 0) return d == 64 ? launch_topk_ml_t<bf16_t, 64>(Q, Klm, mlm, idx, sel, w, BH, L, N, k, scale, st)
+                              : launch_topk_ml_t<bf16_t, 128>(Q, Klm, mlm, idx, sel, w, BH, L, N, k, scale, st);
+  return d == 64 ? launch_topk_ml_t<float, 64>(Q, Klm, mlm, idx, sel, w, BH, L, N, k, scale, st)
+                 : launch_topk_ml_t<float, 128>(Q, Klm, mlm, idx, sel, w, BH, L, N, k, scale, st);
 }
 
 hipError_t launch_topk(int dt, int d, const void* Q, const void* Klm, void* frag_ws, int32_t* idx, float* sel,

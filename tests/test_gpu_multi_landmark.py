@@ -59,6 +59,12 @@ def _check_sets(gi, ri, Qs, lm, k):
     ("bf16", 1, 2, 1024, 128, 16, "firstlast", 2),
     ("f32", 1, 2, 1024, 64, 4, "firstlast", 2),
     ("bf16", 1, 2, 2048, 64, 8, "random", 3),
+    # 129 chunks: the most the one-kernel selection takes (query chunks 64 and 128 score their own
+    # chunk outside the candidate tiles); 160 chunks: separate score matrix and selection kernels
+    ("bf16", 1, 2, 8256, 64, 4, "random", 2),
+    ("bf16", 1, 1, 4160, 128, 16, "random", 3),
+    ("f32", 1, 1, 4160, 128, 8, "firstlast", 2),
+    ("bf16", 1, 1, 10240, 64, 8, "firstlast", 2),
 ])
 def test_fwd_multi_landmark(hils, gpu, dtype, B, H, L, d, k, kind, m):
     say(f"fwd several landmarks dtype={dtype} B={B} H={H} L={L} d={d} k={k} landmarks={kind}x{m}")
@@ -88,6 +94,25 @@ def test_fwd_multi_landmark(hils, gpu, dtype, B, H, L, d, k, kind, m):
     # own-chunk scores
     own = f32(sel).reshape(-1, k + 1)[:, k]
     assert np.abs(own - ref["sel"].reshape(-1, k + 1)[:, k]).max() < 1e-4
+
+
+@pytest.mark.parametrize("L", [8256, 10240])
+def test_fwd_multi_landmark_ties(hils, gpu, L):
+    """Every chunk has the same landmarks, so all chunk scores tie and each query keeps the lowest
+    indices; with more than 64 tied candidates the survivor list overflows and the exact
+    fallback of the selection runs."""
+    B, H, d, k = 1, 1, 64, 8
+    say(f"fwd several landmarks, all scores tied, L={L}")
+    x = synth.prefill_inputs(B, H, L, d, C=64, seed=830, dtype="bf16")
+    row = np.random.default_rng(831).standard_normal((1, 1, 1, 2, d), dtype=np.float32)
+    lm = synth.f32_to_bf16_bits(np.ascontiguousarray(np.broadcast_to(row, (B, H, L // 64, 2, d))))
+    t = to_inputs(x, ("Q", "K", "V"))
+    O, idx, sel, w, lse = hils.sparse_attn_fwd_ml(t["Q"], t["K"], t["V"], dev(lm), k, save_for_backward=True)
+    torch.cuda.synchronize()
+    ref = oracle.fwd_ml(x["Q"], x["K"], x["V"], lm, 64, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref["idx"])
+    assert_close(f32(O), ref["O"], "O (tied scores)", *tol("bf16"))
+    assert_close(f32(w), ref["w"], "w (tied scores)", 1e-5, 1e-5)
 
 
 def test_fwd_multi_landmark_fixed_selection(hils, gpu):
