@@ -222,8 +222,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
         daf[h].set(v8);
       }
       typename PartialOf<T>::type* dst = valid ? dq_part + (row * k1 + in.slot) * D : trash;
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
+      auto dq_block = [&](int db) {
         f32x4_t dq = zero4();
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -232,13 +231,26 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
           a.load4x2(rowp, rowp + 16);
           mma(dq, a, daf[h]);
         }
-        // bf16 parts keep fp32's exponent range (no overflow whatever the scale of dQ); fp32 inputs keep fp32
-        if constexpr (sizeof(typename PartialOf<T>::type) == 2) {
-          *reinterpret_cast<uint2*>(dst + 16 * db + 4 * g) =
-              make_uint2(pack_bf16x2(scale * dq[0], scale * dq[1]), pack_bf16x2(scale * dq[2], scale * dq[3]));
-        } else {
-          *reinterpret_cast<f32x4_t*>(dst + 16 * db + 4 * g) = scale * dq;
+        return dq;
+      };
+      // bf16 parts keep fp32's exponent range (no overflow whatever the scale of dQ); fp32 inputs keep fp32
+      if constexpr (sizeof(typename PartialOf<T>::type) == 2) {
+        // two 16-d blocks at a time: lane groups g and g ^ 1 swap one block's packed values, so that
+        // each lane holds eight consecutive d and stores 16 bytes (even g: d 32p + 4g ..; odd g:
+        // d 32p + 16 + 4(g - 1) ..), a row's 64 bytes per store instruction
+        const bool odd = (g & 1) != 0;
+#pragma unroll
+        for (int p2 = 0; p2 < D / 32; ++p2) {
+          const f32x4_t e = dq_block(2 * p2), o = dq_block(2 * p2 + 1);
+          const uint32_t e0 = pack_bf16x2(scale * e[0], scale * e[1]), e1 = pack_bf16x2(scale * e[2], scale * e[3]);
+          const uint32_t o0 = pack_bf16x2(scale * o[0], scale * o[1]), o1 = pack_bf16x2(scale * o[2], scale * o[3]);
+          const uint32_t r0 = lane_xor_u32(odd ? e0 : o0, 16), r1 = lane_xor_u32(odd ? e1 : o1, 16);
+          const uint4 v = odd ? make_uint4(r0, r1, o0, o1) : make_uint4(e0, e1, r0, r1);
+          *reinterpret_cast<uint4*>(dst + 32 * p2 + (odd ? 16 + 4 * (g - 1) : 4 * g)) = v;
         }
+      } else {
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4_t*>(dst + 16 * db + 4 * g) = scale * dq_block(db);
       }
     }
     __syncthreads();  // previous tile's readers of the staged buffers are done
