@@ -48,9 +48,9 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: {kernel: (FETCH_SIZE KiB, WRITE_SIZE KiB, source digest)}
-    "prefill_8k": {"chunk_attn_fwd": (28610.5, 130572.1, "292684829ec4835a"), "topk_select": (8441.0, 13831.5, "73c31c6e77c56efc"), "own_combine": (92229.7, 16384.0, "292684829ec4835a")},
-    "prefill_128k": {"chunk_attn_fwd": (8508646.3, 17017997.8, "292684829ec4835a"), "topk_select": (533231.9, 835622.5, "73c31c6e77c56efc"), "own_combine": (10197156.5, 1048576.0, "292684829ec4835a")},
-    "train_8k": {"chunk_bwd": (238868.0, 904105.2, "3c3eeb4166e0c5e8"), "chunk_attn_fwd": (105706.1, 522480.8, "292684829ec4835a"), "dq_reduce": (326660.8, 149728.0, "3c3eeb4166e0c5e8")},
+    "prefill_8k": {"chunk_attn_fwd": (28609.3, 130571.7, "292684829ec4835a"), "topk_select": (8433.1, 13829.1, "8627482025ee6375"), "own_combine": (92230.4, 16384.0, "292684829ec4835a")},
+    "prefill_128k": {"chunk_attn_fwd": (8514752.1, 17019380.3, "292684829ec4835a"), "topk_select": (533164.4, 835600.4, "8627482025ee6375"), "own_combine": (10197158.1, 1048576.0, "292684829ec4835a")},
+    "train_8k": {"chunk_bwd": (238399.0, 907126.6, "c98a95fc53c96470"), "chunk_attn_fwd": (105707.1, 522560.5, "292684829ec4835a"), "dq_reduce": (326652.2, 149735.3, "c98a95fc53c96470")},
     "decode_512k": {"decode_scan": (8264.2, 68.0, "8aa435acddc0f2e9"), "decode_attend": (2434.6, 34.1, "8aa435acddc0f2e9")},
 }
 
