@@ -145,9 +145,8 @@ def train_work(B, H, L, d, k, C=64):
     kern["klm_bwd"] = ("hbm", 0, BH * N * d * 4, pairs_all * (2 * d + 8) + BH * N * d * 4)
     # landmark-free chunks only: q and k read, dQ and dK read and written, per row
     kern["lf_bwd"] = ("hbm", 0, BH * L * 2 * d * 2, BH * L * (2 * d * 2 + 4 + 4 * d * 4) + BH * N * d * 4)
-    # two landmarks per chunk only: per pair q and two landmark rows read, dKlm and dQ written
+    # two landmarks per chunk only: per pair q read, the chunk's two landmark rows read and dKlm written
     kern["ml_klm_bwd"] = ("hbm", 0, BH * N * 2 * d * 4, pairs_all * (2 * d + 4) + BH * N * 2 * d * (2 + 4))
-    kern["ml_dq"] = ("hbm", 0, BH * L * d * 4, BH * L * (2 * d + (k + 1) * (8 + 2 * 2 * d) + 2 * 4 * d))
     return {"flops": fw["flops"] + f_bwd, "bytes": fw["bytes"] + b_bwd, "kernels": kern}
 
 

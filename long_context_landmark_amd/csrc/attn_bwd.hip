@@ -344,13 +344,18 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
 // held in registers and every load of a row is issued before any is used (slots past k + 1
 // and dropped slots read a valid address and are not used): two memory round trips per
 // thread, the landmark rows once the indices are in.
-template <typename T, int D, int K1M, bool RQ>
+// MM > 0: mlm <= MM landmarks per chunk (Klm [BH][N][mlm][D]).  A slot's score is the
+// log-sum-exp of its landmark scores, so its term is scale ds_j sum_u p_u Klm_j,u with the shares
+// p_u = softmax_u(scale qs . Klm_j,u) of the scoring query qs (Qs); these terms are summed in slot
+// order apart from the in-chunk parts and added to them at the end.
+template <typename T, int D, int K1M, bool RQ, int MM = 0>
 __global__ __launch_bounds__(256) void dq_reduce_kernel(const typename PartialOf<T>::type* __restrict__ dq_part,
                                                         const float* __restrict__ Dpart,
                                                         const int32_t* __restrict__ idx, const float* __restrict__ w,
                                                         const T* __restrict__ Klm, float* __restrict__ ds_out,
                                                         float* __restrict__ dQ, float* __restrict__ dQr, int64_t rows,
-                                                        int L, int N, int k, float scale, int skip) {
+                                                        int L, int N, int k, float scale, int skip,
+                                                        const T* __restrict__ Qs, int mlm) {
   constexpr int V8 = D / 8;                    // threads per row
   constexpr int LW = 2 * Elem<T>::bytes;       // 32-bit words of eight landmark elements
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -380,9 +385,9 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const typename PartialOf
     ok[r] = r < k1 && (r == k || (jr[r] >= 0 && jr[r] < N));
     if (ok[r]) Dsum += wr[r] * dr[r];
   }
-  uint32_t lw[K1M][LW];
+  uint32_t lw[MM > 0 ? 1 : K1M][LW];
 #pragma unroll
-  for (int r = 0; r < K1M; ++r) {
+  for (int r = 0; r < (MM > 0 ? 0 : K1M); ++r) {
     const uint4* lp = reinterpret_cast<const uint4*>(Klm + (bh * N + (ok[r] ? jr[r] : 0)) * D + 8 * c8);
 #pragma unroll
     for (int v = 0; v < LW / 4; ++v) {
@@ -396,7 +401,7 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const typename PartialOf
   // RQ: the landmark scores came from separate retrieval queries, whose gradient (the
   // ds * Klm terms) goes to dQr; dQ then keeps the in-chunk attention terms only.
   // skip = 1 (landmark-free chunks): the own slot's landmark is not a K_lm row, lf_bwd adds its term;
-  // skip = 2 (several landmarks per chunk): no slot's is, ml_dq adds them
+  // several landmarks per chunk (MM > 0) add theirs below
   float acc[8], accr[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = accr[e] = 0.f;
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const typename PartialOf
     if (!ok[r]) continue;
     const float ds = wr[r] * (dr[r] - Dsum);
     if (c8 == 0) ds_out[row * k1 + r] = ds;
-    const float sds = (skip == 2 || (skip == 1 && r == k)) ? 0.f : scale * ds;
+    const float sds = (MM > 0 || (skip == 1 && r == k)) ? 0.f : scale * ds;
     float h[8];
     if constexpr (VPP == 1) {
       const uint32_t wds[4] = {raw[r][0].x, raw[r][0].y, raw[r][0].z, raw[r][0].w};
@@ -417,16 +422,100 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const typename PartialOf
     } else {
       __builtin_memcpy(h, raw[r], 32);
     }
-    T lm[8];
-    __builtin_memcpy(lm, lw[r], 8 * sizeof(T));
+    if constexpr (MM > 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += h[e];
+    } else {
+      T lm[8];
+      __builtin_memcpy(lm, lw[r], 8 * sizeof(T));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (RQ) {
+          acc[e] += h[e];
+          accr[e] += sds * Elem<T>::to_f32(lm, e);
+        } else {
+          acc[e] += h[e] + sds * Elem<T>::to_f32(lm, e);
+        }
+      }
+    }
+  }
+  if constexpr (MM > 0) {
+    // the scoring query's eight elements, then SB slots at a time: their landmark rows are
+    // requested together; unused slots read chunk 0's rows and add nothing (the same for every
+    // lane of the row, so the shuffles stay within live rows)
+    float qv[8];
+    {
+      T vals[8];
+      constexpr int NQ = 8 * sizeof(T) / 16;
+#pragma unroll
+      for (int h = 0; h < NQ; ++h) {
+        const int4 x = *reinterpret_cast<const int4*>(Qs + row * D + 8 * c8 + h * (8 / NQ));
+        __builtin_memcpy(reinterpret_cast<char*>(vals) + 16 * h, &x, 16);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] = Elem<T>::to_f32(vals, e);
+    }
+    float accm[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) accm[e] = 0.f;
+    constexpr int NV = Elem<T>::bytes == 2 ? 1 : 2;  // 16-byte loads per eight elements
+    constexpr int SB = NV * MM <= 4 ? 4 : 2;
+#pragma unroll
+    for (int r0 = 0; r0 < K1M; r0 += SB) {
+      if (r0 < k1) {
+        int4 lraw[SB][MM][NV];
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb) {
+          const int r = r0 + sb < K1M ? r0 + sb : 0;
+          const int j = (r0 + sb < K1M && ok[r]) ? jr[r] : 0;
+#pragma unroll
+          for (int u = 0; u < MM; ++u) {
+            const T* lp = Klm + ((bh * N + j) * mlm + (u < mlm ? u : 0)) * D + 8 * c8;
+#pragma unroll
+            for (int h = 0; h < NV; ++h) lraw[sb][u][h] = *reinterpret_cast<const int4*>(lp + h * (8 / NV));
+          }
+        }
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb) {
+          const int r = r0 + sb;
+          if (r >= K1M || !ok[r]) continue;
+          const float ds = wr[r] * (dr[r] - Dsum);
+          float lv[MM][8], a[MM], amax = -INFINITY;
+#pragma unroll
+          for (int u = 0; u < MM; ++u) {
+            T vals[8];
+            __builtin_memcpy(vals, &lraw[sb][u][0], 8 * sizeof(T));
+            float dot = 0.f;
+            if (u < mlm) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                lv[u][e] = Elem<T>::to_f32(vals, e);
+                dot += qv[e] * lv[u][e];
+              }
+            }
+#pragma unroll
+            for (int msk = 1; msk < V8; msk <<= 1) dot += lane_xor(dot, msk);
+            a[u] = scale * dot;
+            if (u < mlm) amax = fmaxf(amax, a[u]);
+          }
+          float z = 0.f;
+#pragma unroll
+          for (int u = 0; u < MM; ++u) z += u < mlm ? __expf(a[u] - amax) : 0.f;
+          const float g = scale * ds / z;
+#pragma unroll
+          for (int u = 0; u < MM; ++u) {
+            if (u >= mlm) continue;
+            const float cu = g * __expf(a[u] - amax);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) accm[e] += cu * lv[u][e];
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      if (RQ) {
-        acc[e] += h[e];
-        accr[e] += sds * Elem<T>::to_f32(lm, e);
-      } else {
-        acc[e] += h[e] + sds * Elem<T>::to_f32(lm, e);
-      }
+      if (RQ) accr[e] += accm[e];
+      else acc[e] += accm[e];
     }
   }
   float4* out = reinterpret_cast<float4*>(dQ + row * D + 8 * c8);
@@ -534,26 +623,30 @@ static hipError_t bwd_t(const void* Q, const void* Qr, const void* K, const void
               (PT*)ws.trash, ws.trash_f, dK, dV, L, N, k, scale);
   const dim3 rgrid((unsigned)((rows * (D / 8) + 255) / 256));
   const bool rq = Qr != nullptr;
-  const int skip = mlm > 0 ? 2 : (lf ? 1 : 0);
-  if (k <= 8 && !rq)
-    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 9, false>), rgrid, dim3(256), 0, st, (const PT*)ws.dq_part, ws.Dpart, idx,
-                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, skip);
-  else if (!rq)
-    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 17, false>), rgrid, dim3(256), 0, st, (const PT*)ws.dq_part, ws.Dpart, idx,
-                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, skip);
-  else if (k <= 8)
-    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 9, true>), rgrid, dim3(256), 0, st, (const PT*)ws.dq_part, ws.Dpart, idx,
-                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, skip);
-  else
-    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, 17, true>), rgrid, dim3(256), 0, st, (const PT*)ws.dq_part, ws.Dpart, idx,
-                w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, skip);
+  const int skip = lf ? 1 : 0;
+  const T* Qs = (const T*)(rq ? Qr : Q);
+  auto reduce = [&](auto k1m, auto rqc, auto mmc) {
+    constexpr int K1M = decltype(k1m)::value, MM = decltype(mmc)::value;
+    constexpr bool RQ = decltype(rqc)::value != 0;
+    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, K1M, RQ, MM>), rgrid, dim3(256), 0, st, (const PT*)ws.dq_part,
+                ws.Dpart, idx, w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, skip, Qs, mlm);
+  };
+  auto reduce_m = [&](auto k1m, auto rqc) {
+    if (mlm == 0) reduce(k1m, rqc, IntC<0>{});
+    else if (mlm <= 2) reduce(k1m, rqc, IntC<2>{});
+    else reduce(k1m, rqc, IntC<4>{});
+  };
+  if (k <= 8 && !rq) reduce_m(IntC<9>{}, IntC<0>{});
+  else if (!rq) reduce_m(IntC<17>{}, IntC<0>{});
+  else if (k <= 8) reduce_m(IntC<9>{}, IntC<1>{});
+  else reduce_m(IntC<17>{}, IntC<1>{});
   // dKlm_j sums ds_tj times the query that scored the landmark
   if (mlm > 0) {
     // several landmarks per chunk: the score paths through every landmark's share
     hipError_t e2 = hipGetLastError();
     if (e2 != hipSuccess) return e2;
-    return launch_ml_bwd(Elem<T>::bytes == 2 ? 0 : 1, D, rq ? Qr : Q, Klm, mlm, idx, ws.ds, ws.rb.chunk_off,
-                         ws.rb.pairs, rq ? dQr : dQ, dKlm, BH, L, N, k, scale, st);
+    return launch_ml_bwd(Elem<T>::bytes == 2 ? 0 : 1, D, rq ? Qr : Q, Klm, mlm, ws.ds, ws.rb.chunk_off, ws.rb.pairs,
+                         dKlm, BH, L, N, k, scale, st);
   }
   HILS_LAUNCH("klm_bwd", (klm_bwd_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)(rq ? Qr : Q), ws.ds,
               ws.rb.chunk_off, ws.rb.pairs, dKlm, L, N, k, scale, (int)lf);

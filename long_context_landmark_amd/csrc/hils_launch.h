@@ -121,10 +121,9 @@ hipError_t launch_ml_selection(int dt, int d, const void* Qs, const void* Klm, i
                                float* sel, float* w, int BH, int L, int N, int k, int select, float scale,
                                hipStream_t st);
 // backward tail of several landmarks per chunk (1 <= m <= 4; fp32: d = 64): dKlm [BH][N][m][d] over each
-// chunk's pairs, and every slot's score term into dQs
-hipError_t launch_ml_bwd(int dt, int d, const void* Qs, const void* Klm, int m, const int32_t* idx, const float* ds,
-                         const int* chunk_off, const int* pairs, float* dQs, float* dKlm, int BH, int L, int N, int k,
-                         float scale, hipStream_t st);
+// chunk's pairs (the slots' score terms of dQs are added by the backward's dq_reduce)
+hipError_t launch_ml_bwd(int dt, int d, const void* Qs, const void* Klm, int m, const float* ds, const int* chunk_off,
+                         const int* pairs, float* dKlm, int BH, int L, int N, int k, float scale, hipStream_t st);
 // landmark-free chunk keys: rows 0..nchunks-1 of Klm ([BH][Nlm][d]) = means of the key rows of each chunk
 // (K: [BH][Lk][d])
 hipError_t launch_chunk_means(int dt, int d, const void* K, void* Klm, int BH, int64_t Lk, int64_t Nlm, int nchunks,

@@ -196,8 +196,8 @@ namespace hils {
 //   ml_klm_bwd  one workgroup per (chunk, head), the chunk's pairs in routing order (its own queries
 //               first): dKlm_j,u = scale * sum ds p_u qs_t.  Four lanes per pair split the head
 //               dimension; the chunk's landmark rows sit in LDS.  Deterministic, no atomics.
-//   ml_dq       one group of D/8 lanes per query row: dQs_t += scale * sum over slots of
-//               ds sum_u p_u Klm_j,u (read, added to and written).
+// The query side, dQs_t += scale * sum over slots of ds sum_u p_u Klm_j,u, is formed by the
+// backward's dq_reduce, where ds is made.
 template <typename T, int D, int MM>
 __global__ __launch_bounds__(256) void ml_klm_bwd_kernel(const T* __restrict__ Qs, const T* __restrict__ Klm,
                                                          const float* __restrict__ ds,
@@ -311,139 +311,29 @@ __global__ __launch_bounds__(256) void ml_klm_bwd_kernel(const T* __restrict__ Q
 }
 
 template <typename T, int D, int MM>
-__global__ __launch_bounds__(256) void ml_dq_kernel(const T* __restrict__ Qs, const T* __restrict__ Klm,
-                                                    const int32_t* __restrict__ idx, const float* __restrict__ ds,
-                                                    float* __restrict__ dQs, int64_t rows, int L, int N, int k, int m,
-                                                    float scale) {
-  constexpr int V8 = D / 8;  // lanes per row, eight elements each
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gid / V8;
-  const int c8 = (int)(gid % V8);
-  // rows are whole lane groups (V8 divides 64), so every lane of a group is live or none is
-  if (row >= rows) return;
-  const int64_t bh = row / L;
-  const int k1 = k + 1;
-  float qv[8];
-  {
-    T vals[8];
-    if (Elem<T>::bytes == 2) {
-      const int4 raw = *reinterpret_cast<const int4*>(Qs + row * D + 8 * c8);
-      __builtin_memcpy(vals, &raw, 16);
-    } else {
-      const int4 r0 = *reinterpret_cast<const int4*>(Qs + row * D + 8 * c8);
-      const int4 r1 = *reinterpret_cast<const int4*>(Qs + row * D + 8 * c8 + 4);
-      __builtin_memcpy(vals, &r0, 16);
-      __builtin_memcpy(reinterpret_cast<char*>(vals) + 16, &r1, 16);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qv[e] = Elem<T>::to_f32(vals, e);
-  }
-  float acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  // SB slots at a time: their chunk indices are requested together, then their ds values and
-  // landmark rows (two memory round trips a batch instead of two a slot); the sums still run slot by
-  // slot.  Unused slots read chunk 0's rows and add nothing (the same for every lane of the row).
-  constexpr int NV = Elem<T>::bytes == 2 ? 1 : 2;  // 16-byte loads per eight elements
-  constexpr int SB = NV * MM <= 4 ? 4 : 2;
-  for (int r0 = 0; r0 < k1; r0 += SB) {
-    int jb[SB];
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb) jb[sb] = r0 + sb < k1 ? idx[row * k1 + r0 + sb] : -1;
-    bool ok[SB];
-    float dsb[SB];
-    int4 raw[SB][MM][NV];
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      ok[sb] = jb[sb] >= 0 && jb[sb] < N;
-      const int j = ok[sb] ? jb[sb] : 0;
-      dsb[sb] = ds[row * k1 + (r0 + sb < k1 ? r0 + sb : 0)];
-#pragma unroll
-      for (int u = 0; u < MM; ++u) {
-        const T* lp = Klm + ((bh * N + j) * m + (u < m ? u : 0)) * D + 8 * c8;
-#pragma unroll
-        for (int h = 0; h < NV; ++h) raw[sb][u][h] = *reinterpret_cast<const int4*>(lp + h * (8 / NV));
-      }
-    }
-#pragma unroll
-    for (int sb = 0; sb < SB; ++sb) {
-      if (!ok[sb]) continue;  // the same for every lane of the row
-      const float dsv = dsb[sb];
-      float lv[MM][8], a[MM], amax = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < MM; ++u) {
-        T vals[8];
-        __builtin_memcpy(vals, &raw[sb][u][0], 8 * sizeof(T));
-        float dot = 0.f;
-        if (u < m) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            lv[u][e] = Elem<T>::to_f32(vals, e);
-            dot += qv[e] * lv[u][e];
-          }
-        }
-#pragma unroll
-        for (int msk = 1; msk < V8; msk <<= 1) dot += lane_xor(dot, msk);
-        a[u] = scale * dot;
-        if (u < m) amax = fmaxf(amax, a[u]);
-      }
-      float z = 0.f;
-#pragma unroll
-      for (int u = 0; u < MM; ++u) z += u < m ? __expf(a[u] - amax) : 0.f;
-      const float g = scale * dsv / z;
-#pragma unroll
-      for (int u = 0; u < MM; ++u) {
-        if (u >= m) continue;
-        const float cu = g * __expf(a[u] - amax);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += cu * lv[u][e];
-      }
-    }
-  }
-  float4* out = reinterpret_cast<float4*>(dQs + row * D + 8 * c8);
-  float4 o0 = out[0], o1 = out[1];
-  o0.x += acc[0];
-  o0.y += acc[1];
-  o0.z += acc[2];
-  o0.w += acc[3];
-  o1.x += acc[4];
-  o1.y += acc[5];
-  o1.z += acc[6];
-  o1.w += acc[7];
-  out[0] = o0;
-  out[1] = o1;
-}
-
-template <typename T, int D, int MM>
-static hipError_t ml_bwd_mm(const void* Qs, const void* Klm, int m, const int32_t* idx, const float* ds,
-                            const int* chunk_off, const int* pairs, float* dQs, float* dKlm, int BH, int L, int N,
-                            int k, float scale, hipStream_t st) {
+static hipError_t ml_bwd_mm(const void* Qs, const void* Klm, int m, const float* ds, const int* chunk_off,
+                            const int* pairs, float* dKlm, int BH, int L, int N, int k, float scale, hipStream_t st) {
   HILS_LAUNCH("ml_klm_bwd", (ml_klm_bwd_kernel<T, D, MM>), dim3(N, BH), dim3(256), 0, st, (const T*)Qs,
               (const T*)Klm, ds, chunk_off, pairs, dKlm, L, N, k, m, scale);
-  const int64_t rows = (int64_t)BH * L;
-  HILS_LAUNCH("ml_dq", (ml_dq_kernel<T, D, MM>), dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, st,
-              (const T*)Qs, (const T*)Klm, idx, ds, dQs, rows, L, N, k, m, scale);
   return hipGetLastError();
 }
 
 // the landmark count rounded up to 2 or 4 sizes the per-lane accumulators
 template <typename T, int D>
-static hipError_t ml_bwd_t(const void* Qs, const void* Klm, int m, const int32_t* idx, const float* ds,
-                           const int* chunk_off, const int* pairs, float* dQs, float* dKlm, int BH, int L, int N,
-                           int k, float scale, hipStream_t st) {
-  return m <= 2 ? ml_bwd_mm<T, D, 2>(Qs, Klm, m, idx, ds, chunk_off, pairs, dQs, dKlm, BH, L, N, k, scale, st)
-                : ml_bwd_mm<T, D, 4>(Qs, Klm, m, idx, ds, chunk_off, pairs, dQs, dKlm, BH, L, N, k, scale, st);
+static hipError_t ml_bwd_t(const void* Qs, const void* Klm, int m, const float* ds, const int* chunk_off,
+                           const int* pairs, float* dKlm, int BH, int L, int N, int k, float scale, hipStream_t st) {
+  return m <= 2 ? ml_bwd_mm<T, D, 2>(Qs, Klm, m, ds, chunk_off, pairs, dKlm, BH, L, N, k, scale, st)
+                : ml_bwd_mm<T, D, 4>(Qs, Klm, m, ds, chunk_off, pairs, dKlm, BH, L, N, k, scale, st);
 }
 
-hipError_t launch_ml_bwd(int dt, int d, const void* Qs, const void* Klm, int m, const int32_t* idx, const float* ds,
-                         const int* chunk_off, const int* pairs, float* dQs, float* dKlm, int BH, int L, int N, int k,
-                         float scale, hipStream_t st) {
+hipError_t launch_ml_bwd(int dt, int d, const void* Qs, const void* Klm, int m, const float* ds, const int* chunk_off,
+                         const int* pairs, float* dKlm, int BH, int L, int N, int k, float scale, hipStream_t st) {
   if (m < 1 || m > 4) return hipErrorInvalidValue;
   if (dt == 0)
-    return d == 64 ? ml_bwd_t<bf16_t, 64>(Qs, Klm, m, idx, ds, chunk_off, pairs, dQs, dKlm, BH, L, N, k, scale, st)
-                   : ml_bwd_t<bf16_t, 128>(Qs, Klm, m, idx, ds, chunk_off, pairs, dQs, dKlm, BH, L, N, k, scale, st);
+    return d == 64 ? ml_bwd_t<bf16_t, 64>(Qs, Klm, m, ds, chunk_off, pairs, dKlm, BH, L, N, k, scale, st)
+                   : ml_bwd_t<bf16_t, 128>(Qs, Klm, m, ds, chunk_off, pairs, dKlm, BH, L, N, k, scale, st);
   if (d != 64) return hipErrorInvalidValue;
-  return ml_bwd_t<float, 64>(Qs, Klm, m, idx, ds, chunk_off, pairs, dQs, dKlm, BH, L, N, k, scale, st);
+  return ml_bwd_t<float, 64>(Qs, Klm, m, ds, chunk_off, pairs, dKlm, BH, L, N, k, scale, st);
 }
 
 }  // namespace hils
