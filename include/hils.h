@@ -165,7 +165,7 @@ hils_status hils_decode_step(const void* q, const void* k_new, const void* v_new
  * written in full):  dQ, dK, dV [B][H][L][d];  dK_lm [B][H][N][d].
  * The gradient of the fusion weights uses D = sum_j w_j dO.o_j formed from
  * the per-chunk outputs, so the forward output O is not an input.
- * fp32 inputs: d = 64 only.  Workspace: hils_workspace_size(HILS_OP_BWD, ...).
+ * Workspace: hils_workspace_size(HILS_OP_BWD, ...).
  */
 hils_status hils_sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* K_lm, const void* dO,
                                  const int32_t* idx, const float* w, const float* lse, float* dQ, float* dK,
@@ -287,7 +287,7 @@ hils_status hils_decode_step_ml(const void* q, const void* q_ret, const void* k_
  * as hils_sparse_attn_bwd_rq with the same K_lm [B][H][N][m][d]; landmark u
  * of a kept chunk takes the share p_u = softmax_u of the chunk's landmark
  * scores of its score gradient, so dK_lm is [B][H][N][m][d] float and dQ (or
- * dQ_ret) gets scale * ds * sum_u p_u K_lm[j][u].  fp32 inputs: d = 64 only.
+ * dQ_ret) gets scale * ds * sum_u p_u K_lm[j][u].
  * Workspace: hils_workspace_size(HILS_OP_BWD, ...).
  */
 hils_status hils_sparse_attn_bwd_ml(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm,

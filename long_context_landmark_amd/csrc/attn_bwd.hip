@@ -37,18 +37,25 @@ namespace hils {
 // 16-bit inputs (TR): the tile's Q, dO, w P and dA are staged row-major by tile query (16- and
 // 8-byte stores) and the dV, dK operands are read through transposing LDS loads; fp32 inputs
 // stage them transposed, element by element.
+// SPLIT (fp32 at d = 128, whose seven tiles would take 207 KB): dO and w P are staged and the dV
+// products formed first, then Q and dA take the same buffers for the dK products.
 template <typename T, int D> struct alignas(16) BwdLds {
   static constexpr bool TR = Elem<T>::bytes == 2;
+  static constexpr bool SPLIT = !TR && D == 128;
   static constexpr int KS = D + (Elem<T>::bytes == 2 ? 8 : 4);   // rows indexed by key, d inside
   static constexpr int TS = 64 + (Elem<T>::bytes == 2 ? 8 : 4);  // rows of 64 (keys or tile queries)
   static constexpr int QS = D + 8;                               // TR: rows of D (tile query, d)
   T k[64 * KS];
   T v[64 * KS];
-  T kt[D * TS];               // K^T   [d][key]
-  T qt[TR ? 64 * QS : D * TS];  // TR: Q  [tile query][d];   fp32: Q^T  [d][tile query]
-  T gt[TR ? 64 * QS : D * TS];  // TR: dO [tile query][d];   fp32: dO^T [d][tile query]
-  T pt[64 * TS];              // TR: w P [tile query][key]; fp32: (w P)^T [key][tile query]
-  T dat[64 * TS];             // TR: dA  [tile query][key]; fp32: dA^T  [key][tile query]
+  T kt[D * TS];                             // K^T   [d][key]
+  T qt[TR ? 64 * QS : D * TS];              // TR: Q  [tile query][d];   fp32: Q^T  [d][tile query]
+  T gt_[SPLIT ? 1 : (TR ? 64 * QS : D * TS)];  // TR: dO [tile query][d];   fp32: dO^T [d][tile query]
+  T pt[64 * TS];                            // TR: w P [tile query][key]; fp32: (w P)^T [key][tile query]
+  T dat_[SPLIT ? 1 : 64 * TS];              // TR: dA  [tile query][key]; fp32: dA^T  [key][tile query]
+  __device__ __forceinline__ T* gt() { return SPLIT ? qt : gt_; }
+  __device__ __forceinline__ const T* gt() const { return SPLIT ? qt : gt_; }
+  __device__ __forceinline__ T* dat() { return SPLIT ? pt : dat_; }
+  __device__ __forceinline__ const T* dat() const { return SPLIT ? pt : dat_; }
 };
 
 // The chunk's K and V rows as A fragments of S^T = K Q^T and dP^T = V dO^T: held in registers
@@ -254,65 +261,94 @@ __global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q,
       }
     }
     __syncthreads();  // previous tile's readers of the staged buffers are done
-    if constexpr (S::TR) {
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-        *reinterpret_cast<bf16x8_t*>(&s.qt[qi * S::QS + ks * 32 + 8 * g]) = in.qf[ks].v;
-        *reinterpret_cast<bf16x8_t*>(&s.gt[qi * S::QS + ks * 32 + 8 * g]) = in.gf[ks].v;
-      }
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        u16x4_t pw, da;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pw[i] = f32_to_bf16(w_q * sc[cb][i]);
-          da[i] = f32_to_bf16(dp[cb][i]);
-        }
-        *reinterpret_cast<u16x4_t*>(&s.pt[qi * S::TS + 16 * cb + 4 * g]) = pw;
-        *reinterpret_cast<u16x4_t*>(&s.dat[qi * S::TS + 16 * cb + 4 * g]) = da;
-      }
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          Elem<T>::store(s.qt, (ks * 32 + 8 * g + e) * S::TS + qi, in.qf[ks].get(e));
-          Elem<T>::store(s.gt, (ks * 32 + 8 * g + e) * S::TS + qi, in.gf[ks].get(e));
-        }
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = 16 * cb + 4 * g + i;
-          Elem<T>::store(s.pt, key * S::TS + qi, w_q * sc[cb][i]);
-          Elem<T>::store(s.dat, key * S::TS + qi, dp[cb][i]);
-        }
-    }
-    __syncthreads();
-    // this wave's 16 keys: dV += (wP)^T dO, dK += dA^T Q (contraction over the 64 tile queries)
-#pragma unroll
-    for (int kq = 0; kq < 2; ++kq) {
-      Frag<T> ap, ad;
+    // dO and w P (the dV operands); Q and dA (the dK operands)
+    auto stage_v = [&]() {
       if constexpr (S::TR) {
-        ap.load_tr(s.pt, S::TS, kq * 32 + 8 * g, 16 * wv, lane);
-        ad.load_tr(s.dat, S::TS, kq * 32 + 8 * g, 16 * wv, lane);
-      } else {
-        ap.load(&s.pt[(16 * wv + r16) * S::TS + kq * 32 + 8 * g]);
-        ad.load(&s.dat[(16 * wv + r16) * S::TS + kq * 32 + 8 * g]);
-      }
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        Frag<T> bg, bq;
-        if constexpr (S::TR) {
-          bg.load_tr(s.gt, S::QS, kq * 32 + 8 * g, 16 * db, lane);
-          bq.load_tr(s.qt, S::QS, kq * 32 + 8 * g, 16 * db, lane);
-        } else {
-          bg.load(&s.gt[(16 * db + r16) * S::TS + kq * 32 + 8 * g]);
-          bq.load(&s.qt[(16 * db + r16) * S::TS + kq * 32 + 8 * g]);
+        for (int ks = 0; ks < D / 32; ++ks)
+          *reinterpret_cast<bf16x8_t*>(&s.gt()[qi * S::QS + ks * 32 + 8 * g]) = in.gf[ks].v;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          u16x4_t pw;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pw[i] = f32_to_bf16(w_q * sc[cb][i]);
+          *reinterpret_cast<u16x4_t*>(&s.pt[qi * S::TS + 16 * cb + 4 * g]) = pw;
         }
-        mma(accV[db], ap, bg);
-        mma(accK[db], ad, bq);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) Elem<T>::store(s.gt(), (ks * 32 + 8 * g + e) * S::TS + qi, in.gf[ks].get(e));
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Elem<T>::store(s.pt, (16 * cb + 4 * g + i) * S::TS + qi, w_q * sc[cb][i]);
       }
+    };
+    auto stage_k = [&]() {
+      if constexpr (S::TR) {
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+          *reinterpret_cast<bf16x8_t*>(&s.qt[qi * S::QS + ks * 32 + 8 * g]) = in.qf[ks].v;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          u16x4_t da;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) da[i] = f32_to_bf16(dp[cb][i]);
+          *reinterpret_cast<u16x4_t*>(&s.dat()[qi * S::TS + 16 * cb + 4 * g]) = da;
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) Elem<T>::store(s.qt, (ks * 32 + 8 * g + e) * S::TS + qi, in.qf[ks].get(e));
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Elem<T>::store(s.dat(), (16 * cb + 4 * g + i) * S::TS + qi, dp[cb][i]);
+      }
+    };
+    // this wave's 16 keys: dV += (wP)^T dO, dK += dA^T Q (contraction over the 64 tile queries)
+    auto products = [&](auto vc, auto kc) {
+      constexpr bool DV = decltype(vc)::value != 0, DK = decltype(kc)::value != 0;
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) {
+        Frag<T> ap, ad;
+        if constexpr (S::TR) {
+          if constexpr (DV) ap.load_tr(s.pt, S::TS, kq * 32 + 8 * g, 16 * wv, lane);
+          if constexpr (DK) ad.load_tr(s.dat(), S::TS, kq * 32 + 8 * g, 16 * wv, lane);
+        } else {
+          if constexpr (DV) ap.load(&s.pt[(16 * wv + r16) * S::TS + kq * 32 + 8 * g]);
+          if constexpr (DK) ad.load(&s.dat()[(16 * wv + r16) * S::TS + kq * 32 + 8 * g]);
+        }
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+          Frag<T> bg, bq;
+          if constexpr (S::TR) {
+            if constexpr (DV) bg.load_tr(s.gt(), S::QS, kq * 32 + 8 * g, 16 * db, lane);
+            if constexpr (DK) bq.load_tr(s.qt, S::QS, kq * 32 + 8 * g, 16 * db, lane);
+          } else {
+            if constexpr (DV) bg.load(&s.gt()[(16 * db + r16) * S::TS + kq * 32 + 8 * g]);
+            if constexpr (DK) bq.load(&s.qt[(16 * db + r16) * S::TS + kq * 32 + 8 * g]);
+          }
+          if constexpr (DV) mma(accV[db], ap, bg);
+          if constexpr (DK) mma(accK[db], ad, bq);
+        }
+      }
+    };
+    if constexpr (S::SPLIT) {
+      stage_v();
+      __syncthreads();
+      products(IntC<1>{}, IntC<0>{});
+      __syncthreads();  // the dV operands are read: Q and dA take their buffers
+      stage_k();
+      __syncthreads();
+      products(IntC<0>{}, IntC<1>{});
+    } else {
+      stage_v();
+      stage_k();
+      __syncthreads();
+      products(IntC<1>{}, IntC<1>{});
     }
   };
   TileIn A, B;
@@ -669,9 +705,10 @@ hipError_t launch_bwd(int dt, int d, const void* Q, const void* Qr, const void* 
                                        scale, ws, st)
                    : bwd_t<bf16_t, 128>(Q, Qr, K, V, Klm, lf, mlm, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k,
                                         scale, ws, st);
-  // fp32 inputs: head dim 64 only (the fp32 LDS tiles of d = 128 exceed a workgroup's LDS)
-  if (d != 64) return hipErrorInvalidValue;
-  return bwd_t<float, 64>(Q, Qr, K, V, Klm, lf, mlm, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k, scale, ws, st);
+  return d == 64 ? bwd_t<float, 64>(Q, Qr, K, V, Klm, lf, mlm, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k,
+                                   scale, ws, st)
+                 : bwd_t<float, 128>(Q, Qr, K, V, Klm, lf, mlm, dO, idx, w, lse, dQ, dQr, dK, dV, dKlm, BH, L, N, k,
+                                     scale, ws, st);
 }
 
 }  // namespace hils

@@ -490,7 +490,6 @@ static hils_status bwd_impl(const void* Q, const void* Q_ret, const void* K, con
   hils_status st;
   if ((st = check_dims(B, H, L, d, C, topk, true, &D)) != HILS_OK) return st;
   if ((st = check_dt(dt)) != HILS_OK) return st;
-  if (dt == HILS_FP32 && d != 64) return fail(HILS_ERR_UNSUPPORTED, "fp32 backward supports head dim 64 only");
   if ((Q_ret == nullptr) != (dQ_ret == nullptr))
     return fail(HILS_ERR_INVALID_ARG, "Q_ret and dQ_ret must be given together");
   OPTIONAL_PTR(Q_ret);

@@ -120,7 +120,7 @@ hipError_t launch_decode_paged(int dt, int d, const void* q, const void* qr, con
 hipError_t launch_ml_selection(int dt, int d, const void* Qs, const void* Klm, int m, float* S, int32_t* idx,
                                float* sel, float* w, int BH, int L, int N, int k, int select, float scale,
                                hipStream_t st);
-// backward tail of several landmarks per chunk (1 <= m <= 4; fp32: d = 64): dKlm [BH][N][m][d] over each
+// backward tail of several landmarks per chunk (1 <= m <= 4): dKlm [BH][N][m][d] over each
 // chunk's pairs (the slots' score terms of dQs are added by the backward's dq_reduce)
 hipError_t launch_ml_bwd(int dt, int d, const void* Qs, const void* Klm, int m, const float* ds, const int* chunk_off,
                          const int* pairs, float* dKlm, int BH, int L, int N, int k, float scale, hipStream_t st);

@@ -332,8 +332,8 @@ hipError_t launch_ml_bwd(int dt, int d, const void* Qs, const void* Klm, int m, 
   if (dt == 0)
     return d == 64 ? ml_bwd_t<bf16_t, 64>(Qs, Klm, m, ds, chunk_off, pairs, dKlm, BH, L, N, k, scale, st)
                    : ml_bwd_t<bf16_t, 128>(Qs, Klm, m, ds, chunk_off, pairs, dKlm, BH, L, N, k, scale, st);
-  if (d != 64) return hipErrorInvalidValue;
-  return ml_bwd_t<float, 64>(Qs, Klm, m, ds, chunk_off, pairs, dKlm, BH, L, N, k, scale, st);
+  return d == 64 ? ml_bwd_t<float, 64>(Qs, Klm, m, ds, chunk_off, pairs, dKlm, BH, L, N, k, scale, st)
+                 : ml_bwd_t<float, 128>(Qs, Klm, m, ds, chunk_off, pairs, dKlm, BH, L, N, k, scale, st);
 }
 
 }  // namespace hils

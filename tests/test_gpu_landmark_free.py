@@ -128,6 +128,7 @@ def test_decode_landmark_free(hils, gpu, dtype, B, H, d, ctx, steps, k, rq):
     ("bf16", 1, 2, 2112, 64, 8, False),
     ("bf16", 1, 2, 1024, 128, 16, False),
     ("f32", 1, 2, 1024, 64, 4, False),
+    ("f32", 1, 1, 1024, 128, 4, False),
     ("bf16", 1, 2, 2112, 64, 8, True),
 ])
 def test_bwd_landmark_free(hils, gpu, dtype, B, H, L, d, k, rq):

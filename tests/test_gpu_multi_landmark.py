@@ -140,6 +140,7 @@ def test_fwd_multi_landmark_fixed_selection(hils, gpu):
     ("bf16", 1, 2, 1024, 128, 16, "firstlast", 2, False),
     ("f32", 1, 2, 1024, 64, 4, "firstlast", 2, False),
     ("bf16", 1, 2, 2048, 64, 8, "random", 3, True),
+    ("f32", 1, 1, 1024, 128, 4, "firstlast", 2, False),
 ])
 def test_bwd_multi_landmark(hils, gpu, dtype, B, H, L, d, k, kind, m, rq):
     say(f"bwd several landmarks dtype={dtype} B={B} H={H} L={L} d={d} k={k} landmarks={kind}x{m} retrieval={rq}")

@@ -71,10 +71,8 @@ def test_fwd_retrieval_query_equal_to_q(hils, gpu):
     assert err < 1e-5
 
 
-@pytest.mark.parametrize("dtype,B,H,L,d,k", CASES)
+@pytest.mark.parametrize("dtype,B,H,L,d,k", CASES + [("f32", 1, 1, 1024, 128, 4)])
 def test_bwd_retrieval_query(hils, gpu, dtype, B, H, L, d, k):
-    if dtype == "f32" and d != 64:
-        pytest.skip("fp32 backward: head dim 64 only")
     say(f"bwd retrieval query dtype={dtype} B={B} H={H} L={L} d={d} k={k}")
     x = synth.prefill_inputs(B, H, L, d, C=64, seed=520 + L + d, dtype=dtype, with_dO=True, with_qret=True)
     t = to_inputs(x, ("Q", "Q_ret", "K", "V", "Klm", "dO"))
