@@ -92,8 +92,11 @@ template <typename T, int D> struct KVFrags<T, D, false> {
   }
 };
 
+// bf16 at d = 64: two workgroups per CU, whose 256 registers a lane then all sit in the vector
+// file (unbounded, the compiler puts the tile products in accumulator registers and reads each
+// one back)
 template <typename T, int D>
-__global__ __launch_bounds__(256) void chunk_bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(256, sizeof(T) == 2 && D == 64 ? 2 : 1) void chunk_bwd_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                         const T* __restrict__ V, const T* __restrict__ Klm,
                                                         const T* __restrict__ dO, const float* __restrict__ w,
                                                         const float* __restrict__ lse,
