@@ -21,6 +21,11 @@
 // or above it.  The exact top-m is then ranked out of the few survivors.  A
 // query with more survivors than fit in LDS (possible only with many exactly
 // tied scores) falls back to m exact arg-max sweeps.
+// With several landmarks per chunk (the summary's "Input & chunking" and "Key
+// modules" item 1) a chunk's score is the log-sum-exp of its landmark scores;
+// up to 129 chunks the selection kernel forms those itself from the MFMA
+// products of every landmark (topk_select_ml), longer sequences take the
+// separate score and selection kernels of multi_landmark.hip.
 #include "hils_device.h"
 #include "hils_launch.h"
 
