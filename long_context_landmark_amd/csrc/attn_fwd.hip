@@ -136,7 +136,10 @@ template <typename T, int D> constexpr int frags_in_regs() {
 // chunk).  Returns o = wt * softmax(scale * q K^T) V (4 rows of d per 16-d block; wt is the
 // lane's query weight), the row's scaled maximum and its sum of exponentials relative to it.
 // The exponentials are exp2 of one fused multiply-add: scale * log2(e) is folded into the
-// raw scores, and wt / sum into the probabilities before they are rounded for the PV product.
+// raw scores.  16-bit inputs: they are rounded for the PV product unnormalised, and the row sums
+// come from the same rounded values on the MFMA (a block of ones in place of V^T), so the
+// weights that multiply V sum to one; wt / sum then scales the products.  fp32 inputs (whose
+// fp32 MFMA is slow): the sums are added on the VALU and wt / sum scales the probabilities.
 template <typename T, int D, int REG>
 __device__ __forceinline__ void wave_chunk_attention(const ChunkLds<T, D>& s, const ChunkFrags<T, D, REG>& cf,
                                                      const Frag<T> (&qf)[D / 32], float scale, int causal_q, float wt,
@@ -162,34 +165,64 @@ __device__ __forceinline__ void wave_chunk_attention(const ChunkLds<T, D>& s, co
   mraw = fmaxf(mraw, lane_xor(mraw, 32));
   const float c2 = scale * 1.44269504088896341f;  // scale * log2(e)
   const float off = -mraw * c2;
-  sum = 0.f;
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(sc[cb][i], c2, off));
-      sc[cb][i] = p;
-      sum += p;
-    }
-  sum += lane_xor(sum, 16);
-  sum += lane_xor(sum, 32);
+    for (int i = 0; i < 4; ++i) sc[cb][i] = __builtin_amdgcn_exp2f(fmaf(sc[cb][i], c2, off));
   mx = scale * mraw;
-  const float f = wt * __builtin_amdgcn_rcpf(sum);
   // O^T[d][q] = sum_key V^T[d][key] P^T[key][q]; element e of lane group g is key 32h + 16(e/4) + 4g + e%4
-  Frag<T> pf[2];
+  if constexpr (Elem<T>::bytes == 4) {
+    sum = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum += sc[cb][i];
+    sum += lane_xor(sum, 16);
+    sum += lane_xor(sum, 32);
+    const float f = wt * __builtin_amdgcn_rcpf(sum);
+    Frag<T> pf[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] = f * sc[2 * h + e / 4][e % 4];
+      pf[h].set(pv);
+    }
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      o[db] = zero4();
+#pragma unroll
+      for (int h = 0; h < 2; ++h) mma(o[db], cf.v(s, db, h), pf[h]);
+    }
+    return;
+  }
+  Frag<T> pf[2], ones;
+  {
+    float one[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) one[e] = 1.f;
+    ones.set(one);
+  }
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     float pv[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pv[e] = f * sc[2 * h + e / 4][e % 4];
+    for (int e = 0; e < 8; ++e) pv[e] = sc[2 * h + e / 4][e % 4];
     pf[h].set(pv);
   }
+  f32x4_t rs = zero4();  // every row of it: the lane's query's sum over the 64 keys
+#pragma unroll
+  for (int h = 0; h < 2; ++h) mma(rs, ones, pf[h]);
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) {
     o[db] = zero4();
 #pragma unroll
     for (int h = 0; h < 2; ++h) mma(o[db], cf.v(s, db, h), pf[h]);
   }
+  sum = rs[0];
+  const float f = wt * __builtin_amdgcn_rcpf(sum);
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) o[db] = f * o[db];
 }
 
 template <typename T, int D, bool STREAM_OUT>
