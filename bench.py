@@ -48,10 +48,10 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     # workload: {kernel: (FETCH_SIZE KiB, WRITE_SIZE KiB, source digest)}
-    "prefill_8k": {"chunk_attn_fwd": (28609.3, 130571.7, "292684829ec4835a"), "topk_select": (8433.1, 13829.1, "8627482025ee6375"), "own_combine": (92230.4, 16384.0, "292684829ec4835a")},
-    "prefill_128k": {"chunk_attn_fwd": (8514752.1, 17019380.3, "292684829ec4835a"), "topk_select": (533164.4, 835600.4, "8627482025ee6375"), "own_combine": (10197158.1, 1048576.0, "292684829ec4835a")},
-    "train_8k": {"chunk_bwd": (238399.0, 907126.6, "c98a95fc53c96470"), "chunk_attn_fwd": (105707.1, 522560.5, "292684829ec4835a"), "dq_reduce": (326652.2, 149735.3, "c98a95fc53c96470")},
-    "decode_512k": {"decode_scan": (8264.2, 68.0, "8aa435acddc0f2e9"), "decode_attend": (2434.6, 34.1, "8aa435acddc0f2e9")},
+    "prefill_8k": {"chunk_attn_fwd": (28606.2, 130612.3, "a3092f13320f3339"), "topk_select": (8432.9, 13824.0, "c24c40baa9643cf4"), "own_combine": (92234.5, 16384.0, "a3092f13320f3339")},
+    "prefill_128k": {"chunk_attn_fwd": (8508892.9, 17016466.1, "a3092f13320f3339"), "topk_select": (533183.5, 835601.1, "c24c40baa9643cf4"), "own_combine": (10197151.7, 1048576.0, "a3092f13320f3339")},
+    "train_8k": {"chunk_bwd": (235751.2, 899156.8, "4df19b530d1d611d"), "chunk_attn_fwd": (105704.1, 522531.0, "a3092f13320f3339"), "dq_reduce": (326649.2, 149727.2, "4df19b530d1d611d")},
+    "decode_512k": {"decode_scan": (8264.2, 68.0, "8aa435acddc0f2e9"), "decode_attend": (2434.7, 34.1, "8aa435acddc0f2e9")},
 }
 
 
