@@ -195,3 +195,23 @@ def test_decode_multi_landmark(hils, gpu, dtype, H, d, ctx, steps, k, m):
 
         check_decode_step(f"step {s}", idx.cpu().numpy().reshape(H, k + 1), f32(w).reshape(H, k + 1),
                           f32(o).reshape(H, d), ref, step, [c] * H, past, k, bar)
+
+
+@pytest.mark.parametrize("L", [2048, 10240])
+def test_multi_landmark_deterministic(hils, gpu, L):
+    """Two runs of the several-landmark forward and backward agree bit for bit: the one-kernel selection
+    (up to 129 chunks) and the separate score and selection kernels, and dq_reduce's landmark terms."""
+    B, H, d, k = 1, 2, 64, 8
+    say(f"several landmarks, determinism L={L}")
+    x = synth.prefill_inputs(B, H, L, d, C=64, seed=840 + L, dtype="bf16", with_dO=True)
+    lm = dev(_landmarks(x, "random", 3, seed=841))
+    t = to_inputs(x, ("Q", "K", "V", "dO"))
+    runs = []
+    for _ in range(2):
+        fw = hils.sparse_attn_fwd_ml(t["Q"], t["K"], t["V"], lm, k, save_for_backward=True)
+        O, idx, sel, w, lse = fw
+        g = hils.sparse_attn_bwd_ml(t["Q"], t["K"], t["V"], lm, t["dO"], idx, w, lse, k)
+        torch.cuda.synchronize()
+        runs.append(tuple(fw) + tuple(g))
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
