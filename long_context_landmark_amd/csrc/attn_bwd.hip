@@ -47,11 +47,12 @@ template <typename T, int D> struct alignas(16) BwdLds {
   static constexpr int QS = D + 8;                               // TR: rows of D (tile query, d)
   T k[64 * KS];
   T v[64 * KS];
-  T kt[D * TS];                             // K^T   [d][key]
-  T qt[TR ? 64 * QS : D * TS];              // TR: Q  [tile query][d];   fp32: Q^T  [d][tile query]
-  T gt_[SPLIT ? 1 : (TR ? 64 * QS : D * TS)];  // TR: dO [tile query][d];   fp32: dO^T [d][tile query]
-  T pt[64 * TS];                            // TR: w P [tile query][key]; fp32: (w P)^T [key][tile query]
-  T dat_[SPLIT ? 1 : 64 * TS];              // TR: dA  [tile query][key]; fp32: dA^T  [key][tile query]
+  static constexpr int UNUSED = 16 / (int)sizeof(T);  // one 16-byte piece keeps the next array aligned
+  T kt[D * TS];                                // K^T   [d][key]
+  T qt[TR ? 64 * QS : D * TS];                 // TR: Q  [tile query][d];   fp32: Q^T  [d][tile query]
+  T gt_[SPLIT ? UNUSED : (TR ? 64 * QS : D * TS)];  // TR: dO [tile query][d];   fp32: dO^T [d][tile query]
+  T pt[64 * TS];                               // TR: w P [tile query][key]; fp32: (w P)^T [key][tile query]
+  T dat_[SPLIT ? UNUSED : 64 * TS];            // TR: dA  [tile query][key]; fp32: dA^T  [key][tile query]
   __device__ __forceinline__ T* gt() { return SPLIT ? qt : gt_; }
   __device__ __forceinline__ const T* gt() const { return SPLIT ? qt : gt_; }
   __device__ __forceinline__ T* dat() { return SPLIT ? pt : dat_; }
