@@ -261,9 +261,9 @@ hils_status hils_decode_step_lf(const void* q, const void* q_ret, const void* k_
  * chunk-level one).  K_lm is [B][H][N][m][d] (dt), 1 <= m <= 16; the chunk
  * score is the log-sum-exp of its m landmark scores, for the past chunks and
  * the own chunk alike; with m = 1 it is the plain score.  Otherwise as
- * hils_sparse_attn_fwd_rq (Q_ret may be null).  The causal chunk scores are
- * materialised in the workspace: hils_workspace_size(HILS_OP_FWD_ML, ...)
- * bytes, B*H*L*N*4 more than HILS_OP_FWD.
+ * hils_sparse_attn_fwd_rq (Q_ret may be null).  No chunk score matrix is
+ * formed; workspace: hils_workspace_size(HILS_OP_FWD_ML, ...) bytes, the same
+ * as HILS_OP_FWD.
  */
 hils_status hils_sparse_attn_fwd_ml(const void* Q, const void* Q_ret, const void* K, const void* V, const void* K_lm,
                                     int64_t m, int32_t* idx, float* sel_score, int select, void* O, float* w_out,

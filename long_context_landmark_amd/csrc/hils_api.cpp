@@ -108,7 +108,6 @@ size_t carve_route(Carver& cv, const Dims& D, hils::RouteBufs& rb, int ppi) {
   return cv.off;
 }
 
-size_t ml_scores_bytes(const Dims& D) { return (size_t)D.B * D.H * D.L * D.N * sizeof(float); }
 
 // esz: bytes per element of the per-pair intermediate rows (2: 16-bit inputs, 4: fp32 inputs)
 size_t carve_fwd(void* base, const Dims& D, FwdWs* ws, int esz) {
@@ -193,10 +192,10 @@ size_t hils_workspace_size(int op, int64_t B, int64_t H, int64_t L, int64_t d, i
       FwdWs ws;
       return carve_fwd(nullptr, D, &ws, esz);
     }
-    case HILS_OP_FWD_ML: {
+    case HILS_OP_FWD_ML: {  // as the plain forward: no score matrix is formed
       if (check_dims(B, H, L, d, C, topk, true, &D) != HILS_OK) return 0;
       FwdWs ws;
-      return align_up(carve_fwd(nullptr, D, &ws, esz)) + ml_scores_bytes(D);
+      return carve_fwd(nullptr, D, &ws, esz);
     }
     case HILS_OP_BWD: {
       if (check_dims(B, H, L, d, C, topk, true, &D) != HILS_OK) return 0;
@@ -327,12 +326,9 @@ static hils_status fwd_impl(const void* Q, const void* Q_ret, const void* K, con
   if (!(scale > 0.f)) return fail(HILS_ERR_INVALID_ARG, "scale must be positive");
   FwdWs W;
   const int esz = dt == HILS_FP32 ? 4 : 2;
-  const size_t need0 = carve_fwd(nullptr, D, &W, esz);
-  // several landmarks per chunk: the causal chunk scores are materialised after the plain workspace
-  const size_t need = mlm > 0 ? align_up(need0) + ml_scores_bytes(D) : need0;
+  const size_t need = carve_fwd(nullptr, D, &W, esz);
   if ((st = check_ws(ws, ws_bytes, need)) != HILS_OK) return st;
   carve_fwd(ws, D, &W, esz);
-  float* S_ml = mlm > 0 ? reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(need0)) : nullptr;
   const int BH = (int)(B * H), iL = (int)L, iN = (int)D.N, ik = (int)topk, id = (int)d;
   hipStream_t s = (hipStream_t)stream;
   float* w = w_out ? w_out : W.w_tmp;
@@ -343,8 +339,7 @@ static hils_status fwd_impl(const void* Q, const void* Q_ret, const void* K, con
   if (lf && (e = hils::launch_chunk_means(dt, id, K, (void*)K_lm, BH, L, D.N, iN, s)) != hipSuccess)
     return hip_status(e, "hils_sparse_attn_fwd: chunk means");
   if (mlm > 0)
-    e = hils::launch_ml_selection(dt, id, Qs, K_lm, (int)mlm, S_ml, idx, sel_score, w, BH, iL, iN, ik, select, scale,
-                                  s);
+    e = hils::launch_ml_selection(dt, id, Qs, K_lm, (int)mlm, idx, sel_score, w, BH, iL, iN, ik, select, scale, s);
   else if (select) e = hils::launch_topk(dt, id, Qs, K_lm, W.klm_frag, idx, sel_score, w, BH, iL, iN, ik, scale, s);
   else e = hils::launch_fixed_selection(dt, id, Qs, K_lm, idx, sel_score, w, BH, iL, iN, ik, scale, s);
   if (e != hipSuccess) return hip_status(e, "hils_sparse_attn_fwd: selection");

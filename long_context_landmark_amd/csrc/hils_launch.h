@@ -24,9 +24,8 @@ hipError_t launch_landmark_scores(int dt, int d, const void* Q, const void* Klm,
 size_t topk_workspace_bytes(int BH, int N, int d);
 hipError_t launch_topk(int dt, int d, const void* Q, const void* Klm, void* frag_ws, int32_t* idx, float* sel,
                        float* w, int BH, int L, int N, int k, float scale, hipStream_t st);
-// several landmarks per chunk (Klm [BH][N][mlm][d]) with the selection done in one kernel that forms the
-// log-sum-exp chunk scores itself; only when topk_ml_fused(N) (at most two candidate tiles per query chunk)
-bool topk_ml_fused(int N);
+// several landmarks per chunk (Klm [BH][N][mlm][d]): the selection kernel forming the log-sum-exp chunk
+// scores itself
 hipError_t launch_topk_ml(int dt, int d, const void* Q, const void* Klm, int mlm, int32_t* idx, float* sel, float* w,
                           int BH, int L, int N, int k, float scale, hipStream_t st);
 // scores and weights of a caller-given selection (slots with idx < 0 are unused)
@@ -114,12 +113,10 @@ hipError_t launch_decode_paged(int dt, int d, const void* q, const void* qr, con
                                void* Kp, void* Vp, void* Klm_p, bool lf, int mlm, const int32_t* page_table, int max_pages,
                                int64_t pages, const int64_t* n_ctx, int64_t n_max, int B, int H, void* o,
                                int32_t* idx, float* w, int k, float scale, const DecodeBufs& ws, hipStream_t st);
-// several landmarks per chunk (Klm [BH][N][m][d]): causal chunk scores (log-sum-exp over a chunk's landmarks)
-// into S [BH][L][N], then the selection (select = 1) or the scores of the caller's idx, and the weights;
-// a selection with topk_ml_fused(N) goes to launch_topk_ml and leaves S untouched
-hipError_t launch_ml_selection(int dt, int d, const void* Qs, const void* Klm, int m, float* S, int32_t* idx,
-                               float* sel, float* w, int BH, int L, int N, int k, int select, float scale,
-                               hipStream_t st);
+// several landmarks per chunk (Klm [BH][N][m][d]): the selection (select = 1) or the scores of the caller's
+// idx (select = 0), and the weights; the chunk score is the log-sum-exp of its landmark scores
+hipError_t launch_ml_selection(int dt, int d, const void* Qs, const void* Klm, int m, int32_t* idx, float* sel,
+                               float* w, int BH, int L, int N, int k, int select, float scale, hipStream_t st);
 // backward tail of several landmarks per chunk (1 <= m <= 4): dKlm [BH][N][m][d] over each
 // chunk's pairs (the slots' score terms of dQs are added by the backward's dq_reduce)
 hipError_t launch_ml_bwd(int dt, int d, const void* Qs, const void* Klm, int m, const float* ds, const int* chunk_off,

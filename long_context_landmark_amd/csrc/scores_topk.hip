@@ -23,9 +23,8 @@
 // tied scores) falls back to m exact arg-max sweeps.
 // With several landmarks per chunk (the summary's "Input & chunking" and "Key
 // modules" item 1) a chunk's score is the log-sum-exp of its landmark scores;
-// up to 129 chunks the selection kernel forms those itself from the MFMA
-// products of every landmark (topk_select_ml), longer sequences take the
-// separate score and selection kernels of multi_landmark.hip.
+// the selection kernel forms those itself from the MFMA products of every
+// landmark (topk_select_ml), in both sweeps, so no score matrix is written.
 #include "hils_device.h"
 #include "hils_launch.h"
 
@@ -133,15 +132,15 @@ constexpr int TK_SMALL_N = 129;  // up to this many chunks a query chunk has at 
 // every 64-chunk landmark tile against all 64 queries.
 // SMALL: every query chunk has at most two landmark tiles of candidates (N <= 129 chunks);
 // the score tiles of sweep 1 are then kept in registers for sweep 2.
-// ML (with SMALL): mlm landmarks per chunk (rows j * mlm + u); a chunk's score is the log-sum-exp of
-// its landmark scores, folded over the landmarks in order as the separate score kernel of the
-// several-landmark path does, so that the kept tiles hold finished scores instead of raw products.
+// ML: mlm landmarks per chunk (rows j * mlm + u); a chunk's score is the log-sum-exp of its landmark
+// scores, folded over the landmarks in order, so that the score tiles the sweeps see hold finished
+// scores instead of raw products (short lists keep them in registers, long ones recompute them in
+// each sweep; long lists read the landmark rows directly, without the fragment-order copy).
 template <typename T, int D, bool SMALL, bool ML = false>
-__global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : (ML && D == 128 ? 2 : 3)) : 1) void topk_select_kernel(const T* __restrict__ Q, const T* __restrict__ Klm,
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : ((ML && D == 128) ? 2 : 3)) : 1) void topk_select_kernel(const T* __restrict__ Q, const T* __restrict__ Klm,
                                                           const T* __restrict__ F, int32_t* __restrict__ idx,
                                                           float* __restrict__ sel, float* __restrict__ wout, int L,
                                                           int N, int k, float scale, int mlm) {
-  static_assert(!ML || SMALL, "several landmarks only with short candidate lists");
   const int nc = L / 64;
   int xi, bh;
   xcd_map(xi, bh);  // a head's landmark rows are re-read by all its query chunks: keep them in one L2
@@ -156,7 +155,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : (ML
   auto sc = [&](float x) { return ML ? x : scale * x; };
   // bf16 landmarks of long candidate lists are read from their fragment-order copy (one
   // 1 KiB run per fragment load); with at most two tiles the direct loads are kept
-  constexpr bool FRAG = sizeof(T) == 2 && !SMALL;
+  constexpr bool FRAG = sizeof(T) == 2 && !SMALL && !ML;
   const T* Fb = FRAG ? F + (int64_t)bh * klm_frag_rows(N) * D : nullptr;
 
   // the group maxima (sweep 1), the survivors (sweep 2) and the sorted top keys share storage
@@ -237,12 +236,6 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : (ML
     sweep_from(a0, visit);
   };
 
-  // the first landmark tile and the own-chunk operands are requested before anything waits
-  Frag<T> first_tile[D / 32], second_tile[SMALL && !ML ? D / 32 : 1];
-  if (m > 0) {
-    load_tile(tile_at(0), first_tile);
-    if constexpr (SMALL && !ML) load_tile(min(1, ntile - 1), second_tile);
-  }
   // one landmark's score a folded into the running maximum mx and sum z = sum exp(score - mx)
   // (from mx = -inf, z = 0): one exponential of the lesser minus the greater of a and mx
   auto lse_fold = [](float a, float& mx, float& z) {
@@ -250,6 +243,54 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : (ML
     z = a > mx ? z * e + 1.f : z + e;
     mx = hi;
   };
+  // several landmarks, long candidate lists: every tile's landmarks in turn, folded into a running
+  // log-sum-exp per (query, chunk) whose result the visitor sees; the next landmark rows (or the
+  // next tile's first) are requested before the current products
+  auto ml_sweep = [&](auto&& visit) {
+    Frag<T> cur[D / 32], nxt[D / 32];
+    load_tile(tile_at(0), cur, 0);
+    for (int i = 0; i < ntile; ++i) {
+      const int tile = tile_at(i);
+      float mx[4][4], z[4][4];
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          mx[qb][e] = -INFINITY;
+          z[qb][e] = 0.f;
+        }
+      for (int u = 0; u < mlm; ++u) {
+        const bool more = u + 1 < mlm || i + 1 < ntile;
+        if (u + 1 < mlm) load_tile(tile, nxt, u + 1);
+        else if (i + 1 < ntile) load_tile(tile_at(i + 1), nxt, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+          f32x4_t cc = zero4();
+#pragma unroll
+          for (int ks = 0; ks < D / 32; ++ks) mma(cc, cur[ks], qf[qb][ks]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lse_fold(scale * cc[e], mx[qb][e], z[qb][e]);
+        }
+        if (more) {
+#pragma unroll
+          for (int ks = 0; ks < D / 32; ++ks) cur[ks] = nxt[ks];
+        }
+      }
+      f32x4_t acc[4];
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[qb][e] = mlm == 1 ? mx[qb][e] : mx[qb][e] + __logf(z[qb][e]);
+      visit(tile, acc);
+    }
+  };
+  // the first landmark tile and the own-chunk operands are requested before anything waits
+  Frag<T> first_tile[D / 32], second_tile[SMALL && !ML ? D / 32 : 1];
+  if ((SMALL || !ML) && m > 0) {
+    load_tile(tile_at(0), first_tile);
+    if constexpr (SMALL && !ML) load_tile(min(1, ntile - 1), second_tile);
+  }
   // own-chunk scores.  When chunk c lies in the last candidate tile (c not a multiple of 64) the
   // first sweep's products hold them: the lane that holds (query, c) stores them.  Otherwise
   // wave 0 forms them from the query fragments already held: lane (r16, g) takes the elements
@@ -324,7 +365,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : (ML
         }
       }
     };
-    if constexpr (ML) {
+    if constexpr (ML && SMALL) {
       // a tile's landmarks in order, folded into a running log-sum-exp that ends in its kept
       // tile; the next landmark rows (or the next tile's first) are requested before the
       // current products.  The second tile runs only when it holds candidates.
@@ -371,6 +412,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : (ML
       mma_tile(second_tile, keep1);
       group_max(0, keep0);
       if (ntile > 1) group_max(1, keep1);
+    } else if constexpr (ML) {
+      ml_sweep([&](int tile, f32x4_t(&acc)[4]) { group_max(tile, acc); });
     } else {
       sweep_from(first_tile, [&](int tile, f32x4_t(&acc)[4]) { group_max(tile, acc); });
     }
@@ -401,7 +444,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : (ML
         if (e == m - 1) tau = v[e];
       // long lists test raw accumulators against the least float a0 with fl(scale * a0) >= tau
       // (see below): one lane per query forms it, once
-      if (part == 0) tau_s[q] = SMALL ? tau : least_raw_bound(tau, scale);
+      if (part == 0) tau_s[q] = (SMALL || ML) ? tau : least_raw_bound(tau, scale);
     }
     __syncthreads();
     // sweep 2: keep the candidates at or above the bound.  The rounded product scale * a is
@@ -424,7 +467,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : (ML
       for (int qb = 0; qb < 4; ++qb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          bits |= ((SMALL ? sc(acc[qb][i]) : acc[qb][i]) >= a0[qb] && (whole || jb + i < c)) ? (1u << (4 * qb + i))
+          bits |= (((SMALL || ML) ? sc(acc[qb][i]) : acc[qb][i]) >= a0[qb] && (whole || jb + i < c)) ? (1u << (4 * qb + i))
                                                                                             : 0u;
       if (!__any(bits != 0)) return;
       // long lists: the wave parks its accumulators in LDS (four 16-byte stores a lane) and
@@ -463,6 +506,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : (ML
     if constexpr (SMALL) {
       survive(0, keep0);
       if (ntile > 1) survive(1, keep1);
+    } else if constexpr (ML) {
+      ml_sweep([&](int tile, f32x4_t(&acc)[4]) { survive(tile, acc); });
     } else {
       sweep([&](int tile, f32x4_t(&acc)[4]) { survive(tile, acc); });
     }
@@ -547,10 +592,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : (ML
             if (best) atomicMax((unsigned long long*)&best_s[q], (unsigned long long)best);
           }
         };
-        // several-landmark scores are not recomputed: the kept tiles hold them
-        if constexpr (ML) {
+        // short several-landmark lists are not recomputed: the kept tiles hold them
+        if constexpr (ML && SMALL) {
           least_below(0, keep0);
           if (ntile > 1) least_below(1, keep1);
+        } else if constexpr (ML) {
+          ml_sweep([&](int tile, f32x4_t(&acc)[4]) { least_below(tile, acc); });
         } else {
           sweep([&](int tile, f32x4_t(&acc)[4]) { least_below(tile, acc); });
         }
@@ -639,9 +686,12 @@ hipError_t launch_topk_t(const void* Q, const void* Klm, void* frag_ws, int32_t*
 template <typename T, int D>
 hipError_t launch_topk_ml_t(const void* Q, const void* Klm, int mlm, int32_t* idx, float* sel, float* w, int BH,
                             int L, int N, int k, float scale, hipStream_t st) {
-  if (N > TK_SMALL_N) return hipErrorInvalidValue;
-  HILS_LAUNCH("topk_select_ml", (topk_select_kernel<T, D, true, true>), dim3(L / 64, BH), dim3(256), 0, st,
-              (const T*)Q, (const T*)Klm, (const T*)nullptr, idx, sel, w, L, N, k, scale, mlm);
+  if (N <= TK_SMALL_N)
+    HILS_LAUNCH("topk_select_ml", (topk_select_kernel<T, D, true, true>), dim3(L / 64, BH), dim3(256), 0, st,
+                (const T*)Q, (const T*)Klm, (const T*)nullptr, idx, sel, w, L, N, k, scale, mlm);
+  else
+    HILS_LAUNCH("topk_select_ml", (topk_select_kernel<T, D, false, true>), dim3(L / 64, BH), dim3(256), 0, st,
+                (const T*)Q, (const T*)Klm, (const T*)nullptr, idx, sel, w, L, N, k, scale, mlm);
   return hipGetLastError();
 }
 
@@ -652,8 +702,6 @@ hipError_t launch_landmark_scores(int dt, int d, const void* Q, const void* Klm,
   return d == 64 ? launch_landmark_scores_t<float, 64>(Q, Klm, S, BH, L, N, scale, st)
                  : launch_landmark_scores_t<float, 128>(Q, Klm, S, BH, L, N, scale, st);
 }
-
-bool topk_ml_fused(int N) { return N <= TK_SMALL_N; }
 
 hipError_t launch_topk_ml(int dt, int d, const void* Q, const void* Klm, int mlm, int32_t* idx, float* sel, float* w,
                           int BH, int L, int N, int k, float scale, hipStream_t st) {

@@ -59,12 +59,15 @@ def _check_sets(gi, ri, Qs, lm, k):
     ("bf16", 1, 2, 1024, 128, 16, "firstlast", 2),
     ("f32", 1, 2, 1024, 64, 4, "firstlast", 2),
     ("bf16", 1, 2, 2048, 64, 8, "random", 3),
-    # 129 chunks: the most the one-kernel selection takes (query chunks 64 and 128 score their own
-    # chunk outside the candidate tiles); 160 chunks: separate score matrix and selection kernels
+    # 129 chunks: the most that keep both score tiles in registers (query chunks 64 and 128 score
+    # their own chunk outside the candidate tiles); from 160 chunks on the sweeps recompute them
     ("bf16", 1, 2, 8256, 64, 4, "random", 2),
     ("bf16", 1, 1, 4160, 128, 16, "random", 3),
     ("f32", 1, 1, 4160, 128, 8, "firstlast", 2),
     ("bf16", 1, 1, 10240, 64, 8, "firstlast", 2),
+    # long candidate lists: landmark rows read directly, scores recomputed in each sweep
+    ("bf16", 1, 1, 64 * 200, 128, 16, "random", 3),
+    ("f32", 1, 1, 64 * 140, 64, 4, "random", 2),
 ])
 def test_fwd_multi_landmark(hils, gpu, dtype, B, H, L, d, k, kind, m):
     say(f"fwd several landmarks dtype={dtype} B={B} H={H} L={L} d={d} k={k} landmarks={kind}x{m}")
@@ -100,7 +103,7 @@ def test_fwd_multi_landmark(hils, gpu, dtype, B, H, L, d, k, kind, m):
 def test_fwd_multi_landmark_ties(hils, gpu, L):
     """Every chunk has the same landmarks, so all chunk scores tie and each query keeps the lowest
     indices; with more than 64 tied candidates the survivor list overflows and the exact
-    fallback of the selection runs."""
+    fallback of the selection runs (short lists: over the kept tiles; long ones: recomputed)."""
     B, H, d, k = 1, 1, 64, 8
     say(f"fwd several landmarks, all scores tied, L={L}")
     x = synth.prefill_inputs(B, H, L, d, C=64, seed=830, dtype="bf16")
@@ -199,8 +202,8 @@ def test_decode_multi_landmark(hils, gpu, dtype, H, d, ctx, steps, k, m):
 
 @pytest.mark.parametrize("L", [2048, 10240])
 def test_multi_landmark_deterministic(hils, gpu, L):
-    """Two runs of the several-landmark forward and backward agree bit for bit: the one-kernel selection
-    (up to 129 chunks) and the separate score and selection kernels, and dq_reduce's landmark terms."""
+    """Two runs of the several-landmark forward and backward agree bit for bit, with short (tiles kept
+    in registers) and long candidate lists, and dq_reduce's landmark terms."""
     B, H, d, k = 1, 2, 64, 8
     say(f"several landmarks, determinism L={L}")
     x = synth.prefill_inputs(B, H, L, d, C=64, seed=840 + L, dtype="bf16", with_dO=True)
