@@ -243,6 +243,15 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : ((M
     z = a > mx ? z * e + 1.f : z + e;
     mx = hi;
   };
+  // landmark u's score: the first one starts the fold without an exponential (the same values)
+  auto lse_fold_u = [&](int u, float a, float& mx, float& z) {
+    if (u == 0) {
+      mx = a;
+      z = 1.f;
+    } else {
+      lse_fold(a, mx, z);
+    }
+  };
   // several landmarks, long candidate lists: every tile's landmarks in turn, folded into a running
   // log-sum-exp per (query, chunk) whose result the visitor sees; the next landmark rows (or the
   // next tile's first) are requested before the current products
@@ -270,7 +279,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : ((M
 #pragma unroll
           for (int ks = 0; ks < D / 32; ++ks) mma(cc, cur[ks], qf[qb][ks]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) lse_fold(scale * cc[e], mx[qb][e], z[qb][e]);
+          for (int e = 0; e < 4; ++e) lse_fold_u(u, scale * cc[e], mx[qb][e], z[qb][e]);
         }
         if (more) {
 #pragma unroll
@@ -308,7 +317,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? ((SMALL && D == 64) ? 4 : ((M
       f32x4_t cc[4];
       mma_tile(lf, cc);
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) lse_fold(scale * cc[qb][0], omx[qb], oz[qb]);
+      for (int qb = 0; qb < 4; ++qb) lse_fold_u(u, scale * cc[qb][0], omx[qb], oz[qb]);
     }
     if (g == 0) {
 #pragma unroll
