@@ -218,3 +218,25 @@ def test_multi_landmark_deterministic(hils, gpu, L):
         runs.append(tuple(fw) + tuple(g))
     for a, b in zip(*runs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("L", [8256, 10240])
+def test_one_landmark_matches_plain_forward(hils, gpu, L):
+    """With m = 1 the chunk score is the landmark score itself: the several-landmark selection picks the
+    same chunks as the plain one (the candidate scores come from the same MFMA products), and scores,
+    weights and outputs agree to rounding (the own chunk is scored on another unit for some query
+    chunks)."""
+    B, H, d, k = 1, 2, 64, 8
+    say(f"one landmark against the plain forward, L={L}")
+    x = synth.prefill_inputs(B, H, L, d, C=64, seed=850 + L, dtype="bf16")
+    t = to_inputs(x, ("Q", "K", "V", "Klm"))
+    a = hils.sparse_attn_fwd(t["Q"], t["K"], t["V"], t["Klm"], k, save_for_backward=True)
+    b = hils.sparse_attn_fwd_ml(t["Q"], t["K"], t["V"], t["Klm"][:, :, :, None, :].contiguous(), k,
+                                save_for_backward=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[1], b[1])
+    used = a[1].cpu().numpy() >= 0  # unused slots hold -inf scores in both
+    assert np.array_equal(np.isneginf(f32(a[2])), ~used) and np.array_equal(np.isneginf(f32(b[2])), ~used)
+    assert np.abs(f32(a[2])[used] - f32(b[2])[used]).max() < 1e-4
+    assert np.abs(f32(a[3]) - f32(b[3])).max() < 1e-4
+    assert_close(f32(b[0]), f32(a[0]), "O (one landmark against plain)", 1e-2, 1e-3)
