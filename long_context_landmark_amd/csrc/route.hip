@@ -34,6 +34,15 @@ int route_max_items(int L, int N, int k, int ppi) {
   return N + (int)(((int64_t)L * k + ppi - 1) / ppi);
 }
 
+// Pair f of a run of queries is (query f / k, slot f % k).  The quotient comes from a float
+// product: for f < 2^15 and k <= 32, (f + 1/2) / k lies at least 1/(2k) from an integer while the
+// product's rounding error stays below 2^-8, so truncation gives f / k exactly (a run holds at most
+// 1024 queries x 16 slots).
+__device__ __forceinline__ int2 pair_of(int f, int k, float rk) {
+  const int q = (int)(((float)f + 0.5f) * rk);
+  return make_int2(q, f - __mul24(q, k));
+}
+
 __global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restrict__ idx, int* __restrict__ counts,
                                                           int L, int N, int k, int nseg, int seg_q) {
   extern __shared__ int hist[];
@@ -42,12 +51,15 @@ __global__ __launch_bounds__(256) void route_count_kernel(const int32_t* __restr
   __syncthreads();
   const int t0 = seg * seg_q, t1 = min(L, t0 + seg_q);
   const int total = (t1 - t0) * k;
+  const int32_t* idx_s = idx + ((int64_t)bh * L + t0) * (k + 1);
+  const float rk = 1.f / (float)k;
   for (int f0 = 0; f0 < total; f0 += 8 * 256) {
     int jj[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int f = f0 + u * 256 + tid;
-      jj[u] = f < total ? idx[((int64_t)bh * L + t0 + f / k) * (k + 1) + f % k] : -1;
+      const int2 qr = pair_of(f, k, rk);
+      jj[u] = f < total ? idx_s[qr.x * (k + 1) + qr.y] : -1;
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
@@ -161,11 +173,13 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_kernel(const int32_t* _
   // memory round trips overlap
   constexpr int UBF = FUSED ? 256 * 16 / (NW * 64) : 1;
   int jr[UBF];
+  const float rk = 1.f / (float)k;
   if constexpr (FUSED) {
 #pragma unroll
     for (int u = 0; u < UBF; ++u) {
       const int f = u * 64 + lane;
-      jr[u] = f < total ? idx_w[(f / k) * (k + 1) + f % k] : -1;
+      const int2 qr = pair_of(f, k, rk);
+      jr[u] = f < total ? idx_w[qr.x * (k + 1) + qr.y] : -1;
     }
   }
   if constexpr (FUSED) {
@@ -174,15 +188,18 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_kernel(const int32_t* _
     const int j = tid;
     int before = 0, tot = 0;
     {
+      // segment rows past nseg are skipped as a whole (a uniform branch); lanes past the chunks
+      // read a valid column and count nothing
+      const int* so_h = segoff + (int64_t)bh * nseg * N + min(j, N - 1);
       int cv[ROUTE_FUSED_MAX_SEG];
 #pragma unroll
-      for (int u = 0; u < ROUTE_FUSED_MAX_SEG; ++u)
-        cv[u] = (j < N && u < nseg) ? segoff[((int64_t)bh * nseg + u) * N + j] : 0;
+      for (int u = 0; u < ROUTE_FUSED_MAX_SEG; ++u) cv[u] = u < nseg ? so_h[u * N] : 0;
 #pragma unroll
       for (int u = 0; u < ROUTE_FUSED_MAX_SEG; ++u) {
-        before += u < seg ? cv[u] : 0;
-        tot += cv[u];
+        if (u < seg) before += cv[u];
+        if (u < nseg) tot += cv[u];
       }
+      if (j >= N) before = tot = 0;
     }
     int all, sum_i;
     const int off = block_excl_scan<NW>(tot, buf, &all);
@@ -219,7 +236,8 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_kernel(const int32_t* _
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int f = f0 + u * 64 + lane;
-          jj[u] = f < total ? idx_w[(f / k) * (k + 1) + f % k] : -1;
+          const int2 qr = pair_of(f, k, rk);
+          jj[u] = f < total ? idx_w[qr.x * (k + 1) + qr.y] : -1;
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
@@ -263,7 +281,10 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_kernel(const int32_t* _
     __builtin_amdgcn_wave_barrier();
     if (act && (peers & below) == 0) cur[j] = pos + __popcll(peers);
     __builtin_amdgcn_wave_barrier();
-    if (act) out[pos] = ((tw0 + f / k) << 5) | (f % k);
+    if (act) {
+      const int2 qr = pair_of(f, k, rk);
+      out[pos] = ((tw0 + qr.x) << 5) | qr.y;
+    }
     if (pos_w && f < total) pos_w[f] = act ? pos : -1;
   };
   if constexpr (FUSED) {
@@ -279,7 +300,8 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_kernel(const int32_t* _
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int f = b0 + u * 64 + lane;
-        jj[u] = f < total ? idx_w[(f / k) * (k + 1) + f % k] : -1;
+        const int2 qr = pair_of(f, k, rk);
+        jj[u] = f < total ? idx_w[qr.x * (k + 1) + qr.y] : -1;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) place(b0 + u * 64 + lane, jj[u]);
@@ -335,10 +357,12 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_staged_kernel(const int
   // the wave's chunk ids, all requested at once and kept for the ranking pass
   constexpr int UB = 1024 * 16 / (NW * 64);  // batches of 64 pairs a wave holds at most
   int jr[UB];
+  const float rk = 1.f / (float)k;
 #pragma unroll
   for (int u = 0; u < UB; ++u) {
     const int f = u * 64 + lane;
-    jr[u] = f < total ? idx_w[(f / k) * (k + 1) + f % k] : -1;
+    const int2 qr = pair_of(f, k, rk);
+    jr[u] = f < total ? idx_w[qr.x * (k + 1) + qr.y] : -1;
   }
   uint32_t* cur_words = reinterpret_cast<uint32_t*>(cur_all);
   for (int i = tid; i < (NW * N + 1) / 2; i += 64 * NW) cur_words[i] = 0u;
@@ -431,7 +455,10 @@ __global__ __launch_bounds__(64 * NW) void route_scatter_staged_kernel(const int
         if (act && (peers & below) == 0) cur[j] = (uint16_t)(lpos + __popcll(peers));
       }
       __builtin_amdgcn_wave_barrier();
-      if (act) stage[lpos] = (uint16_t)(((tw0 - t0 + f / k) << 5) | (f % k));
+      if (act) {
+        const int2 qr = pair_of(f, k, rk);
+        stage[lpos] = (uint16_t)(((tw0 - t0 + qr.x) << 5) | qr.y);
+      }
       if (pos_w && f < total) pos_w[f] = act ? lpos + delta[j] : -1;
     }
   }
