@@ -207,3 +207,17 @@ def test_noalloc_decode_validation(lib):
     assert "n_ctx" in lib.hils_last_error().decode()
     assert lib.hils_decode_step_noalloc(*[FAKE] * 5, None, 100, 1024, *[FAKE] * 3, 1, 2, 64, 64, 8,
                                         ctypes.c_float(0.125), 0, None) == INVALID
+
+
+def test_routing_pair_index_division_is_exact():
+    """The routing kernels split a lane's pair number f into (query f // k, slot f % k) with one float
+    product, truncating (f + 1/2) * fl(1/k) in fp32; that must equal the integer quotient for every pair
+    number a routing run can hold (below 1024 queries x 16 slots, checked here up to 2^15) and every k
+    up to 32."""
+    import numpy as np
+
+    f = np.arange(1 << 15, dtype=np.int64)
+    for k in range(1, 33):
+        rk = np.float32(1.0) / np.float32(k)
+        q = ((f.astype(np.float32) + np.float32(0.5)) * rk).astype(np.int64)
+        np.testing.assert_array_equal(q, f // k, err_msg=f"k={k}")

@@ -25,6 +25,7 @@ def _fwd_bwd(hils, x, k):
     ("bf16", 1, 1, 64, 64, 4),      # single chunk: own-chunk tiles only
     ("f32", 1, 2, 1024, 64, 4),     # the tiny fp32 workload
     ("f32", 1, 2, 1024, 128, 4),    # fp32 at d = 128: dV and dK products staged one after the other
+    ("bf16", 1, 2, 2112, 64, 3),    # k = 3: pair indices of a k that is not a power of two
 ])
 def test_bwd_parity(hils, gpu, dtype, B, H, L, d, k):
     say(f"bwd dtype={dtype} B={B} H={H} L={L} d={d} k={k}")

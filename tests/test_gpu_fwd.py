@@ -44,6 +44,10 @@ CASES = [
     ("bf16", 1, 2, 64 * 130, 64, 8, "chunkmean"),  # 130 chunks: the long-list selection with three tiles
     ("bf16", 1, 3, 4096, 64, 1, "iid"),  # top-1, three heads (no XCD remap)
     ("bf16", 3, 1, 2048, 128, 1, "chunkmean"),  # top-1 at d = 128, three sequences
+    # k not a power of two: the routing's pair indices (query t, slot r) of f = t k + r
+    ("bf16", 1, 2, 4096, 64, 5, "iid"),
+    ("bf16", 2, 1, 64 * 96, 128, 12, "chunkmean"),
+    ("bf16", 1, 1, 64 * 300, 64, 7, "iid"),  # 300 chunks: counts scanned apart, staged scatter
 ]
 
 
