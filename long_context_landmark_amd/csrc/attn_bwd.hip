@@ -31,6 +31,7 @@
 //                the chunk's pairs in routing order.
 #include "hils_device.h"
 #include "hils_launch.h"
+#include "lf_means.h"
 
 namespace hils {
 
@@ -388,19 +389,33 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 && D == 64 ? 2 : 1) void chunk_
 // log-sum-exp of its landmark scores, so its term is scale ds_j sum_u p_u Klm_j,u with the shares
 // p_u = softmax_u(scale qs . Klm_j,u) of the scoring query qs (Qs); these terms are summed in slot
 // order apart from the in-chunk parts and added to them at the end.
-template <typename T, int D, int K1M, bool RQ, int MM = 0>
+// LF (landmark-free chunks): the own slot's landmark of query t is m_t, the causal mean of its chunk's
+// keys up to t as the forward rounded it; the workgroup's rows lie in one chunk, whose means are
+// staged in LDS from the keys Kf, and scale ds_own m_t is added after the slot sum.
+template <typename T, int D, int K1M, bool RQ, int MM = 0, bool LF = false>
 __global__ __launch_bounds__(256) void dq_reduce_kernel(const typename PartialOf<T>::type* __restrict__ dq_part,
                                                         const float* __restrict__ Dpart,
                                                         const int32_t* __restrict__ idx, const float* __restrict__ w,
                                                         const T* __restrict__ Klm, float* __restrict__ ds_out,
                                                         float* __restrict__ dQ, float* __restrict__ dQr, int64_t rows,
-                                                        int L, int N, int k, float scale, int skip,
+                                                        int L, int N, int k, float scale, const T* __restrict__ Kf,
                                                         const T* __restrict__ Qs, int mlm) {
   constexpr int V8 = D / 8;                    // threads per row
   constexpr int LW = 2 * Elem<T>::bytes;       // 32-bit words of eight landmark elements
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gid / V8;
   const int c8 = (int)(gid % V8);
+  float lmf[8];  // LF: this thread's eight elements of m_t
+  if constexpr (LF) {
+    // the launch covers whole chunks, so every thread of the workgroup reaches the barriers
+    __shared__ float km[64 * (D + 1)];
+    __shared__ float segsum[256 / D][D];
+    const int64_t crow0 = ((int64_t)blockIdx.x * (256 / V8)) & ~(int64_t)63;
+    stage_prefix_means<T, D>(Kf, crow0, km, segsum, threadIdx.x);
+    const int qi = (int)(row - crow0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lmf[e] = km[qi * (D + 1) + 8 * c8 + e];
+  }
   if (row >= rows) return;
   const int k1 = k + 1;
   const int64_t bh = row / L;
@@ -440,17 +455,19 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const typename PartialOf
   }
   // RQ: the landmark scores came from separate retrieval queries, whose gradient (the
   // ds * Klm terms) goes to dQr; dQ then keeps the in-chunk attention terms only.
-  // skip = 1 (landmark-free chunks): the own slot's landmark is not a K_lm row, lf_bwd adds its term;
+  // LF: the own slot's landmark is not a K_lm row, its term is added after the sum;
   // several landmarks per chunk (MM > 0) add theirs below
   float acc[8], accr[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = accr[e] = 0.f;
+  float ds_own = 0.f;
 #pragma unroll
   for (int r = 0; r < K1M; ++r) {
     if (!ok[r]) continue;
     const float ds = wr[r] * (dr[r] - Dsum);
     if (c8 == 0) ds_out[row * k1 + r] = ds;
-    const float sds = (MM > 0 || (skip == 1 && r == k)) ? 0.f : scale * ds;
+    if (LF && r == k) ds_own = ds;
+    const float sds = (MM > 0 || (LF && r == k)) ? 0.f : scale * ds;
     float h[8];
     if constexpr (VPP == 1) {
       const uint32_t wds[4] = {raw[r][0].x, raw[r][0].y, raw[r][0].z, raw[r][0].w};
@@ -558,6 +575,14 @@ __global__ __launch_bounds__(256) void dq_reduce_kernel(const typename PartialOf
       else acc[e] += accm[e];
     }
   }
+  if constexpr (LF) {
+    const float so = scale * ds_own;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (RQ) accr[e] += so * lmf[e];
+      else acc[e] += so * lmf[e];
+    }
+  }
   float4* out = reinterpret_cast<float4*>(dQ + row * D + 8 * c8);
   out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
   out[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
@@ -661,20 +686,22 @@ static hipError_t bwd_t(const void* Q, const void* Qr, const void* K, const void
   HILS_LAUNCH("chunk_bwd", (chunk_bwd_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)Q, (const T*)K,
               (const T*)V, (const T*)Klm, (const T*)dO, w, lse, ws.rb.chunk_off, ws.rb.pairs, (PT*)ws.dq_part, ws.Dpart,
               (PT*)ws.trash, ws.trash_f, dK, dV, L, N, k, scale);
+  // rows * D / 8 threads: whole workgroups of whole chunks (L is a multiple of 64)
   const dim3 rgrid((unsigned)((rows * (D / 8) + 255) / 256));
   const bool rq = Qr != nullptr;
-  const int skip = lf ? 1 : 0;
   const T* Qs = (const T*)(rq ? Qr : Q);
-  auto reduce = [&](auto k1m, auto rqc, auto mmc) {
+  auto reduce = [&](auto k1m, auto rqc, auto mmc, auto lfc) {
     constexpr int K1M = decltype(k1m)::value, MM = decltype(mmc)::value;
-    constexpr bool RQ = decltype(rqc)::value != 0;
-    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, K1M, RQ, MM>), rgrid, dim3(256), 0, st, (const PT*)ws.dq_part,
-                ws.Dpart, idx, w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale, skip, Qs, mlm);
+    constexpr bool RQ = decltype(rqc)::value != 0, LF = decltype(lfc)::value != 0;
+    HILS_LAUNCH("dq_reduce", (dq_reduce_kernel<T, D, K1M, RQ, MM, LF>), rgrid, dim3(256), 0, st,
+                (const PT*)ws.dq_part, ws.Dpart, idx, w, (const T*)Klm, ws.ds, dQ, dQr, rows, L, N, k, scale,
+                (const T*)K, Qs, mlm);
   };
   auto reduce_m = [&](auto k1m, auto rqc) {
-    if (mlm == 0) reduce(k1m, rqc, IntC<0>{});
-    else if (mlm <= 2) reduce(k1m, rqc, IntC<2>{});
-    else reduce(k1m, rqc, IntC<4>{});
+    if (lf) reduce(k1m, rqc, IntC<0>{}, IntC<1>{});
+    else if (mlm == 0) reduce(k1m, rqc, IntC<0>{}, IntC<0>{});
+    else if (mlm <= 2) reduce(k1m, rqc, IntC<2>{}, IntC<0>{});
+    else reduce(k1m, rqc, IntC<4>{}, IntC<0>{});
   };
   if (k <= 8 && !rq) reduce_m(IntC<9>{}, IntC<0>{});
   else if (!rq) reduce_m(IntC<17>{}, IntC<0>{});
@@ -693,8 +720,7 @@ static hipError_t bwd_t(const void* Q, const void* Qr, const void* K, const void
   if (lf) {
     hipError_t e2 = hipGetLastError();
     if (e2 != hipSuccess) return e2;
-    return launch_lf_bwd(Elem<T>::bytes == 2 ? 0 : 1, D, rq ? Qr : Q, K, ws.ds, dKlm, rq ? dQr : dQ, dK, BH, L, N,
-                         k, scale, st);
+    return launch_lf_bwd(Elem<T>::bytes == 2 ? 0 : 1, D, rq ? Qr : Q, ws.ds, dKlm, dK, BH, L, N, k, scale, st);
   }
   return hipGetLastError();
 }

@@ -97,10 +97,10 @@ hipError_t launch_bwd(int dt, int d, const void* Q, const void* Qr, const void* 
                       bool lf, int mlm, const void* dO, const int32_t* idx, const float* w, const float* lse, float* dQ,
                       float* dQr, float* dK, float* dV, float* dKlm, int BH, int L, int N, int k, float scale,
                       const BwdBufs& ws, hipStream_t st);
-// landmark-free backward tail, per (chunk, head): the own slot's ds against the causal means into dQs, and
-// the mean paths (own slots and the past chunk's dKlm) into dK
-hipError_t launch_lf_bwd(int dt, int d, const void* Qs, const void* K, const float* ds, const float* dKlm, float* dQs,
-                         float* dK, int BH, int L, int N, int k, float scale, hipStream_t st);
+// landmark-free backward tail, per (chunk, head): the mean paths (own slots and the past chunk's dKlm)
+// into dK; the own slot's ds against the causal means reaches dQs in dq_reduce
+hipError_t launch_lf_bwd(int dt, int d, const void* Qs, const float* ds, const float* dKlm, float* dK, int BH, int L,
+                         int N, int k, float scale, hipStream_t st);
 // qr: retrieval query for the landmark scores (null: q).  lf: landmark-free chunks, the step writes
 // the open chunk's landmark row (the mean of its keys so far) before it is read
 // mlm: landmarks per chunk (Klm [BH][Nmax][mlm][d]; the chunk score is the log-sum-exp of theirs)

@@ -12,11 +12,12 @@
 //               prefix mean (four lanes per query), and the own slot's score and the fusion
 //               weights rewritten.  Reads Q (or the retrieval queries) and K once, and the
 //               selection outputs once.
-//   lf_bwd      the backward's tail, per (chunk, head): the own slot's score gradient against the
-//               causal means into dQ (or dQ_ret), and the mean paths into dK (reverse prefix sums
-//               over the chunk's queries plus the past chunk's mean gradient / 64).
+//   lf_bwd      the backward's tail, per (chunk, head): the mean paths into dK (reverse prefix sums
+//               over the chunk's queries plus the past chunk's mean gradient / 64); the own slot's
+//               score gradient against the causal means goes into dQ (or dQ_ret) in dq_reduce.
 #include "hils_device.h"
 #include "hils_launch.h"
+#include "lf_means.h"
 
 namespace hils {
 
@@ -53,54 +54,6 @@ __global__ __launch_bounds__(256) void chunk_mean_kernel(const T* __restrict__ K
     for (int i = 0; i < G; ++i) s += part[i][e];
     Elem<T>::store(Klm, ((int64_t)bh * Nlm + j) * D + e, s * (1.f / 64.f));
   }
-}
-
-// The chunk's keys (rows row0 .. row0+63) staged as fp32 in km (row stride D + 1), then replaced by
-// their causal means: row r becomes the mean of rows 0..r, rounded to the element type like a
-// landmark row.  The prefix sums run as 256/D row segments at once, offset by the earlier segments.
-// Ends with a barrier.
-template <typename T, int D>
-__device__ __forceinline__ void stage_prefix_means(const T* __restrict__ K, int64_t row0, float* km,
-                                                   float (*segsum)[D], int tid) {
-  constexpr int EPP = 16 / Elem<T>::bytes;
-  constexpr int PIECES = D / EPP;
-  constexpr int RPR = 256 / PIECES;
-  constexpr int KS = D + 1;
-  constexpr int SEG = 256 / D;
-  constexpr int RS = 64 / SEG;
-  {
-    const int piece = tid % PIECES, rr = tid / PIECES;
-#pragma unroll
-    for (int r0 = 0; r0 < 64; r0 += RPR) {
-      const int r = r0 + rr;
-      const int4 raw = *reinterpret_cast<const int4*>(K + (row0 + r) * D + piece * EPP);
-      T vals[EPP];
-      __builtin_memcpy(vals, &raw, 16);
-#pragma unroll
-      for (int e = 0; e < EPP; ++e) km[r * KS + piece * EPP + e] = Elem<T>::to_f32(vals, e);
-    }
-  }
-  __syncthreads();
-  const int e = tid % D, sg = tid / D;
-  float run = 0.f;
-#pragma unroll
-  for (int i = 0; i < RS; ++i) {
-    const int r = sg * RS + i;
-    run += km[r * KS + e];
-    km[r * KS + e] = run;
-  }
-  segsum[sg][e] = run;
-  __syncthreads();
-  float off = 0.f;
-  for (int j = 0; j < sg; ++j) off += segsum[j][e];
-#pragma unroll
-  for (int i = 0; i < RS; ++i) {
-    const int r = sg * RS + i;
-    T m[1];
-    Elem<T>::store(m, 0, (km[r * KS + e] + off) / (float)(r + 1));
-    km[r * KS + e] = Elem<T>::to_f32(m, 0);
-  }
-  __syncthreads();
 }
 
 template <typename T, int D>
@@ -168,16 +121,15 @@ __global__ __launch_bounds__(256) void lf_own_kernel(const T* __restrict__ Qs, c
   }
 }
 
-// Backward tail of landmark-free chunks, per (chunk c, head), after klm_bwd:
-//   own slot:  dQs_t += scale ds_t,own m_t (m_t the causal mean the forward used), and each key i <= t
-//              of the chunk gets scale ds_t,own qs_t / (t - 64c + 1): a reverse prefix sum over t;
-//   past use:  each key of the chunk gets dKlm_c / 64 (dKlm_c from klm_bwd, past pairs only).
-// The rounding of the means is passed straight through.  dQs and dK are read, added to and written.
+// Backward tail of landmark-free chunks, per (chunk c, head), after klm_bwd: each key i of the chunk
+// gets scale ds_t,own qs_t / (t - 64c + 1) summed over the chunk's queries t >= i (a reverse prefix
+// sum over t), plus dKlm_c / 64 for the past chunks' use of its mean (dKlm_c from klm_bwd, past pairs
+// only).  The own slot's dQs term, scale ds_t,own m_t, is added by dq_reduce.  The rounding of the means
+// is passed straight through.  dK is read, added to and written.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void lf_bwd_kernel(const T* __restrict__ Qs, const T* __restrict__ K,
-                                                     const float* __restrict__ ds, const float* __restrict__ dKlm,
-                                                     float* __restrict__ dQs, float* __restrict__ dK, int L, int N,
-                                                     int k, float scale) {
+__global__ __launch_bounds__(256) void lf_bwd_kernel(const T* __restrict__ Qs, const float* __restrict__ ds,
+                                                     const float* __restrict__ dKlm, float* __restrict__ dK, int L,
+                                                     int N, int k, float scale) {
   constexpr int EPP = 16 / Elem<T>::bytes;
   constexpr int KS = D + 1;
   constexpr int EQ = D / 4;
@@ -186,7 +138,6 @@ __global__ __launch_bounds__(256) void lf_bwd_kernel(const T* __restrict__ Qs, c
   const int c = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int64_t row0 = (int64_t)bh * L + (int64_t)c * 64;
   const int q = tid >> 2, part = tid & 3;
-  __shared__ float km[64 * KS];
   __shared__ float gm[64 * KS];
   __shared__ float segsum[SEG][D];
   int4 qraw[EQ / EPP];
@@ -194,25 +145,14 @@ __global__ __launch_bounds__(256) void lf_bwd_kernel(const T* __restrict__ Qs, c
   for (int v = 0; v < EQ / EPP; ++v)
     qraw[v] = *reinterpret_cast<const int4*>(Qs + (row0 + q) * D + part * EQ + v * EPP);
   const float sds = scale * ds[(row0 + q) * (k + 1) + k];
-  stage_prefix_means<T, D>(K, row0, km, segsum, tid);
-  // own-slot term of dQs, and g_t = scale ds_t qs_t / (t + 1) for the keys
+  const float e_off = dKlm[((int64_t)bh * N + c) * D + tid % D] * (1.f / 64.f);
+  // g_t = scale ds_t qs_t / (t + 1)
   {
-    float* dq = dQs + (row0 + q) * D + part * EQ;
     const float inv_cnt = 1.f / (float)(q + 1);
 #pragma unroll
     for (int v = 0; v < EQ / EPP; ++v) {
       T vals[EPP];
       __builtin_memcpy(vals, &qraw[v], 16);
-#pragma unroll
-      for (int e4 = 0; e4 < EPP; e4 += 4) {
-        float4 a = *reinterpret_cast<float4*>(dq + v * EPP + e4);
-        const int eb = part * EQ + v * EPP + e4;
-        a.x += sds * km[q * KS + eb];
-        a.y += sds * km[q * KS + eb + 1];
-        a.z += sds * km[q * KS + eb + 2];
-        a.w += sds * km[q * KS + eb + 3];
-        *reinterpret_cast<float4*>(dq + v * EPP + e4) = a;
-      }
 #pragma unroll
       for (int e = 0; e < EPP; ++e) gm[q * KS + part * EQ + v * EPP + e] = sds * Elem<T>::to_f32(vals, e) * inv_cnt;
     }
@@ -229,7 +169,7 @@ __global__ __launch_bounds__(256) void lf_bwd_kernel(const T* __restrict__ Qs, c
   }
   segsum[sg][e] = run;
   __syncthreads();
-  float off = dKlm[((int64_t)bh * N + c) * D + e] * (1.f / 64.f);
+  float off = e_off;
   for (int j = sg + 1; j < SEG; ++j) off += segsum[j][e];
 #pragma unroll
   for (int i = 0; i < RS; ++i) {
@@ -239,20 +179,20 @@ __global__ __launch_bounds__(256) void lf_bwd_kernel(const T* __restrict__ Qs, c
 }
 
 template <typename T, int D>
-static hipError_t lf_bwd_t(const void* Qs, const void* K, const float* ds, const float* dKlm, float* dQs, float* dK,
-                           int BH, int L, int N, int k, float scale, hipStream_t st) {
-  HILS_LAUNCH("lf_bwd", (lf_bwd_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)Qs, (const T*)K, ds, dKlm,
-              dQs, dK, L, N, k, scale);
+static hipError_t lf_bwd_t(const void* Qs, const float* ds, const float* dKlm, float* dK, int BH, int L, int N, int k,
+                           float scale, hipStream_t st) {
+  HILS_LAUNCH("lf_bwd", (lf_bwd_kernel<T, D>), dim3(N, BH), dim3(256), 0, st, (const T*)Qs, ds, dKlm, dK, L, N, k,
+              scale);
   return hipGetLastError();
 }
 
-hipError_t launch_lf_bwd(int dt, int d, const void* Qs, const void* K, const float* ds, const float* dKlm, float* dQs,
-                         float* dK, int BH, int L, int N, int k, float scale, hipStream_t st) {
+hipError_t launch_lf_bwd(int dt, int d, const void* Qs, const float* ds, const float* dKlm, float* dK, int BH, int L,
+                         int N, int k, float scale, hipStream_t st) {
   if (dt == 0)
-    return d == 64 ? lf_bwd_t<bf16_t, 64>(Qs, K, ds, dKlm, dQs, dK, BH, L, N, k, scale, st)
-                   : lf_bwd_t<bf16_t, 128>(Qs, K, ds, dKlm, dQs, dK, BH, L, N, k, scale, st);
-  return d == 64 ? lf_bwd_t<float, 64>(Qs, K, ds, dKlm, dQs, dK, BH, L, N, k, scale, st)
-                 : lf_bwd_t<float, 128>(Qs, K, ds, dKlm, dQs, dK, BH, L, N, k, scale, st);
+    return d == 64 ? lf_bwd_t<bf16_t, 64>(Qs, ds, dKlm, dK, BH, L, N, k, scale, st)
+                   : lf_bwd_t<bf16_t, 128>(Qs, ds, dKlm, dK, BH, L, N, k, scale, st);
+  return d == 64 ? lf_bwd_t<float, 64>(Qs, ds, dKlm, dK, BH, L, N, k, scale, st)
+                 : lf_bwd_t<float, 128>(Qs, ds, dKlm, dK, BH, L, N, k, scale, st);
 }
 
 template <typename T, int D>
