@@ -161,6 +161,23 @@ def test_fwd_deterministic(hils, gpu, H, L, d, k):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("H,L,d,k", [(2, 320, 64, 4), (2, 4160, 128, 16), (1, 8192, 64, 8)])
+def test_fwd_stale_workspace(hils, gpu, H, L, d, k):
+    """A workspace full of leftovers (every byte 0xff) gives the results of a zeroed one, bit for bit:
+    every workspace word a kernel reads (routing counts and lists, work items, partial rows) is
+    written earlier in the same call.  L = 320 and 4160 leave a partial last routing segment."""
+    say(f"stale workspace H={H} L={L} d={d} k={k}")
+    x = _inputs(1, H, L, d, k, seed=7, klm="chunkmean")
+    t = to_inputs(x)
+    n = hils.workspace_size(hils.OP_FWD, 1, H, L, d, 64, k)
+    outs = []
+    for fill in (0, 255):
+        ws = torch.full((n,), fill, dtype=torch.uint8, device=gpu)
+        outs.append(hils.sparse_attn_fwd(t["Q"], t["K"], t["V"], t["Klm"], k, save_for_backward=True, ws=ws))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+
+
 def test_workload_prefill_8k_full(hils, gpu):
     """The 8K prefill workload (B=1 H=16 d=64 L=8192 k=8, chunk-mean landmarks, 4 needles): every row."""
     w = synth.WORKLOADS["prefill_8k"]
