@@ -89,3 +89,23 @@ def test_workload_train_8k_sampled_heads(hils, gpu):
         ref = oracle.bwd(sub["Q"], sub["K"], sub["V"], sub["Klm"], sub["dO"], gi[b:b + 1, h:h + 1], 64, w.k)
         for name, got in zip(("dQ", "dK", "dV", "dKlm"), grads):
             assert_close(f32(got[b:b + 1, h:h + 1]), ref[name], f"{name} (b={b}, h={h})")
+
+
+@pytest.mark.parametrize("B,H,L,d,k", [(1, 2, 2112, 64, 8), (1, 1, 4160, 128, 16)])
+def test_bwd_stale_workspace_and_outputs(hils, gpu, B, H, L, d, k):
+    """Leftovers in the workspace (every byte 0xff) and NaN-filled gradient buffers give, bit for bit,
+    the gradients of a zeroed workspace and zeroed buffers: every gradient element is written, and every
+    workspace word a kernel reads is written earlier in the same call."""
+    say(f"bwd stale workspace B={B} H={H} L={L} d={d} k={k}")
+    x = synth.prefill_inputs(B, H, L, d, C=64, seed=17, dtype="bf16", with_dO=True)
+    Q, K, V, Klm, dO = (dev(x[n]) for n in ("Q", "K", "V", "Klm", "dO"))
+    O, idx, sel, w, lse = hils.sparse_attn_fwd(Q, K, V, Klm, k, save_for_backward=True)
+    n = hils.workspace_size(hils.OP_BWD, B, H, L, d, 64, k)
+    shapes = ((B, H, L, d),) * 3 + ((B, H, L // 64, d),)
+    res = []
+    for fill, val in ((0, 0.0), (255, float("nan"))):
+        ws = torch.full((n,), fill, dtype=torch.uint8, device=gpu)
+        out = tuple(torch.full(sh, val, dtype=torch.float32, device=gpu) for sh in shapes)
+        res.append(hils.sparse_attn_bwd(Q, K, V, Klm, dO, idx, w, lse, k, ws=ws, out=out))
+    for name, a, b in zip(("dQ", "dK", "dV", "dKlm"), *res):
+        assert torch.equal(a, b), name

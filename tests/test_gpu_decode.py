@@ -160,3 +160,22 @@ def test_decode_many_slices(hils, gpu, ctx, d, k):
     say(f"decode many slices ctx={ctx} d={d} k={k} slices={(ctx // 64 + 255) // 256}")
     x = synth.decode_inputs(1, 2, d, ctx, 3, C=64, seed=ctx % 1000, dtype="bf16")
     _run_decode(hils, x, k, 3)
+
+
+@pytest.mark.parametrize("B,H,d,ctx,k", [(1, 2, 64, 64 * 300 + 17, 16), (2, 3, 128, 64 * 40 + 63, 8)])
+def test_decode_stale_workspace(hils, gpu, B, H, d, ctx, k):
+    """Leftovers in the workspace (every byte 0xff) give the step of a zeroed workspace, bit for bit:
+    the slice lists and partial outputs a kernel reads are written earlier in the same step."""
+    say(f"decode stale workspace B={B} H={H} d={d} ctx={ctx} k={k}")
+    x = synth.decode_inputs(B, H, d, ctx, 1, seed=23)
+    Lmax = x["K_cache"].shape[2]
+    n = hils.workspace_size(hils.OP_DECODE, B, H, Lmax, d, 64, k)
+    res = []
+    for fill in (0, 255):
+        Kc, Vc, Klm = dev(x["K_cache"]), dev(x["V_cache"]), dev(x["Klm"])
+        ws = torch.full((n,), fill, dtype=torch.uint8, device=gpu)
+        o, idx, w = hils.decode_step(dev(x["q"])[0], dev(x["k_new"])[0], dev(x["v_new"])[0], Kc, Vc, Klm, ctx, k,
+                                     ws=ws)
+        res.append((o, idx, w, Kc, Vc))
+    for name, a, b in zip(("o", "idx", "w", "K_cache", "V_cache"), *res):
+        assert torch.equal(a, b), name
