@@ -205,24 +205,34 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 && D == 64 ? 2 : 1) void chunk_
         mma(dp[cb], kv.v(s, cb, ks), in.gf[ks]);
       }
     }
-    float Dj = 0.f;
+    // scale w_q p_i straight from the exponential: log2(scale w_q) joins the exponent's bias, so no
+    // per-element multiply weights the probabilities.  Lanes without a pair (w_q = 0) and masked keys
+    // give exp2(-inf) = 0; D_j = sum_i p_i dP_i comes back from the weighted sum with one reciprocal.
+    // The staged w P and dA rows carry the factor scale: the dQ parts and dK need no further multiply,
+    // and dV is divided by scale once, when it is written.
+    const float c2 = scale * 1.44269504088896341f;  // scale * log2(e)
+    const float sw = scale * w_q;
+    const float bias = __log2f(sw) - lse_q * 1.44269504088896341f;
+    const int lim = causal < 0 ? 63 : causal;
+    float Dw = 0.f;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = 16 * cb + 4 * g + i;
-        const float p = (valid && (causal < 0 || key <= causal)) ? __expf(scale * sc[cb][i] - lse_q) : 0.f;
-        sc[cb][i] = p;
-        Dj += p * dp[cb][i];
+        const float pw = __builtin_amdgcn_exp2f(key <= lim ? fmaf(sc[cb][i], c2, bias) : -INFINITY);
+        sc[cb][i] = pw;
+        Dw += pw * dp[cb][i];
       }
-    Dj += lane_xor(Dj, 16);
-    Dj += lane_xor(Dj, 32);
+    Dw += lane_xor(Dw, 16);
+    Dw += lane_xor(Dw, 32);
+    const float Dj = sw > 0.f ? Dw * __builtin_amdgcn_rcpf(sw) : 0.f;
     // the four lane groups hold the same D_j
     *(valid ? Dpart + row * k1 + in.slot : trash_f) = Dj;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dp[cb][i] = w_q * sc[cb][i] * (dp[cb][i] - Dj);  // dA
+      for (int i = 0; i < 4; ++i) dp[cb][i] = sc[cb][i] * (dp[cb][i] - Dj);  // scale dA
     // dQ^T = K^T dA^T (key mapping of the B fragment as in the forward's P V)
     {
       Frag<T> daf[2];
@@ -254,15 +264,15 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 && D == 64 ? 2 : 1) void chunk_
 #pragma unroll
         for (int p2 = 0; p2 < D / 32; ++p2) {
           const f32x4_t e = dq_block(2 * p2), o = dq_block(2 * p2 + 1);
-          const uint32_t e0 = pack_bf16x2(scale * e[0], scale * e[1]), e1 = pack_bf16x2(scale * e[2], scale * e[3]);
-          const uint32_t o0 = pack_bf16x2(scale * o[0], scale * o[1]), o1 = pack_bf16x2(scale * o[2], scale * o[3]);
+          const uint32_t e0 = pack_bf16x2(e[0], e[1]), e1 = pack_bf16x2(e[2], e[3]);
+          const uint32_t o0 = pack_bf16x2(o[0], o[1]), o1 = pack_bf16x2(o[2], o[3]);
           const uint32_t r0 = lane_xor_u32(odd ? e0 : o0, 16), r1 = lane_xor_u32(odd ? e1 : o1, 16);
           const uint4 v = odd ? make_uint4(r0, r1, o0, o1) : make_uint4(e0, e1, r0, r1);
           *reinterpret_cast<uint4*>(dst + 32 * p2 + (odd ? 16 + 4 * (g - 1) : 4 * g)) = v;
         }
       } else {
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4_t*>(dst + 16 * db + 4 * g) = scale * dq_block(db);
+        for (int db = 0; db < D / 16; ++db) *reinterpret_cast<f32x4_t*>(dst + 16 * db + 4 * g) = dq_block(db);
       }
     }
     __syncthreads();  // previous tile's readers of the staged buffers are done
@@ -276,7 +286,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 && D == 64 ? 2 : 1) void chunk_
         for (int cb = 0; cb < 4; ++cb) {
           u16x4_t pw;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pw[i] = f32_to_bf16(w_q * sc[cb][i]);
+          for (int i = 0; i < 4; ++i) pw[i] = f32_to_bf16(sc[cb][i]);
           *reinterpret_cast<u16x4_t*>(&s.pt[qi * S::TS + 16 * cb + 4 * g]) = pw;
         }
       } else {
@@ -287,7 +297,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 && D == 64 ? 2 : 1) void chunk_
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Elem<T>::store(s.pt, (16 * cb + 4 * g + i) * S::TS + qi, w_q * sc[cb][i]);
+          for (int i = 0; i < 4; ++i) Elem<T>::store(s.pt, (16 * cb + 4 * g + i) * S::TS + qi, sc[cb][i]);
       }
     };
     auto stage_k = [&]() {
@@ -371,12 +381,13 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 && D == 64 ? 2 : 1) void chunk_
   }
   // write dK, dV of this chunk: lane holds d = 16db + r16, keys 16wv + 4g + i
   const int64_t krow0 = (int64_t)bh * L + (int64_t)j * 64 + 16 * wv + 4 * g;
+  const float inv_scale = 1.f / scale;
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      dV[(krow0 + i) * D + 16 * db + r16] = accV[db][i];
-      dK[(krow0 + i) * D + 16 * db + r16] = scale * accK[db][i];
+      dV[(krow0 + i) * D + 16 * db + r16] = accV[db][i] * inv_scale;
+      dK[(krow0 + i) * D + 16 * db + r16] = accK[db][i];
     }
 }
 
