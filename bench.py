@@ -149,8 +149,10 @@ def train_work(B, H, L, d, k, C=64):
     return {"flops": fw["flops"] + f_bwd, "bytes": fw["bytes"] + b_bwd, "kernels": kern}
 
 
-def roofline(kernels_ms, work, launches_per_step, workload=None):
-    """Roofline of the kernel with the largest time per step.
+def roofline(kernels_ms, work, launches_per_step, workload=None, by_bytes=False):
+    """Roofline of the kernel with the largest time per step (by_bytes: the largest algorithmic bytes, for
+    the decode step, whose kernels last a few microseconds each, so that the HIP-event brackets, which add
+    a launch's dispatch latency to each, would decide the choice).
 
     achieved = the kernel's algorithmic FLOPs (contractions, against bf16 MFMA) or bytes (against HBM) per
     launch over its average launch time from HIP events on the launching stream; traffic = HBM bytes per
@@ -158,7 +160,10 @@ def roofline(kernels_ms, work, launches_per_step, workload=None):
     hbm_measured their rate over the same launch time."""
     if not kernels_ms:
         return None
-    name = max(kernels_ms, key=lambda n: kernels_ms[n][0])
+    if by_bytes:
+        name = max(kernels_ms, key=lambda n: work["kernels"].get(n, ("hbm", 0, 0, 0))[2])
+    else:
+        name = max(kernels_ms, key=lambda n: kernels_ms[n][0])
     total_ms, calls = kernels_ms[name]
     per_launch_ms = total_ms / max(1, calls)
     bound, flops, nbytes, design = work["kernels"].get(name, ("hbm", 0, 0, 0))
@@ -232,11 +237,22 @@ def timed_graph(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall, g
 
 
+def host_ahead():
+    """Queue a spin kernel of about 20 ms (5e7 shader clocks) so that the host enqueues the profiled
+    launches while the GPU is busy.  The library then times each launch with events that its own dispatch
+    records; when the host lags (a few hundred eager decode launches from Python take several ms), the
+    GPU idles between kernels and those intervals grow by the idle time's dispatch and clock ramp."""
+    import torch
+
+    torch.cuda._sleep(int(5e7))
+
+
 def kernel_times(hils, fn, steps):
     import torch
 
     torch.cuda.synchronize()
     hils.profile_enable(True)
+    host_ahead()
     for _ in range(steps):
         fn()
     torch.cuda.synchronize()
@@ -464,9 +480,10 @@ def bench_decode(hils, synth, name, replicas, warmup, lf=False, ml=False, eager_
     del graph
     calls = w.steps * len(reps)
     us = e0.elapsed_time(e1) * 1e3 / calls
-    # per-kernel times over a further pass of 16 tokens
+    # per-kernel times over a further pass of 4 tokens, enqueued while the GPU is busy
     hils.profile_enable(True)
-    for s in range(16):
+    host_ahead()
+    for s in range(4):
         token(s)
     torch.cuda.synchronize()
     kt = hils.profile_read()
@@ -486,7 +503,7 @@ def bench_decode(hils, synth, name, replicas, warmup, lf=False, ml=False, eager_
         # each kernel bracketed by HIP events on its stream: for kernels of a few microseconds the bracket adds
         # the launch's dispatch latency, so these exceed the kernels' own durations (rocprofv3 gives those)
         "kernel_us": {n: round(t / c * 1e3, 3) for n, (t, c) in kt.items()},
-        "roofline": roofline(kt, work, {n: 1 for n in kt}, None if lf or ml else name),
+        "roofline": roofline(kt, work, {n: 1 for n in kt}, None if lf or ml else name, by_bytes=True),
         "config": {"workload": name, "B": B, "H": H, "d": d, "context": w.L, "steps": w.steps, "k": w.k,
                    "replicas": len(reps), "protocol": "cold" if len(reps) > 1 else "warm",
                    **({"landmark_free": True} if lf else {}), **({"landmarks_per_chunk": 2} if ml else {})},
@@ -532,6 +549,7 @@ def bench_decode_paged(hils, synth, name, warmup):
     del graph
     us = e0.elapsed_time(e1) * 1e3 / w.steps
     hils.profile_enable(True)
+    host_ahead()
     for s in range(8):
         step(s)
     torch.cuda.synchronize()

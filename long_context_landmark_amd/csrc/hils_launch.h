@@ -2,20 +2,28 @@
 // Element type code: 0 = bf16, 1 = fp32.  All launches are asynchronous on
 // the given stream and return the launch status.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace hils {
 
-namespace prof {  // opt-in per-kernel HIP-event timing (off unless enabled through the C ABI)
-void begin(const char* name, hipStream_t st);
-void end(hipStream_t st);
+// Opt-in per-kernel timing (off unless enabled through the C ABI).  When on, each launch carries a
+// start and a stop event that its own dispatch records (hipExtLaunchKernelGGL), so the interval is the
+// kernel's execution, without the marker packets of separately recorded events.
+namespace prof {
+bool make(hipEvent_t* start, hipEvent_t* stop);  // false (and no events) while timing is off
+void add(const char* name, hipEvent_t start, hipEvent_t stop);
 }  // namespace prof
-#define HILS_LAUNCH(name, kernel, grid, block, lds, st, ...)       \
-  do {                                                            \
-    ::hils::prof::begin(name, st);                                \
-    hipLaunchKernelGGL(kernel, grid, block, lds, st, __VA_ARGS__); \
-    ::hils::prof::end(st);                                        \
+#define HILS_LAUNCH(name, kernel, grid, block, lds, st, ...)                                      \
+  do {                                                                                          \
+    hipEvent_t hils_ev_a_ = nullptr, hils_ev_b_ = nullptr;                                      \
+    if (::hils::prof::make(&hils_ev_a_, &hils_ev_b_)) {                                         \
+      hipExtLaunchKernelGGL(kernel, grid, block, lds, st, hils_ev_a_, hils_ev_b_, 0u, __VA_ARGS__); \
+      ::hils::prof::add(name, hils_ev_a_, hils_ev_b_);                                          \
+    } else {                                                                                    \
+      hipLaunchKernelGGL(kernel, grid, block, lds, st, __VA_ARGS__);                            \
+    }                                                                                           \
   } while (0)
 
 hipError_t launch_landmark_scores(int dt, int d, const void* Q, const void* Klm, float* S, int BH, int L, int N,

@@ -25,27 +25,21 @@ std::mutex g_mu;
 bool g_on = false;
 std::vector<Pending> g_pending;
 std::vector<Acc> g_acc;
-thread_local hipEvent_t t_begin = nullptr;
-thread_local const char* t_name = nullptr;
 }  // namespace
 
-void begin(const char* name, hipStream_t st) {
-  if (!g_on) return;
-  hipEvent_t a;
-  if (hipEventCreate(&a) != hipSuccess) return;
-  (void)hipEventRecord(a, st);
-  t_begin = a;
-  t_name = name;
+bool make(hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_on) return false;
+  if (hipEventCreate(start) != hipSuccess) return false;
+  if (hipEventCreate(stop) != hipSuccess) {
+    (void)hipEventDestroy(*start);
+    return false;
+  }
+  return true;
 }
 
-void end(hipStream_t st) {
-  if (!g_on || !t_begin) return;
-  hipEvent_t b;
-  if (hipEventCreate(&b) != hipSuccess) return;
-  (void)hipEventRecord(b, st);
+void add(const char* name, hipEvent_t start, hipEvent_t stop) {
   std::lock_guard<std::mutex> lk(g_mu);
-  g_pending.push_back({t_name, t_begin, b});
-  t_begin = nullptr;
+  g_pending.push_back({name, start, stop});
 }
 
 void collect() {
