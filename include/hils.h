@@ -355,9 +355,12 @@ hils_status hils_decode_step_noalloc(const void* q, const void* k_new, const voi
 
 /*
  * Optional per-kernel timing, for measurement only (off by default; not a
- * step of the method).  While enabled, every kernel an entry point launches is
- * bracketed by a pair of HIP events recorded on the caller's stream, which
- * adds a little launch overhead.  hils_profile_enable(on) clears the totals
+ * step of the method).  While enabled, every kernel an entry point launches
+ * carries a start and a stop HIP event that its own dispatch records on the
+ * caller's stream (hipExtLaunchKernelGGL), so an interval is the kernel's run;
+ * it also includes any time the GPU waited for the host to submit the kernel,
+ * so queue the timed launches ahead of the GPU.  Not for use while the stream
+ * is being captured into a graph.  hils_profile_enable(on) clears the totals
  * and switches recording on or off.  hils_profile_read waits for the recorded
  * events and returns the number of distinct kernels seen so far; for the first
  * max_kernels of them it writes the kernel name (NUL-terminated, name_stride
