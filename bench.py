@@ -49,7 +49,7 @@ KERNEL_SOURCES = {
 MEASURED_TRAFFIC = {
     # workload: {kernel: (FETCH_SIZE KiB, WRITE_SIZE KiB, source digest)}
     "prefill_8k": {"chunk_attn_fwd": (28601.2, 130610.5, "a3092f13320f3339"), "topk_select": (8439.4, 13824.4, "586a724baeaea988"), "own_combine": (92234.5, 16384.0, "a3092f13320f3339")},
-    "prefill_128k": {"chunk_attn_fwd": (8509482.7, 17018842.4, "a3092f13320f3339"), "topk_select": (533198.6, 835609.2, "586a724baeaea988"), "own_combine": (10197152.7, 1048576.0, "a3092f13320f3339")},
+    "prefill_128k": {"chunk_attn_fwd": (8157821.3, 17023151.8, "a3092f13320f3339"), "topk_select": (533198.6, 835609.2, "586a724baeaea988"), "own_combine": (10197152.7, 1048576.0, "a3092f13320f3339")},
     "train_8k": {"chunk_bwd": (235663.0, 898528.4, "f4de254081963b9c"), "chunk_attn_fwd": (105704.4, 522515.0, "a3092f13320f3339"), "dq_reduce": (326648.0, 149726.5, "f4de254081963b9c")},
     "decode_512k": {"decode_scan": (8264.2, 68.0, "8aa435acddc0f2e9"), "decode_attend": (2434.7, 34.1, "8aa435acddc0f2e9")},
 }
