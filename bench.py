@@ -480,6 +480,21 @@ def bench_decode(hils, synth, name, replicas, warmup, lf=False, ml=False, eager_
     del graph
     calls = w.steps * len(reps)
     us = e0.elapsed_time(e1) * 1e3 / calls
+    # per-step distribution: each step (all replicas) in a graph of its own, replayed once untimed and once
+    # timed; re-running a step rewrites the same cache rows, and later rows are not read by it
+    step_us = []
+    for s in range(w.steps):
+        gs = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gs):
+            token(s)
+        gs.replay()
+        e0.record(st)
+        gs.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        step_us.append(e0.elapsed_time(e1) * 1e3 / len(reps))
+        del gs
+    step_us.sort()
     # per-kernel times over a further pass of 4 tokens, enqueued while the GPU is busy
     hils.profile_enable(True)
     host_ahead()
@@ -493,7 +508,10 @@ def bench_decode(hils, synth, name, replicas, warmup, lf=False, ml=False, eager_
     res = {
         "us_per_token": us,
         "us_per_token_eager": eager_us,
-        "timing": "every step of every replica captured in one HIP graph, replayed once",
+        "us_per_token_p50": step_us[len(step_us) // 2],
+        "us_per_token_p90": step_us[(9 * len(step_us)) // 10],
+        "timing": "every step of every replica captured in one HIP graph, replayed once; p50 and p90 over the "
+                  "steps, each step's replicas in a graph of their own",
         "hbm_gbs": work["bytes"] / (us * 1e-6) / 1e9,
         "hbm_frac": work["bytes"] / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
         "step_roofline": step_fractions(work, us * 1e-3),
