@@ -483,7 +483,8 @@ def bench_decode(hils, synth, name, replicas, warmup, lf=False, ml=False, eager_
     # per-step distribution: each step (all replicas) in a graph of its own, replayed once untimed and once
     # timed; re-running a step rewrites the same cache rows, and later rows are not read by it
     step_us = []
-    for s in range(w.steps):
+    # (one replica: a step's graph would hold three kernels and its launch cost would set the figure)
+    for s in range(w.steps if len(reps) > 1 else 0):
         gs = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gs):
             token(s)
@@ -508,8 +509,8 @@ def bench_decode(hils, synth, name, replicas, warmup, lf=False, ml=False, eager_
     res = {
         "us_per_token": us,
         "us_per_token_eager": eager_us,
-        "us_per_token_p50": step_us[len(step_us) // 2],
-        "us_per_token_p90": step_us[(9 * len(step_us)) // 10],
+        "us_per_token_p50": step_us[len(step_us) // 2] if step_us else None,
+        "us_per_token_p90": step_us[(9 * len(step_us)) // 10] if step_us else None,
         "timing": "every step of every replica captured in one HIP graph, replayed once; p50 and p90 over the "
                   "steps, each step's replicas in a graph of their own",
         "hbm_gbs": work["bytes"] / (us * 1e-6) / 1e9,
