@@ -1,6 +1,7 @@
 // Opt-in per-kernel timing with HIP events on the launching stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -22,13 +23,13 @@ struct Acc {
   long calls;
 };
 std::mutex g_mu;
-bool g_on = false;
+std::atomic<bool> g_on{false};  // read by every launch without the lock
 std::vector<Pending> g_pending;
 std::vector<Acc> g_acc;
 }  // namespace
 
 bool make(hipEvent_t* start, hipEvent_t* stop) {
-  if (!g_on) return false;
+  if (!g_on.load(std::memory_order_relaxed)) return false;
   if (hipEventCreate(start) != hipSuccess) return false;
   if (hipEventCreate(stop) != hipSuccess) {
     (void)hipEventDestroy(*start);
@@ -69,7 +70,7 @@ extern "C" {
 void hils_profile_enable(int on) {
   hils::prof::collect();
   std::lock_guard<std::mutex> lk(hils::prof::g_mu);
-  hils::prof::g_on = on != 0;
+  hils::prof::g_on.store(on != 0);
   hils::prof::g_acc.clear();
 }
 
